@@ -1,0 +1,244 @@
+/*
+ * rwkv7.h: C ABI of librwkv7.so, the RWKV-7 decode / prefill hot path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the calls compute.  The RWKV-Server article ("RWKV 批量推理中 Prefill
+ * 的正确打开方式") separates two phases (section 2 table):
+ *   - decode: one token per sequence per step, an O(1) update of a
+ *     fixed-size recurrent state, over B independent sequences;
+ *   - prefill: one sequence, T prompt tokens, an O(n) linear scan that must
+ *     leave the same state as T single-token steps.
+ * Section 4 of the same article argues the two must not share a batch, so
+ * they are separate calls here.  Section 5 (Task.prefill) prefills
+ * prompt[:-1] and feeds the last prompt token to the first decode step; the
+ * per-sequence state is (shift_state, wkv_state, elapsed_t).  The RWKV-Runner
+ * Albatross article describes a pool of pre-allocated state slots and
+ * presence / frequency penalties with a per-step decay before selection.
+ *
+ * Conventions
+ *  - Every pointer argument documented as "device" is HIP device memory that
+ *    the caller allocated and owns (the library allocates nothing on the
+ *    device).  The model handle owns host metadata only.
+ *  - Every call is asynchronous on the caller's stream (`stream` is a
+ *    hipStream_t; NULL = the null stream), except rwkv7_load's validation,
+ *    rwkv7_poll_error (synchronises) and the size queries (host only).
+ *  - Every call returns a status: RWKV7_OK or an error code.  Host-checkable
+ *    misuse (null pointers, sizes, B or T out of range, bad shapes) fails
+ *    synchronously and launches nothing; rwkv7_last_error() describes it.
+ *    Misuse only the device can see (a token id outside [0, V), a slot index
+ *    outside [0, n_slots), a slot listed twice, an all-NaN logits row) sets
+ *    bits in a sticky device word read by rwkv7_poll_error; such rows are
+ *    computed on a clamped token / skipped slot so nothing is accessed out
+ *    of bounds.  After any error the contents of the slots named in that
+ *    call are unspecified: reset and prefill them again.
+ *  - One call in flight per (model, workspace) at a time.
+ */
+#ifndef RWKV7_H
+#define RWKV7_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define RWKV7_OK 0
+#define RWKV7_EINVAL 1     /* bad argument (null pointer, out-of-range count) */
+#define RWKV7_ESHAPE 2     /* a tensor or buffer has the wrong shape / size */
+#define RWKV7_EHIP 3       /* a HIP runtime call failed */
+#define RWKV7_EDEVICE 4    /* rwkv7_poll_error: the device error word was non-zero */
+#define RWKV7_ENOTSUP 5    /* configuration not supported by this build */
+
+/* ---- device error bits (rwkv7_poll_error) ---- */
+#define RWKV7_ERR_SLOT_RANGE 1u   /* a slot index outside [0, n_slots): row skipped */
+#define RWKV7_ERR_SLOT_DUP 2u     /* a slot listed twice in one call: later rows skipped */
+#define RWKV7_ERR_TOKEN_RANGE 4u  /* a token id outside [0, vocab): token 0 used */
+#define RWKV7_ERR_ALL_NAN 8u      /* rwkv7_greedy: a logits row was all NaN: id 0 */
+
+/* ---- tensor dtypes ---- */
+#define RWKV7_F32 0
+#define RWKV7_F16 1
+
+/* Model dimensions.  head_size must be 64; n_embd = n_head * 64. */
+typedef struct rwkv7_config {
+  int32_t n_layer;   /* L */
+  int32_t n_embd;    /* C */
+  int32_t n_head;    /* H */
+  int32_t head_size; /* N = 64 */
+  int32_t ffn;       /* F, channel-mix hidden size */
+  int32_t d_w;       /* decay adapter rank */
+  int32_t d_a;       /* in-context-rate adapter rank */
+  int32_t d_v;       /* value-residual adapter rank */
+  int32_t d_g;       /* gate adapter rank */
+  int32_t vocab;     /* V */
+} rwkv7_config;
+
+/* One named input tensor for rwkv7_load.  `data` is a device pointer to a
+ * dense row-major array of `shape` in `dtype`.  Names and shapes (matrices
+ * are (out, in) like torch.nn.Linear):
+ *   emb.weight [V,C]; ln0.{weight,bias} [C]; ln_out.{weight,bias} [C];
+ *   head.weight [V,C]; and for each layer l, prefix "blocks.l.":
+ *   ln1.{weight,bias}, ln2.{weight,bias} [C];
+ *   att.x_r, att.x_w, att.x_k, att.x_v, att.x_a, att.x_g [C] (token-shift mix);
+ *   att.w0 [C], att.w1 [d_w,C], att.w2 [C,d_w];
+ *   att.a0 [C], att.a1 [d_a,C], att.a2 [C,d_a];
+ *   att.v0 [C], att.v1 [d_v,C], att.v2 [C,d_v]  (unused in layer 0);
+ *   att.g1 [d_g,C], att.g2 [C,d_g];
+ *   att.k_k [C], att.k_a [C], att.r_k [H,N];
+ *   att.receptance.weight, att.key.weight, att.value.weight,
+ *   att.output.weight [C,C]; att.ln_x.{weight,bias} [C];
+ *   ffn.x_k [C], ffn.key.weight [F,C], ffn.key.bias [F], ffn.value.weight [C,F].
+ * Matrices may be F16 or F32 (F32 is rounded to fp16 when packed); vectors
+ * may be F16 or F32 (kept as fp32). */
+typedef struct rwkv7_tensor {
+  const char* name;
+  int32_t dtype;
+  int32_t ndim;
+  int64_t shape[4];
+  const void* data;
+} rwkv7_tensor;
+
+typedef struct rwkv7_model rwkv7_model; /* opaque host handle */
+
+/* ---- sizes (host only) ---- */
+
+/* Bytes of the packed weight buffer rwkv7_load fills. */
+int rwkv7_packed_bytes(const rwkv7_config* cfg, uint64_t* bytes);
+
+/* fp32 elements of one slot's state: for each layer, att_shift[C] |
+ * ffn_shift[C] | S[H][N][N] (S[h][i][j]: value row i, key column j). */
+int rwkv7_slot_floats(const rwkv7_config* cfg, uint64_t* n_floats);
+
+/* Bytes of a pool of n_slots slots: n_slots * slot_floats fp32 values,
+ * then (at a 256-byte aligned offset, returned in *counter_offset) one
+ * int64 step counter per slot (the elapsed-token count). */
+int rwkv7_state_bytes(const rwkv7_config* cfg, int64_t n_slots, uint64_t* bytes,
+                      uint64_t* counter_offset);
+
+/* Bytes of the workspace for decode steps of up to max_B rows and prefill
+ * calls (any T; processed in chunks of up to max_T tokens; max_T >= 1).
+ * The workspace begins with the 4-byte sticky device error word. */
+int rwkv7_workspace_bytes(const rwkv7_config* cfg, int32_t max_B, int32_t max_T,
+                          uint64_t* bytes);
+
+/* ---- model ---- */
+
+/* Validate the tensor table (every name above exactly once, shapes, dtypes),
+ * pack the weights into the caller's `packed` device buffer (>=
+ * rwkv7_packed_bytes), and return a host handle in *out.  Packing is queued
+ * on `stream`; the input tensors may be freed once it has completed.
+ * Layout of the packed buffer: fp16 matrices with the reduction dimension
+ * contiguous (r|k|v|lora-in rows fused into one matrix, each block padded to
+ * 64 rows), the channel-mix value matrix twice (hidden-major for the sparse
+ * path, C-major for the dense path), fp32 vectors.  */
+int rwkv7_load(const rwkv7_config* cfg, const rwkv7_tensor* tensors, int32_t n_tensors,
+               void* packed, uint64_t packed_bytes, void* stream, rwkv7_model** out);
+
+/* Release the host handle (the packed buffer stays the caller's). */
+int rwkv7_free(rwkv7_model* model);
+
+/* Zero the state, both shifts and the step counter of the n listed slots
+ * (slot_idx: device int32[n]). */
+int rwkv7_reset_slots(const rwkv7_model* model, void* pool, int64_t n_slots,
+                      const int32_t* slot_idx, int32_t n, void* ws, uint64_t ws_bytes,
+                      void* stream);
+
+/* ---- the hot path ---- */
+
+/* One decode step: row b consumes token_ids[b] on slot slot_idx[b] and
+ * writes its next-token logits to logits_out[b*V .. b*V+V) (fp32).
+ * slot_idx, token_ids: device int32[B]; logits_out: device fp32[B*V].
+ * Slots not listed are left bit-identical; each listed slot's counter +1.
+ * 1 <= B <= the workspace's max_B and B <= n_slots. */
+int rwkv7_decode_step(rwkv7_model* model, void* pool, int64_t n_slots, int32_t B,
+                      const int32_t* slot_idx, const int32_t* token_ids, float* logits_out,
+                      void* ws, uint64_t ws_bytes, void* stream);
+
+/* Sequence prefill: advance slot `slot` (host int, 0 <= slot < n_slots) by
+ * the T tokens token_ids[0..T) (device int32), updating its state only (no
+ * logits).  T = 0 is a no-op.  The result equals T decode steps up to
+ * rounding.  Serving code prefills prompt[:-1] and feeds the last prompt
+ * token to rwkv7_decode_step. */
+int rwkv7_prefill_seq(rwkv7_model* model, void* pool, int64_t n_slots, int32_t slot,
+                      const int32_t* token_ids, int32_t T, void* ws, uint64_t ws_bytes,
+                      void* stream);
+
+/* Penalised greedy selection over logits [B*V] (device fp32).  For row b
+ * with occ = occ_pool[slot_idx[b]*V ..] (device fp32, per-slot token
+ * occurrence weights), in separately rounded fp32 ops:
+ *   l' = l - (frequency[b]*occ + presence[b]) where occ > 0, else l;
+ *   ids_out[b] = lowest index of the maximum of l' (NaN never wins; an
+ *                all-NaN row gives 0 and RWKV7_ERR_ALL_NAN);
+ *   occ = occ*decay[b]; then occ[id] += 1.
+ * presence, frequency, decay: device fp32[B]; ids_out: device int32[B] (may
+ * be passed straight back as the next step's token_ids).  `ws` is the
+ * decode workspace (or any buffer of rwkv7_greedy_workspace_bytes). */
+int rwkv7_greedy_workspace_bytes(int32_t B, int32_t V, uint64_t* bytes);
+int rwkv7_greedy(int32_t B, int32_t V, const float* logits, float* occ_pool, int64_t n_slots,
+                 const int32_t* slot_idx, const float* presence, const float* frequency,
+                 const float* decay, int32_t* ids_out, void* ws, uint64_t ws_bytes,
+                 void* stream);
+
+/* ---- errors ---- */
+
+/* Synchronise `stream`, read and clear the sticky device error word at the
+ * start of `ws`.  *flags = the RWKV7_ERR_* bits; returns RWKV7_EDEVICE if
+ * any bit was set, else RWKV7_OK. */
+int rwkv7_poll_error(void* ws, void* stream, uint32_t* flags);
+
+const char* rwkv7_status_string(int status);
+
+/* Text of the last host-side error on this thread ("" if none). */
+const char* rwkv7_last_error(void);
+
+/* ---- tuning and measurement ---- */
+
+#define RWKV7_OPT_USE_GRAPH 1      /* 1 (default): replay a HIP graph per decode shape */
+#define RWKV7_OPT_GEMV_MAX_B 2     /* largest B served by the fp32-activation GEMV path */
+#define RWKV7_OPT_SPARSE_MAX_B 3   /* largest B served by the sparse channel-mix value path */
+#define RWKV7_OPT_KERNEL_TIMING 4  /* 1: bracket every launch with HIP events (no graph) */
+#define RWKV7_OPT_PREFILL_CHUNK 5  /* tokens per prefill chunk (<= the workspace's max_T) */
+
+int rwkv7_set_option(rwkv7_model* model, int32_t key, int64_t value);
+int rwkv7_get_option(const rwkv7_model* model, int32_t key, int64_t* value);
+
+/* Kernel classes for rwkv7_kernel_timing. */
+#define RWKV7_K_LN_MIX 0
+#define RWKV7_K_PROJ_IN 1
+#define RWKV7_K_WKV 2
+#define RWKV7_K_PROJ_OUT 3
+#define RWKV7_K_CMIX_KEY 4
+#define RWKV7_K_CMIX_VALUE 5
+#define RWKV7_K_HEAD 6
+#define RWKV7_K_OTHER 7
+#define RWKV7_K_COUNT 8
+
+/* Per-class launch count and summed duration (ms, from HIP events recorded
+ * on the caller's stream) of launches made while RWKV7_OPT_KERNEL_TIMING
+ * was 1; synchronises the recorded events.  `reset` != 0 clears them. */
+int rwkv7_kernel_timing(rwkv7_model* model, int32_t kernel_class, double* total_ms,
+                        int64_t* launches, int32_t reset);
+
+/* Name of the kernel symbol a class launches on the decode path for batch B
+ * (for matching rocprofv3 output), or "" for an unknown class. */
+const char* rwkv7_kernel_name(const rwkv7_model* model, int32_t kernel_class, int32_t B);
+
+/* ---- test hook ---- */
+
+/* Device addresses, inside `ws`, of the sparse channel-mix buffers of the
+ * last layer of the most recent decode step of B rows made with this
+ * workspace: pre-activations (fp32 [B][F], bias included), the union mask
+ * (uint8 [F], 1 where any row's pre-activation is > 0), the ascending
+ * active list (int32 [F]) and its length (int32).  Valid only when that
+ * step took the sparse path (B <= RWKV7_OPT_SPARSE_MAX_B).  The pages'
+ * sparse channel-mix skips value rows whose activation is zero; this hook
+ * lets a test check the skipped set exactly. */
+int rwkv7_debug_cmix_buffers(const rwkv7_model* model, void* ws, int32_t B, void** pre,
+                             void** mask, void** active, void** active_count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RWKV7_H */

@@ -1,0 +1,316 @@
+"""RWKV-7 decode / prefill hot path for AMD MI355X (gfx950).
+
+A thin ctypes binding over ``librwkv7.so`` (include/rwkv7.h).  The functions
+below carry the C names and only marshal arguments: torch CUDA(HIP) tensors
+are passed as device pointers, the stream defaults to torch's current
+stream.  Every step of the computation runs in the library's HIP kernels;
+there is no Python or CPU fallback, and a missing library raises.
+
+``Model`` is a convenience holder that allocates the packed weights, the
+state pool and the workspace through torch and keeps the handle.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librwkv7.so")
+
+RWKV7_OK, RWKV7_EINVAL, RWKV7_ESHAPE, RWKV7_EHIP, RWKV7_EDEVICE, RWKV7_ENOTSUP = range(6)
+ERR_SLOT_RANGE, ERR_SLOT_DUP, ERR_TOKEN_RANGE, ERR_ALL_NAN = 1, 2, 4, 8
+F32, F16 = 0, 1
+OPT_USE_GRAPH, OPT_GEMV_MAX_B, OPT_SPARSE_MAX_B, OPT_KERNEL_TIMING, OPT_PREFILL_CHUNK = 1, 2, 3, 4, 5
+K_LN_MIX, K_PROJ_IN, K_WKV, K_PROJ_OUT, K_CMIX_KEY, K_CMIX_VALUE, K_HEAD, K_OTHER = range(8)
+K_NAMES = ("ln_mix", "proj_in", "wkv", "proj_out", "cmix_key", "cmix_value", "head", "other")
+
+
+class RWKV7Error(RuntimeError):
+    def __init__(self, status: int, where: str, msg: str):
+        super().__init__(f"{where}: status {status}: {msg}")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_layer", "n_embd", "n_head", "head_size", "ffn", "d_w", "d_a", "d_v", "d_g", "vocab")]
+
+
+class Tensor(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("data", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load librwkv7.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m rwkv_linear_attention_decode_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, u64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p
+    P = ctypes.POINTER
+    sig = {
+        "rwkv7_packed_bytes": [P(Config), P(u64)],
+        "rwkv7_slot_floats": [P(Config), P(u64)],
+        "rwkv7_state_bytes": [P(Config), i64, P(u64), P(u64)],
+        "rwkv7_workspace_bytes": [P(Config), i32, i32, P(u64)],
+        "rwkv7_load": [P(Config), P(Tensor), i32, vp, u64, vp, P(vp)],
+        "rwkv7_free": [vp],
+        "rwkv7_reset_slots": [vp, vp, i64, vp, i32, vp, u64, vp],
+        "rwkv7_decode_step": [vp, vp, i64, i32, vp, vp, vp, vp, u64, vp],
+        "rwkv7_prefill_seq": [vp, vp, i64, i32, vp, i32, vp, u64, vp],
+        "rwkv7_greedy_workspace_bytes": [i32, i32, P(u64)],
+        "rwkv7_greedy": [i32, i32, vp, vp, i64, vp, vp, vp, vp, vp, vp, u64, vp],
+        "rwkv7_poll_error": [vp, vp, P(ctypes.c_uint32)],
+        "rwkv7_set_option": [vp, i32, i64],
+        "rwkv7_get_option": [vp, i32, P(i64)],
+        "rwkv7_kernel_timing": [vp, i32, P(ctypes.c_double), P(i64), i32],
+        "rwkv7_debug_cmix_buffers": [vp, vp, i32, P(vp), P(vp), P(vp), P(vp)],
+    }
+    for name, args in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    for name, args in {"rwkv7_status_string": [ctypes.c_int], "rwkv7_last_error": [],
+                       "rwkv7_kernel_name": [vp, i32, i32]}.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(rc: int, where: str):
+    if rc != RWKV7_OK:
+        L = lib()
+        raise RWKV7Error(rc, where, (L.rwkv7_last_error() or L.rwkv7_status_string(rc)).decode())
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def make_config(shape) -> Config:
+    """rwkv7_config from any object with the RWKV-7 dimension attributes."""
+    return Config(shape.n_layer, shape.n_embd, shape.n_head, shape.head_size, shape.ffn,
+                  shape.d_w, shape.d_a, shape.d_v, shape.d_g, shape.vocab)
+
+
+# ------------------------------------------------------------------ sizes
+def rwkv7_packed_bytes(cfg: Config) -> int:
+    v = ctypes.c_uint64()
+    _check(lib().rwkv7_packed_bytes(ctypes.byref(cfg), ctypes.byref(v)), "rwkv7_packed_bytes")
+    return v.value
+
+
+def rwkv7_slot_floats(cfg: Config) -> int:
+    v = ctypes.c_uint64()
+    _check(lib().rwkv7_slot_floats(ctypes.byref(cfg), ctypes.byref(v)), "rwkv7_slot_floats")
+    return v.value
+
+
+def rwkv7_state_bytes(cfg: Config, n_slots: int) -> Tuple[int, int]:
+    v, off = ctypes.c_uint64(), ctypes.c_uint64()
+    _check(lib().rwkv7_state_bytes(ctypes.byref(cfg), n_slots, ctypes.byref(v), ctypes.byref(off)),
+           "rwkv7_state_bytes")
+    return v.value, off.value
+
+
+def rwkv7_workspace_bytes(cfg: Config, max_B: int, max_T: int) -> int:
+    v = ctypes.c_uint64()
+    _check(lib().rwkv7_workspace_bytes(ctypes.byref(cfg), max_B, max_T, ctypes.byref(v)),
+           "rwkv7_workspace_bytes")
+    return v.value
+
+
+def rwkv7_greedy_workspace_bytes(B: int, V: int) -> int:
+    v = ctypes.c_uint64()
+    _check(lib().rwkv7_greedy_workspace_bytes(B, V, ctypes.byref(v)), "rwkv7_greedy_workspace_bytes")
+    return v.value
+
+
+# ------------------------------------------------------------------ model
+def rwkv7_load(cfg: Config, tensors: Dict[str, "object"], packed, stream=None) -> int:
+    """Pack device tensors (name -> torch tensor, fp16 or fp32) into ``packed`` (uint8)."""
+    import torch
+    arr = (Tensor * len(tensors))()
+    keep = []
+    for i, (name, t) in enumerate(tensors.items()):
+        if not t.is_contiguous():
+            t = t.contiguous()
+        keep.append(t)
+        if t.dtype == torch.float16:
+            dt = F16
+        elif t.dtype == torch.float32:
+            dt = F32
+        else:
+            raise TypeError(f"{name}: dtype {t.dtype} is not float16/float32")
+        nm = name.encode()
+        keep.append(nm)
+        arr[i].name = nm
+        arr[i].dtype = dt
+        arr[i].ndim = t.dim()
+        for k in range(t.dim()):
+            arr[i].shape[k] = t.shape[k]
+        arr[i].data = t.data_ptr()
+    h = ctypes.c_void_p()
+    _check(lib().rwkv7_load(ctypes.byref(cfg), arr, len(tensors), packed.data_ptr(), packed.numel(),
+                            _stream(stream), ctypes.byref(h)), "rwkv7_load")
+    return h.value
+
+
+def rwkv7_free(model: int):
+    _check(lib().rwkv7_free(model), "rwkv7_free")
+
+
+def rwkv7_reset_slots(model: int, pool, n_slots: int, slot_idx, ws, stream=None):
+    _check(lib().rwkv7_reset_slots(model, pool.data_ptr(), n_slots, _ptr(slot_idx), slot_idx.numel(),
+                                   ws.data_ptr(), ws.numel(), _stream(stream)), "rwkv7_reset_slots")
+
+
+def rwkv7_decode_step(model: int, pool, n_slots: int, slot_idx, token_ids, logits_out, ws,
+                      stream=None):
+    _check(lib().rwkv7_decode_step(model, pool.data_ptr(), n_slots, slot_idx.numel(),
+                                   _ptr(slot_idx), _ptr(token_ids), _ptr(logits_out),
+                                   ws.data_ptr(), ws.numel(), _stream(stream)), "rwkv7_decode_step")
+
+
+def rwkv7_prefill_seq(model: int, pool, n_slots: int, slot: int, token_ids, ws, stream=None):
+    _check(lib().rwkv7_prefill_seq(model, pool.data_ptr(), n_slots, slot, _ptr(token_ids),
+                                   token_ids.numel(), ws.data_ptr(), ws.numel(), _stream(stream)),
+           "rwkv7_prefill_seq")
+
+
+def rwkv7_greedy(logits, occ_pool, n_slots: int, slot_idx, presence, frequency, decay, ids_out,
+                 ws, stream=None):
+    B, V = logits.shape
+    _check(lib().rwkv7_greedy(B, V, _ptr(logits), _ptr(occ_pool), n_slots, _ptr(slot_idx),
+                              _ptr(presence), _ptr(frequency), _ptr(decay), _ptr(ids_out),
+                              ws.data_ptr(), ws.numel(), _stream(stream)), "rwkv7_greedy")
+
+
+def rwkv7_poll_error(ws, stream=None) -> int:
+    """Synchronise, return and clear the device error bits (0 = none)."""
+    f = ctypes.c_uint32()
+    rc = lib().rwkv7_poll_error(ws.data_ptr(), _stream(stream), ctypes.byref(f))
+    if rc not in (RWKV7_OK, RWKV7_EDEVICE):
+        _check(rc, "rwkv7_poll_error")
+    return f.value
+
+
+def rwkv7_set_option(model: int, key: int, value: int):
+    _check(lib().rwkv7_set_option(model, key, value), "rwkv7_set_option")
+
+
+def rwkv7_get_option(model: int, key: int) -> int:
+    v = ctypes.c_int64()
+    _check(lib().rwkv7_get_option(model, key, ctypes.byref(v)), "rwkv7_get_option")
+    return v.value
+
+
+def rwkv7_kernel_timing(model: int, cls: int, reset: bool = False) -> Tuple[float, int]:
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(lib().rwkv7_kernel_timing(model, cls, ctypes.byref(ms), ctypes.byref(n), int(reset)),
+           "rwkv7_kernel_timing")
+    return ms.value, n.value
+
+
+def rwkv7_kernel_name(model: int, cls: int, B: int) -> str:
+    return lib().rwkv7_kernel_name(model, cls, B).decode()
+
+
+def rwkv7_debug_cmix_buffers(model: int, ws, B: int) -> Tuple[int, int, int, int]:
+    """Device addresses (pre, mask, active, active_count) inside ``ws``."""
+    out = [ctypes.c_void_p() for _ in range(4)]
+    _check(lib().rwkv7_debug_cmix_buffers(model, ws.data_ptr(), B, *[ctypes.byref(o) for o in out]),
+           "rwkv7_debug_cmix_buffers")
+    return tuple(o.value for o in out)
+
+
+# ------------------------------------------------------------------ holder
+class Model:
+    """Packed weights + state pool + workspace on one device, allocated by torch."""
+
+    def __init__(self, cfg: Config, tensors: Dict[str, "object"], n_slots: int, max_B: int,
+                 max_T: int = 512, device: str = "cuda:0"):
+        import torch
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.n_slots = n_slots
+        self.packed = torch.empty(rwkv7_packed_bytes(cfg), dtype=torch.uint8, device=self.device)
+        self.handle = rwkv7_load(cfg, tensors, self.packed)
+        nbytes, self.counter_offset = rwkv7_state_bytes(cfg, n_slots)
+        self.pool = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+        self.slot_floats = rwkv7_slot_floats(cfg)
+        self.ws = torch.zeros(rwkv7_workspace_bytes(cfg, max_B, max_T), dtype=torch.uint8,
+                              device=self.device)
+        torch.cuda.synchronize(self.device)
+
+    @classmethod
+    def from_numpy(cls, shape, weights: Dict[str, "object"], n_slots: int, max_B: int,
+                   max_T: int = 512, device: str = "cuda:0") -> "Model":
+        """Upload host arrays (name -> numpy fp16/fp32) and pack them; the
+        uploaded copies are freed once packing has finished."""
+        import torch
+        dev = torch.device(device)
+        t = {k: torch.from_numpy(v).to(dev) for k, v in weights.items()}
+        m = cls(make_config(shape), t, n_slots, max_B, max_T, device)
+        del t
+        torch.cuda.synchronize(dev)
+        return m
+
+    # views of the pool
+    def slot_state(self, slot: int):
+        """fp32 view of one slot: [n_layer, 2C + H*64*64]."""
+        import torch
+        f = self.pool[: self.counter_offset].view(torch.float32)
+        n = self.slot_floats
+        return f[slot * n:(slot + 1) * n].view(self.cfg.n_layer, -1)
+
+    def counters(self):
+        import torch
+        return self.pool[self.counter_offset: self.counter_offset + 8 * self.n_slots].view(torch.int64)
+
+    def reset(self, slots):
+        rwkv7_reset_slots(self.handle, self.pool, self.n_slots, slots, self.ws)
+
+    def decode_step(self, slot_idx, token_ids, logits_out):
+        rwkv7_decode_step(self.handle, self.pool, self.n_slots, slot_idx, token_ids, logits_out, self.ws)
+
+    def prefill(self, slot: int, token_ids):
+        rwkv7_prefill_seq(self.handle, self.pool, self.n_slots, slot, token_ids, self.ws)
+
+    def greedy(self, logits, occ_pool, slot_idx, presence, frequency, decay, ids_out):
+        rwkv7_greedy(logits, occ_pool, self.n_slots, slot_idx, presence, frequency, decay, ids_out,
+                     self.ws)
+
+    def poll_error(self) -> int:
+        return rwkv7_poll_error(self.ws)
+
+    def set_option(self, key: int, value: int):
+        rwkv7_set_option(self.handle, key, value)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            rwkv7_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

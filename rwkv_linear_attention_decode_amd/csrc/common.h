@@ -1,0 +1,144 @@
+// Shared device helpers and kernel-argument structs for librwkv7 (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define RW_DEV __device__ __forceinline__
+
+typedef _Float16 half_t;
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte loads / stores; the _nt forms are non-temporal (streamed once).
+RW_DEV u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+RW_DEV u32x4 ld16_nt(const void* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
+RW_DEV void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+RW_DEV floatx4 ldf4(const float* p) { return *reinterpret_cast<const floatx4*>(p); }
+RW_DEV floatx4 ldf4_nt(const float* p) { return __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p)); }
+RW_DEV void stf4(float* p, floatx4 v) { *reinterpret_cast<floatx4*>(p) = v; }
+RW_DEV void stf4_nt(float* p, floatx4 v) { __builtin_nontemporal_store(v, reinterpret_cast<floatx4*>(p)); }
+
+// device error bits (same values as the public RWKV7_ERR_* macros)
+enum : uint32_t {
+  ERRB_SLOT_RANGE = 1u,
+  ERRB_SLOT_DUP = 2u,
+  ERRB_TOKEN_RANGE = 4u,
+  ERRB_ALL_NAN = 8u,
+};
+
+// epilogues of the projection kernels
+enum : int {
+  EPI_NONE = 0,      // out_f32 = acc
+  EPI_TANH = 1,      // out_f32 = tanh(acc)
+  EPI_SIGMOID = 2,   // out_f32 = sigmoid(acc)
+  EPI_RESID = 3,     // out_f32 += acc (residual stream)
+  EPI_PRE = 4,       // out_f32 = acc + aux[n]; mask[n] = any row > 0
+  EPI_RELU2_H = 5,   // out_f16 = relu(acc + aux[n])^2
+  EPI_STORE_H = 6,   // out_f16 = acc
+};
+
+// One output block of a fused projection: rows [row0, row1) of the packed
+// matrix read activation `act` (row stride ld_act elements) and write
+// `out` (row stride ld_out elements) through epilogue `epi`.
+struct Seg {
+  int row0, row1;
+  int epi;
+  int ld_act;
+  int ld_out;
+  int pad_;
+  const void* act;
+  void* out;
+  const float* aux;
+  unsigned char* mask;
+};
+
+#define MAX_SEGS 8
+
+struct ProjArgs {
+  const half_t* W;   // [rows][K] fp16, K contiguous
+  int K;
+  int M;             // activation rows (batch rows / tokens)
+  int nseg;
+  int n_tiles;       // MFMA path: number of 64-column tiles
+  int m_tiles;       // MFMA path: number of M tiles
+  int pad_;
+  Seg seg[MAX_SEGS];
+};
+
+RW_DEV float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+RW_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+RW_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Sum over a 256-thread block; `red` is >= 4 floats of LDS.  All threads get the total.
+RW_DEV float block_sum_256(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+RW_DEV void set_err(uint32_t* err, uint32_t bits) {
+  if (err) atomicOr(err, bits);
+}
+
+RW_DEV float h2f(half_t h) { return (float)h; }
+
+// Select the segment whose rows contain `row` (segments sorted by row0).
+RW_DEV Seg pick_seg(const ProjArgs& a, int row) {
+  Seg s = a.seg[0];
+#pragma unroll
+  for (int i = 1; i < MAX_SEGS; ++i)
+    if (i < a.nseg && row >= a.seg[i].row0) s = a.seg[i];
+  return s;
+}
+
+// Apply the epilogue of segment `s` to output column n (relative to the
+// segment), activation row m.
+RW_DEV void epi_store(const Seg& s, int n, int m, float v) {
+  switch (s.epi) {
+    case EPI_NONE:
+      ((float*)s.out)[(long)m * s.ld_out + n] = v;
+      break;
+    case EPI_TANH:
+      ((float*)s.out)[(long)m * s.ld_out + n] = tanhf(v);
+      break;
+    case EPI_SIGMOID:
+      ((float*)s.out)[(long)m * s.ld_out + n] = sigmoidf_(v);
+      break;
+    case EPI_RESID: {
+      float* p = (float*)s.out + (long)m * s.ld_out + n;
+      *p = *p + v;
+      break;
+    }
+    case EPI_PRE:
+      ((float*)s.out)[(long)m * s.ld_out + n] = v + s.aux[n];
+      break;
+    case EPI_RELU2_H: {
+      float z = v + s.aux[n];
+      z = z > 0.0f ? z * z : 0.0f;
+      ((half_t*)s.out)[(long)m * s.ld_out + n] = (half_t)z;
+      break;
+    }
+    case EPI_STORE_H:
+      ((half_t*)s.out)[(long)m * s.ld_out + n] = (half_t)v;
+      break;
+    default:
+      break;
+  }
+}

@@ -1,0 +1,526 @@
+// Element-wise and bookkeeping kernels of librwkv7: row validation, embedding
+// + LN0, the fused residual-fold + LayerNorm + token-shift mix, slot reset,
+// weight packing, the sparse ReLU^2 channel-mix value, and the penalised
+// greedy selection.
+#include "launch.h"
+
+#include <float.h>
+#include <limits.h>
+
+// ============================================================== validation
+// One workgroup.  Decode: checks every row's slot (range, duplicates) and
+// token (range), writes sanitized copies, bumps each valid slot's counter.
+// Prefill: checks tokens and bumps the slot's counter by n_tok.
+__global__ __launch_bounds__(256) void k_validate(ValidateArgs a) {
+  uint32_t bits = 0;
+  for (int b = threadIdx.x; b < a.n_rows; b += 256) {
+    const int s = a.slot_idx[b];
+    int out = s;
+    if (s < 0 || (int64_t)s >= a.n_slots) {
+      bits |= ERRB_SLOT_RANGE;
+      out = -1;
+    } else {
+      for (int j = 0; j < b; ++j)
+        if (a.slot_idx[j] == s) {
+          bits |= ERRB_SLOT_DUP;
+          out = -1;
+          break;
+        }
+    }
+    a.slots_out[b] = out;
+    if (out >= 0 && a.counters) a.counters[out] += 1;
+  }
+  for (int t = threadIdx.x; t < a.n_tok; t += 256) {
+    int tok = a.tokens[t];
+    if (tok < 0 || tok >= a.vocab) {
+      bits |= ERRB_TOKEN_RANGE;
+      tok = 0;
+    }
+    a.tok_out[t] = tok;
+  }
+  if (a.n_rows == 0 && threadIdx.x == 0 && a.counters && a.seq_slot >= 0)
+    a.counters[a.seq_slot] += a.n_tok;
+  if (bits) set_err(a.err, bits);
+}
+
+hipError_t launch_validate(const ValidateArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_validate, dim3(1), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ============================================================== LayerNorm helpers
+// Per-thread slice: elements c = threadIdx.x + 256*e, e < C/256 (<= 16).
+template <int NE>
+RW_DEV void ln_rows(const float* v, float* mean_out, float* rstd_out, float* red) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < NE; ++e) s += v[e];
+  const float C = 256.0f * NE;
+  const float mean = block_sum_256(s, red) / C;
+  float q = 0.f;
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    const float d = v[e] - mean;
+    q += d * d;
+  }
+  const float var = block_sum_256(q, red + 4) / C;
+  *mean_out = mean;
+  *rstd_out = 1.0f / sqrtf(var + 1e-5f);
+}
+
+// ============================================================== embedding
+template <int NE>
+__global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
+  __shared__ float red[8];
+  const int r = blockIdx.x;
+  const int tok = a.tok[r];
+  const half_t* e = a.emb + (long)tok * a.C;
+  float v[NE];
+#pragma unroll
+  for (int i = 0; i < NE; ++i) v[i] = (float)e[threadIdx.x + 256 * i];
+  float mean, rstd;
+  ln_rows<NE>(v, &mean, &rstd, red);
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    a.x[(long)r * a.C + c] = (v[i] - mean) * rstd * a.g[c] + a.b[c];
+  }
+}
+
+#define NE_DISPATCH(C, KERNEL, ...)                                                  \
+  switch ((C) / 256) {                                                                \
+    case 1: hipLaunchKernelGGL(KERNEL<1>, __VA_ARGS__); break;                        \
+    case 2: hipLaunchKernelGGL(KERNEL<2>, __VA_ARGS__); break;                        \
+    case 4: hipLaunchKernelGGL(KERNEL<4>, __VA_ARGS__); break;                        \
+    case 8: hipLaunchKernelGGL(KERNEL<8>, __VA_ARGS__); break;                        \
+    case 10: hipLaunchKernelGGL(KERNEL<10>, __VA_ARGS__); break;                       \
+    case 12: hipLaunchKernelGGL(KERNEL<12>, __VA_ARGS__); break;                       \
+    case 16: hipLaunchKernelGGL(KERNEL<16>, __VA_ARGS__); break;                       \
+    default: return hipErrorInvalidValue;                                             \
+  }
+
+hipError_t launch_embed(const EmbedArgs& a, hipStream_t st) {
+  if (a.C % 256) return hipErrorInvalidValue;
+  NE_DISPATCH(a.C, k_embed, dim3(a.R), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ============================================================== LN + token-shift mix
+template <int NE>
+__global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
+  __shared__ float red[8];
+  const int r = blockIdx.x;
+  const int C = a.C;
+  float v[NE];
+  float* xr = a.x + (long)r * C;
+#pragma unroll
+  for (int i = 0; i < NE; ++i) v[i] = xr[threadIdx.x + 256 * i];
+  if (a.nparts > 0) {
+    for (int s = 0; s < a.nparts; ++s) {
+      const float* p = a.parts + ((long)s * a.R + r) * C;
+#pragma unroll
+      for (int i = 0; i < NE; ++i) v[i] += p[threadIdx.x + 256 * i];
+    }
+#pragma unroll
+    for (int i = 0; i < NE; ++i) xr[threadIdx.x + 256 * i] = v[i];
+  }
+  float mean, rstd;
+  ln_rows<NE>(v, &mean, &rstd, red);
+  float u[NE];
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    u[i] = (v[i] - mean) * rstd * a.g[c] + a.b[c];
+  }
+
+  float prev[NE];
+  if (a.mode == LNMIX_DECODE) {
+    const int slot = a.slots[r];
+    float* sh = slot >= 0 ? a.pool + (long)slot * a.slot_stride + a.shift_off : nullptr;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) prev[i] = sh ? sh[threadIdx.x + 256 * i] : 0.0f;
+    if (sh) {
+#pragma unroll
+      for (int i = 0; i < NE; ++i) sh[threadIdx.x + 256 * i] = u[i];
+    }
+  } else if (a.mode == LNMIX_SEQ) {
+    if (r == 0) {
+      const float* sh = a.pool + (long)a.seq_slot * a.slot_stride + a.shift_off;
+#pragma unroll
+      for (int i = 0; i < NE; ++i) prev[i] = sh[threadIdx.x + 256 * i];
+    } else {
+      // LayerNorm of the previous token's row (x is read-only in this mode)
+      const float* xp = a.x + (long)(r - 1) * C;
+      float w[NE];
+#pragma unroll
+      for (int i = 0; i < NE; ++i) w[i] = xp[threadIdx.x + 256 * i];
+      float m2, rs2;
+      ln_rows<NE>(w, &m2, &rs2, red);
+#pragma unroll
+      for (int i = 0; i < NE; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        prev[i] = (w[i] - m2) * rs2 * a.g[c] + a.b[c];
+      }
+    }
+    if (r == a.R - 1) {
+#pragma unroll
+      for (int i = 0; i < NE; ++i) a.shift_tmp[threadIdx.x + 256 * i] = u[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NE; ++i) prev[i] = u[i];
+  }
+
+  for (int q = 0; q < a.nq; ++q) {
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const float mu = a.mu ? a.mu[(long)q * C + c] : 0.0f;
+      const float o = u[i] + (prev[i] - u[i]) * mu;
+      const long off = q * a.out_q_stride + (long)r * C + c;
+      if (a.out_f16)
+        ((half_t*)a.out)[off] = (half_t)o;
+      else
+        ((float*)a.out)[off] = o;
+    }
+  }
+}
+
+hipError_t launch_ln_mix(const LnMixArgs& a, hipStream_t st) {
+  if (a.C % 256) return hipErrorInvalidValue;
+  if (a.mode == LNMIX_SEQ && a.nparts) return hipErrorInvalidValue;
+  NE_DISPATCH(a.C, k_ln_mix, dim3(a.R), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ============================================================== copies / fills
+__global__ void k_copy_f32(float* d, const float* s, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) d[i] = s[i];
+}
+__global__ void k_fill_f32(float* d, float v, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) d[i] = v;
+}
+
+hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_copy_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dst, src, n);
+  return hipGetLastError();
+}
+hipError_t launch_zero_f32(float* dst, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dst, 0.0f, n);
+  return hipGetLastError();
+}
+hipError_t launch_fill_vec(float* dst, float v, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dst, v, n);
+  return hipGetLastError();
+}
+
+// ============================================================== slot reset
+__global__ void k_reset(ResetArgs a) {
+  const int k = blockIdx.y;
+  const int s = a.slot_idx[k];
+  if (s < 0 || (int64_t)s >= a.n_slots) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) set_err(a.err, ERRB_SLOT_RANGE);
+    return;
+  }
+  float* base = a.pool + (int64_t)s * a.slot_stride;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.slot_stride;
+       i += (int64_t)gridDim.x * blockDim.x)
+    base[i] = 0.0f;
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.counters[s] = 0;
+}
+
+hipError_t launch_reset(const ResetArgs& a, hipStream_t st) {
+  if (a.n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_reset, dim3(256, a.n), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ============================================================== packing
+__global__ void k_pack_matrix(half_t* dst, int64_t dst_ld, const void* src, int src_f16,
+                              int64_t rows, int64_t cols) {
+  const int64_t n = rows * cols;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / cols, c = i % cols;
+    const float v = src_f16 ? (float)((const half_t*)src)[i] : ((const float*)src)[i];
+    dst[r * dst_ld + c] = (half_t)v;
+  }
+}
+
+// dst[c][r] = src[r][c]; 64x64 tiles through LDS.
+__global__ void k_pack_transpose(half_t* dst, const void* src, int src_f16, int64_t rows,
+                                 int64_t cols) {
+  __shared__ float tile[64][65];
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += blockDim.x) {
+    const int rr = i / 64, cc = i % 64;
+    const int64_t r = r0 + rr, c = c0 + cc;
+    float v = 0.f;
+    if (r < rows && c < cols)
+      v = src_f16 ? (float)((const half_t*)src)[r * cols + c] : ((const float*)src)[r * cols + c];
+    tile[rr][cc] = v;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += blockDim.x) {
+    const int cc = i / 64, rr = i % 64;
+    const int64_t r = r0 + rr, c = c0 + cc;
+    if (r < rows && c < cols) dst[c * rows + r] = (half_t)tile[rr][cc];
+  }
+}
+
+__global__ void k_pack_vec(float* dst, const void* src, int src_f16, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src_f16 ? (float)((const half_t*)src)[i] : ((const float*)src)[i];
+}
+
+hipError_t launch_pack_matrix(half_t* dst, int64_t dst_ld, const void* src, int src_f16,
+                              int64_t rows, int64_t cols, hipStream_t st) {
+  const int64_t n = rows * cols;
+  const int64_t blocks = n / 256 + 1;
+  hipLaunchKernelGGL(k_pack_matrix, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256),
+                     0, st, dst, dst_ld, src, src_f16, rows, cols);
+  return hipGetLastError();
+}
+hipError_t launch_pack_transpose(half_t* dst, const void* src, int src_f16, int64_t rows,
+                                 int64_t cols, hipStream_t st) {
+  hipLaunchKernelGGL(k_pack_transpose, dim3((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64)),
+                     dim3(256), 0, st, dst, src, src_f16, rows, cols);
+  return hipGetLastError();
+}
+hipError_t launch_pack_vec(float* dst, const void* src, int src_f16, int64_t n, hipStream_t st) {
+  hipLaunchKernelGGL(k_pack_vec, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dst, src,
+                     src_f16, n);
+  return hipGetLastError();
+}
+
+// ============================================================== sparse channel-mix value
+// Grid: (C/64 column slices) x NS splits of the active list.  Each workgroup
+// compacts the union mask (ascending f, deterministic), takes its split of
+// the list, and accumulates h_f * Wv[f, slice] for every row, with
+// h = relu(pre)^2 recomputed in fp32 from the stored pre-activation.
+// Results go to per-split partials, folded into the residual in a fixed
+// order by the next LayerNorm kernel.
+constexpr int CMIX_MAXF = 16384;
+constexpr int CMIX_MAXB = 4;
+
+template <int B>
+__global__ __launch_bounds__(256) void k_cmix_sparse(CmixArgs a) {
+  __shared__ unsigned short s_idx[CMIX_MAXF];
+  __shared__ int s_wcnt[4];
+  __shared__ float s_red[32][B][64 + 1];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+
+  // ---- compaction of the mask (F <= 16384), ascending order
+  int total = 0;
+  for (int base = 0; base < a.F; base += 256) {
+    const int f = base + t;
+    const bool on = f < a.F && a.mask[f] != 0;
+    const unsigned long long bal = __ballot(on);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) s_wcnt[wave] = __popcll(bal);
+    __syncthreads();
+    int woff = 0;
+    for (int w = 0; w < wave; ++w) woff += s_wcnt[w];
+    const int tot = s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
+    if (on) s_idx[total + woff + before] = (unsigned short)f;
+    total += tot;
+    __syncthreads();
+  }
+  const int s = blockIdx.y;
+  const int p0 = (int)((long)total * s / a.NS);
+  const int p1 = (int)((long)total * (s + 1) / a.NS);
+  if (a.dbg_idx && blockIdx.x == 0 && s == 0) {
+    for (int i = t; i < total; i += 256) a.dbg_idx[i] = s_idx[i];
+    if (t == 0) *a.dbg_cnt = total;
+  }
+
+  // ---- gather: thread t -> row-group rg (32 of them), 8 columns
+  const int rg = t >> 3;
+  const int c8 = (t & 7) * 8;
+  const int cb = blockIdx.x * 64 + c8;
+  float acc[B][8];
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[b][e] = 0.f;
+
+  int p = p0 + rg;
+  for (; p + 96 < p1; p += 128) {
+    u32x4 w4[4];
+    float h4[4][B];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int f = s_idx[p + 32 * u];
+      w4[u] = ld16_nt(a.Wv + (long)f * a.C + cb);
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const float z = a.pre[(long)b * a.F + f];
+        h4[u][b] = z > 0.f ? z * z : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const half8 hv = __builtin_bit_cast(half8, w4[u]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float wf = (float)hv[e];
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[b][e] = fmaf(h4[u][b], wf, acc[b][e]);
+      }
+    }
+  }
+  for (; p < p1; p += 32) {
+    const int f = s_idx[p];
+    const u32x4 w = ld16_nt(a.Wv + (long)f * a.C + cb);
+    const half8 hv = __builtin_bit_cast(half8, w);
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const float z = a.pre[(long)b * a.F + f];
+      const float h = z > 0.f ? z * z : 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[b][e] = fmaf(h, (float)hv[e], acc[b][e]);
+    }
+  }
+
+  // ---- reduce the 32 row-groups in a fixed order
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_red[rg][b][c8 + e] = acc[b][e];
+  __syncthreads();
+  for (int o = t; o < B * 64; o += 256) {
+    const int b = o / 64, c = o % 64;
+    float sum = 0.f;
+    for (int g = 0; g < 32; ++g) sum += s_red[g][b][c];
+    a.part[((long)s * a.B + b) * a.C + blockIdx.x * 64 + c] = sum;
+  }
+}
+
+int cmix_sparse_max_b() { return CMIX_MAXB; }
+const char* cmix_sparse_kernel_name(int B) {
+  (void)B;
+  return "k_cmix_sparse";
+}
+
+hipError_t launch_cmix_sparse(const CmixArgs& a, hipStream_t st) {
+  if (a.F > CMIX_MAXF || a.C % 64 || a.B < 1 || a.B > CMIX_MAXB) return hipErrorInvalidValue;
+  const dim3 grid(a.C / 64, a.NS);
+  switch (a.B) {
+    case 1: hipLaunchKernelGGL(k_cmix_sparse<1>, grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL(k_cmix_sparse<2>, grid, dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL(k_cmix_sparse<3>, grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL(k_cmix_sparse<4>, grid, dim3(256), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+// ============================================================== penalised greedy
+// Pass 1, grid (B, nblk): penalise with the current occurrences, decay them,
+// and reduce each block's slice to (max, lowest index).  Pass 2, grid B:
+// reduce the block results, write the id and add 1 to its occurrence.
+// Every penalty op is a separately rounded fp32 op (no contraction).
+RW_DEV bool better(float v, int i, float bv, int bi) {
+  if (v != v) return false;       // NaN never wins
+  if (bi == INT_MAX) return true;  // first real value
+  return v > bv || (v == bv && i < bi);
+}
+
+constexpr int GREEDY_PER_BLOCK = 2048;
+
+__global__ __launch_bounds__(256) void k_greedy_part(GreedyArgs a) {
+  __shared__ float sv[256];
+  __shared__ int si[256];
+  const int b = blockIdx.x;
+  const int blk = blockIdx.y;
+  const int slot = a.slot_idx[b];
+  const bool ok = slot >= 0 && (int64_t)slot < a.n_slots;
+  if (!ok && blk == 0 && threadIdx.x == 0) set_err(a.err, ERRB_SLOT_RANGE);
+  float* occ = ok ? a.occ + (int64_t)slot * a.V : nullptr;
+  const float pres = a.presence[b], freq = a.frequency[b], dec = a.decay[b];
+  const float* lg = a.logits + (int64_t)b * a.V;
+  float bv = 0.f;
+  int bi = INT_MAX;
+  const int v0 = blk * GREEDY_PER_BLOCK;
+  const int v1 = min(a.V, v0 + GREEDY_PER_BLOCK);
+  for (int v = v0 + threadIdx.x; v < v1; v += 256) {
+    float l = lg[v];
+    if (occ) {
+      const float o = occ[v];
+      if (o > 0.f) l = __fsub_rn(l, __fadd_rn(__fmul_rn(freq, o), pres));
+      occ[v] = __fmul_rn(o, dec);
+    }
+    if (better(l, v, bv, bi)) {
+      bv = l;
+      bi = v;
+    }
+  }
+  sv[threadIdx.x] = bv;
+  si[threadIdx.x] = bi;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) {
+      const float v2 = sv[threadIdx.x + o];
+      const int i2 = si[threadIdx.x + o];
+      if (i2 != INT_MAX && better(v2, i2, sv[threadIdx.x], si[threadIdx.x])) {
+        sv[threadIdx.x] = v2;
+        si[threadIdx.x] = i2;
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    a.part_val[b * a.nblk + blk] = sv[0];
+    a.part_idx[b * a.nblk + blk] = si[0];
+  }
+}
+
+__global__ __launch_bounds__(64) void k_greedy_final(GreedyArgs a) {
+  const int b = blockIdx.x;
+  float bv = 0.f;
+  int bi = INT_MAX;
+  for (int k = threadIdx.x; k < a.nblk; k += 64) {
+    const float v = a.part_val[b * a.nblk + k];
+    const int i = a.part_idx[b * a.nblk + k];
+    if (i != INT_MAX && better(v, i, bv, bi)) {
+      bv = v;
+      bi = i;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const float v2 = __shfl_xor(bv, o);
+    const int i2 = __shfl_xor(bi, o);
+    if (i2 != INT_MAX && better(v2, i2, bv, bi)) {
+      bv = v2;
+      bi = i2;
+    }
+  }
+  if (threadIdx.x == 0) {
+    int id = bi;
+    if (id == INT_MAX) {
+      id = 0;
+      set_err(a.err, ERRB_ALL_NAN);
+    }
+    a.ids[b] = id;
+    const int slot = a.slot_idx[b];
+    if (slot >= 0 && (int64_t)slot < a.n_slots) {
+      float* o = a.occ + (int64_t)slot * a.V + id;
+      *o = __fadd_rn(*o, 1.0f);
+    }
+  }
+}
+
+int greedy_blocks(int V) { return (V + GREEDY_PER_BLOCK - 1) / GREEDY_PER_BLOCK; }
+
+hipError_t launch_greedy(const GreedyArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_greedy_part, dim3(a.B, a.nblk), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_greedy_final, dim3(a.B), dim3(64), 0, st, a);
+  return hipGetLastError();
+}

@@ -1,0 +1,294 @@
+// Projection kernels: fp16 weights [rows][K] (K contiguous) times activations.
+//
+// The RWKV-Server article (section 3) credits the decode speed of its CUDA
+// backend to M=1 specialised linears (a row-1 kernel and a split-K one) and
+// switches to dense GEMMs for prefill.  On gfx950 the same split is:
+//   * k_gemv  : B <= 4 rows, fp32 activations held in VGPRs, each weight row
+//               reduced by one 64-lane (or 32-lane) group with 16-byte
+//               non-temporal loads; no split-K partials, so no second pass.
+//   * k_gemm  : larger B and prefill, fp16 activations staged in LDS, fp16
+//               weights streamed straight from HBM into the B operand of
+//               v_mfma_f32_16x16x32_f16 (fp32 accumulate).
+#include "launch.h"
+
+// ============================================================== GEMV
+template <int B, int LPR, int NCH, int RPW>
+__global__ __launch_bounds__(256) void k_gemv(ProjArgs a) {
+  constexpr int GPW = 64 / LPR;
+  constexpr int ROWS_WAVE = GPW * RPW;
+  constexpr int ROWS_WG = 4 * ROWS_WAVE;
+  constexpr int K = LPR * NCH * 8;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int grp = lane / LPR;
+  const int lig = lane % LPR;
+  const int row_wg = blockIdx.x * ROWS_WG;
+  const Seg sg = pick_seg(a, row_wg);
+  const int row_base = row_wg + wave * ROWS_WAVE + grp * RPW;
+
+  u32x4 w[RPW][NCH];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int row = row_base + i;
+    const half_t* wp = a.W + (long)row * K + lig * 8;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if (row < sg.row1)
+        w[i][c] = ld16_nt(wp + c * LPR * 8);
+      else
+        w[i][c] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  float xa[B][NCH][8];
+  const float* X = reinterpret_cast<const float*>(sg.act);
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const float* xp = X + (long)b * sg.ld_act + (c * LPR + lig) * 8;
+      const floatx4 p0 = ldf4(xp), p1 = ldf4(xp + 4);
+      xa[b][c][0] = p0.x; xa[b][c][1] = p0.y; xa[b][c][2] = p0.z; xa[b][c][3] = p0.w;
+      xa[b][c][4] = p1.x; xa[b][c][5] = p1.y; xa[b][c][6] = p1.z; xa[b][c][7] = p1.w;
+    }
+
+  float acc[RPW][B];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i)
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[i][b] = 0.0f;
+
+#pragma unroll
+  for (int i = 0; i < RPW; ++i)
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const half8 h = __builtin_bit_cast(half8, w[i][c]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float wf = (float)h[e];
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[i][b] = fmaf(wf, xa[b][c][e], acc[i][b]);
+      }
+    }
+
+#pragma unroll
+  for (int i = 0; i < RPW; ++i)
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+      for (int o = LPR / 2; o >= 1; o >>= 1) acc[i][b] += __shfl_xor(acc[i][b], o);
+
+  if (lig == 0) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int row = row_base + i;
+      if (row < sg.row1) {
+        const int n = row - sg.row0;
+        if (sg.epi == EPI_PRE) {
+          bool any = false;
+#pragma unroll
+          for (int b = 0; b < B; ++b) {
+            const float pre = acc[i][b] + sg.aux[n];
+            ((float*)sg.out)[(long)b * sg.ld_out + n] = pre;
+            any |= pre > 0.0f;
+          }
+          if (sg.mask) sg.mask[n] = any ? 1 : 0;
+        } else {
+#pragma unroll
+          for (int b = 0; b < B; ++b) epi_store(sg, n, b, acc[i][b]);
+        }
+      }
+    }
+  }
+}
+
+static constexpr int gemv_rpw(int B) { return B <= 2 ? 4 : 2; }
+
+int gemv_rows_per_wg(int B, int K) {
+  const int lpr = (K == 256) ? 32 : 64;
+  return 4 * (64 / lpr) * gemv_rpw(B);
+}
+
+bool gemv_supported(int B, int K) {
+  if (B < 1 || B > 4) return false;
+  if (K == 256) return true;
+  return K % 512 == 0 && K / 512 >= 1 && K / 512 <= 8;
+}
+
+#define GEMV_NAME(B, L, N) "k_gemv<" #B "," #L "," #N ">"
+
+template <int B>
+static hipError_t gemv_dispatch_b(const ProjArgs& a, int total_rows, hipStream_t st) {
+  constexpr int RPW = gemv_rpw(B);
+  const int K = a.K;
+  const int rows_wg = gemv_rows_per_wg(B, K);
+  const dim3 grid((total_rows + rows_wg - 1) / rows_wg);
+  if (K == 256) {
+    hipLaunchKernelGGL((k_gemv<B, 32, 1, RPW>), grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
+  switch (K / 512) {
+#define CASE(n) case n: hipLaunchKernelGGL((k_gemv<B, 64, n, RPW>), grid, dim3(256), 0, st, a); break;
+    CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
+#undef CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv(const ProjArgs& a, int total_rows, hipStream_t st) {
+  switch (a.M) {
+    case 1: return gemv_dispatch_b<1>(a, total_rows, st);
+    case 2: return gemv_dispatch_b<2>(a, total_rows, st);
+    case 3: return gemv_dispatch_b<3>(a, total_rows, st);
+    case 4: return gemv_dispatch_b<4>(a, total_rows, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+const char* gemv_kernel_name(int B, int K) {
+  (void)B; (void)K;
+  return "k_gemv";
+}
+
+// ============================================================== MFMA GEMM
+// Workgroup tile: MT activation rows x 64 output columns; 4 waves, each
+// owning 16 columns.  K is consumed in chunks of 128: lane l (column l%16,
+// group g = l/16) holds 64 contiguous bytes of its weight row, k in
+// [32g, 32g+32) of the chunk, used as four 8-wide MFMA K slices.  The A
+// operand is read from LDS with the same k mapping, so the product sums
+// over every k exactly once.
+template <int MT>
+__global__ __launch_bounds__(256) void k_gemm(ProjArgs a) {
+  constexpr int KC = 128;
+  constexpr int MT16 = MT / 16;
+  constexpr int LDA = KC + 8;  // halves per LDS row (16-byte skew)
+  __shared__ __attribute__((aligned(16))) half_t As[2][MT][LDA];
+
+  // XCD-aware tile order: consecutive tiles (same column tile, successive
+  // M tiles) go to the same XCD so its L2 serves the repeated weight reads.
+  const int total = a.n_tiles * a.m_tiles;
+  const int per_xcd = (total + 7) / 8;
+  const int lin = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (lin >= total) return;
+  const int n_tile = lin / a.m_tiles;
+  const int m_tile = lin % a.m_tiles;
+  const int n0 = n_tile * 64;
+  const int m0 = m_tile * MT;
+  const Seg sg = pick_seg(a, n0);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int col = n0 + wave * 16 + (lane & 15);
+  const bool col_ok = col < sg.row1;
+  const half_t* wrow = a.W + (long)(col_ok ? col : sg.row0) * a.K + 32 * g;
+  const half_t* X = reinterpret_cast<const half_t*>(sg.act);
+  const int nk = a.K / KC;
+
+  floatx4 acc[MT16];
+#pragma unroll
+  for (int t = 0; t < MT16; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto load_w = [&](int kc, u32x4* dst) {
+    const half_t* p = wrow + kc * KC;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dst[s] = ld16_nt(p + 8 * s);
+  };
+  auto load_a = [&](int kc, int buf) {
+#pragma unroll
+    for (int p = 0; p < MT / 16; ++p) {
+      const int idx = p * 256 + threadIdx.x;
+      const int r = idx >> 4;
+      const int c = idx & 15;
+      const int m = m0 + r;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (m < a.M) v = ld16(X + (long)m * sg.ld_act + kc * KC + c * 8);
+      st16(&As[buf][r][c * 8], v);
+    }
+  };
+
+  u32x4 wf[4], wn[4];
+  load_w(0, wf);
+  load_a(0, 0);
+  __syncthreads();
+  int buf = 0;
+  for (int kc = 0; kc < nk; ++kc) {
+    if (kc + 1 < nk) {
+      load_w(kc + 1, wn);
+      load_a(kc + 1, buf ^ 1);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const half8 bv = __builtin_bit_cast(half8, wf[s]);
+#pragma unroll
+      for (int t = 0; t < MT16; ++t) {
+        const half8 av = *reinterpret_cast<const half8*>(&As[buf][t * 16 + (lane & 15)][32 * g + 8 * s]);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[t], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) wf[s] = wn[s];
+    buf ^= 1;
+  }
+
+  if (!col_ok) return;
+  const int n = col - sg.row0;
+#pragma unroll
+  for (int t = 0; t < MT16; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + t * 16 + 4 * g + i;
+      if (m < a.M) {
+        if (sg.epi == EPI_PRE) {
+          ((float*)sg.out)[(long)m * sg.ld_out + n] = acc[t][i] + sg.aux[n];
+        } else {
+          epi_store(sg, n, m, acc[t][i]);
+        }
+      }
+    }
+}
+
+// Union mask of the sparse path when the key projection runs on MFMA:
+// computed afterwards from the stored pre-activations.
+__global__ void k_pre_mask(const float* pre, int ld, int M, int F, unsigned char* mask) {
+  const int f = blockIdx.x * blockDim.x + threadIdx.x;
+  if (f >= F) return;
+  bool any = false;
+  for (int m = 0; m < M; ++m) any |= pre[(long)m * ld + f] > 0.0f;
+  mask[f] = any ? 1 : 0;
+}
+
+hipError_t launch_gemm(ProjArgs a, int total_rows, hipStream_t st) {
+  if (a.K % 128 != 0) return hipErrorInvalidValue;
+  a.n_tiles = (total_rows + 63) / 64;
+  int mt = a.M <= 16 ? 16 : (a.M <= 32 ? 32 : 64);
+  a.m_tiles = (a.M + mt - 1) / mt;
+  const int total = a.n_tiles * a.m_tiles;
+  const dim3 grid(((total + 7) / 8) * 8);
+  if (mt == 16)
+    hipLaunchKernelGGL((k_gemm<16>), grid, dim3(256), 0, st, a);
+  else if (mt == 32)
+    hipLaunchKernelGGL((k_gemm<32>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_gemm<64>), grid, dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  for (int i = 0; i < a.nseg; ++i) {
+    const Seg& s = a.seg[i];
+    if (s.epi == EPI_PRE && s.mask) {
+      const int F = s.row1 - s.row0;
+      hipLaunchKernelGGL(k_pre_mask, dim3((F + 255) / 256), dim3(256), 0, st,
+                         (const float*)s.out, s.ld_out, a.M, F, s.mask);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+const char* gemm_kernel_name(int M) {
+  (void)M;
+  return "k_gemm";
+}

@@ -1,0 +1,267 @@
+// WKV-7 kernels.
+//
+// The RWKV-Server article (section 2 table) describes decode as an O(1)
+// update of a fixed-size state and prefill as an O(n) linear scan.  For one
+// head the state S is 64x64 fp32, S[i][j] with i the value channel and j the
+// key channel, and one token does
+//     S <- S diag(d) + (S a) b^T + v k~^T ,   y = S r
+// (a = -kappa_hat, b = kappa_hat * alpha), followed by a per-head GroupNorm,
+// the (r . k~ . r_k) v bonus and the gate g.
+//
+// Decode: one workgroup per (row, head).  The head's low-rank adapter
+// outputs (decay, alpha, value gate, gate) are computed in the workgroup from
+// the 480-ish adapter activations, the state streams through VGPRs once
+// (16 floats per thread, 4 threads per value row), and the gated GroupNorm
+// output is written in the activation dtype of the next projection.
+//
+// Prefill: the same per-(token, head) prologue writes d, a, b, k~, v, g and
+// the bonus for every token; a scan kernel then runs the recurrence serially
+// over tokens with value rows spread over workgroups (rows are independent
+// given the per-token vectors), and a post kernel applies GroupNorm + bonus
+// + gate.
+#include "launch.h"
+
+constexpr int LIN_MAX = 1024;
+
+struct HeadVecs {
+  float r[64], k[64], v[64], d[64], al[64], vg[64], g[64], a[64], bb[64], kt[64], y[64];
+  float bonus;
+};
+
+// Adapter outputs + keys for row `b` (a token or a batch row), head `h`.
+// Leaves r, d, a, bb, kt, v (after the value residual), g and bonus in LDS.
+RW_DEV void wkv_prologue(const WkvArgs& a, int b, int h, HeadVecs& hv, float* s_lin, float* red) {
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int C = a.C;
+  for (int i = t; i < a.Lin; i += 256) s_lin[i] = a.lin[(long)b * a.Lin + i];
+  if (t < 64) {
+    const long base = (long)b * 3 * C + h * 64 + t;
+    hv.r[t] = a.rkv[base];
+    hv.k[t] = a.rkv[base + C];
+    hv.v[t] = a.rkv[base + 2 * C];
+  }
+  __syncthreads();
+  {
+    const int c = h * 64 + lane;
+    const half_t* W = wave == 0 ? a.w2 : (wave == 1 ? a.a2 : (wave == 2 ? a.v2 : a.g2));
+    const int ioff = wave == 0 ? 0 : (wave == 1 ? a.off_a : (wave == 2 ? a.off_v : a.off_g));
+    const int D = wave == 0 ? a.Dw : (wave == 1 ? a.Da : (wave == 2 ? a.Dv : a.Dg));
+    const float* in = s_lin + ioff;
+    float acc = 0.f;
+    if (wave != 2 || a.layer > 0) {
+      const half_t* wr = W + (long)c * D;
+      for (int j = 0; j < D; j += 8) {
+        const half8 w8 = *reinterpret_cast<const half8*>(wr + j);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf((float)w8[e], in[j + e], acc);
+      }
+    }
+    if (wave == 0) {
+      // decay = exp(-exp(-softplus(-z) - 0.5)) = exp(-e^{-1/2} sigmoid(z))
+      const float z = a.w0[c] + acc;
+      const float sg = 1.0f / (1.0f + expf(-z));
+      hv.d[lane] = expf(-0.60653065971263342f * sg);
+    } else if (wave == 1) {
+      hv.al[lane] = 1.0f / (1.0f + expf(-(a.a0[c] + acc)));
+    } else if (wave == 2) {
+      hv.vg[lane] = a.layer > 0 ? 1.0f / (1.0f + expf(-(a.v0[c] + acc))) : 0.0f;
+    } else {
+      hv.g[lane] = acc;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int c = h * 64 + lane;
+    const float k = hv.k[lane];
+    const float kap = k * a.k_k[c];
+    const float nrm = sqrtf(wave_sum(kap * kap));
+    const float kh = kap / fmaxf(nrm, 1e-12f);
+    const float al = hv.al[lane];
+    const float kt = k * (1.0f + (al - 1.0f) * a.k_a[c]);
+    hv.a[lane] = -kh;
+    hv.bb[lane] = kh * al;
+    hv.kt[lane] = kt;
+    float v = hv.v[lane];
+    if (a.layer == 0) {
+      a.vfirst[(long)b * C + c] = v;
+    } else {
+      const float vf = a.vfirst[(long)b * C + c];
+      v = v + (vf - v) * hv.vg[lane];
+    }
+    hv.v[lane] = v;
+    const float bon = wave_sum(hv.r[lane] * kt * a.r_k[h * 64 + lane]);
+    if (lane == 0) hv.bonus = bon;
+  }
+  __syncthreads();
+  (void)red;
+}
+
+// GroupNorm over the head's 64 readouts + bonus * v, times the gate (wave 0).
+RW_DEV float wkv_epilogue(const WkvArgs& a, int h, const HeadVecs& hv, float y) {
+  const int lane = threadIdx.x & 63;
+  const int c = h * 64 + lane;
+  const float mean = wave_sum(y) * (1.0f / 64.0f);
+  const float dlt = y - mean;
+  const float var = wave_sum(dlt * dlt) * (1.0f / 64.0f);
+  float o = dlt / sqrtf(var + 64e-5f) * a.lnx_w[c] + a.lnx_b[c];
+  o += hv.bonus * hv.v[lane];
+  return o * hv.g[lane];
+}
+
+__global__ __launch_bounds__(256) void k_wkv_decode(WkvArgs a) {
+  __shared__ HeadVecs hv;
+  __shared__ float s_lin[LIN_MAX];
+  __shared__ float red[8];
+  const int b = blockIdx.x / a.H;
+  const int h = blockIdx.x % a.H;
+  wkv_prologue(a, b, h, hv, s_lin, red);
+
+  const int t = threadIdx.x;
+  const int i = t >> 2;
+  const int j0 = (t & 3) * 16;
+  const int slot = a.slots[b];
+  float* S = slot >= 0 ? a.pool + (long)slot * a.slot_stride + a.layer_off + 2L * a.C +
+                             (long)h * 4096 + i * 64 + j0
+                       : nullptr;
+  float s[16];
+  if (S) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const floatx4 v4 = ldf4_nt(S + 4 * q);
+      s[4 * q] = v4[0]; s[4 * q + 1] = v4[1]; s[4 * q + 2] = v4[2]; s[4 * q + 3] = v4[3];
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) s[q] = 0.f;
+  }
+  float sa = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) sa = fmaf(s[j], hv.a[j0 + j], sa);
+  sa += __shfl_xor(sa, 1);
+  sa += __shfl_xor(sa, 2);
+  const float vi = hv.v[i];
+  float y = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float sn = s[j] * hv.d[j0 + j] + sa * hv.bb[j0 + j] + vi * hv.kt[j0 + j];
+    s[j] = sn;
+    y = fmaf(sn, hv.r[j0 + j], y);
+  }
+  y += __shfl_xor(y, 1);
+  y += __shfl_xor(y, 2);
+  if (S) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      stf4_nt(S + 4 * q, floatx4{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]});
+  }
+  if ((t & 3) == 0) hv.y[i] = y;
+  __syncthreads();
+  if (t < 64) {
+    const float o = wkv_epilogue(a, h, hv, hv.y[t]);
+    const long off = (long)b * a.C + h * 64 + t;
+    if (a.yout_f16)
+      ((half_t*)a.yout)[off] = (half_t)o;
+    else
+      ((float*)a.yout)[off] = o;
+  }
+}
+
+hipError_t launch_wkv_decode(const WkvArgs& a, hipStream_t st) {
+  if (a.Lin > LIN_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_wkv_decode, dim3(a.B * a.H), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- prefill
+__global__ __launch_bounds__(256) void k_wkv_prep(WkvArgs a) {
+  __shared__ HeadVecs hv;
+  __shared__ float s_lin[LIN_MAX];
+  __shared__ float red[8];
+  const int tk = blockIdx.x / a.H;
+  const int h = blockIdx.x % a.H;
+  wkv_prologue(a, tk, h, hv, s_lin, red);
+  const int t = threadIdx.x;
+  if (t < 64) {
+    const long off = (long)tk * a.C + h * 64 + t;
+    a.q_d[off] = hv.d[t];
+    a.q_a[off] = hv.a[t];
+    a.q_b[off] = hv.bb[t];
+    a.q_kt[off] = hv.kt[t];
+    a.q_v[off] = hv.v[t];
+    a.q_g[off] = hv.g[t];
+  }
+  if (t == 0) a.q_bonus[(long)tk * a.H + h] = hv.bonus;
+}
+
+// Grid: H * 4 workgroups; workgroup (h, qb) owns value rows [16 qb, 16 qb + 16)
+// of head h: 4 rows per wave, 16 lanes per row, 4 key columns per lane.
+__global__ __launch_bounds__(256) void k_wkv_scan(WkvArgs a) {
+  const int h = blockIdx.x >> 2;
+  const int qb = blockIdx.x & 3;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = qb * 16 + wave * 4 + (lane >> 4);
+  const int j = (lane & 15) * 4;
+  const int C = a.C;
+  float* S = a.pool + (long)a.seq_slot * a.slot_stride + a.layer_off + 2L * C + (long)h * 4096 +
+             i * 64 + j;
+  float4 s = *reinterpret_cast<const float4*>(S);
+  const long cj = h * 64 + j;
+  const long ci = h * 64 + i;
+  for (int tk = 0; tk < a.B; ++tk) {
+    const long o = (long)tk * C;
+    const float4 av = *reinterpret_cast<const float4*>(a.q_a + o + cj);
+    const float4 bv = *reinterpret_cast<const float4*>(a.q_b + o + cj);
+    const float4 dv = *reinterpret_cast<const float4*>(a.q_d + o + cj);
+    const float4 kv = *reinterpret_cast<const float4*>(a.q_kt + o + cj);
+    const float4 rv = *reinterpret_cast<const float4*>(a.rkv + (long)tk * 3 * C + cj);
+    const float vi = a.q_v[o + ci];
+    float sa = s.x * av.x + s.y * av.y + s.z * av.z + s.w * av.w;
+    sa += __shfl_xor(sa, 1);
+    sa += __shfl_xor(sa, 2);
+    sa += __shfl_xor(sa, 4);
+    sa += __shfl_xor(sa, 8);
+    s.x = s.x * dv.x + sa * bv.x + vi * kv.x;
+    s.y = s.y * dv.y + sa * bv.y + vi * kv.y;
+    s.z = s.z * dv.z + sa * bv.z + vi * kv.z;
+    s.w = s.w * dv.w + sa * bv.w + vi * kv.w;
+    float y = s.x * rv.x + s.y * rv.y + s.z * rv.z + s.w * rv.w;
+    y += __shfl_xor(y, 1);
+    y += __shfl_xor(y, 2);
+    y += __shfl_xor(y, 4);
+    y += __shfl_xor(y, 8);
+    if ((lane & 15) == 0) a.q_y[o + ci] = y;
+  }
+  *reinterpret_cast<float4*>(S) = s;
+}
+
+__global__ __launch_bounds__(64) void k_wkv_post(WkvArgs a) {
+  __shared__ HeadVecs hv;
+  const int tk = blockIdx.x / a.H;
+  const int h = blockIdx.x % a.H;
+  const int t = threadIdx.x;
+  const long off = (long)tk * a.C + h * 64 + t;
+  hv.v[t] = a.q_v[off];
+  hv.g[t] = a.q_g[off];
+  if (t == 0) hv.bonus = a.q_bonus[(long)tk * a.H + h];
+  __syncthreads();
+  const float o = wkv_epilogue(a, h, hv, a.q_y[off]);
+  if (a.yout_f16)
+    ((half_t*)a.yout)[off] = (half_t)o;
+  else
+    ((float*)a.yout)[off] = o;
+}
+
+hipError_t launch_wkv_prep(const WkvArgs& a, hipStream_t st) {
+  if (a.Lin > LIN_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_wkv_prep, dim3(a.B * a.H), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+hipError_t launch_wkv_scan(const WkvArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_wkv_scan, dim3(a.H * 4), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+hipError_t launch_wkv_post(const WkvArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_wkv_post, dim3(a.B * a.H), dim3(64), 0, st, a);
+  return hipGetLastError();
+}

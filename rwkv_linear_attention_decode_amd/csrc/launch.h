@@ -1,0 +1,158 @@
+// Host-side launchers of the librwkv7 kernels (one translation unit each).
+#pragma once
+
+#include "common.h"
+
+// ---------------------------------------------------------------- projections
+// Rows of one GEMV workgroup for batch B and reduction length K (segments
+// must start and end on multiples of it).
+int gemv_rows_per_wg(int B, int K);
+bool gemv_supported(int B, int K);
+hipError_t launch_gemv(const ProjArgs& a, int total_rows, hipStream_t st);
+hipError_t launch_gemm(ProjArgs a, int total_rows, hipStream_t st);
+const char* gemv_kernel_name(int B, int K);
+const char* gemm_kernel_name(int M);
+
+// ---------------------------------------------------------------- misc
+struct ValidateArgs {
+  const int* slot_idx;   // caller's slots [n] (decode) or nullptr (prefill)
+  const int* tokens;     // caller's tokens [n]
+  int n_rows;            // rows with a slot (decode) / 0 (prefill)
+  int n_tok;
+  int64_t n_slots;
+  int vocab;
+  int seq_slot;          // prefill: the (host-validated) slot
+  int* slots_out;        // [n_rows]
+  int* tok_out;          // [n_tok]
+  uint32_t* err;
+  int64_t* counters;     // pool counters; += 1 per valid row, or += n_tok for prefill
+};
+hipError_t launch_validate(const ValidateArgs& a, hipStream_t st);
+
+struct EmbedArgs {
+  const half_t* emb;
+  const float* g;
+  const float* b;
+  const int* tok;
+  float* x;
+  int R, C;
+};
+hipError_t launch_embed(const EmbedArgs& a, hipStream_t st);
+
+enum { LNMIX_DECODE = 0, LNMIX_SEQ = 1, LNMIX_PLAIN = 2 };
+struct LnMixArgs {
+  float* x;                 // [R][C] residual (updated when partials are folded in)
+  const float* parts;       // [nparts][R][C] channel-mix partial sums, or nullptr
+  int nparts;
+  int C, R, mode;
+  const float* g;
+  const float* b;
+  float* pool;              // slot pool
+  int64_t slot_stride;      // floats per slot
+  int64_t shift_off;        // float offset of the shift vector inside a slot
+  const int* slots;         // decode: sanitized slot per row (-1 = skip)
+  int seq_slot;             // sequence mode: the slot
+  float* shift_tmp;         // sequence mode: receives the last row's LN output
+  const float* mu;          // [nq][C] token-shift mix coefficients
+  int nq;
+  void* out;                // [nq][R][C] (q stride out_q_stride elements)
+  int out_f16;
+  int64_t out_q_stride;
+};
+hipError_t launch_ln_mix(const LnMixArgs& a, hipStream_t st);
+
+hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t st);
+hipError_t launch_zero_f32(float* dst, int64_t n, hipStream_t st);
+
+struct ResetArgs {
+  float* pool;
+  int64_t slot_stride;
+  int64_t* counters;
+  const int* slot_idx;
+  int n;
+  int64_t n_slots;
+  uint32_t* err;
+};
+hipError_t launch_reset(const ResetArgs& a, hipStream_t st);
+
+// packing
+hipError_t launch_pack_matrix(half_t* dst, int64_t dst_ld, const void* src, int src_f16,
+                              int64_t rows, int64_t cols, hipStream_t st);
+hipError_t launch_pack_transpose(half_t* dst, const void* src, int src_f16, int64_t rows,
+                                 int64_t cols, hipStream_t st);
+hipError_t launch_pack_vec(float* dst, const void* src, int src_f16, int64_t n, hipStream_t st);
+hipError_t launch_fill_vec(float* dst, float v, int64_t n, hipStream_t st);
+
+// sparse channel-mix value
+struct CmixArgs {
+  const float* pre;           // [B][F] key pre-activations (bias included)
+  const unsigned char* mask;  // [F] union over rows of (pre > 0)
+  const half_t* Wv;           // [F][C] hidden-major value matrix
+  float* part;                // [NS][B][C]
+  int B, C, F, NS;
+  int* dbg_idx;               // optional: the union active list (ascending) of split 0
+  int* dbg_cnt;               // optional: its length
+};
+hipError_t launch_cmix_sparse(const CmixArgs& a, hipStream_t st);
+int cmix_sparse_max_b();
+const char* cmix_sparse_kernel_name(int B);
+
+// greedy
+struct GreedyArgs {
+  const float* logits;
+  float* occ;
+  int64_t n_slots;
+  const int* slot_idx;
+  const float* presence;
+  const float* frequency;
+  const float* decay;
+  int* ids;
+  float* part_val;
+  int* part_idx;
+  uint32_t* err;
+  int B, V, nblk;
+};
+int greedy_blocks(int V);
+hipError_t launch_greedy(const GreedyArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------- WKV
+struct WkvArgs {
+  float* pool;
+  int64_t slot_stride;
+  int64_t layer_off;       // float offset of this layer inside a slot
+  const int* slots;        // decode: per-row slot (-1 = skip)
+  int seq_slot;            // sequence kernels: the slot
+  int B, C, H, layer;
+  const float* rkv;        // [B][3C]: r | k | v
+  const float* lin;        // [B][Lin]: tanh(w1 x) | a1 x | v1 x | sigmoid(g1 x)
+  int Lin, off_a, off_v, off_g;
+  int Dw, Da, Dv, Dg;
+  const half_t* w2;        // [C][Dw]
+  const half_t* a2;        // [C][Da]
+  const half_t* v2;        // [C][Dv]
+  const half_t* g2;        // [C][Dg]
+  const float* w0;
+  const float* a0;
+  const float* v0;
+  const float* k_k;
+  const float* k_a;
+  const float* r_k;
+  const float* lnx_w;
+  const float* lnx_b;
+  float* vfirst;           // [B][C]
+  void* yout;              // [B][C] gated, normalised readout (fp32 or fp16)
+  int yout_f16;
+  // sequence path buffers ([T][C] fp32 each)
+  float* q_d;
+  float* q_a;
+  float* q_b;
+  float* q_kt;
+  float* q_v;
+  float* q_g;
+  float* q_bonus;          // [T][H]
+  float* q_y;              // raw readout
+};
+hipError_t launch_wkv_decode(const WkvArgs& a, hipStream_t st);
+hipError_t launch_wkv_prep(const WkvArgs& a, hipStream_t st);   // sequence: per (t, h)
+hipError_t launch_wkv_scan(const WkvArgs& a, hipStream_t st);   // sequence: serial in t
+hipError_t launch_wkv_post(const WkvArgs& a, hipStream_t st);   // sequence: GroupNorm + bonus + gate

@@ -1,0 +1,379 @@
+"""GPU parity of the HIP path against the fp64 oracle on the tiny shape
+(2 layers, C=256, 4 heads, F=1024, V=1024), through the C ABI.
+
+Tolerances: per-step logits relative L2 <= 1e-2, slot-state relative L2
+<= 1e-2; greedy ids, occurrence updates, slot bookkeeping and sparse
+active sets bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import rwkv7 as O
+
+pytestmark = pytest.mark.gpu
+
+S = synth.TINY
+TOL = 1e-2
+NSLOT = 16
+
+
+@pytest.fixture(scope="module")
+def weights():
+    return synth.make_weights(S)
+
+
+@pytest.fixture(scope="module")
+def W(weights):
+    return O.Weights(S, weights)
+
+
+@pytest.fixture(scope="module")
+def R():
+    import rwkv_linear_attention_decode_amd as R
+    return R
+
+
+@pytest.fixture(scope="module")
+def model(weights, R):
+    m = R.Model.from_numpy(S, weights, n_slots=NSLOT, max_B=8, max_T=64)
+    yield m
+    m.close()
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+
+
+def dev(x):
+    return torch.as_tensor(np.asarray(x, dtype=np.int32), device="cuda")
+
+
+def gstate(m, slot):
+    torch.cuda.synchronize()
+    return m.slot_state(slot).cpu().double().numpy()
+
+
+def fresh(m, slots):
+    m.reset(dev(slots))
+
+
+def prompt(seed, n):
+    return np.random.default_rng(seed).integers(0, S.vocab, size=n).astype(np.int32)
+
+
+def test_tiny_workload_teacher_forced(model, W):
+    """The tiny workload: 8-token prompt (7 prefilled, the 8th fed to the first
+    decode step), then 16 decode steps on a teacher-forced stream."""
+    wl = synth.WORKLOADS["tiny"]
+    p = synth.prompt_tokens(wl, 0, 8)
+    feeds = [int(p[7])] + [int(t) for t in synth.teacher_stream(wl, 0, 15)]
+    fresh(model, [0])
+    model.prefill(0, dev(p[:7]))
+    st = O.State(S)
+    O.seq(W, st, p[:7], want_logits=False)
+    assert rel(gstate(model, 0), st.flat()) <= TOL
+    logits = torch.empty(1, S.vocab, device="cuda")
+    worst = 0.0
+    for tok in feeds:
+        model.decode_step(dev([0]), dev([tok]), logits)
+        ref = O.step(W, [st], [tok])[0]
+        e = rel(logits[0].cpu().numpy(), ref)
+        worst = max(worst, e)
+        assert e <= TOL
+    assert rel(gstate(model, 0), st.flat()) <= TOL
+    assert int(model.counters()[0].item()) == 7 + 16
+    assert model.poll_error() == 0
+    print(f"tiny worst step logits rel L2 = {worst:.3e}")
+
+
+def test_tiny_free_running_greedy(model, W, R):
+    wl = synth.WORKLOADS["tiny"]
+    p = synth.prompt_tokens(wl, 0, 8)
+    fresh(model, [1])
+    model.prefill(1, dev(p[:7]))
+    st = O.State(S)
+    O.seq(W, st, p[:7], want_logits=False)
+    occ = torch.zeros(NSLOT, S.vocab, device="cuda")
+    zeros = torch.zeros(1, device="cuda")
+    ones = torch.ones(1, device="cuda")
+    ids = torch.zeros(1, dtype=torch.int32, device="cuda")
+    logits = torch.empty(1, S.vocab, device="cuda")
+    tok = int(p[7])
+    for step in range(16):
+        model.decode_step(dev([1]), dev([tok]), logits)
+        model.greedy(logits, occ, dev([1]), zeros, zeros, ones, ids)
+        ref = O.step(W, [st], [tok])[0]
+        g = int(ids.item())
+        r = int(np.argmax(ref))
+        if g != r:
+            srt = np.sort(ref)
+            err = float(np.abs(logits[0].cpu().double().numpy() - ref).max())
+            assert srt[-1] - srt[-2] < err, f"step {step}: ids differ with margin above the error"
+            break
+        tok = g
+
+
+@pytest.mark.parametrize("B,gemv,sparse", [
+    (1, 2, 4), (1, 0, 4), (1, 2, 0), (2, 2, 4), (2, 0, 0), (3, 2, 4), (4, 4, 4), (4, 0, 4),
+    (5, 2, 4), (8, 2, 4)])
+def test_batched_step_paths(model, W, R, B, gemv, sparse):
+    """B independent rows through the GEMV / MFMA and sparse / dense paths."""
+    model.set_option(R.OPT_GEMV_MAX_B, gemv)
+    model.set_option(R.OPT_SPARSE_MAX_B, sparse)
+    try:
+        slots = [(5 * i + 3) % NSLOT for i in range(B)]
+        fresh(model, slots)
+        states = []
+        for i, s in enumerate(slots):
+            pr = prompt(100 + i, 3 + i)
+            model.prefill(s, dev(pr))
+            st = O.State(S)
+            O.seq(W, st, pr, want_logits=False)
+            states.append(st)
+        logits = torch.empty(B, S.vocab, device="cuda")
+        for step in range(3):
+            toks = [int(t) for t in prompt(200 + step, B)]
+            model.decode_step(dev(slots), dev(toks), logits)
+            ref = O.step(W, states, toks)
+            got = logits.cpu().numpy()
+            for b in range(B):
+                assert rel(got[b], ref[b]) <= TOL, (step, b)
+        for b, s in enumerate(slots):
+            assert rel(gstate(model, s), states[b].flat()) <= TOL
+        assert model.poll_error() == 0
+    finally:
+        model.set_option(R.OPT_GEMV_MAX_B, 2)
+        model.set_option(R.OPT_SPARSE_MAX_B, 4)
+
+
+def test_prefill_equals_steps_on_gpu(model, R):
+    toks = prompt(7, 37)
+    fresh(model, [2, 3, 4])
+    model.prefill(2, dev(toks))
+    logits = torch.empty(1, S.vocab, device="cuda")
+    for t in toks:
+        model.decode_step(dev([3]), dev([int(t)]), logits)
+    model.set_option(R.OPT_PREFILL_CHUNK, 16)   # 3 chunks: 16 + 16 + 5
+    try:
+        model.prefill(4, dev(toks))
+    finally:
+        model.set_option(R.OPT_PREFILL_CHUNK, 512)
+    a, b, c = gstate(model, 2), gstate(model, 3), gstate(model, 4)
+    assert rel(a, b) <= TOL
+    assert rel(c, a) <= 1e-5
+    cnt = model.counters().cpu().numpy()
+    assert cnt[2] == cnt[3] == cnt[4] == 37
+
+
+def test_prefill_matches_oracle(model, W):
+    toks = prompt(8, 50)
+    fresh(model, [5])
+    model.prefill(5, dev(toks))
+    st = O.State(S)
+    O.seq(W, st, toks, want_logits=False)
+    assert rel(gstate(model, 5), st.flat()) <= TOL
+
+
+def test_zero_length_prefill_is_noop(model):
+    fresh(model, [6])
+    before = model.slot_state(6).clone()
+    model.prefill(6, torch.zeros(0, dtype=torch.int32, device="cuda"))
+    assert torch.equal(before, model.slot_state(6))
+
+
+def test_pure_decay_closed_form_on_gpu(weights, R):
+    """Zero decay adapters, w0 = 0, zero key/value weights: every decay is
+    exp(-e^-1/2 / 2) = 0.7384031 and k = v = 0, so S_T = 0.7384031^T S_0."""
+    w = dict(weights)
+    for l in range(S.n_layer):
+        p = f"blocks.{l}."
+        for n in ("att.w0", "att.w1", "att.w2", "att.key.weight", "att.value.weight"):
+            w[p + n] = np.zeros_like(w[p + n])
+    m = R.Model.from_numpy(S, w, n_slots=2, max_B=1, max_T=8)
+    try:
+        view = m.slot_state(0)
+        g = torch.Generator(device="cpu").manual_seed(3)
+        C = S.n_embd
+        init = torch.randn(view.shape, generator=g)
+        init[:, :2 * C] = 0.0
+        view.copy_(init.cuda())
+        S0 = view[:, 2 * C:].double().cpu().numpy()
+        T = 5
+        logits = torch.empty(1, S.vocab, device="cuda")
+        for t in range(T):
+            m.decode_step(dev([0]), dev([t + 11]), logits)
+        ST = gstate(m, 0)[:, 2 * C:]
+        assert rel(ST, S0 * 0.7384031 ** T) <= 1e-5
+    finally:
+        m.close()
+
+
+def test_unlisted_slots_bit_identical_and_counters(model):
+    g = torch.Generator(device="cpu").manual_seed(5)
+    n = model.counter_offset // 4
+    fpool = model.pool[: model.counter_offset].view(torch.float32)
+    fpool.copy_(torch.randn(n, generator=g).cuda() * 0.1)
+    cnt = model.counters()
+    cnt.copy_(torch.arange(NSLOT, dtype=torch.int64, device="cuda") * 10)
+    before = model.pool.clone()
+    logits = torch.empty(2, S.vocab, device="cuda")
+    model.decode_step(dev([5, 2]), dev([7, 9]), logits)
+    torch.cuda.synchronize()
+    after = model.pool
+    sf = model.slot_floats * 4
+    for s in range(NSLOT):
+        same = torch.equal(before[s * sf:(s + 1) * sf], after[s * sf:(s + 1) * sf])
+        assert same == (s not in (2, 5)), s
+    c = model.counters().cpu().numpy()
+    exp = np.arange(NSLOT) * 10
+    exp[2] += 1
+    exp[5] += 1
+    np.testing.assert_array_equal(c, exp)
+
+
+def test_device_error_flags(model, R):
+    logits = torch.empty(2, S.vocab, device="cuda")
+    model.poll_error()
+    model.decode_step(dev([1]), dev([S.vocab + 5]), logits[:1])
+    assert model.poll_error() == R.ERR_TOKEN_RANGE
+    model.decode_step(dev([1, 1]), dev([3, 4]), logits)
+    assert model.poll_error() == R.ERR_SLOT_DUP
+    model.decode_step(dev([1, NSLOT + 3]), dev([3, 4]), logits)
+    assert model.poll_error() == R.ERR_SLOT_RANGE
+    assert model.poll_error() == 0
+
+
+def test_host_errors_with_model(model, R):
+    logits = torch.empty(1, S.vocab, device="cuda")
+    with pytest.raises(R.RWKV7Error):
+        R.rwkv7_decode_step(model.handle, model.pool, NSLOT, dev([]), dev([]), logits, model.ws)
+    with pytest.raises(R.RWKV7Error):   # workspace too small for B = 9 > max_B
+        R.rwkv7_decode_step(model.handle, model.pool, NSLOT, dev(list(range(9))), dev([1] * 9),
+                            torch.empty(9, S.vocab, device="cuda"), model.ws[:4096])
+    with pytest.raises(R.RWKV7Error):
+        R.rwkv7_prefill_seq(model.handle, model.pool, NSLOT, NSLOT, dev([1, 2]), model.ws)
+
+
+def test_graph_matches_eager_bitwise(model, R):
+    fresh(model, [7])
+    model.prefill(7, dev(prompt(9, 5)))
+    torch.cuda.synchronize()
+    snap = model.slot_state(7).clone()
+    toks = [int(t) for t in prompt(10, 4)]
+    outs = []
+    for graph in (1, 0, 1):
+        model.slot_state(7).copy_(snap)
+        model.set_option(R.OPT_USE_GRAPH, graph)
+        seq = []
+        logits = torch.empty(1, S.vocab, device="cuda")
+        for t in toks:
+            model.decode_step(dev([7]), dev([t]), logits)
+            seq.append(logits.clone())
+        outs.append((torch.stack(seq), model.slot_state(7).clone()))
+    model.set_option(R.OPT_USE_GRAPH, 1)
+    for o in outs[1:]:
+        assert torch.equal(o[0], outs[0][0])
+        assert torch.equal(o[1], outs[0][1])
+
+
+def test_greedy_bit_exact_vs_float32_replica(model):
+    rng = np.random.default_rng(11)
+    B, V = 6, S.vocab
+    slots = [3, 0, 9, 4, 12, 1]
+    L = (rng.integers(-4, 5, size=(B, V)) * 0.25).astype(np.float32)
+    L[2] = np.nan
+    L[4, rng.integers(0, V, 50)] = np.nan
+    L[5] = rng.standard_normal(V).astype(np.float32)
+    occ = np.zeros((NSLOT, V), np.float32)
+    occ[:, rng.integers(0, V, 300)] = rng.random((NSLOT, 300)).astype(np.float32) * 3
+    pres = np.array([1.0, 0.0, 0.5, 1.0, 0.25, 1.0], np.float32)
+    freq = np.array([1.0, 0.5, 0.0, 1.0, 2.0, 1.0], np.float32)
+    dec = np.array([0.996, 1.0, 0.9, 0.996, 0.5, 0.996], np.float32)
+    occ_d = torch.from_numpy(occ).cuda()
+    ids = torch.zeros(B, dtype=torch.int32, device="cuda")
+    model.poll_error()
+    model.greedy(torch.from_numpy(L).cuda(), occ_d, dev(slots), torch.from_numpy(pres).cuda(),
+                 torch.from_numpy(freq).cuda(), torch.from_numpy(dec).cuda(), ids)
+    flags = model.poll_error()
+    rid, rocc, rerr = O.greedy_penalized(L, occ[slots], pres, freq, dec)
+    np.testing.assert_array_equal(ids.cpu().numpy(), rid)
+    got = occ_d.cpu().numpy()
+    for b, s in enumerate(slots):
+        assert np.array_equal(got[s].view(np.uint32), rocc[b].view(np.uint32)), b
+    untouched = [s for s in range(NSLOT) if s not in slots]
+    np.testing.assert_array_equal(got[untouched], occ[untouched])
+    assert rerr[2] and flags == 8
+
+
+def test_sparse_active_set_exact(model, W, R):
+    """The skipped value rows are exactly those with pre-activation <= 0
+    (against the GPU's own pre-activations), and match the oracle's set
+    wherever the oracle's pre-activation is not within 1e-3 rms of zero."""
+    B = 2
+    slots = [10, 11]
+    fresh(model, slots)
+    states = [O.State(S), O.State(S)]
+    for i, s in enumerate(slots):
+        pr = prompt(300 + i, 6)
+        model.prefill(s, dev(pr))
+        O.seq(W, states[i], pr, want_logits=False)
+    toks = [5, 77]
+    logits = torch.empty(B, S.vocab, device="cuda")
+    model.decode_step(dev(slots), dev(toks), logits)
+    torch.cuda.synchronize()
+    p_pre, p_mask, p_act, p_cnt = R.rwkv7_debug_cmix_buffers(model.handle, model.ws, B)
+    base = model.ws.data_ptr()
+    F = S.ffn
+
+    def view(addr, n, dt):
+        off = addr - base
+        return model.ws[off: off + n * torch.tensor([], dtype=dt).element_size()].view(dt)
+
+    pre = view(p_pre, B * F, torch.float32).cpu().numpy().reshape(B, F)
+    mask = view(p_mask, F, torch.uint8).cpu().numpy()
+    cnt = int(view(p_cnt, 1, torch.int32).item())
+    act = view(p_act, F, torch.int32).cpu().numpy()[:cnt]
+    exp_mask = (pre > 0).any(axis=0)
+    np.testing.assert_array_equal(mask.astype(bool), exp_mask)
+    np.testing.assert_array_equal(act, np.nonzero(exp_mask)[0])
+    # against the oracle's last-layer pre-activations
+    zs = []
+    orig = O.cmix_key
+
+    def spy(W_, l, u, prev):
+        z = orig(W_, l, u, prev)
+        zs.append(z + W_.L(l, "ffn.key.bias"))
+        return z
+    O.cmix_key = spy
+    try:
+        O.step(W, states, toks)
+    finally:
+        O.cmix_key = orig
+    zref = zs[-1]
+    assert rel(pre, zref) <= TOL
+    rms = np.sqrt(np.mean(zref ** 2))
+    clear = np.abs(zref) >= 1e-3 * rms
+    assert np.array_equal((pre > 0)[clear], (zref > 0)[clear])
+    assert 0.6 < 1 - (pre > 0).mean() < 0.97   # ~85 % zeros
+
+
+def test_kernel_timing_counts(model, R):
+    model.set_option(R.OPT_KERNEL_TIMING, 1)
+    try:
+        R.rwkv7_kernel_timing(model.handle, 0, reset=True)
+        logits = torch.empty(1, S.vocab, device="cuda")
+        model.decode_step(dev([0]), dev([1]), logits)
+        counts = {R.K_NAMES[k]: R.rwkv7_kernel_timing(model.handle, k)[1] for k in range(8)}
+        Lr = S.n_layer
+        assert counts["ln_mix"] == 2 * Lr + 1
+        assert counts["proj_in"] == counts["wkv"] == counts["proj_out"] == Lr
+        assert counts["cmix_key"] == counts["cmix_value"] == Lr
+        assert counts["head"] == 1
+        ms = R.rwkv7_kernel_timing(model.handle, R.K_HEAD)[0]
+        assert ms > 0
+    finally:
+        model.set_option(R.OPT_KERNEL_TIMING, 0)
