@@ -1,0 +1,364 @@
+#!/usr/bin/env python3
+"""Throughput of the RWKV-7 decode / prefill hot path on one MI355X.
+
+Headline (the JSON line's `value`): decode tokens/s of the 2.9B-shape model
+(32 layers, C 2560, 40 heads x 64, F 10240, V 65536, fp16 weights, fp32
+state) at B = 1: a 64-token uniform-id prompt is prefilled (63 tokens, the
+last one is the first decode input), then every timed step is one decode
+step (rwkv7_decode_step) plus greedy selection (rwkv7_greedy) whose ids feed
+the next step on the device.  Inputs are resident in HBM before timing.
+
+Also in the same line:
+  roofline     the dominant kernel's achieved HBM GB/s (algorithmic bytes per
+               launch / average launch time from HIP events) against 8 TB/s
+  step         algorithmic bytes per decode step / step time
+  kernels      per-class time breakdown of one decode step (HIP events)
+  batched      B = 64 / 256 decode (prompts of 20-2000 tokens, penalties
+               1.0 / 1.0, decay 0.996) with per-projection MFMA TFLOP/s
+  prefill      tokens/s of rwkv7_prefill_seq at T = 128 / 512 / 2048
+  cpu_baseline the fp64 NumPy oracle timed on a bounded sample on the host
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
+
+METRIC = "decode tokens/sec at B=1/64/256 (2.9B-shape fp16) + % of HBM/MFMA roofline"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- algorithmic bytes
+def class_bytes(s, B: int, nnz: int, sparse: bool):
+    """Compulsory HBM bytes per launch of each kernel class for B decode rows:
+    every weight read once, activations / state read and written once."""
+    C, F, V, H = s.n_embd, s.ffn, s.vocab, s.n_head
+    Din = s.d_w + s.d_a + s.d_v + s.d_g
+    n_in = 3 * C + Din
+    ns = max(1, min(32, -(-512 // (C // 64))))
+    b = {}
+    b["ln_mix"] = B * C * 4 * 4 + B * C * 4 * 3.5            # x, shift r/w, mixed outs (avg of 6 and 1)
+    b["proj_in"] = n_in * C * 2 + B * 6 * C * 4 + B * n_in * 4
+    b["wkv"] = B * H * 64 * 64 * 4 * 2 + C * Din * 2 + B * (3 * C + Din + 2 * C) * 4
+    b["proj_out"] = C * C * 2 + B * C * 4 * 3
+    b["cmix_key"] = F * C * 2 + B * C * 4 + B * F * 4
+    if sparse:
+        b["cmix_value"] = nnz * C * 2 + B * F * 4 + ns * B * C * 4
+    else:
+        b["cmix_value"] = F * C * 2 + B * F * 2 + B * C * 4 * 2
+    b["head"] = V * C * 2 + B * C * 4 + B * V * 4
+    b["other"] = B * C * 2 + B * C * 4
+    return b
+
+
+def class_flops(s, B: int):
+    C, F, V = s.n_embd, s.ffn, s.vocab
+    Din = s.d_w + s.d_a + s.d_v + s.d_g
+    return {"proj_in": 2 * B * (3 * C + Din) * C, "proj_out": 2 * B * C * C,
+            "cmix_key": 2 * B * F * C, "cmix_value": 2 * B * F * C, "head": 2 * B * V * C}
+
+
+def step_bytes(s, B, nnz, sparse):
+    cb = class_bytes(s, B, nnz, sparse)
+    L = s.n_layer
+    per_layer = 2 * cb["ln_mix"] + cb["proj_in"] + cb["wkv"] + cb["proj_out"] + cb["cmix_key"] + cb["cmix_value"]
+    greedy = B * s.vocab * 4 * 3   # logits read, occurrences read + written
+    return L * per_layer + cb["ln_mix"] + cb["head"] + cb["other"] + greedy
+
+
+# ---------------------------------------------------------------- helpers
+def build_model(R, shape, n_slots, max_B, max_T):
+    import synth
+    t0 = time.time()
+    w = synth.make_weights(shape)
+    log(f"[bench] generated {shape.name} weights in {time.time() - t0:.1f}s")
+    t0 = time.time()
+    m = R.Model.from_numpy(shape, w, n_slots=n_slots, max_B=max_B, max_T=max_T)
+    log(f"[bench] packed on device in {time.time() - t0:.1f}s")
+    return m, w
+
+
+def i32(x):
+    import torch
+    return torch.as_tensor(np.asarray(x, dtype=np.int32), device="cuda")
+
+
+def measure_active_fraction(R, m, B):
+    import torch
+    p_pre, p_mask, p_act, p_cnt = R.rwkv7_debug_cmix_buffers(m.handle, m.ws, B)
+    off = p_cnt - m.ws.data_ptr()
+    torch.cuda.synchronize()
+    return int(m.ws[off:off + 4].view(torch.int32).item())
+
+
+def kernel_breakdown(R, m, B, run_step, steps=4):
+    import torch
+    m.set_option(R.OPT_KERNEL_TIMING, 1)
+    try:
+        R.rwkv7_kernel_timing(m.handle, 0, reset=True)
+        for _ in range(steps):
+            run_step()
+        torch.cuda.synchronize()
+        out = {}
+        for k, name in enumerate(R.K_NAMES):
+            ms, n = R.rwkv7_kernel_timing(m.handle, k)
+            out[name] = {"ms_per_step": ms / steps, "launches_per_step": n / steps}
+        R.rwkv7_kernel_timing(m.handle, 0, reset=True)
+    finally:
+        m.set_option(R.OPT_KERNEL_TIMING, 0)
+    return out
+
+
+# ---------------------------------------------------------------- decode B=1 (headline)
+def decode_b1(R, args, shape, m):
+    import torch
+    import synth
+    wl = synth.WORKLOADS["decode_b1_2.9b"]
+    p = synth.prompt_tokens(wl, 0, 64)
+    slot = i32([0])
+    m.reset(slot)
+    m.prefill(0, i32(p[:63]))
+    tok = i32([p[63]])                       # also the greedy output buffer
+    logits = torch.empty(1, shape.vocab, device="cuda")
+    occ = torch.zeros(m.n_slots, shape.vocab, device="cuda")
+    zero = torch.zeros(1, device="cuda")
+    one = torch.ones(1, device="cuda")
+
+    def run_step():
+        m.decode_step(slot, tok, logits)
+        m.greedy(logits, occ, slot, zero, zero, one, tok)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    flags = m.poll_error()
+    if flags:
+        raise RuntimeError(f"device error flags {flags} during the timed decode")
+    nnz = measure_active_fraction(R, m, 1)
+    log(f"[bench] B=1: {args.steps} steps in {dt * 1e3:.1f} ms -> {args.steps / dt:.1f} tok/s; "
+        f"last-layer active rows {nnz}/{shape.ffn}")
+    kb = kernel_breakdown(R, m, 1, run_step)
+    return dt, nnz, kb, run_step, slot, tok, logits
+
+
+def roofline_b1(R, shape, m, kb, nnz, slot, tok, logits):
+    """Dominant kernel class of the B=1 step, timed in isolation with HIP events."""
+    cb = class_bytes(shape, 1, nnz, True)
+    dom = max((k for k in kb if k in cb and k != "other"), key=lambda k: kb[k]["ms_per_step"])
+    cls = R.K_NAMES.index(dom)
+    layer = shape.n_layer if dom == "head" else 0
+    avg_ms = R.rwkv7_time_kernel(m.handle, m.pool, m.n_slots, slot, tok, logits, cls, layer, 200, m.ws)
+    gbs = cb[dom] / (avg_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": R.rwkv7_kernel_name(m.handle, cls, 1), "class": dom,
+            "bytes_per_launch": int(cb[dom]), "avg_launch_us": round(avg_ms * 1e3, 3),
+            "launches_per_step": kb[dom]["launches_per_step"]}
+
+
+# ---------------------------------------------------------------- batched decode
+def batched(R, args, shape, m, B):
+    import torch
+    import synth
+    wl = synth.WORKLOADS[f"decode_b{B}_2.9b"] if f"decode_b{B}_2.9b" in synth.WORKLOADS else None
+    lens = synth.prompt_lengths(wl, B)
+    slots_l = list(range(B))
+    slots = i32(slots_l)
+    m.reset(slots)
+    t0 = time.time()
+    for b in range(B):
+        pr = synth.prompt_tokens(wl, b, int(lens[b]))
+        m.prefill(b, i32(pr[:-1]))
+    torch.cuda.synchronize()
+    t_pf = time.time() - t0
+    first = i32([synth.prompt_tokens(wl, b, int(lens[b]))[-1] for b in range(B)])
+    tok = first.clone()
+    logits = torch.empty(B, shape.vocab, device="cuda")
+    occ = torch.zeros(m.n_slots, shape.vocab, device="cuda")
+    pres = torch.full((B,), wl.presence, device="cuda")
+    freq = torch.full((B,), wl.frequency, device="cuda")
+    dec = torch.full((B,), wl.decay, device="cuda")
+
+    def run_step():
+        m.decode_step(slots, tok, logits)
+        m.greedy(logits, occ, slots, pres, freq, dec, tok)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.batched_steps):
+        run_step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    flags = m.poll_error()
+    if flags:
+        raise RuntimeError(f"device error flags {flags} during batched decode B={B}")
+    kb = kernel_breakdown(R, m, B, run_step, steps=2)
+    sparse = B <= R.rwkv7_get_option(m.handle, R.OPT_SPARSE_MAX_B)
+    sb = step_bytes(shape, B, shape.ffn, sparse)
+    ms = dt / args.batched_steps * 1e3
+    res = {"B": B, "tok_s": round(B * args.batched_steps / dt, 1), "ms_per_step": round(ms, 4),
+           "steps": args.batched_steps, "prefill_s": round(t_pf, 2),
+           "prompt_tokens": int(lens.sum()),
+           "step_gbs": round(sb / (ms * 1e-3) / 1e9, 1),
+           "step_hbm_frac": round(sb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in kb.items()}}
+    # MFMA rate of each projection, timed in isolation
+    fl = class_flops(shape, B)
+    proj = {}
+    for name in ("proj_in", "proj_out", "cmix_key", "cmix_value", "head"):
+        cls = R.K_NAMES.index(name)
+        layer = shape.n_layer if name == "head" else 0
+        avg = R.rwkv7_time_kernel(m.handle, m.pool, m.n_slots, slots, tok, logits, cls, layer, 20, m.ws)
+        tf = fl[name] / (avg * 1e-3) / 1e12
+        proj[name] = {"us": round(avg * 1e3, 2), "tflops": round(tf, 1),
+                      "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+    res["projections"] = proj
+    log(f"[bench] B={B}: {res['tok_s']} tok/s, {ms:.3f} ms/step, step {res['step_gbs']} GB/s")
+    return res
+
+
+# ---------------------------------------------------------------- prefill
+def prefill(R, shape, m, Ts):
+    import torch
+    import synth
+    wl = synth.WORKLOADS["prefill_2.9b"]
+    out = {}
+    for T in Ts:
+        toks = i32(synth.prefill_tokens(wl, T))
+        slot = i32([0])
+        m.reset(slot)
+        m.prefill(0, toks)      # warm-up
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(3):
+            m.reset(slot)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            m.prefill(0, toks)
+            torch.cuda.synchronize()
+            times.append(time.perf_counter() - t0)
+        dt = float(np.median(times))
+        out[str(T)] = {"tok_s": round(T / dt, 1), "ms": round(dt * 1e3, 3)}
+        log(f"[bench] prefill T={T}: {T / dt:.0f} tok/s")
+    return out
+
+
+# ---------------------------------------------------------------- CPU oracle
+def cpu_baseline(shape, weights, seconds):
+    from oracle import rwkv7 as O
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [(i.get("internal_api"), i.get("num_threads")) for i in threadpool_info()]
+    except Exception:
+        blas = []
+    cores = len(os.sched_getaffinity(0))
+    threads = max([n for _, n in blas if n] or [1])
+    W = O.Weights(shape, weights, cache=False)
+    st = O.State(shape)
+    wl = synth.WORKLOADS["decode_b1_2.9b"]
+    toks = synth.teacher_stream(wl, 0, 64)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        O.step(W, [st], [int(toks[n % 64])])
+        n += 1
+        if time.perf_counter() - t0 >= seconds or n >= 64:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 4), "unit": "tokens/s", "cores": int(min(threads, cores)),
+            "kind": "oracle",
+            "sample": f"{n} fp64 decode steps of the 2.9B-shape model, B=1, from a zero state "
+                      f"(NumPy, BLAS {blas}, {cores} host cores visible)"}
+
+
+# ---------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--batched", default="64,256", help="extra batched-decode B values ('' = none)")
+    ap.add_argument("--batched-steps", type=int, default=128)
+    ap.add_argument("--prefill", default="128,512,2048", help="prefill T values ('' = none)")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "Decode shards by state slots with no communication; see DESIGN.md.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rwkv_linear_attention_decode_amd as R
+    import synth
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible: the HIP library needs an MI355X")
+    shape = synth.R7_2B9
+    Bs = [int(b) for b in args.batched.split(",") if b]
+    Ts = [int(t) for t in args.prefill.split(",") if t]
+    n_slots = max([1] + Bs)
+    m, weights = build_model(R, shape, n_slots=n_slots, max_B=max([1] + Bs),
+                             max_T=max([512] + [min(t, 512) for t in Ts]))
+
+    dt, nnz, kb, run_step, slot, tok, logits = decode_b1(R, args, shape, m)
+    ms = dt / args.steps * 1e3
+    sb = step_bytes(shape, 1, nnz, True)
+    roof = roofline_b1(R, shape, m, kb, nnz, slot, tok, logits)
+    log(f"[bench] dominant kernel {roof['class']}: {roof['avg_launch_us']} us/launch, "
+        f"{roof['achieved']} GB/s ({roof['frac'] * 100:.1f}% of HBM peak)")
+
+    batched_res = [batched(R, args, shape, m, B) for B in Bs]
+    prefill_res = prefill(R, shape, m, Ts) if Ts else {}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle ...")
+        cpu = cpu_baseline(shape, weights, args.cpu_seconds)
+        log(f"[bench] oracle: {cpu['value']} tok/s")
+    m.close()
+
+    line = {
+        "metric": METRIC, "value": round(args.steps / dt, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "rwkv7 2.9B-shape decode, B=1, 64-token uniform-id prompt, greedy",
+                   "batch": 1, "prompt_tokens": 64, "weights": "fp16 random-init", "state": "fp32",
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "step": {"bytes": int(sb), "gbs": round(sb / (ms * 1e-3) / 1e9, 1),
+                 "hbm_frac": round(sb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "active_ffn_rows_last_layer": nnz},
+        "kernels": {k: {"ms_per_step": round(v["ms_per_step"], 4),
+                        "launches_per_step": v["launches_per_step"]} for k, v in kb.items()},
+        "batched": batched_res,
+        "prefill": prefill_res,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

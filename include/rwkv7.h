@@ -220,6 +220,19 @@ int rwkv7_get_option(const rwkv7_model* model, int32_t key, int64_t* value);
 int rwkv7_kernel_timing(rwkv7_model* model, int32_t kernel_class, double* total_ms,
                         int64_t* launches, int32_t reset);
 
+/* Measure one kernel class in isolation: enqueue, `iters` times back to
+ * back, the launch(es) that class makes at `layer` (0..n_layer-1; n_layer =
+ * the head) of a decode step of B rows with these arguments, between two
+ * HIP events on `stream`; synchronise and return the average per iteration
+ * in *avg_ms.  Run it after a normal decode step with the same arguments so
+ * the workspace holds that step's activations.  It rewrites the listed
+ * slots' state and the workspace (the repeated launches are real), so reset
+ * those slots before using them again. */
+int rwkv7_time_kernel(rwkv7_model* model, void* pool, int64_t n_slots, int32_t B,
+                      const int32_t* slot_idx, const int32_t* token_ids, float* logits_out,
+                      int32_t kernel_class, int32_t layer, int32_t iters, void* ws,
+                      uint64_t ws_bytes, void* stream, double* avg_ms);
+
 /* Name of the kernel symbol a class launches on the decode path for batch B
  * (for matching rocprofv3 output), or "" for an unknown class. */
 const char* rwkv7_kernel_name(const rwkv7_model* model, int32_t kernel_class, int32_t B);

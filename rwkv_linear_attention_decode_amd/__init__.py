@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         "rwkv7_get_option": [vp, i32, P(i64)],
         "rwkv7_kernel_timing": [vp, i32, P(ctypes.c_double), P(i64), i32],
         "rwkv7_debug_cmix_buffers": [vp, vp, i32, P(vp), P(vp), P(vp), P(vp)],
+        "rwkv7_time_kernel": [vp, vp, i64, i32, vp, vp, vp, i32, i32, i32, vp, u64, vp,
+                              P(ctypes.c_double)],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -231,6 +233,17 @@ def rwkv7_kernel_timing(model: int, cls: int, reset: bool = False) -> Tuple[floa
 
 def rwkv7_kernel_name(model: int, cls: int, B: int) -> str:
     return lib().rwkv7_kernel_name(model, cls, B).decode()
+
+
+def rwkv7_time_kernel(model: int, pool, n_slots: int, slot_idx, token_ids, logits_out,
+                      kernel_class: int, layer: int, iters: int, ws, stream=None) -> float:
+    """Average ms of one kernel class's launch at ``layer``, replayed ``iters`` times."""
+    v = ctypes.c_double()
+    _check(lib().rwkv7_time_kernel(model, pool.data_ptr(), n_slots, slot_idx.numel(),
+                                   _ptr(slot_idx), _ptr(token_ids), _ptr(logits_out), kernel_class,
+                                   layer, iters, ws.data_ptr(), ws.numel(), _stream(stream),
+                                   ctypes.byref(v)), "rwkv7_time_kernel")
+    return v.value
 
 
 def rwkv7_debug_cmix_buffers(model: int, ws, B: int) -> Tuple[int, int, int, int]:

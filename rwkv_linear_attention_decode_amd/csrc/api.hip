@@ -232,12 +232,30 @@ struct rwkv7_model {
 namespace {
 
 // Runs one launch, bracketed by events when timing is on.
+// Restricts a launch sequence to one kernel class at one layer, repeated
+// (used to time a kernel in isolation).  layer == n_layer selects the head.
+struct Filter {
+  int cls = -1;
+  int layer = -1;
+  int repeat = 1;
+};
+
 struct Launcher {
   rwkv7_model* m;
   hipStream_t st;
   bool timing;
+  const Filter* flt = nullptr;
+  int layer = -1;
   template <class F>
   int run(int cls, const char* what, F&& f) {
+    if (flt && flt->cls >= 0) {
+      if (cls != flt->cls || layer != flt->layer) return RWKV7_OK;
+      for (int i = 0; i < flt->repeat; ++i) {
+        hipError_t e = f();
+        if (e != hipSuccess) return hip_fail(e, what);
+      }
+      return RWKV7_OK;
+    }
     hipEvent_t ea = nullptr, eb = nullptr;
     if (timing) {
       if (!m->free_events.empty()) {
@@ -303,13 +321,14 @@ void proj_in_args(const Dims& d, const LayerPtrs& q, const Ws& w, int R, bool f1
   a.nseg = 7;
 }
 
-WkvArgs wkv_args(const rwkv7_model* m, int l, float* pool, const Ws& w, int R, bool f16) {
+WkvArgs wkv_args(const rwkv7_model* m, int l, float* pool, int64_t n_slots, const Ws& w, int R, bool f16) {
   const Dims& d = m->d;
   const LayerPtrs& q = m->pk.layers[l];
   WkvArgs a;
   memset(&a, 0, sizeof a);
   a.pool = pool;
   a.slot_stride = d.slot_floats;
+  a.n_slots = n_slots;
   a.layer_off = (int64_t)l * d.layer_floats;
   a.slots = w.slots;
   a.seq_slot = -1;
@@ -340,9 +359,10 @@ Path decode_path(const rwkv7_model* m, int B) {
 }
 
 int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const int* slot_idx,
-                   const int* tok, float* logits, char* ws, hipStream_t st, bool timing) {
+                   const int* tok, float* logits, char* ws, hipStream_t st, bool timing,
+                   const Filter* flt = nullptr) {
   const Dims& d = m->d;
-  Launcher L{m, st, timing};
+  Launcher L{m, st, timing, flt};
   const Ws w = ws_layout(d, B, ws);
   const Path path = decode_path(m, B);
   const bool f16 = !path.gemv;
@@ -355,6 +375,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
   RUN(RWKV7_K_OTHER, "embed", launch_embed(ea, st));
 
   for (int l = 0; l < d.L; ++l) {
+    L.layer = l;
     const LayerPtrs& q = m->pk.layers[l];
     LnMixArgs la;
     memset(&la, 0, sizeof la);
@@ -363,7 +384,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
     la.nparts = la.parts ? m->ns : 0;
     la.C = C; la.R = B; la.mode = LNMIX_DECODE;
     la.g = q.ln1_w; la.b = q.ln1_b;
-    la.pool = pool; la.slot_stride = d.slot_floats; la.shift_off = (int64_t)l * d.layer_floats;
+    la.pool = pool; la.slot_stride = d.slot_floats; la.n_slots = n_slots; la.shift_off = (int64_t)l * d.layer_floats;
     la.slots = w.slots; la.seq_slot = -1;
     la.mu = q.mu6; la.nq = 6;
     la.out = w.xq; la.out_f16 = f16; la.out_q_stride = (int64_t)B * C;
@@ -373,7 +394,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
     proj_in_args(d, q, w, B, f16, pa);
     RUN(RWKV7_K_PROJ_IN, "proj_in", proj(path.gemv, pa, d.Nin, st));
 
-    const WkvArgs wa = wkv_args(m, l, pool, w, B, f16);
+    const WkvArgs wa = wkv_args(m, l, pool, n_slots, w, B, f16);
     RUN(RWKV7_K_WKV, "wkv", launch_wkv_decode(wa, st));
 
     ProjArgs po;
@@ -412,6 +433,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
     }
   }
 
+  L.layer = d.L;
   LnMixArgs lo;
   memset(&lo, 0, sizeof lo);
   lo.x = w.x;
@@ -452,7 +474,7 @@ int enqueue_prefill_chunk(rwkv7_model* m, float* pool, int64_t n_slots, int slot
     memset(&la, 0, sizeof la);
     la.x = w.x; la.C = C; la.R = T; la.mode = LNMIX_SEQ;
     la.g = q.ln1_w; la.b = q.ln1_b;
-    la.pool = pool; la.slot_stride = d.slot_floats; la.shift_off = lo;
+    la.pool = pool; la.slot_stride = d.slot_floats; la.n_slots = n_slots; la.shift_off = lo;
     la.seq_slot = slot; la.shift_tmp = w.shift_tmp;
     la.mu = q.mu6; la.nq = 6;
     la.out = w.xq; la.out_f16 = 1; la.out_q_stride = (int64_t)T * C;
@@ -463,7 +485,7 @@ int enqueue_prefill_chunk(rwkv7_model* m, float* pool, int64_t n_slots, int slot
     proj_in_args(d, q, w, T, true, pa);
     RUN(RWKV7_K_PROJ_IN, "proj_in", launch_gemm(pa, d.Nin, st));
 
-    WkvArgs wa = wkv_args(m, l, pool, w, T, true);
+    WkvArgs wa = wkv_args(m, l, pool, n_slots, w, T, true);
     wa.seq_slot = slot;
     RUN(RWKV7_K_WKV, "wkv_prep", launch_wkv_prep(wa, st));
     RUN(RWKV7_K_WKV, "wkv_scan", launch_wkv_scan(wa, st));
@@ -867,8 +889,13 @@ int rwkv7_greedy(int32_t B, int32_t V, const float* logits, float* occ_pool, int
   a.nblk = greedy_blocks(V);
   char* base = (char*)ws;
   a.err = (uint32_t*)base;
-  a.part_val = (float*)(base + ALIGN);
-  a.part_idx = (int*)(base + ALIGN + align_up((uint64_t)B * a.nblk * 4));
+  // Partial results go at the tail of the workspace, away from the decode
+  // step's buffers at its head (the tail of a decode workspace holds the
+  // prefill-only scan buffers).
+  const uint64_t part = align_up((uint64_t)B * a.nblk * 4);
+  const uint64_t tail = (ws_bytes - 2 * part) / ALIGN * ALIGN;
+  a.part_val = (float*)(base + tail);
+  a.part_idx = (int*)(base + tail + part);
   a.B = B; a.V = V;
   HIP_TRY(launch_greedy(a, (hipStream_t)stream), "greedy");
   return RWKV7_OK;
@@ -936,6 +963,50 @@ int rwkv7_kernel_timing(rwkv7_model* m, int32_t cls, double* total_ms, int64_t* 
   if (reset) {
     for (int i = 0; i < RWKV7_K_COUNT; ++i) { m->t_ms[i] = 0; m->t_n[i] = 0; }
   }
+  return RWKV7_OK;
+}
+
+int rwkv7_time_kernel(rwkv7_model* m, void* pool, int64_t n_slots, int32_t B,
+                      const int32_t* slot_idx, const int32_t* token_ids, float* logits_out,
+                      int32_t kernel_class, int32_t layer, int32_t iters, void* ws,
+                      uint64_t ws_bytes, void* stream, double* avg_ms) {
+  if (!m || !avg_ms) return fail(RWKV7_EINVAL, "null argument");
+  if (B < 1 || B > n_slots) return fail(RWKV7_EINVAL, "B out of range");
+  if (kernel_class < 0 || kernel_class >= RWKV7_K_COUNT) return fail(RWKV7_EINVAL, "bad kernel class");
+  if (layer < 0 || layer > m->d.L) return fail(RWKV7_EINVAL, "layer outside [0, n_layer]");
+  if (iters < 1) return fail(RWKV7_EINVAL, "iters must be >= 1");
+  int rc = check_pool_ws(m, pool, n_slots, ws, ws_bytes, ws_layout(m->d, B, nullptr).bytes);
+  if (rc) return rc;
+  if (!slot_idx || !token_ids || !logits_out) return fail(RWKV7_EINVAL, "null pointer argument");
+  hipStream_t st = (hipStream_t)stream;
+  // Rebuild the step's sanitized rows and embeddings first: other calls on
+  // this workspace (rwkv7_greedy, a prefill) may have reused its buffers.
+  {
+    Filter pre;
+    pre.cls = RWKV7_K_OTHER;
+    pre.layer = -1;
+    rc = enqueue_decode(m, (float*)pool, n_slots, B, slot_idx, token_ids, logits_out, (char*)ws, st,
+                        false, &pre);
+    if (rc) return rc;
+  }
+  Filter f;
+  f.cls = kernel_class;
+  f.layer = layer;
+  f.repeat = iters;
+  hipEvent_t a, b;
+  HIP_TRY(hipEventCreate(&a), "hipEventCreate");
+  HIP_TRY(hipEventCreate(&b), "hipEventCreate");
+  HIP_TRY(hipEventRecord(a, st), "hipEventRecord");
+  rc = enqueue_decode(m, (float*)pool, n_slots, B, slot_idx, token_ids, logits_out, (char*)ws, st,
+                      false, &f);
+  HIP_TRY(hipEventRecord(b, st), "hipEventRecord");
+  HIP_TRY(hipEventSynchronize(b), "hipEventSynchronize");
+  float ms = 0.f;
+  hipEventElapsedTime(&ms, a, b);
+  hipEventDestroy(a);
+  hipEventDestroy(b);
+  if (rc) return rc;
+  *avg_ms = (double)ms / iters;
   return RWKV7_OK;
 }
 

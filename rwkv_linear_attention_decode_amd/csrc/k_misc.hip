@@ -136,7 +136,8 @@ __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
   float prev[NE];
   if (a.mode == LNMIX_DECODE) {
     const int slot = a.slots[r];
-    float* sh = slot >= 0 ? a.pool + (long)slot * a.slot_stride + a.shift_off : nullptr;
+    float* sh = (slot >= 0 && slot < a.n_slots) ? a.pool + (long)slot * a.slot_stride + a.shift_off
+                                                : nullptr;
 #pragma unroll
     for (int i = 0; i < NE; ++i) prev[i] = sh ? sh[threadIdx.x + 256 * i] : 0.0f;
     if (sh) {

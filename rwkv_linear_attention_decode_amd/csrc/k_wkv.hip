@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void k_wkv_decode(WkvArgs a) {
   const int i = t >> 2;
   const int j0 = (t & 3) * 16;
   const int slot = a.slots[b];
-  float* S = slot >= 0 ? a.pool + (long)slot * a.slot_stride + a.layer_off + 2L * a.C +
+  float* S = (slot >= 0 && slot < a.n_slots) ? a.pool + (long)slot * a.slot_stride + a.layer_off + 2L * a.C +
                              (long)h * 4096 + i * 64 + j0
                        : nullptr;
   float s[16];

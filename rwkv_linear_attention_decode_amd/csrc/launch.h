@@ -49,6 +49,7 @@ struct LnMixArgs {
   const float* b;
   float* pool;              // slot pool
   int64_t slot_stride;      // floats per slot
+  int64_t n_slots;          // slots in the pool (rows with other slots are skipped)
   int64_t shift_off;        // float offset of the shift vector inside a slot
   const int* slots;         // decode: sanitized slot per row (-1 = skip)
   int seq_slot;             // sequence mode: the slot
@@ -119,6 +120,7 @@ hipError_t launch_greedy(const GreedyArgs& a, hipStream_t st);
 struct WkvArgs {
   float* pool;
   int64_t slot_stride;
+  int64_t n_slots;         // slots in the pool (rows with other slots are skipped)
   int64_t layer_off;       // float offset of this layer inside a slot
   const int* slots;        // decode: per-row slot (-1 = skip)
   int seq_slot;            // sequence kernels: the slot

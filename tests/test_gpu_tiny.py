@@ -361,6 +361,29 @@ def test_sparse_active_set_exact(model, W, R):
     assert 0.6 < 1 - (pre > 0).mean() < 0.97   # ~85 % zeros
 
 
+def test_time_kernel_after_greedy(model, R):
+    """rwkv7_greedy shares the decode workspace; rwkv7_time_kernel after it
+    must rebuild the rows it reads (regression: greedy partials once
+    overwrote the sanitized slot list at the head of the workspace)."""
+    slots = dev([4, 9])
+    toks = dev([3, 8])
+    fresh(model, [4, 9])
+    logits = torch.empty(2, S.vocab, device="cuda")
+    occ = torch.zeros(NSLOT, S.vocab, device="cuda")
+    z = torch.zeros(2, device="cuda")
+    one = torch.ones(2, device="cuda")
+    ids = torch.zeros(2, dtype=torch.int32, device="cuda")
+    model.decode_step(slots, toks, logits)
+    model.greedy(logits, occ, slots, z, z, one, ids)
+    for cls in range(8):
+        for layer in (0, S.n_layer):
+            ms = R.rwkv7_time_kernel(model.handle, model.pool, NSLOT, slots, toks, logits, cls,
+                                     layer, 3, model.ws)
+            assert ms >= 0.0
+    assert model.poll_error() == 0
+    fresh(model, [4, 9])
+
+
 def test_kernel_timing_counts(model, R):
     model.set_option(R.OPT_KERNEL_TIMING, 1)
     try:
