@@ -199,6 +199,7 @@ const char* rwkv7_last_error(void);
 #define RWKV7_OPT_SPARSE_MAX_B 3   /* largest B served by the sparse channel-mix value path */
 #define RWKV7_OPT_KERNEL_TIMING 4  /* 1: bracket every launch with HIP events (no graph) */
 #define RWKV7_OPT_PREFILL_CHUNK 5  /* tokens per prefill chunk (<= the workspace's max_T) */
+#define RWKV7_OPT_FUSE_LN 6        /* 1 (default): LayerNorm + token shift inside the GEMV path */
 
 int rwkv7_set_option(rwkv7_model* model, int32_t key, int64_t value);
 int rwkv7_get_option(const rwkv7_model* model, int32_t key, int64_t* value);

@@ -63,6 +63,8 @@ int check_config(const rwkv7_config* c, Dims* d) {
   for (int i = 0; i < 4; ++i)
     if (ds[i] < 8 || ds[i] % 8)
       return fail(RWKV7_ENOTSUP, "adapter ranks must be positive multiples of 8");
+  if ((c->d_w + c->d_a + c->d_v + c->d_g) % 32)
+    return fail(RWKV7_ENOTSUP, "the adapter ranks must sum to a multiple of 32");
   Dims r;
   r.L = c->n_layer; r.C = c->n_embd; r.H = c->n_head; r.N = 64; r.F = c->ffn;
   r.Dw = c->d_w; r.Da = c->d_a; r.Dv = c->d_v; r.Dg = c->d_g; r.V = c->vocab;
@@ -135,18 +137,12 @@ Packed pack_layout(const Dims& d, char* base) {
 struct Ws {
   uint32_t* err;
   int *slots, *tok;
-  float *x, *xq, *rkv, *lin, *vfirst, *yg, *xk, *pre, *part, *xo, *shift_tmp;
+  float *x, *xq, *rkv, *lin, *lo, *vfirst, *yg, *xk, *pre, *xo, *shift_tmp, *u_att, *u_ffn;
   unsigned char* mask;
   int *dbg_idx, *dbg_cnt;
   float *q_d, *q_a, *q_b, *q_kt, *q_v, *q_g, *q_bonus, *q_y;
   uint64_t bytes;
 };
-
-int sparse_splits(const Dims& d) {
-  const int slices = d.C / 64;
-  int ns = (512 + slices - 1) / slices;
-  return ns < 1 ? 1 : (ns > 32 ? 32 : ns);
-}
 
 Ws ws_layout(const Dims& d, int R, char* base) {
   uint64_t off = 0;
@@ -156,8 +152,6 @@ Ws ws_layout(const Dims& d, int R, char* base) {
     return p;
   };
   const uint64_t C = d.C, F = d.F, r = R;
-  const int NS = sparse_splits(d);
-  const uint64_t rs = R < cmix_sparse_max_b() ? R : cmix_sparse_max_b();
   Ws w;
   w.err = (uint32_t*)take(4);
   w.slots = (int*)take(r * 4);
@@ -166,16 +160,18 @@ Ws ws_layout(const Dims& d, int R, char* base) {
   w.xq = (float*)take(6 * r * C * 4);
   w.rkv = (float*)take(3 * r * C * 4);
   w.lin = (float*)take(r * d.Lin * 4);
+  w.lo = (float*)take(r * 4 * C * 4);
   w.vfirst = (float*)take(r * C * 4);
   w.yg = (float*)take(r * C * 4);
   w.xk = (float*)take(r * C * 4);
   w.pre = (float*)take(r * F * 4);
   w.mask = (unsigned char*)take(F);
-  w.part = (float*)take(NS * rs * C * 4);
   w.xo = (float*)take(r * C * 4);
   w.shift_tmp = (float*)take(C * 4);
   w.dbg_idx = (int*)take(F * 4);
   w.dbg_cnt = (int*)take(4);
+  w.u_att = (float*)take(r * C * 4);
+  w.u_ffn = (float*)take(r * C * 4);
   w.q_d = (float*)take(r * C * 4);
   w.q_a = (float*)take(r * C * 4);
   w.q_b = (float*)take(r * C * 4);
@@ -217,8 +213,8 @@ struct rwkv7_model {
   rwkv7_config cfg;
   Dims d;
   Packed pk;
-  int ns;
-  int64_t opt_graph = 1, opt_gemv_max = 2, opt_sparse_max = 4, opt_timing = 0, opt_chunk = 512;
+  int64_t opt_graph = 1, opt_gemv_max = 2, opt_sparse_max = 4, opt_timing = 0, opt_chunk = 512,
+          opt_fuse_ln = 1;
   std::vector<TimedLaunch> pending;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> free_events;
   double t_ms[RWKV7_K_COUNT] = {0};
@@ -321,6 +317,29 @@ void proj_in_args(const Dims& d, const LayerPtrs& q, const Ws& w, int R, bool f1
   a.nseg = 7;
 }
 
+// Adapter outputs for all R rows as one MFMA projection: four blocks of C
+// columns, each with its own matrix and rank, writing decay | alpha |
+// value gate | gate into lo [R][4C].
+void lora_args(const Dims& d, const LayerPtrs& q, const Ws& w, int R, ProjArgs& a) {
+  memset(&a, 0, sizeof a);
+  a.W = q.w2;
+  a.K = d.Dw;
+  a.M = R;
+  a.nseg = 4;
+  const int C = d.C;
+  const half_t* W[4] = {q.w2, q.a2, q.v2, q.g2};
+  const int K[4] = {d.Dw, d.Da, d.Dv, d.Dg};
+  const int off[4] = {0, d.Dwp, d.Dwp + d.Dap, d.Dwp + d.Dap + d.Dvp};
+  const int epi[4] = {EPI_DECAY, EPI_SIGB, EPI_SIGB, EPI_NONE};
+  const float* bias[4] = {q.w0, q.a0, q.v0, nullptr};
+  for (int s = 0; s < 4; ++s) {
+    a.seg[s] = mkseg(s * C, (s + 1) * C, epi[s], w.lin, d.Lin, w.lo + (int64_t)s * C, 4 * C, bias[s]);
+    a.seg[s].W = W[s];
+    a.seg[s].K = K[s];
+    a.seg[s].act_off = off[s];
+  }
+}
+
 WkvArgs wkv_args(const rwkv7_model* m, int l, float* pool, int64_t n_slots, const Ws& w, int R, bool f16) {
   const Dims& d = m->d;
   const LayerPtrs& q = m->pk.layers[l];
@@ -348,15 +367,21 @@ WkvArgs wkv_args(const rwkv7_model* m, int l, float* pool, int64_t n_slots, cons
 }
 
 struct Path {
-  bool gemv, sparse;
+  bool gemv, sparse, fused;
 };
 
 Path decode_path(const rwkv7_model* m, int B) {
   Path p;
   p.gemv = B <= m->opt_gemv_max && gemv_supported(B, m->d.C);
-  p.sparse = B <= m->opt_sparse_max && B <= cmix_sparse_max_b() && m->d.F <= 16384 && m->d.C % 64 == 0;
+  p.sparse = B <= m->opt_sparse_max && B <= cmix_sparse_max_b() && m->d.F <= 16384 &&
+             m->d.F % 1024 == 0 && m->d.C % 64 == 0;
+  p.fused = p.gemv && m->opt_fuse_ln && gemv_fused_ok(B, m->d.C);
   return p;
 }
+
+// mixing vector (index into the six time-mix coefficient rows r,w,k,v,a,g)
+// read by each block of the fused input projection
+constexpr int kInMix[7] = {0, 2, 3, 1, 4, 3, 5};
 
 int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const int* slot_idx,
                    const int* tok, float* logits, char* ws, hipStream_t st, bool timing,
@@ -365,36 +390,53 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
   Launcher L{m, st, timing, flt};
   const Ws w = ws_layout(d, B, ws);
   const Path path = decode_path(m, B);
-  const bool f16 = !path.gemv;
+  // activations stay fp32 on both paths (the MFMA kernel splits them itself)
+  const bool f16 = false;
   const int C = d.C;
   int64_t* counters = (int64_t*)((char*)pool + align_up((uint64_t)n_slots * d.slot_floats * 4));
 
-  ValidateArgs va{slot_idx, tok, B, B, n_slots, d.V, -1, w.slots, w.tok, w.err, counters};
+  ValidateArgs va{slot_idx, tok, B, B, n_slots, d.V, -1, w.slots, w.tok, w.err, counters,
+                  nullptr, 0};
   RUN(RWKV7_K_OTHER, "validate", launch_validate(va, st));
   EmbedArgs ea{m->pk.emb, m->pk.ln0_w, m->pk.ln0_b, w.tok, w.x, B, C};
   RUN(RWKV7_K_OTHER, "embed", launch_embed(ea, st));
 
+  // Fused path (small B): LayerNorm + token-shift mix run inside the GEMV
+  // prologues; the new shifts are committed by the following kernel (WKV
+  // for the time mix, the channel-mix value for the channel mix).
+  // Otherwise a LayerNorm kernel writes the mixed rows and the shift.
   for (int l = 0; l < d.L; ++l) {
     L.layer = l;
     const LayerPtrs& q = m->pk.layers[l];
+    const int64_t lo = (int64_t)l * d.layer_floats;
     LnMixArgs la;
     memset(&la, 0, sizeof la);
-    la.x = w.x;
-    la.parts = (l > 0 && path.sparse) ? w.part : nullptr;
-    la.nparts = la.parts ? m->ns : 0;
-    la.C = C; la.R = B; la.mode = LNMIX_DECODE;
+    la.x = w.x; la.C = C; la.R = B; la.mode = LNMIX_DECODE;
     la.g = q.ln1_w; la.b = q.ln1_b;
-    la.pool = pool; la.slot_stride = d.slot_floats; la.n_slots = n_slots; la.shift_off = (int64_t)l * d.layer_floats;
+    la.pool = pool; la.slot_stride = d.slot_floats; la.n_slots = n_slots; la.shift_off = lo;
     la.slots = w.slots; la.seq_slot = -1;
     la.mu = q.mu6; la.nq = 6;
     la.out = w.xq; la.out_f16 = f16; la.out_q_stride = (int64_t)B * C;
-    RUN(RWKV7_K_LN_MIX, "ln_mix(tmix)", launch_ln_mix(la, st));
 
     ProjArgs pa;
     proj_in_args(d, q, w, B, f16, pa);
+    if (path.fused) {
+      pa.ln = LnPro{w.x, q.ln1_w, q.ln1_b, pool, d.slot_floats, n_slots, lo, w.slots, w.u_att, LNP_MIX, 0};
+      for (int s = 0; s < 7; ++s) pa.seg[s].mix = q.mu6 + (int64_t)kInMix[s] * C;
+    } else {
+      RUN(RWKV7_K_LN_MIX, "ln_mix(tmix)", launch_ln_mix(la, st));
+    }
     RUN(RWKV7_K_PROJ_IN, "proj_in", proj(path.gemv, pa, d.Nin, st));
 
-    const WkvArgs wa = wkv_args(m, l, pool, n_slots, w, B, f16);
+    WkvArgs wa = wkv_args(m, l, pool, n_slots, w, B, f16);
+    wa.u_att = path.fused ? w.u_att : nullptr;
+    if (!path.gemv) {
+      // many rows: the adapter outputs as one MFMA projection, WKV reads them
+      ProjArgs pl;
+      lora_args(d, q, w, B, pl);
+      RUN(RWKV7_K_PROJ_IN, "adapters", launch_gemm(pl, 4 * C, st));
+      wa.lo = w.lo;
+    }
     RUN(RWKV7_K_WKV, "wkv", launch_wkv_decode(wa, st));
 
     ProjArgs po;
@@ -403,25 +445,33 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
     po.seg[0] = mkseg(0, C, EPI_RESID, w.yg, C, w.x, C);
     RUN(RWKV7_K_PROJ_OUT, "proj_out", proj(path.gemv, po, C, st));
 
-    LnMixArgs lc = la;
-    lc.parts = nullptr; lc.nparts = 0;
-    lc.g = q.ln2_w; lc.b = q.ln2_b;
-    lc.shift_off = (int64_t)l * d.layer_floats + C;
-    lc.mu = q.mu_k; lc.nq = 1;
-    lc.out = w.xk; lc.out_q_stride = 0;
-    RUN(RWKV7_K_LN_MIX, "ln_mix(cmix)", launch_ln_mix(lc, st));
-
     ProjArgs pk;
     memset(&pk, 0, sizeof pk);
     pk.W = q.w_key; pk.K = C; pk.M = B; pk.nseg = 1;
     if (path.sparse)
       pk.seg[0] = mkseg(0, d.F, EPI_PRE, w.xk, C, w.pre, d.F, q.b_key, w.mask);
     else
-      pk.seg[0] = mkseg(0, d.F, EPI_RELU2_H, w.xk, C, w.pre, d.F, q.b_key);
+      pk.seg[0] = mkseg(0, d.F, EPI_RELU2, w.xk, C, w.pre, d.F, q.b_key);
+    if (path.fused) {
+      pk.ln = LnPro{w.x, q.ln2_w, q.ln2_b, pool, d.slot_floats, n_slots, lo + C, w.slots, w.u_ffn, LNP_MIX, 0};
+      pk.seg[0].mix = q.mu_k;
+    } else {
+      LnMixArgs lc = la;
+      lc.g = q.ln2_w; lc.b = q.ln2_b;
+      lc.shift_off = lo + C;
+      lc.mu = q.mu_k; lc.nq = 1;
+      lc.out = w.xk; lc.out_q_stride = 0;
+      RUN(RWKV7_K_LN_MIX, "ln_mix(cmix)", launch_ln_mix(lc, st));
+    }
     RUN(RWKV7_K_CMIX_KEY, "cmix_key", proj(path.gemv, pk, d.F, st));
 
     if (path.sparse) {
-      CmixArgs ca{w.pre, w.mask, q.w_val_hm, w.part, B, C, d.F, m->ns, nullptr, nullptr};
+      CmixArgs ca;
+      memset(&ca, 0, sizeof ca);
+      ca.pre = w.pre; ca.mask = w.mask; ca.Wv = q.w_val_hm;
+      ca.x = w.x; ca.u_ffn = path.fused ? w.u_ffn : nullptr;
+      ca.pool = pool; ca.slot_stride = d.slot_floats; ca.n_slots = n_slots; ca.shift_off = lo + C;
+      ca.slots = w.slots; ca.B = B; ca.C = C; ca.F = d.F;
       if (l == d.L - 1) { ca.dbg_idx = w.dbg_idx; ca.dbg_cnt = w.dbg_cnt; }
       RUN(RWKV7_K_CMIX_VALUE, "cmix_value", launch_cmix_sparse(ca, st));
     } else {
@@ -430,25 +480,29 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
       pv.W = q.w_val_km; pv.K = d.F; pv.M = B; pv.nseg = 1;
       pv.seg[0] = mkseg(0, C, EPI_RESID, w.pre, d.F, w.x, C);
       RUN(RWKV7_K_CMIX_VALUE, "cmix_value", launch_gemm(pv, C, st));
+      if (path.fused) {
+        CommitArgs ca{w.u_ffn, pool, d.slot_floats, n_slots, lo + C, w.slots, B, C};
+        RUN(RWKV7_K_OTHER, "commit shift", launch_commit_shift(ca, st));
+      }
     }
   }
 
   L.layer = d.L;
-  LnMixArgs lo;
-  memset(&lo, 0, sizeof lo);
-  lo.x = w.x;
-  lo.parts = path.sparse ? w.part : nullptr;
-  lo.nparts = path.sparse ? m->ns : 0;
-  lo.C = C; lo.R = B; lo.mode = LNMIX_PLAIN;
-  lo.g = m->pk.lnout_w; lo.b = m->pk.lnout_b;
-  lo.nq = 1; lo.mu = nullptr;
-  lo.out = w.xo; lo.out_f16 = f16; lo.out_q_stride = 0;
-  RUN(RWKV7_K_LN_MIX, "ln_out", launch_ln_mix(lo, st));
-
   ProjArgs ph;
   memset(&ph, 0, sizeof ph);
   ph.W = m->pk.head; ph.K = C; ph.M = B; ph.nseg = 1;
   ph.seg[0] = mkseg(0, d.V, EPI_NONE, w.xo, C, logits, d.V);
+  if (path.fused) {
+    ph.ln = LnPro{w.x, m->pk.lnout_w, m->pk.lnout_b, nullptr, 0, 0, 0, nullptr, nullptr, LNP_PLAIN, 0};
+  } else {
+    LnMixArgs lo;
+    memset(&lo, 0, sizeof lo);
+    lo.x = w.x; lo.C = C; lo.R = B; lo.mode = LNMIX_PLAIN;
+    lo.g = m->pk.lnout_w; lo.b = m->pk.lnout_b;
+    lo.nq = 1; lo.mu = nullptr;
+    lo.out = w.xo; lo.out_f16 = f16; lo.out_q_stride = 0;
+    RUN(RWKV7_K_LN_MIX, "ln_out", launch_ln_mix(lo, st));
+  }
   RUN(RWKV7_K_HEAD, "head", proj(path.gemv, ph, d.V, st));
   return RWKV7_OK;
 }
@@ -462,7 +516,8 @@ int enqueue_prefill_chunk(rwkv7_model* m, float* pool, int64_t n_slots, int slot
   int64_t* counters = (int64_t*)((char*)pool + align_up((uint64_t)n_slots * d.slot_floats * 4));
   float* slot_base = pool + (int64_t)slot * d.slot_floats;
 
-  ValidateArgs va{nullptr, tok, 0, T, n_slots, d.V, slot, w.slots, w.tok, w.err, counters};
+  ValidateArgs va{nullptr, tok, 0, T, n_slots, d.V, slot, w.slots, w.tok, w.err, counters,
+                  nullptr, 0};
   RUN(RWKV7_K_OTHER, "validate", launch_validate(va, st));
   EmbedArgs ea{m->pk.emb, m->pk.ln0_w, m->pk.ln0_b, w.tok, w.x, T, C};
   RUN(RWKV7_K_OTHER, "embed", launch_embed(ea, st));
@@ -477,16 +532,20 @@ int enqueue_prefill_chunk(rwkv7_model* m, float* pool, int64_t n_slots, int slot
     la.pool = pool; la.slot_stride = d.slot_floats; la.n_slots = n_slots; la.shift_off = lo;
     la.seq_slot = slot; la.shift_tmp = w.shift_tmp;
     la.mu = q.mu6; la.nq = 6;
-    la.out = w.xq; la.out_f16 = 1; la.out_q_stride = (int64_t)T * C;
+    la.out = w.xq; la.out_f16 = 0; la.out_q_stride = (int64_t)T * C;
     RUN(RWKV7_K_LN_MIX, "ln_mix(tmix)", launch_ln_mix(la, st));
     RUN(RWKV7_K_OTHER, "shift copy", launch_copy_f32(slot_base + lo, w.shift_tmp, C, st));
 
     ProjArgs pa;
-    proj_in_args(d, q, w, T, true, pa);
+    proj_in_args(d, q, w, T, false, pa);
     RUN(RWKV7_K_PROJ_IN, "proj_in", launch_gemm(pa, d.Nin, st));
 
-    WkvArgs wa = wkv_args(m, l, pool, n_slots, w, T, true);
+    ProjArgs pl;
+    lora_args(d, q, w, T, pl);
+    RUN(RWKV7_K_PROJ_IN, "adapters", launch_gemm(pl, 4 * C, st));
+    WkvArgs wa = wkv_args(m, l, pool, n_slots, w, T, false);
     wa.seq_slot = slot;
+    wa.lo = w.lo;
     RUN(RWKV7_K_WKV, "wkv_prep", launch_wkv_prep(wa, st));
     RUN(RWKV7_K_WKV, "wkv_scan", launch_wkv_scan(wa, st));
     RUN(RWKV7_K_WKV, "wkv_post", launch_wkv_post(wa, st));
@@ -508,7 +567,7 @@ int enqueue_prefill_chunk(rwkv7_model* m, float* pool, int64_t n_slots, int slot
     ProjArgs pk;
     memset(&pk, 0, sizeof pk);
     pk.W = q.w_key; pk.K = C; pk.M = T; pk.nseg = 1;
-    pk.seg[0] = mkseg(0, d.F, EPI_RELU2_H, w.xk, C, w.pre, d.F, q.b_key);
+    pk.seg[0] = mkseg(0, d.F, EPI_RELU2, w.xk, C, w.pre, d.F, q.b_key);
     RUN(RWKV7_K_CMIX_KEY, "cmix_key", launch_gemm(pk, d.F, st));
 
     ProjArgs pv;
@@ -739,7 +798,6 @@ int rwkv7_load(const rwkv7_config* cfg, const rwkv7_tensor* tensors, int32_t n_t
   m->cfg = *cfg;
   m->d = d;
   m->pk = pk;
-  m->ns = sparse_splits(d);
   hipGetDevice(&m->device);
   *out = m;
   return RWKV7_OK;
@@ -927,8 +985,12 @@ int rwkv7_set_option(rwkv7_model* m, int32_t key, int64_t value) {
     case RWKV7_OPT_PREFILL_CHUNK:
       if (value < 1) return fail(RWKV7_EINVAL, "PREFILL_CHUNK must be >= 1");
       m->opt_chunk = value; break;
+    case RWKV7_OPT_FUSE_LN: m->opt_fuse_ln = value ? 1 : 0; break;
     default: return fail(RWKV7_EINVAL, "unknown option %d", key);
   }
+  // cached graphs bake in the kernel path: drop them when it may change
+  if (key == RWKV7_OPT_GEMV_MAX_B || key == RWKV7_OPT_SPARSE_MAX_B || key == RWKV7_OPT_FUSE_LN)
+    drop_graphs(m);
   return RWKV7_OK;
 }
 
@@ -940,6 +1002,7 @@ int rwkv7_get_option(const rwkv7_model* m, int32_t key, int64_t* value) {
     case RWKV7_OPT_SPARSE_MAX_B: *value = m->opt_sparse_max; break;
     case RWKV7_OPT_KERNEL_TIMING: *value = m->opt_timing; break;
     case RWKV7_OPT_PREFILL_CHUNK: *value = m->opt_chunk; break;
+    case RWKV7_OPT_FUSE_LN: *value = m->opt_fuse_ln; break;
     default: return fail(RWKV7_EINVAL, "unknown option %d", key);
   }
   return RWKV7_OK;

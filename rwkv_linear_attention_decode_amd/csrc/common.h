@@ -37,8 +37,9 @@ enum : int {
   EPI_SIGMOID = 2,   // out_f32 = sigmoid(acc)
   EPI_RESID = 3,     // out_f32 += acc (residual stream)
   EPI_PRE = 4,       // out_f32 = acc + aux[n]; mask[n] = any row > 0
-  EPI_RELU2_H = 5,   // out_f16 = relu(acc + aux[n])^2
-  EPI_STORE_H = 6,   // out_f16 = acc
+  EPI_RELU2 = 5,     // out_f32 = relu(acc + aux[n])^2
+  EPI_DECAY = 6,     // out_f32 = exp(-e^{-1/2} sigmoid(acc + aux[n]))  (WKV decay)
+  EPI_SIGB = 7,      // out_f32 = sigmoid(acc + aux[n])
 };
 
 // One output block of a fused projection: rows [row0, row1) of the packed
@@ -54,9 +55,33 @@ struct Seg {
   void* out;
   const float* aux;
   unsigned char* mask;
+  const float* mix;  // fused-LayerNorm prologue: token-shift mix of this block
+  const half_t* W;   // MFMA path: this block's own matrix [rows][K] (nullptr: the shared one)
+  int K;             // ... and its reduction length (a multiple of 32)
+  int act_off;       // ... and the column of its activation block inside `act`
 };
 
 #define MAX_SEGS 8
+
+enum : int { LNP_NONE = 0, LNP_MIX = 1, LNP_PLAIN = 2 };
+
+// Fused LayerNorm (+ token-shift mix) prologue of the GEMV path: the
+// activation of segment s for row b is u + (prev - u) * s.mix with
+// u = LN(x[b]) and prev the row's stored shift (LNP_MIX), or u (LNP_PLAIN).
+// Workgroup 0 writes u to u_out; a later kernel commits it as the new shift.
+struct LnPro {
+  const float* x;        // [M][C] residual rows
+  const float* g;
+  const float* b;
+  const float* pool;
+  int64_t slot_stride;
+  int64_t n_slots;
+  int64_t shift_off;
+  const int* slots;
+  float* u_out;          // [M][C] or nullptr
+  int mode;
+  int pad_;
+};
 
 struct ProjArgs {
   const half_t* W;   // [rows][K] fp16, K contiguous
@@ -66,6 +91,7 @@ struct ProjArgs {
   int n_tiles;       // MFMA path: number of 64-column tiles
   int m_tiles;       // MFMA path: number of M tiles
   int pad_;
+  LnPro ln;
   Seg seg[MAX_SEGS];
 };
 
@@ -129,14 +155,20 @@ RW_DEV void epi_store(const Seg& s, int n, int m, float v) {
     case EPI_PRE:
       ((float*)s.out)[(long)m * s.ld_out + n] = v + s.aux[n];
       break;
-    case EPI_RELU2_H: {
+    case EPI_RELU2: {
       float z = v + s.aux[n];
       z = z > 0.0f ? z * z : 0.0f;
-      ((half_t*)s.out)[(long)m * s.ld_out + n] = (half_t)z;
+      ((float*)s.out)[(long)m * s.ld_out + n] = z;
       break;
     }
-    case EPI_STORE_H:
-      ((half_t*)s.out)[(long)m * s.ld_out + n] = (half_t)v;
+    case EPI_DECAY: {
+      // exp(-exp(-softplus(-z) - 0.5)) = exp(-e^{-1/2} sigmoid(z))
+      const float sg = 1.0f / (1.0f + expf(-(v + s.aux[n])));
+      ((float*)s.out)[(long)m * s.ld_out + n] = expf(-0.60653065971263342f * sg);
+      break;
+    }
+    case EPI_SIGB:
+      ((float*)s.out)[(long)m * s.ld_out + n] = 1.0f / (1.0f + expf(-(v + s.aux[n])));
       break;
     default:
       break;

@@ -40,11 +40,25 @@ __global__ __launch_bounds__(256) void k_validate(ValidateArgs a) {
   }
   if (a.n_rows == 0 && threadIdx.x == 0 && a.counters && a.seq_slot >= 0)
     a.counters[a.seq_slot] += a.n_tok;
+  for (int i = threadIdx.x; i < a.n_zero; i += 256) a.zero[i] = 0u;
   if (bits) set_err(a.err, bits);
 }
 
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_validate, dim3(1), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+__global__ void k_commit_shift(CommitArgs a) {
+  const int b = blockIdx.y;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int slot = a.slots[b];
+  if (c < a.C && slot >= 0 && slot < a.n_slots)
+    a.pool[(long)slot * a.slot_stride + a.shift_off + c] = a.u[(long)b * a.C + c];
+}
+
+hipError_t launch_commit_shift(const CommitArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_commit_shift, dim3((a.C + 255) / 256, a.B), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -300,65 +314,90 @@ hipError_t launch_pack_vec(float* dst, const void* src, int src_f16, int64_t n, 
 }
 
 // ============================================================== sparse channel-mix value
-// Grid: (C/64 column slices) x NS splits of the active list.  Each workgroup
-// compacts the union mask (ascending f, deterministic), takes its split of
-// the list, and accumulates h_f * Wv[f, slice] for every row, with
-// h = relu(pre)^2 recomputed in fp32 from the stored pre-activation.
-// Results go to per-split partials, folded into the residual in a fixed
-// order by the next LayerNorm kernel.
+// One workgroup of 1024 threads per 32-column slice of the value matrix
+// (64-byte row segments).  It compacts the union mask in one pass (ascending
+// f, deterministic), then gathers h_f * Wv[f, slice] over the whole active
+// list, 4 threads per row segment and 256 rows per pass, with
+// h = relu(pre)^2 recomputed in fp32 from the stored pre-activation.  The
+// sum over rows is reduced in a fixed order (lane shuffles, then the 16
+// waves through LDS), added to the residual, and the new channel-mix shift
+// of these columns is committed.  Nothing leaves the workgroup half-summed.
 constexpr int CMIX_MAXF = 16384;
 constexpr int CMIX_MAXB = 4;
+constexpr int CMIX_COLS = 32;
+constexpr int CMIX_MAXPER = CMIX_MAXF / 256 / 4;  // mask words per compacting thread
 
 template <int B>
-__global__ __launch_bounds__(256) void k_cmix_sparse(CmixArgs a) {
+__global__ __launch_bounds__(1024) void k_cmix_sparse(CmixArgs a) {
   __shared__ unsigned short s_idx[CMIX_MAXF];
   __shared__ int s_wcnt[4];
-  __shared__ float s_red[32][B][64 + 1];
+  __shared__ float s_red[16][B][CMIX_COLS];
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
 
-  // ---- compaction of the mask (F <= 16384), ascending order
-  int total = 0;
-  for (int base = 0; base < a.F; base += 256) {
-    const int f = base + t;
-    const bool on = f < a.F && a.mask[f] != 0;
-    const unsigned long long bal = __ballot(on);
-    const int before = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) s_wcnt[wave] = __popcll(bal);
-    __syncthreads();
-    int woff = 0;
-    for (int w = 0; w < wave; ++w) woff += s_wcnt[w];
-    const int tot = s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
-    if (on) s_idx[total + woff + before] = (unsigned short)f;
-    total += tot;
-    __syncthreads();
+  // ---- compaction by threads 0..255: thread t owns mask bytes
+  // [t*per, (t+1)*per), per = F/256 (a multiple of 4); bytes are 0/1, so a
+  // word's popcount is its count.
+  const int words = a.F / 1024;
+  unsigned int mw[CMIX_MAXPER];
+  int mine = 0, incl = 0;
+  if (t < 256) {
+    const unsigned int* m32 = reinterpret_cast<const unsigned int*>(a.mask) + t * words;
+#pragma unroll
+    for (int i = 0; i < CMIX_MAXPER; ++i) {
+      mw[i] = i < words ? m32[i] : 0u;
+      mine += __popc(mw[i]);
+    }
+    incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) s_wcnt[wave] = incl;
   }
-  const int s = blockIdx.y;
-  const int p0 = (int)((long)total * s / a.NS);
-  const int p1 = (int)((long)total * (s + 1) / a.NS);
-  if (a.dbg_idx && blockIdx.x == 0 && s == 0) {
-    for (int i = t; i < total; i += 256) a.dbg_idx[i] = s_idx[i];
+  __syncthreads();
+  const int total = s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
+  if (t < 256) {
+    int pos = incl - mine;
+    for (int w = 0; w < wave; ++w) pos += s_wcnt[w];
+#pragma unroll
+    for (int i = 0; i < CMIX_MAXPER; ++i) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if ((mw[i] >> (8 * k)) & 1u) s_idx[pos++] = (unsigned short)(t * words * 4 + 4 * i + k);
+    }
+  }
+  __syncthreads();
+  if (a.dbg_idx && blockIdx.x == 0) {
+    for (int i = t; i < total; i += 1024) a.dbg_idx[i] = s_idx[i];
     if (t == 0) *a.dbg_cnt = total;
   }
 
-  // ---- gather: thread t -> row-group rg (32 of them), 8 columns
-  const int rg = t >> 3;
-  const int c8 = (t & 7) * 8;
-  const int cb = blockIdx.x * 64 + c8;
+  // ---- gather: thread t -> row group rg = t/4 (256 of them), 8 columns.
+  // Workgroups are dealt round-robin to the 8 XCDs; consecutive slices go to
+  // the same XCD so the two 64-byte halves of a 128-byte line share an L2.
+  const int nsl = a.C / CMIX_COLS;
+  const int per_xcd = (nsl + 7) / 8;
+  const int slice = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (slice >= nsl) return;
+  const int rg = t >> 2;
+  const int c8 = (t & 3) * 8;
+  const int cb = slice * CMIX_COLS + c8;
   float acc[B][8];
 #pragma unroll
   for (int b = 0; b < B; ++b)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[b][e] = 0.f;
 
-  int p = p0 + rg;
-  for (; p + 96 < p1; p += 128) {
+  int p = rg;
+  for (; p + 768 < total; p += 1024) {
     u32x4 w4[4];
     float h4[4][B];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int f = s_idx[p + 32 * u];
-      w4[u] = ld16_nt(a.Wv + (long)f * a.C + cb);
+      const int f = s_idx[p + 256 * u];
+      w4[u] = ld16(a.Wv + (long)f * a.C + cb);
 #pragma unroll
       for (int b = 0; b < B; ++b) {
         const float z = a.pre[(long)b * a.F + f];
@@ -376,9 +415,9 @@ __global__ __launch_bounds__(256) void k_cmix_sparse(CmixArgs a) {
       }
     }
   }
-  for (; p < p1; p += 32) {
+  for (; p < total; p += 256) {
     const int f = s_idx[p];
-    const u32x4 w = ld16_nt(a.Wv + (long)f * a.C + cb);
+    const u32x4 w = ld16(a.Wv + (long)f * a.C + cb);
     const half8 hv = __builtin_bit_cast(half8, w);
 #pragma unroll
     for (int b = 0; b < B; ++b) {
@@ -389,17 +428,32 @@ __global__ __launch_bounds__(256) void k_cmix_sparse(CmixArgs a) {
     }
   }
 
-  // ---- reduce the 32 row-groups in a fixed order
+  // ---- fixed-order reduction: the 16 row groups of a wave by shuffles
+  // (lane = 4*group + column chunk), then the 16 waves through LDS
 #pragma unroll
   for (int b = 0; b < B; ++b)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s_red[rg][b][c8 + e] = acc[b][e];
+    for (int e = 0; e < 8; ++e) {
+      float v = acc[b][e];
+      v += __shfl_xor(v, 4);
+      v += __shfl_xor(v, 8);
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (lane < 4) s_red[wave][b][c8 + e] = v;
+    }
   __syncthreads();
-  for (int o = t; o < B * 64; o += 256) {
-    const int b = o / 64, c = o % 64;
+  if (t < B * CMIX_COLS) {
+    const int b = t / CMIX_COLS;
+    const int col = slice * CMIX_COLS + t % CMIX_COLS;
     float sum = 0.f;
-    for (int g = 0; g < 32; ++g) sum += s_red[g][b][c];
-    a.part[((long)s * a.B + b) * a.C + blockIdx.x * 64 + c] = sum;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) sum += s_red[w][b][t % CMIX_COLS];
+    a.x[(long)b * a.C + col] += sum;
+    if (a.u_ffn) {
+      const int slot = a.slots[b];
+      if (slot >= 0 && slot < a.n_slots)
+        a.pool[(long)slot * a.slot_stride + a.shift_off + col] = a.u_ffn[(long)b * a.C + col];
+    }
   }
 }
 
@@ -410,13 +464,14 @@ const char* cmix_sparse_kernel_name(int B) {
 }
 
 hipError_t launch_cmix_sparse(const CmixArgs& a, hipStream_t st) {
-  if (a.F > CMIX_MAXF || a.C % 64 || a.B < 1 || a.B > CMIX_MAXB) return hipErrorInvalidValue;
-  const dim3 grid(a.C / 64, a.NS);
+  if (a.F > CMIX_MAXF || a.F % 1024 || a.C % CMIX_COLS || a.B < 1 || a.B > CMIX_MAXB)
+    return hipErrorInvalidValue;
+  const dim3 grid((a.C / CMIX_COLS + 7) / 8 * 8);
   switch (a.B) {
-    case 1: hipLaunchKernelGGL(k_cmix_sparse<1>, grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL(k_cmix_sparse<2>, grid, dim3(256), 0, st, a); break;
-    case 3: hipLaunchKernelGGL(k_cmix_sparse<3>, grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL(k_cmix_sparse<4>, grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL(k_cmix_sparse<1>, grid, dim3(1024), 0, st, a); break;
+    case 2: hipLaunchKernelGGL(k_cmix_sparse<2>, grid, dim3(1024), 0, st, a); break;
+    case 3: hipLaunchKernelGGL(k_cmix_sparse<3>, grid, dim3(1024), 0, st, a); break;
+    case 4: hipLaunchKernelGGL(k_cmix_sparse<4>, grid, dim3(1024), 0, st, a); break;
   }
   return hipGetLastError();
 }

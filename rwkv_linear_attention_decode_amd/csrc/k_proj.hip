@@ -12,6 +12,11 @@
 #include "launch.h"
 
 // ============================================================== GEMV
+// The fused LayerNorm prologue holds a lane's K slice of every row in VGPRs
+// (B * NCH * 8 floats) and the mixed rows in LDS; it is instantiated only
+// up to this many floats per lane.
+constexpr int kFusedMaxFloats = 80;
+
 template <int B, int LPR, int NCH, int RPW>
 __global__ __launch_bounds__(256) void k_gemv(ProjArgs a) {
   constexpr int GPW = 64 / LPR;
@@ -40,17 +45,101 @@ __global__ __launch_bounds__(256) void k_gemv(ProjArgs a) {
     }
   }
 
+  // Activations for this lane's K slice: k = (c * LPR + lig) * 8 + e.
   float xa[B][NCH][8];
-  const float* X = reinterpret_cast<const float*>(sg.act);
+  if (a.ln.mode == LNP_NONE) {
+    const float* X = reinterpret_cast<const float*>(sg.act);
 #pragma unroll
-  for (int b = 0; b < B; ++b)
+    for (int b = 0; b < B; ++b)
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const float* xp = X + (long)b * sg.ld_act + (c * LPR + lig) * 8;
-      const floatx4 p0 = ldf4(xp), p1 = ldf4(xp + 4);
-      xa[b][c][0] = p0.x; xa[b][c][1] = p0.y; xa[b][c][2] = p0.z; xa[b][c][3] = p0.w;
-      xa[b][c][4] = p1.x; xa[b][c][5] = p1.y; xa[b][c][6] = p1.z; xa[b][c][7] = p1.w;
+      for (int c = 0; c < NCH; ++c) {
+        const float* xp = X + (long)b * sg.ld_act + (c * LPR + lig) * 8;
+        const floatx4 p0 = ldf4(xp), p1 = ldf4(xp + 4);
+        xa[b][c][0] = p0.x; xa[b][c][1] = p0.y; xa[b][c][2] = p0.z; xa[b][c][3] = p0.w;
+        xa[b][c][4] = p1.x; xa[b][c][5] = p1.y; xa[b][c][6] = p1.z; xa[b][c][7] = p1.w;
+      }
+  } else if constexpr (B * NCH <= kFusedMaxFloats / 8) {
+    // Fused LayerNorm + token-shift mix, computed once per workgroup while
+    // the weight loads above are in flight: wave w normalises the quarter
+    // [w K/4, (w+1) K/4) of every row (coalesced, stride-64 lanes), row
+    // statistics are combined through LDS, and the mixed row is shared
+    // through LDS with every wave's K slice.
+    constexpr int QK = K / 4;          // elements per wave
+    constexpr int PER = QK / 64;       // per lane
+    __shared__ __attribute__((aligned(16))) float s_xq[B][K];
+    __shared__ float s_st[B][4][2];
+    // every global load of the prologue is issued before the first barrier
+    float xv[B][PER], gv[PER], bv[PER], mv[PER], pvv[B][PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int k = wave * QK + lane + 64 * j;
+      gv[j] = a.ln.g[k];
+      bv[j] = a.ln.b[k];
+      mv[j] = a.ln.mode == LNP_MIX ? sg.mix[k] : 0.f;
     }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const float* prev = nullptr;
+      if (a.ln.mode == LNP_MIX) {
+        const int slot = a.ln.slots[b];
+        if (slot >= 0 && slot < a.ln.n_slots)
+          prev = a.ln.pool + (long)slot * a.ln.slot_stride + a.ln.shift_off;
+      }
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int k = wave * QK + lane + 64 * j;
+        xv[b][j] = a.ln.x[(long)b * K + k];
+        pvv[b][j] = prev ? prev[k] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      float sm = 0.f;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) sm += xv[b][j];
+      sm = wave_sum(sm);
+      if (lane == 0) s_st[b][wave][0] = sm;
+    }
+    __syncthreads();
+    float mean[B], rstd[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      mean[b] = (s_st[b][0][0] + s_st[b][1][0] + s_st[b][2][0] + s_st[b][3][0]) * (1.0f / K);
+      float q = 0.f;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const float d = xv[b][j] - mean[b];
+        q += d * d;
+      }
+      q = wave_sum(q);
+      if (lane == 0) s_st[b][wave][1] = q;
+    }
+    __syncthreads();
+    const bool writer = blockIdx.x == 0 && a.ln.u_out;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      rstd[b] = 1.0f / sqrtf((s_st[b][0][1] + s_st[b][1][1] + s_st[b][2][1] + s_st[b][3][1]) *
+                                 (1.0f / K) + 1e-5f);
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int k = wave * QK + lane + 64 * j;
+        const float u = (xv[b][j] - mean[b]) * rstd[b] * gv[j] + bv[j];
+        if (writer) a.ln.u_out[(long)b * K + k] = u;
+        s_xq[b][k] = a.ln.mode == LNP_MIX ? u + (pvv[b][j] - u) * mv[j] : u;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const float* xp = &s_xq[b][(c * LPR + lig) * 8];
+        const floatx4 p0 = *reinterpret_cast<const floatx4*>(xp);
+        const floatx4 p1 = *reinterpret_cast<const floatx4*>(xp + 4);
+        xa[b][c][0] = p0.x; xa[b][c][1] = p0.y; xa[b][c][2] = p0.z; xa[b][c][3] = p0.w;
+        xa[b][c][4] = p1.x; xa[b][c][5] = p1.y; xa[b][c][6] = p1.z; xa[b][c][7] = p1.w;
+      }
+  }
 
   float acc[RPW][B];
 #pragma unroll
@@ -115,6 +204,14 @@ bool gemv_supported(int B, int K) {
   return K % 512 == 0 && K / 512 >= 1 && K / 512 <= 8;
 }
 
+// The fused LayerNorm prologue keeps a lane's whole K slice of every row in
+// VGPRs; bound that to 80 floats.
+bool gemv_fused_ok(int B, int K) {
+  if (!gemv_supported(B, K)) return false;
+  const int nch = K == 256 ? 1 : K / 512;
+  return B * nch <= kFusedMaxFloats / 8;
+}
+
 #define GEMV_NAME(B, L, N) "k_gemv<" #B "," #L "," #N ">"
 
 template <int B>
@@ -158,12 +255,24 @@ const char* gemv_kernel_name(int B, int K) {
 // [32g, 32g+32) of the chunk, used as four 8-wide MFMA K slices.  The A
 // operand is read from LDS with the same k mapping, so the product sums
 // over every k exactly once.
+//
+// Activations arrive in fp32 and are split while staged into LDS as
+// a = hi + lo * 2^-12 with hi = fp16(a) and lo = fp16((a - hi) * 2^12); each
+// weight fragment meets both planes (two MFMAs into two accumulators, the
+// second scaled back at the end), so the product keeps ~22 bits of the
+// activation while the weights (exact fp16 values) stream once.  The 2^12
+// keeps the residual plane out of the fp16 subnormal range.  A single fp16
+// rounding of the activations loses too much for deep models whose layers
+// amplify relative perturbations.
+constexpr float LO_SCALE = 4096.0f;
+constexpr float LO_UNSCALE = 1.0f / 4096.0f;
 template <int MT>
 __global__ __launch_bounds__(256) void k_gemm(ProjArgs a) {
   constexpr int KC = 128;
   constexpr int MT16 = MT / 16;
   constexpr int LDA = KC + 8;  // halves per LDS row (16-byte skew)
-  __shared__ __attribute__((aligned(16))) half_t As[2][MT][LDA];
+  __shared__ __attribute__((aligned(16))) half_t Ah[2][MT][LDA];
+  __shared__ __attribute__((aligned(16))) half_t Al[2][MT][LDA];
 
   // XCD-aware tile order: consecutive tiles (same column tile, successive
   // M tiles) go to the same XCD so its L2 serves the repeated weight reads.
@@ -182,29 +291,45 @@ __global__ __launch_bounds__(256) void k_gemm(ProjArgs a) {
   const int g = lane >> 4;
   const int col = n0 + wave * 16 + (lane & 15);
   const bool col_ok = col < sg.row1;
-  const half_t* wrow = a.W + (long)(col_ok ? col : sg.row0) * a.K + 32 * g;
-  const half_t* X = reinterpret_cast<const half_t*>(sg.act);
-  const int nk = a.K / KC;
+  // a block may carry its own matrix (rows relative to the block) and K
+  const bool own = sg.W != nullptr;
+  const int K = own ? sg.K : a.K;
+  const long wr = own ? (col_ok ? col - sg.row0 : 0) : (col_ok ? col : sg.row0);
+  const half_t* wrow = (own ? sg.W : a.W) + wr * K + 32 * g;
+  const float* X = reinterpret_cast<const float*>(sg.act) + sg.act_off;
+  const int nk = (K + KC - 1) / KC;   // K is a multiple of 32; the last chunk may be partial
 
-  floatx4 acc[MT16];
+  floatx4 acc[MT16], accl[MT16];
 #pragma unroll
-  for (int t = 0; t < MT16; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < MT16; ++t) {
+    acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    accl[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
 
   auto load_w = [&](int kc, u32x4* dst) {
     const half_t* p = wrow + kc * KC;
+    const bool ok = kc * KC + 32 * g < K;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) dst[s] = ld16_nt(p + 8 * s);
+    for (int s = 0; s < 4; ++s) dst[s] = ok ? ld16_nt(p + 8 * s) : u32x4{0u, 0u, 0u, 0u};
   };
+  // MT rows x 128 fp32 = MT*32 float4; 256 threads -> MT/8 float4 each.
   auto load_a = [&](int kc, int buf) {
 #pragma unroll
-    for (int p = 0; p < MT / 16; ++p) {
+    for (int p = 0; p < MT / 8; ++p) {
       const int idx = p * 256 + threadIdx.x;
-      const int r = idx >> 4;
-      const int c = idx & 15;
+      const int r = idx >> 5;
+      const int c = (idx & 31) * 4;
       const int m = m0 + r;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (m < a.M) v = ld16(X + (long)m * sg.ld_act + kc * KC + c * 8);
-      st16(&As[buf][r][c * 8], v);
+      floatx4 v = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (m < a.M && kc * KC + c < K) v = ldf4(X + (long)m * sg.ld_act + kc * KC + c);
+      half4 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = (half_t)v[e];
+        lo[e] = (half_t)((v[e] - (float)hi[e]) * LO_SCALE);
+      }
+      *reinterpret_cast<half4*>(&Ah[buf][r][c]) = hi;
+      *reinterpret_cast<half4*>(&Al[buf][r][c]) = lo;
     }
   };
 
@@ -223,8 +348,12 @@ __global__ __launch_bounds__(256) void k_gemm(ProjArgs a) {
       const half8 bv = __builtin_bit_cast(half8, wf[s]);
 #pragma unroll
       for (int t = 0; t < MT16; ++t) {
-        const half8 av = *reinterpret_cast<const half8*>(&As[buf][t * 16 + (lane & 15)][32 * g + 8 * s]);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[t], 0, 0, 0);
+        const int r = t * 16 + (lane & 15);
+        const int k = 32 * g + 8 * s;
+        const half8 ah = *reinterpret_cast<const half8*>(&Ah[buf][r][k]);
+        const half8 al = *reinterpret_cast<const half8*>(&Al[buf][r][k]);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bv, acc[t], 0, 0, 0);
+        accl[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bv, accl[t], 0, 0, 0);
       }
     }
     __syncthreads();
@@ -241,10 +370,11 @@ __global__ __launch_bounds__(256) void k_gemm(ProjArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int m = m0 + t * 16 + 4 * g + i;
       if (m < a.M) {
+        const float v = acc[t][i] + accl[t][i] * LO_UNSCALE;
         if (sg.epi == EPI_PRE) {
-          ((float*)sg.out)[(long)m * sg.ld_out + n] = acc[t][i] + sg.aux[n];
+          ((float*)sg.out)[(long)m * sg.ld_out + n] = v + sg.aux[n];
         } else {
-          epi_store(sg, n, m, acc[t][i]);
+          epi_store(sg, n, m, v);
         }
       }
     }
@@ -261,7 +391,10 @@ __global__ void k_pre_mask(const float* pre, int ld, int M, int F, unsigned char
 }
 
 hipError_t launch_gemm(ProjArgs a, int total_rows, hipStream_t st) {
-  if (a.K % 128 != 0) return hipErrorInvalidValue;
+  for (int i = 0; i < a.nseg; ++i) {
+    const int K = a.seg[i].W ? a.seg[i].K : a.K;
+    if (K % 32 != 0 || K <= 0) return hipErrorInvalidValue;
+  }
   a.n_tiles = (total_rows + 63) / 64;
   int mt = a.M <= 16 ? 16 : (a.M <= 32 ? 32 : 64);
   a.m_tiles = (a.M + mt - 1) / mt;

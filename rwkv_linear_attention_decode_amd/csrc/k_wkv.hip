@@ -30,11 +30,52 @@ struct HeadVecs {
 
 // Adapter outputs + keys for row `b` (a token or a batch row), head `h`.
 // Leaves r, d, a, bb, kt, v (after the value residual), g and bonus in LDS.
-RW_DEV void wkv_prologue(const WkvArgs& a, int b, int h, HeadVecs& hv, float* s_lin, float* red) {
+//
+// The adapter outputs of the head's 64 channels are dot products of length
+// Dw, Da, Dv, Dg.  Per channel the four ranks are taken as one concatenated
+// row of NCHK*4 chunks of 8 (ranks are multiples of 8, so a chunk never
+// straddles two adapters); thread t works on channel i = t/4 and chunks
+// [q*NCHK, (q+1)*NCHK) with q = t%4, and the four quarters meet by shuffle.
+// Every global load is issued before the first barrier, so the chain from
+// kernel start to the state update is one memory round trip.
+template <int NCHK>
+RW_DEV void wkv_prologue(const WkvArgs& a, int b, int h, HeadVecs& hv, float* s_lin) {
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int C = a.C;
-  for (int i = t; i < a.Lin; i += 256) s_lin[i] = a.lin[(long)b * a.Lin + i];
+  const int i = t >> 2;
+  const int qd = t & 3;
+  const int c = h * 64 + i;
+  const int e1 = a.Dw, e2 = a.Dw + a.Da, e3 = a.Dw + a.Da + a.Dv;
+
+  u32x4 wch[NCHK];
+#pragma unroll
+  for (int q = 0; q < NCHK; ++q) {
+    const int e0 = (qd * NCHK + q) * 8;
+    const half_t* W;
+    if (e0 < e1) W = a.w2 + (long)c * a.Dw + e0;
+    else if (e0 < e2) W = a.a2 + (long)c * a.Da + (e0 - e1);
+    else if (e0 < e3) W = a.v2 + (long)c * a.Dv + (e0 - e2);
+    else W = a.g2 + (long)c * a.Dg + (e0 - e3);
+    const bool skip = (e0 >= e2 && e0 < e3 && a.layer == 0);  // layer 0 has no value mix
+    wch[q] = skip ? u32x4{0u, 0u, 0u, 0u} : ld16(W);
+  }
+  // per-channel vectors for wave 0's key step
+  float k_k = 0.f, k_a = 0.f, r_k = 0.f, vf = 0.f;
+  if (wave == 0) {
+    const int cc = h * 64 + lane;
+    k_k = a.k_k[cc];
+    k_a = a.k_a[cc];
+    r_k = a.r_k[cc];
+    if (a.layer > 0) vf = a.vfirst[(long)b * C + cc];
+  }
+  float w0 = 0.f, a0 = 0.f, v0 = 0.f;
+  if (qd == 0) {
+    w0 = a.w0[c];
+    a0 = a.a0[c];
+    v0 = a.v0[c];
+  }
+  for (int j = t; j < a.Lin; j += 256) s_lin[j] = a.lin[(long)b * a.Lin + j];
   if (t < 64) {
     const long base = (long)b * 3 * C + h * 64 + t;
     hv.r[t] = a.rkv[base];
@@ -43,58 +84,97 @@ RW_DEV void wkv_prologue(const WkvArgs& a, int b, int h, HeadVecs& hv, float* s_
   }
   __syncthreads();
   {
-    const int c = h * 64 + lane;
-    const half_t* W = wave == 0 ? a.w2 : (wave == 1 ? a.a2 : (wave == 2 ? a.v2 : a.g2));
-    const int ioff = wave == 0 ? 0 : (wave == 1 ? a.off_a : (wave == 2 ? a.off_v : a.off_g));
-    const int D = wave == 0 ? a.Dw : (wave == 1 ? a.Da : (wave == 2 ? a.Dv : a.Dg));
-    const float* in = s_lin + ioff;
-    float acc = 0.f;
-    if (wave != 2 || a.layer > 0) {
-      const half_t* wr = W + (long)c * D;
-      for (int j = 0; j < D; j += 8) {
-        const half8 w8 = *reinterpret_cast<const half8*>(wr + j);
+    float zw = 0.f, za = 0.f, zv = 0.f, zg = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf((float)w8[e], in[j + e], acc);
-      }
+    for (int q = 0; q < NCHK; ++q) {
+      const int e0 = (qd * NCHK + q) * 8;
+      int li;
+      if (e0 < e1) li = e0;
+      else if (e0 < e2) li = a.off_a + (e0 - e1);
+      else if (e0 < e3) li = a.off_v + (e0 - e2);
+      else li = a.off_g + (e0 - e3);
+      const half8 w8 = __builtin_bit_cast(half8, wch[q]);
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s = fmaf((float)w8[e], s_lin[li + e], s);
+      zw += e0 < e1 ? s : 0.f;
+      za += (e0 >= e1 && e0 < e2) ? s : 0.f;
+      zv += (e0 >= e2 && e0 < e3) ? s : 0.f;
+      zg += e0 >= e3 ? s : 0.f;
     }
-    if (wave == 0) {
+    zw += __shfl_xor(zw, 1); zw += __shfl_xor(zw, 2);
+    za += __shfl_xor(za, 1); za += __shfl_xor(za, 2);
+    zv += __shfl_xor(zv, 1); zv += __shfl_xor(zv, 2);
+    zg += __shfl_xor(zg, 1); zg += __shfl_xor(zg, 2);
+    if (qd == 0) {
       // decay = exp(-exp(-softplus(-z) - 0.5)) = exp(-e^{-1/2} sigmoid(z))
-      const float z = a.w0[c] + acc;
-      const float sg = 1.0f / (1.0f + expf(-z));
-      hv.d[lane] = expf(-0.60653065971263342f * sg);
-    } else if (wave == 1) {
-      hv.al[lane] = 1.0f / (1.0f + expf(-(a.a0[c] + acc)));
-    } else if (wave == 2) {
-      hv.vg[lane] = a.layer > 0 ? 1.0f / (1.0f + expf(-(a.v0[c] + acc))) : 0.0f;
-    } else {
-      hv.g[lane] = acc;
+      const float sw = 1.0f / (1.0f + expf(-(w0 + zw)));
+      hv.d[i] = expf(-0.60653065971263342f * sw);
+      hv.al[i] = 1.0f / (1.0f + expf(-(a0 + za)));
+      hv.vg[i] = a.layer > 0 ? 1.0f / (1.0f + expf(-(v0 + zv))) : 0.0f;
+      hv.g[i] = zg;
     }
   }
   __syncthreads();
   if (wave == 0) {
-    const int c = h * 64 + lane;
+    const int cc = h * 64 + lane;
     const float k = hv.k[lane];
-    const float kap = k * a.k_k[c];
+    const float kap = k * k_k;
     const float nrm = sqrtf(wave_sum(kap * kap));
     const float kh = kap / fmaxf(nrm, 1e-12f);
     const float al = hv.al[lane];
-    const float kt = k * (1.0f + (al - 1.0f) * a.k_a[c]);
+    const float kt = k * (1.0f + (al - 1.0f) * k_a);
     hv.a[lane] = -kh;
     hv.bb[lane] = kh * al;
     hv.kt[lane] = kt;
     float v = hv.v[lane];
-    if (a.layer == 0) {
-      a.vfirst[(long)b * C + c] = v;
-    } else {
-      const float vf = a.vfirst[(long)b * C + c];
+    if (a.layer == 0)
+      a.vfirst[(long)b * C + cc] = v;
+    else
       v = v + (vf - v) * hv.vg[lane];
-    }
     hv.v[lane] = v;
-    const float bon = wave_sum(hv.r[lane] * kt * a.r_k[h * 64 + lane]);
+    const float bon = wave_sum(hv.r[lane] * kt * r_k);
     if (lane == 0) hv.bonus = bon;
   }
   __syncthreads();
-  (void)red;
+}
+
+// Same result when the adapter outputs were computed for all rows by the
+// MFMA projection: `lo` holds [rows][4C] = decay | alpha | value gate | gate.
+// Register-light, for many rows per launch.
+RW_DEV void wkv_prologue_lean(const WkvArgs& a, int b, int h, HeadVecs& hv) {
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int C = a.C;
+  if (wave == 0) {
+    const long base = (long)b * 3 * C + h * 64 + lane;
+    const float* lo = a.lo + (long)b * 4 * C + h * 64 + lane;
+    const int cc = h * 64 + lane;
+    const float r = a.rkv[base];
+    const float k = a.rkv[base + C];
+    float v = a.rkv[base + 2 * C];
+    const float al = lo[C];
+    const float kap = k * a.k_k[cc];
+    const float nrm = sqrtf(wave_sum(kap * kap));
+    const float kh = kap / fmaxf(nrm, 1e-12f);
+    const float kt = k * (1.0f + (al - 1.0f) * a.k_a[cc]);
+    if (a.layer == 0) {
+      a.vfirst[(long)b * C + cc] = v;
+    } else {
+      const float vf = a.vfirst[(long)b * C + cc];
+      v = v + (vf - v) * lo[2 * C];
+    }
+    hv.r[lane] = r;
+    hv.d[lane] = lo[0];
+    hv.g[lane] = lo[3 * C];
+    hv.a[lane] = -kh;
+    hv.bb[lane] = kh * al;
+    hv.kt[lane] = kt;
+    hv.v[lane] = v;
+    const float bon = wave_sum(r * kt * a.r_k[cc]);
+    if (lane == 0) hv.bonus = bon;
+  }
+  __syncthreads();
 }
 
 // GroupNorm over the head's 64 readouts + bonus * v, times the gate (wave 0).
@@ -109,21 +189,20 @@ RW_DEV float wkv_epilogue(const WkvArgs& a, int h, const HeadVecs& hv, float y) 
   return o * hv.g[lane];
 }
 
+template <int NCHK>
 __global__ __launch_bounds__(256) void k_wkv_decode(WkvArgs a) {
   __shared__ HeadVecs hv;
   __shared__ float s_lin[LIN_MAX];
-  __shared__ float red[8];
   const int b = blockIdx.x / a.H;
   const int h = blockIdx.x % a.H;
-  wkv_prologue(a, b, h, hv, s_lin, red);
-
   const int t = threadIdx.x;
   const int i = t >> 2;
   const int j0 = (t & 3) * 16;
   const int slot = a.slots[b];
-  float* S = (slot >= 0 && slot < a.n_slots) ? a.pool + (long)slot * a.slot_stride + a.layer_off + 2L * a.C +
-                             (long)h * 4096 + i * 64 + j0
-                       : nullptr;
+  const bool ok = slot >= 0 && slot < a.n_slots;
+  float* base = ok ? a.pool + (long)slot * a.slot_stride + a.layer_off : nullptr;
+  float* S = ok ? base + 2L * a.C + (long)h * 4096 + i * 64 + j0 : nullptr;
+  // the state does not depend on this token: start its loads first
   float s[16];
   if (S) {
 #pragma unroll
@@ -135,6 +214,14 @@ __global__ __launch_bounds__(256) void k_wkv_decode(WkvArgs a) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) s[q] = 0.f;
   }
+  // commit the time-mix shift computed by the fused input projection
+  if (a.u_att && ok && t >= 64 && t < 128)
+    base[h * 64 + (t - 64)] = a.u_att[(long)b * a.C + h * 64 + (t - 64)];
+  if constexpr (NCHK == 0)
+    wkv_prologue_lean(a, b, h, hv);
+  else
+    wkv_prologue<NCHK>(a, b, h, hv, s_lin);
+
   float sa = 0.f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) sa = fmaf(s[j], hv.a[j0 + j], sa);
@@ -167,20 +254,40 @@ __global__ __launch_bounds__(256) void k_wkv_decode(WkvArgs a) {
   }
 }
 
+// chunks of 8 per thread: (Dw + Da + Dv + Dg) / 32
+#define WKV_NCHK_CASES(X) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) \
+  X(13) X(14) X(15) X(16) X(17) X(18) X(19) X(20) X(21) X(22) X(23) X(24) X(25) X(26)   \
+  X(27) X(28) X(29) X(30) X(31) X(32)
+
+// 0 selects the variant that reads precomputed adapter outputs
+static int wkv_nchk(const WkvArgs& a) {
+  if (a.lo) return 0;
+  const int dsum = a.Dw + a.Da + a.Dv + a.Dg;
+  return dsum % 32 ? -1 : dsum / 32;
+}
+
 hipError_t launch_wkv_decode(const WkvArgs& a, hipStream_t st) {
   if (a.Lin > LIN_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_wkv_decode, dim3(a.B * a.H), dim3(256), 0, st, a);
+  switch (wkv_nchk(a)) {
+#define X(n) case n: hipLaunchKernelGGL(k_wkv_decode<n>, dim3(a.B * a.H), dim3(256), 0, st, a); break;
+    X(0) WKV_NCHK_CASES(X)
+#undef X
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- prefill
+template <int NCHK>
 __global__ __launch_bounds__(256) void k_wkv_prep(WkvArgs a) {
   __shared__ HeadVecs hv;
   __shared__ float s_lin[LIN_MAX];
-  __shared__ float red[8];
   const int tk = blockIdx.x / a.H;
   const int h = blockIdx.x % a.H;
-  wkv_prologue(a, tk, h, hv, s_lin, red);
+  if constexpr (NCHK == 0)
+    wkv_prologue_lean(a, tk, h, hv);
+  else
+    wkv_prologue<NCHK>(a, tk, h, hv, s_lin);
   const int t = threadIdx.x;
   if (t < 64) {
     const long off = (long)tk * a.C + h * 64 + t;
@@ -254,7 +361,12 @@ __global__ __launch_bounds__(64) void k_wkv_post(WkvArgs a) {
 
 hipError_t launch_wkv_prep(const WkvArgs& a, hipStream_t st) {
   if (a.Lin > LIN_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_wkv_prep, dim3(a.B * a.H), dim3(256), 0, st, a);
+  switch (wkv_nchk(a)) {
+#define X(n) case n: hipLaunchKernelGGL(k_wkv_prep<n>, dim3(a.B * a.H), dim3(256), 0, st, a); break;
+    X(0) WKV_NCHK_CASES(X)
+#undef X
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 hipError_t launch_wkv_scan(const WkvArgs& a, hipStream_t st) {

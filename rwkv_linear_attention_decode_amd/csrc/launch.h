@@ -26,8 +26,23 @@ struct ValidateArgs {
   int* tok_out;          // [n_tok]
   uint32_t* err;
   int64_t* counters;     // pool counters; += 1 per valid row, or += n_tok for prefill
+  unsigned int* zero;    // words to clear at the start of a step (arrival counters)
+  int n_zero;
 };
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t st);
+
+// Copy new shift rows u [B][C] into each row's slot (rows with bad slots skipped).
+struct CommitArgs {
+  const float* u;
+  float* pool;
+  int64_t slot_stride;
+  int64_t n_slots;
+  int64_t shift_off;
+  const int* slots;
+  int B, C;
+};
+hipError_t launch_commit_shift(const CommitArgs& a, hipStream_t st);
+bool gemv_fused_ok(int B, int K);
 
 struct EmbedArgs {
   const half_t* emb;
@@ -89,9 +104,15 @@ struct CmixArgs {
   const float* pre;           // [B][F] key pre-activations (bias included)
   const unsigned char* mask;  // [F] union over rows of (pre > 0)
   const half_t* Wv;           // [F][C] hidden-major value matrix
-  float* part;                // [NS][B][C]
-  int B, C, F, NS;
-  int* dbg_idx;               // optional: the union active list (ascending) of split 0
+  float* x;                   // [B][C] residual: x += value projection
+  const float* u_ffn;         // [B][C] new channel-mix shift to commit, or nullptr
+  float* pool;
+  int64_t slot_stride;
+  int64_t n_slots;
+  int64_t shift_off;
+  const int* slots;
+  int B, C, F;
+  int* dbg_idx;               // optional: the union active list (ascending)
   int* dbg_cnt;               // optional: its length
 };
 hipError_t launch_cmix_sparse(const CmixArgs& a, hipStream_t st);
@@ -142,6 +163,8 @@ struct WkvArgs {
   const float* lnx_w;
   const float* lnx_b;
   float* vfirst;           // [B][C]
+  const float* lo;         // [B][4C] precomputed decay | alpha | value gate | gate, or nullptr
+  const float* u_att;      // decode: [B][C] new time-mix shift to commit, or nullptr
   void* yout;              // [B][C] gated, normalised readout (fp32 or fp16)
   int yout_f16;
   // sequence path buffers ([T][C] fp32 each)

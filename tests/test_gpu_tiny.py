@@ -117,13 +117,16 @@ def test_tiny_free_running_greedy(model, W, R):
         tok = g
 
 
-@pytest.mark.parametrize("B,gemv,sparse", [
-    (1, 2, 4), (1, 0, 4), (1, 2, 0), (2, 2, 4), (2, 0, 0), (3, 2, 4), (4, 4, 4), (4, 0, 4),
-    (5, 2, 4), (8, 2, 4)])
-def test_batched_step_paths(model, W, R, B, gemv, sparse):
-    """B independent rows through the GEMV / MFMA and sparse / dense paths."""
+@pytest.mark.parametrize("B,gemv,sparse,fuse", [
+    (1, 2, 4, 1), (1, 2, 4, 0), (1, 0, 4, 1), (1, 2, 0, 1), (1, 2, 0, 0), (2, 2, 4, 1),
+    (2, 2, 4, 0), (2, 0, 0, 1), (3, 2, 4, 1), (4, 4, 4, 1), (4, 4, 0, 1), (4, 0, 4, 1),
+    (5, 2, 4, 1), (8, 2, 4, 1)])
+def test_batched_step_paths(model, W, R, B, gemv, sparse, fuse):
+    """B independent rows through the GEMV / MFMA, sparse / dense and fused /
+    separate LayerNorm paths."""
     model.set_option(R.OPT_GEMV_MAX_B, gemv)
     model.set_option(R.OPT_SPARSE_MAX_B, sparse)
+    model.set_option(R.OPT_FUSE_LN, fuse)
     try:
         slots = [(5 * i + 3) % NSLOT for i in range(B)]
         fresh(model, slots)
@@ -148,6 +151,7 @@ def test_batched_step_paths(model, W, R, B, gemv, sparse):
     finally:
         model.set_option(R.OPT_GEMV_MAX_B, 2)
         model.set_option(R.OPT_SPARSE_MAX_B, 4)
+        model.set_option(R.OPT_FUSE_LN, 1)
 
 
 def test_prefill_equals_steps_on_gpu(model, R):
@@ -392,7 +396,8 @@ def test_kernel_timing_counts(model, R):
         model.decode_step(dev([0]), dev([1]), logits)
         counts = {R.K_NAMES[k]: R.rwkv7_kernel_timing(model.handle, k)[1] for k in range(8)}
         Lr = S.n_layer
-        assert counts["ln_mix"] == 2 * Lr + 1
+        assert counts["ln_mix"] == 0          # fused into the GEMV prologues at B = 1
+        assert counts["other"] == 2           # validate + embed
         assert counts["proj_in"] == counts["wkv"] == counts["proj_out"] == Lr
         assert counts["cmix_key"] == counts["cmix_value"] == Lr
         assert counts["head"] == 1
