@@ -390,22 +390,30 @@ __global__ __launch_bounds__(1024) void k_cmix_sparse(CmixArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[b][e] = 0.f;
 
-  int p = rg;
-  for (; p + 768 < total; p += 1024) {
-    u32x4 w4[4];
-    float h4[4][B];
+  // all of a thread's rows (up to CMIX_UNROLL per pass) are loaded before
+  // any is used, so a pass costs one memory round trip
+  constexpr int CMIX_UNROLL = 8;
+  for (int p0 = rg; p0 < total; p0 += 256 * CMIX_UNROLL) {
+    u32x4 w4[CMIX_UNROLL];
+    float h4[CMIX_UNROLL][B];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int f = s_idx[p + 256 * u];
-      w4[u] = ld16(a.Wv + (long)f * a.C + cb);
+    for (int u = 0; u < CMIX_UNROLL; ++u) {
+      const int p = p0 + 256 * u;
+      w4[u] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const float z = a.pre[(long)b * a.F + f];
-        h4[u][b] = z > 0.f ? z * z : 0.f;
+      for (int b = 0; b < B; ++b) h4[u][b] = 0.f;
+      if (p < total) {
+        const int f = s_idx[p];
+        w4[u] = ld16(a.Wv + (long)f * a.C + cb);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const float z = a.pre[(long)b * a.F + f];
+          h4[u][b] = z > 0.f ? z * z : 0.f;
+        }
       }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < CMIX_UNROLL; ++u) {
       const half8 hv = __builtin_bit_cast(half8, w4[u]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -413,18 +421,6 @@ __global__ __launch_bounds__(1024) void k_cmix_sparse(CmixArgs a) {
 #pragma unroll
         for (int b = 0; b < B; ++b) acc[b][e] = fmaf(h4[u][b], wf, acc[b][e]);
       }
-    }
-  }
-  for (; p < total; p += 256) {
-    const int f = s_idx[p];
-    const u32x4 w = ld16(a.Wv + (long)f * a.C + cb);
-    const half8 hv = __builtin_bit_cast(half8, w);
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      const float z = a.pre[(long)b * a.F + f];
-      const float h = z > 0.f ? z * z : 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[b][e] = fmaf(h, (float)hv[e], acc[b][e]);
     }
   }
 

@@ -94,9 +94,14 @@ RW_DEV void wkv_prologue(const WkvArgs& a, int b, int h, HeadVecs& hv, float* s_
       else if (e0 < e3) li = a.off_v + (e0 - e2);
       else li = a.off_g + (e0 - e3);
       const half8 w8 = __builtin_bit_cast(half8, wch[q]);
+      // li is a multiple of 8: two 16-byte LDS reads
+      const floatx4 x0 = *reinterpret_cast<const floatx4*>(s_lin + li);
+      const floatx4 x1 = *reinterpret_cast<const floatx4*>(s_lin + li + 4);
       float s = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s = fmaf((float)w8[e], s_lin[li + e], s);
+      for (int e = 0; e < 4; ++e) s = fmaf((float)w8[e], x0[e], s);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = fmaf((float)w8[e + 4], x1[e], s);
       zw += e0 < e1 ? s : 0.f;
       za += (e0 >= e1 && e0 < e2) ? s : 0.f;
       zv += (e0 >= e2 && e0 < e3) ? s : 0.f;
@@ -192,7 +197,7 @@ RW_DEV float wkv_epilogue(const WkvArgs& a, int h, const HeadVecs& hv, float y) 
 template <int NCHK>
 __global__ __launch_bounds__(256) void k_wkv_decode(WkvArgs a) {
   __shared__ HeadVecs hv;
-  __shared__ float s_lin[LIN_MAX];
+  __shared__ __attribute__((aligned(16))) float s_lin[LIN_MAX];
   const int b = blockIdx.x / a.H;
   const int h = blockIdx.x % a.H;
   const int t = threadIdx.x;
@@ -281,7 +286,7 @@ hipError_t launch_wkv_decode(const WkvArgs& a, hipStream_t st) {
 template <int NCHK>
 __global__ __launch_bounds__(256) void k_wkv_prep(WkvArgs a) {
   __shared__ HeadVecs hv;
-  __shared__ float s_lin[LIN_MAX];
+  __shared__ __attribute__((aligned(16))) float s_lin[LIN_MAX];
   const int tk = blockIdx.x / a.H;
   const int h = blockIdx.x % a.H;
   if constexpr (NCHK == 0)
