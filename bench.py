@@ -81,6 +81,38 @@ def step_bytes(s, B, nnz, sparse):
     return L * per_layer + cb["ln_mix"] + cb["head"] + cb["other"] + greedy
 
 
+# ---------------------------------------------------------------- PMC traffic record
+KERNEL_SRC = {"proj_in": "k_proj.hip", "cmix_key": "k_proj.hip", "proj_out": "k_proj.hip",
+              "head": "k_proj.hip", "cmix_value": "k_misc.hip", "wkv": "k_wkv.hip"}
+
+
+def _src_hash(cls):
+    import hashlib
+    h = hashlib.sha256()
+    for f in (KERNEL_SRC[cls], "common.h"):
+        with open(os.path.join(ROOT, "rwkv_linear_attention_decode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic(kernel, cls):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary (profiles/pmc_traffic_*.txt, copy-calibrated), or None when
+    there is no record or the kernel's source changed since it was taken."""
+    import glob
+    import re
+    if cls not in KERNEL_SRC:
+        return None
+    want = _src_hash(cls)
+    for fn in sorted(glob.glob(os.path.join(ROOT, "profiles", "pmc_traffic_*.txt"))):
+        with open(fn) as fh:
+            for line in fh:
+                m = re.match(r'TRAFFIC kernel="([^"]+)" class=(\S+) src=(\S+) bytes=(\d+)', line)
+                if m and m.group(1) == kernel and m.group(2) == cls and m.group(3) == want:
+                    return int(m.group(4))
+    return None
+
+
 # ---------------------------------------------------------------- helpers
 def build_model(R, shape, n_slots, max_B, max_T):
     import synth
@@ -166,12 +198,15 @@ def roofline_b1(R, shape, m, kb, nnz, slot, tok, logits):
     cb = class_bytes(shape, 1, nnz, True)
     dom = max((k for k in kb if k in cb and k != "other"), key=lambda k: kb[k]["ms_per_step"])
     cls = R.K_NAMES.index(dom)
-    layer = shape.n_layer if dom == "head" else 0
-    avg_ms = R.rwkv7_time_kernel(m.handle, m.pool, m.n_slots, slot, tok, logits, cls, layer, 200, m.ws)
+    # a per-layer class is swept over all layers (as inside a step, no weight is re-read
+    # by the next launch); the head has one layer
+    layer, iters = (shape.n_layer, 200) if dom == "head" else (-1, 8)
+    avg_ms = R.rwkv7_time_kernel(m.handle, m.pool, m.n_slots, slot, tok, logits, cls, layer, iters, m.ws)
     gbs = cb[dom] / (avg_ms * 1e-3) / 1e9
+    kname = R.rwkv7_kernel_name(m.handle, cls, 1)
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": R.rwkv7_kernel_name(m.handle, cls, 1), "class": dom,
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": pmc_traffic(kname, dom),
+            "kernel": kname, "class": dom,
             "bytes_per_launch": int(cb[dom]), "avg_launch_us": round(avg_ms * 1e3, 3),
             "launches_per_step": kb[dom]["launches_per_step"]}
 
@@ -229,8 +264,8 @@ def batched(R, args, shape, m, B):
     proj = {}
     for name in ("proj_in", "proj_out", "cmix_key", "cmix_value", "head"):
         cls = R.K_NAMES.index(name)
-        layer = shape.n_layer if name == "head" else 0
-        avg = R.rwkv7_time_kernel(m.handle, m.pool, m.n_slots, slots, tok, logits, cls, layer, 20, m.ws)
+        layer, iters = (shape.n_layer, 20) if name == "head" else (-1, 1)
+        avg = R.rwkv7_time_kernel(m.handle, m.pool, m.n_slots, slots, tok, logits, cls, layer, iters, m.ws)
         tf = fl[name] / (avg * 1e-3) / 1e12
         proj[name] = {"us": round(avg * 1e3, 2), "tflops": round(tf, 1),
                       "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}

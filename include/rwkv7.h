@@ -225,7 +225,10 @@ int rwkv7_kernel_timing(rwkv7_model* model, int32_t kernel_class, double* total_
  * back, the launch(es) that class makes at `layer` (0..n_layer-1; n_layer =
  * the head) of a decode step of B rows with these arguments, between two
  * HIP events on `stream`; synchronise and return the average per iteration
- * in *avg_ms.  Run it after a normal decode step with the same arguments so
+ * in *avg_ms.  `layer` = -1 (per-layer classes only) sweeps the class over
+ * layers 0..n_layer-1 `iters` times instead, so consecutive launches read
+ * different weights as they do inside a step; *avg_ms is then the average
+ * per launch.  Run it after a normal decode step with the same arguments so
  * the workspace holds that step's activations.  It rewrites the listed
  * slots' state and the workspace (the repeated launches are real), so reset
  * those slots before using them again. */

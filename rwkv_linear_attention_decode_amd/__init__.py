@@ -238,7 +238,8 @@ def rwkv7_kernel_name(model: int, cls: int, B: int) -> str:
 
 def rwkv7_time_kernel(model: int, pool, n_slots: int, slot_idx, token_ids, logits_out,
                       kernel_class: int, layer: int, iters: int, ws, stream=None) -> float:
-    """Average ms of one kernel class's launch at ``layer``, replayed ``iters`` times."""
+    """Average ms per launch of one kernel class at ``layer``, replayed ``iters`` times
+    (``layer`` -1: swept over every layer ``iters`` times)."""
     v = ctypes.c_double()
     _check(lib().rwkv7_time_kernel(model, pool.data_ptr(), n_slots, slot_idx.numel(),
                                    _ptr(slot_idx), _ptr(token_ids), _ptr(logits_out), kernel_class,

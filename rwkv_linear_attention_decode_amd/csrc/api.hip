@@ -233,6 +233,7 @@ namespace {
 struct Filter {
   int cls = -1;
   int layer = -1;
+  bool any_layer = false;   // match the class at every layer
   int repeat = 1;
 };
 
@@ -245,7 +246,7 @@ struct Launcher {
   template <class F>
   int run(int cls, const char* what, F&& f) {
     if (flt && flt->cls >= 0) {
-      if (cls != flt->cls || layer != flt->layer) return RWKV7_OK;
+      if (cls != flt->cls || (!flt->any_layer && layer != flt->layer)) return RWKV7_OK;
       for (int i = 0; i < flt->repeat; ++i) {
         hipError_t e = f();
         if (e != hipSuccess) return hip_fail(e, what);
@@ -1036,7 +1037,7 @@ int rwkv7_time_kernel(rwkv7_model* m, void* pool, int64_t n_slots, int32_t B,
   if (!m || !avg_ms) return fail(RWKV7_EINVAL, "null argument");
   if (B < 1 || B > n_slots) return fail(RWKV7_EINVAL, "B out of range");
   if (kernel_class < 0 || kernel_class >= RWKV7_K_COUNT) return fail(RWKV7_EINVAL, "bad kernel class");
-  if (layer < 0 || layer > m->d.L) return fail(RWKV7_EINVAL, "layer outside [0, n_layer]");
+  if (layer < -1 || layer > m->d.L) return fail(RWKV7_EINVAL, "layer outside [-1, n_layer]");
   if (iters < 1) return fail(RWKV7_EINVAL, "iters must be >= 1");
   int rc = check_pool_ws(m, pool, n_slots, ws, ws_bytes, ws_layout(m->d, B, nullptr).bytes);
   if (rc) return rc;
@@ -1052,16 +1053,25 @@ int rwkv7_time_kernel(rwkv7_model* m, void* pool, int64_t n_slots, int32_t B,
                         false, &pre);
     if (rc) return rc;
   }
+  // layer -1: sweep the class over layers 0..n_layer-1, `iters` times, so
+  // every launch streams other weights than the one before it (as in a step)
+  const bool sweep = layer < 0;
+  if (sweep && (kernel_class == RWKV7_K_HEAD || kernel_class == RWKV7_K_OTHER))
+    return fail(RWKV7_EINVAL, "layer -1 needs a per-layer kernel class");
   Filter f;
   f.cls = kernel_class;
   f.layer = layer;
-  f.repeat = iters;
+  f.any_layer = sweep;
+  f.repeat = sweep ? 1 : iters;
+  const int passes = sweep ? iters : 1;
+  const int launches = sweep ? iters * m->d.L : iters;
   hipEvent_t a, b;
   HIP_TRY(hipEventCreate(&a), "hipEventCreate");
   HIP_TRY(hipEventCreate(&b), "hipEventCreate");
   HIP_TRY(hipEventRecord(a, st), "hipEventRecord");
-  rc = enqueue_decode(m, (float*)pool, n_slots, B, slot_idx, token_ids, logits_out, (char*)ws, st,
-                      false, &f);
+  for (int i = 0; i < passes && rc == RWKV7_OK; ++i)
+    rc = enqueue_decode(m, (float*)pool, n_slots, B, slot_idx, token_ids, logits_out, (char*)ws, st,
+                        false, &f);
   HIP_TRY(hipEventRecord(b, st), "hipEventRecord");
   HIP_TRY(hipEventSynchronize(b), "hipEventSynchronize");
   float ms = 0.f;
@@ -1069,7 +1079,7 @@ int rwkv7_time_kernel(rwkv7_model* m, void* pool, int64_t n_slots, int32_t B,
   hipEventDestroy(a);
   hipEventDestroy(b);
   if (rc) return rc;
-  *avg_ms = (double)ms / iters;
+  *avg_ms = (double)ms / launches;
   return RWKV7_OK;
 }
 
@@ -1078,10 +1088,10 @@ const char* rwkv7_kernel_name(const rwkv7_model* m, int32_t cls, int32_t B) {
   const Path p = decode_path(m, B);
   switch (cls) {
     case RWKV7_K_LN_MIX: return "k_ln_mix";
-    case RWKV7_K_PROJ_IN:
-    case RWKV7_K_PROJ_OUT:
-    case RWKV7_K_CMIX_KEY:
-    case RWKV7_K_HEAD: return p.gemv ? gemv_kernel_name(B, m->d.C) : gemm_kernel_name(B);
+    case RWKV7_K_PROJ_IN: return p.gemv ? gemv_kernel_name(B, m->d.C, -1) : gemm_kernel_name(B);
+    case RWKV7_K_PROJ_OUT: return p.gemv ? gemv_kernel_name(B, m->d.C, EPI_RESID) : gemm_kernel_name(B);
+    case RWKV7_K_CMIX_KEY: return p.gemv ? gemv_kernel_name(B, m->d.C, p.sparse ? EPI_PRE : -1) : gemm_kernel_name(B);
+    case RWKV7_K_HEAD: return p.gemv ? gemv_kernel_name(B, m->d.C, EPI_NONE) : gemm_kernel_name(B);
     case RWKV7_K_WKV: return "k_wkv_decode";
     case RWKV7_K_CMIX_VALUE: return p.sparse ? cmix_sparse_kernel_name(B) : gemm_kernel_name(B);
     default: return kClassName[cls];

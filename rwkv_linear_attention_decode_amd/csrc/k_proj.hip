@@ -11,13 +11,19 @@
 //               v_mfma_f32_16x16x32_f16 (fp32 accumulate).
 #include "launch.h"
 
+#include <stdio.h>
+
 // ============================================================== GEMV
 // The fused LayerNorm prologue holds a lane's K slice of every row in VGPRs
 // (B * NCH * 8 floats) and the mixed rows in LDS; it is instantiated only
 // up to this many floats per lane.
 constexpr int kFusedMaxFloats = 80;
 
-template <int B, int LPR, int NCH, int RPW>
+// Epilogue family fixed at compile time (GV_MIXED reads it per segment);
+// it also gives each projection class its own kernel symbol in traces.
+enum : int { GV_MIXED = 0, GV_PRE = 1, GV_RESID = 2, GV_NONE = 3 };
+
+template <int B, int LPR, int NCH, int RPW, int EPK>
 __global__ __launch_bounds__(256) void k_gemv(ProjArgs a) {
   constexpr int GPW = 64 / LPR;
   constexpr int ROWS_WAVE = GPW * RPW;
@@ -173,7 +179,9 @@ __global__ __launch_bounds__(256) void k_gemv(ProjArgs a) {
       const int row = row_base + i;
       if (row < sg.row1) {
         const int n = row - sg.row0;
-        if (sg.epi == EPI_PRE) {
+        const int epi = EPK == GV_PRE ? EPI_PRE : EPK == GV_RESID ? EPI_RESID
+                        : EPK == GV_NONE ? EPI_NONE : sg.epi;
+        if (epi == EPI_PRE) {
           bool any = false;
 #pragma unroll
           for (int b = 0; b < B; ++b) {
@@ -184,7 +192,15 @@ __global__ __launch_bounds__(256) void k_gemv(ProjArgs a) {
           if (sg.mask) sg.mask[n] = any ? 1 : 0;
         } else {
 #pragma unroll
-          for (int b = 0; b < B; ++b) epi_store(sg, n, b, acc[i][b]);
+          for (int b = 0; b < B; ++b) {
+            float* o = (float*)sg.out + (long)b * sg.ld_out + n;
+            if (epi == EPI_RESID)
+              *o += acc[i][b];
+            else if (epi == EPI_NONE)
+              *o = acc[i][b];
+            else
+              epi_store(sg, n, b, acc[i][b]);
+          }
         }
       }
     }
@@ -212,7 +228,22 @@ bool gemv_fused_ok(int B, int K) {
   return B * nch <= kFusedMaxFloats / 8;
 }
 
-#define GEMV_NAME(B, L, N) "k_gemv<" #B "," #L "," #N ">"
+static int gemv_epk(const ProjArgs& a) {
+  int e = a.seg[0].epi;
+  for (int i = 1; i < a.nseg; ++i)
+    if (a.seg[i].epi != e) return GV_MIXED;
+  return e == EPI_PRE ? GV_PRE : e == EPI_RESID ? GV_RESID : e == EPI_NONE ? GV_NONE : GV_MIXED;
+}
+
+template <int B, int LPR, int NCH, int RPW>
+static void gemv_launch_epk(int epk, dim3 grid, hipStream_t st, const ProjArgs& a) {
+  switch (epk) {
+    case GV_PRE: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_PRE>), grid, dim3(256), 0, st, a); break;
+    case GV_RESID: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_RESID>), grid, dim3(256), 0, st, a); break;
+    case GV_NONE: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_NONE>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_MIXED>), grid, dim3(256), 0, st, a); break;
+  }
+}
 
 template <int B>
 static hipError_t gemv_dispatch_b(const ProjArgs& a, int total_rows, hipStream_t st) {
@@ -220,12 +251,13 @@ static hipError_t gemv_dispatch_b(const ProjArgs& a, int total_rows, hipStream_t
   const int K = a.K;
   const int rows_wg = gemv_rows_per_wg(B, K);
   const dim3 grid((total_rows + rows_wg - 1) / rows_wg);
+  const int epk = gemv_epk(a);
   if (K == 256) {
-    hipLaunchKernelGGL((k_gemv<B, 32, 1, RPW>), grid, dim3(256), 0, st, a);
+    gemv_launch_epk<B, 32, 1, RPW>(epk, grid, st, a);
     return hipGetLastError();
   }
   switch (K / 512) {
-#define CASE(n) case n: hipLaunchKernelGGL((k_gemv<B, 64, n, RPW>), grid, dim3(256), 0, st, a); break;
+#define CASE(n) case n: gemv_launch_epk<B, 64, n, RPW>(epk, grid, st, a); break;
     CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
 #undef CASE
     default: return hipErrorInvalidValue;
@@ -243,9 +275,18 @@ hipError_t launch_gemv(const ProjArgs& a, int total_rows, hipStream_t st) {
   }
 }
 
-const char* gemv_kernel_name(int B, int K) {
-  (void)B; (void)K;
-  return "k_gemv";
+// Template arguments as a trace prints them, e.g. "k_gemv<1, 64, 5, 4, 1>".
+const char* gemv_kernel_name(int B, int K, int epi) {
+  static char names[5][9][4][40];
+  if (!gemv_supported(B, K)) return "k_gemv";
+  const int lpr = K == 256 ? 32 : 64;
+  const int nch = K == 256 ? 1 : K / 512;
+  const int epk = epi == EPI_PRE ? GV_PRE : epi == EPI_RESID ? GV_RESID
+                  : epi == EPI_NONE ? GV_NONE : GV_MIXED;
+  char* s = names[B][nch][epk];
+  if (!s[0])
+    snprintf(s, sizeof(names[0][0][0]), "k_gemv<%d, %d, %d, %d, %d>", B, lpr, nch, gemv_rpw(B), epk);
+  return s;
 }
 
 // ============================================================== MFMA GEMM
