@@ -141,6 +141,8 @@ struct Ws {
   unsigned char* mask;
   int *dbg_idx, *dbg_cnt;
   float *q_d, *q_a, *q_b, *q_kt, *q_v, *q_g, *q_bonus, *q_y;
+  float* part;            // split-K partial sums of the MFMA projections
+  int64_t part_floats;
   uint64_t bytes;
 };
 
@@ -180,6 +182,8 @@ Ws ws_layout(const Dims& d, int R, char* base) {
   w.q_g = (float*)take(r * C * 4);
   w.q_y = (float*)take(r * C * 4);
   w.q_bonus = (float*)take(r * d.H * 4);
+  w.part_floats = (int64_t)(r * 8 * C);
+  w.part = (float*)take(r * 8 * C * 4);
   w.bytes = off;
   return w;
 }
@@ -291,8 +295,10 @@ Seg mkseg(int row0, int row1, int epi, const void* act, int ld_act, void* out, i
   return s;
 }
 
-hipError_t proj(bool gemv, ProjArgs& a, int total_rows, hipStream_t st) {
-  return gemv ? launch_gemv(a, total_rows, st) : launch_gemm(a, total_rows, st);
+hipError_t proj(bool gemv, ProjArgs& a, int total_rows, const Ws& w, hipStream_t st) {
+  if (gemv) return launch_gemv(a, total_rows, st);
+  a.part = w.part;
+  return launch_gemm(a, total_rows, w.part_floats, st);
 }
 
 // Input-projection segments: r | k | v | w1 | a1 | v1 | g1 of the fused matrix.
@@ -303,18 +309,22 @@ void proj_in_args(const Dims& d, const LayerPtrs& q, const Ws& w, int R, bool f1
   a.M = R;
   const size_t es = f16 ? 2 : 4;
   auto xq = [&](int i) { return (const void*)((const char*)w.xq + (size_t)i * R * d.C * es); };
+  // the first-stage adapter outputs feed the second-stage MFMA projection:
+  // fp16 on that path
+  auto lin = [&](int col) { return (void*)((char*)w.lin + (size_t)col * es); };
   const int C = d.C;
   int r0 = 3 * C;
   a.seg[0] = mkseg(0, C, EPI_NONE, xq(0), C, w.rkv, 3 * C);
   a.seg[1] = mkseg(C, 2 * C, EPI_NONE, xq(2), C, w.rkv + C, 3 * C);
   a.seg[2] = mkseg(2 * C, 3 * C, EPI_NONE, xq(3), C, w.rkv + 2 * C, 3 * C);
-  a.seg[3] = mkseg(r0, r0 + d.Dwp, EPI_TANH, xq(1), C, w.lin, d.Lin);
+  a.seg[3] = mkseg(r0, r0 + d.Dwp, EPI_TANH, xq(1), C, lin(0), d.Lin);
   r0 += d.Dwp;
-  a.seg[4] = mkseg(r0, r0 + d.Dap, EPI_NONE, xq(4), C, w.lin + d.Dwp, d.Lin);
+  a.seg[4] = mkseg(r0, r0 + d.Dap, EPI_NONE, xq(4), C, lin(d.Dwp), d.Lin);
   r0 += d.Dap;
-  a.seg[5] = mkseg(r0, r0 + d.Dvp, EPI_NONE, xq(3), C, w.lin + d.Dwp + d.Dap, d.Lin);
+  a.seg[5] = mkseg(r0, r0 + d.Dvp, EPI_NONE, xq(3), C, lin(d.Dwp + d.Dap), d.Lin);
   r0 += d.Dvp;
-  a.seg[6] = mkseg(r0, r0 + d.Dgp, EPI_SIGMOID, xq(5), C, w.lin + d.Dwp + d.Dap + d.Dvp, d.Lin);
+  a.seg[6] = mkseg(r0, r0 + d.Dgp, EPI_SIGMOID, xq(5), C, lin(d.Dwp + d.Dap + d.Dvp), d.Lin);
+  for (int i = 3; i < 7; ++i) a.seg[i].out_f16 = f16 ? 1 : 0;
   a.nseg = 7;
 }
 
@@ -391,8 +401,9 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
   Launcher L{m, st, timing, flt};
   const Ws w = ws_layout(d, B, ws);
   const Path path = decode_path(m, B);
-  // activations stay fp32 on both paths (the MFMA kernel splits them itself)
-  const bool f16 = false;
+  // GEMV path: fp32 activations; MFMA path: every projection input is
+  // written in fp16 by its producer (the residual stream stays fp32)
+  const bool f16 = !path.gemv;
   const int C = d.C;
   int64_t* counters = (int64_t*)((char*)pool + align_up((uint64_t)n_slots * d.slot_floats * 4));
 
@@ -427,7 +438,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
     } else {
       RUN(RWKV7_K_LN_MIX, "ln_mix(tmix)", launch_ln_mix(la, st));
     }
-    RUN(RWKV7_K_PROJ_IN, "proj_in", proj(path.gemv, pa, d.Nin, st));
+    RUN(RWKV7_K_PROJ_IN, "proj_in", proj(path.gemv, pa, d.Nin, w, st));
 
     WkvArgs wa = wkv_args(m, l, pool, n_slots, w, B, f16);
     wa.u_att = path.fused ? w.u_att : nullptr;
@@ -435,7 +446,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
       // many rows: the adapter outputs as one MFMA projection, WKV reads them
       ProjArgs pl;
       lora_args(d, q, w, B, pl);
-      RUN(RWKV7_K_PROJ_IN, "adapters", launch_gemm(pl, 4 * C, st));
+      RUN(RWKV7_K_PROJ_IN, "adapters", proj(false, pl, 4 * C, w, st));
       wa.lo = w.lo;
     }
     RUN(RWKV7_K_WKV, "wkv", launch_wkv_decode(wa, st));
@@ -444,7 +455,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
     memset(&po, 0, sizeof po);
     po.W = q.w_o; po.K = C; po.M = B; po.nseg = 1;
     po.seg[0] = mkseg(0, C, EPI_RESID, w.yg, C, w.x, C);
-    RUN(RWKV7_K_PROJ_OUT, "proj_out", proj(path.gemv, po, C, st));
+    RUN(RWKV7_K_PROJ_OUT, "proj_out", proj(path.gemv, po, C, w, st));
 
     ProjArgs pk;
     memset(&pk, 0, sizeof pk);
@@ -453,6 +464,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
       pk.seg[0] = mkseg(0, d.F, EPI_PRE, w.xk, C, w.pre, d.F, q.b_key, w.mask);
     else
       pk.seg[0] = mkseg(0, d.F, EPI_RELU2, w.xk, C, w.pre, d.F, q.b_key);
+    if (!path.sparse) pk.seg[0].out_f16 = 1;   // the dense (MFMA) value projection's input
     if (path.fused) {
       pk.ln = LnPro{w.x, q.ln2_w, q.ln2_b, pool, d.slot_floats, n_slots, lo + C, w.slots, w.u_ffn, LNP_MIX, 0};
       pk.seg[0].mix = q.mu_k;
@@ -464,7 +476,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
       lc.out = w.xk; lc.out_q_stride = 0;
       RUN(RWKV7_K_LN_MIX, "ln_mix(cmix)", launch_ln_mix(lc, st));
     }
-    RUN(RWKV7_K_CMIX_KEY, "cmix_key", proj(path.gemv, pk, d.F, st));
+    RUN(RWKV7_K_CMIX_KEY, "cmix_key", proj(path.gemv, pk, d.F, w, st));
 
     if (path.sparse) {
       CmixArgs ca;
@@ -480,7 +492,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
       memset(&pv, 0, sizeof pv);
       pv.W = q.w_val_km; pv.K = d.F; pv.M = B; pv.nseg = 1;
       pv.seg[0] = mkseg(0, C, EPI_RESID, w.pre, d.F, w.x, C);
-      RUN(RWKV7_K_CMIX_VALUE, "cmix_value", launch_gemm(pv, C, st));
+      RUN(RWKV7_K_CMIX_VALUE, "cmix_value", proj(false, pv, C, w, st));
       if (path.fused) {
         CommitArgs ca{w.u_ffn, pool, d.slot_floats, n_slots, lo + C, w.slots, B, C};
         RUN(RWKV7_K_OTHER, "commit shift", launch_commit_shift(ca, st));
@@ -504,7 +516,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
     lo.out = w.xo; lo.out_f16 = f16; lo.out_q_stride = 0;
     RUN(RWKV7_K_LN_MIX, "ln_out", launch_ln_mix(lo, st));
   }
-  RUN(RWKV7_K_HEAD, "head", proj(path.gemv, ph, d.V, st));
+  RUN(RWKV7_K_HEAD, "head", proj(path.gemv, ph, d.V, w, st));
   return RWKV7_OK;
 }
 
@@ -533,18 +545,18 @@ int enqueue_prefill_chunk(rwkv7_model* m, float* pool, int64_t n_slots, int slot
     la.pool = pool; la.slot_stride = d.slot_floats; la.n_slots = n_slots; la.shift_off = lo;
     la.seq_slot = slot; la.shift_tmp = w.shift_tmp;
     la.mu = q.mu6; la.nq = 6;
-    la.out = w.xq; la.out_f16 = 0; la.out_q_stride = (int64_t)T * C;
+    la.out = w.xq; la.out_f16 = 1; la.out_q_stride = (int64_t)T * C;
     RUN(RWKV7_K_LN_MIX, "ln_mix(tmix)", launch_ln_mix(la, st));
     RUN(RWKV7_K_OTHER, "shift copy", launch_copy_f32(slot_base + lo, w.shift_tmp, C, st));
 
     ProjArgs pa;
-    proj_in_args(d, q, w, T, false, pa);
-    RUN(RWKV7_K_PROJ_IN, "proj_in", launch_gemm(pa, d.Nin, st));
+    proj_in_args(d, q, w, T, true, pa);
+    RUN(RWKV7_K_PROJ_IN, "proj_in", proj(false, pa, d.Nin, w, st));
 
     ProjArgs pl;
     lora_args(d, q, w, T, pl);
-    RUN(RWKV7_K_PROJ_IN, "adapters", launch_gemm(pl, 4 * C, st));
-    WkvArgs wa = wkv_args(m, l, pool, n_slots, w, T, false);
+    RUN(RWKV7_K_PROJ_IN, "adapters", proj(false, pl, 4 * C, w, st));
+    WkvArgs wa = wkv_args(m, l, pool, n_slots, w, T, true);
     wa.seq_slot = slot;
     wa.lo = w.lo;
     RUN(RWKV7_K_WKV, "wkv_prep", launch_wkv_prep(wa, st));
@@ -555,7 +567,7 @@ int enqueue_prefill_chunk(rwkv7_model* m, float* pool, int64_t n_slots, int slot
     memset(&po, 0, sizeof po);
     po.W = q.w_o; po.K = C; po.M = T; po.nseg = 1;
     po.seg[0] = mkseg(0, C, EPI_RESID, w.yg, C, w.x, C);
-    RUN(RWKV7_K_PROJ_OUT, "proj_out", launch_gemm(po, C, st));
+    RUN(RWKV7_K_PROJ_OUT, "proj_out", proj(false, po, C, w, st));
 
     LnMixArgs lc = la;
     lc.g = q.ln2_w; lc.b = q.ln2_b;
@@ -569,13 +581,14 @@ int enqueue_prefill_chunk(rwkv7_model* m, float* pool, int64_t n_slots, int slot
     memset(&pk, 0, sizeof pk);
     pk.W = q.w_key; pk.K = C; pk.M = T; pk.nseg = 1;
     pk.seg[0] = mkseg(0, d.F, EPI_RELU2, w.xk, C, w.pre, d.F, q.b_key);
-    RUN(RWKV7_K_CMIX_KEY, "cmix_key", launch_gemm(pk, d.F, st));
+    pk.seg[0].out_f16 = 1;
+    RUN(RWKV7_K_CMIX_KEY, "cmix_key", proj(false, pk, d.F, w, st));
 
     ProjArgs pv;
     memset(&pv, 0, sizeof pv);
     pv.W = q.w_val_km; pv.K = d.F; pv.M = T; pv.nseg = 1;
     pv.seg[0] = mkseg(0, C, EPI_RESID, w.pre, d.F, w.x, C);
-    RUN(RWKV7_K_CMIX_VALUE, "cmix_value", launch_gemm(pv, C, st));
+    RUN(RWKV7_K_CMIX_VALUE, "cmix_value", proj(false, pv, C, w, st));
   }
   return RWKV7_OK;
 }

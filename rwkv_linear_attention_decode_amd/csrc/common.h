@@ -50,7 +50,7 @@ struct Seg {
   int epi;
   int ld_act;
   int ld_out;
-  int pad_;
+  int out_f16;       // store the epilogue result as fp16 (the next MFMA projection's input)
   const void* act;
   void* out;
   const float* aux;
@@ -88,9 +88,11 @@ struct ProjArgs {
   int K;
   int M;             // activation rows (batch rows / tokens)
   int nseg;
-  int n_tiles;       // MFMA path: number of 64-column tiles
   int m_tiles;       // MFMA path: number of M tiles
-  int pad_;
+  int split;         // MFMA path: K ranges per tile (1 = the epilogue runs in the GEMM)
+  int total_rows;    // MFMA path: output columns over all segments (partial-sum row length)
+  float* part;       // MFMA path, split > 1: fp32 partial sums [split][M][total_rows]
+  int tile0[MAX_SEGS + 1];  // MFMA path: first column tile of each segment (prefix sums)
   LnPro ln;
   Seg seg[MAX_SEGS];
 };
@@ -137,40 +139,29 @@ RW_DEV Seg pick_seg(const ProjArgs& a, int row) {
 // Apply the epilogue of segment `s` to output column n (relative to the
 // segment), activation row m.
 RW_DEV void epi_store(const Seg& s, int n, int m, float v) {
+  const long i = (long)m * s.ld_out + n;
+  float r;
   switch (s.epi) {
-    case EPI_NONE:
-      ((float*)s.out)[(long)m * s.ld_out + n] = v;
-      break;
-    case EPI_TANH:
-      ((float*)s.out)[(long)m * s.ld_out + n] = tanhf(v);
-      break;
-    case EPI_SIGMOID:
-      ((float*)s.out)[(long)m * s.ld_out + n] = sigmoidf_(v);
-      break;
-    case EPI_RESID: {
-      float* p = (float*)s.out + (long)m * s.ld_out + n;
-      *p = *p + v;
-      break;
-    }
-    case EPI_PRE:
-      ((float*)s.out)[(long)m * s.ld_out + n] = v + s.aux[n];
-      break;
+    case EPI_TANH: r = tanhf(v); break;
+    case EPI_SIGMOID: r = sigmoidf_(v); break;
+    case EPI_RESID: r = (s.out_f16 ? (float)((half_t*)s.out)[i] : ((float*)s.out)[i]) + v; break;
+    case EPI_PRE: r = v + s.aux[n]; break;
     case EPI_RELU2: {
-      float z = v + s.aux[n];
-      z = z > 0.0f ? z * z : 0.0f;
-      ((float*)s.out)[(long)m * s.ld_out + n] = z;
+      const float z = v + s.aux[n];
+      r = z > 0.0f ? z * z : 0.0f;
       break;
     }
     case EPI_DECAY: {
       // exp(-exp(-softplus(-z) - 0.5)) = exp(-e^{-1/2} sigmoid(z))
       const float sg = 1.0f / (1.0f + expf(-(v + s.aux[n])));
-      ((float*)s.out)[(long)m * s.ld_out + n] = expf(-0.60653065971263342f * sg);
+      r = expf(-0.60653065971263342f * sg);
       break;
     }
-    case EPI_SIGB:
-      ((float*)s.out)[(long)m * s.ld_out + n] = 1.0f / (1.0f + expf(-(v + s.aux[n])));
-      break;
-    default:
-      break;
+    case EPI_SIGB: r = 1.0f / (1.0f + expf(-(v + s.aux[n]))); break;
+    default: r = v; break;
   }
+  if (s.out_f16)
+    ((half_t*)s.out)[i] = (half_t)r;
+  else
+    ((float*)s.out)[i] = r;
 }

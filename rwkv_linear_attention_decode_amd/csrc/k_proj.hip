@@ -6,9 +6,10 @@
 //   * k_gemv  : B <= 4 rows, fp32 activations held in VGPRs, each weight row
 //               reduced by one 64-lane (or 32-lane) group with 16-byte
 //               non-temporal loads; no split-K partials, so no second pass.
-//   * k_gemm  : larger B and prefill, fp16 activations staged in LDS, fp16
-//               weights streamed straight from HBM into the B operand of
-//               v_mfma_f32_16x16x32_f16 (fp32 accumulate).
+//   * k_mm    : larger B and prefill, register-blocked MFMA GEMM on fp16
+//               activations and weights staged through LDS
+//               (v_mfma_f32_16x16x32_f16, fp32 accumulate), split over K when
+//               the output has too few tiles to fill the chip.
 #include "launch.h"
 
 #include <stdio.h>
@@ -290,135 +291,185 @@ const char* gemv_kernel_name(int B, int K, int epi) {
 }
 
 // ============================================================== MFMA GEMM
-// Workgroup tile: MT activation rows x 64 output columns; 4 waves, each
-// owning 16 columns.  K is consumed in chunks of 128: lane l (column l%16,
-// group g = l/16) holds 64 contiguous bytes of its weight row, k in
-// [32g, 32g+32) of the chunk, used as four 8-wide MFMA K slices.  The A
-// operand is read from LDS with the same k mapping, so the product sums
-// over every k exactly once.
+// out[m][n] = epi(sum_k A[m][k] W[n][k]) with fp16 A (activations, k
+// contiguous) and fp16 W (weights, k contiguous), fp32 accumulation on
+// v_mfma_f32_16x16x32_f16.
 //
-// Activations arrive in fp32 and are split while staged into LDS as
-// a = hi + lo * 2^-12 with hi = fp16(a) and lo = fp16((a - hi) * 2^12); each
-// weight fragment meets both planes (two MFMAs into two accumulators, the
-// second scaled back at the end), so the product keeps ~22 bits of the
-// activation while the weights (exact fp16 values) stream once.  The 2^12
-// keeps the residual plane out of the fp16 subnormal range.  A single fp16
-// rounding of the activations loses too much for deep models whose layers
-// amplify relative perturbations.
-constexpr float LO_SCALE = 4096.0f;
-constexpr float LO_UNSCALE = 1.0f / 4096.0f;
-template <int MT>
-__global__ __launch_bounds__(256) void k_gemm(ProjArgs a) {
-  constexpr int KC = 128;
-  constexpr int MT16 = MT / 16;
-  constexpr int LDA = KC + 8;  // halves per LDS row (16-byte skew)
-  __shared__ __attribute__((aligned(16))) half_t Ah[2][MT][LDA];
-  __shared__ __attribute__((aligned(16))) half_t Al[2][MT][LDA];
+// Workgroup: 4 waves as 2 x 2, each owning a (16 TM) x (16 TN) block of the
+// (32 TM) x (32 TN) tile, TM x TN accumulators of 16 x 16.  K advances in
+// stages of 64: the next stage's A and W tiles are loaded into registers
+// (16-byte loads, one per thread per 8 x 16-byte chunk row) while the
+// current stage is multiplied out of LDS, then written to the other LDS
+// buffer; one barrier per stage.  In the MFMA operand layout lane l holds
+// row l % 16 and the 8 k values 8 (l / 16) .. +7 of a 32-wide k slice, for
+// both operands, so A and W fragments are plain 16-byte LDS reads of
+// k-contiguous rows (row stride 72 halves: 16 lanes of one read hit 64
+// distinct banks).
+//
+// Column tiles never straddle a segment (each segment has its own
+// activation and epilogue).  With split > 1 each tile's stages are divided
+// into `split` contiguous ranges whose fp32 partial sums a second kernel adds
+// in a fixed order before applying the epilogue, so results do not depend
+// on scheduling.
+constexpr int MM_KS = 64;          // k per stage
+constexpr int MM_LDS = MM_KS + 8;  // halves per LDS row
 
-  // XCD-aware tile order: consecutive tiles (same column tile, successive
-  // M tiles) go to the same XCD so its L2 serves the repeated weight reads.
-  const int total = a.n_tiles * a.m_tiles;
+template <int TM, int TN>
+__global__ __launch_bounds__(256) void k_mm(ProjArgs a) {
+  constexpr int MT = 32 * TM, NT = 32 * TN;
+  constexpr int ACH = MT * 8 / 256;   // 16-byte A chunks per thread and stage
+  constexpr int BCH = NT * 8 / 256;   // 16-byte W chunks per thread and stage
+  __shared__ __attribute__((aligned(16))) half_t As[2][MT][MM_LDS];
+  __shared__ __attribute__((aligned(16))) half_t Bs[2][NT][MM_LDS];
+
+  // XCD-aware order: consecutive work items (same column tile, successive
+  // M tiles and K ranges) go to the same XCD, whose L2 then serves the
+  // repeated weight and activation reads.
+  const int n_tiles = a.tile0[a.nseg];
+  const int total = n_tiles * a.m_tiles * a.split;
   const int per_xcd = (total + 7) / 8;
   const int lin = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (lin >= total) return;
-  const int n_tile = lin / a.m_tiles;
-  const int m_tile = lin % a.m_tiles;
-  const int n0 = n_tile * 64;
+  const int ks_id = lin % a.split;
+  const int m_tile = (lin / a.split) % a.m_tiles;
+  const int n_tile = lin / (a.split * a.m_tiles);
+  // segment of this column tile (selects, not a dynamic index into the arguments)
+  Seg sg = a.seg[0];
+  int t0 = 0;
+#pragma unroll
+  for (int i = 1; i < MAX_SEGS; ++i)
+    if (i < a.nseg && n_tile >= a.tile0[i]) {
+      sg = a.seg[i];
+      t0 = a.tile0[i];
+    }
+  const int n0 = sg.row0 + (n_tile - t0) * NT;   // first output column (global)
   const int m0 = m_tile * MT;
-  const Seg sg = pick_seg(a, n0);
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int g = lane >> 4;
-  const int col = n0 + wave * 16 + (lane & 15);
-  const bool col_ok = col < sg.row1;
-  // a block may carry its own matrix (rows relative to the block) and K
   const bool own = sg.W != nullptr;
   const int K = own ? sg.K : a.K;
-  const long wr = own ? (col_ok ? col - sg.row0 : 0) : (col_ok ? col : sg.row0);
-  const half_t* wrow = (own ? sg.W : a.W) + wr * K + 32 * g;
-  const float* X = reinterpret_cast<const float*>(sg.act) + sg.act_off;
-  const int nk = (K + KC - 1) / KC;   // K is a multiple of 32; the last chunk may be partial
+  const half_t* Wb = own ? sg.W - (long)sg.row0 * K : a.W;  // indexed by global column
+  const half_t* A = reinterpret_cast<const half_t*>(sg.act) + sg.act_off;
+  const int lda = sg.ld_act;
+  const int nst = (K + MM_KS - 1) / MM_KS;
+  const int st0 = (int)((long)nst * ks_id / a.split);
+  const int st1 = (int)((long)nst * (ks_id + 1) / a.split);
 
-  floatx4 acc[MT16], accl[MT16];
-#pragma unroll
-  for (int t = 0; t < MT16; ++t) {
-    acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-    accl[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm0 = (wave >> 1) * 16 * TM;
+  const int wn0 = (wave & 1) * 16 * TN;
+  const int fr = lane & 15;          // fragment row / column
+  const int fk = (lane >> 4) * 8;    // fragment k offset inside a 32-wide slice
 
-  auto load_w = [&](int kc, u32x4* dst) {
-    const half_t* p = wrow + kc * KC;
-    const bool ok = kc * KC + 32 * g < K;
+  floatx4 acc[TM][TN];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) dst[s] = ok ? ld16_nt(p + 8 * s) : u32x4{0u, 0u, 0u, 0u};
-  };
-  // MT rows x 128 fp32 = MT*32 float4; 256 threads -> MT/8 float4 each.
-  auto load_a = [&](int kc, int buf) {
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int p = 0; p < MT / 8; ++p) {
-      const int idx = p * 256 + threadIdx.x;
-      const int r = idx >> 5;
-      const int c = (idx & 31) * 4;
+    for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 ra[ACH], rb[BCH];
+  auto load = [&](int stg) {
+    const int k0 = stg * MM_KS;
+#pragma unroll
+    for (int p = 0; p < ACH; ++p) {
+      const int c = p * 256 + tid;
+      const int r = c >> 3, kc = (c & 7) * 8;
       const int m = m0 + r;
-      floatx4 v = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (m < a.M && kc * KC + c < K) v = ldf4(X + (long)m * sg.ld_act + kc * KC + c);
-      half4 hi, lo;
+      ra[p] = (m < a.M && k0 + kc < K) ? ld16(A + (long)m * lda + k0 + kc) : u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hi[e] = (half_t)v[e];
-        lo[e] = (half_t)((v[e] - (float)hi[e]) * LO_SCALE);
-      }
-      *reinterpret_cast<half4*>(&Ah[buf][r][c]) = hi;
-      *reinterpret_cast<half4*>(&Al[buf][r][c]) = lo;
+    for (int p = 0; p < BCH; ++p) {
+      const int c = p * 256 + tid;
+      const int r = c >> 3, kc = (c & 7) * 8;
+      const int n = n0 + r;
+      rb[p] = (n < sg.row1 && k0 + kc < K) ? ld16(Wb + (long)n * K + k0 + kc) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < ACH; ++p) {
+      const int c = p * 256 + tid;
+      st16(&As[buf][c >> 3][(c & 7) * 8], ra[p]);
+    }
+#pragma unroll
+    for (int p = 0; p < BCH; ++p) {
+      const int c = p * 256 + tid;
+      st16(&Bs[buf][c >> 3][(c & 7) * 8], rb[p]);
     }
   };
 
-  u32x4 wf[4], wn[4];
-  load_w(0, wf);
-  load_a(0, 0);
-  __syncthreads();
-  int buf = 0;
-  for (int kc = 0; kc < nk; ++kc) {
-    if (kc + 1 < nk) {
-      load_w(kc + 1, wn);
-      load_a(kc + 1, buf ^ 1);
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const half8 bv = __builtin_bit_cast(half8, wf[s]);
-#pragma unroll
-      for (int t = 0; t < MT16; ++t) {
-        const int r = t * 16 + (lane & 15);
-        const int k = 32 * g + 8 * s;
-        const half8 ah = *reinterpret_cast<const half8*>(&Ah[buf][r][k]);
-        const half8 al = *reinterpret_cast<const half8*>(&Al[buf][r][k]);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bv, acc[t], 0, 0, 0);
-        accl[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bv, accl[t], 0, 0, 0);
-      }
-    }
+  if (st0 < st1) {
+    load(st0);
+    store(0);
     __syncthreads();
+  }
+  int buf = 0;
+  for (int stg = st0; stg < st1; ++stg) {
+    const bool more = stg + 1 < st1;
+    if (more) load(stg + 1);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) wf[s] = wn[s];
+    for (int kk = 0; kk < MM_KS; kk += 32) {
+      half8 af[TM], bf[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const half8*>(&As[buf][wm0 + 16 * i + fr][kk + fk]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bf[j] = *reinterpret_cast<const half8*>(&Bs[buf][wn0 + 16 * j + fr][kk + fk]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) store(buf ^ 1);
+    __syncthreads();
     buf ^= 1;
   }
 
-  if (!col_ok) return;
-  const int n = col - sg.row0;
+  // D layout: lane l holds rows 4 (l / 16) + e, column l % 16 of each 16 x 16 block
+  const int er = (lane >> 4) * 4;
+  if (a.split > 1) {
+    float* P = a.part + (long)ks_id * a.M * a.total_rows;
 #pragma unroll
-  for (int t = 0; t < MT16; ++t)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + t * 16 + 4 * g + i;
-      if (m < a.M) {
-        const float v = acc[t][i] + accl[t][i] * LO_UNSCALE;
-        if (sg.epi == EPI_PRE) {
-          ((float*)sg.out)[(long)m * sg.ld_out + n] = v + sg.aux[n];
-        } else {
-          epi_store(sg, n, m, v);
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn0 + 16 * j + fr;
+        if (n >= sg.row1) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = m0 + wm0 + 16 * i + er + e;
+          if (m < a.M) P[(long)m * a.total_rows + n] = acc[i][j][e];
         }
       }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + wn0 + 16 * j + fr;
+      if (n >= sg.row1) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + wm0 + 16 * i + er + e;
+        if (m < a.M) epi_store(sg, n - sg.row0, m, acc[i][j][e]);
+      }
     }
+}
+
+// Fixed-order sum of the split-K partials, then the segment's epilogue.
+__global__ __launch_bounds__(256) void k_mm_reduce(ProjArgs a) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  const long total = (long)a.M * a.total_rows;
+  if (idx >= total) return;
+  const int m = (int)(idx / a.total_rows);
+  const int n = (int)(idx % a.total_rows);
+  float v = 0.f;
+  for (int s = 0; s < a.split; ++s) v += a.part[(long)s * total + idx];
+  const Seg sg = pick_seg(a, n);
+  if (n < sg.row1) epi_store(sg, n - sg.row0, m, v);
 }
 
 // Union mask of the sparse path when the key projection runs on MFMA:
@@ -431,24 +482,57 @@ __global__ void k_pre_mask(const float* pre, int ld, int M, int F, unsigned char
   mask[f] = any ? 1 : 0;
 }
 
-hipError_t launch_gemm(ProjArgs a, int total_rows, hipStream_t st) {
+static int mm_tm(int M) { return M <= 32 ? 1 : (M <= 64 ? 2 : 4); }
+static constexpr int MM_TN = 4;
+
+// Tile plan of a launch: column tiles per segment, M tiles, K split.
+int mm_plan(ProjArgs& a, int total_rows, int64_t part_floats) {
+  const int NT = 32 * MM_TN;
+  const int MT = 32 * mm_tm(a.M);
+  a.tile0[0] = 0;
+  int max_nst = 1;
   for (int i = 0; i < a.nseg; ++i) {
-    const int K = a.seg[i].W ? a.seg[i].K : a.K;
-    if (K % 32 != 0 || K <= 0) return hipErrorInvalidValue;
+    const Seg& s = a.seg[i];
+    const int K = s.W ? s.K : a.K;
+    if (K % 32 != 0 || K <= 0) return -1;
+    if (s.row1 <= s.row0) return -1;
+    a.tile0[i + 1] = a.tile0[i] + (s.row1 - s.row0 + NT - 1) / NT;
+    max_nst = max_nst > (K + MM_KS - 1) / MM_KS ? max_nst : (K + MM_KS - 1) / MM_KS;
   }
-  a.n_tiles = (total_rows + 63) / 64;
-  int mt = a.M <= 16 ? 16 : (a.M <= 32 ? 32 : 64);
-  a.m_tiles = (a.M + mt - 1) / mt;
-  const int total = a.n_tiles * a.m_tiles;
-  const dim3 grid(((total + 7) / 8) * 8);
-  if (mt == 16)
-    hipLaunchKernelGGL((k_gemm<16>), grid, dim3(256), 0, st, a);
-  else if (mt == 32)
-    hipLaunchKernelGGL((k_gemm<32>), grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((k_gemm<64>), grid, dim3(256), 0, st, a);
+  for (int i = a.nseg + 1; i <= MAX_SEGS; ++i) a.tile0[i] = a.tile0[a.nseg];
+  a.m_tiles = (a.M + MT - 1) / MT;
+  a.total_rows = total_rows;
+  // Few tiles (N = C projections at moderate M): split K so that about one
+  // workgroup per CU has work, keeping at least 4 stages per range.
+  const int tiles = a.tile0[a.nseg] * a.m_tiles;
+  int split = 1;
+  if (a.part && tiles < 192) {
+    split = (256 + tiles - 1) / tiles;
+    if (split > max_nst / 4) split = max_nst / 4;
+    while (split > 1 && (int64_t)split * a.M * total_rows > part_floats) --split;
+    if (split < 1) split = 1;
+  }
+  a.split = split;
+  return tiles * split;
+}
+
+hipError_t launch_gemm(ProjArgs a, int total_rows, int64_t part_floats, hipStream_t st) {
+  const int items = mm_plan(a, total_rows, part_floats);
+  if (items < 0) return hipErrorInvalidValue;
+  const dim3 grid(((items + 7) / 8) * 8);
+  switch (mm_tm(a.M)) {
+    case 1: hipLaunchKernelGGL((k_mm<1, MM_TN>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_mm<2, MM_TN>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((k_mm<4, MM_TN>), grid, dim3(256), 0, st, a); break;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.split > 1) {
+    const long n = (long)a.M * total_rows;
+    hipLaunchKernelGGL(k_mm_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   for (int i = 0; i < a.nseg; ++i) {
     const Seg& s = a.seg[i];
     if (s.epi == EPI_PRE && s.mask) {
@@ -462,7 +546,11 @@ hipError_t launch_gemm(ProjArgs a, int total_rows, hipStream_t st) {
   return hipSuccess;
 }
 
+// Template arguments as a trace prints them, e.g. "k_mm<4, 4>".
 const char* gemm_kernel_name(int M) {
-  (void)M;
-  return "k_gemm";
+  switch (mm_tm(M)) {
+    case 1: return "k_mm<1, 4>";
+    case 2: return "k_mm<2, 4>";
+    default: return "k_mm<4, 4>";
+  }
 }

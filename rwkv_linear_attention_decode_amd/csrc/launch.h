@@ -9,7 +9,9 @@
 int gemv_rows_per_wg(int B, int K);
 bool gemv_supported(int B, int K);
 hipError_t launch_gemv(const ProjArgs& a, int total_rows, hipStream_t st);
-hipError_t launch_gemm(ProjArgs a, int total_rows, hipStream_t st);
+// MFMA path: A (segment activations) fp16.  `part_floats` bounds the split-K
+// partial buffer a.part (nullptr: no split).
+hipError_t launch_gemm(ProjArgs a, int total_rows, int64_t part_floats, hipStream_t st);
 // `epi`: the epilogue shared by every segment of the launch, or -1 when mixed
 const char* gemv_kernel_name(int B, int K, int epi);
 const char* gemm_kernel_name(int M);
