@@ -105,6 +105,23 @@ RW_DEV float wave_sum(float v) {
   return v;
 }
 
+// Sum over each aligned group of 16 lanes, every lane of the group gets the
+// same total.  DPP lane moves (VALU): quad_perm [1,0,3,2] and [2,3,0,1],
+// then row_half_mirror and row_mirror; each step adds a lane's value to its
+// partner's, and partners compute the same commutative sum.
+template <int CTRL>
+RW_DEV float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, false));
+}
+RW_DEV float sum16(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x140>(v);  // row_mirror
+  return v;
+}
+
 RW_DEV float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -23,7 +23,7 @@
 
 constexpr int LIN_MAX = 1024;
 
-struct HeadVecs {
+struct __attribute__((aligned(16))) HeadVecs {
   float r[64], k[64], v[64], d[64], al[64], vg[64], g[64], a[64], bb[64], kt[64], y[64];
   float bonus;
 };
@@ -182,42 +182,42 @@ RW_DEV void wkv_prologue_lean(const WkvArgs& a, int b, int h, HeadVecs& hv) {
   __syncthreads();
 }
 
-// GroupNorm over the head's 64 readouts + bonus * v, times the gate (wave 0).
-RW_DEV float wkv_epilogue(const WkvArgs& a, int h, const HeadVecs& hv, float y) {
+// GroupNorm over the head's 64 readouts + bonus * v, times the gate (wave 0);
+// gw, gb: this lane's GroupNorm weight and bias (loaded early by the caller).
+RW_DEV float wkv_epilogue(const HeadVecs& hv, float y, float gw, float gb) {
   const int lane = threadIdx.x & 63;
-  const int c = h * 64 + lane;
   const float mean = wave_sum(y) * (1.0f / 64.0f);
   const float dlt = y - mean;
   const float var = wave_sum(dlt * dlt) * (1.0f / 64.0f);
-  float o = dlt / sqrtf(var + 64e-5f) * a.lnx_w[c] + a.lnx_b[c];
+  float o = dlt / sqrtf(var + 64e-5f) * gw + gb;
   o += hv.bonus * hv.v[lane];
   return o * hv.g[lane];
 }
 
+// State layout in the workgroup: the head's 64 x 64 state is 1024 float4;
+// thread t holds float4 number 256 q + t (q = 0..3), i.e. value rows
+// 16 q + t / 16 and key columns 4 (t % 16) .. +3.  Each load or store
+// instruction of a wave then covers 1 KB of contiguous memory, and the row
+// sums (S a and the readout S r) close over the 16 lanes sharing a row.
 template <int NCHK>
 __global__ __launch_bounds__(256) void k_wkv_decode(WkvArgs a) {
   __shared__ HeadVecs hv;
-  __shared__ __attribute__((aligned(16))) float s_lin[LIN_MAX];
+  __shared__ __attribute__((aligned(16))) float s_lin[NCHK ? LIN_MAX : 4];
   const int b = blockIdx.x / a.H;
   const int h = blockIdx.x % a.H;
   const int t = threadIdx.x;
-  const int i = t >> 2;
-  const int j0 = (t & 3) * 16;
   const int slot = a.slots[b];
   const bool ok = slot >= 0 && slot < a.n_slots;
   float* base = ok ? a.pool + (long)slot * a.slot_stride + a.layer_off : nullptr;
-  float* S = ok ? base + 2L * a.C + (long)h * 4096 + i * 64 + j0 : nullptr;
+  float* S = ok ? base + 2L * a.C + (long)h * 4096 + 4 * t : nullptr;
   // the state does not depend on this token: start its loads first
-  float s[16];
-  if (S) {
+  floatx4 s[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const floatx4 v4 = ldf4_nt(S + 4 * q);
-      s[4 * q] = v4[0]; s[4 * q + 1] = v4[1]; s[4 * q + 2] = v4[2]; s[4 * q + 3] = v4[3];
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < 16; ++q) s[q] = 0.f;
+  for (int q = 0; q < 4; ++q) s[q] = S ? ldf4_nt(S + 1024 * q) : floatx4{0.f, 0.f, 0.f, 0.f};
+  float gw = 0.f, gb = 0.f;
+  if (t < 64) {
+    gw = a.lnx_w[h * 64 + t];
+    gb = a.lnx_b[h * 64 + t];
   }
   // commit the time-mix shift computed by the fused input projection
   if (a.u_att && ok && t >= 64 && t < 128)
@@ -227,31 +227,141 @@ __global__ __launch_bounds__(256) void k_wkv_decode(WkvArgs a) {
   else
     wkv_prologue<NCHK>(a, b, h, hv, s_lin);
 
-  float sa = 0.f;
+  const int j0 = 4 * (t & 15);
+  const floatx4 av = *reinterpret_cast<const floatx4*>(&hv.a[j0]);
+  const floatx4 bv = *reinterpret_cast<const floatx4*>(&hv.bb[j0]);
+  const floatx4 kv = *reinterpret_cast<const floatx4*>(&hv.kt[j0]);
+  const floatx4 dv = *reinterpret_cast<const floatx4*>(&hv.d[j0]);
+  const floatx4 rv = *reinterpret_cast<const floatx4*>(&hv.r[j0]);
+  float y[4];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) sa = fmaf(s[j], hv.a[j0 + j], sa);
-  sa += __shfl_xor(sa, 1);
-  sa += __shfl_xor(sa, 2);
-  const float vi = hv.v[i];
-  float y = 0.f;
+  for (int q = 0; q < 4; ++q) {
+    const int i = 16 * q + (t >> 4);
+    const float sa = sum16(s[q][0] * av[0] + s[q][1] * av[1] + s[q][2] * av[2] + s[q][3] * av[3]);
+    const float vi = hv.v[i];
+    float yy = 0.f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const float sn = s[j] * hv.d[j0 + j] + sa * hv.bb[j0 + j] + vi * hv.kt[j0 + j];
-    s[j] = sn;
-    y = fmaf(sn, hv.r[j0 + j], y);
+    for (int c = 0; c < 4; ++c) {
+      const float sn = s[q][c] * dv[c] + sa * bv[c] + vi * kv[c];
+      s[q][c] = sn;
+      yy = fmaf(sn, rv[c], yy);
+    }
+    y[q] = yy;
   }
-  y += __shfl_xor(y, 1);
-  y += __shfl_xor(y, 2);
   if (S) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      stf4_nt(S + 4 * q, floatx4{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]});
+    for (int q = 0; q < 4; ++q) stf4_nt(S + 1024 * q, s[q]);
   }
-  if ((t & 3) == 0) hv.y[i] = y;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float yy = sum16(y[q]);
+    if ((t & 15) == 0) hv.y[16 * q + (t >> 4)] = yy;
+  }
   __syncthreads();
   if (t < 64) {
-    const float o = wkv_epilogue(a, h, hv, hv.y[t]);
+    const float o = wkv_epilogue(hv, hv.y[t], gw, gb);
     const long off = (long)b * a.C + h * 64 + t;
+    if (a.yout_f16)
+      ((half_t*)a.yout)[off] = (half_t)o;
+    else
+      ((float*)a.yout)[off] = o;
+  }
+}
+
+// Many rows with precomputed adapter outputs: one wave per (row, head), four
+// per workgroup.  Lane l owns channel l of the head for the per-channel
+// vectors and float4 number 64 q + l (q = 0..15) of the state: value rows
+// 4 q + l / 16, key columns 4 (l % 16) .. +3, so every state load and store
+// instruction covers 1 KB of contiguous memory and the row sums close over
+// 16 lanes.  No lane idles during the per-channel work.
+struct WaveVecs {
+  float a[64], bb[64], kt[64], d[64], r[64], v[64], y[64];
+};
+
+__global__ __launch_bounds__(256) void k_wkv_decode_rows(WkvArgs a) {
+  __shared__ __attribute__((aligned(16))) WaveVecs wv[4];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int item = blockIdx.x * 4 + wave;        // (row, head) pair
+  const bool live = item < a.B * a.H;
+  const int b = live ? item / a.H : 0;
+  const int h = live ? item % a.H : 0;
+  const int C = a.C;
+  const int slot = live ? a.slots[b] : -1;
+  const bool ok = slot >= 0 && slot < a.n_slots;
+  float* S = ok ? a.pool + (long)slot * a.slot_stride + a.layer_off + 2L * C + (long)h * 4096 + 4 * lane
+                : nullptr;
+  floatx4 s[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) s[q] = S ? ldf4_nt(S + 256 * q) : floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int cc = h * 64 + lane;
+  const long rb = (long)b * 3 * C + cc;
+  const float* lo = a.lo + (long)b * 4 * C + cc;
+  const float r = a.rkv[rb], k = a.rkv[rb + C];
+  float v = a.rkv[rb + 2 * C];
+  const float dk = lo[0], al = lo[C], vg = lo[2 * C], g = lo[3 * C];
+  const float k_k = a.k_k[cc], k_a = a.k_a[cc], r_k = a.r_k[cc];
+  const float gw = a.lnx_w[cc], gb = a.lnx_b[cc];
+  const float vf = a.layer > 0 ? a.vfirst[(long)b * C + cc] : 0.f;
+
+  const float kap = k * k_k;
+  const float nrm = sqrtf(wave_sum(kap * kap));
+  const float kh = kap / fmaxf(nrm, 1e-12f);
+  const float kt = k * (1.0f + (al - 1.0f) * k_a);
+  if (a.layer == 0) {
+    if (live) a.vfirst[(long)b * C + cc] = v;
+  } else {
+    v = v + (vf - v) * vg;
+  }
+  const float bonus = wave_sum(r * kt * r_k);
+  WaveVecs& w = wv[wave];
+  w.a[lane] = -kh;
+  w.bb[lane] = kh * al;
+  w.kt[lane] = kt;
+  w.d[lane] = dk;
+  w.r[lane] = r;
+  w.v[lane] = v;
+  __syncthreads();
+
+  const int j0 = 4 * (lane & 15);
+  const floatx4 av = *reinterpret_cast<const floatx4*>(&w.a[j0]);
+  const floatx4 bv = *reinterpret_cast<const floatx4*>(&w.bb[j0]);
+  const floatx4 kv = *reinterpret_cast<const floatx4*>(&w.kt[j0]);
+  const floatx4 dv = *reinterpret_cast<const floatx4*>(&w.d[j0]);
+  const floatx4 rv = *reinterpret_cast<const floatx4*>(&w.r[j0]);
+  float y[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const float sa = sum16(s[q][0] * av[0] + s[q][1] * av[1] + s[q][2] * av[2] + s[q][3] * av[3]);
+    const float vi = w.v[4 * q + (lane >> 4)];
+    float yy = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float sn = s[q][c] * dv[c] + sa * bv[c] + vi * kv[c];
+      s[q][c] = sn;
+      yy = fmaf(sn, rv[c], yy);
+    }
+    y[q] = yy;
+  }
+  if (S) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) stf4_nt(S + 256 * q, s[q]);
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const float yy = sum16(y[q]);
+    if ((lane & 15) == 0) w.y[4 * q + (lane >> 4)] = yy;
+  }
+  __syncthreads();
+  // GroupNorm over the head's readouts, bonus, gate
+  const float yl = w.y[lane];
+  const float mean = wave_sum(yl) * (1.0f / 64.0f);
+  const float dlt = yl - mean;
+  const float var = wave_sum(dlt * dlt) * (1.0f / 64.0f);
+  const float o = (dlt / sqrtf(var + 64e-5f) * gw + gb + bonus * v) * g;
+  if (live) {
+    const long off = (long)b * C + cc;
     if (a.yout_f16)
       ((half_t*)a.yout)[off] = (half_t)o;
     else
@@ -273,6 +383,11 @@ static int wkv_nchk(const WkvArgs& a) {
 
 hipError_t launch_wkv_decode(const WkvArgs& a, hipStream_t st) {
   if (a.Lin > LIN_MAX) return hipErrorInvalidValue;
+  if (a.lo && !a.u_att) {
+    const int items = a.B * a.H;
+    hipLaunchKernelGGL(k_wkv_decode_rows, dim3((items + 3) / 4), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   switch (wkv_nchk(a)) {
 #define X(n) case n: hipLaunchKernelGGL(k_wkv_decode<n>, dim3(a.B * a.H), dim3(256), 0, st, a); break;
     X(0) WKV_NCHK_CASES(X)
@@ -308,41 +423,93 @@ __global__ __launch_bounds__(256) void k_wkv_prep(WkvArgs a) {
 
 // Grid: H * 4 workgroups; workgroup (h, qb) owns value rows [16 qb, 16 qb + 16)
 // of head h: 4 rows per wave, 16 lanes per row, 4 key columns per lane.
+// The per-token vectors do not depend on the state, so they are staged
+// through LDS in blocks of SCAN_TB tokens, the next block's global loads in
+// flight while the current block runs the recurrence; the serial chain per
+// token is then LDS reads and ALU only.
+constexpr int SCAN_TB = 16;
+struct ScanBlock {
+  float4 a[SCAN_TB][16], b[SCAN_TB][16], d[SCAN_TB][16], kt[SCAN_TB][16], r[SCAN_TB][16];
+  float v[SCAN_TB][16];
+};
+
 __global__ __launch_bounds__(256) void k_wkv_scan(WkvArgs a) {
+  __shared__ ScanBlock sb[2];
   const int h = blockIdx.x >> 2;
   const int qb = blockIdx.x & 3;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i = qb * 16 + wave * 4 + (lane >> 4);
-  const int j = (lane & 15) * 4;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int il = wave * 4 + (lane >> 4);    // row inside the workgroup's 16
+  const int i = qb * 16 + il;
+  const int jq = lane & 15;                 // float4 column index
   const int C = a.C;
   float* S = a.pool + (long)a.seq_slot * a.slot_stride + a.layer_off + 2L * C + (long)h * 4096 +
-             i * 64 + j;
+             i * 64 + 4 * jq;
   float4 s = *reinterpret_cast<const float4*>(S);
-  const long cj = h * 64 + j;
-  const long ci = h * 64 + i;
-  for (int tk = 0; tk < a.B; ++tk) {
-    const long o = (long)tk * C;
-    const float4 av = *reinterpret_cast<const float4*>(a.q_a + o + cj);
-    const float4 bv = *reinterpret_cast<const float4*>(a.q_b + o + cj);
-    const float4 dv = *reinterpret_cast<const float4*>(a.q_d + o + cj);
-    const float4 kv = *reinterpret_cast<const float4*>(a.q_kt + o + cj);
-    const float4 rv = *reinterpret_cast<const float4*>(a.rkv + (long)tk * 3 * C + cj);
-    const float vi = a.q_v[o + ci];
-    float sa = s.x * av.x + s.y * av.y + s.z * av.z + s.w * av.w;
-    sa += __shfl_xor(sa, 1);
-    sa += __shfl_xor(sa, 2);
-    sa += __shfl_xor(sa, 4);
-    sa += __shfl_xor(sa, 8);
-    s.x = s.x * dv.x + sa * bv.x + vi * kv.x;
-    s.y = s.y * dv.y + sa * bv.y + vi * kv.y;
-    s.z = s.z * dv.z + sa * bv.z + vi * kv.z;
-    s.w = s.w * dv.w + sa * bv.w + vi * kv.w;
-    float y = s.x * rv.x + s.y * rv.y + s.z * rv.z + s.w * rv.w;
-    y += __shfl_xor(y, 1);
-    y += __shfl_xor(y, 2);
-    y += __shfl_xor(y, 4);
-    y += __shfl_xor(y, 8);
-    if ((lane & 15) == 0) a.q_y[o + ci] = y;
+  const long cj = h * 64;
+  const int T = a.B;
+
+  // staging: 5 vectors x SCAN_TB tokens x 16 float4 = 1280 float4 (5 per
+  // thread) plus SCAN_TB x 16 value floats (one per thread)
+  float4 ra[5];
+  float rvv = 0.f;
+  auto load = [&](int t0) {
+#pragma unroll
+    for (int p = 0; p < 5; ++p) {
+      const int e = p * 256 + tid;          // [vec][token][float4]
+      const int vec = e / (SCAN_TB * 16);
+      const int tk = t0 + (e / 16) % SCAN_TB;
+      const int c4 = e % 16;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (tk < T) {
+        const long o = (long)tk * C + cj + 4 * c4;
+        const float* src = vec == 0 ? a.q_a + o : vec == 1 ? a.q_b + o : vec == 2 ? a.q_d + o
+                           : vec == 3 ? a.q_kt + o : a.rkv + (long)tk * 3 * C + cj + 4 * c4;
+        x = *reinterpret_cast<const float4*>(src);
+      }
+      ra[p] = x;
+    }
+    const int tk = t0 + tid / 16;
+    rvv = tk < T ? a.q_v[(long)tk * C + cj + qb * 16 + (tid & 15)] : 0.f;
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < 5; ++p) {
+      const int e = p * 256 + tid;
+      const int vec = e / (SCAN_TB * 16);
+      const int tt = (e / 16) % SCAN_TB;
+      const int c4 = e % 16;
+      float4* dst = vec == 0 ? &sb[buf].a[tt][c4] : vec == 1 ? &sb[buf].b[tt][c4]
+                    : vec == 2 ? &sb[buf].d[tt][c4] : vec == 3 ? &sb[buf].kt[tt][c4] : &sb[buf].r[tt][c4];
+      *dst = ra[p];
+    }
+    sb[buf].v[tid / 16][tid & 15] = rvv;
+  };
+
+  load(0);
+  store(0);
+  __syncthreads();
+  int buf = 0;
+  for (int t0 = 0; t0 < T; t0 += SCAN_TB) {
+    const bool more = t0 + SCAN_TB < T;
+    if (more) load(t0 + SCAN_TB);
+    const ScanBlock& B = sb[buf];
+    const int n = T - t0 < SCAN_TB ? T - t0 : SCAN_TB;
+    for (int tt = 0; tt < n; ++tt) {
+      const float4 av = B.a[tt][jq], bv = B.b[tt][jq], dv = B.d[tt][jq], kv = B.kt[tt][jq];
+      const float4 rv = B.r[tt][jq];
+      const float vi = B.v[tt][il];
+      const float sa = sum16(s.x * av.x + s.y * av.y + s.z * av.z + s.w * av.w);
+      s.x = s.x * dv.x + sa * bv.x + vi * kv.x;
+      s.y = s.y * dv.y + sa * bv.y + vi * kv.y;
+      s.z = s.z * dv.z + sa * bv.z + vi * kv.z;
+      s.w = s.w * dv.w + sa * bv.w + vi * kv.w;
+      const float y = sum16(s.x * rv.x + s.y * rv.y + s.z * rv.z + s.w * rv.w);
+      if (jq == 0) a.q_y[(long)(t0 + tt) * C + h * 64 + i] = y;
+    }
+    if (more) store(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
   }
   *reinterpret_cast<float4*>(S) = s;
 }
@@ -353,11 +520,13 @@ __global__ __launch_bounds__(64) void k_wkv_post(WkvArgs a) {
   const int h = blockIdx.x % a.H;
   const int t = threadIdx.x;
   const long off = (long)tk * a.C + h * 64 + t;
+  const float gw = a.lnx_w[h * 64 + t], gb = a.lnx_b[h * 64 + t];
+  const float yv = a.q_y[off];
   hv.v[t] = a.q_v[off];
   hv.g[t] = a.q_g[off];
   if (t == 0) hv.bonus = a.q_bonus[(long)tk * a.H + h];
   __syncthreads();
-  const float o = wkv_epilogue(a, h, hv, a.q_y[off]);
+  const float o = wkv_epilogue(hv, yv, gw, gb);
   if (a.yout_f16)
     ((half_t*)a.yout)[off] = (half_t)o;
   else
