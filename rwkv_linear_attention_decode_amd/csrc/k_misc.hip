@@ -120,78 +120,85 @@ hipError_t launch_embed(const EmbedArgs& a, hipStream_t st) {
 }
 
 // ============================================================== LN + token-shift mix
+// One workgroup per row.  Every global load the row needs (x, partial sums,
+// LayerNorm weights, the stored shift or the previous token's row, and all
+// nq mixing vectors) is issued before the first reduction barrier, so a row
+// costs one memory round trip.
 template <int NE>
 __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
-  __shared__ float red[8];
+  __shared__ float red[16];
   const int r = blockIdx.x;
   const int C = a.C;
-  float v[NE];
+  const int t = threadIdx.x;
+  float v[NE], gv[NE], bv[NE], pv[NE], mu[6][NE];
   float* xr = a.x + (long)r * C;
 #pragma unroll
-  for (int i = 0; i < NE; ++i) v[i] = xr[threadIdx.x + 256 * i];
+  for (int i = 0; i < NE; ++i) {
+    v[i] = xr[t + 256 * i];
+    gv[i] = a.g[t + 256 * i];
+    bv[i] = a.b[t + 256 * i];
+  }
+  const float* sh_in = nullptr;      // stored shift to mix with (decode / first token)
+  float* sh_out = nullptr;           // where the new shift goes (decode)
+  if (a.mode == LNMIX_DECODE) {
+    const int slot = a.slots[r];
+    if (slot >= 0 && slot < a.n_slots) {
+      sh_out = a.pool + (long)slot * a.slot_stride + a.shift_off;
+      sh_in = sh_out;
+    }
+  } else if (a.mode == LNMIX_SEQ && r == 0) {
+    sh_in = a.pool + (long)a.seq_slot * a.slot_stride + a.shift_off;
+  }
+  const bool prev_row = a.mode == LNMIX_SEQ && r > 0;   // LayerNorm of the previous token
+  const float* xp = a.x + (long)(r - 1) * C;
+#pragma unroll
+  for (int i = 0; i < NE; ++i)
+    pv[i] = sh_in ? sh_in[t + 256 * i] : prev_row ? xp[t + 256 * i] : 0.0f;
+#pragma unroll
+  for (int q = 0; q < 6; ++q)
+#pragma unroll
+    for (int i = 0; i < NE; ++i)
+      mu[q][i] = (q < a.nq && a.mu) ? a.mu[(long)q * C + t + 256 * i] : 0.0f;
   if (a.nparts > 0) {
     for (int s = 0; s < a.nparts; ++s) {
       const float* p = a.parts + ((long)s * a.R + r) * C;
 #pragma unroll
-      for (int i = 0; i < NE; ++i) v[i] += p[threadIdx.x + 256 * i];
+      for (int i = 0; i < NE; ++i) v[i] += p[t + 256 * i];
     }
 #pragma unroll
-    for (int i = 0; i < NE; ++i) xr[threadIdx.x + 256 * i] = v[i];
+    for (int i = 0; i < NE; ++i) xr[t + 256 * i] = v[i];
   }
+
   float mean, rstd;
   ln_rows<NE>(v, &mean, &rstd, red);
   float u[NE];
 #pragma unroll
-  for (int i = 0; i < NE; ++i) {
-    const int c = threadIdx.x + 256 * i;
-    u[i] = (v[i] - mean) * rstd * a.g[c] + a.b[c];
+  for (int i = 0; i < NE; ++i) u[i] = (v[i] - mean) * rstd * gv[i] + bv[i];
+  if (prev_row) {
+    float m2, rs2;
+    ln_rows<NE>(pv, &m2, &rs2, red + 8);
+#pragma unroll
+    for (int i = 0; i < NE; ++i) pv[i] = (pv[i] - m2) * rs2 * gv[i] + bv[i];
+  } else if (a.mode == LNMIX_PLAIN) {
+#pragma unroll
+    for (int i = 0; i < NE; ++i) pv[i] = u[i];
+  }
+  if (sh_out) {
+#pragma unroll
+    for (int i = 0; i < NE; ++i) sh_out[t + 256 * i] = u[i];
+  }
+  if (a.mode == LNMIX_SEQ && r == a.R - 1) {
+#pragma unroll
+    for (int i = 0; i < NE; ++i) a.shift_tmp[t + 256 * i] = u[i];
   }
 
-  float prev[NE];
-  if (a.mode == LNMIX_DECODE) {
-    const int slot = a.slots[r];
-    float* sh = (slot >= 0 && slot < a.n_slots) ? a.pool + (long)slot * a.slot_stride + a.shift_off
-                                                : nullptr;
 #pragma unroll
-    for (int i = 0; i < NE; ++i) prev[i] = sh ? sh[threadIdx.x + 256 * i] : 0.0f;
-    if (sh) {
-#pragma unroll
-      for (int i = 0; i < NE; ++i) sh[threadIdx.x + 256 * i] = u[i];
-    }
-  } else if (a.mode == LNMIX_SEQ) {
-    if (r == 0) {
-      const float* sh = a.pool + (long)a.seq_slot * a.slot_stride + a.shift_off;
-#pragma unroll
-      for (int i = 0; i < NE; ++i) prev[i] = sh[threadIdx.x + 256 * i];
-    } else {
-      // LayerNorm of the previous token's row (x is read-only in this mode)
-      const float* xp = a.x + (long)(r - 1) * C;
-      float w[NE];
-#pragma unroll
-      for (int i = 0; i < NE; ++i) w[i] = xp[threadIdx.x + 256 * i];
-      float m2, rs2;
-      ln_rows<NE>(w, &m2, &rs2, red);
-#pragma unroll
-      for (int i = 0; i < NE; ++i) {
-        const int c = threadIdx.x + 256 * i;
-        prev[i] = (w[i] - m2) * rs2 * a.g[c] + a.b[c];
-      }
-    }
-    if (r == a.R - 1) {
-#pragma unroll
-      for (int i = 0; i < NE; ++i) a.shift_tmp[threadIdx.x + 256 * i] = u[i];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < NE; ++i) prev[i] = u[i];
-  }
-
-  for (int q = 0; q < a.nq; ++q) {
+  for (int q = 0; q < 6; ++q) {
+    if (q >= a.nq) break;
 #pragma unroll
     for (int i = 0; i < NE; ++i) {
-      const int c = threadIdx.x + 256 * i;
-      const float mu = a.mu ? a.mu[(long)q * C + c] : 0.0f;
-      const float o = u[i] + (prev[i] - u[i]) * mu;
+      const int c = t + 256 * i;
+      const float o = u[i] + (pv[i] - u[i]) * mu[q][i];
       const long off = q * a.out_q_stride + (long)r * C + c;
       if (a.out_f16)
         ((half_t*)a.out)[off] = (half_t)o;
@@ -203,6 +210,7 @@ __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
 
 hipError_t launch_ln_mix(const LnMixArgs& a, hipStream_t st) {
   if (a.C % 256) return hipErrorInvalidValue;
+  if (a.nq < 1 || a.nq > 6) return hipErrorInvalidValue;
   if (a.mode == LNMIX_SEQ && a.nparts) return hipErrorInvalidValue;
   NE_DISPATCH(a.C, k_ln_mix, dim3(a.R), dim3(256), 0, st, a);
   return hipGetLastError();
