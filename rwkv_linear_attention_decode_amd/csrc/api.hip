@@ -182,8 +182,8 @@ Ws ws_layout(const Dims& d, int R, char* base) {
   w.q_g = (float*)take(r * C * 4);
   w.q_y = (float*)take(r * C * 4);
   w.q_bonus = (float*)take(r * d.H * 4);
-  w.part_floats = (int64_t)(r * 8 * C);
-  w.part = (float*)take(r * 8 * C * 4);
+  w.part_floats = (int64_t)(r * 16 * C);
+  w.part = (float*)take(r * 16 * C * 4);
   w.bytes = off;
   return w;
 }
@@ -1101,12 +1101,22 @@ const char* rwkv7_kernel_name(const rwkv7_model* m, int32_t cls, int32_t B) {
   const Path p = decode_path(m, B);
   switch (cls) {
     case RWKV7_K_LN_MIX: return "k_ln_mix";
-    case RWKV7_K_PROJ_IN: return p.gemv ? gemv_kernel_name(B, m->d.C, -1) : gemm_kernel_name(B);
-    case RWKV7_K_PROJ_OUT: return p.gemv ? gemv_kernel_name(B, m->d.C, EPI_RESID) : gemm_kernel_name(B);
-    case RWKV7_K_CMIX_KEY: return p.gemv ? gemv_kernel_name(B, m->d.C, p.sparse ? EPI_PRE : -1) : gemm_kernel_name(B);
-    case RWKV7_K_HEAD: return p.gemv ? gemv_kernel_name(B, m->d.C, EPI_NONE) : gemm_kernel_name(B);
-    case RWKV7_K_WKV: return "k_wkv_decode";
-    case RWKV7_K_CMIX_VALUE: return p.sparse ? cmix_sparse_kernel_name(B) : gemm_kernel_name(B);
+    case RWKV7_K_PROJ_IN:
+      return p.gemv ? gemv_kernel_name(B, m->d.C, -1) : gemm_kernel_name(B, m->d.Nin, m->d.C);
+    case RWKV7_K_PROJ_OUT:
+      return p.gemv ? gemv_kernel_name(B, m->d.C, EPI_RESID) : gemm_kernel_name(B, m->d.C, m->d.C);
+    case RWKV7_K_CMIX_KEY:
+      return p.gemv ? gemv_kernel_name(B, m->d.C, p.sparse ? EPI_PRE : -1) : gemm_kernel_name(B, m->d.F, m->d.C);
+    case RWKV7_K_HEAD:
+      return p.gemv ? gemv_kernel_name(B, m->d.C, EPI_NONE) : gemm_kernel_name(B, m->d.V, m->d.C);
+    case RWKV7_K_WKV: {
+      if (!p.gemv) return "k_wkv_decode_rows";
+      static char name[32];
+      snprintf(name, sizeof name, "k_wkv_decode<%d>", (m->d.Dw + m->d.Da + m->d.Dv + m->d.Dg) / 32);
+      return name;
+    }
+    case RWKV7_K_CMIX_VALUE:
+      return p.sparse ? cmix_sparse_kernel_name(B) : gemm_kernel_name(B, m->d.C, m->d.F);
     default: return kClassName[cls];
   }
 }

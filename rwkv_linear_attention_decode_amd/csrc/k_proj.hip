@@ -13,6 +13,7 @@
 #include "launch.h"
 
 #include <stdio.h>
+#include <string.h>
 
 // ============================================================== GEMV
 // The fused LayerNorm prologue holds a lane's K slice of every row in VGPRs
@@ -311,16 +312,20 @@ const char* gemv_kernel_name(int B, int K, int epi) {
 // into `split` contiguous ranges whose fp32 partial sums a second kernel adds
 // in a fixed order before applying the epilogue, so results do not depend
 // on scheduling.
-constexpr int MM_KS = 64;          // k per stage
-constexpr int MM_LDS = MM_KS + 8;  // halves per LDS row
+// LDS rows are KS + 16 halves: with a row stride of KS + 8 halves the
+// fragment reads and the staging writes still meet bank conflicts on gfx950
+// (measured with SQ_LDS_BANK_CONFLICT); + 16 removes them.
+constexpr int MM_PAD = 16;
 
-template <int TM, int TN>
+template <int TM, int TN, int KS>
 __global__ __launch_bounds__(256) void k_mm(ProjArgs a) {
   constexpr int MT = 32 * TM, NT = 32 * TN;
-  constexpr int ACH = MT * 8 / 256;   // 16-byte A chunks per thread and stage
-  constexpr int BCH = NT * 8 / 256;   // 16-byte W chunks per thread and stage
-  __shared__ __attribute__((aligned(16))) half_t As[2][MT][MM_LDS];
-  __shared__ __attribute__((aligned(16))) half_t Bs[2][NT][MM_LDS];
+  constexpr int CPR = KS / 8;          // 16-byte chunks per row and stage
+  constexpr int ACH = MT * CPR / 256;  // 16-byte A chunks per thread and stage
+  constexpr int BCH = NT * CPR / 256;  // 16-byte W chunks per thread and stage
+  constexpr int LDSR = KS + MM_PAD;    // halves per LDS row
+  __shared__ __attribute__((aligned(16))) half_t As[2][MT][LDSR];
+  __shared__ __attribute__((aligned(16))) half_t Bs[2][NT][LDSR];
 
   // XCD-aware order: consecutive work items (same column tile, successive
   // M tiles and K ranges) go to the same XCD, whose L2 then serves the
@@ -349,7 +354,7 @@ __global__ __launch_bounds__(256) void k_mm(ProjArgs a) {
   const half_t* Wb = own ? sg.W - (long)sg.row0 * K : a.W;  // indexed by global column
   const half_t* A = reinterpret_cast<const half_t*>(sg.act) + sg.act_off;
   const int lda = sg.ld_act;
-  const int nst = (K + MM_KS - 1) / MM_KS;
+  const int nst = (K + KS - 1) / KS;
   const int st0 = (int)((long)nst * ks_id / a.split);
   const int st1 = (int)((long)nst * (ks_id + 1) / a.split);
 
@@ -369,18 +374,18 @@ __global__ __launch_bounds__(256) void k_mm(ProjArgs a) {
 
   u32x4 ra[ACH], rb[BCH];
   auto load = [&](int stg) {
-    const int k0 = stg * MM_KS;
+    const int k0 = stg * KS;
 #pragma unroll
     for (int p = 0; p < ACH; ++p) {
       const int c = p * 256 + tid;
-      const int r = c >> 3, kc = (c & 7) * 8;
+      const int r = c / CPR, kc = (c % CPR) * 8;
       const int m = m0 + r;
       ra[p] = (m < a.M && k0 + kc < K) ? ld16(A + (long)m * lda + k0 + kc) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int p = 0; p < BCH; ++p) {
       const int c = p * 256 + tid;
-      const int r = c >> 3, kc = (c & 7) * 8;
+      const int r = c / CPR, kc = (c % CPR) * 8;
       const int n = n0 + r;
       rb[p] = (n < sg.row1 && k0 + kc < K) ? ld16(Wb + (long)n * K + k0 + kc) : u32x4{0u, 0u, 0u, 0u};
     }
@@ -389,12 +394,12 @@ __global__ __launch_bounds__(256) void k_mm(ProjArgs a) {
 #pragma unroll
     for (int p = 0; p < ACH; ++p) {
       const int c = p * 256 + tid;
-      st16(&As[buf][c >> 3][(c & 7) * 8], ra[p]);
+      st16(&As[buf][c / CPR][(c % CPR) * 8], ra[p]);
     }
 #pragma unroll
     for (int p = 0; p < BCH; ++p) {
       const int c = p * 256 + tid;
-      st16(&Bs[buf][c >> 3][(c & 7) * 8], rb[p]);
+      st16(&Bs[buf][c / CPR][(c % CPR) * 8], rb[p]);
     }
   };
 
@@ -408,7 +413,7 @@ __global__ __launch_bounds__(256) void k_mm(ProjArgs a) {
     const bool more = stg + 1 < st1;
     if (more) load(stg + 1);
 #pragma unroll
-    for (int kk = 0; kk < MM_KS; kk += 32) {
+    for (int kk = 0; kk < KS; kk += 32) {
       half8 af[TM], bf[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -482,13 +487,14 @@ __global__ void k_pre_mask(const float* pre, int ld, int M, int F, unsigned char
   mask[f] = any ? 1 : 0;
 }
 
-static int mm_tm(int M) { return M <= 32 ? 1 : (M <= 64 ? 2 : 4); }
-static constexpr int MM_TN = 4;
-
-// Tile plan of a launch: column tiles per segment, M tiles, K split.
-int mm_plan(ProjArgs& a, int total_rows, int64_t part_floats) {
-  const int NT = 32 * MM_TN;
-  const int MT = 32 * mm_tm(a.M);
+// Tile plan of a launch with TM x TN blocks of 16 x 16 per wave (tile
+// 32 TM x 32 TN) and KS-deep stages: column tiles per segment, M tiles, and
+// the K split (split_req 0: about 1.5 workgroups per CU when the tiles are
+// fewer than the CUs, at least 4 stages per range, within the partial-sum
+// buffer).
+int mm_plan(ProjArgs& a, int total_rows, int tm, int tn, int ks, int split_req, int64_t part_floats) {
+  const int NT = 32 * tn;
+  const int MT = 32 * tm;
   a.tile0[0] = 0;
   int max_nst = 1;
   for (int i = 0; i < a.nseg; ++i) {
@@ -497,18 +503,22 @@ int mm_plan(ProjArgs& a, int total_rows, int64_t part_floats) {
     if (K % 32 != 0 || K <= 0) return -1;
     if (s.row1 <= s.row0) return -1;
     a.tile0[i + 1] = a.tile0[i] + (s.row1 - s.row0 + NT - 1) / NT;
-    max_nst = max_nst > (K + MM_KS - 1) / MM_KS ? max_nst : (K + MM_KS - 1) / MM_KS;
+    const int nst = (K + ks - 1) / ks;
+    max_nst = max_nst > nst ? max_nst : nst;
   }
   for (int i = a.nseg + 1; i <= MAX_SEGS; ++i) a.tile0[i] = a.tile0[a.nseg];
   a.m_tiles = (a.M + MT - 1) / MT;
   a.total_rows = total_rows;
-  // Few tiles (N = C projections at moderate M): split K so that about one
-  // workgroup per CU has work, keeping at least 4 stages per range.
   const int tiles = a.tile0[a.nseg] * a.m_tiles;
   int split = 1;
-  if (a.part && tiles < 192) {
-    split = (256 + tiles - 1) / tiles;
-    if (split > max_nst / 4) split = max_nst / 4;
+  if (a.part) {
+    if (split_req > 0) {
+      split = split_req;
+    } else if (tiles < 256) {
+      split = (384 + tiles - 1) / tiles;
+      if (split > max_nst / 4) split = max_nst / 4;
+    }
+    if (split > max_nst) split = max_nst;
     while (split > 1 && (int64_t)split * a.M * total_rows > part_floats) --split;
     if (split < 1) split = 1;
   }
@@ -516,14 +526,76 @@ int mm_plan(ProjArgs& a, int total_rows, int64_t part_floats) {
   return tiles * split;
 }
 
-hipError_t launch_gemm(ProjArgs a, int total_rows, int64_t part_floats, hipStream_t st) {
-  const int items = mm_plan(a, total_rows, part_floats);
+// LDS bytes of a k_mm instantiation (two stage buffers of A and W rows)
+static constexpr int mm_lds_bytes(int tm, int tn, int ks) { return 2 * 32 * (tm + tn) * (ks + MM_PAD) * 2; }
+
+template <int TM, int TN>
+static void mm_launch(int ks, dim3 grid, hipStream_t st, const ProjArgs& a) {
+  if constexpr (TM >= 2) {
+    if (ks == 32) {
+      hipLaunchKernelGGL((k_mm<TM, TN, 32>), grid, dim3(256), 0, st, a);
+      return;
+    }
+  }
+  if constexpr (mm_lds_bytes(TM, TN, 128) <= 65536) {
+    if (ks == 128) {
+      hipLaunchKernelGGL((k_mm<TM, TN, 128>), grid, dim3(256), 0, st, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((k_mm<TM, TN, 64>), grid, dim3(256), 0, st, a);
+}
+
+static bool mm_cfg_ok(int tm, int tn, int ks) {
+  if (!((tm == 1 || tm == 2 || tm == 4 || tm == 8) && (tn == 2 || tn == 4))) return false;
+  if (ks == 32) return tm >= 2;
+  if (ks == 128) return mm_lds_bytes(tm, tn, 128) <= 65536;
+  return ks == 64;
+}
+
+// Default tile shape by problem shape, from a sweep of (tm, tn, ks, split)
+// over the 2.9B projections at M = 64, 256 and 512 on MI355X: output widths
+// of one model width (value, output projection) favour narrow tiles with a K
+// split, the wide vocabulary head favours 128 x 128 tiles, the rest 64 x 64.
+static void mm_choose(const ProjArgs& a, int total_rows, int* tm, int* tn, int* ks) {
+  const int M = a.M, N = total_rows;
+  int K = a.K;
+  for (int i = 0; i < a.nseg; ++i)
+    if (a.seg[i].W && a.seg[i].K > K) K = a.seg[i].K;
+  if (M <= 32) {
+    *tm = 1; *tn = 2; *ks = 128;
+  } else if (N <= 4096) {
+    if (M <= 64) {
+      *tm = 1; *tn = 2; *ks = 128;
+    } else if (M <= 256) {
+      const bool deep = K >= 8192;
+      *tm = deep ? 2 : 1; *tn = deep ? 4 : 2; *ks = deep ? 64 : 128;
+    } else {
+      *tm = 4; *tn = 4; *ks = 64;
+    }
+  } else if (N >= 32768) {
+    *tm = M <= 64 ? 2 : 4; *tn = 4; *ks = 64;
+  } else {
+    *tm = 2; *tn = M >= 512 ? 4 : 2; *ks = 64;
+  }
+}
+
+hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int tm, int tn, int ks,
+                           int split, hipStream_t st) {
+  if (tm <= 0 || tn <= 0 || ks <= 0) mm_choose(a, total_rows, &tm, &tn, &ks);
+  if (!mm_cfg_ok(tm, tn, ks)) return hipErrorInvalidValue;
+  const int items = mm_plan(a, total_rows, tm, tn, ks, split, part_floats);
   if (items < 0) return hipErrorInvalidValue;
   const dim3 grid(((items + 7) / 8) * 8);
-  switch (mm_tm(a.M)) {
-    case 1: hipLaunchKernelGGL((k_mm<1, MM_TN>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_mm<2, MM_TN>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((k_mm<4, MM_TN>), grid, dim3(256), 0, st, a); break;
+  switch (tm * 10 + tn) {
+    case 12: mm_launch<1, 2>(ks, grid, st, a); break;
+    case 14: mm_launch<1, 4>(ks, grid, st, a); break;
+    case 22: mm_launch<2, 2>(ks, grid, st, a); break;
+    case 24: mm_launch<2, 4>(ks, grid, st, a); break;
+    case 42: mm_launch<4, 2>(ks, grid, st, a); break;
+    case 82: mm_launch<8, 2>(ks, grid, st, a); break;
+    case 84: mm_launch<8, 4>(ks, grid, st, a); break;
+    default: mm_launch<4, 4>(ks, grid, st, a); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -546,11 +618,21 @@ hipError_t launch_gemm(ProjArgs a, int total_rows, int64_t part_floats, hipStrea
   return hipSuccess;
 }
 
-// Template arguments as a trace prints them, e.g. "k_mm<4, 4>".
-const char* gemm_kernel_name(int M) {
-  switch (mm_tm(M)) {
-    case 1: return "k_mm<1, 4>";
-    case 2: return "k_mm<2, 4>";
-    default: return "k_mm<4, 4>";
-  }
+hipError_t launch_gemm(ProjArgs a, int total_rows, int64_t part_floats, hipStream_t st) {
+  return launch_gemm_cfg(a, total_rows, part_floats, 0, 0, 0, 0, st);
+}
+
+// Template arguments as a trace prints them, e.g. "k_mm<4, 4, 64>", for an
+// M x N x K projection with the default plan.
+const char* gemm_kernel_name(int M, int N, int K) {
+  ProjArgs a;
+  memset(&a, 0, sizeof a);
+  a.M = M;
+  a.K = K;
+  int tm, tn, ks;
+  mm_choose(a, N, &tm, &tn, &ks);
+  static char names[4][2][3][24];
+  char* s = names[tm == 1 ? 0 : tm == 2 ? 1 : tm == 4 ? 2 : 3][tn == 2 ? 0 : 1][ks == 32 ? 0 : ks == 64 ? 1 : 2];
+  if (!s[0]) snprintf(s, sizeof(names[0][0][0]), "k_mm<%d, %d, %d>", tm, tn, ks);
+  return s;
 }

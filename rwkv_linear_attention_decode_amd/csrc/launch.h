@@ -12,9 +12,13 @@ hipError_t launch_gemv(const ProjArgs& a, int total_rows, hipStream_t st);
 // MFMA path: A (segment activations) fp16.  `part_floats` bounds the split-K
 // partial buffer a.part (nullptr: no split).
 hipError_t launch_gemm(ProjArgs a, int total_rows, int64_t part_floats, hipStream_t st);
+// Same with an explicit tile (tm, tn: 16 x 16 blocks per wave), stage depth
+// ks (64 or 128) and K split; 0 selects the default / automatic value.
+hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int tm, int tn, int ks,
+                           int split, hipStream_t st);
 // `epi`: the epilogue shared by every segment of the launch, or -1 when mixed
 const char* gemv_kernel_name(int B, int K, int epi);
-const char* gemm_kernel_name(int M);
+const char* gemm_kernel_name(int M, int N, int K);
 
 // ---------------------------------------------------------------- misc
 struct ValidateArgs {
