@@ -82,8 +82,9 @@ def step_bytes(s, B, nnz, sparse):
 
 
 # ---------------------------------------------------------------- PMC traffic record
-KERNEL_SRC = {"proj_in": "k_proj.hip", "cmix_key": "k_proj.hip", "proj_out": "k_proj.hip",
-              "head": "k_proj.hip", "cmix_value": "k_misc.hip", "wkv": "k_wkv.hip"}
+# source file of each B=1 kernel class (the traffic record is tied to its text)
+KERNEL_SRC = {"proj_in": "k_gemv.hip", "cmix_key": "k_gemv.hip", "proj_out": "k_gemv.hip",
+              "head": "k_gemv.hip", "cmix_value": "k_misc.hip", "wkv": "k_wkv.hip"}
 
 
 def _src_hash(cls):

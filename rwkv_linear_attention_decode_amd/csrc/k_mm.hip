@@ -1,295 +1,11 @@
-// Projection kernels: fp16 weights [rows][K] (K contiguous) times activations.
-//
-// The RWKV-Server article (section 3) credits the decode speed of its CUDA
-// backend to M=1 specialised linears (a row-1 kernel and a split-K one) and
-// switches to dense GEMMs for prefill.  On gfx950 the same split is:
-//   * k_gemv  : B <= 4 rows, fp32 activations held in VGPRs, each weight row
-//               reduced by one 64-lane (or 32-lane) group with 16-byte
-//               non-temporal loads; no split-K partials, so no second pass.
-//   * k_mm    : larger B and prefill, register-blocked MFMA GEMM on fp16
-//               activations and weights staged through LDS
-//               (v_mfma_f32_16x16x32_f16, fp32 accumulate), split over K when
-//               the output has too few tiles to fill the chip.
+// Projections for larger batches and prefill: a register-blocked MFMA GEMM
+// on fp16 activations and weights (v_mfma_f32_16x16x32_f16, fp32
+// accumulate), split over K when the output has too few tiles to fill the
+// chip.  The small-batch GEMV is in k_gemv.hip.
 #include "launch.h"
 
 #include <stdio.h>
 #include <string.h>
-
-// ============================================================== GEMV
-// The fused LayerNorm prologue holds a lane's K slice of every row in VGPRs
-// (B * NCH * 8 floats) and the mixed rows in LDS; it is instantiated only
-// up to this many floats per lane.
-constexpr int kFusedMaxFloats = 80;
-
-// Epilogue family fixed at compile time (GV_MIXED reads it per segment);
-// it also gives each projection class its own kernel symbol in traces.
-enum : int { GV_MIXED = 0, GV_PRE = 1, GV_RESID = 2, GV_NONE = 3 };
-
-template <int B, int LPR, int NCH, int RPW, int EPK>
-__global__ __launch_bounds__(256) void k_gemv(ProjArgs a) {
-  constexpr int GPW = 64 / LPR;
-  constexpr int ROWS_WAVE = GPW * RPW;
-  constexpr int ROWS_WG = 4 * ROWS_WAVE;
-  constexpr int K = LPR * NCH * 8;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int grp = lane / LPR;
-  const int lig = lane % LPR;
-  const int row_wg = blockIdx.x * ROWS_WG;
-  const Seg sg = pick_seg(a, row_wg);
-  const int row_base = row_wg + wave * ROWS_WAVE + grp * RPW;
-
-  u32x4 w[RPW][NCH];
-#pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    const int row = row_base + i;
-    const half_t* wp = a.W + (long)row * K + lig * 8;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      if (row < sg.row1)
-        w[i][c] = ld16_nt(wp + c * LPR * 8);
-      else
-        w[i][c] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-
-  // Activations for this lane's K slice: k = (c * LPR + lig) * 8 + e.
-  float xa[B][NCH][8];
-  if (a.ln.mode == LNP_NONE) {
-    const float* X = reinterpret_cast<const float*>(sg.act);
-#pragma unroll
-    for (int b = 0; b < B; ++b)
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const float* xp = X + (long)b * sg.ld_act + (c * LPR + lig) * 8;
-        const floatx4 p0 = ldf4(xp), p1 = ldf4(xp + 4);
-        xa[b][c][0] = p0.x; xa[b][c][1] = p0.y; xa[b][c][2] = p0.z; xa[b][c][3] = p0.w;
-        xa[b][c][4] = p1.x; xa[b][c][5] = p1.y; xa[b][c][6] = p1.z; xa[b][c][7] = p1.w;
-      }
-  } else if constexpr (B * NCH <= kFusedMaxFloats / 8) {
-    // Fused LayerNorm + token-shift mix, computed once per workgroup while
-    // the weight loads above are in flight: wave w normalises the quarter
-    // [w K/4, (w+1) K/4) of every row (coalesced, stride-64 lanes), row
-    // statistics are combined through LDS, and the mixed row is shared
-    // through LDS with every wave's K slice.
-    constexpr int QK = K / 4;          // elements per wave
-    constexpr int PER = QK / 64;       // per lane
-    __shared__ __attribute__((aligned(16))) float s_xq[B][K];
-    __shared__ float s_st[B][4][2];
-    // every global load of the prologue is issued before the first barrier
-    float xv[B][PER], gv[PER], bv[PER], mv[PER], pvv[B][PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int k = wave * QK + lane + 64 * j;
-      gv[j] = a.ln.g[k];
-      bv[j] = a.ln.b[k];
-      mv[j] = a.ln.mode == LNP_MIX ? sg.mix[k] : 0.f;
-    }
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      const float* prev = nullptr;
-      if (a.ln.mode == LNP_MIX) {
-        const int slot = a.ln.slots[b];
-        if (slot >= 0 && slot < a.ln.n_slots)
-          prev = a.ln.pool + (long)slot * a.ln.slot_stride + a.ln.shift_off;
-      }
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int k = wave * QK + lane + 64 * j;
-        xv[b][j] = a.ln.x[(long)b * K + k];
-        pvv[b][j] = prev ? prev[k] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      float sm = 0.f;
-#pragma unroll
-      for (int j = 0; j < PER; ++j) sm += xv[b][j];
-      sm = wave_sum(sm);
-      if (lane == 0) s_st[b][wave][0] = sm;
-    }
-    __syncthreads();
-    float mean[B], rstd[B];
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      mean[b] = (s_st[b][0][0] + s_st[b][1][0] + s_st[b][2][0] + s_st[b][3][0]) * (1.0f / K);
-      float q = 0.f;
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const float d = xv[b][j] - mean[b];
-        q += d * d;
-      }
-      q = wave_sum(q);
-      if (lane == 0) s_st[b][wave][1] = q;
-    }
-    __syncthreads();
-    const bool writer = blockIdx.x == 0 && a.ln.u_out;
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      rstd[b] = 1.0f / sqrtf((s_st[b][0][1] + s_st[b][1][1] + s_st[b][2][1] + s_st[b][3][1]) *
-                                 (1.0f / K) + 1e-5f);
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int k = wave * QK + lane + 64 * j;
-        const float u = (xv[b][j] - mean[b]) * rstd[b] * gv[j] + bv[j];
-        if (writer) a.ln.u_out[(long)b * K + k] = u;
-        s_xq[b][k] = a.ln.mode == LNP_MIX ? u + (pvv[b][j] - u) * mv[j] : u;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int b = 0; b < B; ++b)
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const float* xp = &s_xq[b][(c * LPR + lig) * 8];
-        const floatx4 p0 = *reinterpret_cast<const floatx4*>(xp);
-        const floatx4 p1 = *reinterpret_cast<const floatx4*>(xp + 4);
-        xa[b][c][0] = p0.x; xa[b][c][1] = p0.y; xa[b][c][2] = p0.z; xa[b][c][3] = p0.w;
-        xa[b][c][4] = p1.x; xa[b][c][5] = p1.y; xa[b][c][6] = p1.z; xa[b][c][7] = p1.w;
-      }
-  }
-
-  float acc[RPW][B];
-#pragma unroll
-  for (int i = 0; i < RPW; ++i)
-#pragma unroll
-    for (int b = 0; b < B; ++b) acc[i][b] = 0.0f;
-
-#pragma unroll
-  for (int i = 0; i < RPW; ++i)
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const half8 h = __builtin_bit_cast(half8, w[i][c]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float wf = (float)h[e];
-#pragma unroll
-        for (int b = 0; b < B; ++b) acc[i][b] = fmaf(wf, xa[b][c][e], acc[i][b]);
-      }
-    }
-
-#pragma unroll
-  for (int i = 0; i < RPW; ++i)
-#pragma unroll
-    for (int b = 0; b < B; ++b)
-#pragma unroll
-      for (int o = LPR / 2; o >= 1; o >>= 1) acc[i][b] += __shfl_xor(acc[i][b], o);
-
-  if (lig == 0) {
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int row = row_base + i;
-      if (row < sg.row1) {
-        const int n = row - sg.row0;
-        const int epi = EPK == GV_PRE ? EPI_PRE : EPK == GV_RESID ? EPI_RESID
-                        : EPK == GV_NONE ? EPI_NONE : sg.epi;
-        if (epi == EPI_PRE) {
-          bool any = false;
-#pragma unroll
-          for (int b = 0; b < B; ++b) {
-            const float pre = acc[i][b] + sg.aux[n];
-            ((float*)sg.out)[(long)b * sg.ld_out + n] = pre;
-            any |= pre > 0.0f;
-          }
-          if (sg.mask) sg.mask[n] = any ? 1 : 0;
-        } else {
-#pragma unroll
-          for (int b = 0; b < B; ++b) {
-            float* o = (float*)sg.out + (long)b * sg.ld_out + n;
-            if (epi == EPI_RESID)
-              *o += acc[i][b];
-            else if (epi == EPI_NONE)
-              *o = acc[i][b];
-            else
-              epi_store(sg, n, b, acc[i][b]);
-          }
-        }
-      }
-    }
-  }
-}
-
-static constexpr int gemv_rpw(int B) { return B <= 2 ? 4 : 2; }
-
-int gemv_rows_per_wg(int B, int K) {
-  const int lpr = (K == 256) ? 32 : 64;
-  return 4 * (64 / lpr) * gemv_rpw(B);
-}
-
-bool gemv_supported(int B, int K) {
-  if (B < 1 || B > 4) return false;
-  if (K == 256) return true;
-  return K % 512 == 0 && K / 512 >= 1 && K / 512 <= 8;
-}
-
-// The fused LayerNorm prologue keeps a lane's whole K slice of every row in
-// VGPRs; bound that to 80 floats.
-bool gemv_fused_ok(int B, int K) {
-  if (!gemv_supported(B, K)) return false;
-  const int nch = K == 256 ? 1 : K / 512;
-  return B * nch <= kFusedMaxFloats / 8;
-}
-
-static int gemv_epk(const ProjArgs& a) {
-  int e = a.seg[0].epi;
-  for (int i = 1; i < a.nseg; ++i)
-    if (a.seg[i].epi != e) return GV_MIXED;
-  return e == EPI_PRE ? GV_PRE : e == EPI_RESID ? GV_RESID : e == EPI_NONE ? GV_NONE : GV_MIXED;
-}
-
-template <int B, int LPR, int NCH, int RPW>
-static void gemv_launch_epk(int epk, dim3 grid, hipStream_t st, const ProjArgs& a) {
-  switch (epk) {
-    case GV_PRE: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_PRE>), grid, dim3(256), 0, st, a); break;
-    case GV_RESID: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_RESID>), grid, dim3(256), 0, st, a); break;
-    case GV_NONE: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_NONE>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_MIXED>), grid, dim3(256), 0, st, a); break;
-  }
-}
-
-template <int B>
-static hipError_t gemv_dispatch_b(const ProjArgs& a, int total_rows, hipStream_t st) {
-  constexpr int RPW = gemv_rpw(B);
-  const int K = a.K;
-  const int rows_wg = gemv_rows_per_wg(B, K);
-  const dim3 grid((total_rows + rows_wg - 1) / rows_wg);
-  const int epk = gemv_epk(a);
-  if (K == 256) {
-    gemv_launch_epk<B, 32, 1, RPW>(epk, grid, st, a);
-    return hipGetLastError();
-  }
-  switch (K / 512) {
-#define CASE(n) case n: gemv_launch_epk<B, 64, n, RPW>(epk, grid, st, a); break;
-    CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
-#undef CASE
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_gemv(const ProjArgs& a, int total_rows, hipStream_t st) {
-  switch (a.M) {
-    case 1: return gemv_dispatch_b<1>(a, total_rows, st);
-    case 2: return gemv_dispatch_b<2>(a, total_rows, st);
-    case 3: return gemv_dispatch_b<3>(a, total_rows, st);
-    case 4: return gemv_dispatch_b<4>(a, total_rows, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-// Template arguments as a trace prints them, e.g. "k_gemv<1, 64, 5, 4, 1>".
-const char* gemv_kernel_name(int B, int K, int epi) {
-  static char names[5][9][4][40];
-  if (!gemv_supported(B, K)) return "k_gemv";
-  const int lpr = K == 256 ? 32 : 64;
-  const int nch = K == 256 ? 1 : K / 512;
-  const int epk = epi == EPI_PRE ? GV_PRE : epi == EPI_RESID ? GV_RESID
-                  : epi == EPI_NONE ? GV_NONE : GV_MIXED;
-  char* s = names[B][nch][epk];
-  if (!s[0])
-    snprintf(s, sizeof(names[0][0][0]), "k_gemv<%d, %d, %d, %d, %d>", B, lpr, nch, gemv_rpw(B), epk);
-  return s;
-}
 
 // ============================================================== MFMA GEMM
 // out[m][n] = epi(sum_k A[m][k] W[n][k]) with fp16 A (activations, k
@@ -298,14 +14,12 @@ const char* gemv_kernel_name(int B, int K, int epi) {
 //
 // Workgroup: 4 waves as 2 x 2, each owning a (16 TM) x (16 TN) block of the
 // (32 TM) x (32 TN) tile, TM x TN accumulators of 16 x 16.  K advances in
-// stages of 64: the next stage's A and W tiles are loaded into registers
-// (16-byte loads, one per thread per 8 x 16-byte chunk row) while the
-// current stage is multiplied out of LDS, then written to the other LDS
-// buffer; one barrier per stage.  In the MFMA operand layout lane l holds
-// row l % 16 and the 8 k values 8 (l / 16) .. +7 of a 32-wide k slice, for
-// both operands, so A and W fragments are plain 16-byte LDS reads of
-// k-contiguous rows (row stride 72 halves: 16 lanes of one read hit 64
-// distinct banks).
+// stages of KS (32, 64 or 128): the next stage's A and W tiles are loaded
+// into registers (16-byte loads) while the current stage is multiplied out
+// of LDS, then written to the other LDS buffer; one barrier per stage.  In
+// the MFMA operand layout lane l holds row l % 16 and the 8 k values
+// 8 (l / 16) .. +7 of a 32-wide k slice, for both operands, so A and W
+// fragments are plain 16-byte LDS reads of k-contiguous rows.
 //
 // Column tiles never straddle a segment (each segment has its own
 // activation and epilogue).  With split > 1 each tile's stages are divided
