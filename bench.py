@@ -13,8 +13,9 @@ Also in the same line:
                launch / average launch time from HIP events) against 8 TB/s
   step         algorithmic bytes per decode step / step time
   kernels      per-class time breakdown of one decode step (HIP events)
-  batched      B = 64 / 256 decode (prompts of 20-2000 tokens, penalties
-               1.0 / 1.0, decay 0.996) with per-projection MFMA TFLOP/s
+  batched      B = 64 / 256 decode of the 2.9B shape and B = 256 of the 7.2B
+               shape (prompts of 20-2000 tokens, penalties 1.0 / 1.0, decay
+               0.996) with per-projection MFMA TFLOP/s
   prefill      tokens/s of rwkv7_prefill_seq at T = 128 / 512 / 2048
   cpu_baseline the fp64 NumPy oracle timed on a bounded sample on the host
 
@@ -216,7 +217,7 @@ def roofline_b1(R, shape, m, kb, nnz, slot, tok, logits):
 def batched(R, args, shape, m, B):
     import torch
     import synth
-    wl = synth.WORKLOADS[f"decode_b{B}_2.9b"] if f"decode_b{B}_2.9b" in synth.WORKLOADS else None
+    wl = synth.WORKLOADS[f"decode_b{B}_{shape.name}"]
     lens = synth.prompt_lengths(wl, B)
     slots_l = list(range(B))
     slots = i32(slots_l)
@@ -254,7 +255,8 @@ def batched(R, args, shape, m, B):
     sparse = B <= R.rwkv7_get_option(m.handle, R.OPT_SPARSE_MAX_B)
     sb = step_bytes(shape, B, shape.ffn, sparse)
     ms = dt / args.batched_steps * 1e3
-    res = {"B": B, "tok_s": round(B * args.batched_steps / dt, 1), "ms_per_step": round(ms, 4),
+    res = {"model": f"{shape.name}-shape", "B": B, "tok_s": round(B * args.batched_steps / dt, 1),
+           "ms_per_step": round(ms, 4),
            "steps": args.batched_steps, "prefill_s": round(t_pf, 2),
            "prompt_tokens": int(lens.sum()),
            "step_gbs": round(sb / (ms * 1e-3) / 1e9, 1),
@@ -339,6 +341,7 @@ def main():
     ap.add_argument("--batched", default="64,256", help="extra batched-decode B values ('' = none)")
     ap.add_argument("--batched-steps", type=int, default=128)
     ap.add_argument("--prefill", default="128,512,2048", help="prefill T values ('' = none)")
+    ap.add_argument("--big", default="256", help="batched-decode B values of the 7.2B shape ('' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -374,6 +377,16 @@ def main():
         cpu = cpu_baseline(shape, weights, args.cpu_seconds)
         log(f"[bench] oracle: {cpu['value']} tok/s")
     m.close()
+    del weights
+
+    # the 7.2B shape: batched decode only (its B=1 and prefill paths are the same kernels)
+    big_res = []
+    Bb = [int(b) for b in args.big.split(",") if b]
+    if Bb:
+        torch.cuda.empty_cache()
+        m7, _ = build_model(R, synth.R7_7B2, n_slots=max(Bb), max_B=max(Bb), max_T=512)
+        big_res = [batched(R, args, synth.R7_7B2, m7, B) for B in Bb]
+        m7.close()
 
     line = {
         "metric": METRIC, "value": round(args.steps / dt, 2), "unit": "tokens/s", "n_gpus": 1,
@@ -389,7 +402,7 @@ def main():
                  "active_ffn_rows_last_layer": nnz},
         "kernels": {k: {"ms_per_step": round(v["ms_per_step"], 4),
                         "launches_per_step": v["launches_per_step"]} for k, v in kb.items()},
-        "batched": batched_res,
+        "batched": batched_res + big_res,
         "prefill": prefill_res,
         "cpu_baseline": cpu,
     }

@@ -144,3 +144,69 @@ def test_prefill_128_vs_oracle_and_steps(model, W):
     assert rel(a, b) <= TOL
     cnt = model.counters().cpu().numpy()
     assert cnt[0] == cnt[1] == 128
+
+
+@pytest.fixture(scope="module")
+def big(weights):
+    """A second model in the bench's large configuration: 512 slots, B up to
+    256 (MFMA projections with the M = 256 tile plan), prefill chunks of 512."""
+    import rwkv_linear_attention_decode_amd as R
+    m = R.Model.from_numpy(S, weights, n_slots=512, max_B=256, max_T=512)
+    yield m
+    m.close()
+
+
+@pytest.mark.timeout(900)
+def test_batched_b256_rows_vs_b1_and_oracle(big, W):
+    """B = 256 in one step (rows = slots 0..255, short prompts) against the
+    same rows stepped one at a time on the B = 1 GEMV path (slots 256..511),
+    every row; rows 0, 131 and 255 also against the oracle."""
+    B = 256
+    wl = synth.WORKLOADS["decode_b256_2.9b"]
+    prompts = [synth.prompt_tokens(wl, b, 5) for b in range(B)]
+    big.reset(dev(list(range(2 * B))))
+    for b in range(B):
+        big.prefill(b, dev(prompts[b][:-1]))
+        big.prefill(B + b, dev(prompts[b][:-1]))
+    toks = [int(p[-1]) for p in prompts]
+    logits = torch.empty(B, S.vocab, device="cuda")
+    one = torch.empty(1, S.vocab, device="cuda")
+    big.decode_step(dev(list(range(B))), dev(toks), logits)
+    L = logits.cpu().numpy()
+    worst = 0.0
+    for b in range(B):
+        big.decode_step(dev([B + b]), dev([toks[b]]), one)
+        worst = max(worst, rel(L[b], one.cpu().numpy()[0]))
+    print(f"2.9B B=256 vs B=1 rows: worst logits rel L2 {worst:.3e}")
+    assert worst <= TOL
+    for b in (0, 131, 255):
+        st = O.State(S)
+        O.seq(W, st, prompts[b][:-1], want_logits=False)
+        ref = O.step(W, [st], [toks[b]])[0]
+        e = rel(L[b], ref)
+        print(f"2.9B B=256 row {b} vs oracle: {e:.3e}")
+        assert e <= TOL
+        assert rel(big.slot_state(b).cpu().double().numpy(), st.flat()) <= TOL
+    assert big.poll_error() == 0
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("T", [512, 2048])
+def test_prefill_long_equals_steps(big, T):
+    """Prefill of T tokens in 512-token chunks (M = 512 MFMA tiles, LDS-staged
+    scan) lands on the state of T single-token GPU steps."""
+    wl = synth.WORKLOADS["prefill_2.9b"]
+    toks = synth.prefill_tokens(wl, T)
+    big.reset(dev([0, 1]))
+    big.prefill(0, dev(toks))
+    logits = torch.empty(1, S.vocab, device="cuda")
+    for t in toks:
+        big.decode_step(dev([1]), dev([int(t)]), logits)
+    torch.cuda.synchronize()
+    a = big.slot_state(0).cpu().double().numpy()
+    b = big.slot_state(1).cpu().double().numpy()
+    e = rel(a, b)
+    print(f"2.9B prefill T={T} vs {T} GPU steps: state rel L2 {e:.3e}")
+    assert e <= TOL
+    cnt = big.counters().cpu().numpy()
+    assert cnt[0] == cnt[1] == T
