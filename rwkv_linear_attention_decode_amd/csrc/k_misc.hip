@@ -11,17 +11,27 @@
 // One workgroup.  Decode: checks every row's slot (range, duplicates) and
 // token (range), writes sanitized copies, bumps each valid slot's counter.
 // Prefill: checks tokens and bumps the slot's counter by n_tok.
+// Rows whose slot repeats an earlier row's slot are dropped (the first
+// occurrence keeps it).  The slot list is scanned from LDS when it fits.
+constexpr int VALIDATE_LDS_ROWS = 4096;
 __global__ __launch_bounds__(256) void k_validate(ValidateArgs a) {
+  __shared__ int s_slot[VALIDATE_LDS_ROWS];
+  const bool in_lds = a.n_rows <= VALIDATE_LDS_ROWS;
+  if (in_lds) {
+    for (int b = threadIdx.x; b < a.n_rows; b += 256) s_slot[b] = a.slot_idx[b];
+    __syncthreads();
+  }
+  const int* list = in_lds ? s_slot : a.slot_idx;
   uint32_t bits = 0;
   for (int b = threadIdx.x; b < a.n_rows; b += 256) {
-    const int s = a.slot_idx[b];
+    const int s = list[b];
     int out = s;
     if (s < 0 || (int64_t)s >= a.n_slots) {
       bits |= ERRB_SLOT_RANGE;
       out = -1;
     } else {
       for (int j = 0; j < b; ++j)
-        if (a.slot_idx[j] == s) {
+        if (list[j] == s) {
           bits |= ERRB_SLOT_DUP;
           out = -1;
           break;

@@ -251,7 +251,7 @@ static void mm_launch(int ks, dim3 grid, hipStream_t st, const ProjArgs& a) {
       return;
     }
   }
-  if constexpr (mm_lds_bytes(TM, TN, 128) <= 65536) {
+  if constexpr (mm_lds_bytes(TM, TN, 128) <= 81920) {
     if (ks == 128) {
       hipLaunchKernelGGL((k_mm<TM, TN, 128>), grid, dim3(256), 0, st, a);
       return;
@@ -263,14 +263,15 @@ static void mm_launch(int ks, dim3 grid, hipStream_t st, const ProjArgs& a) {
 static bool mm_cfg_ok(int tm, int tn, int ks) {
   if (!((tm == 1 || tm == 2 || tm == 4 || tm == 8) && (tn == 2 || tn == 4))) return false;
   if (ks == 32) return tm >= 2;
-  if (ks == 128) return mm_lds_bytes(tm, tn, 128) <= 65536;
+  if (ks == 128) return mm_lds_bytes(tm, tn, 128) <= 81920;
   return ks == 64;
 }
 
-// Default tile shape by problem shape, from a sweep of (tm, tn, ks, split)
-// over the 2.9B projections at M = 64, 256 and 512 on MI355X: output widths
-// of one model width (value, output projection) favour narrow tiles with a K
-// split, the wide vocabulary head favours 128 x 128 tiles, the rest 64 x 64.
+// Default tile shape by problem shape, from sweeps of (tm, tn, ks, split)
+// over the 2.9B projections at M = 64, 256 and 512 on MI355X with weights
+// streamed from HBM: output widths of one model width (value, output
+// projection) favour narrow tiles with a K split, the wide vocabulary head
+// favours 128 x 128 tiles, the rest 64 x 64.
 static void mm_choose(const ProjArgs& a, int total_rows, int* tm, int* tn, int* ks) {
   const int M = a.M, N = total_rows;
   int K = a.K;
@@ -290,7 +291,8 @@ static void mm_choose(const ProjArgs& a, int total_rows, int* tm, int* tn, int* 
   } else if (N >= 32768) {
     *tm = M <= 64 ? 2 : 4; *tn = 4; *ks = 64;
   } else {
-    *tm = 2; *tn = M >= 512 ? 4 : 2; *ks = 64;
+    // 64 x 64 tiles; 128-deep stages except for the widest outputs at M = 256
+    *tm = 2; *tn = 2; *ks = (M <= 64 || M >= 512 || N <= 8192) ? 128 : 64;
   }
 }
 

@@ -536,8 +536,10 @@ __global__ __launch_bounds__(64) void k_wkv_post(WkvArgs a) {
 hipError_t launch_wkv_prep(const WkvArgs& a, hipStream_t st) {
   if (a.Lin > LIN_MAX) return hipErrorInvalidValue;
   switch (wkv_nchk(a)) {
+    // precomputed adapters: only wave 0 has work, so one wave per (token, head)
+    case 0: hipLaunchKernelGGL(k_wkv_prep<0>, dim3(a.B * a.H), dim3(64), 0, st, a); break;
 #define X(n) case n: hipLaunchKernelGGL(k_wkv_prep<n>, dim3(a.B * a.H), dim3(256), 0, st, a); break;
-    X(0) WKV_NCHK_CASES(X)
+    WKV_NCHK_CASES(X)
 #undef X
     default: return hipErrorInvalidValue;
   }
