@@ -219,6 +219,8 @@ def batched(R, args, shape, m, B):
     import synth
     wl = synth.WORKLOADS[f"decode_b{B}_{shape.name}"]
     lens = synth.prompt_lengths(wl, B)
+    if args.prompt_len > 0:        # profiling aid: same decode shapes, short prompts
+        lens = np.full(B, args.prompt_len, dtype=np.int64)
     slots_l = list(range(B))
     slots = i32(slots_l)
     m.reset(slots)
@@ -342,6 +344,9 @@ def main():
     ap.add_argument("--batched-steps", type=int, default=128)
     ap.add_argument("--prefill", default="128,512,2048", help="prefill T values ('' = none)")
     ap.add_argument("--big", default="256", help="batched-decode B values of the 7.2B shape ('' = none)")
+    ap.add_argument("--prompt-len", type=int, default=0,
+                    help="batched decode: fixed prompt length instead of the workload's 20-2000 "
+                         "(profiling runs only; the decode step shapes do not change)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
