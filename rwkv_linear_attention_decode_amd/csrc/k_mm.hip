@@ -31,7 +31,10 @@
 // (measured with SQ_LDS_BANK_CONFLICT); + 16 removes them.
 constexpr int MM_PAD = 16;
 
-template <int TM, int TN, int KS>
+// PIPE = 1 runs the K loop as a three-deep software pipeline (LDS fragment
+// reads of the next stage overlap the current stage's MFMAs); it costs
+// 2 (TM + TN) KS / 32 fragment registers and pays off on some shapes only.
+template <int TM, int TN, int KS, int PIPE>
 __global__ __launch_bounds__(256) void k_mm(ProjArgs a) {
   constexpr int MT = 32 * TM, NT = 32 * TN;
   constexpr int CPR = KS / 8;          // 16-byte chunks per row and stage
@@ -117,6 +120,7 @@ __global__ __launch_bounds__(256) void k_mm(ProjArgs a) {
     }
   };
 
+  if constexpr (!PIPE) {
   if (st0 < st1) {
     load(st0);
     store(0);
@@ -144,6 +148,57 @@ __global__ __launch_bounds__(256) void k_mm(ProjArgs a) {
     if (more) store(buf ^ 1);
     __syncthreads();
     buf ^= 1;
+  }
+  } else {
+  // Software pipeline: the fragments of stage s + 1 are read from LDS while
+  // the MFMAs of stage s run, stage s + 2 waits in registers and is written
+  // to LDS after them, and stage s + 3 is in flight from global memory.
+  constexpr int KH = KS / 32;
+  half8 fa[2][KH][TM], fb[2][KH][TN];
+  auto read_frags = [&](int buf, half8 (*pa)[TM], half8 (*pb)[TN]) {
+#pragma unroll
+    for (int h = 0; h < KH; ++h) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        pa[h][i] = *reinterpret_cast<const half8*>(&As[buf][wm0 + 16 * i + fr][32 * h + fk]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        pb[h][j] = *reinterpret_cast<const half8*>(&Bs[buf][wn0 + 16 * j + fr][32 * h + fk]);
+    }
+  };
+  auto mfmas = [&](half8 (*pa)[TM], half8 (*pb)[TN]) {
+#pragma unroll
+    for (int h = 0; h < KH; ++h)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[h][i], pb[h][j], acc[i][j], 0, 0, 0);
+  };
+  const int nrel = st1 - st0;
+  if (nrel > 0) {
+    load(st0);
+    store(0);
+    if (nrel > 1) load(st0 + 1);
+    __syncthreads();
+    if (nrel > 1) store(1);
+    read_frags(0, fa[0], fb[0]);
+    if (nrel > 2) load(st0 + 2);
+    __syncthreads();
+  }
+  for (int r0 = 0; r0 < nrel; r0 += 2) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int r = r0 + p;
+      if (r < nrel) {
+        if (r + 1 < nrel) read_frags((r + 1) & 1, fa[p ^ 1], fb[p ^ 1]);
+        mfmas(fa[p], fb[p]);
+        if (r + 2 < nrel) store(r & 1);
+        if (r + 3 < nrel) load(st0 + r + 3);
+        __syncthreads();
+      }
+    }
+  }
   }
 
   // D layout: lane l holds rows 4 (l / 16) + e, column l % 16 of each 16 x 16 block
@@ -243,75 +298,95 @@ int mm_plan(ProjArgs& a, int total_rows, int tm, int tn, int ks, int split_req, 
 // LDS bytes of a k_mm instantiation (two stage buffers of A and W rows)
 static constexpr int mm_lds_bytes(int tm, int tn, int ks) { return 2 * 32 * (tm + tn) * (ks + MM_PAD) * 2; }
 
-template <int TM, int TN>
-static void mm_launch(int ks, dim3 grid, hipStream_t st, const ProjArgs& a) {
+template <int TM, int TN, int PIPE>
+static void mm_launch_p(int ks, dim3 grid, hipStream_t st, const ProjArgs& a) {
   if constexpr (TM >= 2) {
     if (ks == 32) {
-      hipLaunchKernelGGL((k_mm<TM, TN, 32>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_mm<TM, TN, 32, PIPE>), grid, dim3(256), 0, st, a);
       return;
     }
   }
-  if constexpr (mm_lds_bytes(TM, TN, 128) <= 81920) {
+  if constexpr (mm_lds_bytes(TM, TN, 128) <= 81920 && !(PIPE && TM + TN > 4)) {
     if (ks == 128) {
-      hipLaunchKernelGGL((k_mm<TM, TN, 128>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_mm<TM, TN, 128, PIPE>), grid, dim3(256), 0, st, a);
       return;
     }
   }
-  hipLaunchKernelGGL((k_mm<TM, TN, 64>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_mm<TM, TN, 64, PIPE>), grid, dim3(256), 0, st, a);
 }
 
-static bool mm_cfg_ok(int tm, int tn, int ks) {
-  if (!((tm == 1 || tm == 2 || tm == 4 || tm == 8) && (tn == 2 || tn == 4))) return false;
+template <int TM, int TN>
+static void mm_launch(int ks, int pipe, dim3 grid, hipStream_t st, const ProjArgs& a) {
+  if constexpr (TM + TN <= 6) {
+    if (pipe) {
+      mm_launch_p<TM, TN, 1>(ks, grid, st, a);
+      return;
+    }
+  }
+  mm_launch_p<TM, TN, 0>(ks, grid, st, a);
+}
+
+static bool mm_cfg_ok(int tm, int tn, int ks, int pipe) {
+  if (pipe && (tm + tn > 6 || (ks == 128 && tm + tn > 4))) return false;
+  if (!((tm == 1 || tm == 2 || tm == 4) && (tn == 2 || tn == 4))) return false;
   if (ks == 32) return tm >= 2;
   if (ks == 128) return mm_lds_bytes(tm, tn, 128) <= 81920;
   return ks == 64;
 }
 
-// Default tile shape by problem shape, from sweeps of (tm, tn, ks, split)
-// over the 2.9B projections at M = 64, 256 and 512 on MI355X with weights
-// streamed from HBM: output widths of one model width (value, output
-// projection) favour narrow tiles with a K split, the wide vocabulary head
-// favours 128 x 128 tiles, the rest 64 x 64.
-static void mm_choose(const ProjArgs& a, int total_rows, int* tm, int* tn, int* ks) {
+// Default plan by problem shape, from a sweep of (tm, tn, ks, pipe, split)
+// over the 2.9B and 7.2B projections at M = 64, 256 and 512 on MI355X with
+// the weights streamed from HBM (rotated over six copies) and random
+// operands.  "Narrow" outputs are one model width (value, output
+// projection), "head" the vocabulary, "wide" the rest (key, input
+// projection, adapters).  split 0 = automatic.
+struct MmPlan {
+  int tm, tn, ks, pipe, split;
+};
+static MmPlan mm_choose(const ProjArgs& a, int total_rows) {
   const int M = a.M, N = total_rows;
   int K = a.K;
   for (int i = 0; i < a.nseg; ++i)
     if (a.seg[i].W && a.seg[i].K > K) K = a.seg[i].K;
-  if (M <= 32) {
-    *tm = 1; *tn = 2; *ks = 128;
-  } else if (N <= 4096) {
-    if (M <= 64) {
-      *tm = 1; *tn = 2; *ks = 128;
-    } else if (M <= 256) {
-      const bool deep = K >= 8192;
-      *tm = deep ? 2 : 1; *tn = deep ? 4 : 2; *ks = deep ? 64 : 128;
-    } else {
-      *tm = 4; *tn = 4; *ks = 64;
-    }
-  } else if (N >= 32768) {
-    *tm = M <= 64 ? 2 : 4; *tn = 4; *ks = 64;
-  } else {
-    // 64 x 64 tiles; 128-deep stages except for the widest outputs at M = 256
-    *tm = 2; *tn = 2; *ks = (M <= 64 || M >= 512 || N <= 8192) ? 128 : 64;
+  if (M <= 32) return {1, 2, 128, 0, 0};
+  if (N <= 4096) {                                   // narrow
+    if (M <= 64) return {1, 2, 128, 0, 0};
+    if (K >= 8192) return {K >= 16384 ? 4 : (M <= 256 ? 2 : 4), 4, 64, 0, 6};
+    return M <= 256 ? MmPlan{1, 2, 128, 0, 0} : MmPlan{2, 2, 128, 0, 1};
   }
+  if (N >= 32768) return {M <= 64 ? 2 : 4, 4, 64, 0, 0};   // head
+  if (M <= 64) return {2, 2, 128, 0, 0};                  // wide
+  if (M <= 256) {
+    if (K >= 4096) return N >= 16384 ? MmPlan{4, 2, 64, 1, 1} : MmPlan{4, 4, 64, 0, 2};
+    return N <= 8192 ? MmPlan{2, 2, 128, 0, 0} : MmPlan{2, 2, 64, 1, 0};
+  }
+  return N >= 10240 ? MmPlan{2, 4, 32, 1, 1} : MmPlan{4, 2, 64, 1, 1};
 }
 
 hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int tm, int tn, int ks,
                            int split, hipStream_t st) {
-  if (tm <= 0 || tn <= 0 || ks <= 0) mm_choose(a, total_rows, &tm, &tn, &ks);
-  if (!mm_cfg_ok(tm, tn, ks)) return hipErrorInvalidValue;
+  // ks >= 1000: the software-pipelined loop with stage depth ks - 1000
+  int pipe = 0;
+  if (ks >= 1000) {
+    pipe = 1;
+    ks -= 1000;
+  }
+  if (tm <= 0 || tn <= 0 || ks <= 0) {
+    const MmPlan p = mm_choose(a, total_rows);
+    tm = p.tm; tn = p.tn; ks = p.ks; pipe = p.pipe;
+    if (split <= 0) split = p.split;
+  }
+  if (!mm_cfg_ok(tm, tn, ks, pipe)) return hipErrorInvalidValue;
   const int items = mm_plan(a, total_rows, tm, tn, ks, split, part_floats);
   if (items < 0) return hipErrorInvalidValue;
   const dim3 grid(((items + 7) / 8) * 8);
   switch (tm * 10 + tn) {
-    case 12: mm_launch<1, 2>(ks, grid, st, a); break;
-    case 14: mm_launch<1, 4>(ks, grid, st, a); break;
-    case 22: mm_launch<2, 2>(ks, grid, st, a); break;
-    case 24: mm_launch<2, 4>(ks, grid, st, a); break;
-    case 42: mm_launch<4, 2>(ks, grid, st, a); break;
-    case 82: mm_launch<8, 2>(ks, grid, st, a); break;
-    case 84: mm_launch<8, 4>(ks, grid, st, a); break;
-    default: mm_launch<4, 4>(ks, grid, st, a); break;
+    case 12: mm_launch<1, 2>(ks, pipe, grid, st, a); break;
+    case 14: mm_launch<1, 4>(ks, pipe, grid, st, a); break;
+    case 22: mm_launch<2, 2>(ks, pipe, grid, st, a); break;
+    case 24: mm_launch<2, 4>(ks, pipe, grid, st, a); break;
+    case 42: mm_launch<4, 2>(ks, pipe, grid, st, a); break;
+    default: mm_launch<4, 4>(ks, pipe, grid, st, a); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -338,17 +413,18 @@ hipError_t launch_gemm(ProjArgs a, int total_rows, int64_t part_floats, hipStrea
   return launch_gemm_cfg(a, total_rows, part_floats, 0, 0, 0, 0, st);
 }
 
-// Template arguments as a trace prints them, e.g. "k_mm<4, 4, 64>", for an
+// Template arguments as a trace prints them, e.g. "k_mm<4, 4, 64, 0>", for an
 // M x N x K projection with the default plan.
 const char* gemm_kernel_name(int M, int N, int K) {
   ProjArgs a;
   memset(&a, 0, sizeof a);
   a.M = M;
   a.K = K;
-  int tm, tn, ks;
-  mm_choose(a, N, &tm, &tn, &ks);
-  static char names[4][2][3][24];
-  char* s = names[tm == 1 ? 0 : tm == 2 ? 1 : tm == 4 ? 2 : 3][tn == 2 ? 0 : 1][ks == 32 ? 0 : ks == 64 ? 1 : 2];
-  if (!s[0]) snprintf(s, sizeof(names[0][0][0]), "k_mm<%d, %d, %d>", tm, tn, ks);
+  const MmPlan p = mm_choose(a, N);
+  const int tm = p.tm, tn = p.tn, ks = p.ks, pipe = p.pipe;
+  static char names[4][2][3][2][28];
+  char* s = names[tm == 1 ? 0 : tm == 2 ? 1 : tm == 4 ? 2 : 3][tn == 2 ? 0 : 1][ks == 32 ? 0 : ks == 64 ? 1 : 2]
+                 [pipe];
+  if (!s[0]) snprintf(s, sizeof(names[0][0][0][0]), "k_mm<%d, %d, %d, %d>", tm, tn, ks, pipe);
   return s;
 }
