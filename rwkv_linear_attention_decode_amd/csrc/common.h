@@ -99,11 +99,6 @@ struct ProjArgs {
 
 RW_DEV float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
-RW_DEV float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
 
 // Sum over each aligned group of 16 lanes, every lane of the group gets the
 // same total.  DPP lane moves (VALU): quad_perm [1,0,3,2] and [2,3,0,1],
@@ -120,6 +115,18 @@ RW_DEV float sum16(float v) {
   v += dpp<0x141>(v);  // row_half_mirror
   v += dpp<0x140>(v);  // row_mirror
   return v;
+}
+
+// Sum over the 64 lanes of a wave (all lanes active): 16-lane sums by DPP,
+// then the four row sums read as scalars and added in a fixed order, so
+// every lane returns the same value.
+RW_DEV float wave_sum(float v) {
+  const int s = __builtin_bit_cast(int, sum16(v));
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(s, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(s, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(s, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(s, 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 RW_DEV float wave_max(float v) {

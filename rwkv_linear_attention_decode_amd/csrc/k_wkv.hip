@@ -107,10 +107,11 @@ RW_DEV void wkv_prologue(const WkvArgs& a, int b, int h, HeadVecs& hv, float* s_
       zv += (e0 >= e2 && e0 < e3) ? s : 0.f;
       zg += e0 >= e3 ? s : 0.f;
     }
-    zw += __shfl_xor(zw, 1); zw += __shfl_xor(zw, 2);
-    za += __shfl_xor(za, 1); za += __shfl_xor(za, 2);
-    zv += __shfl_xor(zv, 1); zv += __shfl_xor(zv, 2);
-    zg += __shfl_xor(zg, 1); zg += __shfl_xor(zg, 2);
+    // the four quarters of a channel are lanes 4i .. 4i+3: quad sums by DPP
+    zw += dpp<0xB1>(zw); zw += dpp<0x4E>(zw);
+    za += dpp<0xB1>(za); za += dpp<0x4E>(za);
+    zv += dpp<0xB1>(zv); zv += dpp<0x4E>(zv);
+    zg += dpp<0xB1>(zg); zg += dpp<0x4E>(zg);
     if (qd == 0) {
       // decay = exp(-exp(-softplus(-z) - 0.5)) = exp(-e^{-1/2} sigmoid(z))
       const float sw = 1.0f / (1.0f + expf(-(w0 + zw)));
