@@ -45,9 +45,11 @@ def log(*a):
 
 
 # ---------------------------------------------------------------- algorithmic bytes
-def class_bytes(s, B: int, nnz: int, sparse: bool):
+def class_bytes(s, B: int, nnz: int, sparse: bool, fused_value: bool = False):
     """Compulsory HBM bytes per launch of each kernel class for B decode rows:
-    every weight read once, activations / state read and written once."""
+    every weight read once, activations / state read and written once.  With
+    the value fused into the key projection (B <= 2) the active value rows
+    count in that kernel, and the fold only moves the residual."""
     C, F, V, H = s.n_embd, s.ffn, s.vocab, s.n_head
     Din = s.d_w + s.d_a + s.d_v + s.d_g
     n_in = 3 * C + Din
@@ -62,6 +64,9 @@ def class_bytes(s, B: int, nnz: int, sparse: bool):
         b["cmix_value"] = nnz * C * 2 + B * F * 4 + ns * B * C * 4
     else:
         b["cmix_value"] = F * C * 2 + B * F * 2 + B * C * 4 * 2
+    if fused_value:
+        b["cmix_key"] += nnz * C * 2
+        b["cmix_value"] = B * C * 4 * 2
     b["head"] = V * C * 2 + B * C * 4 + B * V * 4
     b["other"] = B * C * 2 + B * C * 4
     return b
@@ -75,7 +80,7 @@ def class_flops(s, B: int):
 
 
 def step_bytes(s, B, nnz, sparse):
-    cb = class_bytes(s, B, nnz, sparse)
+    cb = class_bytes(s, B, nnz, sparse)   # the same total with or without the fused value
     L = s.n_layer
     per_layer = 2 * cb["ln_mix"] + cb["proj_in"] + cb["wkv"] + cb["proj_out"] + cb["cmix_key"] + cb["cmix_value"]
     greedy = B * s.vocab * 4 * 3   # logits read, occurrences read + written
@@ -197,7 +202,8 @@ def decode_b1(R, args, shape, m):
 
 def roofline_b1(R, shape, m, kb, nnz, slot, tok, logits):
     """Dominant kernel class of the B=1 step, timed in isolation with HIP events."""
-    cb = class_bytes(shape, 1, nnz, True)
+    fused = bool(R.rwkv7_get_option(m.handle, R.OPT_FUSE_VALUE))
+    cb = class_bytes(shape, 1, nnz, True, fused)
     dom = max((k for k in kb if k in cb and k != "other"), key=lambda k: kb[k]["ms_per_step"])
     cls = R.K_NAMES.index(dom)
     # a per-layer class is swept over all layers (as inside a step, no weight is re-read

@@ -200,6 +200,9 @@ const char* rwkv7_last_error(void);
 #define RWKV7_OPT_KERNEL_TIMING 4  /* 1: bracket every launch with HIP events (no graph) */
 #define RWKV7_OPT_PREFILL_CHUNK 5  /* tokens per prefill chunk (<= the workspace's max_T) */
 #define RWKV7_OPT_FUSE_LN 6        /* 1 (default): LayerNorm + token shift inside the GEMV path */
+#define RWKV7_OPT_FUSE_VALUE 7     /* 1 (default): on the GEMV path (B <= 2, sparse), each key
+                                      workgroup also adds its active rows' value contributions
+                                      into per-workgroup partial sums, folded in a fixed order */
 
 int rwkv7_set_option(rwkv7_model* model, int32_t key, int64_t value);
 int rwkv7_get_option(const rwkv7_model* model, int32_t key, int64_t* value);

@@ -23,6 +23,7 @@ ERR_SLOT_RANGE, ERR_SLOT_DUP, ERR_TOKEN_RANGE, ERR_ALL_NAN = 1, 2, 4, 8
 F32, F16 = 0, 1
 OPT_USE_GRAPH, OPT_GEMV_MAX_B, OPT_SPARSE_MAX_B, OPT_KERNEL_TIMING, OPT_PREFILL_CHUNK = 1, 2, 3, 4, 5
 OPT_FUSE_LN = 6
+OPT_FUSE_VALUE = 7
 K_LN_MIX, K_PROJ_IN, K_WKV, K_PROJ_OUT, K_CMIX_KEY, K_CMIX_VALUE, K_HEAD, K_OTHER = range(8)
 K_NAMES = ("ln_mix", "proj_in", "wkv", "proj_out", "cmix_key", "cmix_value", "head", "other")
 

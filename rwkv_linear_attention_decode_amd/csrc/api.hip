@@ -143,6 +143,8 @@ struct Ws {
   float *q_d, *q_a, *q_b, *q_kt, *q_v, *q_g, *q_bonus, *q_y;
   float* part;            // split-K partial sums of the MFMA projections
   int64_t part_floats;
+  float* vpart;           // value partials of the fused key projection
+  int vpart_nwg;
   uint64_t bytes;
 };
 
@@ -184,6 +186,9 @@ Ws ws_layout(const Dims& d, int R, char* base) {
   w.q_bonus = (float*)take(r * d.H * 4);
   w.part_floats = (int64_t)(r * 16 * C);
   w.part = (float*)take(r * 16 * C * 4);
+  // value partials of the fused key projection (B <= 2 rows, 16 key rows per workgroup)
+  w.vpart_nwg = (int)((F + 15) / 16);
+  w.vpart = (float*)take((uint64_t)w.vpart_nwg * (r < 2 ? r : 2) * C * 4);
   w.bytes = off;
   return w;
 }
@@ -218,7 +223,7 @@ struct rwkv7_model {
   Dims d;
   Packed pk;
   int64_t opt_graph = 1, opt_gemv_max = 2, opt_sparse_max = 4, opt_timing = 0, opt_chunk = 512,
-          opt_fuse_ln = 1;
+          opt_fuse_ln = 1, opt_fuse_value = 1;
   std::vector<TimedLaunch> pending;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> free_events;
   double t_ms[RWKV7_K_COUNT] = {0};
@@ -378,7 +383,7 @@ WkvArgs wkv_args(const rwkv7_model* m, int l, float* pool, int64_t n_slots, cons
 }
 
 struct Path {
-  bool gemv, sparse, fused;
+  bool gemv, sparse, fused, fuse_value;
 };
 
 Path decode_path(const rwkv7_model* m, int B) {
@@ -387,6 +392,8 @@ Path decode_path(const rwkv7_model* m, int B) {
   p.sparse = B <= m->opt_sparse_max && B <= cmix_sparse_max_b() && m->d.F <= 16384 &&
              m->d.F % 1024 == 0 && m->d.C % 64 == 0;
   p.fused = p.gemv && m->opt_fuse_ln && gemv_fused_ok(B, m->d.C);
+  p.fuse_value = p.gemv && p.sparse && B <= 2 && m->opt_fuse_value && m->d.C % 8 == 0 &&
+                 m->d.C / 8 <= 512;
   return p;
 }
 
@@ -465,6 +472,11 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
     else
       pk.seg[0] = mkseg(0, d.F, EPI_RELU2, w.xk, C, w.pre, d.F, q.b_key);
     if (!path.sparse) pk.seg[0].out_f16 = 1;   // the dense (MFMA) value projection's input
+    if (path.fuse_value) {
+      pk.vW = q.w_val_hm;
+      pk.vpart = w.vpart;
+      pk.vC = C;
+    }
     if (path.fused) {
       pk.ln = LnPro{w.x, q.ln2_w, q.ln2_b, pool, d.slot_floats, n_slots, lo + C, w.slots, w.u_ffn, LNP_MIX, 0};
       pk.seg[0].mix = q.mu_k;
@@ -478,7 +490,16 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
     }
     RUN(RWKV7_K_CMIX_KEY, "cmix_key", proj(path.gemv, pk, d.F, w, st));
 
-    if (path.sparse) {
+    if (path.fuse_value) {
+      CmixFoldArgs fa;
+      memset(&fa, 0, sizeof fa);
+      fa.part = w.vpart; fa.nwg = (d.F + gemv_rows_per_wg(B, C) - 1) / gemv_rows_per_wg(B, C);
+      fa.mask = w.mask; fa.x = w.x; fa.u_ffn = path.fused ? w.u_ffn : nullptr;
+      fa.pool = pool; fa.slot_stride = d.slot_floats; fa.n_slots = n_slots; fa.shift_off = lo + C;
+      fa.slots = w.slots; fa.B = B; fa.C = C; fa.F = d.F;
+      if (l == d.L - 1) { fa.dbg_idx = w.dbg_idx; fa.dbg_cnt = w.dbg_cnt; }
+      RUN(RWKV7_K_CMIX_VALUE, "cmix_fold", launch_cmix_fold(fa, st));
+    } else if (path.sparse) {
       CmixArgs ca;
       memset(&ca, 0, sizeof ca);
       ca.pre = w.pre; ca.mask = w.mask; ca.Wv = q.w_val_hm;
@@ -1000,10 +1021,12 @@ int rwkv7_set_option(rwkv7_model* m, int32_t key, int64_t value) {
       if (value < 1) return fail(RWKV7_EINVAL, "PREFILL_CHUNK must be >= 1");
       m->opt_chunk = value; break;
     case RWKV7_OPT_FUSE_LN: m->opt_fuse_ln = value ? 1 : 0; break;
+    case RWKV7_OPT_FUSE_VALUE: m->opt_fuse_value = value ? 1 : 0; break;
     default: return fail(RWKV7_EINVAL, "unknown option %d", key);
   }
   // cached graphs bake in the kernel path: drop them when it may change
-  if (key == RWKV7_OPT_GEMV_MAX_B || key == RWKV7_OPT_SPARSE_MAX_B || key == RWKV7_OPT_FUSE_LN)
+  if (key == RWKV7_OPT_GEMV_MAX_B || key == RWKV7_OPT_SPARSE_MAX_B || key == RWKV7_OPT_FUSE_LN ||
+      key == RWKV7_OPT_FUSE_VALUE)
     drop_graphs(m);
   return RWKV7_OK;
 }
@@ -1017,6 +1040,7 @@ int rwkv7_get_option(const rwkv7_model* m, int32_t key, int64_t* value) {
     case RWKV7_OPT_KERNEL_TIMING: *value = m->opt_timing; break;
     case RWKV7_OPT_PREFILL_CHUNK: *value = m->opt_chunk; break;
     case RWKV7_OPT_FUSE_LN: *value = m->opt_fuse_ln; break;
+    case RWKV7_OPT_FUSE_VALUE: *value = m->opt_fuse_value; break;
     default: return fail(RWKV7_EINVAL, "unknown option %d", key);
   }
   return RWKV7_OK;
@@ -1106,7 +1130,8 @@ const char* rwkv7_kernel_name(const rwkv7_model* m, int32_t cls, int32_t B) {
     case RWKV7_K_PROJ_OUT:
       return p.gemv ? gemv_kernel_name(B, m->d.C, EPI_RESID) : gemm_kernel_name(B, m->d.C, m->d.C);
     case RWKV7_K_CMIX_KEY:
-      return p.gemv ? gemv_kernel_name(B, m->d.C, p.sparse ? EPI_PRE : -1) : gemm_kernel_name(B, m->d.F, m->d.C);
+      return p.gemv ? gemv_kernel_name(B, m->d.C, p.fuse_value ? -2 : p.sparse ? EPI_PRE : -1)
+                    : gemm_kernel_name(B, m->d.F, m->d.C);
     case RWKV7_K_HEAD:
       return p.gemv ? gemv_kernel_name(B, m->d.C, EPI_NONE) : gemm_kernel_name(B, m->d.V, m->d.C);
     case RWKV7_K_WKV: {
@@ -1116,6 +1141,7 @@ const char* rwkv7_kernel_name(const rwkv7_model* m, int32_t cls, int32_t B) {
       return name;
     }
     case RWKV7_K_CMIX_VALUE:
+      if (p.fuse_value) return B == 1 ? "k_cmix_fold<1>" : "k_cmix_fold<2>";
       return p.sparse ? cmix_sparse_kernel_name(B) : gemm_kernel_name(B, m->d.C, m->d.F);
     default: return kClassName[cls];
   }

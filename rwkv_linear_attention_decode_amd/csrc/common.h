@@ -92,6 +92,9 @@ struct ProjArgs {
   int split;         // MFMA path: K ranges per tile (1 = the epilogue runs in the GEMM)
   int total_rows;    // MFMA path: output columns over all segments (partial-sum row length)
   float* part;       // MFMA path, split > 1: fp32 partial sums [split][M][total_rows]
+  const half_t* vW;  // GEMV key path with the value fused: hidden-major W_val [rows][vC]
+  float* vpart;      // ... and its per-workgroup partial sums [workgroups][M][vC]
+  int vC;
   int tile0[MAX_SEGS + 1];  // MFMA path: first column tile of each segment (prefix sums)
   LnPro ln;
   Seg seg[MAX_SEGS];

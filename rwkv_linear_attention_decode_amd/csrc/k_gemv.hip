@@ -20,7 +20,13 @@ constexpr int kFusedMaxFloats = 80;
 
 // Epilogue family fixed at compile time (GV_MIXED reads it per segment);
 // it also gives each projection class its own kernel symbol in traces.
-enum : int { GV_MIXED = 0, GV_PRE = 1, GV_RESID = 2, GV_NONE = 3 };
+// GV_PREV: the channel-mix key (EPI_PRE) followed by that workgroup's share
+// of the sparse value projection: for each of its rows with h = relu(pre)^2
+// > 0 in some batch row, h times the row's W_val row is added into a
+// per-workgroup partial sum of the output, which k_cmix_fold adds up in a
+// fixed order.  Only active value rows are read, and the value work no
+// longer waits behind a separate compaction pass.
+enum : int { GV_MIXED = 0, GV_PRE = 1, GV_RESID = 2, GV_NONE = 3, GV_PREV = 4 };
 
 template <int B, int LPR, int NCH, int RPW, int EPK>
 __global__ __launch_bounds__(256) void k_gemv(ProjArgs a) {
@@ -172,13 +178,19 @@ __global__ __launch_bounds__(256) void k_gemv(ProjArgs a) {
 #pragma unroll
       for (int o = LPR / 2; o >= 1; o >>= 1) acc[i][b] += __shfl_xor(acc[i][b], o);
 
+  __shared__ float s_h[EPK == GV_PREV ? B : 1][EPK == GV_PREV ? ROWS_WG : 1];
+  if constexpr (EPK == GV_PREV) {
+    // rows past the end stay inactive
+    if (threadIdx.x < B * ROWS_WG) s_h[threadIdx.x / ROWS_WG][threadIdx.x % ROWS_WG] = 0.0f;
+    __syncthreads();
+  }
   if (lig == 0) {
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
       const int row = row_base + i;
       if (row < sg.row1) {
         const int n = row - sg.row0;
-        const int epi = EPK == GV_PRE ? EPI_PRE : EPK == GV_RESID ? EPI_RESID
+        const int epi = (EPK == GV_PRE || EPK == GV_PREV) ? EPI_PRE : EPK == GV_RESID ? EPI_RESID
                         : EPK == GV_NONE ? EPI_NONE : sg.epi;
         if (epi == EPI_PRE) {
           bool any = false;
@@ -187,6 +199,7 @@ __global__ __launch_bounds__(256) void k_gemv(ProjArgs a) {
             const float pre = acc[i][b] + sg.aux[n];
             ((float*)sg.out)[(long)b * sg.ld_out + n] = pre;
             any |= pre > 0.0f;
+            if constexpr (EPK == GV_PREV) s_h[b][row - row_wg] = pre > 0.0f ? pre * pre : 0.0f;
           }
           if (sg.mask) sg.mask[n] = any ? 1 : 0;
         } else {
@@ -201,6 +214,73 @@ __global__ __launch_bounds__(256) void k_gemv(ProjArgs a) {
               epi_store(sg, n, b, acc[i][b]);
           }
         }
+      }
+    }
+  }
+
+  if constexpr (EPK == GV_PREV) {
+    __syncthreads();
+    // rows of this workgroup with any active batch row, as a bit set
+    unsigned act = 0;
+#pragma unroll
+    for (int i = 0; i < ROWS_WG; ++i) {
+      bool any = false;
+#pragma unroll
+      for (int b = 0; b < B; ++b) any |= s_h[b][i] > 0.0f;
+      act |= any ? (1u << i) : 0u;
+    }
+    // thread t owns 8-column chunks t and t + 256 of the output row
+    const int nchunk = a.vC / 8;
+    const int c0 = threadIdx.x, c1 = threadIdx.x + 256;
+    float pacc[B][2][8];
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { pacc[b][0][e] = 0.f; pacc[b][1][e] = 0.f; }
+    // up to four active rows per pass: their loads are issued together
+    while (act) {
+      int rr[4];
+      int nr = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        rr[u] = act ? __builtin_ctz(act) : 0;
+        nr += act ? 1 : 0;
+        act &= act - 1;
+      }
+      u32x4 w0[4], w1[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const half_t* wr = a.vW + (long)(row_wg + rr[u]) * a.vC;
+        w0[u] = (u < nr && c0 < nchunk) ? ld16(wr + c0 * 8) : u32x4{0u, 0u, 0u, 0u};
+        w1[u] = (u < nr && c1 < nchunk) ? ld16(wr + c1 * 8) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (u < nr) {
+          const half8 h0 = __builtin_bit_cast(half8, w0[u]);
+          const half8 h1 = __builtin_bit_cast(half8, w1[u]);
+#pragma unroll
+          for (int b = 0; b < B; ++b) {
+            const float hb = s_h[b][rr[u]];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              pacc[b][0][e] = fmaf(hb, (float)h0[e], pacc[b][0][e]);
+              pacc[b][1][e] = fmaf(hb, (float)h1[e], pacc[b][1][e]);
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      float* dst = a.vpart + ((long)blockIdx.x * B + b) * a.vC;
+      if (c0 < nchunk) {
+        stf4(dst + c0 * 8, floatx4{pacc[b][0][0], pacc[b][0][1], pacc[b][0][2], pacc[b][0][3]});
+        stf4(dst + c0 * 8 + 4, floatx4{pacc[b][0][4], pacc[b][0][5], pacc[b][0][6], pacc[b][0][7]});
+      }
+      if (c1 < nchunk) {
+        stf4(dst + c1 * 8, floatx4{pacc[b][1][0], pacc[b][1][1], pacc[b][1][2], pacc[b][1][3]});
+        stf4(dst + c1 * 8 + 4, floatx4{pacc[b][1][4], pacc[b][1][5], pacc[b][1][6], pacc[b][1][7]});
       }
     }
   }
@@ -228,6 +308,7 @@ bool gemv_fused_ok(int B, int K) {
 }
 
 static int gemv_epk(const ProjArgs& a) {
+  if (a.vW) return GV_PREV;
   int e = a.seg[0].epi;
   for (int i = 1; i < a.nseg; ++i)
     if (a.seg[i].epi != e) return GV_MIXED;
@@ -240,6 +321,7 @@ static void gemv_launch_epk(int epk, dim3 grid, hipStream_t st, const ProjArgs& 
     case GV_PRE: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_PRE>), grid, dim3(256), 0, st, a); break;
     case GV_RESID: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_RESID>), grid, dim3(256), 0, st, a); break;
     case GV_NONE: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_NONE>), grid, dim3(256), 0, st, a); break;
+    case GV_PREV: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_PREV>), grid, dim3(256), 0, st, a); break;
     default: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_MIXED>), grid, dim3(256), 0, st, a); break;
   }
 }
@@ -276,11 +358,11 @@ hipError_t launch_gemv(const ProjArgs& a, int total_rows, hipStream_t st) {
 
 // Template arguments as a trace prints them, e.g. "k_gemv<1, 64, 5, 4, 1>".
 const char* gemv_kernel_name(int B, int K, int epi) {
-  static char names[5][9][4][40];
+  static char names[5][9][5][40];
   if (!gemv_supported(B, K)) return "k_gemv";
   const int lpr = K == 256 ? 32 : 64;
   const int nch = K == 256 ? 1 : K / 512;
-  const int epk = epi == EPI_PRE ? GV_PRE : epi == EPI_RESID ? GV_RESID
+  const int epk = epi == -2 ? GV_PREV : epi == EPI_PRE ? GV_PRE : epi == EPI_RESID ? GV_RESID
                   : epi == EPI_NONE ? GV_NONE : GV_MIXED;
   char* s = names[B][nch][epk];
   if (!s[0])

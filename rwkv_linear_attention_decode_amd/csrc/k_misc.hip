@@ -345,22 +345,18 @@ constexpr int CMIX_MAXB = 4;
 constexpr int CMIX_COLS = 32;
 constexpr int CMIX_MAXPER = CMIX_MAXF / 256 / 4;  // mask words per compacting thread
 
-template <int B>
-__global__ __launch_bounds__(1024) void k_cmix_sparse(CmixArgs a) {
-  __shared__ unsigned short s_idx[CMIX_MAXF];
-  __shared__ int s_wcnt[4];
-  __shared__ float s_red[16][B][CMIX_COLS];
+// Ascending list of the set bytes of mask[0..F) into s_idx (threads 0..255
+// of a 1024-thread workgroup take part; all threads must call it).  Thread t
+// owns mask bytes [t*per, (t+1)*per), per = F/256 (a multiple of 4); bytes
+// are 0/1, so a word's popcount is its count.  Returns the count.
+RW_DEV int cmix_compact(const unsigned char* mask, int F, unsigned short* s_idx, int* s_wcnt) {
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-
-  // ---- compaction by threads 0..255: thread t owns mask bytes
-  // [t*per, (t+1)*per), per = F/256 (a multiple of 4); bytes are 0/1, so a
-  // word's popcount is its count.
-  const int words = a.F / 1024;
+  const int words = F / 1024;
   unsigned int mw[CMIX_MAXPER];
   int mine = 0, incl = 0;
   if (t < 256) {
-    const unsigned int* m32 = reinterpret_cast<const unsigned int*>(a.mask) + t * words;
+    const unsigned int* m32 = reinterpret_cast<const unsigned int*>(mask) + t * words;
 #pragma unroll
     for (int i = 0; i < CMIX_MAXPER; ++i) {
       mw[i] = i < words ? m32[i] : 0u;
@@ -387,6 +383,18 @@ __global__ __launch_bounds__(1024) void k_cmix_sparse(CmixArgs a) {
     }
   }
   __syncthreads();
+  return total;
+}
+
+template <int B>
+__global__ __launch_bounds__(1024) void k_cmix_sparse(CmixArgs a) {
+  __shared__ unsigned short s_idx[CMIX_MAXF];
+  __shared__ int s_wcnt[4];
+  __shared__ float s_red[16][B][CMIX_COLS];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+
+  const int total = cmix_compact(a.mask, a.F, s_idx, s_wcnt);
   if (a.dbg_idx && blockIdx.x == 0) {
     for (int i = t; i < total; i += 1024) a.dbg_idx[i] = s_idx[i];
     if (t == 0) *a.dbg_cnt = total;
@@ -469,6 +477,95 @@ __global__ __launch_bounds__(1024) void k_cmix_sparse(CmixArgs a) {
         a.pool[(long)slot * a.slot_stride + a.shift_off + col] = a.u_ffn[(long)b * a.C + col];
     }
   }
+}
+
+// x += the value partial sums of the fused key projection, in workgroup
+// order: thread t sums 8 columns over workgroups rg, rg + 256, ... (rg =
+// t / 4), then the 256 row groups meet in the same fixed-order reduction as
+// above.  Workgroup 0 also writes the debug active list when asked.
+template <int B>
+__global__ __launch_bounds__(1024) void k_cmix_fold(CmixFoldArgs a) {
+  __shared__ float s_red[16][B][CMIX_COLS];
+  __shared__ unsigned short s_idx[CMIX_MAXF];
+  __shared__ int s_wcnt[4];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int nsl = a.C / CMIX_COLS;
+  const int per_xcd = (nsl + 7) / 8;
+  const int slice = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (a.dbg_idx && blockIdx.x == 0) {
+    const int total = cmix_compact(a.mask, a.F, s_idx, s_wcnt);
+    for (int i = t; i < total; i += 1024) a.dbg_idx[i] = s_idx[i];
+    if (t == 0) *a.dbg_cnt = total;
+  }
+  if (slice >= nsl) return;
+  const int rg = t >> 2;
+  const int c8 = (t & 3) * 8;
+  const int cb = slice * CMIX_COLS + c8;
+  float acc[B][8];
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[b][e] = 0.f;
+  constexpr int U = 4;
+  for (int w0 = rg; w0 < a.nwg; w0 += 256 * U) {
+    floatx4 v[U][B][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int w = w0 + 256 * u;
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const float* p = a.part + ((long)w * B + b) * a.C + cb;
+        v[u][b][0] = w < a.nwg ? ldf4(p) : floatx4{0.f, 0.f, 0.f, 0.f};
+        v[u][b][1] = w < a.nwg ? ldf4(p + 4) : floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[b][e] += v[u][b][0][e];
+          acc[b][e + 4] += v[u][b][1][e];
+        }
+  }
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = acc[b][e];
+      v += __shfl_xor(v, 4);
+      v += __shfl_xor(v, 8);
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (lane < 4) s_red[wave][b][c8 + e] = v;
+    }
+  __syncthreads();
+  if (t < B * CMIX_COLS) {
+    const int b = t / CMIX_COLS;
+    const int col = slice * CMIX_COLS + t % CMIX_COLS;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) sum += s_red[w][b][t % CMIX_COLS];
+    a.x[(long)b * a.C + col] += sum;
+    if (a.u_ffn) {
+      const int slot = a.slots[b];
+      if (slot >= 0 && slot < a.n_slots)
+        a.pool[(long)slot * a.slot_stride + a.shift_off + col] = a.u_ffn[(long)b * a.C + col];
+    }
+  }
+}
+
+hipError_t launch_cmix_fold(const CmixFoldArgs& a, hipStream_t st) {
+  if (a.F > CMIX_MAXF || a.F % 1024 || a.C % CMIX_COLS || a.B < 1 || a.B > 2 || a.nwg < 1)
+    return hipErrorInvalidValue;
+  const dim3 grid((a.C / CMIX_COLS + 7) / 8 * 8);
+  if (a.B == 1)
+    hipLaunchKernelGGL(k_cmix_fold<1>, grid, dim3(1024), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_cmix_fold<2>, grid, dim3(1024), 0, st, a);
+  return hipGetLastError();
 }
 
 int cmix_sparse_max_b() { return CMIX_MAXB; }

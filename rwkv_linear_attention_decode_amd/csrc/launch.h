@@ -16,7 +16,8 @@ hipError_t launch_gemm(ProjArgs a, int total_rows, int64_t part_floats, hipStrea
 // ks (64 or 128) and K split; 0 selects the default / automatic value.
 hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int tm, int tn, int ks,
                            int split, hipStream_t st);
-// `epi`: the epilogue shared by every segment of the launch, or -1 when mixed
+// `epi`: the epilogue shared by every segment of the launch, -1 when mixed,
+// -2 for the key projection with the sparse value fused into it
 const char* gemv_kernel_name(int B, int K, int epi);
 const char* gemm_kernel_name(int M, int N, int K);
 
@@ -123,6 +124,26 @@ struct CmixArgs {
   int* dbg_cnt;               // optional: its length
 };
 hipError_t launch_cmix_sparse(const CmixArgs& a, hipStream_t st);
+
+// Fold of the per-workgroup value partial sums written by the fused key
+// projection: x[b][c] += sum over workgroups w (in order) of part[w][b][c],
+// then the channel-mix shift commit; optionally the union active list.
+struct CmixFoldArgs {
+  const float* part;          // [nwg][B][C]
+  int nwg;
+  const unsigned char* mask;  // [F] union over rows of (pre > 0), for the debug list
+  float* x;
+  const float* u_ffn;
+  float* pool;
+  int64_t slot_stride;
+  int64_t n_slots;
+  int64_t shift_off;
+  const int* slots;
+  int B, C, F;
+  int* dbg_idx;
+  int* dbg_cnt;
+};
+hipError_t launch_cmix_fold(const CmixFoldArgs& a, hipStream_t st);
 int cmix_sparse_max_b();
 const char* cmix_sparse_kernel_name(int B);
 

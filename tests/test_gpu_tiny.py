@@ -117,16 +117,18 @@ def test_tiny_free_running_greedy(model, W, R):
         tok = g
 
 
-@pytest.mark.parametrize("B,gemv,sparse,fuse", [
-    (1, 2, 4, 1), (1, 2, 4, 0), (1, 0, 4, 1), (1, 2, 0, 1), (1, 2, 0, 0), (2, 2, 4, 1),
-    (2, 2, 4, 0), (2, 0, 0, 1), (3, 2, 4, 1), (4, 4, 4, 1), (4, 4, 0, 1), (4, 0, 4, 1),
-    (5, 2, 4, 1), (8, 2, 4, 1)])
-def test_batched_step_paths(model, W, R, B, gemv, sparse, fuse):
-    """B independent rows through the GEMV / MFMA, sparse / dense and fused /
-    separate LayerNorm paths."""
+@pytest.mark.parametrize("B,gemv,sparse,fuse,fval", [
+    (1, 2, 4, 1, 1), (1, 2, 4, 1, 0), (1, 2, 4, 0, 1), (1, 0, 4, 1, 1), (1, 2, 0, 1, 1),
+    (1, 2, 0, 0, 1), (2, 2, 4, 1, 1), (2, 2, 4, 1, 0), (2, 2, 4, 0, 1), (2, 0, 0, 1, 1),
+    (3, 2, 4, 1, 1), (4, 4, 4, 1, 1), (4, 4, 0, 1, 1), (4, 0, 4, 1, 1), (5, 2, 4, 1, 1),
+    (8, 2, 4, 1, 1)])
+def test_batched_step_paths(model, W, R, B, gemv, sparse, fuse, fval):
+    """B independent rows through the GEMV / MFMA, sparse / dense, fused /
+    separate LayerNorm and fused / separate sparse value paths."""
     model.set_option(R.OPT_GEMV_MAX_B, gemv)
     model.set_option(R.OPT_SPARSE_MAX_B, sparse)
     model.set_option(R.OPT_FUSE_LN, fuse)
+    model.set_option(R.OPT_FUSE_VALUE, fval)
     try:
         slots = [(5 * i + 3) % NSLOT for i in range(B)]
         fresh(model, slots)
@@ -152,6 +154,7 @@ def test_batched_step_paths(model, W, R, B, gemv, sparse, fuse):
         model.set_option(R.OPT_GEMV_MAX_B, 2)
         model.set_option(R.OPT_SPARSE_MAX_B, 4)
         model.set_option(R.OPT_FUSE_LN, 1)
+        model.set_option(R.OPT_FUSE_VALUE, 1)
 
 
 def test_prefill_equals_steps_on_gpu(model, R):
