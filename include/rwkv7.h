@@ -203,6 +203,18 @@ const char* rwkv7_last_error(void);
 #define RWKV7_OPT_FUSE_VALUE 7     /* 1 (default): on the GEMV path (B <= 2, sparse), each key
                                       workgroup also adds its active rows' value contributions
                                       into per-workgroup partial sums, folded in a fixed order */
+/* Tile plan of one MFMA projection (B > GEMV_MAX_B and prefill); 0 (default) = the built-in
+   plan for the shape.  Otherwise the decimal digits "T N KKK P S" of the value give the
+   workgroup tile (32 T rows x 32 N columns, T in {1, 2, 4}, N in {2, 4}), the K stage depth
+   KKK (32, 64 or 128), the K loop P (0 plain, 1 pipelined LDS reads, 2 two stages of global
+   loads in flight) and the K split S (0 automatic); e.g. 2206420 = 64 x 64 tiles, 64-deep
+   stages, loop 2, automatic split.  Unsupported combinations fail with EINVAL. */
+#define RWKV7_OPT_GEMM_PLAN_PROJ_IN 8     /* r, k, v and the adapters' first stage */
+#define RWKV7_OPT_GEMM_PLAN_ADAPTERS 9    /* the adapters' second stage (decay, alpha, gates) */
+#define RWKV7_OPT_GEMM_PLAN_PROJ_OUT 10   /* W_o + residual */
+#define RWKV7_OPT_GEMM_PLAN_CMIX_KEY 11   /* channel-mix key */
+#define RWKV7_OPT_GEMM_PLAN_CMIX_VALUE 12 /* dense channel-mix value */
+#define RWKV7_OPT_GEMM_PLAN_HEAD 13       /* output head */
 
 int rwkv7_set_option(rwkv7_model* model, int32_t key, int64_t value);
 int rwkv7_get_option(const rwkv7_model* model, int32_t key, int64_t* value);

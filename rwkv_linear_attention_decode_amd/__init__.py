@@ -24,6 +24,19 @@ F32, F16 = 0, 1
 OPT_USE_GRAPH, OPT_GEMV_MAX_B, OPT_SPARSE_MAX_B, OPT_KERNEL_TIMING, OPT_PREFILL_CHUNK = 1, 2, 3, 4, 5
 OPT_FUSE_LN = 6
 OPT_FUSE_VALUE = 7
+# tile plan per MFMA projection: decimal digits "T N KKK P S" (0 = built-in)
+OPT_GEMM_PLAN_PROJ_IN = 8
+OPT_GEMM_PLAN_ADAPTERS = 9
+OPT_GEMM_PLAN_PROJ_OUT = 10
+OPT_GEMM_PLAN_CMIX_KEY = 11
+OPT_GEMM_PLAN_CMIX_VALUE = 12
+OPT_GEMM_PLAN_HEAD = 13
+
+
+def gemm_plan_code(tm, tn, ks, pipe=0, split=0):
+    """Value of an OPT_GEMM_PLAN_* option: tile 32*tm x 32*tn, stage depth ks,
+    K loop `pipe` (0, 1 or 2), K split (0 = automatic)."""
+    return ((tm * 10 + tn) * 1000 + ks) * 100 + pipe * 10 + split
 K_LN_MIX, K_PROJ_IN, K_WKV, K_PROJ_OUT, K_CMIX_KEY, K_CMIX_VALUE, K_HEAD, K_OTHER = range(8)
 K_NAMES = ("ln_mix", "proj_in", "wkv", "proj_out", "cmix_key", "cmix_value", "head", "other")
 

@@ -224,6 +224,8 @@ struct rwkv7_model {
   Packed pk;
   int64_t opt_graph = 1, opt_gemv_max = 2, opt_sparse_max = 4, opt_timing = 0, opt_chunk = 512,
           opt_fuse_ln = 1, opt_fuse_value = 1;
+  // tile plan per MFMA projection (RWKV7_OPT_GEMM_PLAN_* order), 0 = built-in
+  int64_t opt_plan[6] = {0, 0, 0, 0, 0, 0};
   std::vector<TimedLaunch> pending;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> free_events;
   double t_ms[RWKV7_K_COUNT] = {0};
@@ -300,10 +302,21 @@ Seg mkseg(int row0, int row1, int epi, const void* act, int ld_act, void* out, i
   return s;
 }
 
-hipError_t proj(bool gemv, ProjArgs& a, int total_rows, const Ws& w, hipStream_t st) {
+// A tile plan code (RWKV7_OPT_GEMM_PLAN_*): decimal digits tm tn kkk p s.
+struct PlanCode {
+  int tm, tn, ks, pipe, split;
+};
+static PlanCode decode_plan(int64_t v) {
+  return {(int)(v / 1000000 % 10), (int)(v / 100000 % 10), (int)(v / 100 % 1000), (int)(v / 10 % 10),
+          (int)(v % 10)};
+}
+
+hipError_t proj(bool gemv, ProjArgs& a, int total_rows, const Ws& w, hipStream_t st, int64_t plan = 0) {
   if (gemv) return launch_gemv(a, total_rows, st);
   a.part = w.part;
-  return launch_gemm(a, total_rows, w.part_floats, st);
+  if (plan == 0) return launch_gemm(a, total_rows, w.part_floats, st);
+  const PlanCode c = decode_plan(plan);
+  return launch_gemm_cfg(a, total_rows, w.part_floats, c.tm, c.tn, c.ks + 1000 * c.pipe, c.split, st);
 }
 
 // Input-projection segments: r | k | v | w1 | a1 | v1 | g1 of the fused matrix.
@@ -445,7 +458,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
     } else {
       RUN(RWKV7_K_LN_MIX, "ln_mix(tmix)", launch_ln_mix(la, st));
     }
-    RUN(RWKV7_K_PROJ_IN, "proj_in", proj(path.gemv, pa, d.Nin, w, st));
+    RUN(RWKV7_K_PROJ_IN, "proj_in", proj(path.gemv, pa, d.Nin, w, st, m->opt_plan[0]));
 
     WkvArgs wa = wkv_args(m, l, pool, n_slots, w, B, f16);
     wa.u_att = path.fused ? w.u_att : nullptr;
@@ -453,7 +466,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
       // many rows: the adapter outputs as one MFMA projection, WKV reads them
       ProjArgs pl;
       lora_args(d, q, w, B, pl);
-      RUN(RWKV7_K_PROJ_IN, "adapters", proj(false, pl, 4 * C, w, st));
+      RUN(RWKV7_K_PROJ_IN, "adapters", proj(false, pl, 4 * C, w, st, m->opt_plan[1]));
       wa.lo = w.lo;
     }
     RUN(RWKV7_K_WKV, "wkv", launch_wkv_decode(wa, st));
@@ -462,7 +475,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
     memset(&po, 0, sizeof po);
     po.W = q.w_o; po.K = C; po.M = B; po.nseg = 1;
     po.seg[0] = mkseg(0, C, EPI_RESID, w.yg, C, w.x, C);
-    RUN(RWKV7_K_PROJ_OUT, "proj_out", proj(path.gemv, po, C, w, st));
+    RUN(RWKV7_K_PROJ_OUT, "proj_out", proj(path.gemv, po, C, w, st, m->opt_plan[2]));
 
     ProjArgs pk;
     memset(&pk, 0, sizeof pk);
@@ -488,7 +501,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
       lc.out = w.xk; lc.out_q_stride = 0;
       RUN(RWKV7_K_LN_MIX, "ln_mix(cmix)", launch_ln_mix(lc, st));
     }
-    RUN(RWKV7_K_CMIX_KEY, "cmix_key", proj(path.gemv, pk, d.F, w, st));
+    RUN(RWKV7_K_CMIX_KEY, "cmix_key", proj(path.gemv, pk, d.F, w, st, m->opt_plan[3]));
 
     if (path.fuse_value) {
       CmixFoldArgs fa;
@@ -513,7 +526,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
       memset(&pv, 0, sizeof pv);
       pv.W = q.w_val_km; pv.K = d.F; pv.M = B; pv.nseg = 1;
       pv.seg[0] = mkseg(0, C, EPI_RESID, w.pre, d.F, w.x, C);
-      RUN(RWKV7_K_CMIX_VALUE, "cmix_value", proj(false, pv, C, w, st));
+      RUN(RWKV7_K_CMIX_VALUE, "cmix_value", proj(false, pv, C, w, st, m->opt_plan[4]));
       if (path.fused) {
         CommitArgs ca{w.u_ffn, pool, d.slot_floats, n_slots, lo + C, w.slots, B, C};
         RUN(RWKV7_K_OTHER, "commit shift", launch_commit_shift(ca, st));
@@ -537,7 +550,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
     lo.out = w.xo; lo.out_f16 = f16; lo.out_q_stride = 0;
     RUN(RWKV7_K_LN_MIX, "ln_out", launch_ln_mix(lo, st));
   }
-  RUN(RWKV7_K_HEAD, "head", proj(path.gemv, ph, d.V, w, st));
+  RUN(RWKV7_K_HEAD, "head", proj(path.gemv, ph, d.V, w, st, m->opt_plan[5]));
   return RWKV7_OK;
 }
 
@@ -572,11 +585,11 @@ int enqueue_prefill_chunk(rwkv7_model* m, float* pool, int64_t n_slots, int slot
 
     ProjArgs pa;
     proj_in_args(d, q, w, T, true, pa);
-    RUN(RWKV7_K_PROJ_IN, "proj_in", proj(false, pa, d.Nin, w, st));
+    RUN(RWKV7_K_PROJ_IN, "proj_in", proj(false, pa, d.Nin, w, st, m->opt_plan[0]));
 
     ProjArgs pl;
     lora_args(d, q, w, T, pl);
-    RUN(RWKV7_K_PROJ_IN, "adapters", proj(false, pl, 4 * C, w, st));
+    RUN(RWKV7_K_PROJ_IN, "adapters", proj(false, pl, 4 * C, w, st, m->opt_plan[1]));
     WkvArgs wa = wkv_args(m, l, pool, n_slots, w, T, true);
     wa.seq_slot = slot;
     wa.lo = w.lo;
@@ -588,7 +601,7 @@ int enqueue_prefill_chunk(rwkv7_model* m, float* pool, int64_t n_slots, int slot
     memset(&po, 0, sizeof po);
     po.W = q.w_o; po.K = C; po.M = T; po.nseg = 1;
     po.seg[0] = mkseg(0, C, EPI_RESID, w.yg, C, w.x, C);
-    RUN(RWKV7_K_PROJ_OUT, "proj_out", proj(false, po, C, w, st));
+    RUN(RWKV7_K_PROJ_OUT, "proj_out", proj(false, po, C, w, st, m->opt_plan[2]));
 
     LnMixArgs lc = la;
     lc.g = q.ln2_w; lc.b = q.ln2_b;
@@ -603,13 +616,13 @@ int enqueue_prefill_chunk(rwkv7_model* m, float* pool, int64_t n_slots, int slot
     pk.W = q.w_key; pk.K = C; pk.M = T; pk.nseg = 1;
     pk.seg[0] = mkseg(0, d.F, EPI_RELU2, w.xk, C, w.pre, d.F, q.b_key);
     pk.seg[0].out_f16 = 1;
-    RUN(RWKV7_K_CMIX_KEY, "cmix_key", proj(false, pk, d.F, w, st));
+    RUN(RWKV7_K_CMIX_KEY, "cmix_key", proj(false, pk, d.F, w, st, m->opt_plan[3]));
 
     ProjArgs pv;
     memset(&pv, 0, sizeof pv);
     pv.W = q.w_val_km; pv.K = d.F; pv.M = T; pv.nseg = 1;
     pv.seg[0] = mkseg(0, C, EPI_RESID, w.pre, d.F, w.x, C);
-    RUN(RWKV7_K_CMIX_VALUE, "cmix_value", proj(false, pv, C, w, st));
+    RUN(RWKV7_K_CMIX_VALUE, "cmix_value", proj(false, pv, C, w, st, m->opt_plan[4]));
   }
   return RWKV7_OK;
 }
@@ -1022,11 +1035,25 @@ int rwkv7_set_option(rwkv7_model* m, int32_t key, int64_t value) {
       m->opt_chunk = value; break;
     case RWKV7_OPT_FUSE_LN: m->opt_fuse_ln = value ? 1 : 0; break;
     case RWKV7_OPT_FUSE_VALUE: m->opt_fuse_value = value ? 1 : 0; break;
+    case RWKV7_OPT_GEMM_PLAN_PROJ_IN:
+    case RWKV7_OPT_GEMM_PLAN_ADAPTERS:
+    case RWKV7_OPT_GEMM_PLAN_PROJ_OUT:
+    case RWKV7_OPT_GEMM_PLAN_CMIX_KEY:
+    case RWKV7_OPT_GEMM_PLAN_CMIX_VALUE:
+    case RWKV7_OPT_GEMM_PLAN_HEAD: {
+      if (value != 0) {
+        const PlanCode c = decode_plan(value);
+        if (value < 0 || value >= 10000000 || !gemm_cfg_ok(c.tm, c.tn, c.ks, c.pipe))
+          return fail(RWKV7_EINVAL, "GEMM plan %lld is not a supported tile configuration", (long long)value);
+      }
+      m->opt_plan[key - RWKV7_OPT_GEMM_PLAN_PROJ_IN] = value;
+      break;
+    }
     default: return fail(RWKV7_EINVAL, "unknown option %d", key);
   }
   // cached graphs bake in the kernel path: drop them when it may change
   if (key == RWKV7_OPT_GEMV_MAX_B || key == RWKV7_OPT_SPARSE_MAX_B || key == RWKV7_OPT_FUSE_LN ||
-      key == RWKV7_OPT_FUSE_VALUE)
+      key == RWKV7_OPT_FUSE_VALUE || (key >= RWKV7_OPT_GEMM_PLAN_PROJ_IN && key <= RWKV7_OPT_GEMM_PLAN_HEAD))
     drop_graphs(m);
   return RWKV7_OK;
 }
@@ -1041,6 +1068,12 @@ int rwkv7_get_option(const rwkv7_model* m, int32_t key, int64_t* value) {
     case RWKV7_OPT_PREFILL_CHUNK: *value = m->opt_chunk; break;
     case RWKV7_OPT_FUSE_LN: *value = m->opt_fuse_ln; break;
     case RWKV7_OPT_FUSE_VALUE: *value = m->opt_fuse_value; break;
+    case RWKV7_OPT_GEMM_PLAN_PROJ_IN:
+    case RWKV7_OPT_GEMM_PLAN_ADAPTERS:
+    case RWKV7_OPT_GEMM_PLAN_PROJ_OUT:
+    case RWKV7_OPT_GEMM_PLAN_CMIX_KEY:
+    case RWKV7_OPT_GEMM_PLAN_CMIX_VALUE:
+    case RWKV7_OPT_GEMM_PLAN_HEAD: *value = m->opt_plan[key - RWKV7_OPT_GEMM_PLAN_PROJ_IN]; break;
     default: return fail(RWKV7_EINVAL, "unknown option %d", key);
   }
   return RWKV7_OK;

@@ -34,6 +34,7 @@ constexpr int MM_PAD = 16;
 // PIPE = 1 runs the K loop as a three-deep software pipeline (LDS fragment
 // reads of the next stage overlap the current stage's MFMAs); it costs
 // 2 (TM + TN) KS / 32 fragment registers and pays off on some shapes only.
+// PIPE = 2 keeps two stages of global loads in flight (see below).
 template <int TM, int TN, int KS, int PIPE>
 __global__ __launch_bounds__(256) void k_mm(ProjArgs a) {
   constexpr int MT = 32 * TM, NT = 32 * TN;
@@ -120,7 +121,96 @@ __global__ __launch_bounds__(256) void k_mm(ProjArgs a) {
     }
   };
 
-  if constexpr (!PIPE) {
+  if constexpr (PIPE == 2) {
+  // Two stages in flight in registers.  The loads read clamped (always
+  // valid) addresses and are issued unconditionally in the steady-state
+  // loop, so the waitcnt before each LDS write waits for its own stage
+  // only; k beyond K is zeroed when written to LDS.  The scheduling
+  // barriers keep the loads at the top of each stage (left alone, the
+  // scheduler sinks them below the MFMAs and the latency is exposed).
+  const int mlast = a.M - 1, nlast = sg.row1 - 1, klast = K - 8;
+  u32x4 qa[2][ACH], qb[2][BCH];
+  auto load2 = [&](int stg, u32x4* pa, u32x4* pb) {
+    const int k0 = stg * KS;
+#pragma unroll
+    for (int p = 0; p < ACH; ++p) {
+      const int c = p * 256 + tid;
+      const int m = min(m0 + c / CPR, mlast), k = min(k0 + (c % CPR) * 8, klast);
+      pa[p] = ld16(A + (long)m * lda + k);
+    }
+#pragma unroll
+    for (int p = 0; p < BCH; ++p) {
+      const int c = p * 256 + tid;
+      const int n = min(n0 + c / CPR, nlast), k = min(k0 + (c % CPR) * 8, klast);
+      pb[p] = ld16(Wb + (long)n * K + k);
+    }
+  };
+  auto store2 = [&](int stg, int buf, const u32x4* pa, const u32x4* pb) {
+    const int k0 = stg * KS;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int p = 0; p < ACH; ++p) {
+      const int c = p * 256 + tid;
+      st16(&As[buf][c / CPR][(c % CPR) * 8], k0 + (c % CPR) * 8 < K ? pa[p] : z);
+    }
+#pragma unroll
+    for (int p = 0; p < BCH; ++p) {
+      const int c = p * 256 + tid;
+      st16(&Bs[buf][c / CPR][(c % CPR) * 8], k0 + (c % CPR) * 8 < K ? pb[p] : z);
+    }
+  };
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int kk = 0; kk < KS; kk += 32) {
+      half8 af[TM], bf[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const half8*>(&As[buf][wm0 + 16 * i + fr][kk + fk]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bf[j] = *reinterpret_cast<const half8*>(&Bs[buf][wn0 + 16 * j + fr][kk + fk]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  // ring: at stage r, qa/qb[r & 1] hold stage r (already in LDS buffer
+  // r & 1) and qa/qb[(r + 1) & 1] hold stage r + 1 (in flight)
+  const int nrel = st1 - st0;
+  if (nrel > 0) {
+    load2(st0, qa[0], qb[0]);
+    if (nrel > 1) load2(st0 + 1, qa[1], qb[1]);
+    store2(st0, 0, qa[0], qb[0]);
+    __syncthreads();
+  }
+  int r0 = 0;
+  for (; r0 + 4 <= nrel; r0 += 2) {
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const int r = r0 + d;
+      load2(st0 + r + 2, qa[d], qb[d]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(d);
+      __builtin_amdgcn_sched_barrier(0);
+      store2(st0 + r + 1, d ^ 1, qa[d ^ 1], qb[d ^ 1]);
+      __syncthreads();
+    }
+  }
+  for (; r0 < nrel; r0 += 2) {
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const int r = r0 + d;
+      if (r < nrel) {
+        if (r + 2 < nrel) load2(st0 + r + 2, qa[d], qb[d]);
+        compute(d);
+        if (r + 1 < nrel) store2(st0 + r + 1, d ^ 1, qa[d ^ 1], qb[d ^ 1]);
+        __syncthreads();
+      }
+    }
+  }
+  } else if constexpr (!PIPE) {
   if (st0 < st1) {
     load(st0);
     store(0);
@@ -318,8 +408,12 @@ static void mm_launch_p(int ks, dim3 grid, hipStream_t st, const ProjArgs& a) {
 template <int TM, int TN>
 static void mm_launch(int ks, int pipe, dim3 grid, hipStream_t st, const ProjArgs& a) {
   if constexpr (TM + TN <= 6) {
-    if (pipe) {
+    if (pipe == 1) {
       mm_launch_p<TM, TN, 1>(ks, grid, st, a);
+      return;
+    }
+    if (pipe == 2) {
+      mm_launch_p<TM, TN, 2>(ks, grid, st, a);
       return;
     }
   }
@@ -327,6 +421,7 @@ static void mm_launch(int ks, int pipe, dim3 grid, hipStream_t st, const ProjArg
 }
 
 static bool mm_cfg_ok(int tm, int tn, int ks, int pipe) {
+  if (pipe < 0 || pipe > 2) return false;
   if (pipe && (tm + tn > 6 || (ks == 128 && tm + tn > 4))) return false;
   if (!((tm == 1 || tm == 2 || tm == 4) && (tn == 2 || tn == 4))) return false;
   if (ks == 32) return tm >= 2;
@@ -334,12 +429,14 @@ static bool mm_cfg_ok(int tm, int tn, int ks, int pipe) {
   return ks == 64;
 }
 
-// Default plan by problem shape, from a sweep of (tm, tn, ks, pipe, split)
-// over the 2.9B and 7.2B projections at M = 64, 256 and 512 on MI355X with
-// the weights streamed from HBM (rotated over six copies) and random
-// operands.  "Narrow" outputs are one model width (value, output
-// projection), "head" the vocabulary, "wide" the rest (key, input
-// projection, adapters).  split 0 = automatic.
+// Default plan by problem shape, from sweeps of (tm, tn, ks, pipe, split) on
+// MI355X: the 2.9B and 7.2B projections at M = 64, 256 and 512 with the
+// weights streamed from HBM (rotated over six copies), and the 2.9B model's
+// own projections (segments, epilogues) timed in place at B = 64, 256 and a
+// 512-token prefill chunk.  "Narrow" outputs are one model width (value,
+// output projection), "head" the vocabulary, "wide" the rest (key, input
+// projection, adapters' second stage, whose K is an adapter rank).
+// split 0 = automatic.
 struct MmPlan {
   int tm, tn, ks, pipe, split;
 };
@@ -350,26 +447,36 @@ static MmPlan mm_choose(const ProjArgs& a, int total_rows) {
     if (a.seg[i].W && a.seg[i].K > K) K = a.seg[i].K;
   if (M <= 32) return {1, 2, 128, 0, 0};
   if (N <= 4096) {                                   // narrow
+    if (K >= 8192) {                                 // channel-mix value
+      if (K >= 16384) return {4, 4, 64, 0, 6};
+      if (M <= 64) return {2, 2, 64, 2, 0};
+      return M <= 256 ? MmPlan{2, 4, 64, 2, 6} : MmPlan{4, 4, 64, 0, 6};
+    }
     if (M <= 64) return {1, 2, 128, 0, 0};
-    if (K >= 8192) return {K >= 16384 ? 4 : (M <= 256 ? 2 : 4), 4, 64, 0, 6};
-    return M <= 256 ? MmPlan{1, 2, 128, 0, 0} : MmPlan{2, 2, 128, 0, 1};
+    return M <= 256 ? MmPlan{2, 2, 64, 2, 0} : MmPlan{1, 2, 64, 2, 0};
   }
-  if (N >= 32768) return {M <= 64 ? 2 : 4, 4, 64, 0, 0};   // head
-  if (M <= 64) return {2, 2, 128, 0, 0};                  // wide
+  if (N >= 32768) return M <= 64 ? MmPlan{2, 4, 64, 1, 0} : MmPlan{4, 4, 64, 0, 0};   // head
+  const bool rank_k = K < 1024;                      // adapters' second stage
+  if (M <= 64) {
+    if (rank_k) return {1, 2, 128, 0, 0};
+    return N <= 8192 ? MmPlan{1, 2, 128, 2, 0} : MmPlan{2, 2, 128, 0, 0};
+  }
   if (M <= 256) {
+    if (rank_k) return {2, 2, 64, 2, 0};
     if (K >= 4096) return N >= 16384 ? MmPlan{4, 2, 64, 1, 1} : MmPlan{4, 4, 64, 0, 2};
-    return N <= 8192 ? MmPlan{2, 2, 128, 0, 0} : MmPlan{2, 2, 64, 1, 0};
+    return N <= 8192 ? MmPlan{2, 2, 128, 2, 0} : MmPlan{2, 2, 64, 1, 0};
   }
-  return N >= 10240 ? MmPlan{2, 4, 32, 1, 1} : MmPlan{4, 2, 64, 1, 1};
+  if (rank_k) return {2, 2, 32, 2, 0};
+  return N >= 10240 ? MmPlan{2, 4, 32, 1, 1} : MmPlan{4, 2, 64, 2, 0};
 }
 
 hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int tm, int tn, int ks,
                            int split, hipStream_t st) {
-  // ks >= 1000: the software-pipelined loop with stage depth ks - 1000
+  // ks >= 1000: pipelined loop number ks / 1000 with stage depth ks % 1000
   int pipe = 0;
   if (ks >= 1000) {
-    pipe = 1;
-    ks -= 1000;
+    pipe = ks / 1000;
+    ks %= 1000;
   }
   if (tm <= 0 || tn <= 0 || ks <= 0) {
     const MmPlan p = mm_choose(a, total_rows);
@@ -409,6 +516,8 @@ hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int 
   return hipSuccess;
 }
 
+bool gemm_cfg_ok(int tm, int tn, int ks, int pipe) { return mm_cfg_ok(tm, tn, ks, pipe); }
+
 hipError_t launch_gemm(ProjArgs a, int total_rows, int64_t part_floats, hipStream_t st) {
   return launch_gemm_cfg(a, total_rows, part_floats, 0, 0, 0, 0, st);
 }
@@ -422,7 +531,7 @@ const char* gemm_kernel_name(int M, int N, int K) {
   a.K = K;
   const MmPlan p = mm_choose(a, N);
   const int tm = p.tm, tn = p.tn, ks = p.ks, pipe = p.pipe;
-  static char names[4][2][3][2][28];
+  static char names[4][2][3][3][28];
   char* s = names[tm == 1 ? 0 : tm == 2 ? 1 : tm == 4 ? 2 : 3][tn == 2 ? 0 : 1][ks == 32 ? 0 : ks == 64 ? 1 : 2]
                  [pipe];
   if (!s[0]) snprintf(s, sizeof(names[0][0][0][0]), "k_mm<%d, %d, %d, %d>", tm, tn, ks, pipe);

@@ -157,6 +157,69 @@ def test_batched_step_paths(model, W, R, B, gemv, sparse, fuse, fval):
         model.set_option(R.OPT_FUSE_VALUE, 1)
 
 
+GEMM_PLAN_KEYS = (8, 9, 10, 11, 12, 13)   # OPT_GEMM_PLAN_PROJ_IN .. _HEAD
+
+
+@pytest.mark.parametrize("tm,tn,ks,pipe,split", [
+    (1, 2, 128, 0, 0), (2, 2, 32, 1, 0), (2, 4, 64, 1, 1), (4, 4, 64, 0, 3),
+    (2, 2, 64, 2, 0), (2, 2, 128, 2, 0), (1, 2, 64, 2, 0), (2, 4, 32, 2, 2),
+    (4, 2, 64, 2, 1), (1, 4, 64, 2, 3)])
+def test_gemm_plans_match_oracle(model, W, R, tm, tn, ks, pipe, split):
+    """Every MFMA projection (prefill and an 8-row step) forced onto one tile
+    plan: tile shapes, stage depths, the three K loops and K splits, with K
+    from 32 (adapter ranks) to 1024 (channel-mix value) and ragged row
+    counts, against the oracle and against the built-in plans."""
+    code = R.gemm_plan_code(tm, tn, ks, pipe, split)
+    B = 8
+    slots = [(3 * i + 1) % NSLOT for i in range(B)]
+    toks = [[int(t) for t in prompt(400 + step, B)] for step in range(2)]
+
+    def run():
+        fresh(model, slots)
+        for i, s in enumerate(slots):
+            model.prefill(s, dev(prompt(300 + i, 5 + 3 * i)))
+        out = []
+        logits = torch.empty(B, S.vocab, device="cuda")
+        for t in toks:
+            model.decode_step(dev(slots), dev(t), logits)
+            out.append(logits.cpu().numpy().copy())
+        return out, [gstate(model, s) for s in slots]
+
+    base, base_states = run()
+    for k in GEMM_PLAN_KEYS:
+        model.set_option(k, code)
+    try:
+        got, got_states = run()
+    finally:
+        for k in GEMM_PLAN_KEYS:
+            model.set_option(k, 0)
+    states = []
+    for i in range(B):
+        st = O.State(S)
+        O.seq(W, st, prompt(300 + i, 5 + 3 * i), want_logits=False)
+        states.append(st)
+    # Plans differ in fp32 summation order; the fp16 activations written
+    # between projections can then round one ulp (2^-11 relative) apart, so
+    # the plans agree to about 1e-3, not bitwise.  A wrong tile is O(1) off.
+    for step, t in enumerate(toks):
+        ref = O.step(W, states, t)
+        for b in range(B):
+            assert rel(got[step][b], ref[b]) <= TOL, (step, b)
+            assert rel(got[step][b], base[step][b]) <= 2e-3, (step, b)
+    for b in range(B):
+        assert rel(got_states[b], states[b].flat()) <= TOL
+        assert rel(got_states[b], base_states[b]) <= 2e-3
+    assert model.poll_error() == 0
+
+
+def test_gemm_plan_option_validation(model, R):
+    for bad in (R.gemm_plan_code(3, 2, 64), R.gemm_plan_code(2, 2, 48), R.gemm_plan_code(4, 4, 64, 2),
+                R.gemm_plan_code(4, 4, 128), R.gemm_plan_code(2, 2, 64, 3), -5, 10 ** 8):
+        with pytest.raises(R.RWKV7Error):
+            model.set_option(8, bad)
+    model.set_option(8, 0)
+
+
 def test_prefill_equals_steps_on_gpu(model, R):
     toks = prompt(7, 37)
     fresh(model, [2, 3, 4])
