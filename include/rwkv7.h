@@ -118,7 +118,8 @@ int rwkv7_state_bytes(const rwkv7_config* cfg, int64_t n_slots, uint64_t* bytes,
 
 /* Bytes of the workspace for decode steps of up to max_B rows and prefill
  * calls (any T; processed in chunks of up to max_T tokens; max_T >= 1).
- * The workspace begins with the 4-byte sticky device error word. */
+ * The workspace begins with the 4-byte sticky device error word; the caller
+ * zero-fills the workspace once before its first use. */
 int rwkv7_workspace_bytes(const rwkv7_config* cfg, int32_t max_B, int32_t max_T,
                           uint64_t* bytes);
 
@@ -205,10 +206,13 @@ const char* rwkv7_last_error(void);
                                       into per-workgroup partial sums, folded in a fixed order */
 /* Tile plan of one MFMA projection (B > GEMV_MAX_B and prefill); 0 (default) = the built-in
    plan for the shape.  Otherwise the decimal digits "T N KKK P S" of the value give the
-   workgroup tile (32 T rows x 32 N columns, T in {1, 2, 4}, N in {2, 4}), the K stage depth
+   workgroup tile (32 T rows x 32 N columns, T in {1, 2, 4}, N in {2, 4}; also T = 2, N = 5
+   with loop 3 and 64-deep stages), the K stage depth
    KKK (32, 64 or 128), the K loop P (0 plain, 1 pipelined LDS reads, 2 two stages of global
-   loads in flight) and the K split S (0 automatic); e.g. 2206420 = 64 x 64 tiles, 64-deep
-   stages, loop 2, automatic split.  Unsupported combinations fail with EINVAL. */
+   loads in flight, 3 stages loaded straight into a three-deep LDS ring; 3 falls back to 2
+   (0 for 4 x 4 tiles) where K is not a multiple of KKK) and the K split S (0 automatic); e.g. 2206430 = 64 x 64
+   tiles, 64-deep stages, loop 3, automatic split.  Unsupported combinations fail with
+   EINVAL. */
 #define RWKV7_OPT_GEMM_PLAN_PROJ_IN 8     /* r, k, v and the adapters' first stage */
 #define RWKV7_OPT_GEMM_PLAN_ADAPTERS 9    /* the adapters' second stage (decay, alpha, gates) */
 #define RWKV7_OPT_GEMM_PLAN_PROJ_OUT 10   /* W_o + residual */

@@ -31,10 +31,43 @@
 // (measured with SQ_LDS_BANK_CONFLICT); + 16 removes them.
 constexpr int MM_PAD = 16;
 
+// Epilogue of a workgroup's tile (acc in the MFMA D layout: lane l holds
+// rows 4 (l / 16) + e, column l % 16 of each 16 x 16 block).  With one K
+// range the segment's epilogue runs here; with several, each range stores
+// its fp32 partial sums and k_mm_reduce adds them in range order.  (Adding
+// them in the last range to finish needs device-scope release / acquire
+// fences, which on gfx950 write back and invalidate the whole L2 of the
+// XCD under the running GEMM: measured 2.5 - 5x slower than the extra
+// launch.)
+template <int TM, int TN>
+__device__ __forceinline__ void mm_epilogue(const ProjArgs& a, const Seg& sg, const floatx4 (&acc)[TM][TN],
+                                            int ks_id, int n0, int m0, int wm0, int wn0, int lane) {
+  const int fr = lane & 15;
+  const int er = (lane >> 4) * 4;
+  float* P = a.part + (long)ks_id * a.M * a.total_rows;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + wn0 + 16 * j + fr;
+      if (n >= sg.row1) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + wm0 + 16 * i + er + e;
+        if (m >= a.M) continue;
+        if (a.split > 1)
+          P[(long)m * a.total_rows + n] = acc[i][j][e];
+        else
+          epi_store(sg, n - sg.row0, m, acc[i][j][e]);
+      }
+    }
+}
+
 // PIPE = 1 runs the K loop as a three-deep software pipeline (LDS fragment
 // reads of the next stage overlap the current stage's MFMAs); it costs
 // 2 (TM + TN) KS / 32 fragment registers and pays off on some shapes only.
-// PIPE = 2 keeps two stages of global loads in flight (see below).
+// PIPE = 2 keeps two stages of global loads in flight (see below); the
+// LDS-DMA variant k_mm_dma (K loop 3) is further down.
 template <int TM, int TN, int KS, int PIPE>
 __global__ __launch_bounds__(256) void k_mm(ProjArgs a) {
   constexpr int MT = 32 * TM, NT = 32 * TN;
@@ -291,36 +324,162 @@ __global__ __launch_bounds__(256) void k_mm(ProjArgs a) {
   }
   }
 
-  // D layout: lane l holds rows 4 (l / 16) + e, column l % 16 of each 16 x 16 block
-  const int er = (lane >> 4) * 4;
-  if (a.split > 1) {
-    float* P = a.part + (long)ks_id * a.M * a.total_rows;
+  mm_epilogue<TM, TN>(a, sg, acc, ks_id, n0, m0, wm0, wn0, lane);
+}
+
+// ------------------------------------------------------- LDS-DMA variant
+// The same tile and epilogue, with each stage going from global memory
+// straight into LDS (global_load_lds_dwordx4 writes each lane's 16 bytes at
+// M0 + 16 * lane): no staging registers and no LDS write instructions, three
+// stages in an LDS ring, one of them in flight while another is multiplied.
+// The loads are issued from inline assembly and their waits placed by hand:
+// for the compiler's own form of the load, the waitcnt pass drains every
+// pending LDS DMA before any LDS read, which would leave nothing in flight.
+// The main loop issues no other vector-memory instruction, so the counts
+// below are exact.  Requires K to be a multiple of KS.
+//
+// LDS layout per stage: the A rows, then the W rows, KS halves each with no
+// padding (a DMA instruction fills 1 KB contiguously).  Fragment reads take
+// 16 rows at one k chunk; rows 16 apart would share banks, so chunk c of
+// row r is stored at position c ^ swz(r), which spreads those 16 reads over
+// all 64 banks.
+__device__ inline void dma16(const half_t* g, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
+}
+template <int N>
+__device__ inline void wait_vm() {   // vmcnt <= N; lgkmcnt and expcnt unconstrained
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+template <int CPR>
+__device__ inline int swz(int r) {
+  return CPR == 4 ? ((r >> 2) & 3) : CPR == 8 ? ((r >> 1) & 7) : (r & 15);
+}
+template <int TM, int TN, int KS>
+__global__ __launch_bounds__(256) void k_mm_dma(ProjArgs a) {
+  constexpr int MT = 32 * TM, NT = 32 * TN, CPR = KS / 8, KH = KS / 32;
+  constexpr int SLOTS = (MT + NT) * CPR;   // 16-byte slots per stage
+  constexpr int NIW = SLOTS / 256;         // DMA instructions per wave and stage
+  constexpr int ASL = MT * CPR;            // slots of the A rows
+  static_assert(SLOTS % 256 == 0, "whole DMA instructions per wave");
+  __shared__ __attribute__((aligned(1024))) half_t L[3][SLOTS * 8];
+
+  const int n_tiles = a.tile0[a.nseg];
+  const int total = n_tiles * a.m_tiles * a.split;
+  const int per_xcd = (total + 7) / 8;
+  const int lin = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (lin >= total) return;
+  const int ks_id = lin % a.split;
+  const int m_tile = (lin / a.split) % a.m_tiles;
+  const int n_tile = lin / (a.split * a.m_tiles);
+  Seg sg = a.seg[0];
+  int t0 = 0;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+  for (int i = 1; i < MAX_SEGS; ++i)
+    if (i < a.nseg && n_tile >= a.tile0[i]) {
+      sg = a.seg[i];
+      t0 = a.tile0[i];
+    }
+  const int n0 = sg.row0 + (n_tile - t0) * NT;
+  const int m0 = m_tile * MT;
+  const bool own = sg.W != nullptr;
+  const int K = own ? sg.K : a.K;
+  const half_t* Wb = own ? sg.W - (long)sg.row0 * K : a.W;
+  const half_t* A = reinterpret_cast<const half_t*>(sg.act) + sg.act_off;
+  const int lda = sg.ld_act;
+  const int nst = K / KS;
+  const int st0 = (int)((long)nst * ks_id / a.split);
+  const int st1 = (int)((long)nst * (ks_id + 1) / a.split);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm0 = (wave >> 1) * 16 * TM, wn0 = (wave & 1) * 16 * TN;
+
+  // source of each lane in this wave's DMA instructions, at stage 0; rows
+  // past the end read the last row (their outputs are not stored)
+  const half_t* src[NIW];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn0 + 16 * j + fr;
-        if (n >= sg.row1) continue;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int m = m0 + wm0 + 16 * i + er + e;
-          if (m < a.M) P[(long)m * a.total_rows + n] = acc[i][j][e];
-        }
-      }
-    return;
+  for (int q = 0; q < NIW; ++q) {
+    const int S = (q * 4 + wave) * 64 + lane;
+    if (S < ASL) {
+      const int r = S / CPR, c = (S % CPR) ^ swz<CPR>(r);
+      src[q] = A + (long)min(m0 + r, a.M - 1) * lda + c * 8;
+    } else {
+      const int r = (S - ASL) / CPR, c = ((S - ASL) % CPR) ^ swz<CPR>(r);
+      src[q] = Wb + (long)min(n0 + r, sg.row1 - 1) * K + c * 8;
+    }
   }
+  const unsigned lds0 = (unsigned)(uintptr_t)&L[0][0];
+  auto issue = [&](int stg, int slot) {
+#pragma unroll
+    for (int q = 0; q < NIW; ++q)
+      dma16(src[q] + (long)stg * KS,
+            __builtin_amdgcn_readfirstlane(lds0 + slot * SLOTS * 16 + (q * 4 + wave) * 1024));
+  };
+  int aoff[KH][TM], boff[KH][TN];   // byte offsets of this lane's fragments in a stage
+#pragma unroll
+  for (int h = 0; h < KH; ++h) {
+    const int c = 4 * h + (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = wm0 + 16 * i + (lane & 15);
+      aoff[h][i] = (r * CPR + (c ^ swz<CPR>(r))) * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int r = wn0 + 16 * j + (lane & 15);
+      boff[h][j] = (ASL + r * CPR + (c ^ swz<CPR>(r))) * 16;
+    }
+  }
+  floatx4 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = n0 + wn0 + 16 * j + fr;
-      if (n >= sg.row1) continue;
+    for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int slot) {
+    const char* Lb = reinterpret_cast<const char*>(&L[slot][0]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = m0 + wm0 + 16 * i + er + e;
-        if (m < a.M) epi_store(sg, n - sg.row0, m, acc[i][j][e]);
+    for (int h = 0; h < KH; ++h) {
+      half8 af[TM], bf[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const half8*>(Lb + aoff[h][i]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bf[j] = *reinterpret_cast<const half8*>(Lb + boff[h][j]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  // stage r lives in slot r % 3; at the top of stage r, stages r and r + 1
+  // are in flight (NIW instructions each per wave)
+  const int nrel = st1 - st0;
+  if (nrel > 0) issue(st0, 0);
+  if (nrel > 1) issue(st0 + 1, 1);
+  int r0 = 0;
+  for (; r0 + 5 <= nrel; r0 += 3) {
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+      wait_vm<NIW>();     // this wave's part of stage r0 + d has landed
+      __syncthreads();    // ... every wave's; and every wave is done with slot (d + 2) % 3
+      issue(st0 + r0 + d + 2, (d + 2) % 3);
+      compute(d);
+    }
+  }
+  for (; r0 < nrel; r0 += 3) {
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+      const int r = r0 + d;
+      if (r < nrel) {
+        if (r + 1 < nrel) wait_vm<NIW>();
+        else wait_vm<0>();
+        __syncthreads();
+        if (r + 2 < nrel) issue(st0 + r + 2, (d + 2) % 3);
+        compute(d);
       }
     }
+  }
+  wait_vm<0>();
+  mm_epilogue<TM, TN>(a, sg, acc, ks_id, n0, m0, wm0, wn0, lane);
 }
 
 // Fixed-order sum of the split-K partials, then the segment's epilogue.
@@ -405,8 +564,32 @@ static void mm_launch_p(int ks, dim3 grid, hipStream_t st, const ProjArgs& a) {
   hipLaunchKernelGGL((k_mm<TM, TN, 64, PIPE>), grid, dim3(256), 0, st, a);
 }
 
+// LDS bytes of a k_mm_dma instantiation (three unpadded stages)
+static constexpr int mm_dma_lds_bytes(int tm, int tn, int ks) { return 3 * 32 * (tm + tn) * ks * 2; }
+
+template <int TM, int TN>
+static void mm_launch_dma(int ks, dim3 grid, hipStream_t st, const ProjArgs& a) {
+  if constexpr (TM >= 2 && (TM + TN) % 2 == 0) {
+    if (ks == 32) {
+      hipLaunchKernelGGL((k_mm_dma<TM, TN, 32>), grid, dim3(256), 0, st, a);
+      return;
+    }
+  }
+  if constexpr (mm_dma_lds_bytes(TM, TN, 128) <= 98304) {
+    if (ks == 128) {
+      hipLaunchKernelGGL((k_mm_dma<TM, TN, 128>), grid, dim3(256), 0, st, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((k_mm_dma<TM, TN, 64>), grid, dim3(256), 0, st, a);
+}
+
 template <int TM, int TN>
 static void mm_launch(int ks, int pipe, dim3 grid, hipStream_t st, const ProjArgs& a) {
+  if (pipe == 3) {
+    mm_launch_dma<TM, TN>(ks, grid, st, a);
+    return;
+  }
   if constexpr (TM + TN <= 6) {
     if (pipe == 1) {
       mm_launch_p<TM, TN, 1>(ks, grid, st, a);
@@ -421,7 +604,13 @@ static void mm_launch(int ks, int pipe, dim3 grid, hipStream_t st, const ProjArg
 }
 
 static bool mm_cfg_ok(int tm, int tn, int ks, int pipe) {
-  if (pipe < 0 || pipe > 2) return false;
+  if (pipe < 0 || pipe > 3) return false;
+  if (pipe == 3) {
+    if (tm == 2 && tn == 5) return ks == 64;   // 64 x 160 tiles (see mm_choose)
+    if (!((tm == 1 || tm == 2 || tm == 4) && (tn == 2 || tn == 4))) return false;
+    if (ks == 32) return tm >= 2;
+    return (ks == 64 || ks == 128) && mm_dma_lds_bytes(tm, tn, ks) <= 98304;
+  }
   if (pipe && (tm + tn > 6 || (ks == 128 && tm + tn > 4))) return false;
   if (!((tm == 1 || tm == 2 || tm == 4) && (tn == 2 || tn == 4))) return false;
   if (ks == 32) return tm >= 2;
@@ -431,9 +620,11 @@ static bool mm_cfg_ok(int tm, int tn, int ks, int pipe) {
 
 // Default plan by problem shape, from sweeps of (tm, tn, ks, pipe, split) on
 // MI355X: the 2.9B and 7.2B projections at M = 64, 256 and 512 with the
-// weights streamed from HBM (rotated over six copies), and the 2.9B model's
-// own projections (segments, epilogues) timed in place at B = 64, 256 and a
-// 512-token prefill chunk.  "Narrow" outputs are one model width (value,
+// weights streamed from HBM (rotated over six copies), then the 2.9B model's
+// own projections chosen one at a time on whole graph-replayed decode steps
+// (B = 64, 256) and 512-token prefill chunks.  A kernel timed alone can
+// rank plans differently from the step it runs in (the 64 x 160 key tiles
+// are 12 % faster alone and only even in the step), so the step decides.  "Narrow" outputs are one model width (value,
 // output projection), "head" the vocabulary, "wide" the rest (key, input
 // projection, adapters' second stage, whose K is an adapter rank).
 // split 0 = automatic.
@@ -450,24 +641,33 @@ static MmPlan mm_choose(const ProjArgs& a, int total_rows) {
     if (K >= 8192) {                                 // channel-mix value
       if (K >= 16384) return {4, 4, 64, 0, 6};
       if (M <= 64) return {2, 2, 64, 2, 0};
-      return M <= 256 ? MmPlan{2, 4, 64, 2, 6} : MmPlan{4, 4, 64, 0, 6};
+      return M <= 256 ? MmPlan{2, 4, 64, 2, 6} : MmPlan{2, 4, 64, 3, 3};
     }
     if (M <= 64) return {1, 2, 128, 0, 0};
-    return M <= 256 ? MmPlan{2, 2, 64, 2, 0} : MmPlan{1, 2, 64, 2, 0};
+    return M <= 256 ? MmPlan{2, 2, 64, 3, 0} : MmPlan{4, 2, 64, 3, 0};
   }
-  if (N >= 32768) return M <= 64 ? MmPlan{2, 4, 64, 1, 0} : MmPlan{4, 4, 64, 0, 0};   // head
+  if (N >= 32768) return M <= 64 ? MmPlan{2, 4, 64, 3, 0} : MmPlan{4, 4, 64, 0, 0};   // head
   const bool rank_k = K < 1024;                      // adapters' second stage
   if (M <= 64) {
     if (rank_k) return {1, 2, 128, 0, 0};
-    return N <= 8192 ? MmPlan{1, 2, 128, 2, 0} : MmPlan{2, 2, 128, 0, 0};
+    return N <= 8192 ? MmPlan{1, 2, 128, 3, 0} : MmPlan{2, 2, 64, 2, 0};
   }
   if (M <= 256) {
     if (rank_k) return {2, 2, 64, 2, 0};
     if (K >= 4096) return N >= 16384 ? MmPlan{4, 2, 64, 1, 1} : MmPlan{4, 4, 64, 0, 2};
-    return N <= 8192 ? MmPlan{2, 2, 128, 2, 0} : MmPlan{2, 2, 64, 1, 0};
+    // one segment: 64 x 160 tiles when they fill the CUs in fewer column-widths
+    // of rounds than 64 x 64 tiles (2.9B key at M = 256: 256 tiles, one per CU,
+    // instead of 640, which leave half the CUs a third round)
+    if (a.nseg == 1 && K % 64 == 0) {
+      const long mt = (M + 63) / 64;
+      const long r2 = ((N + 63) / 64 * mt + 255) / 256, r5 = ((N + 159) / 160 * mt + 255) / 256;
+      if (r5 * 160 < r2 * 64) return {2, 5, 64, 3, 0};
+    }
+    return N <= 8192 ? MmPlan{2, 2, 64, 2, 0} : MmPlan{2, 2, 64, 1, 0};
   }
   if (rank_k) return {2, 2, 32, 2, 0};
-  return N >= 10240 ? MmPlan{2, 4, 32, 1, 1} : MmPlan{4, 2, 64, 2, 0};
+  if (K >= 4096) return N >= 10240 ? MmPlan{2, 4, 32, 1, 1} : MmPlan{4, 2, 64, 2, 0};
+  return N >= 10240 ? MmPlan{2, 2, 64, 3, 0} : MmPlan{4, 2, 64, 3, 0};
 }
 
 hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int tm, int tn, int ks,
@@ -484,6 +684,13 @@ hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int 
     if (split <= 0) split = p.split;
   }
   if (!mm_cfg_ok(tm, tn, ks, pipe)) return hipErrorInvalidValue;
+  if (pipe == 3)   // the DMA loop needs whole stages: otherwise a register-staged loop
+    for (int i = 0; i < a.nseg; ++i)
+      if ((a.seg[i].W ? a.seg[i].K : a.K) % ks != 0) {
+        if (tn == 5) tn = 4;   // 160-wide tiles exist for the DMA loop only
+        pipe = mm_cfg_ok(tm, tn, ks, 2) ? 2 : 0;
+      }
+  if (!mm_cfg_ok(tm, tn, ks, pipe)) return hipErrorInvalidValue;
   const int items = mm_plan(a, total_rows, tm, tn, ks, split, part_floats);
   if (items < 0) return hipErrorInvalidValue;
   const dim3 grid(((items + 7) / 8) * 8);
@@ -493,6 +700,7 @@ hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int 
     case 22: mm_launch<2, 2>(ks, pipe, grid, st, a); break;
     case 24: mm_launch<2, 4>(ks, pipe, grid, st, a); break;
     case 42: mm_launch<4, 2>(ks, pipe, grid, st, a); break;
+    case 25: mm_launch_dma<2, 5>(ks, grid, st, a); break;   // loop 3, ks 64 only
     default: mm_launch<4, 4>(ks, pipe, grid, st, a); break;
   }
   hipError_t e = hipGetLastError();
@@ -529,11 +737,25 @@ const char* gemm_kernel_name(int M, int N, int K) {
   memset(&a, 0, sizeof a);
   a.M = M;
   a.K = K;
+  a.nseg = 1;   // one segment of N rows
+  a.seg[0].row0 = 0;
+  a.seg[0].row1 = N;
   const MmPlan p = mm_choose(a, N);
-  const int tm = p.tm, tn = p.tn, ks = p.ks, pipe = p.pipe;
-  static char names[4][2][3][3][28];
-  char* s = names[tm == 1 ? 0 : tm == 2 ? 1 : tm == 4 ? 2 : 3][tn == 2 ? 0 : 1][ks == 32 ? 0 : ks == 64 ? 1 : 2]
-                 [pipe];
-  if (!s[0]) snprintf(s, sizeof(names[0][0][0][0]), "k_mm<%d, %d, %d, %d>", tm, tn, ks, pipe);
+  const int tm = p.tm, ks = p.ks, pipe = p.pipe;
+  int tn = p.tn;
+  int ep = pipe;   // as launch_gemm_cfg falls back
+  if (pipe == 3 && K % ks != 0) {
+    if (tn == 5) tn = 4;
+    ep = mm_cfg_ok(tm, tn, ks, 2) ? 2 : 0;
+  }
+  static char names[4][3][3][4][28];
+  char* s = names[tm == 1 ? 0 : tm == 2 ? 1 : tm == 4 ? 2 : 3][tn == 2 ? 0 : tn == 4 ? 1 : 2]
+                 [ks == 32 ? 0 : ks == 64 ? 1 : 2][ep];
+  if (!s[0]) {
+    if (ep == 3)
+      snprintf(s, sizeof(names[0][0][0][0]), "k_mm_dma<%d, %d, %d>", tm, tn, ks);
+    else
+      snprintf(s, sizeof(names[0][0][0][0]), "k_mm<%d, %d, %d, %d>", tm, tn, ks, ep);
+  }
   return s;
 }
