@@ -311,12 +311,16 @@ static PlanCode decode_plan(int64_t v) {
           (int)(v % 10)};
 }
 
-hipError_t proj(bool gemv, ProjArgs& a, int total_rows, const Ws& w, hipStream_t st, int64_t plan = 0) {
+// `deferred` (MFMA path): see launch_gemm; the GEMV path never defers.
+hipError_t proj(bool gemv, ProjArgs& a, int total_rows, const Ws& w, hipStream_t st, int64_t plan = 0,
+                int* deferred = nullptr) {
+  if (deferred) *deferred = 0;
   if (gemv) return launch_gemv(a, total_rows, st);
   a.part = w.part;
-  if (plan == 0) return launch_gemm(a, total_rows, w.part_floats, st);
+  if (plan == 0) return launch_gemm(a, total_rows, w.part_floats, st, deferred);
   const PlanCode c = decode_plan(plan);
-  return launch_gemm_cfg(a, total_rows, w.part_floats, c.tm, c.tn, c.ks + 1000 * c.pipe, c.split, st);
+  return launch_gemm_cfg(a, total_rows, w.part_floats, c.tm, c.tn, c.ks + 1000 * c.pipe, c.split, st,
+                         deferred);
 }
 
 // Input-projection segments: r | k | v | w1 | a1 | v1 | g1 of the fused matrix.
@@ -437,6 +441,10 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
   // prologues; the new shifts are committed by the following kernel (WKV
   // for the time mix, the channel-mix value for the channel mix).
   // Otherwise a LayerNorm kernel writes the mixed rows and the shift.
+  // MFMA path: a residual projection split over K leaves its partial sums
+  // for the LayerNorm that follows it to add into x (no reduction launch)
+  int pending = 0;
+  int* const defer = path.fused ? nullptr : &pending;
   for (int l = 0; l < d.L; ++l) {
     L.layer = l;
     const LayerPtrs& q = m->pk.layers[l];
@@ -444,6 +452,8 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
     LnMixArgs la;
     memset(&la, 0, sizeof la);
     la.x = w.x; la.C = C; la.R = B; la.mode = LNMIX_DECODE;
+    la.parts = pending ? w.part : nullptr; la.nparts = pending;
+    pending = 0;
     la.g = q.ln1_w; la.b = q.ln1_b;
     la.pool = pool; la.slot_stride = d.slot_floats; la.n_slots = n_slots; la.shift_off = lo;
     la.slots = w.slots; la.seq_slot = -1;
@@ -475,7 +485,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
     memset(&po, 0, sizeof po);
     po.W = q.w_o; po.K = C; po.M = B; po.nseg = 1;
     po.seg[0] = mkseg(0, C, EPI_RESID, w.yg, C, w.x, C);
-    RUN(RWKV7_K_PROJ_OUT, "proj_out", proj(path.gemv, po, C, w, st, m->opt_plan[2]));
+    RUN(RWKV7_K_PROJ_OUT, "proj_out", proj(path.gemv, po, C, w, st, m->opt_plan[2], defer));
 
     ProjArgs pk;
     memset(&pk, 0, sizeof pk);
@@ -499,8 +509,10 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
       lc.shift_off = lo + C;
       lc.mu = q.mu_k; lc.nq = 1;
       lc.out = w.xk; lc.out_q_stride = 0;
+      lc.parts = pending ? w.part : nullptr; lc.nparts = pending;
       RUN(RWKV7_K_LN_MIX, "ln_mix(cmix)", launch_ln_mix(lc, st));
     }
+    pending = 0;
     RUN(RWKV7_K_CMIX_KEY, "cmix_key", proj(path.gemv, pk, d.F, w, st, m->opt_plan[3]));
 
     if (path.fuse_value) {
@@ -526,7 +538,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
       memset(&pv, 0, sizeof pv);
       pv.W = q.w_val_km; pv.K = d.F; pv.M = B; pv.nseg = 1;
       pv.seg[0] = mkseg(0, C, EPI_RESID, w.pre, d.F, w.x, C);
-      RUN(RWKV7_K_CMIX_VALUE, "cmix_value", proj(false, pv, C, w, st, m->opt_plan[4]));
+      RUN(RWKV7_K_CMIX_VALUE, "cmix_value", proj(false, pv, C, w, st, m->opt_plan[4], defer));
       if (path.fused) {
         CommitArgs ca{w.u_ffn, pool, d.slot_floats, n_slots, lo + C, w.slots, B, C};
         RUN(RWKV7_K_OTHER, "commit shift", launch_commit_shift(ca, st));
@@ -548,6 +560,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
     lo.g = m->pk.lnout_w; lo.b = m->pk.lnout_b;
     lo.nq = 1; lo.mu = nullptr;
     lo.out = w.xo; lo.out_f16 = f16; lo.out_q_stride = 0;
+    lo.parts = pending ? w.part : nullptr; lo.nparts = pending;
     RUN(RWKV7_K_LN_MIX, "ln_out", launch_ln_mix(lo, st));
   }
   RUN(RWKV7_K_HEAD, "head", proj(path.gemv, ph, d.V, w, st, m->opt_plan[5]));

@@ -170,13 +170,21 @@ __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
     for (int i = 0; i < NE; ++i)
       mu[q][i] = (q < a.nq && a.mu) ? a.mu[(long)q * C + t + 256 * i] : 0.0f;
   if (a.nparts > 0) {
+    // x += (sum of the split-K partials of the residual projection, in range
+    // order): the same arithmetic as the GEMM's own reduction pass
+    float acc[NE];
+#pragma unroll
+    for (int i = 0; i < NE; ++i) acc[i] = 0.0f;
     for (int s = 0; s < a.nparts; ++s) {
       const float* p = a.parts + ((long)s * a.R + r) * C;
 #pragma unroll
-      for (int i = 0; i < NE; ++i) v[i] += p[t + 256 * i];
+      for (int i = 0; i < NE; ++i) acc[i] += p[t + 256 * i];
     }
 #pragma unroll
-    for (int i = 0; i < NE; ++i) xr[t + 256 * i] = v[i];
+    for (int i = 0; i < NE; ++i) {
+      v[i] += acc[i];
+      xr[t + 256 * i] = v[i];
+    }
   }
 
   float mean, rstd;

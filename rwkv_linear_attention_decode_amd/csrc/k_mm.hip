@@ -671,7 +671,8 @@ static MmPlan mm_choose(const ProjArgs& a, int total_rows) {
 }
 
 hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int tm, int tn, int ks,
-                           int split, hipStream_t st) {
+                           int split, hipStream_t st, int* deferred) {
+  if (deferred) *deferred = 0;
   // ks >= 1000: pipelined loop number ks / 1000 with stage depth ks % 1000
   int pipe = 0;
   if (ks >= 1000) {
@@ -705,7 +706,11 @@ hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.split > 1) {
+  const bool can_defer = a.nseg == 1 && a.seg[0].epi == EPI_RESID && !a.seg[0].out_f16 &&
+                         a.seg[0].row0 == 0 && a.seg[0].row1 == total_rows && a.seg[0].ld_out == total_rows;
+  if (a.split > 1 && deferred && can_defer) {
+    *deferred = a.split;
+  } else if (a.split > 1) {
     const long n = (long)a.M * total_rows;
     hipLaunchKernelGGL(k_mm_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
     e = hipGetLastError();
@@ -726,8 +731,8 @@ hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int 
 
 bool gemm_cfg_ok(int tm, int tn, int ks, int pipe) { return mm_cfg_ok(tm, tn, ks, pipe); }
 
-hipError_t launch_gemm(ProjArgs a, int total_rows, int64_t part_floats, hipStream_t st) {
-  return launch_gemm_cfg(a, total_rows, part_floats, 0, 0, 0, 0, st);
+hipError_t launch_gemm(ProjArgs a, int total_rows, int64_t part_floats, hipStream_t st, int* deferred) {
+  return launch_gemm_cfg(a, total_rows, part_floats, 0, 0, 0, 0, st, deferred);
 }
 
 // Template arguments as a trace prints them, e.g. "k_mm<4, 4, 64, 0>", for an

@@ -11,11 +11,16 @@ bool gemv_supported(int B, int K);
 hipError_t launch_gemv(const ProjArgs& a, int total_rows, hipStream_t st);
 // MFMA path: A (segment activations) fp16.  `part_floats` bounds the split-K
 // partial buffer a.part (nullptr: no split).
-hipError_t launch_gemm(ProjArgs a, int total_rows, int64_t part_floats, hipStream_t st);
+// With `deferred` non-null, a launch whose only segment is a residual add
+// (EPI_RESID into fp32 rows of total_rows) leaves its split-K partials in
+// a.part for the caller to add (k_ln_mix does) and sets *deferred to the
+// number of K ranges; otherwise (and when not split) it sets 0.
+hipError_t launch_gemm(ProjArgs a, int total_rows, int64_t part_floats, hipStream_t st,
+                       int* deferred = nullptr);
 // Same with an explicit tile (tm, tn: 16 x 16 blocks per wave), stage depth
 // ks (64 or 128) and K split; 0 selects the default / automatic value.
 hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int tm, int tn, int ks,
-                           int split, hipStream_t st);
+                           int split, hipStream_t st, int* deferred = nullptr);
 // `epi`: the epilogue shared by every segment of the launch, -1 when mixed,
 // -2 for the key projection with the sparse value fused into it
 const char* gemv_kernel_name(int B, int K, int epi);
@@ -67,7 +72,8 @@ hipError_t launch_embed(const EmbedArgs& a, hipStream_t st);
 enum { LNMIX_DECODE = 0, LNMIX_SEQ = 1, LNMIX_PLAIN = 2 };
 struct LnMixArgs {
   float* x;                 // [R][C] residual (updated when partials are folded in)
-  const float* parts;       // [nparts][R][C] channel-mix partial sums, or nullptr
+  const float* parts;       // [nparts][R][C] split-K partials of the residual projection that
+                            // precedes (added into x first), or nullptr; not in sequence mode
   int nparts;
   int C, R, mode;
   const float* g;
