@@ -172,13 +172,27 @@ __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
   if (a.nparts > 0) {
     // x += (sum of the split-K partials of the residual projection, in range
     // order): the same arithmetic as the GEMM's own reduction pass
+    // loads four ranges at a time (one memory round trip per four), adds in order
     float acc[NE];
 #pragma unroll
     for (int i = 0; i < NE; ++i) acc[i] = 0.0f;
-    for (int s = 0; s < a.nparts; ++s) {
-      const float* p = a.parts + ((long)s * a.R + r) * C;
+    const long rs = (long)a.R * C;   // floats between ranges
+    const float* p = a.parts + (long)r * C + t;
+    int s = 0;
+    for (; s + 4 <= a.nparts; s += 4) {
+      float q[4][NE];
 #pragma unroll
-      for (int i = 0; i < NE; ++i) acc[i] += p[t + 256 * i];
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < NE; ++i) q[j][i] = p[(s + j) * rs + 256 * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < NE; ++i) acc[i] += q[j][i];
+    }
+    for (; s < a.nparts; ++s) {
+#pragma unroll
+      for (int i = 0; i < NE; ++i) acc[i] += p[s * rs + 256 * i];
     }
 #pragma unroll
     for (int i = 0; i < NE; ++i) {
