@@ -140,7 +140,7 @@ struct Ws {
   float *x, *xq, *rkv, *lin, *lo, *vfirst, *yg, *xk, *pre, *xo, *shift_tmp, *u_att, *u_ffn;
   unsigned char* mask;
   int *dbg_idx, *dbg_cnt;
-  float *q_d, *q_a, *q_b, *q_kt, *q_v, *q_g, *q_bonus, *q_y;
+  float *q_d, *q_a, *q_b, *q_kt, *q_v, *q_g, *q_bonus, *q_brk, *q_y;
   float* part;            // split-K partial sums of the MFMA projections
   int64_t part_floats;
   float* vpart;           // value partials of the fused key projection
@@ -184,6 +184,7 @@ Ws ws_layout(const Dims& d, int R, char* base) {
   w.q_g = (float*)take(r * C * 4);
   w.q_y = (float*)take(r * C * 4);
   w.q_bonus = (float*)take(r * d.H * 4);
+  w.q_brk = (float*)take(r * d.H * 2 * 4);
   w.part_floats = (int64_t)(r * 16 * C);
   w.part = (float*)take(r * 16 * C * 4);
   // value partials of the fused key projection (B <= 2 rows, 16 key rows per workgroup)
@@ -395,7 +396,7 @@ WkvArgs wkv_args(const rwkv7_model* m, int l, float* pool, int64_t n_slots, cons
   a.yout = w.yg;
   a.yout_f16 = f16 ? 1 : 0;
   a.q_d = w.q_d; a.q_a = w.q_a; a.q_b = w.q_b; a.q_kt = w.q_kt; a.q_v = w.q_v; a.q_g = w.q_g;
-  a.q_bonus = w.q_bonus; a.q_y = w.q_y;
+  a.q_bonus = w.q_bonus; a.q_brk = w.q_brk; a.q_y = w.q_y;
   return a;
 }
 

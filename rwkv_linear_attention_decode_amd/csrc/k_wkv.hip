@@ -420,6 +420,15 @@ __global__ __launch_bounds__(256) void k_wkv_prep(WkvArgs a) {
     a.q_g[off] = hv.g[t];
   }
   if (t == 0) a.q_bonus[(long)tk * a.H + h] = hv.bonus;
+  // the scan reads y off the state before its update: y = S (d*r) + (S a)(b.r) + v (kt.r)
+  if (t < 64) {
+    const float br = wave_sum(hv.bb[t] * hv.r[t]);
+    const float kr = wave_sum(hv.kt[t] * hv.r[t]);
+    if (t == 0) {
+      a.q_brk[((long)tk * a.H + h) * 2] = br;
+      a.q_brk[((long)tk * a.H + h) * 2 + 1] = kr;
+    }
+  }
 }
 
 // Grid: H * 4 workgroups; workgroup (h, qb) owns value rows [16 qb, 16 qb + 16)
@@ -432,6 +441,7 @@ constexpr int SCAN_TB = 16;
 struct ScanBlock {
   float4 a[SCAN_TB][16], b[SCAN_TB][16], d[SCAN_TB][16], kt[SCAN_TB][16], r[SCAN_TB][16];
   float v[SCAN_TB][16];
+  float brk[SCAN_TB][2];   // b.r, kt.r
 };
 
 __global__ __launch_bounds__(256) void k_wkv_scan(WkvArgs a) {
@@ -453,7 +463,7 @@ __global__ __launch_bounds__(256) void k_wkv_scan(WkvArgs a) {
   // staging: 5 vectors x SCAN_TB tokens x 16 float4 = 1280 float4 (5 per
   // thread) plus SCAN_TB x 16 value floats (one per thread)
   float4 ra[5];
-  float rvv = 0.f;
+  float rvv = 0.f, rbk = 0.f;
   auto load = [&](int t0) {
 #pragma unroll
     for (int p = 0; p < 5; ++p) {
@@ -472,6 +482,8 @@ __global__ __launch_bounds__(256) void k_wkv_scan(WkvArgs a) {
     }
     const int tk = t0 + tid / 16;
     rvv = tk < T ? a.q_v[(long)tk * C + cj + qb * 16 + (tid & 15)] : 0.f;
+    const int tb = t0 + (tid >> 1);
+    rbk = (tid < 2 * SCAN_TB && tb < T) ? a.q_brk[((long)tb * a.H + h) * 2 + (tid & 1)] : 0.f;
   };
   auto store = [&](int buf) {
 #pragma unroll
@@ -485,6 +497,7 @@ __global__ __launch_bounds__(256) void k_wkv_scan(WkvArgs a) {
       *dst = ra[p];
     }
     sb[buf].v[tid / 16][tid & 15] = rvv;
+    if (tid < 2 * SCAN_TB) sb[buf].brk[tid >> 1][tid & 1] = rbk;
   };
 
   load(0);
@@ -496,17 +509,28 @@ __global__ __launch_bounds__(256) void k_wkv_scan(WkvArgs a) {
     if (more) load(t0 + SCAN_TB);
     const ScanBlock& B = sb[buf];
     const int n = T - t0 < SCAN_TB ? T - t0 : SCAN_TB;
-    for (int tt = 0; tt < n; ++tt) {
+    // one token: both row sums read the state before the update, so they run
+    // side by side: y = S (d*r) + (S a)(b.r) + v (kt.r), then
+    // S <- S diag(d) + (S a) b^T + v kt^T
+    auto token = [&](int tt) {
       const float4 av = B.a[tt][jq], bv = B.b[tt][jq], dv = B.d[tt][jq], kv = B.kt[tt][jq];
       const float4 rv = B.r[tt][jq];
       const float vi = B.v[tt][il];
+      const float4 dr = make_float4(dv.x * rv.x, dv.y * rv.y, dv.z * rv.z, dv.w * rv.w);
       const float sa = sum16(s.x * av.x + s.y * av.y + s.z * av.z + s.w * av.w);
+      const float sd = sum16(s.x * dr.x + s.y * dr.y + s.z * dr.z + s.w * dr.w);
+      const float y = sd + sa * B.brk[tt][0] + vi * B.brk[tt][1];
       s.x = s.x * dv.x + sa * bv.x + vi * kv.x;
       s.y = s.y * dv.y + sa * bv.y + vi * kv.y;
       s.z = s.z * dv.z + sa * bv.z + vi * kv.z;
       s.w = s.w * dv.w + sa * bv.w + vi * kv.w;
-      const float y = sum16(s.x * rv.x + s.y * rv.y + s.z * rv.z + s.w * rv.w);
       if (jq == 0) a.q_y[(long)(t0 + tt) * C + h * 64 + i] = y;
+    };
+    if (n == SCAN_TB) {   // whole block unrolled: the next token's LDS reads overlap this one
+#pragma unroll
+      for (int tt = 0; tt < SCAN_TB; ++tt) token(tt);
+    } else {
+      for (int tt = 0; tt < n; ++tt) token(tt);
     }
     if (more) store(buf ^ 1);
     __syncthreads();

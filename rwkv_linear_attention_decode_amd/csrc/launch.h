@@ -211,6 +211,7 @@ struct WkvArgs {
   float* q_v;
   float* q_g;
   float* q_bonus;          // [T][H]
+  float* q_brk;            // [T][H][2]: b.r and kt.r of each token and head (prefill scan)
   float* q_y;              // raw readout
 };
 hipError_t launch_wkv_decode(const WkvArgs& a, hipStream_t st);
