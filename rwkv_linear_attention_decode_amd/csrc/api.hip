@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <utility>
 #include <string>
 #include <tuple>
 #include <vector>
@@ -137,7 +138,7 @@ Packed pack_layout(const Dims& d, char* base) {
 struct Ws {
   uint32_t* err;
   int *slots, *tok;
-  float *x, *xq, *rkv, *lin, *lo, *vfirst, *yg, *xk, *pre, *xo, *shift_tmp, *u_att, *u_ffn;
+  float *x, *x2, *xq, *rkv, *lin, *lo, *vfirst, *yg, *xk, *pre, *xo, *shift_tmp, *u_att, *u_ffn;
   unsigned char* mask;
   int *dbg_idx, *dbg_cnt;
   float *q_d, *q_a, *q_b, *q_kt, *q_v, *q_g, *q_bonus, *q_brk, *q_y;
@@ -161,6 +162,7 @@ Ws ws_layout(const Dims& d, int R, char* base) {
   w.slots = (int*)take(r * 4);
   w.tok = (int*)take(r * 4);
   w.x = (float*)take(r * C * 4);
+  w.x2 = (float*)take(r * C * 4);   // prefill: the other residual buffer
   w.xq = (float*)take(6 * r * C * 4);
   w.rkv = (float*)take(3 * r * C * 4);
   w.lin = (float*)take(r * d.Lin * 4);
@@ -583,12 +585,23 @@ int enqueue_prefill_chunk(rwkv7_model* m, float* pool, int64_t n_slots, int slot
   EmbedArgs ea{m->pk.emb, m->pk.ln0_w, m->pk.ln0_b, w.tok, w.x, T, C};
   RUN(RWKV7_K_OTHER, "embed", launch_embed(ea, st));
 
+  // The residual projections split over K leave their partials to the next
+  // LayerNorm, which writes the folded residual to the other buffer (a row
+  // also reads the previous row's residual, so it cannot be updated in place).
+  float* xc = w.x;
+  float* xn = w.x2;
+  int pending = 0;
   for (int l = 0; l < d.L; ++l) {
     const LayerPtrs& q = m->pk.layers[l];
     const int64_t lo = (int64_t)l * d.layer_floats;
     LnMixArgs la;
     memset(&la, 0, sizeof la);
-    la.x = w.x; la.C = C; la.R = T; la.mode = LNMIX_SEQ;
+    la.x = xc; la.C = C; la.R = T; la.mode = LNMIX_SEQ;
+    if (pending) {
+      la.parts = w.part; la.nparts = pending; la.x_out = xn;
+      std::swap(xc, xn);
+      pending = 0;
+    }
     la.g = q.ln1_w; la.b = q.ln1_b;
     la.pool = pool; la.slot_stride = d.slot_floats; la.n_slots = n_slots; la.shift_off = lo;
     la.seq_slot = slot; la.shift_tmp = w.shift_tmp;
@@ -614,14 +627,20 @@ int enqueue_prefill_chunk(rwkv7_model* m, float* pool, int64_t n_slots, int slot
     ProjArgs po;
     memset(&po, 0, sizeof po);
     po.W = q.w_o; po.K = C; po.M = T; po.nseg = 1;
-    po.seg[0] = mkseg(0, C, EPI_RESID, w.yg, C, w.x, C);
-    RUN(RWKV7_K_PROJ_OUT, "proj_out", proj(false, po, C, w, st, m->opt_plan[2]));
+    po.seg[0] = mkseg(0, C, EPI_RESID, w.yg, C, xc, C);
+    RUN(RWKV7_K_PROJ_OUT, "proj_out", proj(false, po, C, w, st, m->opt_plan[2], &pending));
 
     LnMixArgs lc = la;
     lc.g = q.ln2_w; lc.b = q.ln2_b;
     lc.shift_off = lo + C;
     lc.mu = q.mu_k; lc.nq = 1;
     lc.out = w.xk; lc.out_q_stride = 0;
+    lc.x = xc; lc.parts = nullptr; lc.nparts = 0; lc.x_out = nullptr;
+    if (pending) {
+      lc.parts = w.part; lc.nparts = pending; lc.x_out = xn;
+      std::swap(xc, xn);
+      pending = 0;
+    }
     RUN(RWKV7_K_LN_MIX, "ln_mix(cmix)", launch_ln_mix(lc, st));
     RUN(RWKV7_K_OTHER, "shift copy", launch_copy_f32(slot_base + lo + C, w.shift_tmp, C, st));
 
@@ -635,9 +654,10 @@ int enqueue_prefill_chunk(rwkv7_model* m, float* pool, int64_t n_slots, int slot
     ProjArgs pv;
     memset(&pv, 0, sizeof pv);
     pv.W = q.w_val_km; pv.K = d.F; pv.M = T; pv.nseg = 1;
-    pv.seg[0] = mkseg(0, C, EPI_RESID, w.pre, d.F, w.x, C);
-    RUN(RWKV7_K_CMIX_VALUE, "cmix_value", proj(false, pv, C, w, st, m->opt_plan[4]));
+    pv.seg[0] = mkseg(0, C, EPI_RESID, w.pre, d.F, xc, C);
+    RUN(RWKV7_K_CMIX_VALUE, "cmix_value", proj(false, pv, C, w, st, m->opt_plan[4], &pending));
   }
+  // the last layer's value partials are not needed: prefill returns no logits
   return RWKV7_OK;
 }
 

@@ -164,6 +164,21 @@ __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
 #pragma unroll
   for (int i = 0; i < NE; ++i)
     pv[i] = sh_in ? sh_in[t + 256 * i] : prev_row ? xp[t + 256 * i] : 0.0f;
+  if (prev_row && a.nparts > 0) {
+    // the previous row's residual with its partials folded in, computed the
+    // same way as that row's own workgroup does (which writes it to x_out)
+    float acc[NE];
+#pragma unroll
+    for (int i = 0; i < NE; ++i) acc[i] = 0.0f;
+    const long rs = (long)a.R * C;
+    const float* p = a.parts + (long)(r - 1) * C + t;
+    for (int s = 0; s < a.nparts; ++s) {
+#pragma unroll
+      for (int i = 0; i < NE; ++i) acc[i] += p[s * rs + 256 * i];
+    }
+#pragma unroll
+    for (int i = 0; i < NE; ++i) pv[i] += acc[i];
+  }
 #pragma unroll
   for (int q = 0; q < 6; ++q)
 #pragma unroll
@@ -194,10 +209,11 @@ __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
 #pragma unroll
       for (int i = 0; i < NE; ++i) acc[i] += p[s * rs + 256 * i];
     }
+    float* xw = a.x_out ? a.x_out + (long)r * C : xr;
 #pragma unroll
     for (int i = 0; i < NE; ++i) {
       v[i] += acc[i];
-      xr[t + 256 * i] = v[i];
+      xw[t + 256 * i] = v[i];
     }
   }
 
@@ -243,7 +259,7 @@ __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
 hipError_t launch_ln_mix(const LnMixArgs& a, hipStream_t st) {
   if (a.C % 256) return hipErrorInvalidValue;
   if (a.nq < 1 || a.nq > 6) return hipErrorInvalidValue;
-  if (a.mode == LNMIX_SEQ && a.nparts) return hipErrorInvalidValue;
+  if (a.mode == LNMIX_SEQ && a.nparts && (!a.x_out || a.x_out == a.x)) return hipErrorInvalidValue;
   NE_DISPATCH(a.C, k_ln_mix, dim3(a.R), dim3(256), 0, st, a);
   return hipGetLastError();
 }

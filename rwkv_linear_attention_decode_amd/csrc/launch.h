@@ -73,7 +73,9 @@ enum { LNMIX_DECODE = 0, LNMIX_SEQ = 1, LNMIX_PLAIN = 2 };
 struct LnMixArgs {
   float* x;                 // [R][C] residual (updated when partials are folded in)
   const float* parts;       // [nparts][R][C] split-K partials of the residual projection that
-                            // precedes (added into x first), or nullptr; not in sequence mode
+                            // precedes (added into x first), or nullptr
+  float* x_out;             // nullptr: the folded residual replaces x; else it goes here (needed
+                            // in sequence mode, where a row also reads the previous row's x)
   int nparts;
   int C, R, mode;
   const float* g;
