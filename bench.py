@@ -371,7 +371,7 @@ def main():
     Ts = [int(t) for t in args.prefill.split(",") if t]
     n_slots = max([1] + Bs)
     m, weights = build_model(R, shape, n_slots=n_slots, max_B=max([1] + Bs),
-                             max_T=max([512] + [min(t, 512) for t in Ts]))
+                             max_T=max([512] + Ts))
 
     dt, nnz, kb, run_step, slot, tok, logits = decode_b1(R, args, shape, m)
     ms = dt / args.steps * 1e3

@@ -199,7 +199,8 @@ const char* rwkv7_last_error(void);
 #define RWKV7_OPT_GEMV_MAX_B 2     /* largest B served by the fp32-activation GEMV path */
 #define RWKV7_OPT_SPARSE_MAX_B 3   /* largest B served by the sparse channel-mix value path */
 #define RWKV7_OPT_KERNEL_TIMING 4  /* 1: bracket every launch with HIP events (no graph) */
-#define RWKV7_OPT_PREFILL_CHUNK 5  /* tokens per prefill chunk (<= the workspace's max_T) */
+#define RWKV7_OPT_PREFILL_CHUNK 5  /* tokens per prefill chunk (default 2048; halved until the
+                                      workspace holds it) */
 #define RWKV7_OPT_FUSE_LN 6        /* 1 (default): LayerNorm + token shift inside the GEMV path */
 #define RWKV7_OPT_FUSE_VALUE 7     /* 1 (default): on the GEMV path (B <= 2, sparse), each key
                                       workgroup also adds its active rows' value contributions

@@ -225,7 +225,7 @@ struct rwkv7_model {
   rwkv7_config cfg;
   Dims d;
   Packed pk;
-  int64_t opt_graph = 1, opt_gemv_max = 2, opt_sparse_max = 4, opt_timing = 0, opt_chunk = 512,
+  int64_t opt_graph = 1, opt_gemv_max = 2, opt_sparse_max = 4, opt_timing = 0, opt_chunk = 2048,
           opt_fuse_ln = 1, opt_fuse_value = 1;
   // tile plan per MFMA projection (RWKV7_OPT_GEMM_PLAN_* order), 0 = built-in
   int64_t opt_plan[6] = {0, 0, 0, 0, 0, 0};

@@ -622,7 +622,7 @@ static bool mm_cfg_ok(int tm, int tn, int ks, int pipe) {
 // MI355X: the 2.9B and 7.2B projections at M = 64, 256 and 512 with the
 // weights streamed from HBM (rotated over six copies), then the 2.9B model's
 // own projections chosen one at a time on whole graph-replayed decode steps
-// (B = 64, 256) and 512-token prefill chunks.  A kernel timed alone can
+// (B = 64, 256) and 512- and 2048-token prefill chunks.  A kernel timed alone can
 // rank plans differently from the step it runs in (the 64 x 160 key tiles
 // are 12 % faster alone and only even in the step), so the step decides.  "Narrow" outputs are one model width (value,
 // output projection), "head" the vocabulary, "wide" the rest (key, input
@@ -667,7 +667,8 @@ static MmPlan mm_choose(const ProjArgs& a, int total_rows) {
   }
   if (rank_k) return {2, 2, 32, 2, 0};
   if (K >= 4096) return N >= 10240 ? MmPlan{2, 4, 32, 1, 1} : MmPlan{4, 2, 64, 2, 0};
-  return N >= 10240 ? MmPlan{2, 2, 64, 3, 0} : MmPlan{4, 2, 64, 3, 0};
+  if (N >= 10240 && M <= 1024) return {2, 2, 64, 3, 0};
+  return {4, 2, 64, 3, 0};
 }
 
 hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int tm, int tn, int ks,

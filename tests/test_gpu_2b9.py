@@ -149,9 +149,10 @@ def test_prefill_128_vs_oracle_and_steps(model, W):
 @pytest.fixture(scope="module")
 def big(weights):
     """A second model in the bench's large configuration: 512 slots, B up to
-    256 (MFMA projections with the M = 256 tile plan), prefill chunks of 512."""
+    256 (MFMA projections with the M = 256 tile plan), prefill chunks of up
+    to 2048 tokens."""
     import rwkv_linear_attention_decode_amd as R
-    m = R.Model.from_numpy(S, weights, n_slots=512, max_B=256, max_T=512)
+    m = R.Model.from_numpy(S, weights, n_slots=512, max_B=256, max_T=2048)
     yield m
     m.close()
 
@@ -193,20 +194,27 @@ def test_batched_b256_rows_vs_b1_and_oracle(big, W):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("T", [512, 2048])
 def test_prefill_long_equals_steps(big, T):
-    """Prefill of T tokens in 512-token chunks (M = 512 MFMA tiles, LDS-staged
-    scan) lands on the state of T single-token GPU steps."""
+    """Prefill of T tokens as one chunk (M = T MFMA tiles, LDS-staged scan)
+    and in 512-token chunks lands on the state of T single-token GPU steps."""
+    import rwkv_linear_attention_decode_amd as R
     wl = synth.WORKLOADS["prefill_2.9b"]
     toks = synth.prefill_tokens(wl, T)
-    big.reset(dev([0, 1]))
+    big.reset(dev([0, 1, 2]))
     big.prefill(0, dev(toks))
+    big.set_option(R.OPT_PREFILL_CHUNK, 512)
+    try:
+        big.prefill(2, dev(toks))
+    finally:
+        big.set_option(R.OPT_PREFILL_CHUNK, 2048)
     logits = torch.empty(1, S.vocab, device="cuda")
     for t in toks:
         big.decode_step(dev([1]), dev([int(t)]), logits)
     torch.cuda.synchronize()
     a = big.slot_state(0).cpu().double().numpy()
     b = big.slot_state(1).cpu().double().numpy()
-    e = rel(a, b)
-    print(f"2.9B prefill T={T} vs {T} GPU steps: state rel L2 {e:.3e}")
-    assert e <= TOL
+    c = big.slot_state(2).cpu().double().numpy()
+    e, ec = rel(a, b), rel(c, b)
+    print(f"2.9B prefill T={T} vs {T} GPU steps: state rel L2 {e:.3e} (one chunk), {ec:.3e} (512-token chunks)")
+    assert e <= TOL and ec <= TOL
     cnt = big.counters().cpu().numpy()
-    assert cnt[0] == cnt[1] == T
+    assert cnt[0] == cnt[1] == cnt[2] == T

@@ -235,7 +235,7 @@ def test_prefill_equals_steps_on_gpu(model, R):
     try:
         model.prefill(4, dev(toks))
     finally:
-        model.set_option(R.OPT_PREFILL_CHUNK, 512)
+        model.set_option(R.OPT_PREFILL_CHUNK, 2048)
     a, b, c = gstate(model, 2), gstate(model, 3), gstate(model, 4)
     assert rel(a, b) <= TOL
     assert rel(c, a) <= 1e-5
