@@ -210,8 +210,9 @@ const char* rwkv7_last_error(void);
    workgroup tile (32 T rows x 32 N columns, T in {1, 2, 4}, N in {2, 4}; also T = 2, N = 5
    with loop 3 and 64-deep stages), the K stage depth
    KKK (32, 64 or 128), the K loop P (0 plain, 1 pipelined LDS reads, 2 two stages of global
-   loads in flight, 3 stages loaded straight into a three-deep LDS ring; 3 falls back to 2
-   (0 for 4 x 4 tiles) where K is not a multiple of KKK) and the K split S (0 automatic); e.g. 2206430 = 64 x 64
+   loads in flight, 3 stages loaded straight into a three-deep LDS ring, 4 the same with
+   eight waves (T, N in {2, 4}); 3 and 4 fall back to 2 (0 for 4 x 4 tiles) where K is not a
+   multiple of KKK) and the K split S (0 automatic); e.g. 2206430 = 64 x 64
    tiles, 64-deep stages, loop 3, automatic split.  Unsupported combinations fail with
    EINVAL. */
 #define RWKV7_OPT_GEMM_PLAN_PROJ_IN 8     /* r, k, v and the adapters' first stage */

@@ -36,7 +36,7 @@ OPT_GEMM_PLAN_HEAD = 13
 def gemm_plan_code(tm, tn, ks, pipe=0, split=0):
     """Value of an OPT_GEMM_PLAN_* option: tile 32*tm x 32*tn, stage depth ks,
     K loop `pipe` (0 plain, 1 pipelined LDS reads, 2 two stages of global loads in
-    flight, 3 LDS-DMA ring), K split (0 = automatic)."""
+    flight, 3 LDS-DMA ring, 4 the same with eight waves), K split (0 = automatic)."""
     return ((tm * 10 + tn) * 1000 + ks) * 100 + pipe * 10 + split
 K_LN_MIX, K_PROJ_IN, K_WKV, K_PROJ_OUT, K_CMIX_KEY, K_CMIX_VALUE, K_HEAD, K_OTHER = range(8)
 K_NAMES = ("ln_mix", "proj_in", "wkv", "proj_out", "cmix_key", "cmix_value", "head", "other")

@@ -354,13 +354,17 @@ template <int CPR>
 __device__ inline int swz(int r) {
   return CPR == 4 ? ((r >> 2) & 3) : CPR == 8 ? ((r >> 1) & 7) : (r & 15);
 }
-template <int TM, int TN, int KS>
-__global__ __launch_bounds__(256) void k_mm_dma(ProjArgs a) {
+// NW = 4: waves as 2 x 2, each (16 TM) x (16 TN); NW = 8 (K loop 4): waves
+// as 2 x 4, each (16 TM) x (8 TN): two waves per SIMD on the same tile.
+template <int TM, int TN, int KS, int NW>
+__global__ __launch_bounds__(64 * NW) void k_mm_dma(ProjArgs a) {
   constexpr int MT = 32 * TM, NT = 32 * TN, CPR = KS / 8, KH = KS / 32;
+  constexpr int WC = NW / 2;               // wave columns
+  constexpr int BN = 2 * TN / WC;          // 16 x 16 blocks per wave along N
   constexpr int SLOTS = (MT + NT) * CPR;   // 16-byte slots per stage
-  constexpr int NIW = SLOTS / 256;         // DMA instructions per wave and stage
+  constexpr int NIW = SLOTS / (64 * NW);   // DMA instructions per wave and stage
   constexpr int ASL = MT * CPR;            // slots of the A rows
-  static_assert(SLOTS % 256 == 0, "whole DMA instructions per wave");
+  static_assert(SLOTS % (64 * NW) == 0 && (2 * TN) % WC == 0, "whole DMA instructions and blocks per wave");
   __shared__ __attribute__((aligned(1024))) half_t L[3][SLOTS * 8];
 
   const int n_tiles = a.tile0[a.nseg];
@@ -391,14 +395,14 @@ __global__ __launch_bounds__(256) void k_mm_dma(ProjArgs a) {
   const int st1 = (int)((long)nst * (ks_id + 1) / a.split);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm0 = (wave >> 1) * 16 * TM, wn0 = (wave & 1) * 16 * TN;
+  const int wm0 = (wave / WC) * 16 * TM, wn0 = (wave % WC) * 16 * BN;
 
   // source of each lane in this wave's DMA instructions, at stage 0; rows
   // past the end read the last row (their outputs are not stored)
   const half_t* src[NIW];
 #pragma unroll
   for (int q = 0; q < NIW; ++q) {
-    const int S = (q * 4 + wave) * 64 + lane;
+    const int S = (q * NW + wave) * 64 + lane;
     if (S < ASL) {
       const int r = S / CPR, c = (S % CPR) ^ swz<CPR>(r);
       src[q] = A + (long)min(m0 + r, a.M - 1) * lda + c * 8;
@@ -412,9 +416,9 @@ __global__ __launch_bounds__(256) void k_mm_dma(ProjArgs a) {
 #pragma unroll
     for (int q = 0; q < NIW; ++q)
       dma16(src[q] + (long)stg * KS,
-            __builtin_amdgcn_readfirstlane(lds0 + slot * SLOTS * 16 + (q * 4 + wave) * 1024));
+            __builtin_amdgcn_readfirstlane(lds0 + slot * SLOTS * 16 + (q * NW + wave) * 1024));
   };
-  int aoff[KH][TM], boff[KH][TN];   // byte offsets of this lane's fragments in a stage
+  int aoff[KH][TM], boff[KH][BN];   // byte offsets of this lane's fragments in a stage
 #pragma unroll
   for (int h = 0; h < KH; ++h) {
     const int c = 4 * h + (lane >> 4);
@@ -424,29 +428,29 @@ __global__ __launch_bounds__(256) void k_mm_dma(ProjArgs a) {
       aoff[h][i] = (r * CPR + (c ^ swz<CPR>(r))) * 16;
     }
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
+    for (int j = 0; j < BN; ++j) {
       const int r = wn0 + 16 * j + (lane & 15);
       boff[h][j] = (ASL + r * CPR + (c ^ swz<CPR>(r))) * 16;
     }
   }
-  floatx4 acc[TM][TN];
+  floatx4 acc[TM][BN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < BN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int slot) {
     const char* Lb = reinterpret_cast<const char*>(&L[slot][0]);
 #pragma unroll
     for (int h = 0; h < KH; ++h) {
-      half8 af[TM], bf[TN];
+      half8 af[TM], bf[BN];
 #pragma unroll
       for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const half8*>(Lb + aoff[h][i]);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bf[j] = *reinterpret_cast<const half8*>(Lb + boff[h][j]);
+      for (int j = 0; j < BN; ++j) bf[j] = *reinterpret_cast<const half8*>(Lb + boff[h][j]);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < BN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
   };
@@ -479,7 +483,7 @@ __global__ __launch_bounds__(256) void k_mm_dma(ProjArgs a) {
     }
   }
   wait_vm<0>();
-  mm_epilogue<TM, TN>(a, sg, acc, ks_id, n0, m0, wm0, wn0, lane);
+  mm_epilogue<TM, BN>(a, sg, acc, ks_id, n0, m0, wm0, wn0, lane);
 }
 
 // Fixed-order sum of the split-K partials, then the segment's epilogue.
@@ -567,28 +571,34 @@ static void mm_launch_p(int ks, dim3 grid, hipStream_t st, const ProjArgs& a) {
 // LDS bytes of a k_mm_dma instantiation (three unpadded stages)
 static constexpr int mm_dma_lds_bytes(int tm, int tn, int ks) { return 3 * 32 * (tm + tn) * ks * 2; }
 
-template <int TM, int TN>
+template <int TM, int TN, int NW>
 static void mm_launch_dma(int ks, dim3 grid, hipStream_t st, const ProjArgs& a) {
-  if constexpr (TM >= 2 && (TM + TN) % 2 == 0) {
+  if constexpr (TM >= 2 && (TM + TN) % (NW / 2) == 0) {
     if (ks == 32) {
-      hipLaunchKernelGGL((k_mm_dma<TM, TN, 32>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_mm_dma<TM, TN, 32, NW>), grid, dim3(64 * NW), 0, st, a);
       return;
     }
   }
   if constexpr (mm_dma_lds_bytes(TM, TN, 128) <= 98304) {
     if (ks == 128) {
-      hipLaunchKernelGGL((k_mm_dma<TM, TN, 128>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_mm_dma<TM, TN, 128, NW>), grid, dim3(64 * NW), 0, st, a);
       return;
     }
   }
-  hipLaunchKernelGGL((k_mm_dma<TM, TN, 64>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_mm_dma<TM, TN, 64, NW>), grid, dim3(64 * NW), 0, st, a);
 }
 
 template <int TM, int TN>
 static void mm_launch(int ks, int pipe, dim3 grid, hipStream_t st, const ProjArgs& a) {
   if (pipe == 3) {
-    mm_launch_dma<TM, TN>(ks, grid, st, a);
+    mm_launch_dma<TM, TN, 4>(ks, grid, st, a);
     return;
+  }
+  if constexpr (TN % 2 == 0 && (TM + TN) % 2 == 0) {
+    if (pipe == 4) {
+      mm_launch_dma<TM, TN, 8>(ks, grid, st, a);
+      return;
+    }
   }
   if constexpr (TM + TN <= 6) {
     if (pipe == 1) {
@@ -604,7 +614,12 @@ static void mm_launch(int ks, int pipe, dim3 grid, hipStream_t st, const ProjArg
 }
 
 static bool mm_cfg_ok(int tm, int tn, int ks, int pipe) {
-  if (pipe < 0 || pipe > 3) return false;
+  if (pipe < 0 || pipe > 4) return false;
+  if (pipe == 4) {   // eight waves: N blocks split over four wave columns
+    if (!((tm == 2 || tm == 4) && (tn == 2 || tn == 4))) return false;
+    if (ks == 32) return (tm + tn) % 4 == 0;
+    return (ks == 64 || ks == 128) && mm_dma_lds_bytes(tm, tn, ks) <= 98304;
+  }
   if (pipe == 3) {
     if (tm == 2 && tn == 5) return ks == 64;   // 64 x 160 tiles (see mm_choose)
     if (!((tm == 1 || tm == 2 || tm == 4) && (tn == 2 || tn == 4))) return false;
@@ -641,10 +656,11 @@ static MmPlan mm_choose(const ProjArgs& a, int total_rows) {
     if (K >= 8192) {                                 // channel-mix value
       if (K >= 16384) return {4, 4, 64, 0, 6};
       if (M <= 64) return {2, 2, 64, 2, 0};
-      return M <= 256 ? MmPlan{2, 4, 64, 2, 6} : MmPlan{2, 4, 64, 3, 3};
+      if (M <= 256) return {4, 4, 64, 4, 6};
+      return M <= 1024 ? MmPlan{2, 4, 64, 3, 3} : MmPlan{4, 4, 64, 4, 0};
     }
     if (M <= 64) return {1, 2, 128, 0, 0};
-    return M <= 256 ? MmPlan{2, 2, 64, 3, 0} : MmPlan{4, 2, 64, 3, 0};
+    return M <= 256 ? MmPlan{2, 2, 64, 4, 0} : MmPlan{2, 4, 64, 4, 0};
   }
   if (N >= 32768) return M <= 64 ? MmPlan{2, 4, 64, 3, 0} : MmPlan{4, 4, 64, 0, 0};   // head
   const bool rank_k = K < 1024;                      // adapters' second stage
@@ -663,12 +679,12 @@ static MmPlan mm_choose(const ProjArgs& a, int total_rows) {
       const long r2 = ((N + 63) / 64 * mt + 255) / 256, r5 = ((N + 159) / 160 * mt + 255) / 256;
       if (r5 * 160 < r2 * 64) return {2, 5, 64, 3, 0};
     }
-    return N <= 8192 ? MmPlan{2, 2, 64, 2, 0} : MmPlan{2, 2, 64, 1, 0};
+    return N <= 8192 ? MmPlan{4, 2, 64, 4, 0} : MmPlan{2, 2, 64, 1, 0};
   }
   if (rank_k) return {2, 2, 32, 2, 0};
   if (K >= 4096) return N >= 10240 ? MmPlan{2, 4, 32, 1, 1} : MmPlan{4, 2, 64, 2, 0};
-  if (N >= 10240 && M <= 1024) return {2, 2, 64, 3, 0};
-  return {4, 2, 64, 3, 0};
+  if (N >= 10240) return M <= 1024 ? MmPlan{2, 2, 64, 4, 0} : MmPlan{4, 4, 64, 4, 0};
+  return {4, 2, 64, 4, 0};
 }
 
 hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int tm, int tn, int ks,
@@ -686,7 +702,7 @@ hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int 
     if (split <= 0) split = p.split;
   }
   if (!mm_cfg_ok(tm, tn, ks, pipe)) return hipErrorInvalidValue;
-  if (pipe == 3)   // the DMA loop needs whole stages: otherwise a register-staged loop
+  if (pipe >= 3)   // the DMA loops need whole stages: otherwise a register-staged loop
     for (int i = 0; i < a.nseg; ++i)
       if ((a.seg[i].W ? a.seg[i].K : a.K) % ks != 0) {
         if (tn == 5) tn = 4;   // 160-wide tiles exist for the DMA loop only
@@ -702,7 +718,7 @@ hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int 
     case 22: mm_launch<2, 2>(ks, pipe, grid, st, a); break;
     case 24: mm_launch<2, 4>(ks, pipe, grid, st, a); break;
     case 42: mm_launch<4, 2>(ks, pipe, grid, st, a); break;
-    case 25: mm_launch_dma<2, 5>(ks, grid, st, a); break;   // loop 3, ks 64 only
+    case 25: mm_launch_dma<2, 5, 4>(ks, grid, st, a); break;   // loop 3, ks 64 only
     default: mm_launch<4, 4>(ks, pipe, grid, st, a); break;
   }
   hipError_t e = hipGetLastError();
@@ -750,16 +766,16 @@ const char* gemm_kernel_name(int M, int N, int K) {
   const int tm = p.tm, ks = p.ks, pipe = p.pipe;
   int tn = p.tn;
   int ep = pipe;   // as launch_gemm_cfg falls back
-  if (pipe == 3 && K % ks != 0) {
+  if (pipe >= 3 && K % ks != 0) {
     if (tn == 5) tn = 4;
     ep = mm_cfg_ok(tm, tn, ks, 2) ? 2 : 0;
   }
-  static char names[4][3][3][4][28];
+  static char names[4][3][3][5][32];
   char* s = names[tm == 1 ? 0 : tm == 2 ? 1 : tm == 4 ? 2 : 3][tn == 2 ? 0 : tn == 4 ? 1 : 2]
                  [ks == 32 ? 0 : ks == 64 ? 1 : 2][ep];
   if (!s[0]) {
-    if (ep == 3)
-      snprintf(s, sizeof(names[0][0][0][0]), "k_mm_dma<%d, %d, %d>", tm, tn, ks);
+    if (ep >= 3)
+      snprintf(s, sizeof(names[0][0][0][0]), "k_mm_dma<%d, %d, %d, %d>", tm, tn, ks, ep == 4 ? 8 : 4);
     else
       snprintf(s, sizeof(names[0][0][0][0]), "k_mm<%d, %d, %d, %d>", tm, tn, ks, ep);
   }

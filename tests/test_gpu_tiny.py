@@ -165,10 +165,12 @@ GEMM_PLAN_KEYS = (8, 9, 10, 11, 12, 13)   # OPT_GEMM_PLAN_PROJ_IN .. _HEAD
     (2, 2, 64, 2, 0), (2, 2, 128, 2, 0), (1, 2, 64, 2, 0), (2, 4, 32, 2, 2),
     (4, 2, 64, 2, 1), (1, 4, 64, 2, 3),
     (2, 2, 64, 3, 0), (4, 4, 64, 3, 0), (1, 2, 128, 3, 0), (2, 4, 32, 3, 2),
-    (4, 2, 64, 3, 1), (1, 4, 64, 3, 3), (2, 2, 128, 3, 0), (2, 5, 64, 3, 0), (2, 5, 64, 3, 2)])
+    (4, 2, 64, 3, 1), (1, 4, 64, 3, 3), (2, 2, 128, 3, 0), (2, 5, 64, 3, 0), (2, 5, 64, 3, 2),
+    (2, 2, 64, 4, 0), (4, 4, 64, 4, 0), (2, 4, 64, 4, 2), (4, 2, 64, 4, 1), (2, 2, 32, 4, 0),
+    (4, 4, 32, 4, 3), (2, 2, 128, 4, 0)])
 def test_gemm_plans_match_oracle(model, W, R, tm, tn, ks, pipe, split):
     """Every MFMA projection (prefill and an 8-row step) forced onto one tile
-    plan: tile shapes, stage depths, the four K loops and K splits, with K
+    plan: tile shapes, stage depths, the five K loops and K splits, with K
     from 32 (adapter ranks) to 1024 (channel-mix value) and ragged row
     counts, against the oracle and against the built-in plans."""
     code = R.gemm_plan_code(tm, tn, ks, pipe, split)
@@ -216,9 +218,10 @@ def test_gemm_plans_match_oracle(model, W, R, tm, tn, ks, pipe, split):
 
 def test_gemm_plan_option_validation(model, R):
     for bad in (R.gemm_plan_code(3, 2, 64), R.gemm_plan_code(2, 2, 48), R.gemm_plan_code(4, 4, 64, 2),
-                R.gemm_plan_code(4, 4, 128), R.gemm_plan_code(2, 2, 64, 4), R.gemm_plan_code(2, 4, 128, 3),
+                R.gemm_plan_code(4, 4, 128), R.gemm_plan_code(1, 4, 64, 4), R.gemm_plan_code(2, 4, 128, 3),
                 R.gemm_plan_code(1, 2, 32, 3), R.gemm_plan_code(2, 5, 32, 3), R.gemm_plan_code(2, 5, 64, 2),
-                R.gemm_plan_code(4, 5, 64, 3), -5, 10 ** 8):
+                R.gemm_plan_code(4, 5, 64, 3), R.gemm_plan_code(1, 2, 64, 4), R.gemm_plan_code(2, 4, 32, 4),
+                R.gemm_plan_code(2, 4, 128, 4), R.gemm_plan_code(2, 2, 64, 5), -5, 10 ** 8):
         with pytest.raises(R.RWKV7Error):
             model.set_option(8, bad)
     model.set_option(8, 0)
