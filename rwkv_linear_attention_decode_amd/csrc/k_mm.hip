@@ -637,7 +637,8 @@ static bool mm_cfg_ok(int tm, int tn, int ks, int pipe) {
 // MI355X: the 2.9B and 7.2B projections at M = 64, 256 and 512 with the
 // weights streamed from HBM (rotated over six copies), then the 2.9B model's
 // own projections chosen one at a time on whole graph-replayed decode steps
-// (B = 64, 256) and 512- and 2048-token prefill chunks.  A kernel timed alone can
+// (B = 64, 256; the 7.2B model at B = 256) and 512- and 2048-token prefill
+// chunks.  A kernel timed alone can
 // rank plans differently from the step it runs in (the 64 x 160 key tiles
 // are 12 % faster alone and only even in the step), so the step decides.  "Narrow" outputs are one model width (value,
 // output projection), "head" the vocabulary, "wide" the rest (key, input
@@ -654,7 +655,7 @@ static MmPlan mm_choose(const ProjArgs& a, int total_rows) {
   if (M <= 32) return {1, 2, 128, 0, 0};
   if (N <= 4096) {                                   // narrow
     if (K >= 8192) {                                 // channel-mix value
-      if (K >= 16384) return {4, 4, 64, 0, 6};
+      if (K >= 16384) return M > 64 && M <= 256 ? MmPlan{4, 4, 64, 4, 3} : MmPlan{4, 4, 64, 0, 6};
       if (M <= 64) return {2, 2, 64, 2, 0};
       if (M <= 256) return {4, 4, 64, 4, 6};
       return M <= 1024 ? MmPlan{2, 4, 64, 3, 3} : MmPlan{4, 4, 64, 4, 0};
@@ -670,7 +671,7 @@ static MmPlan mm_choose(const ProjArgs& a, int total_rows) {
   }
   if (M <= 256) {
     if (rank_k) return {2, 2, 64, 2, 0};
-    if (K >= 4096) return N >= 16384 ? MmPlan{4, 2, 64, 1, 1} : MmPlan{4, 4, 64, 0, 2};
+    if (K >= 4096) return N >= 16384 ? MmPlan{4, 4, 64, 4, 0} : MmPlan{4, 2, 64, 4, 0};
     // one segment: 64 x 160 tiles when they fill the CUs in fewer column-widths
     // of rounds than 64 x 64 tiles (2.9B key at M = 256: 256 tiles, one per CU,
     // instead of 640, which leave half the CUs a third round)
