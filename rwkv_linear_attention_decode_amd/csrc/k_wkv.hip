@@ -516,21 +516,32 @@ __global__ __launch_bounds__(256) void k_wkv_scan(WkvArgs a) {
       const float4 av = B.a[tt][jq], bv = B.b[tt][jq], dv = B.d[tt][jq], kv = B.kt[tt][jq];
       const float4 rv = B.r[tt][jq];
       const float vi = B.v[tt][il];
+      const float br = B.brk[tt][0], kr = B.brk[tt][1];
       const float4 dr = make_float4(dv.x * rv.x, dv.y * rv.y, dv.z * rv.z, dv.w * rv.w);
       const float sa = sum16(s.x * av.x + s.y * av.y + s.z * av.z + s.w * av.w);
       const float sd = sum16(s.x * dr.x + s.y * dr.y + s.z * dr.z + s.w * dr.w);
-      const float y = sd + sa * B.brk[tt][0] + vi * B.brk[tt][1];
       s.x = s.x * dv.x + sa * bv.x + vi * kv.x;
       s.y = s.y * dv.y + sa * bv.y + vi * kv.y;
       s.z = s.z * dv.z + sa * bv.z + vi * kv.z;
       s.w = s.w * dv.w + sa * bv.w + vi * kv.w;
-      if (jq == 0) a.q_y[(long)(t0 + tt) * C + h * 64 + i] = y;
+      return sd + sa * br + vi * kr;   // the same in all 16 lanes of the row
     };
-    if (n == SCAN_TB) {   // whole block unrolled: the next token's LDS reads overlap this one
+    if (n == SCAN_TB) {
+      // whole block unrolled and branch-free, so the next token's LDS reads
+      // overlap this one: lane jq of each row keeps token jq's readout and
+      // stores it after the block
+      float ykeep = 0.f;
 #pragma unroll
-      for (int tt = 0; tt < SCAN_TB; ++tt) token(tt);
+      for (int tt = 0; tt < SCAN_TB; ++tt) {
+        const float y = token(tt);
+        ykeep = jq == tt ? y : ykeep;
+      }
+      a.q_y[(long)(t0 + jq) * C + h * 64 + i] = ykeep;
     } else {
-      for (int tt = 0; tt < n; ++tt) token(tt);
+      for (int tt = 0; tt < n; ++tt) {
+        const float y = token(tt);
+        if (jq == 0) a.q_y[(long)(t0 + tt) * C + h * 64 + i] = y;
+      }
     }
     if (more) store(buf ^ 1);
     __syncthreads();
