@@ -518,12 +518,16 @@ __global__ __launch_bounds__(256) void k_wkv_scan(WkvArgs a) {
       const float vi = B.v[tt][il];
       const float br = B.brk[tt][0], kr = B.brk[tt][1];
       const float4 dr = make_float4(dv.x * rv.x, dv.y * rv.y, dv.z * rv.z, dv.w * rv.w);
-      const float sa = sum16(s.x * av.x + s.y * av.y + s.z * av.z + s.w * av.w);
-      const float sd = sum16(s.x * dr.x + s.y * dr.y + s.z * dr.z + s.w * dr.w);
-      s.x = s.x * dv.x + sa * bv.x + vi * kv.x;
-      s.y = s.y * dv.y + sa * bv.y + vi * kv.y;
-      s.z = s.z * dv.z + sa * bv.z + vi * kv.z;
-      s.w = s.w * dv.w + sa * bv.w + vi * kv.w;
+      // pairwise partial dots (depth 3), and the update's terms that do not
+      // need S a computed while the row sums are in flight
+      const float sa = sum16(fmaf(s.y, av.y, s.x * av.x) + fmaf(s.w, av.w, s.z * av.z));
+      const float sd = sum16(fmaf(s.y, dr.y, s.x * dr.x) + fmaf(s.w, dr.w, s.z * dr.z));
+      const float4 u = make_float4(fmaf(vi, kv.x, s.x * dv.x), fmaf(vi, kv.y, s.y * dv.y),
+                                   fmaf(vi, kv.z, s.z * dv.z), fmaf(vi, kv.w, s.w * dv.w));
+      s.x = fmaf(sa, bv.x, u.x);
+      s.y = fmaf(sa, bv.y, u.y);
+      s.z = fmaf(sa, bv.z, u.z);
+      s.w = fmaf(sa, bv.w, u.w);
       return sd + sa * br + vi * kr;   // the same in all 16 lanes of the row
     };
     if (n == SCAN_TB) {
