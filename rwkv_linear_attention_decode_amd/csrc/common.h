@@ -163,6 +163,27 @@ RW_DEV Seg pick_seg(const ProjArgs& a, int row) {
   return s;
 }
 
+// The epilogue of segment `s` for a sum v at output column n (relative to
+// the segment); `resid` is the stored value EPI_RESID adds to.
+RW_DEV float epi_value(const Seg& s, int n, float v, float resid) {
+  switch (s.epi) {
+    case EPI_TANH: return tanhf(v);
+    case EPI_SIGMOID: return sigmoidf_(v);
+    case EPI_RESID: return resid + v;
+    case EPI_PRE: return v + s.aux[n];
+    case EPI_RELU2: {
+      const float z = v + s.aux[n];
+      return z > 0.0f ? z * z : 0.0f;
+    }
+    case EPI_DECAY: {
+      const float sg = 1.0f / (1.0f + expf(-(v + s.aux[n])));
+      return expf(-0.60653065971263342f * sg);
+    }
+    case EPI_SIGB: return 1.0f / (1.0f + expf(-(v + s.aux[n])));
+    default: return v;
+  }
+}
+
 // Apply the epilogue of segment `s` to output column n (relative to the
 // segment), activation row m.
 RW_DEV void epi_store(const Seg& s, int n, int m, float v) {

@@ -63,6 +63,77 @@ __device__ __forceinline__ void mm_epilogue(const ProjArgs& a, const Seg& sg, co
     }
 }
 
+// The same through LDS: the tile's sums go to `smem` (MT rows of NT + 4
+// floats; the stage buffers are free once the K loop is done), then every
+// thread writes runs of four columns of a row with one 16-byte store (fp32)
+// or 8-byte store (fp16), instead of the MFMA layout's single floats.
+// Ragged edges and unaligned outputs take the single-element path.
+template <int TM, int TN, int MT, int NT>
+__device__ __forceinline__ void mm_epilogue_lds(const ProjArgs& a, const Seg& sg, const floatx4 (&acc)[TM][TN],
+                                                int ks_id, int n0, int m0, int wm0, int wn0, int lane,
+                                                float* smem) {
+  constexpr int LDR = NT + 4;
+  constexpr int C4 = NT / 4;
+  const int fr = lane & 15;
+  const int er = (lane >> 4) * 4;
+  __syncthreads();   // every wave is done reading the stage buffers
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) smem[(wm0 + 16 * i + er + e) * LDR + wn0 + 16 * j + fr] = acc[i][j][e];
+  __syncthreads();
+  const bool split = a.split > 1;
+  float* P = a.part + (long)ks_id * a.M * a.total_rows;
+  const bool f16 = sg.out_f16 != 0;
+  for (int c = threadIdx.x; c < MT * C4; c += blockDim.x) {
+    const int r = c / C4, c4 = (c % C4) * 4;
+    const int m = m0 + r, n = n0 + c4;
+    if (m >= a.M || n >= sg.row1) continue;
+    const floatx4 v = *reinterpret_cast<const floatx4*>(&smem[r * LDR + c4]);
+    const bool whole = n + 3 < sg.row1;
+    if (split) {
+      float* q = P + (long)m * a.total_rows + n;
+      if (whole && ((uintptr_t)q & 15) == 0) {
+        stf4(q, v);
+      } else {
+        for (int k = 0; k < 4 && n + k < sg.row1; ++k) q[k] = v[k];
+      }
+      continue;
+    }
+    const int nl = n - sg.row0;
+    const long o = (long)m * sg.ld_out + nl;
+    const bool vec = whole && (f16 ? (((uintptr_t)((half_t*)sg.out + o) & 7) == 0)
+                                   : (((uintptr_t)((float*)sg.out + o) & 15) == 0));
+    if (!vec) {
+      for (int k = 0; k < 4 && n + k < sg.row1; ++k) epi_store(sg, nl + k, m, v[k]);
+      continue;
+    }
+    floatx4 rs = {0.f, 0.f, 0.f, 0.f};
+    if (sg.epi == EPI_RESID) {
+      if (f16) {
+        const half4 h = *reinterpret_cast<const half4*>((const half_t*)sg.out + o);
+        rs = floatx4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+      } else {
+        rs = ldf4((const float*)sg.out + o);
+      }
+    }
+    floatx4 out;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) out[k] = epi_value(sg, nl + k, v[k], rs[k]);
+    if (f16) {
+      half4 h;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) h[k] = (half_t)out[k];
+      *reinterpret_cast<half4*>((half_t*)sg.out + o) = h;
+    } else {
+      stf4((float*)sg.out + o, out);
+    }
+  }
+}
+
+
 // PIPE = 1 runs the K loop as a three-deep software pipeline (LDS fragment
 // reads of the next stage overlap the current stage's MFMAs); it costs
 // 2 (TM + TN) KS / 32 fragment registers and pays off on some shapes only.
@@ -75,8 +146,9 @@ __global__ __launch_bounds__(256) void k_mm(ProjArgs a) {
   constexpr int ACH = MT * CPR / 256;  // 16-byte A chunks per thread and stage
   constexpr int BCH = NT * CPR / 256;  // 16-byte W chunks per thread and stage
   constexpr int LDSR = KS + MM_PAD;    // halves per LDS row
-  __shared__ __attribute__((aligned(16))) half_t As[2][MT][LDSR];
-  __shared__ __attribute__((aligned(16))) half_t Bs[2][NT][LDSR];
+  // stage buffers: A rows 0 .. MT - 1, then the W rows (one array, so the
+  // epilogue can reuse it as one block)
+  __shared__ __attribute__((aligned(16))) half_t Sm[2][MT + NT][LDSR];
 
   // XCD-aware order: consecutive work items (same column tile, successive
   // M tiles and K ranges) go to the same XCD, whose L2 then serves the
@@ -145,12 +217,12 @@ __global__ __launch_bounds__(256) void k_mm(ProjArgs a) {
 #pragma unroll
     for (int p = 0; p < ACH; ++p) {
       const int c = p * 256 + tid;
-      st16(&As[buf][c / CPR][(c % CPR) * 8], ra[p]);
+      st16(&Sm[buf][c / CPR][(c % CPR) * 8], ra[p]);
     }
 #pragma unroll
     for (int p = 0; p < BCH; ++p) {
       const int c = p * 256 + tid;
-      st16(&Bs[buf][c / CPR][(c % CPR) * 8], rb[p]);
+      st16(&Sm[buf][MT + c / CPR][(c % CPR) * 8], rb[p]);
     }
   };
 
@@ -184,12 +256,12 @@ __global__ __launch_bounds__(256) void k_mm(ProjArgs a) {
 #pragma unroll
     for (int p = 0; p < ACH; ++p) {
       const int c = p * 256 + tid;
-      st16(&As[buf][c / CPR][(c % CPR) * 8], k0 + (c % CPR) * 8 < K ? pa[p] : z);
+      st16(&Sm[buf][c / CPR][(c % CPR) * 8], k0 + (c % CPR) * 8 < K ? pa[p] : z);
     }
 #pragma unroll
     for (int p = 0; p < BCH; ++p) {
       const int c = p * 256 + tid;
-      st16(&Bs[buf][c / CPR][(c % CPR) * 8], k0 + (c % CPR) * 8 < K ? pb[p] : z);
+      st16(&Sm[buf][MT + c / CPR][(c % CPR) * 8], k0 + (c % CPR) * 8 < K ? pb[p] : z);
     }
   };
   auto compute = [&](int buf) {
@@ -198,10 +270,10 @@ __global__ __launch_bounds__(256) void k_mm(ProjArgs a) {
       half8 af[TM], bf[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const half8*>(&As[buf][wm0 + 16 * i + fr][kk + fk]);
+        af[i] = *reinterpret_cast<const half8*>(&Sm[buf][wm0 + 16 * i + fr][kk + fk]);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        bf[j] = *reinterpret_cast<const half8*>(&Bs[buf][wn0 + 16 * j + fr][kk + fk]);
+        bf[j] = *reinterpret_cast<const half8*>(&Sm[buf][MT + wn0 + 16 * j + fr][kk + fk]);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -258,10 +330,10 @@ __global__ __launch_bounds__(256) void k_mm(ProjArgs a) {
       half8 af[TM], bf[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const half8*>(&As[buf][wm0 + 16 * i + fr][kk + fk]);
+        af[i] = *reinterpret_cast<const half8*>(&Sm[buf][wm0 + 16 * i + fr][kk + fk]);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        bf[j] = *reinterpret_cast<const half8*>(&Bs[buf][wn0 + 16 * j + fr][kk + fk]);
+        bf[j] = *reinterpret_cast<const half8*>(&Sm[buf][MT + wn0 + 16 * j + fr][kk + fk]);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -283,10 +355,10 @@ __global__ __launch_bounds__(256) void k_mm(ProjArgs a) {
     for (int h = 0; h < KH; ++h) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        pa[h][i] = *reinterpret_cast<const half8*>(&As[buf][wm0 + 16 * i + fr][32 * h + fk]);
+        pa[h][i] = *reinterpret_cast<const half8*>(&Sm[buf][wm0 + 16 * i + fr][32 * h + fk]);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        pb[h][j] = *reinterpret_cast<const half8*>(&Bs[buf][wn0 + 16 * j + fr][32 * h + fk]);
+        pb[h][j] = *reinterpret_cast<const half8*>(&Sm[buf][MT + wn0 + 16 * j + fr][32 * h + fk]);
     }
   };
   auto mfmas = [&](half8 (*pa)[TM], half8 (*pb)[TN]) {
@@ -324,7 +396,10 @@ __global__ __launch_bounds__(256) void k_mm(ProjArgs a) {
   }
   }
 
-  mm_epilogue<TM, TN>(a, sg, acc, ks_id, n0, m0, wm0, wn0, lane);
+  if constexpr (sizeof(Sm) >= MT * (NT + 4) * 4)
+    mm_epilogue_lds<TM, TN, MT, NT>(a, sg, acc, ks_id, n0, m0, wm0, wn0, lane, reinterpret_cast<float*>(&Sm[0][0][0]));
+  else
+    mm_epilogue<TM, TN>(a, sg, acc, ks_id, n0, m0, wm0, wn0, lane);
 }
 
 // ------------------------------------------------------- LDS-DMA variant
@@ -483,7 +558,10 @@ __global__ __launch_bounds__(64 * NW) void k_mm_dma(ProjArgs a) {
     }
   }
   wait_vm<0>();
-  mm_epilogue<TM, BN>(a, sg, acc, ks_id, n0, m0, wm0, wn0, lane);
+  if constexpr (sizeof(L) >= MT * (NT + 4) * 4)
+    mm_epilogue_lds<TM, BN, MT, NT>(a, sg, acc, ks_id, n0, m0, wm0, wn0, lane, reinterpret_cast<float*>(&L[0][0]));
+  else
+    mm_epilogue<TM, BN>(a, sg, acc, ks_id, n0, m0, wm0, wn0, lane);
 }
 
 // Fixed-order sum of the split-K partials, then the segment's epilogue.
