@@ -134,6 +134,53 @@ hipError_t launch_embed(const EmbedArgs& a, hipStream_t st) {
 // LayerNorm weights, the stored shift or the previous token's row, and all
 // nq mixing vectors) is issued before the first reduction barrier, so a row
 // costs one memory round trip.
+// Row access of k_ln_mix: with NE even, element i of thread t is column
+// 2t + 512 (i / 2) + i % 2, so every access moves two adjacent columns (one
+// 8-byte load or store); with NE odd, column t + 256 i.
+template <int NE>
+RW_DEV int lnm_col(int t, int i) {
+  return NE % 2 == 0 ? 2 * t + 512 * (i >> 1) + (i & 1) : t + 256 * i;
+}
+template <int NE>
+RW_DEV void lnm_load(const float* p, float (&d)[NE], int t) {
+  if constexpr (NE % 2 == 0) {
+#pragma unroll
+    for (int k = 0; k < NE / 2; ++k) {
+      const float2 x = *reinterpret_cast<const float2*>(p + 2 * t + 512 * k);
+      d[2 * k] = x.x;
+      d[2 * k + 1] = x.y;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NE; ++i) d[i] = p[t + 256 * i];
+  }
+}
+template <int NE>
+RW_DEV void lnm_store(float* p, const float (&v)[NE], int t) {
+  if constexpr (NE % 2 == 0) {
+#pragma unroll
+    for (int k = 0; k < NE / 2; ++k) *reinterpret_cast<float2*>(p + 2 * t + 512 * k) = make_float2(v[2 * k], v[2 * k + 1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NE; ++i) p[t + 256 * i] = v[i];
+  }
+}
+template <int NE>
+RW_DEV void lnm_store_f16(half_t* p, const float (&v)[NE], int t) {
+  if constexpr (NE % 2 == 0) {
+#pragma unroll
+    for (int k = 0; k < NE / 2; ++k) {
+      half2v h;
+      h[0] = (half_t)v[2 * k];
+      h[1] = (half_t)v[2 * k + 1];
+      *reinterpret_cast<half2v*>(p + 2 * t + 512 * k) = h;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NE; ++i) p[t + 256 * i] = (half_t)v[i];
+  }
+}
+
 template <int NE>
 __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
   __shared__ float red[16];
@@ -142,12 +189,9 @@ __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
   const int t = threadIdx.x;
   float v[NE], gv[NE], bv[NE], pv[NE], mu[6][NE];
   float* xr = a.x + (long)r * C;
-#pragma unroll
-  for (int i = 0; i < NE; ++i) {
-    v[i] = xr[t + 256 * i];
-    gv[i] = a.g[t + 256 * i];
-    bv[i] = a.b[t + 256 * i];
-  }
+  lnm_load<NE>(xr, v, t);
+  lnm_load<NE>(a.g, gv, t);
+  lnm_load<NE>(a.b, bv, t);
   const float* sh_in = nullptr;      // stored shift to mix with (decode / first token)
   float* sh_out = nullptr;           // where the new shift goes (decode)
   if (a.mode == LNMIX_DECODE) {
@@ -161,9 +205,14 @@ __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
   }
   const bool prev_row = a.mode == LNMIX_SEQ && r > 0;   // LayerNorm of the previous token
   const float* xp = a.x + (long)(r - 1) * C;
+  if (sh_in) {
+    lnm_load<NE>(sh_in, pv, t);
+  } else if (prev_row) {
+    lnm_load<NE>(xp, pv, t);
+  } else {
 #pragma unroll
-  for (int i = 0; i < NE; ++i)
-    pv[i] = sh_in ? sh_in[t + 256 * i] : prev_row ? xp[t + 256 * i] : 0.0f;
+    for (int i = 0; i < NE; ++i) pv[i] = 0.0f;
+  }
   if (prev_row && a.nparts > 0) {
     // the previous row's residual with its partials folded in, computed the
     // same way as that row's own workgroup does (which writes it to x_out)
@@ -171,19 +220,25 @@ __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
 #pragma unroll
     for (int i = 0; i < NE; ++i) acc[i] = 0.0f;
     const long rs = (long)a.R * C;
-    const float* p = a.parts + (long)(r - 1) * C + t;
+    const float* p = a.parts + (long)(r - 1) * C;
     for (int s = 0; s < a.nparts; ++s) {
+      float q[NE];
+      lnm_load<NE>(p + s * rs, q, t);
 #pragma unroll
-      for (int i = 0; i < NE; ++i) acc[i] += p[s * rs + 256 * i];
+      for (int i = 0; i < NE; ++i) acc[i] += q[i];
     }
 #pragma unroll
     for (int i = 0; i < NE; ++i) pv[i] += acc[i];
   }
 #pragma unroll
-  for (int q = 0; q < 6; ++q)
+  for (int q = 0; q < 6; ++q) {
+    if (q < a.nq && a.mu) {
+      lnm_load<NE>(a.mu + (long)q * C, mu[q], t);
+    } else {
 #pragma unroll
-    for (int i = 0; i < NE; ++i)
-      mu[q][i] = (q < a.nq && a.mu) ? a.mu[(long)q * C + t + 256 * i] : 0.0f;
+      for (int i = 0; i < NE; ++i) mu[q][i] = 0.0f;
+    }
+  }
   if (a.nparts > 0) {
     // x += (sum of the split-K partials of the residual projection, in range
     // order): the same arithmetic as the GEMM's own reduction pass
@@ -192,29 +247,26 @@ __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
 #pragma unroll
     for (int i = 0; i < NE; ++i) acc[i] = 0.0f;
     const long rs = (long)a.R * C;   // floats between ranges
-    const float* p = a.parts + (long)r * C + t;
+    const float* p = a.parts + (long)r * C;
     int s = 0;
     for (; s + 4 <= a.nparts; s += 4) {
       float q[4][NE];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < NE; ++i) q[j][i] = p[(s + j) * rs + 256 * i];
+      for (int j = 0; j < 4; ++j) lnm_load<NE>(p + (s + j) * rs, q[j], t);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < NE; ++i) acc[i] += q[j][i];
     }
     for (; s < a.nparts; ++s) {
+      float q[NE];
+      lnm_load<NE>(p + s * rs, q, t);
 #pragma unroll
-      for (int i = 0; i < NE; ++i) acc[i] += p[s * rs + 256 * i];
+      for (int i = 0; i < NE; ++i) acc[i] += q[i];
     }
-    float* xw = a.x_out ? a.x_out + (long)r * C : xr;
 #pragma unroll
-    for (int i = 0; i < NE; ++i) {
-      v[i] += acc[i];
-      xw[t + 256 * i] = v[i];
-    }
+    for (int i = 0; i < NE; ++i) v[i] += acc[i];
+    lnm_store<NE>(a.x_out ? a.x_out + (long)r * C : xr, v, t);
   }
 
   float mean, rstd;
@@ -231,28 +283,20 @@ __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
 #pragma unroll
     for (int i = 0; i < NE; ++i) pv[i] = u[i];
   }
-  if (sh_out) {
-#pragma unroll
-    for (int i = 0; i < NE; ++i) sh_out[t + 256 * i] = u[i];
-  }
-  if (a.mode == LNMIX_SEQ && r == a.R - 1) {
-#pragma unroll
-    for (int i = 0; i < NE; ++i) a.shift_tmp[t + 256 * i] = u[i];
-  }
+  if (sh_out) lnm_store<NE>(sh_out, u, t);
+  if (a.mode == LNMIX_SEQ && r == a.R - 1) lnm_store<NE>(a.shift_tmp, u, t);
 
 #pragma unroll
   for (int q = 0; q < 6; ++q) {
     if (q >= a.nq) break;
+    float o[NE];
 #pragma unroll
-    for (int i = 0; i < NE; ++i) {
-      const int c = t + 256 * i;
-      const float o = u[i] + (pv[i] - u[i]) * mu[q][i];
-      const long off = q * a.out_q_stride + (long)r * C + c;
-      if (a.out_f16)
-        ((half_t*)a.out)[off] = (half_t)o;
-      else
-        ((float*)a.out)[off] = o;
-    }
+    for (int i = 0; i < NE; ++i) o[i] = u[i] + (pv[i] - u[i]) * mu[q][i];
+    const long off = q * a.out_q_stride + (long)r * C;
+    if (a.out_f16)
+      lnm_store_f16<NE>((half_t*)a.out + off, o, t);
+    else
+      lnm_store<NE>((float*)a.out + off, o, t);
   }
 }
 
