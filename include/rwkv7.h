@@ -205,6 +205,10 @@ const char* rwkv7_last_error(void);
 #define RWKV7_OPT_FUSE_VALUE 7     /* 1 (default): on the GEMV path (B <= 2, sparse), each key
                                       workgroup also adds its active rows' value contributions
                                       into per-workgroup partial sums, folded in a fixed order */
+#define RWKV7_OPT_PREFILL_SCAN 14  /* WKV recurrence of rwkv7_prefill_seq: 0 (default) chunked
+                                      for chunks of >= 32 tokens, else serial; 1 serial (one
+                                      token after another); 2 chunked (16-token blocks in closed
+                                      form, the state carried block to block) */
 /* Tile plan of one MFMA projection (B > GEMV_MAX_B and prefill); 0 (default) = the built-in
    plan for the shape.  Otherwise the decimal digits "T N KKK P S" of the value give the
    workgroup tile (32 T rows x 32 N columns, T in {1, 2, 4}, N in {2, 4}; also T = 2, N = 5

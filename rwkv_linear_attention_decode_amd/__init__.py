@@ -31,6 +31,7 @@ OPT_GEMM_PLAN_PROJ_OUT = 10
 OPT_GEMM_PLAN_CMIX_KEY = 11
 OPT_GEMM_PLAN_CMIX_VALUE = 12
 OPT_GEMM_PLAN_HEAD = 13
+OPT_PREFILL_SCAN = 14
 
 
 def gemm_plan_code(tm, tn, ks, pipe=0, split=0):

@@ -41,6 +41,8 @@ int hip_fail(hipError_t e, const char* what) {
   } while (0)
 
 constexpr uint64_t ALIGN = 256;
+// shortest prefill chunk that takes the chunked WKV scan under the automatic choice
+constexpr int PREFILL_CHUNKED_MIN_T = 32;
 inline uint64_t align_up(uint64_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 inline int pad64(int x) { return (x + 63) / 64 * 64; }
 
@@ -142,6 +144,7 @@ struct Ws {
   unsigned char* mask;
   int *dbg_idx, *dbg_cnt;
   float *q_d, *q_a, *q_b, *q_kt, *q_v, *q_g, *q_bonus, *q_brk, *q_y;
+  float* q_rec;           // chunked prefill scan records
   float* part;            // split-K partial sums of the MFMA projections
   int64_t part_floats;
   float* vpart;           // value partials of the fused key projection
@@ -187,6 +190,7 @@ Ws ws_layout(const Dims& d, int R, char* base) {
   w.q_y = (float*)take(r * C * 4);
   w.q_bonus = (float*)take(r * d.H * 4);
   w.q_brk = (float*)take(r * d.H * 2 * 4);
+  w.q_rec = (float*)take((uint64_t)wkv_chunk_rec_floats(R, d.H) * 4);
   w.part_floats = (int64_t)(r * 16 * C);
   w.part = (float*)take(r * 16 * C * 4);
   // value partials of the fused key projection (B <= 2 rows, 16 key rows per workgroup)
@@ -226,7 +230,7 @@ struct rwkv7_model {
   Dims d;
   Packed pk;
   int64_t opt_graph = 1, opt_gemv_max = 2, opt_sparse_max = 4, opt_timing = 0, opt_chunk = 2048,
-          opt_fuse_ln = 1, opt_fuse_value = 1;
+          opt_fuse_ln = 1, opt_fuse_value = 1, opt_prefill_scan = 0;
   // tile plan per MFMA projection (RWKV7_OPT_GEMM_PLAN_* order), 0 = built-in
   int64_t opt_plan[6] = {0, 0, 0, 0, 0, 0};
   std::vector<TimedLaunch> pending;
@@ -398,7 +402,7 @@ WkvArgs wkv_args(const rwkv7_model* m, int l, float* pool, int64_t n_slots, cons
   a.yout = w.yg;
   a.yout_f16 = f16 ? 1 : 0;
   a.q_d = w.q_d; a.q_a = w.q_a; a.q_b = w.q_b; a.q_kt = w.q_kt; a.q_v = w.q_v; a.q_g = w.q_g;
-  a.q_bonus = w.q_bonus; a.q_brk = w.q_brk; a.q_y = w.q_y;
+  a.q_bonus = w.q_bonus; a.q_brk = w.q_brk; a.q_y = w.q_y; a.q_rec = w.q_rec;
   return a;
 }
 
@@ -621,7 +625,12 @@ int enqueue_prefill_chunk(rwkv7_model* m, float* pool, int64_t n_slots, int slot
     wa.seq_slot = slot;
     wa.lo = w.lo;
     RUN(RWKV7_K_WKV, "wkv_prep", launch_wkv_prep(wa, st));
-    RUN(RWKV7_K_WKV, "wkv_scan", launch_wkv_scan(wa, st));
+    if (m->opt_prefill_scan == 2 || (m->opt_prefill_scan == 0 && T >= PREFILL_CHUNKED_MIN_T)) {
+      RUN(RWKV7_K_WKV, "wkv_chunk_prep", launch_wkv_chunk_prep(wa, st));
+      RUN(RWKV7_K_WKV, "wkv_chunk_scan", launch_wkv_chunk_scan(wa, st));
+    } else {
+      RUN(RWKV7_K_WKV, "wkv_scan", launch_wkv_scan(wa, st));
+    }
     RUN(RWKV7_K_WKV, "wkv_post", launch_wkv_post(wa, st));
 
     ProjArgs po;
@@ -1069,6 +1078,9 @@ int rwkv7_set_option(rwkv7_model* m, int32_t key, int64_t value) {
       m->opt_chunk = value; break;
     case RWKV7_OPT_FUSE_LN: m->opt_fuse_ln = value ? 1 : 0; break;
     case RWKV7_OPT_FUSE_VALUE: m->opt_fuse_value = value ? 1 : 0; break;
+    case RWKV7_OPT_PREFILL_SCAN:
+      if (value < 0 || value > 2) return fail(RWKV7_EINVAL, "PREFILL_SCAN must be 0, 1 or 2");
+      m->opt_prefill_scan = value; break;
     case RWKV7_OPT_GEMM_PLAN_PROJ_IN:
     case RWKV7_OPT_GEMM_PLAN_ADAPTERS:
     case RWKV7_OPT_GEMM_PLAN_PROJ_OUT:
@@ -1102,6 +1114,7 @@ int rwkv7_get_option(const rwkv7_model* m, int32_t key, int64_t* value) {
     case RWKV7_OPT_PREFILL_CHUNK: *value = m->opt_chunk; break;
     case RWKV7_OPT_FUSE_LN: *value = m->opt_fuse_ln; break;
     case RWKV7_OPT_FUSE_VALUE: *value = m->opt_fuse_value; break;
+    case RWKV7_OPT_PREFILL_SCAN: *value = m->opt_prefill_scan; break;
     case RWKV7_OPT_GEMM_PLAN_PROJ_IN:
     case RWKV7_OPT_GEMM_PLAN_ADAPTERS:
     case RWKV7_OPT_GEMM_PLAN_PROJ_OUT:

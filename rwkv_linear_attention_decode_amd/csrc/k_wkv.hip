@@ -554,6 +554,279 @@ __global__ __launch_bounds__(256) void k_wkv_scan(WkvArgs a) {
   *reinterpret_cast<float4*>(S) = s;
 }
 
+// ---------------------------------------------------------------- chunked prefill scan
+// The recurrence above, taken CH = 16 tokens at a time in closed form (the
+// product of a chunk's transitions diag(d_t) + a_t b_t^T in WY form).  Per
+// key column j let l_t = sum_{s <= t} log d_s and define the decayed vectors
+//   abar_t = a_t e^{l_{t-1}}, rbar_t = r_t e^{l_t}, bhat_t = b_t e^{-l_t},
+//   khat_t = k_t e^{-l_t},    btil_t = b_t e^{l_L - l_t}, ktil_t = k_t e^{l_L - l_t}
+// (t = 1..L, l_0 = 0).  With the 16 x 16 matrices C = abar bhat^T and
+// E = abar khat^T below the diagonal, F = rbar bhat^T and H = rbar khat^T on
+// and below it,
+//   A2 = (I - C)^{-1} abar,  G = (I - C)^{-1} E,  K2 = ktil + G^T btil,
+//   Q = rbar + F A2,          Z = F G + H,
+// the chunk's readouts (rows t of Y) and the state after it are
+//   Y = S Q^T + (Z V)^T,      S' = S diag(e^{l_L}) + (S A2^T) btil + V^T K2
+// with S the state entering the chunk and V the chunk's values.  Everything
+// but the last line is independent of S, so k_wkv_chunk_prep computes it for
+// all (chunk, head) pairs at once; k_wkv_chunk_scan then carries S through
+// the chunks, two 16-deep contractions per chunk instead of 16 dependent
+// rank-1 steps.  Padding tokens (past T) have d = 1 and zero vectors, so they
+// change nothing.
+constexpr int CH = 16;
+// per (chunk, head) record, floats:
+//   A2 [16][64] | Q [16][64] | btil^T [64][16] | K2^T [64][16] | Z [16][16] | e^{l_L} [64]
+enum : int { R_A2 = 0, R_Q = 1024, R_BT = 2048, R_K2T = 3072, R_Z = 4096, R_EL = 4352, REC = 4416 };
+
+// D += A B over a 4-deep slice on the fp32 matrix cores: lane l supplies
+// A[l % 16][l / 16] and B[l / 16][l % 16] and holds D[4 (l / 16) + i][l % 16]
+// in component i.
+RW_DEV floatx4 mfma4(float x, float y, floatx4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, acc, 0, 0, 0);
+}
+
+struct ChunkPrepLds {
+  float ab[CH][64], rb[CH][64], bh[CH][64], kh[CH][64], bt[CH][64], kt[CH][64], ld[CH][64];
+  float a2[CH][64];
+  float m[4][CH][CH + 1];   // C, E, F, H
+  float g[CH][CH + 1];
+};
+
+// Grid: n_chunks * H workgroups of 256 threads; thread (t, j4) = (tid / 16,
+// 4 (tid % 16)) owns token t of the chunk and key columns j4..j4+3.
+__global__ __launch_bounds__(256) void k_wkv_chunk_prep(WkvArgs a) {
+  __shared__ __attribute__((aligned(16))) ChunkPrepLds L;
+  const int H = a.H, C = a.C, T = a.B;
+  const int c = blockIdx.x / H, h = blockIdx.x % H;
+  const int tid = threadIdx.x;
+  const int t = tid >> 4, j4 = (tid & 15) * 4;
+  const int tk = c * CH + t;
+  const bool live = tk < T;
+  const int tc = live ? tk : T - 1;   // clamped: every load is issued
+  const long o = (long)tc * C + h * 64 + j4;
+  floatx4 av = ldf4(a.q_a + o), bv = ldf4(a.q_b + o), kv = ldf4(a.q_kt + o), dv = ldf4(a.q_d + o);
+  floatx4 rv = ldf4(a.rkv + (long)tc * 3 * C + h * 64 + j4);
+  if (!live) {
+    av = bv = kv = rv = floatx4{0.f, 0.f, 0.f, 0.f};
+    dv = floatx4{1.f, 1.f, 1.f, 1.f};
+  }
+  floatx4 lg;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) lg[e] = logf(dv[e]);
+  stf4(&L.ld[t][j4], lg);
+  __syncthreads();
+  // prefix sums of log d: l_{t-1}, l_t and l_L, added in the same order by every thread
+  floatx4 run = {0.f, 0.f, 0.f, 0.f}, lm1 = run, lt = run;
+#pragma unroll
+  for (int s = 0; s < CH; ++s) {
+    if (s == t) lm1 = run;
+    run += ldf4(&L.ld[s][j4]);
+    if (s == t) lt = run;
+  }
+  floatx4 ab, rb, bh, kh, bt, kt, el;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float em1 = expf(lm1[e]), et = expf(lt[e]), ent = expf(-lt[e]), eLt = expf(run[e] - lt[e]);
+    ab[e] = av[e] * em1;
+    rb[e] = rv[e] * et;
+    bh[e] = bv[e] * ent;
+    kh[e] = kv[e] * ent;
+    bt[e] = bv[e] * eLt;
+    kt[e] = kv[e] * eLt;
+    el[e] = expf(run[e]);
+  }
+  stf4(&L.ab[t][j4], ab);
+  stf4(&L.rb[t][j4], rb);
+  stf4(&L.bh[t][j4], bh);
+  stf4(&L.kh[t][j4], kh);
+  stf4(&L.bt[t][j4], bt);
+  stf4(&L.kt[t][j4], kt);
+  __syncthreads();
+
+  // wave w forms one of C, E, F, H (16 x 16, 64-deep) on the matrix cores;
+  // the 64 key columns are visited in 16 slices of 4, lane group g taking
+  // columns 16 jb + 4 g + kk of slice 4 jb + kk, so each lane reads float4s
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  {
+    const float(*A)[64] = w < 2 ? L.ab : L.rb;
+    const float(*B)[64] = (w & 1) ? L.kh : L.bh;
+    floatx4 m = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      const floatx4 x = ldf4(&A[c16][16 * jb + 4 * g]);
+      const floatx4 y = ldf4(&B[c16][16 * jb + 4 * g]);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) m = mfma4(x[kk], y[kk], m);
+    }
+    const bool strict = w < 2;   // C and E exclude the diagonal
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int r = 4 * g + ii;
+      L.m[w][r][c16] = (c16 < r || (!strict && c16 == r)) ? m[ii] : 0.f;
+    }
+  }
+  __syncthreads();
+  // (I - C) X = [abar | E] by forward substitution, one column per thread
+  if (tid < 64 + CH) {
+    float x[CH];
+#pragma unroll
+    for (int r = 0; r < CH; ++r) {
+      float v = tid < 64 ? L.ab[r][tid] : L.m[1][r][tid - 64];
+#pragma unroll
+      for (int s = 0; s < r; ++s) v = fmaf(L.m[0][r][s], x[s], v);
+      x[r] = v;
+    }
+#pragma unroll
+    for (int r = 0; r < CH; ++r) {
+      if (tid < 64) L.a2[r][tid] = x[r];
+      else L.g[r][tid - 64] = x[r];
+    }
+  }
+  __syncthreads();
+
+  float* rec = a.q_rec + ((long)c * H + h) * REC;
+  {
+    // A2 and Q = rbar + F A2, row t
+    const floatx4 a2 = ldf4(&L.a2[t][j4]);
+    floatx4 qv = rb;
+#pragma unroll
+    for (int s = 0; s < CH; ++s) {
+      const float f = L.m[2][t][s];
+      const floatx4 x = ldf4(&L.a2[s][j4]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qv[e] = fmaf(f, x[e], qv[e]);
+    }
+    stf4(rec + R_A2 + t * 64 + j4, a2);
+    stf4(rec + R_Q + t * 64 + j4, qv);
+    if (tid < 16) stf4(rec + R_EL + j4, el);
+  }
+  {
+    // Z = F G + H, entry (t, s)
+    const int zt = tid >> 4, zs = tid & 15;
+    float z = L.m[3][zt][zs];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) z = fmaf(L.m[2][zt][u], L.g[u][zs], z);
+    rec[R_Z + zt * CH + zs] = z;
+  }
+  {
+    // btil^T and K2^T = ktil^T + btil^T G, key column j, tokens s4..s4+3
+    const int j = tid >> 2, s4 = (tid & 3) * 4;
+    floatx4 bq, k2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bq[e] = L.bt[s4 + e][j];
+      k2[e] = L.kt[s4 + e][j];
+    }
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const float bb = L.bt[u][j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) k2[e] = fmaf(L.g[u][s4 + e], bb, k2[e]);
+    }
+    stf4(rec + R_BT + j * CH + s4, bq);
+    stf4(rec + R_K2T + j * CH + s4, k2);
+  }
+}
+
+// Grid: H * 4 workgroups; workgroup (h, q) carries value rows [16 q, 16 q + 16)
+// of head h.  Wave w holds the 16 x 16 block of S^T for key columns
+// [16 w, 16 w + 16) in the matrix-core accumulator layout (lane l, component
+// i: S[16 q + l % 16][16 w + 4 (l / 16) + i]), which is also the operand
+// layout of both contractions:
+//   readouts  P^T = [A2; Q] S^T   (each wave sums its 16 key columns; the four
+//                                  partial tiles meet through LDS)
+//   update    S^T <- diag(e^{l_L}) S^T + btil^T (S A2^T)^T + K2^T V
+// Chunk records are staged through a three-deep LDS ring, loaded two chunks
+// ahead, so one barrier per chunk orders the ring, the partial sums and the
+// readouts.
+struct ChunkBuf {
+  float rec[REC];
+  float vt[16][20];   // V^T of the workgroup's 16 value rows (row stride 20 keeps float4 alignment)
+};
+
+__global__ __launch_bounds__(256) void k_wkv_chunk_scan(WkvArgs a) {
+  __shared__ __attribute__((aligned(16))) ChunkBuf cb[3];
+  __shared__ floatx4 xch[2][4][2][64];
+  const int h = blockIdx.x >> 2, q = blockIdx.x & 3;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int C = a.C, T = a.B, H = a.H;
+  const int nc = (T + CH - 1) / CH;
+  float* S = a.pool + (long)a.seq_slot * a.slot_stride + a.layer_off + 2L * C + (long)h * 4096 +
+             (16 * q + c16) * 64 + 16 * w + 4 * g;
+  floatx4 st = ldf4(S);
+
+  floatx4 rr[5];
+  float rv = 0.f;
+  auto load = [&](int c) {
+    const float* rec = a.q_rec + ((long)c * H + h) * REC;
+#pragma unroll
+    for (int p = 0; p < 5; ++p) {
+      const int e = p * 256 + tid;
+      rr[p] = ldf4(rec + 4 * (e < REC / 4 ? e : REC / 4 - 1));
+    }
+    const int tk = c * CH + (tid >> 4);
+    const float v = a.q_v[(long)(tk < T ? tk : T - 1) * C + h * 64 + 16 * q + (tid & 15)];
+    rv = tk < T ? v : 0.f;
+  };
+  auto store = [&](int b) {
+#pragma unroll
+    for (int p = 0; p < 5; ++p) {
+      const int e = p * 256 + tid;
+      if (e < REC / 4) stf4(&cb[b].rec[4 * e], rr[p]);
+    }
+    cb[b].vt[tid & 15][tid >> 4] = rv;
+  };
+
+  load(0);
+  store(0);
+  if (nc > 1) load(1);
+  __syncthreads();
+  for (int c = 0; c < nc; ++c) {
+    const ChunkBuf& B = cb[c % 3];
+    // this wave's share of the readout sums: 16 key columns of S A2^T and
+    // S Q^T, plus key slice w of Z V
+    floatx4 pa = {0.f, 0.f, 0.f, 0.f}, pq = pa;
+    {
+      const floatx4 av = ldf4(&B.rec[R_A2 + c16 * 64 + 16 * w + 4 * g]);
+      const floatx4 qv = ldf4(&B.rec[R_Q + c16 * 64 + 16 * w + 4 * g]);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        pa = mfma4(av[kk], st[kk], pa);
+        pq = mfma4(qv[kk], st[kk], pq);
+      }
+      pq = mfma4(B.rec[R_Z + c16 * CH + 4 * w + g], B.vt[c16][4 * w + g], pq);
+    }
+    xch[c & 1][w][0][lane] = pa;
+    xch[c & 1][w][1][lane] = pq;
+    if (c + 1 < nc) store((c + 1) % 3);
+    __syncthreads();
+    if (c + 2 < nc) load(c + 2);
+    // the four waves' partial tiles, added in wave order: lane l, component i
+    // holds (S A2^T)[16 q + l % 16][4 (l / 16) + i] and likewise the readout
+    floatx4 sa = xch[c & 1][0][0][lane], sq = xch[c & 1][0][1][lane];
+#pragma unroll
+    for (int v = 1; v < 4; ++v) {
+      sa += xch[c & 1][v][0][lane];
+      sq += xch[c & 1][v][1][lane];
+    }
+    {
+      const int ty = c * CH + 4 * g + w;   // wave w stores component w
+      const float y = w == 0 ? sq[0] : w == 1 ? sq[1] : w == 2 ? sq[2] : sq[3];
+      if (ty < T) a.q_y[(long)ty * C + h * 64 + 16 * q + c16] = y;
+    }
+    const floatx4 el = ldf4(&B.rec[R_EL + 16 * w + 4 * g]);
+    const floatx4 bq = ldf4(&B.rec[R_BT + (16 * w + c16) * CH + 4 * g]);
+    const floatx4 k2 = ldf4(&B.rec[R_K2T + (16 * w + c16) * CH + 4 * g]);
+    const floatx4 vq = ldf4(&B.vt[c16][4 * g]);
+    st *= el;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) st = mfma4(bq[kk], sa[kk], st);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) st = mfma4(k2[kk], vq[kk], st);
+  }
+  stf4(S, st);
+}
+
 __global__ __launch_bounds__(64) void k_wkv_post(WkvArgs a) {
   __shared__ HeadVecs hv;
   const int tk = blockIdx.x / a.H;
@@ -589,6 +862,18 @@ hipError_t launch_wkv_scan(const WkvArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_wkv_scan, dim3(a.H * 4), dim3(256), 0, st, a);
   return hipGetLastError();
 }
+hipError_t launch_wkv_chunk_prep(const WkvArgs& a, hipStream_t st) {
+  if (!a.q_rec || a.B < 1) return hipErrorInvalidValue;
+  const int nc = (a.B + CH - 1) / CH;
+  hipLaunchKernelGGL(k_wkv_chunk_prep, dim3(nc * a.H), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+hipError_t launch_wkv_chunk_scan(const WkvArgs& a, hipStream_t st) {
+  if (!a.q_rec || a.B < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_wkv_chunk_scan, dim3(a.H * 4), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+int64_t wkv_chunk_rec_floats(int T, int H) { return (int64_t)((T + CH - 1) / CH) * H * REC; }
 hipError_t launch_wkv_post(const WkvArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_wkv_post, dim3(a.B * a.H), dim3(64), 0, st, a);
   return hipGetLastError();

@@ -194,18 +194,24 @@ def test_batched_b256_rows_vs_b1_and_oracle(big, W):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("T", [512, 2048])
 def test_prefill_long_equals_steps(big, T):
-    """Prefill of T tokens as one chunk (M = T MFMA tiles, LDS-staged scan)
-    and in 512-token chunks lands on the state of T single-token GPU steps."""
+    """Prefill of T tokens as one chunk (M = T MFMA tiles, chunked WKV scan)
+    and in 512-token chunks lands on the state of T single-token GPU steps; the
+    serial WKV scan lands on the same state."""
     import rwkv_linear_attention_decode_amd as R
     wl = synth.WORKLOADS["prefill_2.9b"]
     toks = synth.prefill_tokens(wl, T)
-    big.reset(dev([0, 1, 2]))
+    big.reset(dev([0, 1, 2, 3]))
     big.prefill(0, dev(toks))
     big.set_option(R.OPT_PREFILL_CHUNK, 512)
     try:
         big.prefill(2, dev(toks))
     finally:
         big.set_option(R.OPT_PREFILL_CHUNK, 2048)
+    big.set_option(R.OPT_PREFILL_SCAN, 1)   # serial WKV scan
+    try:
+        big.prefill(3, dev(toks))
+    finally:
+        big.set_option(R.OPT_PREFILL_SCAN, 0)
     logits = torch.empty(1, S.vocab, device="cuda")
     for t in toks:
         big.decode_step(dev([1]), dev([int(t)]), logits)
@@ -213,8 +219,11 @@ def test_prefill_long_equals_steps(big, T):
     a = big.slot_state(0).cpu().double().numpy()
     b = big.slot_state(1).cpu().double().numpy()
     c = big.slot_state(2).cpu().double().numpy()
-    e, ec = rel(a, b), rel(c, b)
-    print(f"2.9B prefill T={T} vs {T} GPU steps: state rel L2 {e:.3e} (one chunk), {ec:.3e} (512-token chunks)")
+    d = big.slot_state(3).cpu().double().numpy()
+    e, ec, es = rel(a, b), rel(c, b), rel(a, d)
+    print(f"2.9B prefill T={T} vs {T} GPU steps: state rel L2 {e:.3e} (one chunk), {ec:.3e} "
+          f"(512-token chunks); chunked vs serial scan {es:.3e}")
     assert e <= TOL and ec <= TOL
+    assert es <= 1e-3   # differently rounded scans; fp16 activations downstream (step 4.9e-4)
     cnt = big.counters().cpu().numpy()
-    assert cnt[0] == cnt[1] == cnt[2] == T
+    assert cnt[0] == cnt[1] == cnt[2] == cnt[3] == T
