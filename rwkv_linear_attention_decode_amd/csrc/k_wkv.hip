@@ -572,8 +572,12 @@ __global__ __launch_bounds__(256) void k_wkv_scan(WkvArgs a) {
 // all (chunk, head) pairs at once; k_wkv_chunk_scan then carries S through
 // the chunks, two 16-deep contractions per chunk instead of 16 dependent
 // rank-1 steps.  Padding tokens (past T) have d = 1 and zero vectors, so they
-// change nothing.
+// change nothing: their columns of Z and rows of K2 are exactly zero, so
+// whatever value they carry is multiplied by zero, and a chunk of padding
+// only is the identity (e^{l_L} = 1, every other entry 0).  The chunk count
+// is padded to a multiple of 3 (the scan's unroll) with such chunks.
 constexpr int CH = 16;
+__host__ __device__ inline int chunk_count(int T) { return ((T + CH - 1) / CH + 2) / 3 * 3; }
 // per (chunk, head) record, floats:
 //   A2 [16][64] | Q [16][64] | btil^T [64][16] | K2^T [64][16] | Z [16][16] | e^{l_L} [64]
 enum : int { R_A2 = 0, R_Q = 1024, R_BT = 2048, R_K2T = 3072, R_Z = 4096, R_EL = 4352, REC = 4416 };
@@ -736,56 +740,64 @@ __global__ __launch_bounds__(256) void k_wkv_chunk_prep(WkvArgs a) {
 //   readouts  P^T = [A2; Q] S^T   (each wave sums its 16 key columns; the four
 //                                  partial tiles meet through LDS)
 //   update    S^T <- diag(e^{l_L}) S^T + btil^T (S A2^T)^T + K2^T V
-// Chunk records are staged through a three-deep LDS ring, loaded two chunks
-// ahead, so one barrier per chunk orders the ring, the partial sums and the
-// readouts.
+// The chunk records were written just before (too many for L2), so each is
+// loaded three chunks ahead into one of three register sets and staged
+// through a three-slot LDS ring; the chunk loop is unrolled by three so every
+// ring and register index is static, and one barrier per chunk orders the
+// ring, the partial sums and the readouts.
 struct ChunkBuf {
   float rec[REC];
   float vt[16][20];   // V^T of the workgroup's 16 value rows (row stride 20 keeps float4 alignment)
 };
+struct ChunkRegs {
+  floatx4 r[5];
+  float v;
+};
+template <int U> struct RingSlot { static constexpr int value = U; };
 
 __global__ __launch_bounds__(256) void k_wkv_chunk_scan(WkvArgs a) {
   __shared__ __attribute__((aligned(16))) ChunkBuf cb[3];
-  __shared__ floatx4 xch[2][4][2][64];
+  __shared__ floatx4 xch[3][4][2][64];
   const int h = blockIdx.x >> 2, q = blockIdx.x & 3;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int C = a.C, T = a.B, H = a.H;
-  const int nc = (T + CH - 1) / CH;
+  const int nc = chunk_count(T);
   float* S = a.pool + (long)a.seq_slot * a.slot_stride + a.layer_off + 2L * C + (long)h * 4096 +
              (16 * q + c16) * 64 + 16 * w + 4 * g;
   floatx4 st = ldf4(S);
 
-  floatx4 rr[5];
-  float rv = 0.f;
-  auto load = [&](int c) {
+  // loads are unconditional (chunks past the end repeat the last record and
+  // are never read; values past T are clamped to token T - 1 and only meet
+  // zeros), so the wait before each staging store is exact
+  ChunkRegs rs[3];
+  auto load = [&](ChunkRegs& r, int c) {
+    c = c < nc ? c : nc - 1;
     const float* rec = a.q_rec + ((long)c * H + h) * REC;
 #pragma unroll
     for (int p = 0; p < 5; ++p) {
       const int e = p * 256 + tid;
-      rr[p] = ldf4(rec + 4 * (e < REC / 4 ? e : REC / 4 - 1));
+      r.r[p] = ldf4(rec + 4 * (e < REC / 4 ? e : REC / 4 - 1));
     }
     const int tk = c * CH + (tid >> 4);
-    const float v = a.q_v[(long)(tk < T ? tk : T - 1) * C + h * 64 + 16 * q + (tid & 15)];
-    rv = tk < T ? v : 0.f;
+    r.v = a.q_v[(long)(tk < T ? tk : T - 1) * C + h * 64 + 16 * q + (tid & 15)];
   };
-  auto store = [&](int b) {
+  auto store = [&](const ChunkRegs& r, ChunkBuf& b) {
 #pragma unroll
     for (int p = 0; p < 5; ++p) {
       const int e = p * 256 + tid;
-      if (e < REC / 4) stf4(&cb[b].rec[4 * e], rr[p]);
+      if (e < REC / 4) stf4(&b.rec[4 * e], r.r[p]);
     }
-    cb[b].vt[tid & 15][tid >> 4] = rv;
+    b.vt[tid & 15][tid >> 4] = r.v;
   };
 
-  load(0);
-  store(0);
-  if (nc > 1) load(1);
-  __syncthreads();
-  for (int c = 0; c < nc; ++c) {
-    const ChunkBuf& B = cb[c % 3];
+  // chunk c, held in ring slot U = c % 3
+  auto chunk = [&](int c, auto slot) {
+    constexpr int U = decltype(slot)::value;
+    ChunkBuf& B = cb[U];
     // this wave's share of the readout sums: 16 key columns of S A2^T and
-    // S Q^T, plus key slice w of Z V
-    floatx4 pa = {0.f, 0.f, 0.f, 0.f}, pq = pa;
+    // S Q^T, plus key slice w of Z V; and the update's V^T K2 term, which does
+    // not involve S
+    floatx4 pa = {0.f, 0.f, 0.f, 0.f}, pq = pa, kv = pa;
     {
       const floatx4 av = ldf4(&B.rec[R_A2 + c16 * 64 + 16 * w + 4 * g]);
       const floatx4 qv = ldf4(&B.rec[R_Q + c16 * 64 + 16 * w + 4 * g]);
@@ -795,19 +807,23 @@ __global__ __launch_bounds__(256) void k_wkv_chunk_scan(WkvArgs a) {
         pq = mfma4(qv[kk], st[kk], pq);
       }
       pq = mfma4(B.rec[R_Z + c16 * CH + 4 * w + g], B.vt[c16][4 * w + g], pq);
+      const floatx4 k2 = ldf4(&B.rec[R_K2T + (16 * w + c16) * CH + 4 * g]);
+      const floatx4 vq = ldf4(&B.vt[c16][4 * g]);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) kv = mfma4(k2[kk], vq[kk], kv);
     }
-    xch[c & 1][w][0][lane] = pa;
-    xch[c & 1][w][1][lane] = pq;
-    if (c + 1 < nc) store((c + 1) % 3);
+    xch[U][w][0][lane] = pa;
+    xch[U][w][1][lane] = pq;
+    store(rs[(U + 1) % 3], cb[(U + 1) % 3]);   // chunk c + 1
     __syncthreads();
-    if (c + 2 < nc) load(c + 2);
+    load(rs[U], c + 3);
     // the four waves' partial tiles, added in wave order: lane l, component i
     // holds (S A2^T)[16 q + l % 16][4 (l / 16) + i] and likewise the readout
-    floatx4 sa = xch[c & 1][0][0][lane], sq = xch[c & 1][0][1][lane];
+    floatx4 sa = xch[U][0][0][lane], sq = xch[U][0][1][lane];
 #pragma unroll
     for (int v = 1; v < 4; ++v) {
-      sa += xch[c & 1][v][0][lane];
-      sq += xch[c & 1][v][1][lane];
+      sa += xch[U][v][0][lane];
+      sq += xch[U][v][1][lane];
     }
     {
       const int ty = c * CH + 4 * g + w;   // wave w stores component w
@@ -816,13 +832,23 @@ __global__ __launch_bounds__(256) void k_wkv_chunk_scan(WkvArgs a) {
     }
     const floatx4 el = ldf4(&B.rec[R_EL + 16 * w + 4 * g]);
     const floatx4 bq = ldf4(&B.rec[R_BT + (16 * w + c16) * CH + 4 * g]);
-    const floatx4 k2 = ldf4(&B.rec[R_K2T + (16 * w + c16) * CH + 4 * g]);
-    const floatx4 vq = ldf4(&B.vt[c16][4 * g]);
-    st *= el;
+    st = st * el + kv;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) st = mfma4(bq[kk], sa[kk], st);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) st = mfma4(k2[kk], vq[kk], st);
+  };
+
+  load(rs[0], 0);
+  load(rs[1], 1);
+  load(rs[2], 2);
+  store(rs[0], cb[0]);
+  // drain the prologue's loads (issued in an order the loop does not repeat),
+  // so the waits inside the loop follow the loop's own order
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __syncthreads();
+  for (int c = 0; c < nc; c += 3) {
+    chunk(c, RingSlot<0>{});
+    chunk(c + 1, RingSlot<1>{});
+    chunk(c + 2, RingSlot<2>{});
   }
   stf4(S, st);
 }
@@ -864,7 +890,7 @@ hipError_t launch_wkv_scan(const WkvArgs& a, hipStream_t st) {
 }
 hipError_t launch_wkv_chunk_prep(const WkvArgs& a, hipStream_t st) {
   if (!a.q_rec || a.B < 1) return hipErrorInvalidValue;
-  const int nc = (a.B + CH - 1) / CH;
+  const int nc = chunk_count(a.B);
   hipLaunchKernelGGL(k_wkv_chunk_prep, dim3(nc * a.H), dim3(256), 0, st, a);
   return hipGetLastError();
 }
@@ -873,7 +899,7 @@ hipError_t launch_wkv_chunk_scan(const WkvArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_wkv_chunk_scan, dim3(a.H * 4), dim3(256), 0, st, a);
   return hipGetLastError();
 }
-int64_t wkv_chunk_rec_floats(int T, int H) { return (int64_t)((T + CH - 1) / CH) * H * REC; }
+int64_t wkv_chunk_rec_floats(int T, int H) { return (int64_t)chunk_count(T) * H * REC; }
 hipError_t launch_wkv_post(const WkvArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_wkv_post, dim3(a.B * a.H), dim3(64), 0, st, a);
   return hipGetLastError();
