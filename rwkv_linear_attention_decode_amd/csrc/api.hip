@@ -187,7 +187,7 @@ Ws ws_layout(const Dims& d, int R, char* base) {
   w.q_kt = (float*)take(r * C * 4);
   w.q_v = (float*)take(r * C * 4);
   w.q_g = (float*)take(r * C * 4);
-  w.q_y = (float*)take(r * C * 4);
+  w.q_y = (float*)take((uint64_t)wkv_chunk_rows(R) * C * 4);   // padded rows for the chunked scan
   w.q_bonus = (float*)take(r * d.H * 4);
   w.q_brk = (float*)take(r * d.H * 2 * 4);
   w.q_rec = (float*)take((uint64_t)wkv_chunk_rec_floats(R, d.H) * 4);

@@ -746,8 +746,8 @@ __global__ __launch_bounds__(256) void k_wkv_chunk_prep(WkvArgs a) {
 // ring and register index is static, and one barrier per chunk orders the
 // ring, the partial sums and the readouts.
 struct ChunkBuf {
-  float rec[REC];
-  float vt[16][20];   // V^T of the workgroup's 16 value rows (row stride 20 keeps float4 alignment)
+  float rec[5 * 256 * 4];   // a record (REC floats) in the slots of five float4 per thread
+  float vt[16][20];         // V^T of the workgroup's 16 value rows (row stride 20 keeps float4 alignment)
 };
 struct ChunkRegs {
   floatx4 r[5];
@@ -758,7 +758,11 @@ template <int U> struct RingSlot { static constexpr int value = U; };
 __global__ __launch_bounds__(256) void k_wkv_chunk_scan(WkvArgs a) {
   __shared__ __attribute__((aligned(16))) ChunkBuf cb[3];
   __shared__ floatx4 xch[3][4][2][64];
-  const int h = blockIdx.x >> 2, q = blockIdx.x & 3;
+  // the four workgroups of a head read the same records: give them one XCD
+  // (workgroups are dealt to the eight XCDs round robin) when 8 divides the grid
+  const int nwg = 4 * a.H;
+  const int lin = nwg % 8 ? (int)blockIdx.x : (blockIdx.x & 7) * (nwg / 8) + (blockIdx.x >> 3);
+  const int h = lin >> 2, q = lin & 3;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int C = a.C, T = a.B, H = a.H;
   const int nc = chunk_count(T);
@@ -775,7 +779,7 @@ __global__ __launch_bounds__(256) void k_wkv_chunk_scan(WkvArgs a) {
     const float* rec = a.q_rec + ((long)c * H + h) * REC;
 #pragma unroll
     for (int p = 0; p < 5; ++p) {
-      const int e = p * 256 + tid;
+      const int e = p * 256 + tid;   // slots past the record repeat its last float4
       r.r[p] = ldf4(rec + 4 * (e < REC / 4 ? e : REC / 4 - 1));
     }
     const int tk = c * CH + (tid >> 4);
@@ -783,10 +787,7 @@ __global__ __launch_bounds__(256) void k_wkv_chunk_scan(WkvArgs a) {
   };
   auto store = [&](const ChunkRegs& r, ChunkBuf& b) {
 #pragma unroll
-    for (int p = 0; p < 5; ++p) {
-      const int e = p * 256 + tid;
-      if (e < REC / 4) stf4(&b.rec[4 * e], r.r[p]);
-    }
+    for (int p = 0; p < 5; ++p) stf4(&b.rec[4 * (p * 256 + tid)], r.r[p]);
     b.vt[tid & 15][tid >> 4] = r.v;
   };
 
@@ -826,9 +827,9 @@ __global__ __launch_bounds__(256) void k_wkv_chunk_scan(WkvArgs a) {
       sq += xch[U][v][1][lane];
     }
     {
-      const int ty = c * CH + 4 * g + w;   // wave w stores component w
-      const float y = w == 0 ? sq[0] : w == 1 ? sq[1] : w == 2 ? sq[2] : sq[3];
-      if (ty < T) a.q_y[(long)ty * C + h * 64 + 16 * q + c16] = y;
+      // wave w stores component w; rows past T land in q_y's padding rows
+      const int ty = c * CH + 4 * g + w;
+      a.q_y[(long)ty * C + h * 64 + 16 * q + c16] = sq[__builtin_amdgcn_readfirstlane(w)];
     }
     const floatx4 el = ldf4(&B.rec[R_EL + 16 * w + 4 * g]);
     const floatx4 bq = ldf4(&B.rec[R_BT + (16 * w + c16) * CH + 4 * g]);
@@ -900,6 +901,7 @@ hipError_t launch_wkv_chunk_scan(const WkvArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 int64_t wkv_chunk_rec_floats(int T, int H) { return (int64_t)chunk_count(T) * H * REC; }
+int wkv_chunk_rows(int T) { return chunk_count(T) * CH; }
 hipError_t launch_wkv_post(const WkvArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_wkv_post, dim3(a.B * a.H), dim3(64), 0, st, a);
   return hipGetLastError();

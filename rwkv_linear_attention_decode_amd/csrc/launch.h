@@ -214,7 +214,7 @@ struct WkvArgs {
   float* q_g;
   float* q_bonus;          // [T][H]
   float* q_brk;            // [T][H][2]: b.r and kt.r of each token and head (prefill scan)
-  float* q_y;              // raw readout
+  float* q_y;              // raw readout ([wkv_chunk_rows(T)][C] for the chunked scan)
   float* q_rec;            // chunked scan: per (16-token chunk, head) records (wkv_chunk_rec_floats)
 };
 hipError_t launch_wkv_decode(const WkvArgs& a, hipStream_t st);
@@ -227,3 +227,6 @@ hipError_t launch_wkv_post(const WkvArgs& a, hipStream_t st);   // sequence: Gro
 hipError_t launch_wkv_chunk_prep(const WkvArgs& a, hipStream_t st);
 hipError_t launch_wkv_chunk_scan(const WkvArgs& a, hipStream_t st);
 int64_t wkv_chunk_rec_floats(int T, int H);
+// Rows of q_y the chunked scan writes (T rounded up to whole unrolled chunks; rows past T
+// are padding).
+int wkv_chunk_rows(int T);
