@@ -624,11 +624,11 @@ int enqueue_prefill_chunk(rwkv7_model* m, float* pool, int64_t n_slots, int slot
     WkvArgs wa = wkv_args(m, l, pool, n_slots, w, T, true);
     wa.seq_slot = slot;
     wa.lo = w.lo;
-    RUN(RWKV7_K_WKV, "wkv_prep", launch_wkv_prep(wa, st));
     if (m->opt_prefill_scan == 2 || (m->opt_prefill_scan == 0 && T >= PREFILL_CHUNKED_MIN_T)) {
       RUN(RWKV7_K_WKV, "wkv_chunk_prep", launch_wkv_chunk_prep(wa, st));
       RUN(RWKV7_K_WKV, "wkv_chunk_scan", launch_wkv_chunk_scan(wa, st));
     } else {
+      RUN(RWKV7_K_WKV, "wkv_prep", launch_wkv_prep(wa, st));
       RUN(RWKV7_K_WKV, "wkv_scan", launch_wkv_scan(wa, st));
     }
     RUN(RWKV7_K_WKV, "wkv_post", launch_wkv_post(wa, st));

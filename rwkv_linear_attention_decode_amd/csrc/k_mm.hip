@@ -694,6 +694,8 @@ static void mm_launch(int ks, int pipe, dim3 grid, hipStream_t st, const ProjArg
 static bool mm_cfg_ok(int tm, int tn, int ks, int pipe) {
   if (pipe < 0 || pipe > 4) return false;
   if (pipe == 4) {   // eight waves: N blocks split over four wave columns
+    if (tn == 8)      // 256-wide tiles, 64-deep stages (three of them fill up to 144 KB of LDS)
+      return (tm == 2 || tm == 4) && ks == 64;
     if (!((tm == 2 || tm == 4) && (tn == 2 || tn == 4))) return false;
     if (ks == 32) return (tm + tn) % 4 == 0;
     return (ks == 64 || ks == 128) && mm_dma_lds_bytes(tm, tn, ks) <= 98304;
@@ -736,7 +738,7 @@ static MmPlan mm_choose(const ProjArgs& a, int total_rows) {
       if (K >= 16384) return M > 64 && M <= 256 ? MmPlan{4, 4, 64, 4, 3} : MmPlan{4, 4, 64, 0, 6};
       if (M <= 64) return {2, 2, 64, 2, 0};
       if (M <= 256) return {4, 4, 64, 4, 6};
-      return M <= 1024 ? MmPlan{2, 4, 64, 3, 3} : MmPlan{4, 4, 64, 4, 0};
+      return M <= 1024 ? MmPlan{2, 4, 64, 3, 3} : MmPlan{4, 8, 64, 4, 0};
     }
     if (M <= 64) return {1, 2, 128, 0, 0};
     return M <= 256 ? MmPlan{2, 2, 64, 4, 0} : MmPlan{2, 4, 64, 4, 0};
@@ -784,7 +786,7 @@ hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int 
   if (pipe >= 3)   // the DMA loops need whole stages: otherwise a register-staged loop
     for (int i = 0; i < a.nseg; ++i)
       if ((a.seg[i].W ? a.seg[i].K : a.K) % ks != 0) {
-        if (tn == 5) tn = 4;   // 160-wide tiles exist for the DMA loop only
+        if (tn == 5 || tn == 8) tn = 4;   // 160- and 256-wide tiles exist for the DMA loops only
         pipe = mm_cfg_ok(tm, tn, ks, 2) ? 2 : 0;
       }
   if (!mm_cfg_ok(tm, tn, ks, pipe)) return hipErrorInvalidValue;
@@ -798,6 +800,8 @@ hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int 
     case 24: mm_launch<2, 4>(ks, pipe, grid, st, a); break;
     case 42: mm_launch<4, 2>(ks, pipe, grid, st, a); break;
     case 25: mm_launch_dma<2, 5, 4>(ks, grid, st, a); break;   // loop 3, ks 64 only
+    case 28: hipLaunchKernelGGL((k_mm_dma<2, 8, 64, 8>), grid, dim3(512), 0, st, a); break;   // loop 4
+    case 48: hipLaunchKernelGGL((k_mm_dma<4, 8, 64, 8>), grid, dim3(512), 0, st, a); break;   // loop 4
     default: mm_launch<4, 4>(ks, pipe, grid, st, a); break;
   }
   hipError_t e = hipGetLastError();
@@ -846,11 +850,11 @@ const char* gemm_kernel_name(int M, int N, int K) {
   int tn = p.tn;
   int ep = pipe;   // as launch_gemm_cfg falls back
   if (pipe >= 3 && K % ks != 0) {
-    if (tn == 5) tn = 4;
+    if (tn == 5 || tn == 8) tn = 4;
     ep = mm_cfg_ok(tm, tn, ks, 2) ? 2 : 0;
   }
-  static char names[4][3][3][5][32];
-  char* s = names[tm == 1 ? 0 : tm == 2 ? 1 : tm == 4 ? 2 : 3][tn == 2 ? 0 : tn == 4 ? 1 : 2]
+  static char names[4][4][3][5][32];
+  char* s = names[tm == 1 ? 0 : tm == 2 ? 1 : tm == 4 ? 2 : 3][tn == 2 ? 0 : tn == 4 ? 1 : tn == 5 ? 2 : 3]
                  [ks == 32 ? 0 : ks == 64 ? 1 : 2][ep];
   if (!s[0]) {
     if (ep >= 3)

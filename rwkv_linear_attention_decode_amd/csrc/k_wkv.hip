@@ -597,7 +597,12 @@ struct ChunkPrepLds {
 };
 
 // Grid: n_chunks * H workgroups of 256 threads; thread (t, j4) = (tid / 16,
-// 4 (tid % 16)) owns token t of the chunk and key columns j4..j4+3.
+// 4 (tid % 16)) owns token t of the chunk and key columns j4..j4+3.  The
+// per-token head vectors are formed here from the projections and the
+// precomputed adapter outputs (as in the decode prologue: the key normalised
+// per head, the in-context rate folded into k~ and b, the value residual),
+// the 16 lanes of a token closing the per-head sums; v, the gate and the
+// bonus go to q_v, q_g and q_bonus for the scan and the GroupNorm kernel.
 __global__ __launch_bounds__(256) void k_wkv_chunk_prep(WkvArgs a) {
   __shared__ __attribute__((aligned(16))) ChunkPrepLds L;
   const int H = a.H, C = a.C, T = a.B;
@@ -607,9 +612,37 @@ __global__ __launch_bounds__(256) void k_wkv_chunk_prep(WkvArgs a) {
   const int tk = c * CH + t;
   const bool live = tk < T;
   const int tc = live ? tk : T - 1;   // clamped: every load is issued
-  const long o = (long)tc * C + h * 64 + j4;
-  floatx4 av = ldf4(a.q_a + o), bv = ldf4(a.q_b + o), kv = ldf4(a.q_kt + o), dv = ldf4(a.q_d + o);
-  floatx4 rv = ldf4(a.rkv + (long)tc * 3 * C + h * 64 + j4);
+  const int cc = h * 64 + j4;
+  floatx4 av, bv, kv, dv, rv;
+  {
+    const long ro = (long)tc * 3 * C + cc, lo = (long)tc * 4 * C + cc, xo = (long)tc * C + cc;
+    rv = ldf4(a.rkv + ro);
+    const floatx4 kraw = ldf4(a.rkv + ro + C);
+    floatx4 vv = ldf4(a.rkv + ro + 2 * C);
+    dv = ldf4(a.lo + lo);
+    const floatx4 al = ldf4(a.lo + lo + C), vg = ldf4(a.lo + lo + 2 * C), gg = ldf4(a.lo + lo + 3 * C);
+    const floatx4 kk = ldf4(a.k_k + cc), ka = ldf4(a.k_a + cc), rk = ldf4(a.r_k + cc);
+    const floatx4 vf = ldf4(a.vfirst + xo);   // layer 0 writes it below instead
+    const floatx4 kap = kraw * kk;
+    const float nrm = sqrtf(sum16(kap[0] * kap[0] + kap[1] * kap[1] + kap[2] * kap[2] + kap[3] * kap[3]));
+    const float den = fmaxf(nrm, 1e-12f);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float kh = kap[e] / den;
+      kv[e] = kraw[e] * (1.0f + (al[e] - 1.0f) * ka[e]);
+      av[e] = -kh;
+      bv[e] = kh * al[e];
+    }
+    if (a.layer != 0) vv = vv + (vf - vv) * vg;
+    const float bon = sum16(rv[0] * kv[0] * rk[0] + rv[1] * kv[1] * rk[1] + rv[2] * kv[2] * rk[2] +
+                            rv[3] * kv[3] * rk[3]);
+    if (live) {
+      if (a.layer == 0) stf4(a.vfirst + xo, vv);
+      stf4(a.q_v + xo, vv);
+      stf4(a.q_g + xo, gg);
+      if ((tid & 15) == 0) a.q_bonus[(long)tk * H + h] = bon;
+    }
+  }
   if (!live) {
     av = bv = kv = rv = floatx4{0.f, 0.f, 0.f, 0.f};
     dv = floatx4{1.f, 1.f, 1.f, 1.f};
@@ -890,7 +923,7 @@ hipError_t launch_wkv_scan(const WkvArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 hipError_t launch_wkv_chunk_prep(const WkvArgs& a, hipStream_t st) {
-  if (!a.q_rec || a.B < 1) return hipErrorInvalidValue;
+  if (!a.q_rec || !a.lo || a.B < 1) return hipErrorInvalidValue;
   const int nc = chunk_count(a.B);
   hipLaunchKernelGGL(k_wkv_chunk_prep, dim3(nc * a.H), dim3(256), 0, st, a);
   return hipGetLastError();

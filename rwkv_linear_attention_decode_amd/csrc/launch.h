@@ -221,9 +221,10 @@ hipError_t launch_wkv_decode(const WkvArgs& a, hipStream_t st);
 hipError_t launch_wkv_prep(const WkvArgs& a, hipStream_t st);   // sequence: per (t, h)
 hipError_t launch_wkv_scan(const WkvArgs& a, hipStream_t st);   // sequence: serial in t
 hipError_t launch_wkv_post(const WkvArgs& a, hipStream_t st);   // sequence: GroupNorm + bonus + gate
-// Chunked form of the sequence scan (same q_y and final state as launch_wkv_scan, up to
-// rounding): per-chunk matrices for every (16-token chunk, head), then the state carried
-// chunk to chunk.  Reads q_a, q_b, q_kt, q_d, q_v and r; q_rec needs wkv_chunk_rec_floats.
+// Chunked form of launch_wkv_prep + launch_wkv_scan (same q_v, q_g, q_bonus, q_y and
+// final state, up to rounding): the head vectors and per-chunk matrices for every (16-token
+// chunk, head), then the state carried chunk to chunk.  Needs the precomputed adapter
+// outputs (lo); q_rec needs wkv_chunk_rec_floats, q_y wkv_chunk_rows rows.
 hipError_t launch_wkv_chunk_prep(const WkvArgs& a, hipStream_t st);
 hipError_t launch_wkv_chunk_scan(const WkvArgs& a, hipStream_t st);
 int64_t wkv_chunk_rec_floats(int T, int H);

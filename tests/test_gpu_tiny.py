@@ -167,7 +167,7 @@ GEMM_PLAN_KEYS = (8, 9, 10, 11, 12, 13)   # OPT_GEMM_PLAN_PROJ_IN .. _HEAD
     (2, 2, 64, 3, 0), (4, 4, 64, 3, 0), (1, 2, 128, 3, 0), (2, 4, 32, 3, 2),
     (4, 2, 64, 3, 1), (1, 4, 64, 3, 3), (2, 2, 128, 3, 0), (2, 5, 64, 3, 0), (2, 5, 64, 3, 2),
     (2, 2, 64, 4, 0), (4, 4, 64, 4, 0), (2, 4, 64, 4, 2), (4, 2, 64, 4, 1), (2, 2, 32, 4, 0),
-    (4, 4, 32, 4, 3), (2, 2, 128, 4, 0)])
+    (4, 4, 32, 4, 3), (2, 2, 128, 4, 0), (4, 8, 64, 4, 0), (2, 8, 64, 4, 2)])
 def test_gemm_plans_match_oracle(model, W, R, tm, tn, ks, pipe, split):
     """Every MFMA projection (prefill and an 8-row step) forced onto one tile
     plan: tile shapes, stage depths, the five K loops and K splits, with K
@@ -221,7 +221,8 @@ def test_gemm_plan_option_validation(model, R):
                 R.gemm_plan_code(4, 4, 128), R.gemm_plan_code(1, 4, 64, 4), R.gemm_plan_code(2, 4, 128, 3),
                 R.gemm_plan_code(1, 2, 32, 3), R.gemm_plan_code(2, 5, 32, 3), R.gemm_plan_code(2, 5, 64, 2),
                 R.gemm_plan_code(4, 5, 64, 3), R.gemm_plan_code(1, 2, 64, 4), R.gemm_plan_code(2, 4, 32, 4),
-                R.gemm_plan_code(2, 4, 128, 4), R.gemm_plan_code(2, 2, 64, 5), -5, 10 ** 8):
+                R.gemm_plan_code(2, 4, 128, 4), R.gemm_plan_code(2, 2, 64, 5), R.gemm_plan_code(4, 8, 64, 3),
+                R.gemm_plan_code(4, 8, 128, 4), R.gemm_plan_code(1, 8, 64, 4), -5, 10 ** 8):
         with pytest.raises(R.RWKV7Error):
             model.set_option(8, bad)
     model.set_option(8, 0)
@@ -234,11 +235,14 @@ def test_prefill_equals_steps_on_gpu(model, R):
     logits = torch.empty(1, S.vocab, device="cuda")
     for t in toks:
         model.decode_step(dev([3]), dev([int(t)]), logits)
-    model.set_option(R.OPT_PREFILL_CHUNK, 16)   # 3 chunks: 16 + 16 + 5
+    # 3 chunks: 16 + 16 + 5, with the same (chunked) WKV scan as the one 37-token chunk
+    model.set_option(R.OPT_PREFILL_CHUNK, 16)
+    model.set_option(R.OPT_PREFILL_SCAN, 2)
     try:
         model.prefill(4, dev(toks))
     finally:
         model.set_option(R.OPT_PREFILL_CHUNK, 2048)
+        model.set_option(R.OPT_PREFILL_SCAN, 0)
     a, b, c = gstate(model, 2), gstate(model, 3), gstate(model, 4)
     assert rel(a, b) <= TOL
     assert rel(c, a) <= 1e-5
