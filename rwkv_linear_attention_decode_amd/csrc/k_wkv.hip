@@ -48,17 +48,19 @@ RW_DEV void wkv_prologue(const WkvArgs& a, int b, int h, HeadVecs& hv, float* s_
   const int c = h * 64 + i;
   const int e1 = a.Dw, e2 = a.Dw + a.Da, e3 = a.Dw + a.Da + a.Dv;
 
+  // every load unconditional and its address picked by selects, so the
+  // NCHK loads issue back to back (layer 0 loads its unused value-gate rows
+  // too: they are packed like every layer's, and its gate is not applied)
   u32x4 wch[NCHK];
 #pragma unroll
   for (int q = 0; q < NCHK; ++q) {
     const int e0 = (qd * NCHK + q) * 8;
-    const half_t* W;
-    if (e0 < e1) W = a.w2 + (long)c * a.Dw + e0;
-    else if (e0 < e2) W = a.a2 + (long)c * a.Da + (e0 - e1);
-    else if (e0 < e3) W = a.v2 + (long)c * a.Dv + (e0 - e2);
-    else W = a.g2 + (long)c * a.Dg + (e0 - e3);
-    const bool skip = (e0 >= e2 && e0 < e3 && a.layer == 0);  // layer 0 has no value mix
-    wch[q] = skip ? u32x4{0u, 0u, 0u, 0u} : ld16(W);
+    const half_t* pw = a.w2 + (long)c * a.Dw + e0;
+    const half_t* pa = a.a2 + (long)c * a.Da + (e0 - e1);
+    const half_t* pv = a.v2 + (long)c * a.Dv + (e0 - e2);
+    const half_t* pg = a.g2 + (long)c * a.Dg + (e0 - e3);
+    const half_t* W = e0 < e1 ? pw : e0 < e2 ? pa : e0 < e3 ? pv : pg;
+    wch[q] = ld16(W);
   }
   // per-channel vectors for wave 0's key step
   float k_k = 0.f, k_a = 0.f, r_k = 0.f, vf = 0.f;
@@ -220,9 +222,10 @@ __global__ __launch_bounds__(256) void k_wkv_decode(WkvArgs a) {
     gw = a.lnx_w[h * 64 + t];
     gb = a.lnx_b[h * 64 + t];
   }
-  // commit the time-mix shift computed by the fused input projection
-  if (a.u_att && ok && t >= 64 && t < 128)
-    base[h * 64 + (t - 64)] = a.u_att[(long)b * a.C + h * 64 + (t - 64)];
+  // the time-mix shift computed by the fused input projection: loaded now,
+  // committed at the end (a store here would wait for every load above)
+  const bool commit = a.u_att && ok && t >= 64 && t < 128;
+  const float u_new = commit ? a.u_att[(long)b * a.C + h * 64 + (t - 64)] : 0.f;
   if constexpr (NCHK == 0)
     wkv_prologue_lean(a, b, h, hv);
   else
@@ -267,6 +270,7 @@ __global__ __launch_bounds__(256) void k_wkv_decode(WkvArgs a) {
     else
       ((float*)a.yout)[off] = o;
   }
+  if (commit) base[h * 64 + (t - 64)] = u_new;
 }
 
 // Many rows with precomputed adapter outputs: one wave per (row, head), four
