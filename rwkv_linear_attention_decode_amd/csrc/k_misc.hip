@@ -561,18 +561,24 @@ __global__ __launch_bounds__(1024) void k_cmix_sparse(CmixArgs a) {
   }
 }
 
-// x += the value partial sums of the fused key projection, in workgroup
-// order: thread t sums 8 columns over workgroups rg, rg + 256, ... (rg =
-// t / 4), then the 256 row groups meet in the same fixed-order reduction as
-// above.  Workgroup 0 also writes the debug active list when asked.
+// x += the value partial sums of the fused key projection.  Each workgroup
+// owns FOLD_COLS columns: thread t sums 8 of them over partials rg, rg + R,
+// ... (R = 1024 / (FOLD_COLS / 8) row groups, rg = t / (FOLD_COLS / 8)),
+// then lanes and waves meet in a fixed order, so the result does not depend
+// on timing.  32-column slices read whole 128-byte lines of each partial row
+// (8-column slices, with four times the workgroups, measured slower).
+// Workgroup 0 also writes the debug active list when asked.
+constexpr int FOLD_COLS = 32;
 template <int B>
 __global__ __launch_bounds__(1024) void k_cmix_fold(CmixFoldArgs a) {
-  __shared__ float s_red[16][B][CMIX_COLS];
+  constexpr int CPT = FOLD_COLS / 8;   // threads per row group
+  constexpr int RG = 1024 / CPT;       // row groups
+  __shared__ float s_red[16][B][FOLD_COLS];
   __shared__ unsigned short s_idx[CMIX_MAXF];
   __shared__ int s_wcnt[4];
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  const int nsl = a.C / CMIX_COLS;
+  const int nsl = a.C / FOLD_COLS;
   const int per_xcd = (nsl + 7) / 8;
   const int slice = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (a.dbg_idx && blockIdx.x == 0) {
@@ -581,20 +587,20 @@ __global__ __launch_bounds__(1024) void k_cmix_fold(CmixFoldArgs a) {
     if (t == 0) *a.dbg_cnt = total;
   }
   if (slice >= nsl) return;
-  const int rg = t >> 2;
-  const int c8 = (t & 3) * 8;
-  const int cb = slice * CMIX_COLS + c8;
+  const int rg = t / CPT;
+  const int c8 = (t % CPT) * 8;
+  const int cb = slice * FOLD_COLS + c8;
   float acc[B][8];
 #pragma unroll
   for (int b = 0; b < B; ++b)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[b][e] = 0.f;
   constexpr int U = 4;
-  for (int w0 = rg; w0 < a.nwg; w0 += 256 * U) {
+  for (int w0 = rg; w0 < a.nwg; w0 += RG * U) {
     floatx4 v[U][B][2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int w = w0 + 256 * u;
+      const int w = w0 + RG * u;
 #pragma unroll
       for (int b = 0; b < B; ++b) {
         const float* p = a.part + ((long)w * B + b) * a.C + cb;
@@ -617,19 +623,17 @@ __global__ __launch_bounds__(1024) void k_cmix_fold(CmixFoldArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float v = acc[b][e];
-      v += __shfl_xor(v, 4);
-      v += __shfl_xor(v, 8);
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      if (lane < 4) s_red[wave][b][c8 + e] = v;
+#pragma unroll
+      for (int o = CPT; o < 64; o <<= 1) v += __shfl_xor(v, o);
+      if (lane < CPT) s_red[wave][b][c8 + e] = v;
     }
   __syncthreads();
-  if (t < B * CMIX_COLS) {
-    const int b = t / CMIX_COLS;
-    const int col = slice * CMIX_COLS + t % CMIX_COLS;
+  if (t < B * FOLD_COLS) {
+    const int b = t / FOLD_COLS;
+    const int col = slice * FOLD_COLS + t % FOLD_COLS;
     float sum = 0.f;
 #pragma unroll
-    for (int w = 0; w < 16; ++w) sum += s_red[w][b][t % CMIX_COLS];
+    for (int w = 0; w < 16; ++w) sum += s_red[w][b][t % FOLD_COLS];
     a.x[(long)b * a.C + col] += sum;
     if (a.u_ffn) {
       const int slot = a.slots[b];
@@ -640,9 +644,9 @@ __global__ __launch_bounds__(1024) void k_cmix_fold(CmixFoldArgs a) {
 }
 
 hipError_t launch_cmix_fold(const CmixFoldArgs& a, hipStream_t st) {
-  if (a.F > CMIX_MAXF || a.F % 1024 || a.C % CMIX_COLS || a.B < 1 || a.B > 2 || a.nwg < 1)
+  if (a.F > CMIX_MAXF || a.F % 1024 || a.C % FOLD_COLS || a.B < 1 || a.B > 2 || a.nwg < 1)
     return hipErrorInvalidValue;
-  const dim3 grid((a.C / CMIX_COLS + 7) / 8 * 8);
+  const dim3 grid((a.C / FOLD_COLS + 7) / 8 * 8);
   if (a.B == 1)
     hipLaunchKernelGGL(k_cmix_fold<1>, grid, dim3(1024), 0, st, a);
   else
