@@ -618,13 +618,19 @@ int enqueue_prefill_chunk(rwkv7_model* m, float* pool, int64_t n_slots, int slot
     proj_in_args(d, q, w, T, true, pa);
     RUN(RWKV7_K_PROJ_IN, "proj_in", proj(false, pa, d.Nin, w, st, m->opt_plan[0]));
 
-    ProjArgs pl;
-    lora_args(d, q, w, T, pl);
-    RUN(RWKV7_K_PROJ_IN, "adapters", proj(false, pl, 4 * C, w, st, m->opt_plan[1]));
     WkvArgs wa = wkv_args(m, l, pool, n_slots, w, T, true);
     wa.seq_slot = slot;
-    wa.lo = w.lo;
-    if (m->opt_prefill_scan == 2 || (m->opt_prefill_scan == 0 && T >= PREFILL_CHUNKED_MIN_T)) {
+    const bool chunked = m->opt_prefill_scan == 2 || (m->opt_prefill_scan == 0 && T >= PREFILL_CHUNKED_MIN_T);
+    // the chunked scan computes the adapters' second stage itself when the ranks allow
+    if (chunked && wkv_chunk_adapters_ok(wa)) {
+      wa.lo = nullptr;
+    } else {
+      ProjArgs pl;
+      lora_args(d, q, w, T, pl);
+      RUN(RWKV7_K_PROJ_IN, "adapters", proj(false, pl, 4 * C, w, st, m->opt_plan[1]));
+      wa.lo = w.lo;
+    }
+    if (chunked) {
       RUN(RWKV7_K_WKV, "wkv_chunk_prep", launch_wkv_chunk_prep(wa, st));
       RUN(RWKV7_K_WKV, "wkv_chunk_scan", launch_wkv_chunk_scan(wa, st));
     } else {

@@ -594,20 +594,45 @@ RW_DEV floatx4 mfma4(float x, float y, floatx4 acc) {
 }
 
 struct ChunkPrepLds {
+  // ab, rb, bh, kh first hold the adapter outputs (decay, alpha, value gate,
+  // gate) when the kernel computes them itself; they are read before the
+  // barrier that precedes the first write of the decayed vectors
   float ab[CH][64], rb[CH][64], bh[CH][64], kh[CH][64], bt[CH][64], kt[CH][64], ld[CH][64];
   float a2[CH][64];
   float m[4][CH][CH + 1];   // C, E, F, H
   float g[CH][CH + 1];
 };
 
+// Adapter outputs of 16 tokens x 16 channels on the fp16 matrix cores: D =
+// lin_seg (16 x D) W_seg^T (D x 16), 32 ranks per step; lane l supplies lin
+// row l % 16 and weight row l % 16, ranks 8 (l / 16) .. +7 of the step, and
+// holds D[4 (l / 16) + i][l % 16] in component i.
+template <int D>
+RW_DEV floatx4 chunk_adapter(const half_t* lin_row, const half_t* w_row) {
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k0 = 0; k0 < D; k0 += 32) {
+    const half8 x = __builtin_bit_cast(half8, ld16(lin_row + k0));
+    const half8 y = __builtin_bit_cast(half8, ld16(w_row + k0));
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(x, y, acc, 0, 0, 0);
+  }
+  return acc;
+}
+
 // Grid: n_chunks * H workgroups of 256 threads; thread (t, j4) = (tid / 16,
 // 4 (tid % 16)) owns token t of the chunk and key columns j4..j4+3.  The
-// per-token head vectors are formed here from the projections and the
-// precomputed adapter outputs (as in the decode prologue: the key normalised
-// per head, the in-context rate folded into k~ and b, the value residual),
-// the 16 lanes of a token closing the per-head sums; v, the gate and the
-// bonus go to q_v, q_g and q_bonus for the scan and the GroupNorm kernel.
-__global__ __launch_bounds__(256) void k_wkv_chunk_prep(WkvArgs a) {
+// per-token head vectors are formed here (as in the decode prologue: the key
+// normalised per head, the in-context rate folded into k~ and b, the value
+// residual), the 16 lanes of a token closing the per-head sums; v, the gate
+// and the bonus go to q_v, q_g and q_bonus for the scan and the GroupNorm
+// kernel.  The adapter outputs (decay, alpha, value gate, gate) are read from
+// lo, or (ranks DW, DA, DV, DG > 0) computed here from the first-stage
+// activations (fp16 lin) and the second-stage matrices, wave w taking
+// channels 16 w .. 16 w + 15 of all four adapters; the ranks are template
+// arguments so every load of that step issues at once.
+template <int DW, int DA, int DV, int DG>
+__global__ __launch_bounds__(256, 3) void k_wkv_chunk_prep(WkvArgs a) {
+  constexpr bool AD = DW > 0;
   __shared__ __attribute__((aligned(16))) ChunkPrepLds L;
   const int H = a.H, C = a.C, T = a.B;
   const int c = blockIdx.x / H, h = blockIdx.x % H;
@@ -617,16 +642,47 @@ __global__ __launch_bounds__(256) void k_wkv_chunk_prep(WkvArgs a) {
   const bool live = tk < T;
   const int tc = live ? tk : T - 1;   // clamped: every load is issued
   const int cc = h * 64 + j4;
-  floatx4 av, bv, kv, dv, rv;
-  {
-    const long ro = (long)tc * 3 * C + cc, lo = (long)tc * 4 * C + cc, xo = (long)tc * C + cc;
-    rv = ldf4(a.rkv + ro);
-    const floatx4 kraw = ldf4(a.rkv + ro + C);
-    floatx4 vv = ldf4(a.rkv + ro + 2 * C);
+  const long ro = (long)tc * 3 * C + cc, xo = (long)tc * C + cc;
+  floatx4 av, bv, kv, dv, rv = ldf4(a.rkv + ro);
+  const floatx4 kraw = ldf4(a.rkv + ro + C);
+  floatx4 vv = ldf4(a.rkv + ro + 2 * C);
+  const floatx4 kk = ldf4(a.k_k + cc), ka = ldf4(a.k_a + cc), rk = ldf4(a.r_k + cc);
+  const floatx4 vf = ldf4(a.vfirst + xo);   // layer 0 writes it below instead
+  floatx4 al, vg, gg;
+  if constexpr (AD) {
+    const int lane = tid & 63, w = tid >> 6;
+    const int r16 = lane & 15, k8 = 8 * (lane >> 4);
+    const int tr = c * CH + r16;
+    const half_t* lin = reinterpret_cast<const half_t*>(a.lin) + (long)(tr < T ? tr : T - 1) * a.Lin + k8;
+    const int ch = h * 64 + 16 * w + r16;   // weight row of this lane
+    const floatx4 zw = chunk_adapter<DW>(lin, a.w2 + (long)ch * DW + k8);
+    const floatx4 za = chunk_adapter<DA>(lin + a.off_a, a.a2 + (long)ch * DA + k8);
+    const floatx4 zv = chunk_adapter<DV>(lin + a.off_v, a.v2 + (long)ch * DV + k8);
+    const floatx4 zg = chunk_adapter<DG>(lin + a.off_g, a.g2 + (long)ch * DG + k8);
+    // lane holds channel 16 w + r16 of tokens 4 (lane / 16) + i
+    const float w0 = a.w0[ch], a0 = a.a0[ch], v0 = a.v0[ch];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tt = 4 * (lane >> 4) + i, col = 16 * w + r16;
+      const float sw = 1.0f / (1.0f + expf(-(zw[i] + w0)));
+      L.ab[tt][col] = expf(-0.60653065971263342f * sw);     // decay
+      L.rb[tt][col] = 1.0f / (1.0f + expf(-(za[i] + a0)));  // alpha
+      L.bh[tt][col] = 1.0f / (1.0f + expf(-(zv[i] + v0)));  // value gate
+      L.kh[tt][col] = zg[i];                                // gate
+    }
+    __syncthreads();
+    dv = ldf4(&L.ab[t][j4]);
+    al = ldf4(&L.rb[t][j4]);
+    vg = ldf4(&L.bh[t][j4]);
+    gg = ldf4(&L.kh[t][j4]);
+  } else {
+    const long lo = (long)tc * 4 * C + cc;
     dv = ldf4(a.lo + lo);
-    const floatx4 al = ldf4(a.lo + lo + C), vg = ldf4(a.lo + lo + 2 * C), gg = ldf4(a.lo + lo + 3 * C);
-    const floatx4 kk = ldf4(a.k_k + cc), ka = ldf4(a.k_a + cc), rk = ldf4(a.r_k + cc);
-    const floatx4 vf = ldf4(a.vfirst + xo);   // layer 0 writes it below instead
+    al = ldf4(a.lo + lo + C);
+    vg = ldf4(a.lo + lo + 2 * C);
+    gg = ldf4(a.lo + lo + 3 * C);
+  }
+  {
     const floatx4 kap = kraw * kk;
     const float nrm = sqrtf(sum16(kap[0] * kap[0] + kap[1] * kap[1] + kap[2] * kap[2] + kap[3] * kap[3]));
     const float den = fmaxf(nrm, 1e-12f);
@@ -926,11 +982,30 @@ hipError_t launch_wkv_scan(const WkvArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_wkv_scan, dim3(a.H * 4), dim3(256), 0, st, a);
   return hipGetLastError();
 }
+// adapter ranks (w, a, v, g) with an in-kernel second stage: the tiny, 2.9B and 7.2B shapes
+#define CHUNK_AD_CASES(X) X(32, 32, 32, 64) X(64, 64, 32, 320) X(128, 128, 64, 480)
+bool wkv_chunk_adapters_ok(const WkvArgs& a) {
+  if (a.off_a % 8 || a.off_v % 8 || a.off_g % 8 || a.Lin % 8) return false;
+#define X(w, al, v, g) if (a.Dw == w && a.Da == al && a.Dv == v && a.Dg == g) return true;
+  CHUNK_AD_CASES(X)
+#undef X
+  return false;
+}
 hipError_t launch_wkv_chunk_prep(const WkvArgs& a, hipStream_t st) {
-  if (!a.q_rec || !a.lo || a.B < 1) return hipErrorInvalidValue;
-  const int nc = chunk_count(a.B);
-  hipLaunchKernelGGL(k_wkv_chunk_prep, dim3(nc * a.H), dim3(256), 0, st, a);
-  return hipGetLastError();
+  if (!a.q_rec || a.B < 1) return hipErrorInvalidValue;
+  const dim3 grid(chunk_count(a.B) * a.H);
+  if (a.lo) {
+    hipLaunchKernelGGL((k_wkv_chunk_prep<0, 0, 0, 0>), grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
+#define X(w, al, v, g)                                                                   \
+  if (a.Dw == w && a.Da == al && a.Dv == v && a.Dg == g && wkv_chunk_adapters_ok(a)) {   \
+    hipLaunchKernelGGL((k_wkv_chunk_prep<w, al, v, g>), grid, dim3(256), 0, st, a);      \
+    return hipGetLastError();                                                             \
+  }
+  CHUNK_AD_CASES(X)
+#undef X
+  return hipErrorInvalidValue;
 }
 hipError_t launch_wkv_chunk_scan(const WkvArgs& a, hipStream_t st) {
   if (!a.q_rec || a.B < 1) return hipErrorInvalidValue;

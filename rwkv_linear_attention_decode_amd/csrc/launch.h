@@ -223,11 +223,14 @@ hipError_t launch_wkv_scan(const WkvArgs& a, hipStream_t st);   // sequence: ser
 hipError_t launch_wkv_post(const WkvArgs& a, hipStream_t st);   // sequence: GroupNorm + bonus + gate
 // Chunked form of launch_wkv_prep + launch_wkv_scan (same q_v, q_g, q_bonus, q_y and
 // final state, up to rounding): the head vectors and per-chunk matrices for every (16-token
-// chunk, head), then the state carried chunk to chunk.  Needs the precomputed adapter
-// outputs (lo); q_rec needs wkv_chunk_rec_floats, q_y wkv_chunk_rows rows.
+// chunk, head), then the state carried chunk to chunk.  The adapter outputs come from lo
+// when it is set, else they are computed in the chunk kernel from fp16 lin and the
+// second-stage matrices (needs wkv_chunk_adapters_ok); q_rec needs wkv_chunk_rec_floats,
+// q_y wkv_chunk_rows rows.
 hipError_t launch_wkv_chunk_prep(const WkvArgs& a, hipStream_t st);
 hipError_t launch_wkv_chunk_scan(const WkvArgs& a, hipStream_t st);
 int64_t wkv_chunk_rec_floats(int T, int H);
+bool wkv_chunk_adapters_ok(const WkvArgs& a);
 // Rows of q_y the chunked scan writes (T rounded up to whole unrolled chunks; rows past T
 // are padding).
 int wkv_chunk_rows(int T);
