@@ -293,6 +293,18 @@ int gemv_rows_per_wg(int B, int K) {
   return 4 * (64 / lpr) * gemv_rpw(B);
 }
 
+// Rows per workgroup of a launch.  Workgroups spread evenly over the 256 CUs,
+// so the CU holding the most rows sets the time: a one-segment launch at B = 1
+// takes 20-row workgroups (5 rows per wave) when that lowers it (the 2.9B
+// channel-mix key: 640 workgroups of 16 rows leave half the CUs three, 512 of
+// 20 give every CU two).  K = 2560 and 4096 only.
+int gemv_launch_rows(int B, int K, int rows, int nseg) {
+  const int base = gemv_rows_per_wg(B, K);
+  if (B != 1 || nseg != 1 || (K != 2560 && K != 4096) || rows % 20) return base;
+  auto per_cu = [&](int r) { return (rows / r + 255) / 256 * r; };
+  return per_cu(20) < per_cu(base) ? 20 : base;
+}
+
 bool gemv_supported(int B, int K) {
   if (B < 1 || B > 4) return false;
   if (K == 256) return true;
@@ -330,9 +342,16 @@ template <int B>
 static hipError_t gemv_dispatch_b(const ProjArgs& a, int total_rows, hipStream_t st) {
   constexpr int RPW = gemv_rpw(B);
   const int K = a.K;
-  const int rows_wg = gemv_rows_per_wg(B, K);
+  const int rows_wg = gemv_launch_rows(B, K, total_rows, a.nseg);
   const dim3 grid((total_rows + rows_wg - 1) / rows_wg);
   const int epk = gemv_epk(a);
+  if constexpr (B == 1) {
+    if (rows_wg == 20) {
+      if (K == 2560) gemv_launch_epk<1, 64, 5, 5>(epk, grid, st, a);
+      else gemv_launch_epk<1, 64, 8, 5>(epk, grid, st, a);
+      return hipGetLastError();
+    }
+  }
   if (K == 256) {
     gemv_launch_epk<B, 32, 1, RPW>(epk, grid, st, a);
     return hipGetLastError();
@@ -356,16 +375,18 @@ hipError_t launch_gemv(const ProjArgs& a, int total_rows, hipStream_t st) {
   }
 }
 
-// Template arguments as a trace prints them, e.g. "k_gemv<1, 64, 5, 4, 1>".
-const char* gemv_kernel_name(int B, int K, int epi) {
-  static char names[5][9][5][40];
+// Template arguments as a trace prints them, e.g. "k_gemv<1, 64, 5, 4, 1>", for
+// a launch of `rows` output rows in `nseg` segments.
+const char* gemv_kernel_name(int B, int K, int epi, int rows, int nseg) {
+  static char names[5][9][5][2][40];
   if (!gemv_supported(B, K)) return "k_gemv";
   const int lpr = K == 256 ? 32 : 64;
   const int nch = K == 256 ? 1 : K / 512;
   const int epk = epi == -2 ? GV_PREV : epi == EPI_PRE ? GV_PRE : epi == EPI_RESID ? GV_RESID
                   : epi == EPI_NONE ? GV_NONE : GV_MIXED;
-  char* s = names[B][nch][epk];
+  const bool r20 = gemv_launch_rows(B, K, rows, nseg) == 20;
+  char* s = names[B][nch][epk][r20];
   if (!s[0])
-    snprintf(s, sizeof(names[0][0][0]), "k_gemv<%d, %d, %d, %d, %d>", B, lpr, nch, gemv_rpw(B), epk);
+    snprintf(s, sizeof(names[0][0][0][0]), "k_gemv<%d, %d, %d, %d, %d>", B, lpr, nch, r20 ? 5 : gemv_rpw(B), epk);
   return s;
 }
