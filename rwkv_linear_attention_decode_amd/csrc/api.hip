@@ -525,7 +525,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
     if (path.fuse_value) {
       CmixFoldArgs fa;
       memset(&fa, 0, sizeof fa);
-      fa.part = w.vpart; fa.nwg = (d.F + gemv_launch_rows(B, C, d.F, 1) - 1) / gemv_launch_rows(B, C, d.F, 1);
+      fa.part = w.vpart; fa.nwg = (d.F + gemv_launch_rows(B, C, d.F, 1, true) - 1) / gemv_launch_rows(B, C, d.F, 1, true);
       fa.mask = w.mask; fa.x = w.x; fa.u_ffn = path.fused ? w.u_ffn : nullptr;
       fa.pool = pool; fa.slot_stride = d.slot_floats; fa.n_slots = n_slots; fa.shift_off = lo + C;
       fa.slots = w.slots; fa.B = B; fa.C = C; fa.F = d.F;
@@ -1212,14 +1212,15 @@ const char* rwkv7_kernel_name(const rwkv7_model* m, int32_t cls, int32_t B) {
   switch (cls) {
     case RWKV7_K_LN_MIX: return "k_ln_mix";
     case RWKV7_K_PROJ_IN:
-      return p.gemv ? gemv_kernel_name(B, m->d.C, -1, m->d.Nin, 7) : gemm_kernel_name(B, m->d.Nin, m->d.C);
+      return p.gemv ? gemv_kernel_name(B, m->d.C, -1, m->d.Nin, 7, p.fused) : gemm_kernel_name(B, m->d.Nin, m->d.C);
     case RWKV7_K_PROJ_OUT:
-      return p.gemv ? gemv_kernel_name(B, m->d.C, EPI_RESID, m->d.C, 1) : gemm_kernel_name(B, m->d.C, m->d.C);
+      return p.gemv ? gemv_kernel_name(B, m->d.C, EPI_RESID, m->d.C, 1, false) : gemm_kernel_name(B, m->d.C, m->d.C);
     case RWKV7_K_CMIX_KEY:
-      return p.gemv ? gemv_kernel_name(B, m->d.C, p.fuse_value ? -2 : p.sparse ? EPI_PRE : -1, m->d.F, 1)
+      return p.gemv ? gemv_kernel_name(B, m->d.C, p.fuse_value ? -2 : p.sparse ? EPI_PRE : -1, m->d.F, 1,
+                                      p.fused || p.fuse_value)
                     : gemm_kernel_name(B, m->d.F, m->d.C);
     case RWKV7_K_HEAD:
-      return p.gemv ? gemv_kernel_name(B, m->d.C, EPI_NONE, m->d.V, 1) : gemm_kernel_name(B, m->d.V, m->d.C);
+      return p.gemv ? gemv_kernel_name(B, m->d.C, EPI_NONE, m->d.V, 1, p.fused) : gemm_kernel_name(B, m->d.V, m->d.C);
     case RWKV7_K_WKV: {
       if (!p.gemv) return "k_wkv_decode_rows";
       static char name[32];

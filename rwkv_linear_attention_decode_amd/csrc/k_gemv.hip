@@ -28,11 +28,14 @@ constexpr int kFusedMaxFloats = 80;
 // longer waits behind a separate compaction pass.
 enum : int { GV_MIXED = 0, GV_PRE = 1, GV_RESID = 2, GV_NONE = 3, GV_PREV = 4 };
 
-template <int B, int LPR, int NCH, int RPW, int EPK>
-__global__ __launch_bounds__(256) void k_gemv(ProjArgs a) {
+// NWV waves per workgroup: 4, or 5 for launches with neither the fused
+// LayerNorm prologue nor the value epilogue (both written for four waves).
+template <int B, int LPR, int NCH, int RPW, int EPK, int NWV = 4>
+__global__ __launch_bounds__(64 * NWV) void k_gemv(ProjArgs a) {
+  static_assert(NWV == 4 || EPK != GV_PREV, "the value epilogue assumes four waves");
   constexpr int GPW = 64 / LPR;
   constexpr int ROWS_WAVE = GPW * RPW;
-  constexpr int ROWS_WG = 4 * ROWS_WAVE;
+  constexpr int ROWS_WG = NWV * ROWS_WAVE;
   constexpr int K = LPR * NCH * 8;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -69,7 +72,7 @@ __global__ __launch_bounds__(256) void k_gemv(ProjArgs a) {
         xa[b][c][0] = p0.x; xa[b][c][1] = p0.y; xa[b][c][2] = p0.z; xa[b][c][3] = p0.w;
         xa[b][c][4] = p1.x; xa[b][c][5] = p1.y; xa[b][c][6] = p1.z; xa[b][c][7] = p1.w;
       }
-  } else if constexpr (B * NCH <= kFusedMaxFloats / 8) {
+  } else if constexpr (B * NCH <= kFusedMaxFloats / 8 && NWV == 4) {
     // Fused LayerNorm + token-shift mix, computed once per workgroup while
     // the weight loads above are in flight: wave w normalises the quarter
     // [w K/4, (w+1) K/4) of every row (coalesced, stride-64 lanes), row
@@ -295,14 +298,20 @@ int gemv_rows_per_wg(int B, int K) {
 
 // Rows per workgroup of a launch.  Workgroups spread evenly over the 256 CUs,
 // so the CU holding the most rows sets the time: a one-segment launch at B = 1
-// takes 20-row workgroups (5 rows per wave) when that lowers it (the 2.9B
-// channel-mix key: 640 workgroups of 16 rows leave half the CUs three, 512 of
-// 20 give every CU two).  K = 2560 and 4096 only.
-int gemv_launch_rows(int B, int K, int rows, int nseg) {
+// takes 20-row workgroups (four waves of 5 rows) or, unless it needs four
+// waves (fused prologue or value epilogue), 10-row ones (five waves of 2
+// rows) when that lowers it (2.9B:
+// the channel-mix key's 640 workgroups of 16 rows leave half the CUs three,
+// 512 of 20 give every CU two; W_o's 160 workgroups leave 96 CUs idle, 256 of
+// 10 fill them).  K = 2560 and 4096 only.
+int gemv_launch_rows(int B, int K, int rows, int nseg, bool four_waves) {
   const int base = gemv_rows_per_wg(B, K);
-  if (B != 1 || nseg != 1 || (K != 2560 && K != 4096) || rows % 20) return base;
-  auto per_cu = [&](int r) { return (rows / r + 255) / 256 * r; };
-  return per_cu(20) < per_cu(base) ? 20 : base;
+  if (B != 1 || nseg != 1 || (K != 2560 && K != 4096)) return base;
+  auto per_cu = [&](int r) { return rows % r ? 1 << 30 : (rows / r + 255) / 256 * r; };
+  int best = base;
+  if (per_cu(20) < per_cu(best)) best = 20;
+  if (!four_waves && per_cu(10) < per_cu(best)) best = 10;
+  return best;
 }
 
 bool gemv_supported(int B, int K) {
@@ -327,14 +336,18 @@ static int gemv_epk(const ProjArgs& a) {
   return e == EPI_PRE ? GV_PRE : e == EPI_RESID ? GV_RESID : e == EPI_NONE ? GV_NONE : GV_MIXED;
 }
 
-template <int B, int LPR, int NCH, int RPW>
+template <int B, int LPR, int NCH, int RPW, int NWV = 4>
 static void gemv_launch_epk(int epk, dim3 grid, hipStream_t st, const ProjArgs& a) {
+  const dim3 blk(64 * NWV);
   switch (epk) {
-    case GV_PRE: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_PRE>), grid, dim3(256), 0, st, a); break;
-    case GV_RESID: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_RESID>), grid, dim3(256), 0, st, a); break;
-    case GV_NONE: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_NONE>), grid, dim3(256), 0, st, a); break;
-    case GV_PREV: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_PREV>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_MIXED>), grid, dim3(256), 0, st, a); break;
+    case GV_PRE: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_PRE, NWV>), grid, blk, 0, st, a); break;
+    case GV_RESID: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_RESID, NWV>), grid, blk, 0, st, a); break;
+    case GV_NONE: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_NONE, NWV>), grid, blk, 0, st, a); break;
+    case GV_PREV:
+      if constexpr (NWV == 4)
+        hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_PREV, NWV>), grid, blk, 0, st, a);
+      break;
+    default: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_MIXED, NWV>), grid, blk, 0, st, a); break;
   }
 }
 
@@ -342,13 +355,18 @@ template <int B>
 static hipError_t gemv_dispatch_b(const ProjArgs& a, int total_rows, hipStream_t st) {
   constexpr int RPW = gemv_rpw(B);
   const int K = a.K;
-  const int rows_wg = gemv_launch_rows(B, K, total_rows, a.nseg);
+  const int rows_wg = gemv_launch_rows(B, K, total_rows, a.nseg, a.ln.mode != LNP_NONE || a.vW != nullptr);
   const dim3 grid((total_rows + rows_wg - 1) / rows_wg);
   const int epk = gemv_epk(a);
   if constexpr (B == 1) {
     if (rows_wg == 20) {
       if (K == 2560) gemv_launch_epk<1, 64, 5, 5>(epk, grid, st, a);
       else gemv_launch_epk<1, 64, 8, 5>(epk, grid, st, a);
+      return hipGetLastError();
+    }
+    if (rows_wg == 10) {   // five waves: no prologue, no value epilogue
+      if (K == 2560) gemv_launch_epk<1, 64, 5, 2, 5>(epk, grid, st, a);
+      else gemv_launch_epk<1, 64, 8, 2, 5>(epk, grid, st, a);
       return hipGetLastError();
     }
   }
@@ -376,17 +394,23 @@ hipError_t launch_gemv(const ProjArgs& a, int total_rows, hipStream_t st) {
 }
 
 // Template arguments as a trace prints them, e.g. "k_gemv<1, 64, 5, 4, 1>", for
-// a launch of `rows` output rows in `nseg` segments.
-const char* gemv_kernel_name(int B, int K, int epi, int rows, int nseg) {
-  static char names[5][9][5][2][40];
+// a launch of `rows` output rows in `nseg` segments (four_waves: it has the
+// fused prologue or the value epilogue).
+const char* gemv_kernel_name(int B, int K, int epi, int rows, int nseg, bool four_waves) {
+  static char names[5][9][5][3][40];
   if (!gemv_supported(B, K)) return "k_gemv";
   const int lpr = K == 256 ? 32 : 64;
   const int nch = K == 256 ? 1 : K / 512;
   const int epk = epi == -2 ? GV_PREV : epi == EPI_PRE ? GV_PRE : epi == EPI_RESID ? GV_RESID
                   : epi == EPI_NONE ? GV_NONE : GV_MIXED;
-  const bool r20 = gemv_launch_rows(B, K, rows, nseg) == 20;
-  char* s = names[B][nch][epk][r20];
-  if (!s[0])
-    snprintf(s, sizeof(names[0][0][0][0]), "k_gemv<%d, %d, %d, %d, %d>", B, lpr, nch, r20 ? 5 : gemv_rpw(B), epk);
+  const int rw = gemv_launch_rows(B, K, rows, nseg, four_waves);
+  char* s = names[B][nch][epk][rw == 20 ? 1 : rw == 10 ? 2 : 0];
+  if (!s[0]) {
+    if (rw == 10)
+      snprintf(s, sizeof(names[0][0][0][0]), "k_gemv<%d, %d, %d, 2, %d, 5>", B, lpr, nch, epk);
+    else
+      snprintf(s, sizeof(names[0][0][0][0]), "k_gemv<%d, %d, %d, %d, %d>", B, lpr, nch,
+               rw == 20 ? 5 : gemv_rpw(B), epk);
+  }
   return s;
 }

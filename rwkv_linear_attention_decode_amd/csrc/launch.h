@@ -7,8 +7,9 @@
 // Rows of one GEMV workgroup for batch B and reduction length K (segments
 // must start and end on multiples of it).
 int gemv_rows_per_wg(int B, int K);
-// Rows per workgroup that launch_gemv uses for `rows` output rows in `nseg` segments.
-int gemv_launch_rows(int B, int K, int rows, int nseg);
+// Rows per workgroup that launch_gemv uses for `rows` output rows in `nseg` segments;
+// four_waves: the launch has the fused LayerNorm prologue or the value epilogue.
+int gemv_launch_rows(int B, int K, int rows, int nseg, bool four_waves);
 bool gemv_supported(int B, int K);
 hipError_t launch_gemv(const ProjArgs& a, int total_rows, hipStream_t st);
 // MFMA path: A (segment activations) fp16.  `part_floats` bounds the split-K
@@ -25,7 +26,7 @@ hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int 
                            int split, hipStream_t st, int* deferred = nullptr);
 // `epi`: the epilogue shared by every segment of the launch, -1 when mixed,
 // -2 for the key projection with the sparse value fused into it
-const char* gemv_kernel_name(int B, int K, int epi, int rows, int nseg);
+const char* gemv_kernel_name(int B, int K, int epi, int rows, int nseg, bool four_waves);
 const char* gemm_kernel_name(int M, int N, int K);
 // Whether launch_gemm_cfg supports tile (32 tm x 32 tn), stage depth ks and K loop pipe.
 bool gemm_cfg_ok(int tm, int tn, int ks, int pipe);
