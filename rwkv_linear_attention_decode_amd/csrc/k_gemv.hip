@@ -393,7 +393,7 @@ hipError_t launch_gemv(const ProjArgs& a, int total_rows, hipStream_t st) {
   }
 }
 
-// Template arguments as a trace prints them, e.g. "k_gemv<1, 64, 5, 4, 1>", for
+// Template arguments as a trace prints them, e.g. "k_gemv<1, 64, 5, 4, 1, 4>", for
 // a launch of `rows` output rows in `nseg` segments (four_waves: it has the
 // fused prologue or the value epilogue).
 const char* gemv_kernel_name(int B, int K, int epi, int rows, int nseg, bool four_waves) {
@@ -405,12 +405,8 @@ const char* gemv_kernel_name(int B, int K, int epi, int rows, int nseg, bool fou
                   : epi == EPI_NONE ? GV_NONE : GV_MIXED;
   const int rw = gemv_launch_rows(B, K, rows, nseg, four_waves);
   char* s = names[B][nch][epk][rw == 20 ? 1 : rw == 10 ? 2 : 0];
-  if (!s[0]) {
-    if (rw == 10)
-      snprintf(s, sizeof(names[0][0][0][0]), "k_gemv<%d, %d, %d, 2, %d, 5>", B, lpr, nch, epk);
-    else
-      snprintf(s, sizeof(names[0][0][0][0]), "k_gemv<%d, %d, %d, %d, %d>", B, lpr, nch,
-               rw == 20 ? 5 : gemv_rpw(B), epk);
-  }
+  if (!s[0])
+    snprintf(s, sizeof(names[0][0][0][0]), "k_gemv<%d, %d, %d, %d, %d, %d>", B, lpr, nch,
+             rw == 10 ? 2 : rw == 20 ? 5 : gemv_rpw(B), epk, rw == 10 ? 5 : 4);
   return s;
 }
