@@ -743,7 +743,8 @@ static MmPlan mm_choose(const ProjArgs& a, int total_rows) {
     if (M <= 64) return {1, 2, 128, 0, 0};
     return M <= 256 ? MmPlan{2, 2, 64, 4, 0} : MmPlan{2, 4, 64, 4, 0};
   }
-  if (N >= 32768) return M <= 64 ? MmPlan{2, 4, 64, 3, 0} : MmPlan{4, 4, 64, 0, 0};   // head
+  if (N >= 32768)   // head
+    return M <= 64 ? MmPlan{2, 4, 64, 3, 0} : M <= 256 ? MmPlan{4, 8, 64, 4, 0} : MmPlan{4, 4, 64, 0, 0};
   const bool rank_k = K < 1024;                      // adapters' second stage
   if (M <= 64) {
     if (rank_k) return {1, 2, 128, 0, 0};
