@@ -387,3 +387,92 @@ def greedy_penalized(logits: np.ndarray, occ: np.ndarray, presence, frequency, d
         o[best] = np.add(o[best], f32(1.0), dtype=np.float32)
         occ_new[b] = o
     return ids, occ_new, err
+
+
+def _order_key(z: np.ndarray) -> np.ndarray:
+    """float32 -> uint32 increasing with the IEEE total order (-0 before +0)."""
+    bits = z.astype(np.float32).view(np.uint32).astype(np.uint64)
+    return np.where(bits >> 31, (~bits) & 0xFFFFFFFF, bits | 0x80000000)
+
+
+def sample_penalized(logits: np.ndarray, occ: np.ndarray, presence, frequency, decay_, temperature,
+                     top_p, top_k, forbidden, uniform):
+    """Penalised temperature / top-k / top-p sampling per row, with the occurrence update.
+
+    Albatross article (RWKV-Runner): the adapter inherits the sampling
+    defaults temperature 1.0, top_p 0.3, top_k 0 with the penalty defaults of
+    greedy_penalized, and the worker masks forbidden tokens, applies the
+    presence / frequency penalties and samples the decode rows as one batch.
+    The pages give no formulas.  Reading: plain temperature, top-k and nucleus
+    sampling, defined so that every decision is exact integer arithmetic:
+      l' as in greedy_penalized (float32); z = l' / T (float32);
+      candidates: tokens not forbidden with z finite;
+      order: z descending (IEEE total order, -0 after +0), then index ascending;
+      weight: W = floor(exp(z - max z) * 2**31), computed in float64 (0 .. 2**31);
+      top-k (0 < k < candidates): the first k candidates in that order;
+      top-p (p < 1): the shortest non-empty prefix of those whose weight sum
+        reaches ceil(p * S_k) (float64 product, S_k = their weight sum);
+      draw: u clamped to [0, 1 - 2**-24]; target = floor(u * S) (float64, S the
+        kept weight sum); the first kept token whose running weight sum
+        exceeds target;
+      T not > 0 (or NaN): z = l' and k = 1 (the penalised greedy pick);
+      occ = occ * decay; occ[id] += 1.
+    A row with no candidate gives id 0 and an error flag (occ is still updated).
+
+    logits, occ: float32 [B, V] (occ rows of the listed slots); presence,
+    frequency, decay_, temperature, top_p, uniform: float32 [B]; top_k: int
+    [B]; forbidden: bool [V] or None.  Returns (ids int32 [B], new occ float32
+    [B, V], error bool [B]).
+    """
+    logits = np.asarray(logits, dtype=np.float32)
+    occ = np.asarray(occ, dtype=np.float32)
+    B, V = logits.shape
+    f32 = np.float32
+    ids = np.zeros(B, dtype=np.int32)
+    err = np.zeros(B, dtype=bool)
+    occ_new = np.empty_like(occ)
+    idx = np.arange(V, dtype=np.uint64)
+    for b in range(B):
+        t = np.multiply(f32(frequency[b]), occ[b], dtype=np.float32)
+        pen = np.add(t, f32(presence[b]), dtype=np.float32)
+        lp = np.where(occ[b] > 0, np.subtract(logits[b], pen, dtype=np.float32), logits[b])
+        T = f32(temperature[b])
+        greedy = not (T > 0)
+        with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+            z = lp if greedy else np.divide(lp, T, dtype=np.float32)
+        cand = np.isfinite(z)
+        if forbidden is not None:
+            cand &= ~np.asarray(forbidden, dtype=bool)
+        best = 0
+        if not cand.any():
+            err[b] = True
+        else:
+            ci = np.nonzero(cand)[0]
+            zc = z[ci]
+            comp = (_order_key(zc) << np.uint64(16)) | (np.uint64(0xFFFF) - idx[ci])
+            order = ci[np.argsort(comp)[::-1]]                       # descending, unique keys
+            m = np.float64(zc.max())
+            w = np.floor(np.exp(z[order].astype(np.float64) - m) * 2.0 ** 31).astype(np.int64)
+            n = len(order)
+            k = 1 if greedy else int(top_k[b])
+            kk = n if (k <= 0 or k >= n) else k
+            csum = np.cumsum(w[:kk])
+            p = np.float64(f32(top_p[b]))
+            keep = kk
+            if p < 1.0:
+                goal = max(int(np.ceil(p * np.float64(csum[-1]))), 1)
+                keep = int(np.searchsorted(csum, goal, side="left")) + 1
+            S = int(csum[keep - 1])
+            u = f32(uniform[b])
+            if not (u >= 0):
+                u = f32(0.0)
+            if u >= 1:
+                u = f32(1.0 - 2.0 ** -24)
+            target = int(np.floor(np.float64(u) * np.float64(S)))
+            j = int(np.searchsorted(csum[:keep], target, side="right"))   # first running sum > target
+            best = int(order[j])
+        ids[b] = best
+        o = np.multiply(occ[b], f32(decay_[b]), dtype=np.float32)
+        o[best] = np.add(o[best], f32(1.0), dtype=np.float32)
+        occ_new[b] = o
+    return ids, occ_new, err
