@@ -54,7 +54,8 @@ extern "C" {
 #define RWKV7_ERR_SLOT_RANGE 1u   /* a slot index outside [0, n_slots): row skipped */
 #define RWKV7_ERR_SLOT_DUP 2u     /* a slot listed twice in one call: later rows skipped */
 #define RWKV7_ERR_TOKEN_RANGE 4u  /* a token id outside [0, vocab): token 0 used */
-#define RWKV7_ERR_ALL_NAN 8u      /* rwkv7_greedy: a logits row was all NaN: id 0 */
+#define RWKV7_ERR_ALL_NAN 8u      /* rwkv7_greedy: a logits row was all NaN; rwkv7_sample: a row
+                                     had no candidate: id 0 */
 
 /* ---- tensor dtypes ---- */
 #define RWKV7_F32 0
@@ -180,6 +181,39 @@ int rwkv7_greedy(int32_t B, int32_t V, const float* logits, float* occ_pool, int
                  const int32_t* slot_idx, const float* presence, const float* frequency,
                  const float* decay, int32_t* ids_out, void* ws, uint64_t ws_bytes,
                  void* stream);
+
+/* Penalised temperature / top-k / top-p sampling over logits [B*V] (device
+ * fp32, V <= 65536).  The Albatross article (RWKV-Runner backend) names the
+ * adapter's sampling defaults (temperature 1.0, top_p 0.3, top_k 0) and the
+ * worker's per-step order: forbidden-token mask, presence / frequency
+ * penalty, batched sampling; it gives no formulas.  Per row b, with occ as
+ * in rwkv7_greedy:
+ *   l' as in rwkv7_greedy; z = l' / temperature[b] (fp32);
+ *   candidates: tokens with forbidden[v] == 0 (forbidden may be NULL) and z
+ *     finite;
+ *   order: z descending (IEEE total order, -0 after +0), then index ascending;
+ *   weight: floor(exp(z - max z) * 2^31), computed in fp64;
+ *   top-k (0 < top_k[b] < candidates): the first top_k[b] candidates;
+ *   top-p (top_p[b] < 1): the shortest non-empty prefix of those whose weight
+ *     sum reaches ceil(top_p[b] * their total) (fp64 product);
+ *   draw: u = uniform[b] clamped to [0, 1 - 2^-24]; the first kept token whose
+ *     running weight sum exceeds floor(u * kept total) (fp64 product);
+ *   temperature not > 0: z = l' and top_k = 1 (the greedy pick);
+ *   occ = occ*decay[b]; then occ[id] += 1.
+ * Every decision is integer arithmetic, so the result does not depend on
+ * timing.  A row without candidates gives 0 and RWKV7_ERR_ALL_NAN.
+ * temperature, top_p, uniform, presence, frequency, decay: device fp32[B];
+ * top_k: device int32[B]; forbidden: device uint8[V] or NULL; ids_out:
+ * device int32[B].  The caller draws the uniforms.  `ws`: a device buffer of
+ * rwkv7_sample_workspace_bytes (its first word is the error word read by
+ * rwkv7_poll_error).  EINVAL for null pointers or sizes, ENOTSUP for V >
+ * 65536, ESHAPE for a short workspace; nothing is launched then. */
+int rwkv7_sample_workspace_bytes(int32_t B, int32_t V, uint64_t* bytes);
+int rwkv7_sample(int32_t B, int32_t V, const float* logits, float* occ_pool, int64_t n_slots,
+                 const int32_t* slot_idx, const float* presence, const float* frequency,
+                 const float* decay, const float* temperature, const float* top_p,
+                 const int32_t* top_k, const uint8_t* forbidden, const float* uniform,
+                 int32_t* ids_out, void* ws, uint64_t ws_bytes, void* stream);
 
 /* ---- errors ---- */
 

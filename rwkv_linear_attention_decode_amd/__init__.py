@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
         "rwkv7_prefill_seq": [vp, vp, i64, i32, vp, i32, vp, u64, vp],
         "rwkv7_greedy_workspace_bytes": [i32, i32, P(u64)],
         "rwkv7_greedy": [i32, i32, vp, vp, i64, vp, vp, vp, vp, vp, vp, u64, vp],
+        "rwkv7_sample_workspace_bytes": [i32, i32, P(u64)],
+        "rwkv7_sample": [i32, i32, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, u64, vp],
         "rwkv7_poll_error": [vp, vp, P(ctypes.c_uint32)],
         "rwkv7_set_option": [vp, i32, i64],
         "rwkv7_get_option": [vp, i32, P(i64)],
@@ -220,6 +222,25 @@ def rwkv7_greedy(logits, occ_pool, n_slots: int, slot_idx, presence, frequency, 
     _check(lib().rwkv7_greedy(B, V, _ptr(logits), _ptr(occ_pool), n_slots, _ptr(slot_idx),
                               _ptr(presence), _ptr(frequency), _ptr(decay), _ptr(ids_out),
                               ws.data_ptr(), ws.numel(), _stream(stream)), "rwkv7_greedy")
+
+
+def rwkv7_sample_workspace_bytes(B: int, V: int) -> int:
+    v = ctypes.c_uint64()
+    _check(lib().rwkv7_sample_workspace_bytes(B, V, ctypes.byref(v)), "rwkv7_sample_workspace_bytes")
+    return v.value
+
+
+def rwkv7_sample(logits, occ_pool, n_slots: int, slot_idx, presence, frequency, decay, temperature,
+                 top_p, top_k, forbidden, uniform, ids_out, ws, stream=None):
+    """Penalised temperature / top-k / top-p sampling (see include/rwkv7.h).
+    forbidden: uint8 [V] tensor or None; ws: a uint8 tensor of
+    rwkv7_sample_workspace_bytes(B, V) bytes (its first word is an error word)."""
+    B, V = logits.shape
+    _check(lib().rwkv7_sample(B, V, _ptr(logits), _ptr(occ_pool), n_slots, _ptr(slot_idx),
+                              _ptr(presence), _ptr(frequency), _ptr(decay), _ptr(temperature),
+                              _ptr(top_p), _ptr(top_k), None if forbidden is None else _ptr(forbidden),
+                              _ptr(uniform), _ptr(ids_out), ws.data_ptr(), ws.numel(), _stream(stream)),
+           "rwkv7_sample")
 
 
 def rwkv7_poll_error(ws, stream=None) -> int:

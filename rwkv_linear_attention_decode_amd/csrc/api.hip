@@ -1056,6 +1056,43 @@ int rwkv7_greedy(int32_t B, int32_t V, const float* logits, float* occ_pool, int
   return RWKV7_OK;
 }
 
+int rwkv7_sample_workspace_bytes(int32_t B, int32_t V, uint64_t* bytes) {
+  if (!bytes) return fail(RWKV7_EINVAL, "bytes is NULL");
+  if (B < 1 || V < 1) return fail(RWKV7_EINVAL, "B and V must be >= 1");
+  *bytes = ALIGN + align_up((uint64_t)B * V * 8) + align_up((uint64_t)B * V * 4);
+  return RWKV7_OK;
+}
+
+int rwkv7_sample(int32_t B, int32_t V, const float* logits, float* occ_pool, int64_t n_slots,
+                 const int32_t* slot_idx, const float* presence, const float* frequency,
+                 const float* decay, const float* temperature, const float* top_p,
+                 const int32_t* top_k, const uint8_t* forbidden, const float* uniform,
+                 int32_t* ids_out, void* ws, uint64_t ws_bytes, void* stream) {
+  if (B < 1 || V < 1) return fail(RWKV7_EINVAL, "B and V must be >= 1");
+  if (V > SAMPLE_MAX_V) return fail(RWKV7_ENOTSUP, "V must be <= %d (got %d)", SAMPLE_MAX_V, V);
+  if (n_slots < 1) return fail(RWKV7_EINVAL, "n_slots must be >= 1");
+  if (!logits || !occ_pool || !slot_idx || !presence || !frequency || !decay || !temperature ||
+      !top_p || !top_k || !uniform || !ids_out || !ws)
+    return fail(RWKV7_EINVAL, "null pointer argument");
+  uint64_t need = 0;
+  rwkv7_sample_workspace_bytes(B, V, &need);
+  if (ws_bytes < need)
+    return fail(RWKV7_ESHAPE, "workspace too small: %llu < %llu bytes", (unsigned long long)ws_bytes,
+                (unsigned long long)need);
+  SampleArgs a;
+  a.logits = logits; a.occ = occ_pool; a.n_slots = n_slots; a.slot_idx = slot_idx;
+  a.presence = presence; a.frequency = frequency; a.decay = decay;
+  a.temperature = temperature; a.top_p = top_p; a.top_k = top_k; a.forbidden = forbidden;
+  a.uniform = uniform; a.ids = ids_out;
+  char* base = (char*)ws;
+  a.err = (uint32_t*)base;
+  a.key = (uint64_t*)(base + ALIGN);
+  a.wt = (uint32_t*)(base + ALIGN + align_up((uint64_t)B * V * 8));
+  a.B = B; a.V = V;
+  HIP_TRY(launch_sample(a, (hipStream_t)stream), "sample");
+  return RWKV7_OK;
+}
+
 int rwkv7_poll_error(void* ws, void* stream, uint32_t* flags) {
   if (!ws) return fail(RWKV7_EINVAL, "workspace is NULL");
   hipStream_t st = (hipStream_t)stream;

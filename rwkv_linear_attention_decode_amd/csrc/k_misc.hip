@@ -768,6 +768,213 @@ __global__ __launch_bounds__(64) void k_greedy_final(GreedyArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- sampling
+// Penalised temperature / top-k / top-p sampling (the Albatross article's
+// adapter defaults and per-step order: forbidden-token mask, presence /
+// frequency penalty, batched sampling).  Every decision is integer
+// arithmetic so that the pick is reproducible bit for bit:
+//   z = l' / T (fp32, l' as in greedy); candidates: not forbidden, z finite;
+//   order: the 48-bit key (ordered bits of z) << 16 | (0xFFFF - index), so
+//   z descending then index ascending, every key distinct;
+//   weight: floor(exp(z - max z) * 2^31) in fp64;
+//   top-k, top-p and the draw each take the shortest prefix of that order
+//   whose count or weight sum reaches a goal (k; ceil(p * S_k); floor(u * S)
+//   + 1), found by a radix select over the key, 12 bits per level, with
+//   count and weight histograms in LDS (integer atomics, so the sums do not
+//   depend on timing).
+// One 1024-thread workgroup per row; the keys and weights go through the
+// workspace between the passes.
+constexpr int SMP_THREADS = 1024;
+constexpr int SMP_BINS = 4096;
+
+struct SampleLds {
+  uint32_t cnt[SMP_BINS];
+  unsigned long long mass[SMP_BINS];
+  unsigned long long wtot[16];
+  float fred[16];
+  int sel_digit;
+  unsigned long long sel_c, sel_m, sel_here;
+};
+
+RW_DEV uint64_t smp_order_key(float z) {
+  const uint32_t b = __float_as_uint(z);
+  return (b >> 31) ? (uint64_t)(~b) : (uint64_t)(b | 0x80000000u);
+}
+
+// Exclusive prefix sum over the 1024 threads (in thread order).
+RW_DEV unsigned long long smp_exscan(unsigned long long v, SampleLds& L) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  unsigned long long incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long n = __shfl_up(incl, o);
+    if (lane >= o) incl += n;
+  }
+  if (lane == 63) L.wtot[wave] = incl;
+  __syncthreads();
+  unsigned long long base = 0;
+  for (int w = 0; w < wave; ++w) base += L.wtot[w];
+  __syncthreads();
+  return base + incl - v;
+}
+
+RW_DEV unsigned long long smp_sum(unsigned long long v, SampleLds& L) {
+  const unsigned long long e = smp_exscan(v, L);
+  if (threadIdx.x == SMP_THREADS - 1) L.sel_here = e + v;
+  __syncthreads();
+  const unsigned long long r = L.sel_here;
+  __syncthreads();
+  return r;
+}
+
+// The shortest prefix, in descending key order, of the row's candidates with
+// key >= lo whose count (by_mass false) or weight sum reaches goal (1 <= goal
+// <= that set's total).  Returns the key of its last token; *pm: the prefix's
+// weight sum.
+RW_DEV uint64_t smp_select(const uint64_t* key, const uint32_t* wt, int V, uint64_t lo, bool by_mass,
+                           unsigned long long goal, unsigned long long* pm, SampleLds& L) {
+  const int t = threadIdx.x;
+  uint64_t prefix = 0;
+  unsigned long long above_c = 0, above_m = 0, here_m = 0;
+  for (int level = 0; level < 4; ++level) {
+    const int shift = 36 - 12 * level;
+    for (int i = t; i < SMP_BINS; i += SMP_THREADS) {
+      L.cnt[i] = 0;
+      L.mass[i] = 0;
+    }
+    __syncthreads();
+    for (int v = t; v < V; v += SMP_THREADS) {
+      const uint64_t c = key[v];
+      if (c >= lo && c != 0 && (level == 0 || (c >> (shift + 12)) == (prefix >> (shift + 12)))) {
+        const int d = (int)((c >> shift) & (SMP_BINS - 1));
+        atomicAdd(&L.cnt[d], 1u);
+        atomicAdd(&L.mass[d], (unsigned long long)wt[v]);
+      }
+    }
+    __syncthreads();
+    // thread t owns bins 4095 - 4t down to 4092 - 4t
+    unsigned long long bc[4], bm[4], sc = 0, sm = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d = SMP_BINS - 1 - 4 * t - q;
+      bc[q] = L.cnt[d];
+      bm[q] = L.mass[d];
+      sc += bc[q];
+      sm += bm[q];
+    }
+    unsigned long long rc = above_c + smp_exscan(sc, L), rm = above_m + smp_exscan(sm, L);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const unsigned long long before = by_mass ? rm : rc, here = by_mass ? bm[q] : bc[q];
+      if (here && before < goal && before + here >= goal) {
+        L.sel_digit = SMP_BINS - 1 - 4 * t - q;
+        L.sel_c = rc;
+        L.sel_m = rm;
+        L.sel_here = bm[q];
+      }
+      rc += bc[q];
+      rm += bm[q];
+    }
+    __syncthreads();
+    prefix |= (uint64_t)L.sel_digit << shift;
+    above_c = L.sel_c;
+    above_m = L.sel_m;
+    here_m = L.sel_here;
+    __syncthreads();
+  }
+  *pm = above_m + here_m;   // the last level's bin holds the boundary token alone
+  return prefix;
+}
+
+__global__ __launch_bounds__(1024) void k_sample(SampleArgs a) {
+  __shared__ SampleLds L;
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int V = a.V;
+  const int slot = a.slot_idx[b];
+  float* occ = (slot >= 0 && (int64_t)slot < a.n_slots) ? a.occ + (int64_t)slot * V : nullptr;
+  const float* lg = a.logits + (int64_t)b * V;
+  uint64_t* key = a.key + (int64_t)b * V;
+  uint32_t* wt = a.wt + (int64_t)b * V;
+  const float T = a.temperature[b], pres = a.presence[b], freq = a.frequency[b];
+  const bool greedy = !(T > 0.f);
+
+  // penalised, tempered logit of token v; NaN marks a token that is not a
+  // candidate (the second pass recomputes it: the same fp32 ops)
+  auto zval = [&](int v) {
+    const float l = lg[v];
+    const float o = occ ? occ[v] : 0.f;
+    const float lp = o > 0.f ? __fsub_rn(l, __fadd_rn(__fmul_rn(freq, o), pres)) : l;
+    const float x = greedy ? lp : __fdiv_rn(lp, T);
+    return (!isfinite(x) || (a.forbidden && a.forbidden[v])) ? NAN : x;
+  };
+  float mx = -INFINITY;
+  for (int v = t; v < V; v += SMP_THREADS) {
+    const float x = zval(v);
+    if (x == x) mx = fmaxf(mx, x);
+  }
+  mx = wave_max(mx);
+  if (lane == 0) L.fred[wave] = mx;
+  __syncthreads();
+  mx = L.fred[0];
+  for (int w = 1; w < SMP_THREADS / 64; ++w) mx = fmaxf(mx, L.fred[w]);
+
+  unsigned long long n = 0, tot = 0;
+#pragma unroll 1
+  for (int v = t; v < V; v += SMP_THREADS) {
+    const float x = zval(v);
+    const bool c = x == x;
+    const uint32_t w = c ? (uint32_t)floor(exp((double)x - (double)mx) * 2147483648.0) : 0u;
+    key[v] = c ? (smp_order_key(x) << 16) | (uint64_t)(0xFFFF - v) : 0ull;
+    wt[v] = w;
+    n += c;
+    tot += w;
+  }
+  n = smp_sum(n, L);
+  tot = smp_sum(tot, L);   // the barriers inside also publish key / wt to the workgroup
+
+  int id = 0;
+  if (n == 0) {
+    if (t == 0) set_err(a.err, ERRB_ALL_NAN);
+  } else {
+    const int k = greedy ? 1 : a.top_k[b];
+    uint64_t lo = 1;
+    unsigned long long S = tot;
+    if (k > 0 && (unsigned long long)k < n) lo = smp_select(key, wt, V, lo, false, (unsigned long long)k, &S, L);
+    const float p = a.top_p[b];
+    if (p < 1.f) {
+      const double g = ceil((double)p * (double)S);
+      lo = smp_select(key, wt, V, lo, true, g < 1.0 ? 1ull : (unsigned long long)g, &S, L);
+    }
+    float u = a.uniform[b];
+    if (!(u >= 0.f)) u = 0.f;
+    if (u >= 1.f) u = 0x1.fffffep-1f;
+    const unsigned long long target = (unsigned long long)floor((double)u * (double)S);
+    unsigned long long m;
+    const uint64_t kb = smp_select(key, wt, V, lo, true, target + 1, &m, L);
+    id = 0xFFFF - (int)(kb & 0xFFFF);
+    if (id >= V) {   // not reachable when every goal is within its set's total
+      id = 0;
+      if (t == 0) set_err(a.err, ERRB_ALL_NAN);
+    }
+  }
+  if (occ) {
+    const float dec = a.decay[b];
+    for (int v = t; v < V; v += SMP_THREADS) {
+      float o = __fmul_rn(occ[v], dec);
+      if (v == id) o = __fadd_rn(o, 1.0f);
+      occ[v] = o;
+    }
+  }
+  if (t == 0) a.ids[b] = id;
+}
+
+hipError_t launch_sample(const SampleArgs& a, hipStream_t st) {
+  if (a.B < 1 || a.V < 1 || a.V > SAMPLE_MAX_V) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_sample, dim3(a.B), dim3(SMP_THREADS), 0, st, a);
+  return hipGetLastError();
+}
+
 int greedy_blocks(int V) { return (V + GREEDY_PER_BLOCK - 1) / GREEDY_PER_BLOCK; }
 
 hipError_t launch_greedy(const GreedyArgs& a, hipStream_t st) {

@@ -178,6 +178,29 @@ struct GreedyArgs {
 int greedy_blocks(int V);
 hipError_t launch_greedy(const GreedyArgs& a, hipStream_t st);
 
+// penalised temperature / top-k / top-p sampling (one workgroup per row, V <= 65536)
+struct SampleArgs {
+  const float* logits;
+  float* occ;
+  int64_t n_slots;
+  const int* slot_idx;
+  const float* presence;
+  const float* frequency;
+  const float* decay;
+  const float* temperature;
+  const float* top_p;
+  const int* top_k;
+  const unsigned char* forbidden;   // [V] nonzero = never sampled, or nullptr
+  const float* uniform;             // [B] draws in [0, 1)
+  int* ids;
+  uint32_t* err;
+  uint64_t* key;                    // [B][V] workspace: order keys (0 = not a candidate)
+  uint32_t* wt;                     // [B][V] workspace: fixed-point weights
+  int B, V;
+};
+constexpr int SAMPLE_MAX_V = 65536;
+hipError_t launch_sample(const SampleArgs& a, hipStream_t st);
+
 // ---------------------------------------------------------------- WKV
 struct WkvArgs {
   float* pool;
