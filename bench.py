@@ -281,8 +281,48 @@ def batched(R, args, shape, m, B):
         proj[name] = {"us": round(avg * 1e3, 2), "tflops": round(tf, 1),
                       "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
     res["projections"] = proj
-    log(f"[bench] B={B}: {res['tok_s']} tok/s, {ms:.3f} ms/step, step {res['step_gbs']} GB/s")
+    res["sample"] = sample_timing(R, m, logits, occ, slots, pres, freq, dec)
+    log(f"[bench] B={B}: {res['tok_s']} tok/s, {ms:.3f} ms/step, step {res['step_gbs']} GB/s; "
+        f"rwkv7_sample {res['sample']['us']} us")
     return res
+
+
+def sample_timing(R, m, logits, occ, slots, pres, freq, dec, reps=20):
+    """rwkv7_sample on a step's logits with the adapter defaults the pages give
+    (temperature 1.0, top_p 0.3, top_k 0) and the workload's penalties; seeded
+    uniforms, a copy of the occurrence rows.  Algorithmic bytes: logits read
+    plus occurrence read and write (12 B per token); the workspace passes of
+    the radix selects stay in L2 and are not counted."""
+    import torch
+    B, V = logits.shape
+    ws = torch.zeros(R.rwkv7_sample_workspace_bytes(B, V), dtype=torch.uint8, device="cuda")
+    occ2 = occ.clone()
+    temp = torch.ones(B, device="cuda")
+    top_p = torch.full((B,), 0.3, device="cuda")
+    top_k = torch.zeros(B, dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234)
+    uni = torch.rand(B, device="cuda", generator=g)
+    ids = torch.empty(B, dtype=torch.int32, device="cuda")
+
+    def call():
+        R.rwkv7_sample(logits, occ2, m.n_slots, slots, pres, freq, dec, temp, top_p, top_k, None, uni, ids, ws)
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    if R.rwkv7_poll_error(ws):
+        raise RuntimeError("device error flags from rwkv7_sample")
+    gbs = 12.0 * B * V / (us * 1e-6) / 1e9
+    return {"us": round(us, 2), "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "distinct_ids": int(torch.unique(ids).numel())}
 
 
 # ---------------------------------------------------------------- prefill
@@ -379,6 +419,10 @@ def main():
     roof = roofline_b1(R, shape, m, kb, nnz, slot, tok, logits)
     log(f"[bench] dominant kernel {roof['class']}: {roof['avg_launch_us']} us/launch, "
         f"{roof['achieved']} GB/s ({roof['frac'] * 100:.1f}% of HBM peak)")
+    pen = torch.ones(1, device="cuda")
+    samp_b1 = sample_timing(R, m, logits, torch.zeros(m.n_slots, shape.vocab, device="cuda"), slot, pen, pen,
+                            pen * 0.996)
+    log(f"[bench] rwkv7_sample B=1: {samp_b1['us']} us")
 
     batched_res = [batched(R, args, shape, m, B) for B in Bs]
     prefill_res = prefill(R, shape, m, Ts) if Ts else {}
@@ -414,6 +458,7 @@ def main():
         "kernels": {k: {"ms_per_step": round(v["ms_per_step"], 4),
                         "launches_per_step": v["launches_per_step"]} for k, v in kb.items()},
         "batched": batched_res + big_res,
+        "sample_b1": samp_b1,
         "prefill": prefill_res,
         "cpu_baseline": cpu,
     }

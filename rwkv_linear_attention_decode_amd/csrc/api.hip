@@ -1059,7 +1059,7 @@ int rwkv7_greedy(int32_t B, int32_t V, const float* logits, float* occ_pool, int
 int rwkv7_sample_workspace_bytes(int32_t B, int32_t V, uint64_t* bytes) {
   if (!bytes) return fail(RWKV7_EINVAL, "bytes is NULL");
   if (B < 1 || V < 1) return fail(RWKV7_EINVAL, "B and V must be >= 1");
-  *bytes = ALIGN + align_up((uint64_t)B * V * 8) + align_up((uint64_t)B * V * 4);
+  *bytes = ALIGN + align_up((uint64_t)B * V * 4) * 2;
   return RWKV7_OK;
 }
 
@@ -1086,8 +1086,8 @@ int rwkv7_sample(int32_t B, int32_t V, const float* logits, float* occ_pool, int
   a.uniform = uniform; a.ids = ids_out;
   char* base = (char*)ws;
   a.err = (uint32_t*)base;
-  a.key = (uint64_t*)(base + ALIGN);
-  a.wt = (uint32_t*)(base + ALIGN + align_up((uint64_t)B * V * 8));
+  a.key = (uint32_t*)(base + ALIGN);
+  a.wt = (uint32_t*)(base + ALIGN + align_up((uint64_t)B * V * 4));
   a.B = B; a.V = V;
   HIP_TRY(launch_sample(a, (hipStream_t)stream), "sample");
   return RWKV7_OK;

@@ -787,9 +787,14 @@ __global__ __launch_bounds__(64) void k_greedy_final(GreedyArgs a) {
 constexpr int SMP_THREADS = 1024;
 constexpr int SMP_BINS = 4096;
 
+constexpr int SMP_LIST = 4096;   // tokens of one top-level bin kept in LDS for the finer levels
+
 struct SampleLds {
   uint32_t cnt[SMP_BINS];
   unsigned long long mass[SMP_BINS];
+  unsigned long long lkey[SMP_LIST];
+  uint32_t lwt[SMP_LIST];
+  int lcount;
   unsigned long long wtot[16];
   float fred[16];
   int sel_digit;
@@ -830,28 +835,50 @@ RW_DEV unsigned long long smp_sum(unsigned long long v, SampleLds& L) {
 // The shortest prefix, in descending key order, of the row's candidates with
 // key >= lo whose count (by_mass false) or weight sum reaches goal (1 <= goal
 // <= that set's total).  Returns the key of its last token; *pm: the prefix's
-// weight sum.
-RW_DEV uint64_t smp_select(const uint64_t* key, const uint32_t* wt, int V, uint64_t lo, bool by_mass,
-                           unsigned long long goal, unsigned long long* pm, SampleLds& L) {
+// weight sum.  The first level reads the row from the workspace; when the
+// chosen top-level bin holds at most SMP_LIST tokens they are gathered into
+// LDS once and the three finer levels read that list instead.
+RW_DEV uint64_t smp_key(const uint32_t* key, int v) {   // 48-bit order key of token v (0: none)
+  const uint32_t k = key[v];
+  return k ? ((uint64_t)k << 16) | (uint64_t)(0xFFFF - v) : 0ull;
+}
+
+RW_DEV uint64_t smp_select(const uint32_t* key, const uint32_t* wt, int V, uint64_t lo, bool by_mass,
+                           unsigned long long goal, unsigned long long* pm, SampleLds& L,
+                           bool hist_ready = false) {
   const int t = threadIdx.x;
   uint64_t prefix = 0;
   unsigned long long above_c = 0, above_m = 0, here_m = 0;
+  bool listed = false;
   for (int level = 0; level < 4; ++level) {
     const int shift = 36 - 12 * level;
+    if (level == 0 && hist_ready) goto scan;   // the top-level histogram of every candidate is in LDS
     for (int i = t; i < SMP_BINS; i += SMP_THREADS) {
       L.cnt[i] = 0;
       L.mass[i] = 0;
     }
     __syncthreads();
-    for (int v = t; v < V; v += SMP_THREADS) {
-      const uint64_t c = key[v];
-      if (c >= lo && c != 0 && (level == 0 || (c >> (shift + 12)) == (prefix >> (shift + 12)))) {
-        const int d = (int)((c >> shift) & (SMP_BINS - 1));
-        atomicAdd(&L.cnt[d], 1u);
-        atomicAdd(&L.mass[d], (unsigned long long)wt[v]);
+    if (listed) {
+      for (int i = t; i < L.lcount; i += SMP_THREADS) {
+        const uint64_t c = L.lkey[i];
+        if ((c >> (shift + 12)) == (prefix >> (shift + 12))) {
+          const int d = (int)((c >> shift) & (SMP_BINS - 1));
+          atomicAdd(&L.cnt[d], 1u);
+          atomicAdd(&L.mass[d], (unsigned long long)L.lwt[i]);
+        }
+      }
+    } else {
+      for (int v = t; v < V; v += SMP_THREADS) {
+        const uint64_t c = smp_key(key, v);
+        if (c >= lo && c != 0 && (level == 0 || (c >> (shift + 12)) == (prefix >> (shift + 12)))) {
+          const int d = (int)((c >> shift) & (SMP_BINS - 1));
+          atomicAdd(&L.cnt[d], 1u);
+          atomicAdd(&L.mass[d], (unsigned long long)wt[v]);
+        }
       }
     }
     __syncthreads();
+  scan:
     // thread t owns bins 4095 - 4t down to 4092 - 4t
     unsigned long long bc[4], bm[4], sc = 0, sm = 0;
 #pragma unroll
@@ -880,7 +907,22 @@ RW_DEV uint64_t smp_select(const uint64_t* key, const uint32_t* wt, int V, uint6
     above_c = L.sel_c;
     above_m = L.sel_m;
     here_m = L.sel_here;
+    const bool gather = level == 0 && L.cnt[L.sel_digit] <= SMP_LIST;   // the same in every thread
+    if (gather && t == 0) L.lcount = 0;
     __syncthreads();
+    if (gather) {
+      // the tokens of the chosen bin (all >= lo: the bin is at or above lo's)
+      for (int v = t; v < V; v += SMP_THREADS) {
+        const uint64_t c = smp_key(key, v);
+        if (c >= lo && c != 0 && (c >> 36) == (prefix >> 36)) {
+          const int i = atomicAdd(&L.lcount, 1);
+          L.lkey[i] = c;
+          L.lwt[i] = wt[v];
+        }
+      }
+      __syncthreads();
+      listed = true;
+    }
   }
   *pm = above_m + here_m;   // the last level's bin holds the boundary token alone
   return prefix;
@@ -894,7 +936,7 @@ __global__ __launch_bounds__(1024) void k_sample(SampleArgs a) {
   const int slot = a.slot_idx[b];
   float* occ = (slot >= 0 && (int64_t)slot < a.n_slots) ? a.occ + (int64_t)slot * V : nullptr;
   const float* lg = a.logits + (int64_t)b * V;
-  uint64_t* key = a.key + (int64_t)b * V;
+  uint32_t* key = a.key + (int64_t)b * V;
   uint32_t* wt = a.wt + (int64_t)b * V;
   const float T = a.temperature[b], pres = a.presence[b], freq = a.frequency[b];
   const bool greedy = !(T > 0.f);
@@ -919,14 +961,27 @@ __global__ __launch_bounds__(1024) void k_sample(SampleArgs a) {
   mx = L.fred[0];
   for (int w = 1; w < SMP_THREADS / 64; ++w) mx = fmaxf(mx, L.fred[w]);
 
+  // keys and weights, and the top-level histogram of every candidate (the
+  // first selection starts from it)
+  for (int i = t; i < SMP_BINS; i += SMP_THREADS) {
+    L.cnt[i] = 0;
+    L.mass[i] = 0;
+  }
+  __syncthreads();
   unsigned long long n = 0, tot = 0;
 #pragma unroll 1
   for (int v = t; v < V; v += SMP_THREADS) {
     const float x = zval(v);
     const bool c = x == x;
     const uint32_t w = c ? (uint32_t)floor(exp((double)x - (double)mx) * 2147483648.0) : 0u;
-    key[v] = c ? (smp_order_key(x) << 16) | (uint64_t)(0xFFFF - v) : 0ull;
+    const uint32_t k = c ? (uint32_t)smp_order_key(x) : 0u;
+    key[v] = k;
     wt[v] = w;
+    if (c) {
+      const int d = (int)(k >> 20);   // bits 47..36 of the 48-bit key
+      atomicAdd(&L.cnt[d], 1u);
+      atomicAdd(&L.mass[d], (unsigned long long)w);
+    }
     n += c;
     tot += w;
   }
@@ -940,18 +995,23 @@ __global__ __launch_bounds__(1024) void k_sample(SampleArgs a) {
     const int k = greedy ? 1 : a.top_k[b];
     uint64_t lo = 1;
     unsigned long long S = tot;
-    if (k > 0 && (unsigned long long)k < n) lo = smp_select(key, wt, V, lo, false, (unsigned long long)k, &S, L);
+    bool ready = true;   // the histogram in LDS covers every candidate (key >= 1)
+    if (k > 0 && (unsigned long long)k < n) {
+      lo = smp_select(key, wt, V, lo, false, (unsigned long long)k, &S, L, ready);
+      ready = false;
+    }
     const float p = a.top_p[b];
     if (p < 1.f) {
       const double g = ceil((double)p * (double)S);
-      lo = smp_select(key, wt, V, lo, true, g < 1.0 ? 1ull : (unsigned long long)g, &S, L);
+      lo = smp_select(key, wt, V, lo, true, g < 1.0 ? 1ull : (unsigned long long)g, &S, L, ready);
+      ready = false;
     }
     float u = a.uniform[b];
     if (!(u >= 0.f)) u = 0.f;
     if (u >= 1.f) u = 0x1.fffffep-1f;
     const unsigned long long target = (unsigned long long)floor((double)u * (double)S);
     unsigned long long m;
-    const uint64_t kb = smp_select(key, wt, V, lo, true, target + 1, &m, L);
+    const uint64_t kb = smp_select(key, wt, V, lo, true, target + 1, &m, L, ready);
     id = 0xFFFF - (int)(kb & 0xFFFF);
     if (id >= V) {   // not reachable when every goal is within its set's total
       id = 0;

@@ -194,7 +194,7 @@ struct SampleArgs {
   const float* uniform;             // [B] draws in [0, 1)
   int* ids;
   uint32_t* err;
-  uint64_t* key;                    // [B][V] workspace: order keys (0 = not a candidate)
+  uint32_t* key;                    // [B][V] workspace: ordered bits of z (0 = not a candidate)
   uint32_t* wt;                     // [B][V] workspace: fixed-point weights
   int B, V;
 };
