@@ -325,6 +325,55 @@ def sample_timing(R, m, logits, occ, slots, pres, freq, dec, reps=20):
             "distinct_ids": int(torch.unique(ids).numel())}
 
 
+# ---------------------------------------------------------------- serving
+def serving(R, shape, m, max_b, n_tasks, new_tokens):
+    """The continuous-batching scheduler (rwkv7_sched over the GPU backend) on a
+    synthetic serving load: n_tasks prompts with the decode workload's length
+    mix, each generating new_tokens tokens with the adapter's sampling defaults
+    (temperature 1.0, top_p 0.3, top_k 0) and the workload's penalties, at most
+    max_b at once.  Wall time from the first round to the last task's end,
+    prefills included; generated tokens per second of it."""
+    import torch
+    import synth
+    wl = synth.WORKLOADS[f"decode_b{max_b}_{shape.name}"]
+    lens = synth.prompt_lengths(wl, n_tasks)
+    V = shape.vocab
+    occ = torch.zeros(m.n_slots * V, device="cuda")
+    sws = torch.zeros(R.rwkv7_sample_workspace_bytes(max_b, V), dtype=torch.uint8, device="cuda")
+    be = R.rwkv7_sched_gpu_backend(m.handle, m.pool, m.n_slots, occ, None, max_b, m.ws, sws)
+    s = R.rwkv7_sched_create(R.SchedConfig(max_b, 0, 0, 0, V), be)
+    for i in range(n_tasks):
+        prm = R.SchedParams(1.0, 0.3, 0, wl.presence, wl.frequency, wl.decay, new_tokens, -1, 9000 + i)
+        R.rwkv7_sched_submit(s, synth.prompt_tokens(wl, i, int(lens[i])).tolist(), prm)
+    torch.cuda.synchronize()
+    rounds = rows = seq = seq_tok = gen = 0
+    t0 = time.perf_counter()
+    for _ in range(n_tasks * (new_tokens + int(lens.max()) + 2)):   # every round makes progress
+        st = R.rwkv7_sched_step(s)
+        rounds += 1
+        rows += st.decode_rows + st.one_prefill_rows
+        seq += st.seq_prefills
+        seq_tok += st.seq_prefill_tokens
+        gen += st.decode_rows
+        R.rwkv7_sched_poll(s)
+        if st.active == 0 and st.queued == 0:
+            break
+    else:
+        raise RuntimeError("the scheduler did not drain its tasks")
+    dt = time.perf_counter() - t0
+    R.rwkv7_sched_free(s)
+    R.rwkv7_sched_gpu_backend_free(be)
+    if gen != n_tasks * new_tokens:
+        raise RuntimeError(f"scheduler generated {gen} tokens, expected {n_tasks * new_tokens}")
+    res = {"max_batch": max_b, "tasks": n_tasks, "new_tokens": new_tokens, "prompt_tokens": int(lens.sum()),
+           "seconds": round(dt, 3), "gen_tok_s": round(gen / dt, 1), "rounds": rounds,
+           "mean_rows_per_round": round(rows / rounds, 2), "seq_prefills": seq, "seq_prefill_tokens": seq_tok,
+           "ms_per_round": round(dt / rounds * 1e3, 3)}
+    log(f"[bench] scheduler max_batch={max_b}: {res['gen_tok_s']} generated tok/s over {rounds} rounds "
+        f"({res['mean_rows_per_round']} rows/round, {seq} sequence prefills)")
+    return res
+
+
 # ---------------------------------------------------------------- prefill
 def prefill(R, shape, m, Ts):
     import torch
@@ -393,6 +442,9 @@ def main():
     ap.add_argument("--prompt-len", type=int, default=0,
                     help="batched decode: fixed prompt length instead of the workload's 20-2000 "
                          "(profiling runs only; the decode step shapes do not change)")
+    ap.add_argument("--serve", default="64", help="scheduler max_batch values ('' = none)")
+    ap.add_argument("--serve-tasks", type=int, default=128)
+    ap.add_argument("--serve-new", type=int, default=256)
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -409,8 +461,9 @@ def main():
     shape = synth.R7_2B9
     Bs = [int(b) for b in args.batched.split(",") if b]
     Ts = [int(t) for t in args.prefill.split(",") if t]
-    n_slots = max([1] + Bs)
-    m, weights = build_model(R, shape, n_slots=n_slots, max_B=max([1] + Bs),
+    Ss = [int(b) for b in args.serve.split(",") if b]
+    n_slots = max([1] + Bs + Ss)
+    m, weights = build_model(R, shape, n_slots=n_slots, max_B=max([1] + Bs + Ss),
                              max_T=max([512] + Ts))
 
     dt, nnz, kb, run_step, slot, tok, logits = decode_b1(R, args, shape, m)
@@ -426,6 +479,7 @@ def main():
 
     batched_res = [batched(R, args, shape, m, B) for B in Bs]
     prefill_res = prefill(R, shape, m, Ts) if Ts else {}
+    serve_res = [serving(R, shape, m, B, args.serve_tasks, args.serve_new) for B in Ss]
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")
@@ -460,6 +514,7 @@ def main():
         "batched": batched_res + big_res,
         "sample_b1": samp_b1,
         "prefill": prefill_res,
+        "serving": serve_res,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -59,6 +59,54 @@ class Tensor(ctypes.Structure):
                 ("shape", ctypes.c_int64 * 4), ("data", ctypes.c_void_p)]
 
 
+# ---- scheduler structures (include/rwkv7_sched.h)
+TASK_QUEUED, TASK_PREFILL, TASK_READY, TASK_RUNNING, TASK_FINISHED = range(5)
+EV_TOKEN, EV_FINISHED = 1, 2
+FIN_LENGTH, FIN_STOP, FIN_ABORT = 1, 2, 3
+
+
+class SchedConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "max_batch", "max_prefill_count", "decode_prefill_ratio", "min_forward_seq_len", "vocab")]
+
+
+class SchedParams(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("top_p", ctypes.c_float), ("top_k", ctypes.c_int32),
+                ("presence", ctypes.c_float), ("frequency", ctypes.c_float), ("decay", ctypes.c_float),
+                ("max_new_tokens", ctypes.c_int32), ("stop_token", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+
+
+class SchedBatch(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("slots", ctypes.POINTER(ctypes.c_int32)),
+                ("tokens", ctypes.POINTER(ctypes.c_int32)), ("n_sample", ctypes.c_int32),
+                ("temperature", ctypes.POINTER(ctypes.c_float)), ("top_p", ctypes.POINTER(ctypes.c_float)),
+                ("top_k", ctypes.POINTER(ctypes.c_int32)), ("presence", ctypes.POINTER(ctypes.c_float)),
+                ("frequency", ctypes.POINTER(ctypes.c_float)), ("decay", ctypes.POINTER(ctypes.c_float)),
+                ("uniform", ctypes.POINTER(ctypes.c_float))]
+
+
+RESET_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int32)
+PREFILL_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                              ctypes.c_int32)
+STEP_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(SchedBatch),
+                           ctypes.POINTER(ctypes.c_int32))
+
+
+class SchedBackend(ctypes.Structure):
+    _fields_ = [("ctx", ctypes.c_void_p), ("reset", RESET_FN), ("prefill", PREFILL_FN), ("step", STEP_FN)]
+
+
+class SchedEvent(ctypes.Structure):
+    _fields_ = [("task", ctypes.c_int64), ("kind", ctypes.c_int32), ("value", ctypes.c_int32),
+                ("index", ctypes.c_int32), ("pad", ctypes.c_int32)]
+
+
+class SchedStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "decode_rows", "one_prefill_rows", "seq_prefills", "seq_prefill_tokens", "admitted", "finished",
+        "queued", "active")]
+
+
 _lib = None
 
 
@@ -94,6 +142,15 @@ def lib() -> ctypes.CDLL:
         "rwkv7_debug_cmix_buffers": [vp, vp, i32, P(vp), P(vp), P(vp), P(vp)],
         "rwkv7_time_kernel": [vp, vp, i64, i32, vp, vp, vp, i32, i32, i32, vp, u64, vp,
                               P(ctypes.c_double)],
+        "rwkv7_sched_create": [P(SchedConfig), P(SchedBackend), P(vp)],
+        "rwkv7_sched_free": [vp],
+        "rwkv7_sched_submit": [vp, P(i32), i32, P(SchedParams), P(i64)],
+        "rwkv7_sched_abort": [vp, i64],
+        "rwkv7_sched_step": [vp, P(SchedStats)],
+        "rwkv7_sched_poll": [vp, P(SchedEvent), i32, P(i32)],
+        "rwkv7_sched_task_state": [vp, i64, P(i32)],
+        "rwkv7_sched_gpu_backend": [vp, vp, i64, vp, vp, i32, vp, u64, vp, u64, vp, P(SchedBackend)],
+        "rwkv7_sched_gpu_backend_free": [P(SchedBackend)],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -291,6 +348,102 @@ def rwkv7_debug_cmix_buffers(model: int, ws, B: int) -> Tuple[int, int, int, int
     _check(lib().rwkv7_debug_cmix_buffers(model, ws.data_ptr(), B, *[ctypes.byref(o) for o in out]),
            "rwkv7_debug_cmix_buffers")
     return tuple(o.value for o in out)
+
+
+# ------------------------------------------------------------------ scheduler
+def sched_backend(reset, prefill, step) -> SchedBackend:
+    """A backend whose callbacks are Python callables (used by host-logic tests):
+    reset(slot); prefill(slot, tokens: list); step(slots, tokens, n_sample, params) -> ids,
+    where params maps temperature/top_p/top_k/presence/frequency/decay/uniform to lists of
+    n_sample values.  A callable that raises makes the round fail with RWKV7_EINVAL."""
+    names = ("temperature", "top_p", "top_k", "presence", "frequency", "decay", "uniform")
+
+    def c_reset(_ctx, slot):
+        try:
+            reset(slot)
+            return RWKV7_OK
+        except Exception:
+            return RWKV7_EINVAL
+
+    def c_prefill(_ctx, slot, toks, T):
+        try:
+            prefill(slot, toks[:T])
+            return RWKV7_OK
+        except Exception:
+            return RWKV7_EINVAL
+
+    def c_step(_ctx, bp, ids):
+        try:
+            b = bp.contents
+            S = b.n_sample
+            params = {n: getattr(b, n)[:S] for n in names}
+            out = step(b.slots[:b.B], b.tokens[:b.B], S, params)
+            for i in range(S):
+                ids[i] = int(out[i])
+            return RWKV7_OK
+        except Exception:
+            return RWKV7_EINVAL
+
+    be = SchedBackend(None, RESET_FN(c_reset), PREFILL_FN(c_prefill), STEP_FN(c_step))
+    be._keep = (be.reset, be.prefill, be.step)
+    return be
+
+
+def rwkv7_sched_create(cfg: SchedConfig, backend: SchedBackend) -> int:
+    h = ctypes.c_void_p()
+    _check(lib().rwkv7_sched_create(ctypes.byref(cfg), ctypes.byref(backend), ctypes.byref(h)),
+           "rwkv7_sched_create")
+    return h.value
+
+
+def rwkv7_sched_free(s: int):
+    _check(lib().rwkv7_sched_free(s), "rwkv7_sched_free")
+
+
+def rwkv7_sched_submit(s: int, prompt, params: SchedParams) -> int:
+    n = len(prompt)
+    arr = (ctypes.c_int32 * max(n, 1))(*[int(x) for x in prompt])
+    tid = ctypes.c_int64()
+    _check(lib().rwkv7_sched_submit(s, arr, n, ctypes.byref(params), ctypes.byref(tid)), "rwkv7_sched_submit")
+    return tid.value
+
+
+def rwkv7_sched_abort(s: int, task_id: int):
+    _check(lib().rwkv7_sched_abort(s, task_id), "rwkv7_sched_abort")
+
+
+def rwkv7_sched_step(s: int) -> SchedStats:
+    st = SchedStats()
+    _check(lib().rwkv7_sched_step(s, ctypes.byref(st)), "rwkv7_sched_step")
+    return st
+
+
+def rwkv7_sched_poll(s: int, cap: int = 4096):
+    """Pending events, oldest first, as (task, kind, value, index) tuples."""
+    buf = (SchedEvent * cap)()
+    n = ctypes.c_int32()
+    _check(lib().rwkv7_sched_poll(s, buf, cap, ctypes.byref(n)), "rwkv7_sched_poll")
+    return [(e.task, e.kind, e.value, e.index) for e in buf[:n.value]]
+
+
+def rwkv7_sched_task_state(s: int, task_id: int) -> int:
+    v = ctypes.c_int32()
+    _check(lib().rwkv7_sched_task_state(s, task_id, ctypes.byref(v)), "rwkv7_sched_task_state")
+    return v.value
+
+
+def rwkv7_sched_gpu_backend(model: int, pool, n_slots: int, occ_pool, forbidden, max_B: int, ws, sample_ws,
+                            stream=None) -> SchedBackend:
+    be = SchedBackend()
+    _check(lib().rwkv7_sched_gpu_backend(model, pool.data_ptr(), n_slots, _ptr(occ_pool), _ptr(forbidden),
+                                         max_B, ws.data_ptr(), ws.numel(), sample_ws.data_ptr(),
+                                         sample_ws.numel(), _stream(stream), ctypes.byref(be)),
+           "rwkv7_sched_gpu_backend")
+    return be
+
+
+def rwkv7_sched_gpu_backend_free(backend: SchedBackend):
+    _check(lib().rwkv7_sched_gpu_backend_free(ctypes.byref(backend)), "rwkv7_sched_gpu_backend_free")
 
 
 # ------------------------------------------------------------------ holder

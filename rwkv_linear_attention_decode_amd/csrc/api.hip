@@ -43,6 +43,9 @@ int hip_fail(hipError_t e, const char* what) {
 constexpr uint64_t ALIGN = 256;
 // shortest prefill chunk that takes the chunked WKV scan under the automatic choice
 constexpr int PREFILL_CHUNKED_MIN_T = 32;
+// decode graphs kept instantiated (least recently used evicted): a serving
+// loop's batch size wanders over 1 .. max_batch as tasks come and go
+constexpr size_t GRAPH_CACHE = 128;
 inline uint64_t align_up(uint64_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 inline int pad64(int x) { return (x + 63) / 64 * 64; }
 
@@ -729,6 +732,10 @@ std::vector<Expect> expected_tensors(const Dims& d) {
 
 }  // namespace
 
+// Library-internal entry points for the scheduler (sched.hip).
+int lib_fail(int code, const char* msg) { return fail(code, "%s", msg); }
+int lib_model_vocab(const rwkv7_model* m) { return m ? m->cfg.vocab : 0; }
+
 // ====================================================================== C ABI
 extern "C" {
 
@@ -962,7 +969,7 @@ int rwkv7_decode_step(rwkv7_model* m, void* pool, int64_t n_slots, int32_t B,
   auto it = m->graphs.find(key);
   if (it == m->graphs.end()) {
     if (!m->cap_stream) HIP_TRY(hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking), "hipStreamCreate");
-    if (m->graphs.size() >= 16) {
+    if (m->graphs.size() >= GRAPH_CACHE) {
       auto oldest = m->graphs.begin();
       for (auto j = m->graphs.begin(); j != m->graphs.end(); ++j)
         if (j->second.last_use < oldest->second.last_use) oldest = j;

@@ -201,6 +201,12 @@ struct SampleArgs {
 constexpr int SAMPLE_MAX_V = 65536;
 hipError_t launch_sample(const SampleArgs& a, hipStream_t st);
 
+// api.hip, for the scheduler: set the thread's last-error text and return
+// `code`; a loaded model's vocabulary size.
+struct rwkv7_model;
+int lib_fail(int code, const char* msg);
+int lib_model_vocab(const rwkv7_model* m);
+
 // ---------------------------------------------------------------- WKV
 struct WkvArgs {
   float* pool;
