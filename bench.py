@@ -326,25 +326,52 @@ def sample_timing(R, m, logits, occ, slots, pres, freq, dec, reps=20):
 
 
 # ---------------------------------------------------------------- serving
-def serving(R, shape, m, max_b, n_tasks, new_tokens):
+def serving(R, shape, m, max_b, n_tasks, new_tokens, system_len=0, use_cache=False):
     """The continuous-batching scheduler (rwkv7_sched over the GPU backend) on a
     synthetic serving load: n_tasks prompts with the decode workload's length
     mix, each generating new_tokens tokens with the adapter's sampling defaults
     (temperature 1.0, top_p 0.3, top_k 0) and the workload's penalties, at most
     max_b at once.  Wall time from the first round to the last task's end,
-    prefills included; generated tokens per second of it."""
+    prefills included; generated tokens per second of it.
+    system_len > 0: every prompt is one shared system_len-token system prompt
+    followed by a suffix a tenth of the mix's length; use_cache attaches a
+    prefix-state cache holding the system prompt's state, stored before the
+    timed region."""
     import torch
     import synth
     wl = synth.WORKLOADS[f"decode_b{max_b}_{shape.name}"]
     lens = synth.prompt_lengths(wl, n_tasks)
+    if system_len:
+        lens = np.maximum(lens // 10, 2)
     V = shape.vocab
     occ = torch.zeros(m.n_slots * V, device="cuda")
     sws = torch.zeros(R.rwkv7_sample_workspace_bytes(max_b, V), dtype=torch.uint8, device="cuda")
     be = R.rwkv7_sched_gpu_backend(m.handle, m.pool, m.n_slots, occ, None, max_b, m.ws, sws)
+    system = synth.prefill_tokens(wl, system_len).tolist() if system_len else []
+    cache = arena = None
+    restore = None
+    if use_cache:
+        snap = R.rwkv7_snapshot_bytes(m.cfg)
+        arena = torch.empty(4 * ((snap + 255) // 256 * 256), dtype=torch.uint8, device="cuda")
+        cache = R.rwkv7_prefix_cache_create(m.handle, arena)
+        m.reset(i32([0]))
+        m.prefill(0, i32(system))
+        R.rwkv7_prefix_cache_store(cache, m.pool, m.n_slots, 0, system)
+        # restore cost: one snapshot copied into a slot (read + write of the snapshot)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        R.rwkv7_prefix_cache_lookup(cache, m.pool, m.n_slots, 1, system)
+        e0.record()
+        for _ in range(20):
+            R.rwkv7_prefix_cache_lookup(cache, m.pool, m.n_slots, 1, system)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 20
+        restore = {"snapshot_bytes": snap, "us": round(us, 2), "gbs": round(2 * snap / (us * 1e-6) / 1e9, 1)}
+        R.rwkv7_sched_gpu_backend_set_cache(be, cache)
     s = R.rwkv7_sched_create(R.SchedConfig(max_b, 0, 0, 0, V), be)
     for i in range(n_tasks):
         prm = R.SchedParams(1.0, 0.3, 0, wl.presence, wl.frequency, wl.decay, new_tokens, -1, 9000 + i)
-        R.rwkv7_sched_submit(s, synth.prompt_tokens(wl, i, int(lens[i])).tolist(), prm)
+        R.rwkv7_sched_submit(s, system + synth.prompt_tokens(wl, i, int(lens[i])).tolist(), prm)
     torch.cuda.synchronize()
     rounds = rows = seq = seq_tok = gen = 0
     t0 = time.perf_counter()
@@ -361,16 +388,23 @@ def serving(R, shape, m, max_b, n_tasks, new_tokens):
     else:
         raise RuntimeError("the scheduler did not drain its tasks")
     dt = time.perf_counter() - t0
+    restored, prefilled = R.rwkv7_sched_gpu_backend_counts(be)
     R.rwkv7_sched_free(s)
     R.rwkv7_sched_gpu_backend_free(be)
+    if cache:
+        R.rwkv7_prefix_cache_free(cache)
     if gen != n_tasks * new_tokens:
         raise RuntimeError(f"scheduler generated {gen} tokens, expected {n_tasks * new_tokens}")
-    res = {"max_batch": max_b, "tasks": n_tasks, "new_tokens": new_tokens, "prompt_tokens": int(lens.sum()),
+    res = {"max_batch": max_b, "tasks": n_tasks, "new_tokens": new_tokens,
+           "prompt_tokens": int(lens.sum()) + n_tasks * len(system), "system_prompt": len(system),
+           "prefix_cache": use_cache, "tokens_restored": restored, "tokens_prefilled": prefilled,
+           "snapshot_restore": restore,
            "seconds": round(dt, 3), "gen_tok_s": round(gen / dt, 1), "rounds": rounds,
            "mean_rows_per_round": round(rows / rounds, 2), "seq_prefills": seq, "seq_prefill_tokens": seq_tok,
            "ms_per_round": round(dt / rounds * 1e3, 3)}
-    log(f"[bench] scheduler max_batch={max_b}: {res['gen_tok_s']} generated tok/s over {rounds} rounds "
-        f"({res['mean_rows_per_round']} rows/round, {seq} sequence prefills)")
+    log(f"[bench] scheduler max_batch={max_b} system={len(system)} cache={use_cache}: {res['gen_tok_s']} "
+        f"generated tok/s over {rounds} rounds ({res['mean_rows_per_round']} rows/round, {seq} sequence "
+        f"prefills, {prefilled} tokens prefilled, {restored} restored)")
     return res
 
 
@@ -445,6 +479,8 @@ def main():
     ap.add_argument("--serve", default="64", help="scheduler max_batch values ('' = none)")
     ap.add_argument("--serve-tasks", type=int, default=128)
     ap.add_argument("--serve-new", type=int, default=256)
+    ap.add_argument("--serve-system", type=int, default=1024,
+                    help="shared system-prompt length of the prefix-cache serving runs (0 = none)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -480,6 +516,11 @@ def main():
     batched_res = [batched(R, args, shape, m, B) for B in Bs]
     prefill_res = prefill(R, shape, m, Ts) if Ts else {}
     serve_res = [serving(R, shape, m, B, args.serve_tasks, args.serve_new) for B in Ss]
+    for B in Ss[:1]:
+        if args.serve_system > 0:
+            for use_cache in (False, True):
+                serve_res.append(serving(R, shape, m, B, args.serve_tasks, args.serve_new,
+                                         args.serve_system, use_cache))
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")

@@ -186,6 +186,18 @@ int rwkv7_sched_gpu_backend(rwkv7_model* model, void* pool, int64_t n_slots, flo
                             rwkv7_sched_backend* out);
 int rwkv7_sched_gpu_backend_free(rwkv7_sched_backend* backend);
 
+/* Attach a prefix-state cache (include/rwkv7_prefix.h; NULL detaches) to a
+ * GPU backend.  Its sequence prefills then restore the longest cached prefix
+ * of prompt[0 .. n-1), prefill only the rest, and store the result under
+ * prompt[0 .. n-1), so a prompt that extends an earlier one (the next turn
+ * of a conversation, a shared system prompt stored by the caller) skips the
+ * tokens already consumed.  *tokens_restored / *tokens_prefilled (either may
+ * be NULL) of rwkv7_sched_gpu_backend_counts report the totals. */
+struct rwkv7_prefix_cache;
+int rwkv7_sched_gpu_backend_set_cache(rwkv7_sched_backend* backend, struct rwkv7_prefix_cache* cache);
+int rwkv7_sched_gpu_backend_counts(const rwkv7_sched_backend* backend, int64_t* tokens_restored,
+                                   int64_t* tokens_prefilled);
+
 #ifdef __cplusplus
 }
 #endif

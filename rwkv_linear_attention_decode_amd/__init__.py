@@ -107,6 +107,11 @@ class SchedStats(ctypes.Structure):
         "queued", "active")]
 
 
+class PrefixStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("lookups", "hits", "hit_tokens", "stores", "offloads", "drops")] + \
+               [(n, ctypes.c_int32) for n in ("device_entries", "host_entries", "device_capacity", "host_capacity")]
+
+
 _lib = None
 
 
@@ -151,6 +156,16 @@ def lib() -> ctypes.CDLL:
         "rwkv7_sched_task_state": [vp, i64, P(i32)],
         "rwkv7_sched_gpu_backend": [vp, vp, i64, vp, vp, i32, vp, u64, vp, u64, vp, P(SchedBackend)],
         "rwkv7_sched_gpu_backend_free": [P(SchedBackend)],
+        "rwkv7_sched_gpu_backend_set_cache": [P(SchedBackend), vp],
+        "rwkv7_sched_gpu_backend_counts": [P(SchedBackend), P(i64), P(i64)],
+        "rwkv7_snapshot_bytes": [P(Config), P(u64)],
+        "rwkv7_slot_export": [vp, vp, i64, i32, vp, vp],
+        "rwkv7_slot_import": [vp, vp, i64, i32, vp, vp],
+        "rwkv7_prefix_cache_create": [vp, vp, u64, vp, u64, P(vp)],
+        "rwkv7_prefix_cache_free": [vp],
+        "rwkv7_prefix_cache_store": [vp, vp, i64, i32, P(i32), i32, vp],
+        "rwkv7_prefix_cache_lookup": [vp, vp, i64, i32, P(i32), i32, P(i32), vp],
+        "rwkv7_prefix_cache_stats": [vp, P(PrefixStats)],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -444,6 +459,75 @@ def rwkv7_sched_gpu_backend(model: int, pool, n_slots: int, occ_pool, forbidden,
 
 def rwkv7_sched_gpu_backend_free(backend: SchedBackend):
     _check(lib().rwkv7_sched_gpu_backend_free(ctypes.byref(backend)), "rwkv7_sched_gpu_backend_free")
+
+
+def rwkv7_sched_gpu_backend_set_cache(backend: SchedBackend, cache: Optional[int]):
+    _check(lib().rwkv7_sched_gpu_backend_set_cache(ctypes.byref(backend), cache), "rwkv7_sched_gpu_backend_set_cache")
+
+
+def rwkv7_sched_gpu_backend_counts(backend: SchedBackend) -> Tuple[int, int]:
+    """(tokens restored from the prefix cache, tokens prefilled) so far."""
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().rwkv7_sched_gpu_backend_counts(ctypes.byref(backend), ctypes.byref(a), ctypes.byref(b)),
+           "rwkv7_sched_gpu_backend_counts")
+    return a.value, b.value
+
+
+# ------------------------------------------------------------------ snapshots, prefix cache
+def rwkv7_snapshot_bytes(cfg: Config) -> int:
+    v = ctypes.c_uint64()
+    _check(lib().rwkv7_snapshot_bytes(ctypes.byref(cfg), ctypes.byref(v)), "rwkv7_snapshot_bytes")
+    return v.value
+
+
+def rwkv7_slot_export(model: int, pool, n_slots: int, slot: int, dst, stream=None):
+    """Copy one slot (state, then its int64 step counter) into dst (a uint8 tensor, device or pinned host)."""
+    _check(lib().rwkv7_slot_export(model, pool.data_ptr(), n_slots, slot, dst.data_ptr(), _stream(stream)),
+           "rwkv7_slot_export")
+
+
+def rwkv7_slot_import(model: int, pool, n_slots: int, slot: int, src, stream=None):
+    _check(lib().rwkv7_slot_import(model, pool.data_ptr(), n_slots, slot, src.data_ptr(), _stream(stream)),
+           "rwkv7_slot_import")
+
+
+def rwkv7_prefix_cache_create(model: int, arena, host_arena=None) -> int:
+    """A prefix-state cache over a device uint8 tensor and an optional pinned host one."""
+    h = ctypes.c_void_p()
+    _check(lib().rwkv7_prefix_cache_create(model, arena.data_ptr(), arena.numel(), _ptr(host_arena),
+                                           0 if host_arena is None else host_arena.numel(), ctypes.byref(h)),
+           "rwkv7_prefix_cache_create")
+    return h.value
+
+
+def rwkv7_prefix_cache_free(cache: int):
+    _check(lib().rwkv7_prefix_cache_free(cache), "rwkv7_prefix_cache_free")
+
+
+def _tok_array(tokens):
+    n = len(tokens)
+    return (ctypes.c_int32 * max(n, 1))(*[int(x) for x in tokens]), n
+
+
+def rwkv7_prefix_cache_store(cache: int, pool, n_slots: int, slot: int, tokens, stream=None):
+    arr, n = _tok_array(tokens)
+    _check(lib().rwkv7_prefix_cache_store(cache, pool.data_ptr(), n_slots, slot, arr, n, _stream(stream)),
+           "rwkv7_prefix_cache_store")
+
+
+def rwkv7_prefix_cache_lookup(cache: int, pool, n_slots: int, slot: int, tokens, stream=None) -> int:
+    """Restore the longest cached prefix of tokens into the slot; its length (0: none)."""
+    arr, n = _tok_array(tokens)
+    m = ctypes.c_int32()
+    _check(lib().rwkv7_prefix_cache_lookup(cache, pool.data_ptr(), n_slots, slot, arr, n, ctypes.byref(m),
+                                           _stream(stream)), "rwkv7_prefix_cache_lookup")
+    return m.value
+
+
+def rwkv7_prefix_cache_stats(cache: int) -> PrefixStats:
+    st = PrefixStats()
+    _check(lib().rwkv7_prefix_cache_stats(cache, ctypes.byref(st)), "rwkv7_prefix_cache_stats")
+    return st
 
 
 # ------------------------------------------------------------------ holder

@@ -735,6 +735,7 @@ std::vector<Expect> expected_tensors(const Dims& d) {
 // Library-internal entry points for the scheduler (sched.hip).
 int lib_fail(int code, const char* msg) { return fail(code, "%s", msg); }
 int lib_model_vocab(const rwkv7_model* m) { return m ? m->cfg.vocab : 0; }
+int64_t lib_model_slot_floats(const rwkv7_model* m) { return m ? m->d.slot_floats : 0; }
 
 // ====================================================================== C ABI
 extern "C" {

@@ -206,6 +206,7 @@ hipError_t launch_sample(const SampleArgs& a, hipStream_t st);
 struct rwkv7_model;
 int lib_fail(int code, const char* msg);
 int lib_model_vocab(const rwkv7_model* m);
+int64_t lib_model_slot_floats(const rwkv7_model* m);
 
 // ---------------------------------------------------------------- WKV
 struct WkvArgs {

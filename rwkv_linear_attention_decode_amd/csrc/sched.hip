@@ -10,6 +10,7 @@
 // ordering row indices, not swapping state.
 #include "launch.h"
 #include "../../include/rwkv7_sched.h"
+#include "../../include/rwkv7_prefix.h"
 
 #include <hip/hip_runtime.h>
 
@@ -363,6 +364,8 @@ struct GpuBackend {
   float* d_logits = nullptr;   // [max_B * V]
   int32_t* d_tok = nullptr;    // prefill tokens
   int tok_cap = 0;
+  rwkv7_prefix_cache* cache = nullptr;
+  int64_t restored = 0, prefilled = 0;
 };
 
 int gb_hip(hipError_t e, const char* what) {
@@ -383,8 +386,18 @@ int gb_reset(void* ctx, int32_t slot) {
   return gb_hip(hipStreamSynchronize(g->st), "reset sync");
 }
 
-int gb_prefill(void* ctx, int32_t slot, const int32_t* tokens, int32_t T) {
+int gb_prefill(void* ctx, int32_t slot, const int32_t* all_tokens, int32_t T_all) {
   GpuBackend* g = (GpuBackend*)ctx;
+  int32_t start = 0;
+  if (g->cache) {
+    int rc = rwkv7_prefix_cache_lookup(g->cache, g->pool, g->n_slots, slot, all_tokens, T_all, &start, g->st);
+    if (rc) return rc;
+  }
+  g->restored += start;
+  const int32_t* tokens = all_tokens + start;
+  const int32_t T = T_all - start;
+  if (T == 0) return gb_hip(hipStreamSynchronize(g->st), "prefill sync");
+  g->prefilled += T;
   if (T > g->tok_cap) {
     if (g->d_tok) hipFree(g->d_tok);
     g->d_tok = nullptr;
@@ -398,6 +411,10 @@ int gb_prefill(void* ctx, int32_t slot, const int32_t* tokens, int32_t T) {
   if (rc) return rc;
   rc = rwkv7_prefill_seq(g->model, g->pool, g->n_slots, slot, g->d_tok, T, g->ws, g->ws_bytes, g->st);
   if (rc) return rc;
+  if (g->cache) {
+    rc = rwkv7_prefix_cache_store(g->cache, g->pool, g->n_slots, slot, all_tokens, T_all, g->st);
+    if (rc) return rc;
+  }
   return gb_hip(hipStreamSynchronize(g->st), "prefill sync");
 }
 
@@ -493,6 +510,23 @@ int rwkv7_sched_gpu_backend(rwkv7_model* model, void* pool, int64_t n_slots, flo
   out->reset = gb_reset;
   out->prefill = gb_prefill;
   out->step = gb_step;
+  return RWKV7_OK;
+}
+
+int rwkv7_sched_gpu_backend_set_cache(rwkv7_sched_backend* backend, rwkv7_prefix_cache* cache) {
+  if (!backend || backend->step != gb_step || !backend->ctx)
+    return sfail(RWKV7_EINVAL, "not a backend made by rwkv7_sched_gpu_backend");
+  ((GpuBackend*)backend->ctx)->cache = cache;
+  return RWKV7_OK;
+}
+
+int rwkv7_sched_gpu_backend_counts(const rwkv7_sched_backend* backend, int64_t* tokens_restored,
+                                   int64_t* tokens_prefilled) {
+  if (!backend || backend->step != gb_step || !backend->ctx)
+    return sfail(RWKV7_EINVAL, "not a backend made by rwkv7_sched_gpu_backend");
+  const GpuBackend* g = (const GpuBackend*)backend->ctx;
+  if (tokens_restored) *tokens_restored = g->restored;
+  if (tokens_prefilled) *tokens_prefilled = g->prefilled;
   return RWKV7_OK;
 }
 

@@ -108,3 +108,10 @@ def test_load_rejects_bad_tables_before_touching_memory():
     rc = L.rwkv7_load(ctypes.byref(cfg), arr, 1, ctypes.c_void_p(0x1000), big, None, ctypes.byref(h))
     assert rc in (R.RWKV7_EINVAL, R.RWKV7_ESHAPE)
     assert h.value is None
+
+
+def test_snapshot_bytes_formula():
+    cfg = R.make_config(synth.TINY)
+    assert R.rwkv7_snapshot_bytes(cfg) == R.rwkv7_slot_floats(cfg) * 4 + 8
+    cfg = R.make_config(synth.R7_2B9)
+    assert R.rwkv7_snapshot_bytes(cfg) == 32 * (2 * 2560 + 40 * 64 * 64) * 4 + 8
