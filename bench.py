@@ -45,12 +45,25 @@ def log(*a):
 
 
 # ---------------------------------------------------------------- algorithmic bytes
-def class_bytes(s, B: int, nnz: int, sparse: bool, fused_value: bool = False):
+def class_bytes(s, B: int, nnz: int, sparse: bool, fused_value: bool = False, int8: bool = False):
     """Compulsory HBM bytes per launch of each kernel class for B decode rows:
     every weight read once, activations / state read and written once.  With
     the value fused into the key projection (B <= 2) the active value rows
-    count in that kernel, and the fold only moves the residual."""
+    count in that kernel, and the fold only moves the residual.  int8: the
+    GEMV-streamed matrices at one byte per weight plus a 4-byte scale per row
+    (the adapters' second stage, read by the WKV kernel, stays fp16)."""
     C, F, V, H = s.n_embd, s.ffn, s.vocab, s.n_head
+    if int8:
+        b = class_bytes(s, B, nnz, sparse, fused_value)
+        Din = s.d_w + s.d_a + s.d_v + s.d_g
+        n_in = 3 * C + Din
+        b["proj_in"] -= n_in * C - n_in * 4
+        b["proj_out"] -= C * C - C * 4
+        b["cmix_key"] -= F * C - F * 4
+        if fused_value:
+            b["cmix_key"] -= nnz * C - nnz * 4
+        b["head"] -= V * C - V * 4
+        return b
     Din = s.d_w + s.d_a + s.d_v + s.d_g
     n_in = 3 * C + Din
     ns = max(1, min(32, -(-512 // (C // 64))))
@@ -79,8 +92,9 @@ def class_flops(s, B: int):
             "cmix_key": 2 * B * F * C, "cmix_value": 2 * B * F * C, "head": 2 * B * V * C}
 
 
-def step_bytes(s, B, nnz, sparse):
-    cb = class_bytes(s, B, nnz, sparse)   # the same total with or without the fused value
+def step_bytes(s, B, nnz, sparse, int8=False):
+    # the same total with or without the fused value (int8 applies with it)
+    cb = class_bytes(s, B, nnz, sparse, fused_value=int8, int8=int8)
     L = s.n_layer
     per_layer = 2 * cb["ln_mix"] + cb["proj_in"] + cb["wkv"] + cb["proj_out"] + cb["cmix_key"] + cb["cmix_value"]
     greedy = B * s.vocab * 4 * 3   # logits read, occurrences read + written
@@ -217,6 +231,50 @@ def roofline_b1(R, shape, m, kb, nnz, slot, tok, logits):
             "kernel": kname, "class": dom,
             "bytes_per_launch": int(cb[dom]), "avg_launch_us": round(avg_ms * 1e3, 3),
             "launches_per_step": kb[dom]["launches_per_step"]}
+
+
+def int8_b1(R, args, shape, m, run_step, slot, tok, logits):
+    """The B=1 workload with the int8 weight route (rwkv7_quantize_int8 +
+    RWKV7_OPT_INT8): the same steps, timed the same way, and its dominant
+    kernel class against the HBM roofline with the int8 algorithmic bytes."""
+    import torch
+    buf = torch.empty(R.rwkv7_int8_bytes(m.cfg), dtype=torch.uint8, device="cuda")
+    R.rwkv7_quantize_int8(m.handle, buf)
+    R.rwkv7_set_option(m.handle, R.OPT_INT8, 1)
+    try:
+        for _ in range(args.warmup):
+            run_step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            run_step()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        if m.poll_error():
+            raise RuntimeError("device error flags during the int8 decode")
+        nnz = measure_active_fraction(R, m, 1)
+        kb = kernel_breakdown(R, m, 1, run_step)
+        cb = class_bytes(shape, 1, nnz, True, True, int8=True)
+        dom = max((k for k in kb if k in cb and k != "other"), key=lambda k: kb[k]["ms_per_step"])
+        cls = R.K_NAMES.index(dom)
+        layer, iters = (shape.n_layer, 200) if dom == "head" else (-1, 8)
+        avg_ms = R.rwkv7_time_kernel(m.handle, m.pool, m.n_slots, slot, tok, logits, cls, layer, iters, m.ws)
+        gbs = cb[dom] / (avg_ms * 1e-3) / 1e9
+        ms = dt / args.steps * 1e3
+        sb = step_bytes(shape, 1, nnz, True, int8=True)
+    finally:
+        R.rwkv7_set_option(m.handle, R.OPT_INT8, 0)
+    del buf
+    res = {"tok_s": round(args.steps / dt, 1), "ms_per_step": round(ms, 4), "step_bytes": int(sb),
+           "step_gbs": round(sb / (ms * 1e-3) / 1e9, 1),
+           "step_hbm_frac": round(sb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "roofline": {"bound": "hbm", "class": dom, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": int(cb[dom]),
+                        "avg_launch_us": round(avg_ms * 1e3, 3)},
+           "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in kb.items()}}
+    log(f"[bench] B=1 int8 weights: {res['tok_s']} tok/s, {ms:.3f} ms/step, step {res['step_gbs']} GB/s; "
+        f"dominant {dom} {res['roofline']['achieved']} GB/s")
+    return res
 
 
 # ---------------------------------------------------------------- batched decode
@@ -481,6 +539,8 @@ def main():
     ap.add_argument("--serve-new", type=int, default=256)
     ap.add_argument("--serve-system", type=int, default=1024,
                     help="shared system-prompt length of the prefix-cache serving runs (0 = none)")
+    ap.add_argument("--no-int8", dest="int8", action="store_false",
+                    help="skip the B=1 run on int8 weights")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -508,6 +568,7 @@ def main():
     roof = roofline_b1(R, shape, m, kb, nnz, slot, tok, logits)
     log(f"[bench] dominant kernel {roof['class']}: {roof['avg_launch_us']} us/launch, "
         f"{roof['achieved']} GB/s ({roof['frac'] * 100:.1f}% of HBM peak)")
+    i8 = int8_b1(R, args, shape, m, run_step, slot, tok, logits) if args.int8 else None
     pen = torch.ones(1, device="cuda")
     samp_b1 = sample_timing(R, m, logits, torch.zeros(m.n_slots, shape.vocab, device="cuda"), slot, pen, pen,
                             pen * 0.996)
@@ -554,6 +615,7 @@ def main():
                         "launches_per_step": v["launches_per_step"]} for k, v in kb.items()},
         "batched": batched_res + big_res,
         "sample_b1": samp_b1,
+        "int8_b1": i8,
         "prefill": prefill_res,
         "serving": serve_res,
         "cpu_baseline": cpu,

@@ -215,6 +215,33 @@ int rwkv7_sample(int32_t B, int32_t V, const float* logits, float* occ_pool, int
                  const int32_t* top_k, const uint8_t* forbidden, const float* uniform,
                  int32_t* ids_out, void* ws, uint64_t ws_bytes, void* stream);
 
+/* ---- int8 weights (small-batch decode) ----
+ * The Albatross article (RWKV-Runner backend, "boundaries and follow-up
+ * route") names int8 quantised weights as a performance item it leaves out,
+ * without a scheme.  A single-token step streams every weight once, so this
+ * build offers symmetric per-row int8 copies of the matrices the small-batch
+ * path streams: the fused r | k | v | adapter-input matrix, W_o, the channel-mix
+ * key, the channel-mix value (per hidden unit, as the sparse path reads it)
+ * and the head.  Per row: m = max |w| of the packed fp16 row, s = m / 127 in
+ * fp32, code = rint(w / s) (ties to even) clamped to [-127, 127], 0 where
+ * s = 0; the weight used is code * s.  Bytes hold code + 128.  The adapters'
+ * second stage and the embedding stay fp16; larger batches and prefill keep
+ * the fp16 MFMA path.
+ *
+ * rwkv7_int8_bytes: size of the caller's buffer for those copies.
+ * rwkv7_quantize_int8: fill it from the packed weights (queued on `stream`;
+ * the buffer must stay allocated while the model is used with
+ * RWKV7_OPT_INT8 = 1).  ESHAPE for a short buffer. */
+int rwkv7_int8_bytes(const rwkv7_config* cfg, uint64_t* bytes);
+int rwkv7_quantize_int8(rwkv7_model* model, void* buf, uint64_t bytes, void* stream);
+
+/* Device addresses of one int8 matrix for tests: which = 0 fused input
+ * matrix, 1 W_o, 2 channel-mix key, 3 channel-mix value (hidden-major) of
+ * `layer`, 4 the head; *rows x *K bytes (code + 128) and *rows fp32 scales.
+ * ENOTSUP before rwkv7_quantize_int8. */
+int rwkv7_debug_int8_matrix(const rwkv7_model* model, int32_t layer, int32_t which, const void** codes,
+                            const float** scales, int64_t* rows, int32_t* K);
+
 /* ---- errors ---- */
 
 /* Synchronise `stream`, read and clear the sticky device error word at the
@@ -260,6 +287,8 @@ const char* rwkv7_last_error(void);
 #define RWKV7_OPT_GEMM_PLAN_CMIX_VALUE 12 /* dense channel-mix value */
 #define RWKV7_OPT_GEMM_PLAN_HEAD 13       /* output head */
 
+#define RWKV7_OPT_INT8 15  /* 1: decode steps of B <= 2 on the GEMV path stream the int8 copies made
+                              by rwkv7_quantize_int8 (ENOTSUP before it); 0 (default): fp16 */
 int rwkv7_set_option(rwkv7_model* model, int32_t key, int64_t value);
 int rwkv7_get_option(const rwkv7_model* model, int32_t key, int64_t* value);
 

@@ -70,3 +70,23 @@ def int8_weights(weights: Dict[str, np.ndarray], n_layer: int) -> Dict[str, np.n
         out[p + "ffn.value.weight"] = dequantize_rows(*quantize_rows(np.asarray(wv).T)).T
     out["head.weight"] = dequantize_rows(*quantize_rows(weights["head.weight"]))
     return out
+
+
+class Int8View:
+    """The weight table of int8_weights, dequantising each int8-route matrix
+    when it is read (for shapes whose fp64 copies would not fit at once)."""
+
+    def __init__(self, weights: Dict[str, np.ndarray], n_layer: int):
+        self.w = weights
+        self.rowwise = {f"blocks.{l}.{n}" for l in range(n_layer) for n in INT8_ROWWISE} | {"head.weight"}
+        self.colwise = {f"blocks.{l}.ffn.value.weight" for l in range(n_layer)}
+
+    def __getitem__(self, name: str) -> np.ndarray:
+        if name in self.rowwise:
+            return dequantize_rows(*quantize_rows(self.w[name]))
+        if name in self.colwise:
+            return dequantize_rows(*quantize_rows(np.asarray(self.w[name]).T)).T
+        return self.w[name]
+
+    def __contains__(self, name: str) -> bool:
+        return name in self.w

@@ -32,6 +32,7 @@ OPT_GEMM_PLAN_CMIX_KEY = 11
 OPT_GEMM_PLAN_CMIX_VALUE = 12
 OPT_GEMM_PLAN_HEAD = 13
 OPT_PREFILL_SCAN = 14
+OPT_INT8 = 15
 
 
 def gemm_plan_code(tm, tn, ks, pipe=0, split=0):
@@ -158,6 +159,9 @@ def lib() -> ctypes.CDLL:
         "rwkv7_sched_gpu_backend_free": [P(SchedBackend)],
         "rwkv7_sched_gpu_backend_set_cache": [P(SchedBackend), vp],
         "rwkv7_sched_gpu_backend_counts": [P(SchedBackend), P(i64), P(i64)],
+        "rwkv7_int8_bytes": [P(Config), P(u64)],
+        "rwkv7_quantize_int8": [vp, vp, u64, vp],
+        "rwkv7_debug_int8_matrix": [vp, i32, i32, P(vp), P(vp), P(i64), P(i32)],
         "rwkv7_snapshot_bytes": [P(Config), P(u64)],
         "rwkv7_slot_export": [vp, vp, i64, i32, vp, vp],
         "rwkv7_slot_import": [vp, vp, i64, i32, vp, vp],
@@ -471,6 +475,26 @@ def rwkv7_sched_gpu_backend_counts(backend: SchedBackend) -> Tuple[int, int]:
     _check(lib().rwkv7_sched_gpu_backend_counts(ctypes.byref(backend), ctypes.byref(a), ctypes.byref(b)),
            "rwkv7_sched_gpu_backend_counts")
     return a.value, b.value
+
+
+# ------------------------------------------------------------------ int8 weights
+def rwkv7_int8_bytes(cfg: Config) -> int:
+    v = ctypes.c_uint64()
+    _check(lib().rwkv7_int8_bytes(ctypes.byref(cfg), ctypes.byref(v)), "rwkv7_int8_bytes")
+    return v.value
+
+
+def rwkv7_quantize_int8(model: int, buf, stream=None):
+    """Fill ``buf`` (a device uint8 tensor of rwkv7_int8_bytes) with the int8 copies."""
+    _check(lib().rwkv7_quantize_int8(model, buf.data_ptr(), buf.numel(), _stream(stream)), "rwkv7_quantize_int8")
+
+
+def rwkv7_debug_int8_matrix(model: int, layer: int, which: int) -> Tuple[int, int, int, int]:
+    """(codes address, scales address, rows, K) of one int8 matrix."""
+    c, s_, r, k = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_int64(), ctypes.c_int32()
+    _check(lib().rwkv7_debug_int8_matrix(model, layer, which, ctypes.byref(c), ctypes.byref(s_), ctypes.byref(r),
+                                         ctypes.byref(k)), "rwkv7_debug_int8_matrix")
+    return c.value, s_.value, r.value, k.value
 
 
 # ------------------------------------------------------------------ snapshots, prefix cache

@@ -98,6 +98,47 @@ struct Packed {
   uint64_t bytes;
 };
 
+// int8 copies of the matrices the small-batch GEMV path streams: per-row
+// symmetric codes stored as code + 128, and fp32 row scales.
+struct Q8Layer {
+  uint8_t *w_in, *w_o, *w_key, *w_val;
+  float *s_in, *s_o, *s_key, *s_val;
+};
+struct Q8 {
+  uint8_t* head;
+  float* s_head;
+  std::vector<Q8Layer> layers;
+  uint64_t bytes;
+};
+
+// With base == nullptr only the size is computed.
+Q8 q8_layout(const Dims& d, char* base) {
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) -> char* {
+    char* p = base ? base + off : nullptr;
+    off = align_up(off + bytes);
+    return p;
+  };
+  const uint64_t C = d.C, F = d.F, V = d.V;
+  Q8 q;
+  q.head = (uint8_t*)take(V * C);
+  q.s_head = (float*)take(V * 4);
+  for (int l = 0; l < d.L; ++l) {
+    Q8Layer y;
+    y.w_in = (uint8_t*)take((uint64_t)d.Nin * C);
+    y.s_in = (float*)take((uint64_t)d.Nin * 4);
+    y.w_o = (uint8_t*)take(C * C);
+    y.s_o = (float*)take(C * 4);
+    y.w_key = (uint8_t*)take(F * C);
+    y.s_key = (float*)take(F * 4);
+    y.w_val = (uint8_t*)take(F * C);
+    y.s_val = (float*)take(F * 4);
+    q.layers.push_back(y);
+  }
+  q.bytes = off;
+  return q;
+}
+
 // With base == nullptr only the size is computed.
 Packed pack_layout(const Dims& d, char* base) {
   uint64_t off = 0;
@@ -233,7 +274,9 @@ struct rwkv7_model {
   Dims d;
   Packed pk;
   int64_t opt_graph = 1, opt_gemv_max = 2, opt_sparse_max = 4, opt_timing = 0, opt_chunk = 2048,
-          opt_fuse_ln = 1, opt_fuse_value = 1, opt_prefill_scan = 0;
+          opt_fuse_ln = 1, opt_fuse_value = 1, opt_prefill_scan = 0, opt_int8 = 0;
+  Q8 q8{};
+  bool has_q8 = false;
   // tile plan per MFMA projection (RWKV7_OPT_GEMM_PLAN_* order), 0 = built-in
   int64_t opt_plan[6] = {0, 0, 0, 0, 0, 0};
   std::vector<TimedLaunch> pending;
@@ -438,6 +481,8 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
   // GEMV path: fp32 activations; MFMA path: every projection input is
   // written in fp16 by its producer (the residual stream stays fp32)
   const bool f16 = !path.gemv;
+  // int8 weights on the small-batch GEMV path when enabled
+  const bool q8 = m->opt_int8 && m->has_q8 && path.gemv && B <= 2;
   const int C = d.C;
   int64_t* counters = (int64_t*)((char*)pool + align_up((uint64_t)n_slots * d.slot_floats * 4));
 
@@ -472,6 +517,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
 
     ProjArgs pa;
     proj_in_args(d, q, w, B, f16, pa);
+    if (q8) { pa.Wq = m->q8.layers[l].w_in; pa.Wsc = m->q8.layers[l].s_in; }
     if (path.fused) {
       pa.ln = LnPro{w.x, q.ln1_w, q.ln1_b, pool, d.slot_floats, n_slots, lo, w.slots, w.u_att, LNP_MIX, 0};
       for (int s = 0; s < 7; ++s) pa.seg[s].mix = q.mu6 + (int64_t)kInMix[s] * C;
@@ -495,6 +541,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
     memset(&po, 0, sizeof po);
     po.W = q.w_o; po.K = C; po.M = B; po.nseg = 1;
     po.seg[0] = mkseg(0, C, EPI_RESID, w.yg, C, w.x, C);
+    if (q8) { po.Wq = m->q8.layers[l].w_o; po.Wsc = m->q8.layers[l].s_o; }
     RUN(RWKV7_K_PROJ_OUT, "proj_out", proj(path.gemv, po, C, w, st, m->opt_plan[2], defer));
 
     ProjArgs pk;
@@ -509,6 +556,10 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
       pk.vW = q.w_val_hm;
       pk.vpart = w.vpart;
       pk.vC = C;
+    }
+    if (q8) {
+      pk.Wq = m->q8.layers[l].w_key; pk.Wsc = m->q8.layers[l].s_key;
+      if (path.fuse_value) { pk.vWq = m->q8.layers[l].w_val; pk.vSc = m->q8.layers[l].s_val; }
     }
     if (path.fused) {
       pk.ln = LnPro{w.x, q.ln2_w, q.ln2_b, pool, d.slot_floats, n_slots, lo + C, w.slots, w.u_ffn, LNP_MIX, 0};
@@ -561,6 +612,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
   memset(&ph, 0, sizeof ph);
   ph.W = m->pk.head; ph.K = C; ph.M = B; ph.nseg = 1;
   ph.seg[0] = mkseg(0, d.V, EPI_NONE, w.xo, C, logits, d.V);
+  if (q8) { ph.Wq = m->q8.head; ph.Wsc = m->q8.s_head; }
   if (path.fused) {
     ph.ln = LnPro{w.x, m->pk.lnout_w, m->pk.lnout_b, nullptr, 0, 0, 0, nullptr, nullptr, LNP_PLAIN, 0};
   } else {
@@ -1101,6 +1153,56 @@ int rwkv7_sample(int32_t B, int32_t V, const float* logits, float* occ_pool, int
   return RWKV7_OK;
 }
 
+int rwkv7_int8_bytes(const rwkv7_config* cfg, uint64_t* bytes) {
+  Dims d;
+  int rc = check_config(cfg, &d);
+  if (rc) return rc;
+  if (!bytes) return fail(RWKV7_EINVAL, "bytes is NULL");
+  *bytes = q8_layout(d, nullptr).bytes;
+  return RWKV7_OK;
+}
+
+int rwkv7_quantize_int8(rwkv7_model* m, void* buf, uint64_t bytes, void* stream) {
+  if (!m || !buf) return fail(RWKV7_EINVAL, "model and buf must be non-NULL");
+  const Dims& d = m->d;
+  Q8 q = q8_layout(d, (char*)buf);
+  if (bytes < q.bytes)
+    return fail(RWKV7_ESHAPE, "int8 buffer of %llu bytes, %llu needed", (unsigned long long)bytes,
+                (unsigned long long)q.bytes);
+  hipStream_t st = (hipStream_t)stream;
+  HIP_TRY(launch_quant_rows(m->pk.head, d.V, d.C, q.head, q.s_head, st), "quantize head");
+  for (int l = 0; l < d.L; ++l) {
+    const LayerPtrs& p = m->pk.layers[l];
+    const Q8Layer& y = q.layers[l];
+    HIP_TRY(launch_quant_rows(p.w_in, d.Nin, d.C, y.w_in, y.s_in, st), "quantize w_in");
+    HIP_TRY(launch_quant_rows(p.w_o, d.C, d.C, y.w_o, y.s_o, st), "quantize w_o");
+    HIP_TRY(launch_quant_rows(p.w_key, d.F, d.C, y.w_key, y.s_key, st), "quantize w_key");
+    HIP_TRY(launch_quant_rows(p.w_val_hm, d.F, d.C, y.w_val, y.s_val, st), "quantize w_val");
+  }
+  m->q8 = q;
+  m->has_q8 = true;
+  drop_graphs(m);
+  return RWKV7_OK;
+}
+
+int rwkv7_debug_int8_matrix(const rwkv7_model* m, int32_t layer, int32_t which, const void** codes,
+                            const float** scales, int64_t* rows, int32_t* K) {
+  if (!m || !codes || !scales || !rows || !K) return fail(RWKV7_EINVAL, "null argument");
+  if (!m->has_q8) return fail(RWKV7_ENOTSUP, "no int8 weights (rwkv7_quantize_int8 first)");
+  const Dims& d = m->d;
+  if (which == 4) {
+    *codes = m->q8.head; *scales = m->q8.s_head; *rows = d.V; *K = d.C;
+    return RWKV7_OK;
+  }
+  if (layer < 0 || layer >= d.L || which < 0 || which > 3) return fail(RWKV7_EINVAL, "bad layer or matrix");
+  const Q8Layer& y = m->q8.layers[layer];
+  const uint8_t* c[4] = {y.w_in, y.w_o, y.w_key, y.w_val};
+  const float* s4[4] = {y.s_in, y.s_o, y.s_key, y.s_val};
+  const int64_t r[4] = {d.Nin, d.C, d.F, d.F};
+  *codes = c[which]; *scales = s4[which]; *rows = r[which]; *K = d.C;
+  return RWKV7_OK;
+}
+
 int rwkv7_poll_error(void* ws, void* stream, uint32_t* flags) {
   if (!ws) return fail(RWKV7_EINVAL, "workspace is NULL");
   hipStream_t st = (hipStream_t)stream;
@@ -1132,6 +1234,9 @@ int rwkv7_set_option(rwkv7_model* m, int32_t key, int64_t value) {
     case RWKV7_OPT_PREFILL_SCAN:
       if (value < 0 || value > 2) return fail(RWKV7_EINVAL, "PREFILL_SCAN must be 0, 1 or 2");
       m->opt_prefill_scan = value; break;
+    case RWKV7_OPT_INT8:
+      if (value && !m->has_q8) return fail(RWKV7_ENOTSUP, "INT8 needs rwkv7_quantize_int8 first");
+      m->opt_int8 = value ? 1 : 0; break;
     case RWKV7_OPT_GEMM_PLAN_PROJ_IN:
     case RWKV7_OPT_GEMM_PLAN_ADAPTERS:
     case RWKV7_OPT_GEMM_PLAN_PROJ_OUT:
@@ -1150,7 +1255,7 @@ int rwkv7_set_option(rwkv7_model* m, int32_t key, int64_t value) {
   }
   // cached graphs bake in the kernel path: drop them when it may change
   if (key == RWKV7_OPT_GEMV_MAX_B || key == RWKV7_OPT_SPARSE_MAX_B || key == RWKV7_OPT_FUSE_LN ||
-      key == RWKV7_OPT_FUSE_VALUE || (key >= RWKV7_OPT_GEMM_PLAN_PROJ_IN && key <= RWKV7_OPT_GEMM_PLAN_HEAD))
+      key == RWKV7_OPT_FUSE_VALUE || key == RWKV7_OPT_INT8 || (key >= RWKV7_OPT_GEMM_PLAN_PROJ_IN && key <= RWKV7_OPT_GEMM_PLAN_HEAD))
     drop_graphs(m);
   return RWKV7_OK;
 }
@@ -1166,6 +1271,7 @@ int rwkv7_get_option(const rwkv7_model* m, int32_t key, int64_t* value) {
     case RWKV7_OPT_FUSE_LN: *value = m->opt_fuse_ln; break;
     case RWKV7_OPT_FUSE_VALUE: *value = m->opt_fuse_value; break;
     case RWKV7_OPT_PREFILL_SCAN: *value = m->opt_prefill_scan; break;
+    case RWKV7_OPT_INT8: *value = m->opt_int8; break;
     case RWKV7_OPT_GEMM_PLAN_PROJ_IN:
     case RWKV7_OPT_GEMM_PLAN_ADAPTERS:
     case RWKV7_OPT_GEMM_PLAN_PROJ_OUT:

@@ -14,6 +14,9 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // 16-byte loads / stores; the _nt forms are non-temporal (streamed once).
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+RW_DEV u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+RW_DEV u32x2 ld8_nt(const void* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p)); }
 RW_DEV u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 RW_DEV u32x4 ld16_nt(const void* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
 RW_DEV void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
@@ -95,6 +98,12 @@ struct ProjArgs {
   const half_t* vW;  // GEMV key path with the value fused: hidden-major W_val [rows][vC]
   float* vpart;      // ... and its per-workgroup partial sums [workgroups][M][vC]
   int vC;
+  // int8 route (GEMV, B <= 2): codes + 128 as bytes [rows][K] and fp32 row
+  // scales, used instead of W (and vW) when Wq is set
+  const uint8_t* Wq;
+  const float* Wsc;
+  const uint8_t* vWq;
+  const float* vSc;
   int tile0[MAX_SEGS + 1];  // MFMA path: first column tile of each segment (prefix sums)
   LnPro ln;
   Seg seg[MAX_SEGS];

@@ -11,6 +11,7 @@
 #include "launch.h"
 
 #include <stdio.h>
+#include <type_traits>
 
 // ============================================================== GEMV
 // The fused LayerNorm prologue holds a lane's K slice of every row in VGPRs
@@ -30,7 +31,10 @@ enum : int { GV_MIXED = 0, GV_PRE = 1, GV_RESID = 2, GV_NONE = 3, GV_PREV = 4 };
 
 // NWV waves per workgroup: 4, or 5 for launches with neither the fused
 // LayerNorm prologue nor the value epilogue (both written for four waves).
-template <int B, int LPR, int NCH, int RPW, int EPK, int NWV = 4>
+// Q: the int8 route.  A weight byte u holds the code u - 128 of a symmetric
+// per-row scale s, so a row's dot product is s (sum u x - 128 sum x): one
+// unsigned-byte convert and one FMA per weight, as for fp16, at half the bytes.
+template <int B, int LPR, int NCH, int RPW, int EPK, int NWV = 4, bool Q = false>
 __global__ __launch_bounds__(64 * NWV) void k_gemv(ProjArgs a) {
   static_assert(NWV == 4 || EPK != GV_PREV, "the value epilogue assumes four waves");
   constexpr int GPW = 64 / LPR;
@@ -45,17 +49,32 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv(ProjArgs a) {
   const Seg sg = pick_seg(a, row_wg);
   const int row_base = row_wg + wave * ROWS_WAVE + grp * RPW;
 
-  u32x4 w[RPW][NCH];
+  using WV = typename std::conditional<Q, u32x2, u32x4>::type;
+  WV w[RPW][NCH];
+  float wsc[RPW];
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
     const int row = row_base + i;
-    const half_t* wp = a.W + (long)row * K + lig * 8;
+    if constexpr (Q) {
+      const uint8_t* wp = a.Wq + (long)row * K + lig * 8;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      if (row < sg.row1)
-        w[i][c] = ld16_nt(wp + c * LPR * 8);
-      else
-        w[i][c] = u32x4{0u, 0u, 0u, 0u};
+      for (int c = 0; c < NCH; ++c) {
+        if (row < sg.row1)
+          w[i][c] = ld8_nt(wp + c * LPR * 8);
+        else
+          w[i][c] = WV{0u, 0u};
+      }
+      wsc[i] = row < sg.row1 ? a.Wsc[row] : 0.0f;
+    } else {
+      const half_t* wp = a.W + (long)row * K + lig * 8;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        if (row < sg.row1)
+          w[i][c] = ld16_nt(wp + c * LPR * 8);
+        else
+          w[i][c] = WV{0u, 0u, 0u, 0u};
+      }
+      wsc[i] = 1.0f;
     }
   }
 
@@ -165,12 +184,22 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv(ProjArgs a) {
   for (int i = 0; i < RPW; ++i)
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const half8 h = __builtin_bit_cast(half8, w[i][c]);
+      if constexpr (Q) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float wf = (float)h[e];
+        for (int e = 0; e < 8; ++e) {
+          const unsigned word = e < 4 ? w[i][c].x : w[i][c].y;
+          const float wf = (float)((word >> (8 * (e & 3))) & 0xFFu);
 #pragma unroll
-        for (int b = 0; b < B; ++b) acc[i][b] = fmaf(wf, xa[b][c][e], acc[i][b]);
+          for (int b = 0; b < B; ++b) acc[i][b] = fmaf(wf, xa[b][c][e], acc[i][b]);
+        }
+      } else {
+        const half8 h = __builtin_bit_cast(half8, w[i][c]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float wf = (float)h[e];
+#pragma unroll
+          for (int b = 0; b < B; ++b) acc[i][b] = fmaf(wf, xa[b][c][e], acc[i][b]);
+        }
       }
     }
 
@@ -180,6 +209,26 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv(ProjArgs a) {
     for (int b = 0; b < B; ++b)
 #pragma unroll
       for (int o = LPR / 2; o >= 1; o >>= 1) acc[i][b] += __shfl_xor(acc[i][b], o);
+
+  if constexpr (Q) {
+    // remove the byte bias with the group's activation sums, then scale the row
+    float sx[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      float t = 0.0f;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t += xa[b][c][e];
+#pragma unroll
+      for (int o = LPR / 2; o >= 1; o >>= 1) t += __shfl_xor(t, o);
+      sx[b] = t;
+    }
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+#pragma unroll
+      for (int b = 0; b < B; ++b) acc[i][b] = wsc[i] * fmaf(-128.0f, sx[b], acc[i][b]);
+  }
 
   __shared__ float s_h[EPK == GV_PREV ? B : 1][EPK == GV_PREV ? ROWS_WG : 1];
   if constexpr (EPK == GV_PREV) {
@@ -240,6 +289,9 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv(ProjArgs a) {
     for (int b = 0; b < B; ++b)
 #pragma unroll
       for (int e = 0; e < 8; ++e) { pacc[b][0][e] = 0.f; pacc[b][1][e] = 0.f; }
+    float corr[B];   // int8 route: sum of h * s over the rows taken, times the bias 128
+#pragma unroll
+    for (int b = 0; b < B; ++b) corr[b] = 0.f;
     // up to four active rows per pass: their loads are issued together
     while (act) {
       int rr[4];
@@ -249,6 +301,35 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv(ProjArgs a) {
         rr[u] = act ? __builtin_ctz(act) : 0;
         nr += act ? 1 : 0;
         act &= act - 1;
+      }
+      if constexpr (Q) {
+        u32x2 q0[4], q1[4];
+        float vs[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint8_t* wr = a.vWq + (long)(row_wg + rr[u]) * a.vC;
+          q0[u] = (u < nr && c0 < nchunk) ? ld8(wr + c0 * 8) : u32x2{0u, 0u};
+          q1[u] = (u < nr && c1 < nchunk) ? ld8(wr + c1 * 8) : u32x2{0u, 0u};
+          vs[u] = u < nr ? a.vSc[row_wg + rr[u]] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (u < nr) {
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+              const float hs = s_h[b][rr[u]] * vs[u];
+              corr[b] += hs;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const unsigned w0e = e < 4 ? q0[u].x : q0[u].y;
+                const unsigned w1e = e < 4 ? q1[u].x : q1[u].y;
+                pacc[b][0][e] = fmaf(hs, (float)((w0e >> (8 * (e & 3))) & 0xFFu), pacc[b][0][e]);
+                pacc[b][1][e] = fmaf(hs, (float)((w1e >> (8 * (e & 3))) & 0xFFu), pacc[b][1][e]);
+              }
+            }
+          }
+        }
+        continue;
       }
       u32x4 w0[4], w1[4];
 #pragma unroll
@@ -273,6 +354,15 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv(ProjArgs a) {
           }
         }
       }
+    }
+    if constexpr (Q) {
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pacc[b][0][e] = fmaf(-128.0f, corr[b], pacc[b][0][e]);
+          pacc[b][1][e] = fmaf(-128.0f, corr[b], pacc[b][1][e]);
+        }
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
@@ -336,22 +426,22 @@ static int gemv_epk(const ProjArgs& a) {
   return e == EPI_PRE ? GV_PRE : e == EPI_RESID ? GV_RESID : e == EPI_NONE ? GV_NONE : GV_MIXED;
 }
 
-template <int B, int LPR, int NCH, int RPW, int NWV = 4>
+template <int B, int LPR, int NCH, int RPW, int NWV = 4, bool Q = false>
 static void gemv_launch_epk(int epk, dim3 grid, hipStream_t st, const ProjArgs& a) {
   const dim3 blk(64 * NWV);
   switch (epk) {
-    case GV_PRE: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_PRE, NWV>), grid, blk, 0, st, a); break;
-    case GV_RESID: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_RESID, NWV>), grid, blk, 0, st, a); break;
-    case GV_NONE: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_NONE, NWV>), grid, blk, 0, st, a); break;
+    case GV_PRE: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_PRE, NWV, Q>), grid, blk, 0, st, a); break;
+    case GV_RESID: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_RESID, NWV, Q>), grid, blk, 0, st, a); break;
+    case GV_NONE: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_NONE, NWV, Q>), grid, blk, 0, st, a); break;
     case GV_PREV:
       if constexpr (NWV == 4)
-        hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_PREV, NWV>), grid, blk, 0, st, a);
+        hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_PREV, NWV, Q>), grid, blk, 0, st, a);
       break;
-    default: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_MIXED, NWV>), grid, blk, 0, st, a); break;
+    default: hipLaunchKernelGGL((k_gemv<B, LPR, NCH, RPW, GV_MIXED, NWV, Q>), grid, blk, 0, st, a); break;
   }
 }
 
-template <int B>
+template <int B, bool Q = false>
 static hipError_t gemv_dispatch_b(const ProjArgs& a, int total_rows, hipStream_t st) {
   constexpr int RPW = gemv_rpw(B);
   const int K = a.K;
@@ -360,22 +450,22 @@ static hipError_t gemv_dispatch_b(const ProjArgs& a, int total_rows, hipStream_t
   const int epk = gemv_epk(a);
   if constexpr (B == 1) {
     if (rows_wg == 20) {
-      if (K == 2560) gemv_launch_epk<1, 64, 5, 5>(epk, grid, st, a);
-      else gemv_launch_epk<1, 64, 8, 5>(epk, grid, st, a);
+      if (K == 2560) gemv_launch_epk<1, 64, 5, 5, 4, Q>(epk, grid, st, a);
+      else gemv_launch_epk<1, 64, 8, 5, 4, Q>(epk, grid, st, a);
       return hipGetLastError();
     }
     if (rows_wg == 10) {   // five waves: no prologue, no value epilogue
-      if (K == 2560) gemv_launch_epk<1, 64, 5, 2, 5>(epk, grid, st, a);
-      else gemv_launch_epk<1, 64, 8, 2, 5>(epk, grid, st, a);
+      if (K == 2560) gemv_launch_epk<1, 64, 5, 2, 5, Q>(epk, grid, st, a);
+      else gemv_launch_epk<1, 64, 8, 2, 5, Q>(epk, grid, st, a);
       return hipGetLastError();
     }
   }
   if (K == 256) {
-    gemv_launch_epk<B, 32, 1, RPW>(epk, grid, st, a);
+    gemv_launch_epk<B, 32, 1, RPW, 4, Q>(epk, grid, st, a);
     return hipGetLastError();
   }
   switch (K / 512) {
-#define CASE(n) case n: gemv_launch_epk<B, 64, n, RPW>(epk, grid, st, a); break;
+#define CASE(n) case n: gemv_launch_epk<B, 64, n, RPW, 4, Q>(epk, grid, st, a); break;
     CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
 #undef CASE
     default: return hipErrorInvalidValue;
@@ -384,6 +474,14 @@ static hipError_t gemv_dispatch_b(const ProjArgs& a, int total_rows, hipStream_t
 }
 
 hipError_t launch_gemv(const ProjArgs& a, int total_rows, hipStream_t st) {
+  if (a.Wq) {
+    if (a.vW && !a.vWq) return hipErrorInvalidValue;
+    switch (a.M) {
+      case 1: return gemv_dispatch_b<1, true>(a, total_rows, st);
+      case 2: return gemv_dispatch_b<2, true>(a, total_rows, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (a.M) {
     case 1: return gemv_dispatch_b<1>(a, total_rows, st);
     case 2: return gemv_dispatch_b<2>(a, total_rows, st);

@@ -1044,3 +1044,32 @@ hipError_t launch_greedy(const GreedyArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_greedy_final, dim3(a.B), dim3(64), 0, st, a);
   return hipGetLastError();
 }
+
+// ============================================================== int8 weights
+// One wave per row: m = max |w| over the row, s = m / 127 (fp32, correctly
+// rounded), code q = rint(w / s) clamped to [-127, 127] (0 when s = 0),
+// stored as the byte q + 128, and s.  A one-time packing pass.
+__global__ __launch_bounds__(256) void k_quant_rows(const half_t* __restrict__ W, int64_t rows, int K,
+                                                    uint8_t* __restrict__ q, float* __restrict__ sc) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;   // a whole wave leaves together; no barrier follows
+  const half_t* w = W + row * K;
+  float m = 0.0f;
+  for (int k = lane; k < K; k += 64) m = fmaxf(m, fabsf((float)w[k]));
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  const float s = m / 127.0f;
+  uint8_t* qr = q + row * K;
+  for (int k = lane; k < K; k += 64) {
+    float r = 0.0f;
+    if (s > 0.0f) r = fminf(fmaxf(rintf((float)w[k] / s), -127.0f), 127.0f);
+    qr[k] = (uint8_t)((int)r + 128);
+  }
+  if (lane == 0) sc[row] = s;
+}
+
+hipError_t launch_quant_rows(const half_t* W, int64_t rows, int K, uint8_t* q, float* sc, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_quant_rows, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, W, rows, K, q, sc);
+  return hipGetLastError();
+}

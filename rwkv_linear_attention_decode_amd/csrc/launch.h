@@ -201,6 +201,9 @@ struct SampleArgs {
 constexpr int SAMPLE_MAX_V = 65536;
 hipError_t launch_sample(const SampleArgs& a, hipStream_t st);
 
+// int8 weights: per-row symmetric codes (byte = code + 128) and fp32 scales of W [rows][K]
+hipError_t launch_quant_rows(const half_t* W, int64_t rows, int K, uint8_t* q, float* sc, hipStream_t st);
+
 // api.hip, for the scheduler: set the thread's last-error text and return
 // `code`; a loaded model's vocabulary size.
 struct rwkv7_model;

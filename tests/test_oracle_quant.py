@@ -70,3 +70,12 @@ def test_value_matrix_is_scaled_per_hidden_unit():
         assert np.all(np.abs(v - src) <= col_max / 127 * 0.5 * (1 + 1e-5))
         r = out[f"blocks.{l}.att.key.weight"]
         assert np.array_equal(r, Q.dequantize_rows(*Q.quantize_rows(w[f"blocks.{l}.att.key.weight"])))
+
+
+def test_lazy_view_equals_table():
+    s = synth.TINY
+    w = synth.make_weights(s)
+    full = Q.int8_weights(w, s.n_layer)
+    lazy = Q.Int8View(w, s.n_layer)
+    for name in ("head.weight", "blocks.1.ffn.value.weight", "blocks.0.att.g1", "blocks.0.att.g2", "emb.weight"):
+        assert np.array_equal(np.asarray(lazy[name], np.float64), np.asarray(full[name], np.float64)), name
