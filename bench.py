@@ -262,6 +262,7 @@ def int8_b1(R, args, shape, m, run_step, slot, tok, logits):
         gbs = cb[dom] / (avg_ms * 1e-3) / 1e9
         ms = dt / args.steps * 1e3
         sb = step_bytes(shape, 1, nnz, True, int8=True)
+        kname = R.rwkv7_kernel_name(m.handle, cls, 1)
     finally:
         R.rwkv7_set_option(m.handle, R.OPT_INT8, 0)
     del buf
@@ -270,7 +271,8 @@ def int8_b1(R, args, shape, m, run_step, slot, tok, logits):
            "step_hbm_frac": round(sb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
            "roofline": {"bound": "hbm", "class": dom, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": int(cb[dom]),
-                        "avg_launch_us": round(avg_ms * 1e3, 3)},
+                        "avg_launch_us": round(avg_ms * 1e3, 3), "kernel": kname,
+                        "traffic": pmc_traffic(kname, dom)},
            "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in kb.items()}}
     log(f"[bench] B=1 int8 weights: {res['tok_s']} tok/s, {ms:.3f} ms/step, step {res['step_gbs']} GB/s; "
         f"dominant {dom} {res['roofline']['achieved']} GB/s")

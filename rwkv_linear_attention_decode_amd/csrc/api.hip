@@ -1360,18 +1360,19 @@ int rwkv7_time_kernel(rwkv7_model* m, void* pool, int64_t n_slots, int32_t B,
 const char* rwkv7_kernel_name(const rwkv7_model* m, int32_t cls, int32_t B) {
   if (!m || cls < 0 || cls >= RWKV7_K_COUNT) return "";
   const Path p = decode_path(m, B);
+  const bool q = m->opt_int8 && m->has_q8 && p.gemv && B <= 2;
   switch (cls) {
     case RWKV7_K_LN_MIX: return "k_ln_mix";
     case RWKV7_K_PROJ_IN:
-      return p.gemv ? gemv_kernel_name(B, m->d.C, -1, m->d.Nin, 7, p.fused) : gemm_kernel_name(B, m->d.Nin, m->d.C);
+      return p.gemv ? gemv_kernel_name(B, m->d.C, -1, m->d.Nin, 7, p.fused, q) : gemm_kernel_name(B, m->d.Nin, m->d.C);
     case RWKV7_K_PROJ_OUT:
-      return p.gemv ? gemv_kernel_name(B, m->d.C, EPI_RESID, m->d.C, 1, false) : gemm_kernel_name(B, m->d.C, m->d.C);
+      return p.gemv ? gemv_kernel_name(B, m->d.C, EPI_RESID, m->d.C, 1, false, q) : gemm_kernel_name(B, m->d.C, m->d.C);
     case RWKV7_K_CMIX_KEY:
       return p.gemv ? gemv_kernel_name(B, m->d.C, p.fuse_value ? -2 : p.sparse ? EPI_PRE : -1, m->d.F, 1,
-                                      p.fused || p.fuse_value)
+                                      p.fused || p.fuse_value, q)
                     : gemm_kernel_name(B, m->d.F, m->d.C);
     case RWKV7_K_HEAD:
-      return p.gemv ? gemv_kernel_name(B, m->d.C, EPI_NONE, m->d.V, 1, p.fused) : gemm_kernel_name(B, m->d.V, m->d.C);
+      return p.gemv ? gemv_kernel_name(B, m->d.C, EPI_NONE, m->d.V, 1, p.fused, q) : gemm_kernel_name(B, m->d.V, m->d.C);
     case RWKV7_K_WKV: {
       if (!p.gemv) return "k_wkv_decode_rows";
       static char name[32];

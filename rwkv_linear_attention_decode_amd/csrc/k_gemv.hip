@@ -491,20 +491,20 @@ hipError_t launch_gemv(const ProjArgs& a, int total_rows, hipStream_t st) {
   }
 }
 
-// Template arguments as a trace prints them, e.g. "k_gemv<1, 64, 5, 4, 1, 4>", for
+// Template arguments as a trace prints them, e.g. "k_gemv<1, 64, 5, 4, 1, 4, false>", for
 // a launch of `rows` output rows in `nseg` segments (four_waves: it has the
-// fused prologue or the value epilogue).
-const char* gemv_kernel_name(int B, int K, int epi, int rows, int nseg, bool four_waves) {
-  static char names[5][9][5][3][40];
+// fused prologue or the value epilogue; q8: the int8 route).
+const char* gemv_kernel_name(int B, int K, int epi, int rows, int nseg, bool four_waves, bool q8) {
+  static char names[2][5][9][5][3][48];
   if (!gemv_supported(B, K)) return "k_gemv";
   const int lpr = K == 256 ? 32 : 64;
   const int nch = K == 256 ? 1 : K / 512;
   const int epk = epi == -2 ? GV_PREV : epi == EPI_PRE ? GV_PRE : epi == EPI_RESID ? GV_RESID
                   : epi == EPI_NONE ? GV_NONE : GV_MIXED;
   const int rw = gemv_launch_rows(B, K, rows, nseg, four_waves);
-  char* s = names[B][nch][epk][rw == 20 ? 1 : rw == 10 ? 2 : 0];
+  char* s = names[q8 ? 1 : 0][B][nch][epk][rw == 20 ? 1 : rw == 10 ? 2 : 0];
   if (!s[0])
-    snprintf(s, sizeof(names[0][0][0][0]), "k_gemv<%d, %d, %d, %d, %d, %d>", B, lpr, nch,
-             rw == 10 ? 2 : rw == 20 ? 5 : gemv_rpw(B), epk, rw == 10 ? 5 : 4);
+    snprintf(s, sizeof(names[0][0][0][0][0]), "k_gemv<%d, %d, %d, %d, %d, %d, %s>", B, lpr, nch,
+             rw == 10 ? 2 : rw == 20 ? 5 : gemv_rpw(B), epk, rw == 10 ? 5 : 4, q8 ? "true" : "false");
   return s;
 }

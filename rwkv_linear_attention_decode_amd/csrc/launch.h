@@ -26,7 +26,7 @@ hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int 
                            int split, hipStream_t st, int* deferred = nullptr);
 // `epi`: the epilogue shared by every segment of the launch, -1 when mixed,
 // -2 for the key projection with the sparse value fused into it
-const char* gemv_kernel_name(int B, int K, int epi, int rows, int nseg, bool four_waves);
+const char* gemv_kernel_name(int B, int K, int epi, int rows, int nseg, bool four_waves, bool q8);
 const char* gemm_kernel_name(int M, int N, int K);
 // Whether launch_gemm_cfg supports tile (32 tm x 32 tn), stage depth ks and K loop pipe.
 bool gemm_cfg_ok(int tm, int tn, int ks, int pipe);
