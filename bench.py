@@ -548,7 +548,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
-              "Decode shards by state slots with no communication; see DESIGN.md.", file=sys.stderr)
+              "Decode would shard by state slots, one process per GPU, with no communication.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -23,7 +23,7 @@ What it computes, and where that comes from:
 * One addition that RWKV-7 does not have: a channel-mix key bias, used only
   to make ~85 % of the ReLU^2 outputs zero (the synthetic-weight recipe).
 
-Readings taken where the pages are silent are listed in the design doc.
+Where the pages are silent, the plainest reading is taken and stated at the function that takes it.
 
 Pins (tests/test_oracle_*.py): LayerNorm / GroupNorm / L2-normalise against
 torch's fp64 library routines; decay closed form; WKV closed forms (first
