@@ -179,7 +179,8 @@ int rwkv7_sched_task_state(const rwkv7_sched* s, int64_t task_id, int32_t* state
  * NULL; sample_ws: rwkv7_sample_workspace_bytes(max_B, vocab) bytes.  The
  * backend allocates its own staging (device and pinned host memory for
  * max_B rows and max_B logits rows); rwkv7_sched_gpu_backend_free releases
- * it.  max_B <= n_slots. */
+ * it.  max_B <= n_slots; a scheduler driving it needs max_batch <= max_B
+ * (a larger round fails with RWKV7_EINVAL and is not advanced). */
 int rwkv7_sched_gpu_backend(rwkv7_model* model, void* pool, int64_t n_slots, float* occ_pool,
                             const uint8_t* forbidden, int32_t max_B, void* ws, uint64_t ws_bytes,
                             void* sample_ws, uint64_t sample_ws_bytes, void* stream,
