@@ -374,7 +374,9 @@ def sched_backend(reset, prefill, step) -> SchedBackend:
     """A backend whose callbacks are Python callables (used by host-logic tests):
     reset(slot); prefill(slot, tokens: list); step(slots, tokens, n_sample, params) -> ids,
     where params maps temperature/top_p/top_k/presence/frequency/decay/uniform to lists of
-    n_sample values.  A callable that raises makes the round fail with RWKV7_EINVAL."""
+    n_sample values.  A callable that raises makes the round fail with RWKV7_EINVAL.
+    The returned structure holds the C callbacks: keep it alive while a
+    scheduler created over it is in use."""
     names = ("temperature", "top_p", "top_k", "presence", "frequency", "decay", "uniform")
 
     def c_reset(_ctx, slot):
