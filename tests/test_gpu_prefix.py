@@ -204,3 +204,65 @@ def test_scheduler_backend_reuses_prefixes(weights, W, R):
     R.rwkv7_sched_gpu_backend_free(be)
     R.rwkv7_prefix_cache_free(cache)
     m.close()
+
+
+def test_scheduler_restores_from_host_tier_and_stops(weights, W, R):
+    """One device snapshot and two host ones: the second task's store moves
+    the first prompt's state to the host arena, and the third task (which
+    extends the first prompt) is restored from there.  The first task stops
+    on its stop token (the oracle's third greedy pick)."""
+    n_slots = max_b = 2
+    m = R.Model.from_numpy(S, weights, n_slots=n_slots, max_B=max_b, max_T=64)
+    stride = (R.rwkv7_snapshot_bytes(m.cfg) + 255) // 256 * 256
+    arena = torch.empty(stride, dtype=torch.uint8, device="cuda")
+    host = torch.empty(2 * stride, dtype=torch.uint8).pin_memory()
+    cache = R.rwkv7_prefix_cache_create(m.handle, arena, host)
+    occ = torch.zeros(n_slots * V, device="cuda")
+    sws = torch.zeros(R.rwkv7_sample_workspace_bytes(max_b, V), dtype=torch.uint8, device="cuda")
+    be = R.rwkv7_sched_gpu_backend(m.handle, m.pool, n_slots, occ, None, max_b, m.ws, sws)
+    R.rwkv7_sched_gpu_backend_set_cache(be, cache)
+    s = R.rwkv7_sched_create(R.SchedConfig(max_b, 1, 0, 10, V), be)
+    p1, p2 = toks(60, 20).tolist(), toks(61, 24).tolist()
+    p3 = p1 + toks(62, 5).tolist()
+    # the oracle's greedy stream of p1 (penalties as below) gives the stop token
+    st = O.State(S)
+    O.seq(W, st, p1[:-1], want_logits=False)
+    occ0 = np.zeros((1, V), np.float32)
+    tok, greedy = p1[-1], []
+    for _ in range(3):
+        lg = O.step(W, [st], [tok])[0].astype(np.float32)[None]
+        ids, occ0, _ = O.sample_penalized(lg, occ0, [0.3], [0.3], [0.996], [0.0], [1.0], [0], None, [0.5])
+        tok = int(ids[0])
+        greedy.append(tok)
+    prm = [R.SchedParams(0.0, 1.0, 0, 0.3, 0.3, 0.996, 10, greedy[2], 1),
+           R.SchedParams(1.0, 0.3, 0, 0.3, 0.3, 0.996, 6, -1, 2),
+           R.SchedParams(0.0, 1.0, 0, 0.3, 0.3, 0.996, 6, -1, 3)]
+    if greedy[2] in greedy[:2]:
+        pytest.skip("the stop token occurs earlier in the stream")
+    tasks = {}
+    for p, q in zip((p1, p2, p3), prm):
+        tasks[R.rwkv7_sched_submit(s, p, q)] = (p, q)
+    events = []
+    for _ in range(200):
+        R.rwkv7_sched_step(s)
+        events += R.rwkv7_sched_poll(s)
+        if all(R.rwkv7_sched_task_state(s, t) == R.TASK_FINISHED for t in tasks):
+            break
+    streams, fin = {}, {}
+    for task, kind, value, index in events:
+        if kind == R.EV_TOKEN:
+            streams.setdefault(task, []).append(value)
+        else:
+            fin[task] = (value, index)
+    t1, t2, t3 = list(tasks)
+    assert streams[t1] == greedy and fin[t1] == (R.FIN_STOP, 3)
+    assert fin[t2] == (R.FIN_LENGTH, 6) and fin[t3] == (R.FIN_LENGTH, 6)
+    assert R.rwkv7_sched_gpu_backend_counts(be) == (19, 19 + 23 + 5)
+    cs = R.rwkv7_prefix_cache_stats(cache)
+    assert cs.hits == 1 and cs.hit_tokens == 19 and cs.offloads >= 1 and cs.host_entries >= 1
+    near = sum(replay(W, p, q, streams[t], np.zeros(V, bool)) for t, (p, q) in tasks.items())
+    assert near <= 2
+    R.rwkv7_sched_free(s)
+    R.rwkv7_sched_gpu_backend_free(be)
+    R.rwkv7_prefix_cache_free(cache)
+    m.close()
