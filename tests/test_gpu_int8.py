@@ -185,3 +185,39 @@ def test_int8_2b9_b1_steps(R):
     print("2.9B int8 B=1 logits rel errors:", ["%.2e" % e for e in errs])
     assert max(errs) <= TOL
     m.close()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("shape,B", [("2.9b", 2), ("7.2b", 1)])
+def test_int8_full_shapes(R, shape, B):
+    """The other GEMV instantiations at full size: B = 2 at K = 2560 and B = 1
+    at K = 4096 (the 7.2B shape), a few teacher-forced steps after short
+    prefills, against the int8 oracle."""
+    S = synth.R7_2B9 if shape == "2.9b" else synth.R7_7B2
+    w = synth.make_weights(S)
+    m = R.Model.from_numpy(S, w, n_slots=B, max_B=B, max_T=64)
+    buf = torch.empty(R.rwkv7_int8_bytes(m.cfg), dtype=torch.uint8, device="cuda")
+    R.rwkv7_quantize_int8(m.handle, buf)
+    R.rwkv7_set_option(m.handle, R.OPT_INT8, 1)
+    rng = np.random.default_rng(77)
+    prompts = [rng.integers(0, S.vocab, 6 + 3 * b) for b in range(B)]
+    feeds = rng.integers(0, S.vocab, (2, B))
+    m.reset(dev(list(range(B))))
+    for b in range(B):
+        m.prefill(b, dev(prompts[b]))
+    out = torch.empty(B, S.vocab, device="cuda")
+    got = []
+    for t in range(len(feeds)):
+        m.decode_step(dev(list(range(B))), dev(feeds[t]), out)
+        got.append(out.cpu().numpy().copy())
+    W16 = O.Weights(S, w, cache=False)
+    W8 = O.Weights(S, Q.Int8View(w, S.n_layer), cache=False)
+    errs = []
+    for b in range(B):
+        st = O.State(S)
+        O.seq(W16, st, prompts[b].tolist(), want_logits=False)
+        ref = O.seq(W8, st, [int(feeds[t][b]) for t in range(len(feeds))])
+        errs += [rel(got[t][b], ref[t]) for t in range(len(feeds))]
+    print(f"{shape} int8 B={B} logits rel errors:", ["%.2e" % e for e in errs])
+    assert max(errs) <= TOL
+    m.close()
