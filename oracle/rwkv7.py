@@ -28,11 +28,17 @@ Where the pages are silent, the plainest reading is taken and stated at the func
 Pins (tests/test_oracle_*.py): LayerNorm / GroupNorm / L2-normalise against
 torch's fp64 library routines; decay closed form; WKV closed forms (first
 token from zero state, pure decay, delta-rule recall, row permutation) and a
-hand-worked N=2 example (tests/golden/wkv_n2.json); sparse = dense
-channel-mix; whole-model invariants (sequence = steps, batch = singles, prefix
-split, slot permutation, bounded state); greedy brute force and a hand-worked
-penalty example (tests/golden/greedy_penalty.json).  Parity against any third
-party is unpinned: the pages print no logits, states or weights.
+hand-worked N=2 example (tests/golden/wkv_n2.json); a hand-worked two-layer,
+two-token model in exact rationals (tests/golden/layer_n2.json) that fixes
+the layer assembly -- tmix_inputs (adapters, alpha, kappa_hat, k~, the
+v_first residual), tmix_output (GroupNorm, bonus, gate), the key bias inside
+the ReLU^2, the a = -kappa_hat / b = kappa_hat*alpha wiring of step and seq,
+the shifts and the head -- with planted slips in each that the fixture
+rejects; sparse = dense channel-mix; whole-model invariants (sequence =
+steps, batch = singles, prefix split, slot permutation, bounded state);
+greedy brute force and a hand-worked penalty example
+(tests/golden/greedy_penalty.json).  Parity against any third party is
+unpinned: the pages print no logits, states or weights.
 """
 from __future__ import annotations
 
