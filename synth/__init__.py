@@ -105,9 +105,10 @@ def tensor_specs(s: ModelShape) -> List[Tuple[str, Tuple[int, ...], tuple]]:
             (p + "att.value.weight", (C, C), ("normal", C)),
             (p + "att.output.weight", (C, C), ("normal", C)),
             # per-head GroupNorm gain 0.1: at gain 1 this random network
-            # amplifies a 1e-7 relative perturbation by 1e4..1e6 over 32
-            # layers (near-singular heads), which no fp32 kernel can match
-            # to 1e-2; at 0.1 such perturbations grow at most ~3x.
+            # amplifies a 1e-7 relative perturbation of its weights up to
+            # ~4e4-fold in the logits over 32 layers, too much for fp16
+            # activations to stay within 1e-2; at 0.1 such perturbations
+            # grow at most ~10x (oracle/gn_gain_sensitivity.py measures both).
             (p + "att.ln_x.weight", (C,), ("std", 0.1, 0.01)),
             (p + "att.ln_x.bias", (C,), ("std", 0.0, 0.01)),
             (p + "ln2.weight", (C,), gamma),
