@@ -177,6 +177,49 @@ def kernel_breakdown(R, m, B, run_step, steps=4):
     return out
 
 
+def time_repeats(run_step, steps: int, repeats: int):
+    """Wall time of `steps` consecutive steps, `repeats` times, each bracketed
+    by a device synchronisation on both sides; returns the list of seconds."""
+    import torch
+    out = []
+    for _ in range(max(1, repeats)):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            run_step()
+        torch.cuda.synchronize()
+        out.append(time.perf_counter() - t0)
+    return out
+
+
+def hbm_attainable():
+    """Measured HBM bandwidth of plain streaming kernels on a 4 GiB buffer
+    (far beyond the 256 MB MALL): a full read (sum of fp32 elements) and a
+    device-to-device copy (read + write).  Reported beside the 8 TB/s peak
+    that the roofline fractions use."""
+    import torch
+    n = 1 << 30
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    res = {}
+    for name, fn, nbytes in (("read", lambda: x.sum(), 4 * n), ("copy", lambda: y.copy_(x), 8 * n)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(5):
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        res[f"{name}_gbs"] = round(nbytes / float(np.median(ts)) / 1e9, 1)
+    del x, y
+    torch.cuda.empty_cache()
+    res["how"] = "torch sum (read) and copy_ (read + write) of a 4 GiB fp32 buffer, median of 5, HIP events"
+    return res
+
+
 # ---------------------------------------------------------------- decode B=1 (headline)
 def decode_b1(R, args, shape, m):
     import torch
@@ -198,20 +241,17 @@ def decode_b1(R, args, shape, m):
 
     for _ in range(args.warmup):
         run_step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        run_step()
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
+    reps = time_repeats(run_step, args.steps, args.repeats)
+    dt = float(np.median(reps))
     flags = m.poll_error()
     if flags:
         raise RuntimeError(f"device error flags {flags} during the timed decode")
     nnz = measure_active_fraction(R, m, 1)
-    log(f"[bench] B=1: {args.steps} steps in {dt * 1e3:.1f} ms -> {args.steps / dt:.1f} tok/s; "
+    log(f"[bench] B=1: {args.steps} steps, median of {len(reps)} repeats {dt * 1e3:.1f} ms -> "
+        f"{args.steps / dt:.1f} tok/s (repeats {[round(args.steps / r, 1) for r in reps]}); "
         f"last-layer active rows {nnz}/{shape.ffn}")
     kb = kernel_breakdown(R, m, 1, run_step)
-    return dt, nnz, kb, run_step, slot, tok, logits
+    return dt, reps, nnz, kb, run_step, slot, tok, logits
 
 
 def roofline_b1(R, shape, m, kb, nnz, slot, tok, logits):
@@ -228,6 +268,7 @@ def roofline_b1(R, shape, m, kb, nnz, slot, tok, logits):
     kname = R.rwkv7_kernel_name(m.handle, cls, 1)
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": pmc_traffic(kname, dom),
+            "scope": "dominant kernel (frac); step_frac below is the whole decode step",
             "kernel": kname, "class": dom,
             "bytes_per_launch": int(cb[dom]), "avg_launch_us": round(avg_ms * 1e3, 3),
             "launches_per_step": kb[dom]["launches_per_step"]}
@@ -244,12 +285,7 @@ def int8_b1(R, args, shape, m, run_step, slot, tok, logits):
     try:
         for _ in range(args.warmup):
             run_step()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            run_step()
-        torch.cuda.synchronize()
-        dt = time.perf_counter() - t0
+        dt = float(np.median(time_repeats(run_step, args.steps, args.repeats)))
         if m.poll_error():
             raise RuntimeError("device error flags during the int8 decode")
         nnz = measure_active_fraction(R, m, 1)
@@ -310,12 +346,8 @@ def batched(R, args, shape, m, B):
 
     for _ in range(args.warmup):
         run_step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.batched_steps):
-        run_step()
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
+    reps = time_repeats(run_step, args.batched_steps, args.repeats)
+    dt = float(np.median(reps))
     flags = m.poll_error()
     if flags:
         raise RuntimeError(f"device error flags {flags} during batched decode B={B}")
@@ -325,6 +357,7 @@ def batched(R, args, shape, m, B):
     ms = dt / args.batched_steps * 1e3
     res = {"model": f"{shape.name}-shape", "B": B, "tok_s": round(B * args.batched_steps / dt, 1),
            "ms_per_step": round(ms, 4),
+           "tok_s_repeats": [round(B * args.batched_steps / r, 1) for r in reps],
            "steps": args.batched_steps, "prefill_s": round(t_pf, 2),
            "prompt_tokens": int(lens.sum()),
            "step_gbs": round(sb / (ms * 1e-3) / 1e9, 1),
@@ -406,7 +439,7 @@ def serving(R, shape, m, max_b, n_tasks, new_tokens, system_len=0, use_cache=Fal
     V = shape.vocab
     occ = torch.zeros(m.n_slots * V, device="cuda")
     sws = torch.zeros(R.rwkv7_sample_workspace_bytes(max_b, V), dtype=torch.uint8, device="cuda")
-    be = R.rwkv7_sched_gpu_backend(m.handle, m.pool, m.n_slots, occ, None, max_b, m.ws, sws)
+    be = R.rwkv7_sched_gpu_backend(m.handle, m.pool, m.n_slots, occ, None, max_b, m.ws, sws, m.max_T)
     system = synth.prefill_tokens(wl, system_len).tolist() if system_len else []
     cache = arena = None
     restore = None
@@ -496,6 +529,18 @@ def prefill(R, shape, m, Ts):
 
 # ---------------------------------------------------------------- CPU oracle
 def cpu_baseline(shape, weights, seconds):
+    """The fp64 oracle (oracle/rwkv7.py, unchanged) timed on the host cores on a
+    bounded sample of each workload it can reach within about `seconds`:
+      tiny        the whole workload (7 prompt tokens prefilled, 16 decode steps);
+      2.9B B=1    decode steps (the headline `value`, tokens/s);
+      2.9B B=8    batched decode steps of eight rows, the protocol subset size
+                  of the B = 64 / 256 workloads (rows x steps per second);
+      2.9B T=128  one 128-token sequence prefill (tokens/s).
+    The oracle keeps fp64 copies of the weights (Weights(cache=True)); that
+    one-time conversion is outside the timed regions, as the GPU's weight
+    packing is.  States start at zero: the oracle's cost does not depend on
+    their contents.  The 7.2B shape is not timed (another 58 GB of fp64
+    copies on the host)."""
     from oracle import rwkv7 as O
     import synth
     try:
@@ -505,22 +550,62 @@ def cpu_baseline(shape, weights, seconds):
         blas = []
     cores = len(os.sched_getaffinity(0))
     threads = max([n for _, n in blas if n] or [1])
-    W = O.Weights(shape, weights, cache=False)
-    st = O.State(shape)
-    wl = synth.WORKLOADS["decode_b1_2.9b"]
-    toks = synth.teacher_stream(wl, 0, 64)
-    n = 0
+    per = {}
+
+    def timed(fn, budget, max_n):
+        n, t0 = 0, time.perf_counter()
+        while n < max_n:
+            fn(n)
+            n += 1
+            if time.perf_counter() - t0 >= budget:
+                break
+        return n, time.perf_counter() - t0
+
+    # tiny, in full
+    tw = synth.make_weights(synth.TINY)
+    Wt = O.Weights(synth.TINY, tw, cache=True)
+    wl = synth.WORKLOADS["tiny"]
+    p = synth.prompt_tokens(wl, 0, 8)
+    feeds = [int(p[7])] + [int(t) for t in synth.teacher_stream(wl, 0, 15)]
+    st = O.State(synth.TINY)
     t0 = time.perf_counter()
-    while True:
-        O.step(W, [st], [int(toks[n % 64])])
-        n += 1
-        if time.perf_counter() - t0 >= seconds or n >= 64:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(n / dt, 4), "unit": "tokens/s", "cores": int(min(threads, cores)),
+    O.seq(Wt, st, p[:7], want_logits=False)
+    t1 = time.perf_counter()
+    for t in feeds:
+        O.step(Wt, [st], [t])
+    t2 = time.perf_counter()
+    per["tiny"] = {"decode_tok_s": round(16 / (t2 - t1), 2), "total_s": round(t2 - t0, 3),
+                   "sample": "7-token prefill + 16 decode steps (the whole workload)"}
+
+    t0 = time.perf_counter()
+    W = O.Weights(shape, weights, cache=True)
+    for name in weights:
+        W(name)
+    upcast_s = time.perf_counter() - t0
+    toks = synth.teacher_stream(synth.WORKLOADS["decode_b1_2.9b"], 0, 64)
+    st = O.State(shape)
+    n, dt = timed(lambda i: O.step(W, [st], [int(toks[i])]), 0.4 * seconds, 16)
+    value = n / dt
+    per["decode_b1_2.9b"] = {"tok_s": round(value, 3), "steps": n}
+    states = [O.State(shape) for _ in range(8)]
+    tb = synth.teacher_stream(synth.WORKLOADS["decode_b64_2.9b"], 0, 64)
+    n, dt = timed(lambda i: O.step(W, states, [int(x) for x in tb[8 * i % 56: 8 * i % 56 + 8]]),
+                  0.3 * seconds, 16)
+    per["decode_b8_2.9b"] = {"row_tok_s": round(8 * n / dt, 3), "steps": n,
+                             "sample": "8 rows per step (the protocol subset of the B=64 / B=256 workloads)"}
+    pt = synth.prefill_tokens(synth.WORKLOADS["prefill_2.9b"], 128)
+    st = O.State(shape)
+    t0 = time.perf_counter()
+    O.seq(W, st, pt, want_logits=False)
+    per["prefill_2.9b_T128"] = {"tok_s": round(128 / (time.perf_counter() - t0), 3)}
+    del W
+    return {"value": round(value, 4), "unit": "tokens/s", "cores": int(min(threads, cores)),
             "kind": "oracle",
-            "sample": f"{n} fp64 decode steps of the 2.9B-shape model, B=1, from a zero state "
-                      f"(NumPy, BLAS {blas}, {cores} host cores visible)"}
+            "sample": f"{per['decode_b1_2.9b']['steps']} fp64 decode steps of the 2.9B-shape model, B=1 "
+                      f"(value); also tiny in full, 8-row batched steps and a 128-token prefill (per_config); "
+                      f"NumPy with BLAS {blas}, {cores} host cores visible; fp64 weight copies made once "
+                      f"({upcast_s:.1f} s, untimed)",
+            "per_config": per}
 
 
 # ---------------------------------------------------------------- main
@@ -543,7 +628,10 @@ def main():
                     help="shared system-prompt length of the prefix-cache serving runs (0 = none)")
     ap.add_argument("--no-int8", dest="int8", action="store_false",
                     help="skip the B=1 run on int8 weights")
-    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed passes of K steps per decode config; the median is reported")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="time budget of the CPU oracle baseline (split over its configs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -564,10 +652,13 @@ def main():
     m, weights = build_model(R, shape, n_slots=n_slots, max_B=max([1] + Bs + Ss),
                              max_T=max([512] + Ts))
 
-    dt, nnz, kb, run_step, slot, tok, logits = decode_b1(R, args, shape, m)
+    hbm = hbm_attainable()
+    log(f"[bench] attainable HBM: read {hbm['read_gbs']} GB/s, copy {hbm['copy_gbs']} GB/s")
+    dt, reps, nnz, kb, run_step, slot, tok, logits = decode_b1(R, args, shape, m)
     ms = dt / args.steps * 1e3
     sb = step_bytes(shape, 1, nnz, True)
     roof = roofline_b1(R, shape, m, kb, nnz, slot, tok, logits)
+    roof["step_frac"] = round(sb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     log(f"[bench] dominant kernel {roof['class']}: {roof['avg_launch_us']} us/launch, "
         f"{roof['achieved']} GB/s ({roof['frac'] * 100:.1f}% of HBM peak)")
     i8 = int8_b1(R, args, shape, m, run_step, slot, tok, logits) if args.int8 else None
@@ -610,9 +701,13 @@ def main():
                    "batch": 1, "prompt_tokens": 64, "weights": "fp16 random-init", "state": "fp32",
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,
+        "repeats": {"n": len(reps), "tok_s": [round(args.steps / r, 2) for r in reps],
+                    "value_is": "median"},
         "step": {"bytes": int(sb), "gbs": round(sb / (ms * 1e-3) / 1e9, 1),
                  "hbm_frac": round(sb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "hbm_frac_of_measured_read": round(sb / (ms * 1e-3) / 1e9 / hbm["read_gbs"], 4),
                  "active_ffn_rows_last_layer": nnz},
+        "hbm_measured": hbm,
         "kernels": {k: {"ms_per_step": round(v["ms_per_step"], 4),
                         "launches_per_step": v["launches_per_step"]} for k, v in kb.items()},
         "batched": batched_res + big_res,

@@ -175,7 +175,10 @@ int rwkv7_prefill_seq(rwkv7_model* model, void* pool, int64_t n_slots, int32_t s
  *   occ = occ*decay[b]; then occ[id] += 1.
  * presence, frequency, decay: device fp32[B]; ids_out: device int32[B] (may
  * be passed straight back as the next step's token_ids).  `ws` is the
- * decode workspace (or any buffer of rwkv7_greedy_workspace_bytes). */
+ * decode workspace (or any buffer of rwkv7_greedy_workspace_bytes).
+ * A row whose slot lies outside [0, n_slots) (RWKV7_ERR_SLOT_RANGE) or
+ * repeats an earlier row's slot (RWKV7_ERR_SLOT_DUP) reads and updates no
+ * occurrences: its id is the pick on its unpenalised logits. */
 int rwkv7_greedy_workspace_bytes(int32_t B, int32_t V, uint64_t* bytes);
 int rwkv7_greedy(int32_t B, int32_t V, const float* logits, float* occ_pool, int64_t n_slots,
                  const int32_t* slot_idx, const float* presence, const float* frequency,
@@ -201,7 +204,9 @@ int rwkv7_greedy(int32_t B, int32_t V, const float* logits, float* occ_pool, int
  *   temperature not > 0: z = l' and top_k = 1 (the greedy pick);
  *   occ = occ*decay[b]; then occ[id] += 1.
  * Every decision is integer arithmetic, so the result does not depend on
- * timing.  A row without candidates gives 0 and RWKV7_ERR_ALL_NAN.
+ * timing.  A row without candidates gives 0 and RWKV7_ERR_ALL_NAN.  Slots
+ * outside the pool or repeated as in rwkv7_greedy set RWKV7_ERR_SLOT_RANGE /
+ * RWKV7_ERR_SLOT_DUP, and that row reads and updates no occurrences.
  * temperature, top_p, uniform, presence, frequency, decay: device fp32[B];
  * top_k: device int32[B]; forbidden: device uint8[V] or NULL; ids_out:
  * device int32[B].  The caller draws the uniforms.  `ws`: a device buffer of
@@ -341,6 +346,15 @@ const char* rwkv7_kernel_name(const rwkv7_model* model, int32_t kernel_class, in
  * lets a test check the skipped set exactly. */
 int rwkv7_debug_cmix_buffers(const rwkv7_model* model, void* ws, int32_t B, void** pre,
                              void** mask, void** active, void** active_count);
+
+/* Device address, inside `ws`, of the time-mix output of the last layer of
+ * the most recent decode step of B rows made with this workspace, before
+ * the output projection: (GroupNorm(S r) + bonus * v) * g per row, [B][C].
+ * *is_f16 = 1 when that step stores it in fp16 (the MFMA path, B above the
+ * GEMV limit), 0 for fp32.  The RWKV-Server article's section 2 table gives
+ * the per-token state update whose readout this is; the hook lets a test
+ * compare the WKV stage on its own, ahead of W_o. */
+int rwkv7_debug_wkv_out(const rwkv7_model* model, void* ws, int32_t B, void** out, int32_t* is_f16);
 
 #ifdef __cplusplus
 }

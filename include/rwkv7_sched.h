@@ -169,22 +169,33 @@ int rwkv7_sched_poll(rwkv7_sched* s, rwkv7_sched_event* out, int32_t cap, int32_
 int rwkv7_sched_task_state(const rwkv7_sched* s, int64_t task_id, int32_t* state);
 
 /* A backend over a loaded model: reset = rwkv7_reset_slots plus zeroing the
- * slot's row of occ_pool; prefill = rwkv7_prefill_seq; step =
+ * slot's row of occ_pool; prefill = rwkv7_prefill_seq, in pieces of at most
+ * max_T tokens (prefilling a then b lands where a || b does); step =
  * rwkv7_decode_step over the B rows, then rwkv7_sample over the first
  * n_sample rows' logits, on `stream`, with one host-to-device copy of the
  * round's arrays and one synchronisation for the ids.  A non-zero device
  * error word of either workspace fails the round with RWKV7_EDEVICE.
- * pool / n_slots / ws: as for rwkv7_decode_step (ws sized for max_B rows);
- * occ_pool: device fp32[n_slots * vocab]; forbidden: device uint8[vocab] or
- * NULL; sample_ws: rwkv7_sample_workspace_bytes(max_B, vocab) bytes.  The
- * backend allocates its own staging (device and pinned host memory for
- * max_B rows and max_B logits rows); rwkv7_sched_gpu_backend_free releases
- * it.  max_B <= n_slots; a scheduler driving it needs max_batch <= max_B
- * (a larger round fails with RWKV7_EINVAL and is not advanced). */
+ * pool / n_slots / ws: as for rwkv7_decode_step (ws sized for max_B rows and
+ * max_T prefill tokens); occ_pool: device fp32[n_slots * vocab]; forbidden:
+ * device uint8[vocab] or NULL; sample_ws: rwkv7_sample_workspace_bytes(max_B,
+ * vocab) bytes.
+ * Ownership: the backend allocates nothing.  Its staging lives in two
+ * caller-owned, 256-byte aligned buffers whose sizes
+ * rwkv7_sched_gpu_backend_bytes gives: dev_buf (device memory: the round's
+ * arrays, the ids, max_B logits rows, max_T prefill tokens) and host_buf
+ * (pinned host memory, e.g. hipHostMalloc or torch's pin_memory; pageable
+ * memory works but makes every copy synchronous).  Both must outlive the
+ * backend; rwkv7_sched_gpu_backend_free releases only its host-side record.
+ * EINVAL for NULL pointers, max_B outside [1, n_slots], max_T < 1 or
+ * misaligned buffers; ESHAPE for buffers or a sample workspace too small.
+ * A scheduler driving it needs max_batch <= max_B (a larger round fails
+ * with RWKV7_EINVAL and is not advanced). */
+int rwkv7_sched_gpu_backend_bytes(const rwkv7_model* model, int32_t max_B, int32_t max_T,
+                                  uint64_t* device_bytes, uint64_t* host_bytes);
 int rwkv7_sched_gpu_backend(rwkv7_model* model, void* pool, int64_t n_slots, float* occ_pool,
-                            const uint8_t* forbidden, int32_t max_B, void* ws, uint64_t ws_bytes,
-                            void* sample_ws, uint64_t sample_ws_bytes, void* stream,
-                            rwkv7_sched_backend* out);
+                            const uint8_t* forbidden, int32_t max_B, int32_t max_T, void* ws, uint64_t ws_bytes,
+                            void* sample_ws, uint64_t sample_ws_bytes, void* dev_buf, uint64_t dev_bytes,
+                            void* host_buf, uint64_t host_bytes, void* stream, rwkv7_sched_backend* out);
 int rwkv7_sched_gpu_backend_free(rwkv7_sched_backend* backend);
 
 /* Attach a prefix-state cache (include/rwkv7_prefix.h; NULL detaches) to a

@@ -146,6 +146,7 @@ def lib() -> ctypes.CDLL:
         "rwkv7_get_option": [vp, i32, P(i64)],
         "rwkv7_kernel_timing": [vp, i32, P(ctypes.c_double), P(i64), i32],
         "rwkv7_debug_cmix_buffers": [vp, vp, i32, P(vp), P(vp), P(vp), P(vp)],
+        "rwkv7_debug_wkv_out": [vp, vp, i32, P(vp), P(i32)],
         "rwkv7_time_kernel": [vp, vp, i64, i32, vp, vp, vp, i32, i32, i32, vp, u64, vp,
                               P(ctypes.c_double)],
         "rwkv7_sched_create": [P(SchedConfig), P(SchedBackend), P(vp)],
@@ -155,7 +156,9 @@ def lib() -> ctypes.CDLL:
         "rwkv7_sched_step": [vp, P(SchedStats)],
         "rwkv7_sched_poll": [vp, P(SchedEvent), i32, P(i32)],
         "rwkv7_sched_task_state": [vp, i64, P(i32)],
-        "rwkv7_sched_gpu_backend": [vp, vp, i64, vp, vp, i32, vp, u64, vp, u64, vp, P(SchedBackend)],
+        "rwkv7_sched_gpu_backend_bytes": [vp, i32, i32, P(u64), P(u64)],
+        "rwkv7_sched_gpu_backend": [vp, vp, i64, vp, vp, i32, i32, vp, u64, vp, u64, vp, u64, vp, u64, vp,
+                                    P(SchedBackend)],
         "rwkv7_sched_gpu_backend_free": [P(SchedBackend)],
         "rwkv7_sched_gpu_backend_set_cache": [P(SchedBackend), vp],
         "rwkv7_sched_gpu_backend_counts": [P(SchedBackend), P(i64), P(i64)],
@@ -369,6 +372,15 @@ def rwkv7_debug_cmix_buffers(model: int, ws, B: int) -> Tuple[int, int, int, int
     return tuple(o.value for o in out)
 
 
+def rwkv7_debug_wkv_out(model: int, ws, B: int) -> Tuple[int, bool]:
+    """(device address inside ``ws`` of the last layer's time-mix output
+    before W_o, [B][C], whether it is fp16)."""
+    out, f16 = ctypes.c_void_p(), ctypes.c_int32()
+    _check(lib().rwkv7_debug_wkv_out(model, ws.data_ptr(), B, ctypes.byref(out), ctypes.byref(f16)),
+           "rwkv7_debug_wkv_out")
+    return out.value, bool(f16.value)
+
+
 # ------------------------------------------------------------------ scheduler
 def sched_backend(reset, prefill, step) -> SchedBackend:
     """A backend whose callbacks are Python callables (used by host-logic tests):
@@ -453,13 +465,34 @@ def rwkv7_sched_task_state(s: int, task_id: int) -> int:
     return v.value
 
 
+def rwkv7_sched_gpu_backend_bytes(model: int, max_B: int, max_T: int) -> Tuple[int, int]:
+    """(device bytes, pinned host bytes) of the GPU backend's staging."""
+    d, h = ctypes.c_uint64(), ctypes.c_uint64()
+    _check(lib().rwkv7_sched_gpu_backend_bytes(model, max_B, max_T, ctypes.byref(d), ctypes.byref(h)),
+           "rwkv7_sched_gpu_backend_bytes")
+    return d.value, h.value
+
+
 def rwkv7_sched_gpu_backend(model: int, pool, n_slots: int, occ_pool, forbidden, max_B: int, ws, sample_ws,
-                            stream=None) -> SchedBackend:
+                            max_T: int, dev_buf=None, host_buf=None, stream=None) -> SchedBackend:
+    """The GPU backend over caller-owned staging.  dev_buf / host_buf (uint8
+    tensors, device and pinned host) default to torch allocations of the sizes
+    rwkv7_sched_gpu_backend_bytes gives; the returned record keeps them alive."""
+    import torch
+    if dev_buf is None or host_buf is None:
+        nd, nh = rwkv7_sched_gpu_backend_bytes(model, max_B, max_T)
+        if dev_buf is None:
+            dev_buf = torch.empty(nd, dtype=torch.uint8, device=pool.device)
+        if host_buf is None:
+            host_buf = torch.empty(nh, dtype=torch.uint8, pin_memory=True)
     be = SchedBackend()
     _check(lib().rwkv7_sched_gpu_backend(model, pool.data_ptr(), n_slots, _ptr(occ_pool), _ptr(forbidden),
-                                         max_B, ws.data_ptr(), ws.numel(), sample_ws.data_ptr(),
-                                         sample_ws.numel(), _stream(stream), ctypes.byref(be)),
+                                         max_B, max_T, ws.data_ptr(), ws.numel(), sample_ws.data_ptr(),
+                                         sample_ws.numel(), dev_buf.data_ptr(), dev_buf.numel(),
+                                         host_buf.data_ptr(), host_buf.numel(), _stream(stream),
+                                         ctypes.byref(be)),
            "rwkv7_sched_gpu_backend")
+    be.buffers = (dev_buf, host_buf)
     return be
 
 
@@ -566,6 +599,7 @@ class Model:
         self.cfg = cfg
         self.device = torch.device(device)
         self.n_slots = n_slots
+        self.max_B, self.max_T = max_B, max_T
         self.packed = torch.empty(rwkv7_packed_bytes(cfg), dtype=torch.uint8, device=self.device)
         self.handle = rwkv7_load(cfg, tensors, self.packed)
         nbytes, self.counter_offset = rwkv7_state_bytes(cfg, n_slots)

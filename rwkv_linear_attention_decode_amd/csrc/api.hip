@@ -1399,4 +1399,13 @@ int rwkv7_debug_cmix_buffers(const rwkv7_model* m, void* ws, int32_t B, void** p
   return RWKV7_OK;
 }
 
+int rwkv7_debug_wkv_out(const rwkv7_model* m, void* ws, int32_t B, void** out, int32_t* is_f16) {
+  if (!m || !ws || !out || !is_f16) return fail(RWKV7_EINVAL, "null argument");
+  if (B < 1) return fail(RWKV7_EINVAL, "B must be >= 1");
+  const Ws w = ws_layout(m->d, B, (char*)ws);
+  *out = w.yg;
+  *is_f16 = decode_path(m, B).gemv ? 0 : 1;
+  return RWKV7_OK;
+}
+
 }  // extern "C"

@@ -686,15 +686,26 @@ RW_DEV bool better(float v, int i, float bv, int bi) {
 
 constexpr int GREEDY_PER_BLOCK = 2048;
 
+// Error bits of row b's slot: outside the pool, or listed by an earlier row.
+// Such a row reads and updates no occurrence row (two rows naming one slot
+// would otherwise update it from two workgroups at once).
+RW_DEV uint32_t row_slot_bits(const int* slot_idx, int b, int64_t n_slots) {
+  const int slot = slot_idx[b];
+  if (slot < 0 || (int64_t)slot >= n_slots) return ERRB_SLOT_RANGE;
+  for (int j = 0; j < b; ++j)
+    if (slot_idx[j] == slot) return ERRB_SLOT_DUP;
+  return 0u;
+}
+
 __global__ __launch_bounds__(256) void k_greedy_part(GreedyArgs a) {
   __shared__ float sv[256];
   __shared__ int si[256];
   const int b = blockIdx.x;
   const int blk = blockIdx.y;
   const int slot = a.slot_idx[b];
-  const bool ok = slot >= 0 && (int64_t)slot < a.n_slots;
-  if (!ok && blk == 0 && threadIdx.x == 0) set_err(a.err, ERRB_SLOT_RANGE);
-  float* occ = ok ? a.occ + (int64_t)slot * a.V : nullptr;
+  const uint32_t bad = row_slot_bits(a.slot_idx, b, a.n_slots);
+  if (bad && blk == 0 && threadIdx.x == 0) set_err(a.err, bad);
+  float* occ = bad ? nullptr : a.occ + (int64_t)slot * a.V;
   const float pres = a.presence[b], freq = a.frequency[b], dec = a.decay[b];
   const float* lg = a.logits + (int64_t)b * a.V;
   float bv = 0.f;
@@ -761,7 +772,7 @@ __global__ __launch_bounds__(64) void k_greedy_final(GreedyArgs a) {
     }
     a.ids[b] = id;
     const int slot = a.slot_idx[b];
-    if (slot >= 0 && (int64_t)slot < a.n_slots) {
+    if (!row_slot_bits(a.slot_idx, b, a.n_slots)) {
       float* o = a.occ + (int64_t)slot * a.V + id;
       *o = __fadd_rn(*o, 1.0f);
     }
@@ -934,7 +945,9 @@ __global__ __launch_bounds__(1024) void k_sample(SampleArgs a) {
   const int lane = t & 63, wave = t >> 6;
   const int V = a.V;
   const int slot = a.slot_idx[b];
-  float* occ = (slot >= 0 && (int64_t)slot < a.n_slots) ? a.occ + (int64_t)slot * V : nullptr;
+  const uint32_t bad = row_slot_bits(a.slot_idx, b, a.n_slots);
+  if (bad && t == 0) set_err(a.err, bad);
+  float* occ = bad ? nullptr : a.occ + (int64_t)slot * V;
   const float* lg = a.logits + (int64_t)b * V;
   uint32_t* key = a.key + (int64_t)b * V;
   uint32_t* wt = a.wt + (int64_t)b * V;

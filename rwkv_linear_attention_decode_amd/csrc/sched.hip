@@ -342,8 +342,30 @@ namespace {
 // Device and pinned staging of one round: int32 slots | tokens | top_k, then
 // fp32 temperature | top_p | presence | frequency | decay | uniform, max_B
 // entries each; the ids and both workspaces' error words come back in one
-// pinned block.
+// pinned block.  Both buffers are the caller's (rwkv7_sched_gpu_backend_bytes).
 constexpr int STAGE_ARRAYS = 9;
+
+uint64_t up256(uint64_t n) { return (n + 255) & ~(uint64_t)255; }
+
+// Byte offsets of the backend's pieces inside the caller's buffers.
+struct GbLayout {
+  uint64_t d_stage, d_ids, d_logits, d_tok, dev_bytes;
+  uint64_t h_stage, h_back, host_bytes;
+};
+
+GbLayout gb_layout(int max_B, int V, int max_T) {
+  GbLayout o;
+  const uint64_t stage = (uint64_t)STAGE_ARRAYS * max_B * 4;
+  o.d_stage = 0;
+  o.d_ids = o.d_stage + up256(stage);
+  o.d_logits = o.d_ids + up256((uint64_t)max_B * 4);
+  o.d_tok = o.d_logits + up256((uint64_t)max_B * V * 4);
+  o.dev_bytes = o.d_tok + up256((uint64_t)max_T * 4);
+  o.h_stage = 0;
+  o.h_back = up256(stage);
+  o.host_bytes = o.h_back + up256((uint64_t)(max_B + 2) * 4);
+  return o;
+}
 
 struct GpuBackend {
   rwkv7_model* model = nullptr;
@@ -351,19 +373,18 @@ struct GpuBackend {
   int64_t n_slots = 0;
   float* occ = nullptr;
   const uint8_t* forbidden = nullptr;
-  int max_B = 0, V = 0;
+  int max_B = 0, V = 0, max_T = 0;
   void* ws = nullptr;
   uint64_t ws_bytes = 0;
   void* sws = nullptr;
   uint64_t sws_bytes = 0;
   hipStream_t st = nullptr;
-  int32_t* h_stage = nullptr;  // pinned, STAGE_ARRAYS * max_B words
-  int32_t* d_stage = nullptr;
+  int32_t* h_stage = nullptr;  // caller's pinned buffer: STAGE_ARRAYS * max_B words
+  int32_t* d_stage = nullptr;  // caller's device buffer from here on
   int32_t* h_back = nullptr;   // pinned: ids[max_B], err[2]
   int32_t* d_ids = nullptr;
   float* d_logits = nullptr;   // [max_B * V]
-  int32_t* d_tok = nullptr;    // prefill tokens
-  int tok_cap = 0;
+  int32_t* d_tok = nullptr;    // prefill tokens, max_T per piece
   rwkv7_prefix_cache* cache = nullptr;
   int64_t restored = 0, prefilled = 0;
 };
@@ -398,19 +419,18 @@ int gb_prefill(void* ctx, int32_t slot, const int32_t* all_tokens, int32_t T_all
   const int32_t T = T_all - start;
   if (T == 0) return gb_hip(hipStreamSynchronize(g->st), "prefill sync");
   g->prefilled += T;
-  if (T > g->tok_cap) {
-    if (g->d_tok) hipFree(g->d_tok);
-    g->d_tok = nullptr;
-    g->tok_cap = 0;
-    int rc = gb_hip(hipMalloc((void**)&g->d_tok, (size_t)T * 4), "prefill token buffer");
+  // pieces of at most max_T tokens: prefilling a then b lands where a || b does.
+  // Each piece's copy is queued behind the previous piece's kernels on the same
+  // stream, so the token buffer is never overwritten while still being read.
+  int rc = RWKV7_OK;
+  for (int32_t done = 0; done < T; done += g->max_T) {
+    const int32_t n = T - done < g->max_T ? T - done : g->max_T;
+    rc = gb_hip(hipMemcpyAsync(g->d_tok, tokens + done, (size_t)n * 4, hipMemcpyHostToDevice, g->st),
+                "stage prefill tokens");
     if (rc) return rc;
-    g->tok_cap = T;
+    rc = rwkv7_prefill_seq(g->model, g->pool, g->n_slots, slot, g->d_tok, n, g->ws, g->ws_bytes, g->st);
+    if (rc) return rc;
   }
-  int rc = gb_hip(hipMemcpyAsync(g->d_tok, tokens, (size_t)T * 4, hipMemcpyHostToDevice, g->st),
-                  "stage prefill tokens");
-  if (rc) return rc;
-  rc = rwkv7_prefill_seq(g->model, g->pool, g->n_slots, slot, g->d_tok, T, g->ws, g->ws_bytes, g->st);
-  if (rc) return rc;
   if (g->cache) {
     rc = rwkv7_prefix_cache_store(g->cache, g->pool, g->n_slots, slot, all_tokens, T_all, g->st);
     if (rc) return rc;
@@ -462,29 +482,35 @@ int gb_step(void* ctx, const rwkv7_sched_batch* b, int32_t* ids_out) {
   return RWKV7_OK;
 }
 
-void gb_release(GpuBackend* g) {
-  if (g->h_stage) hipHostFree(g->h_stage);
-  if (g->h_back) hipHostFree(g->h_back);
-  if (g->d_stage) hipFree(g->d_stage);
-  if (g->d_ids) hipFree(g->d_ids);
-  if (g->d_logits) hipFree(g->d_logits);
-  if (g->d_tok) hipFree(g->d_tok);
-  delete g;
-}
+void gb_release(GpuBackend* g) { delete g; }  // the buffers stay the caller's
 
 }  // namespace
 
 extern "C" {
 
+int rwkv7_sched_gpu_backend_bytes(const rwkv7_model* model, int32_t max_B, int32_t max_T,
+                                  uint64_t* device_bytes, uint64_t* host_bytes) {
+  if (!model || !device_bytes || !host_bytes)
+    return sfail(RWKV7_EINVAL, "model, device_bytes and host_bytes must be non-NULL");
+  if (max_B < 1 || max_T < 1) return sfail(RWKV7_EINVAL, "max_B and max_T must be >= 1 (got %d, %d)", max_B, max_T);
+  const GbLayout o = gb_layout(max_B, lib_model_vocab(model), max_T);
+  *device_bytes = o.dev_bytes;
+  *host_bytes = o.host_bytes;
+  return RWKV7_OK;
+}
+
 int rwkv7_sched_gpu_backend(rwkv7_model* model, void* pool, int64_t n_slots, float* occ_pool,
-                            const uint8_t* forbidden, int32_t max_B, void* ws, uint64_t ws_bytes,
-                            void* sample_ws, uint64_t sample_ws_bytes, void* stream,
-                            rwkv7_sched_backend* out) {
-  if (!model || !pool || !occ_pool || !ws || !sample_ws || !out)
-    return sfail(RWKV7_EINVAL, "model, pool, occ_pool, ws, sample_ws and out must be non-NULL");
+                            const uint8_t* forbidden, int32_t max_B, int32_t max_T, void* ws, uint64_t ws_bytes,
+                            void* sample_ws, uint64_t sample_ws_bytes, void* dev_buf, uint64_t dev_bytes,
+                            void* host_buf, uint64_t host_bytes, void* stream, rwkv7_sched_backend* out) {
+  if (!model || !pool || !occ_pool || !ws || !sample_ws || !dev_buf || !host_buf || !out)
+    return sfail(RWKV7_EINVAL, "model, pool, occ_pool, ws, sample_ws, dev_buf, host_buf and out must be non-NULL");
   if (max_B < 1 || max_B > n_slots)
     return sfail(RWKV7_EINVAL, "max_B must lie in [1, n_slots] (got %d, n_slots %lld)", max_B,
                  (long long)n_slots);
+  if (max_T < 1) return sfail(RWKV7_EINVAL, "max_T must be >= 1 (got %d)", max_T);
+  if (((uintptr_t)dev_buf & 255) || ((uintptr_t)host_buf & 255))
+    return sfail(RWKV7_EINVAL, "dev_buf and host_buf must be 256-byte aligned");
   const int V = lib_model_vocab(model);
   uint64_t need = 0;
   int rc = rwkv7_sample_workspace_bytes(max_B, V, &need);
@@ -492,20 +518,24 @@ int rwkv7_sched_gpu_backend(rwkv7_model* model, void* pool, int64_t n_slots, flo
   if (sample_ws_bytes < need)
     return sfail(RWKV7_ESHAPE, "sample workspace of %llu bytes, %llu needed", (unsigned long long)sample_ws_bytes,
                  (unsigned long long)need);
+  const GbLayout o = gb_layout(max_B, V, max_T);
+  if (dev_bytes < o.dev_bytes || host_bytes < o.host_bytes)
+    return sfail(RWKV7_ESHAPE, "backend buffers of %llu (device) / %llu (host) bytes, %llu / %llu needed",
+                 (unsigned long long)dev_bytes, (unsigned long long)host_bytes,
+                 (unsigned long long)o.dev_bytes, (unsigned long long)o.host_bytes);
   GpuBackend* g = new GpuBackend;
   g->model = model; g->pool = pool; g->n_slots = n_slots; g->occ = occ_pool; g->forbidden = forbidden;
-  g->max_B = max_B; g->V = V; g->ws = ws; g->ws_bytes = ws_bytes; g->sws = sample_ws;
+  g->max_B = max_B; g->V = V; g->max_T = max_T; g->ws = ws; g->ws_bytes = ws_bytes; g->sws = sample_ws;
   g->sws_bytes = sample_ws_bytes; g->st = (hipStream_t)stream;
-  const size_t stage = (size_t)STAGE_ARRAYS * max_B * 4;
-  if ((rc = gb_hip(hipHostMalloc((void**)&g->h_stage, stage), "pinned staging")) ||
-      (rc = gb_hip(hipHostMalloc((void**)&g->h_back, (size_t)(max_B + 2) * 4), "pinned ids")) ||
-      (rc = gb_hip(hipMalloc((void**)&g->d_stage, stage), "device staging")) ||
-      (rc = gb_hip(hipMalloc((void**)&g->d_ids, (size_t)max_B * 4), "device ids")) ||
-      (rc = gb_hip(hipMalloc((void**)&g->d_logits, (size_t)max_B * V * 4), "logits"))) {
-    gb_release(g);
-    return rc;
-  }
-  std::memset(g->h_stage, 0, stage);
+  char* d = (char*)dev_buf;
+  char* h = (char*)host_buf;
+  g->d_stage = (int32_t*)(d + o.d_stage);
+  g->d_ids = (int32_t*)(d + o.d_ids);
+  g->d_logits = (float*)(d + o.d_logits);
+  g->d_tok = (int32_t*)(d + o.d_tok);
+  g->h_stage = (int32_t*)(h + o.h_stage);
+  g->h_back = (int32_t*)(h + o.h_back);
+  std::memset(g->h_stage, 0, (size_t)STAGE_ARRAYS * max_B * 4);
   out->ctx = g;
   out->reset = gb_reset;
   out->prefill = gb_prefill;

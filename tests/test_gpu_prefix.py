@@ -174,7 +174,7 @@ def test_scheduler_backend_reuses_prefixes(weights, W, R):
     sws = torch.zeros(R.rwkv7_sample_workspace_bytes(max_b, V), dtype=torch.uint8, device="cuda")
     arena = torch.empty(8 * R.rwkv7_snapshot_bytes(m.cfg) + 2048, dtype=torch.uint8, device="cuda")
     cache = R.rwkv7_prefix_cache_create(m.handle, arena)
-    be = R.rwkv7_sched_gpu_backend(m.handle, m.pool, n_slots, occ, None, max_b, m.ws, sws)
+    be = R.rwkv7_sched_gpu_backend(m.handle, m.pool, n_slots, occ, None, max_b, m.ws, sws, m.max_T)
     R.rwkv7_sched_gpu_backend_set_cache(be, cache)
     s = R.rwkv7_sched_create(R.SchedConfig(max_b, 1, 0, 10, V), be)
     p1 = toks(40, 30).tolist()
@@ -219,7 +219,7 @@ def test_scheduler_restores_from_host_tier_and_stops(weights, W, R):
     cache = R.rwkv7_prefix_cache_create(m.handle, arena, host)
     occ = torch.zeros(n_slots * V, device="cuda")
     sws = torch.zeros(R.rwkv7_sample_workspace_bytes(max_b, V), dtype=torch.uint8, device="cuda")
-    be = R.rwkv7_sched_gpu_backend(m.handle, m.pool, n_slots, occ, None, max_b, m.ws, sws)
+    be = R.rwkv7_sched_gpu_backend(m.handle, m.pool, n_slots, occ, None, max_b, m.ws, sws, m.max_T)
     R.rwkv7_sched_gpu_backend_set_cache(be, cache)
     s = R.rwkv7_sched_create(R.SchedConfig(max_b, 1, 0, 10, V), be)
     p1, p2 = toks(60, 20).tolist(), toks(61, 24).tolist()

@@ -83,14 +83,15 @@ def replay(W, prompt, prm, stream, forb):
 
 def test_scheduler_streams_match_oracle(weights, W, R):
     n_slots, max_b = 6, 6
-    m = R.Model.from_numpy(S, weights, n_slots=n_slots, max_B=max_b, max_T=64)
+    # max_T 16: prompts of 17..64 tokens are prefilled by the backend in 16-token pieces
+    m = R.Model.from_numpy(S, weights, n_slots=n_slots, max_B=max_b, max_T=16)
     occ = torch.zeros(n_slots * V, device="cuda")
     forb = np.zeros(V, bool)
     forb[:8] = True
     forb[500:520] = True
     forb_t = torch.tensor(forb.astype(np.uint8), device="cuda")
     sws = torch.zeros(R.rwkv7_sample_workspace_bytes(max_b, V), dtype=torch.uint8, device="cuda")
-    be = R.rwkv7_sched_gpu_backend(m.handle, m.pool, n_slots, occ, forb_t, max_b, m.ws, sws)
+    be = R.rwkv7_sched_gpu_backend(m.handle, m.pool, n_slots, occ, forb_t, max_b, m.ws, sws, m.max_T)
     s = R.rwkv7_sched_create(R.SchedConfig(max_b, 2, 3, 10, V), be)
     kinds = [(0.0, 1.0, 0), (1.0, 0.3, 0), (0.8, 0.9, 5), (1.3, 1.0, 0)]
     tasks = {}
@@ -142,8 +143,25 @@ def test_gpu_backend_rejects_bad_sizes(weights, R):
     occ = torch.zeros(2 * V, device="cuda")
     small = torch.zeros(64, dtype=torch.uint8, device="cuda")
     with pytest.raises(R.RWKV7Error):
-        R.rwkv7_sched_gpu_backend(m.handle, m.pool, 2, occ, None, 2, m.ws, small)
+        R.rwkv7_sched_gpu_backend(m.handle, m.pool, 2, occ, None, 2, m.ws, small, m.max_T)
     sws = torch.zeros(R.rwkv7_sample_workspace_bytes(3, V), dtype=torch.uint8, device="cuda")
     with pytest.raises(R.RWKV7Error):
-        R.rwkv7_sched_gpu_backend(m.handle, m.pool, 2, occ, None, 3, m.ws, sws)
+        R.rwkv7_sched_gpu_backend(m.handle, m.pool, 2, occ, None, 3, m.ws, sws, m.max_T)
+    # caller-owned staging: too small (ESHAPE), misaligned (EINVAL), max_T < 1 (EINVAL)
+    sws2 = torch.zeros(R.rwkv7_sample_workspace_bytes(2, V), dtype=torch.uint8, device="cuda")
+    nd, nh = R.rwkv7_sched_gpu_backend_bytes(m.handle, 2, m.max_T)
+    assert nd >= 2 * V * 4 + m.max_T * 4 and nh >= 9 * 2 * 4
+    dev = torch.empty(nd + 256, dtype=torch.uint8, device="cuda")
+    host = torch.empty(nh + 256, dtype=torch.uint8, pin_memory=True)
+    with pytest.raises(R.RWKV7Error) as e:
+        R.rwkv7_sched_gpu_backend(m.handle, m.pool, 2, occ, None, 2, m.ws, sws2, m.max_T, dev[:nd - 256], host)
+    assert e.value.status == R.RWKV7_ESHAPE
+    with pytest.raises(R.RWKV7Error) as e:
+        R.rwkv7_sched_gpu_backend(m.handle, m.pool, 2, occ, None, 2, m.ws, sws2, m.max_T, dev[4:], host)
+    assert e.value.status == R.RWKV7_EINVAL
+    with pytest.raises(R.RWKV7Error) as e:
+        R.rwkv7_sched_gpu_backend(m.handle, m.pool, 2, occ, None, 2, m.ws, sws2, 0, dev, host)
+    assert e.value.status == R.RWKV7_EINVAL
+    be = R.rwkv7_sched_gpu_backend(m.handle, m.pool, 2, occ, None, 2, m.ws, sws2, m.max_T, dev, host)
+    R.rwkv7_sched_gpu_backend_free(be)
     m.close()

@@ -359,6 +359,44 @@ def test_device_error_flags(model, R):
     assert model.poll_error() == 0
 
 
+def test_selection_slot_errors(model, R):
+    """rwkv7_greedy and rwkv7_sample with a slot listed twice or outside the
+    pool: the error bit is set, the first row of a repeated slot keeps its
+    occurrence update, the later row and the out-of-range row touch none, and
+    their picks are the plain argmax of their logits."""
+    V = S.vocab
+    g = torch.Generator().manual_seed(3)
+    logits = torch.randn(3, V, generator=g).cuda()
+    occ0 = torch.rand(NSLOT, V, generator=g).cuda() * (torch.rand(NSLOT, V, generator=g).cuda() < 0.1)
+    ones = torch.ones(3, device="cuda")
+    dec = torch.full((3,), 0.5, device="cuda")
+    ids = torch.zeros(3, dtype=torch.int32, device="cuda")
+    sws = torch.zeros(R.rwkv7_sample_workspace_bytes(3, V), dtype=torch.uint8, device="cuda")
+    plain = logits.argmax(1).cpu().numpy()
+    for use_sample in (False, True):
+        for slots, bit in (([2, 5, 2], R.ERR_SLOT_DUP), ([2, 5, NSLOT + 1], R.ERR_SLOT_RANGE)):
+            occ = occ0.clone()
+            if use_sample:
+                R.rwkv7_sample(logits, occ, NSLOT, dev(slots), ones, ones, dec, torch.zeros(3, device="cuda"),
+                               ones, torch.zeros(3, dtype=torch.int32, device="cuda"), None,
+                               torch.full((3,), 0.5, device="cuda"), ids, sws)
+                flags = R.rwkv7_poll_error(sws)
+            else:
+                R.rwkv7_greedy(logits, occ, NSLOT, dev(slots), ones, ones, dec, ids, model.ws)
+                flags = model.poll_error()
+            assert flags == bit, (use_sample, slots, flags)
+            got = ids.cpu().numpy()
+            assert got[2] == plain[2]                       # unpenalised pick on the flagged row
+            o = occ.cpu().numpy()
+            o0 = occ0.cpu().numpy()
+            untouched = [s for s in range(NSLOT) if s not in (2, 5)]
+            assert np.array_equal(o[untouched], o0[untouched])
+            for b, s in ((0, 2), (1, 5)):                   # the rows that own their slots
+                want = (o0[s] * np.float32(0.5)).astype(np.float32)
+                want[got[b]] += np.float32(1.0)
+                assert np.array_equal(o[s], want), (use_sample, slots, b)
+
+
 def test_host_errors_with_model(model, R):
     logits = torch.empty(1, S.vocab, device="cuda")
     with pytest.raises(R.RWKV7Error):
