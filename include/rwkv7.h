@@ -185,6 +185,21 @@ int rwkv7_greedy(int32_t B, int32_t V, const float* logits, float* occ_pool, int
                  const float* decay, int32_t* ids_out, void* ws, uint64_t ws_bytes,
                  void* stream);
 
+/* rwkv7_greedy for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same selection and occurrence update, bit for bit, with its partial
+ * results in a static device array of the library (64 KB per GPU, held until
+ * the process ends) instead of a caller workspace.  It calls no hipMalloc /
+ * hipFree.  Limit: B * ceil(V / 2048) <= 8192 row-blocks (B <= 256 at
+ * V = 65536); larger calls fail with RWKV7_ESHAPE before any launch.  Device
+ * error bits (as for rwkv7_greedy) are ORed into *flags_out (device uint32,
+ * cleared by the caller).  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (two streams, two threads) race and must be
+ * serialised by the caller.  The stream must belong to the current device. */
+int rwkv7_greedy_noalloc(int32_t B, int32_t V, const float* logits, float* occ_pool, int64_t n_slots,
+                         const int32_t* slot_idx, const float* presence, const float* frequency,
+                         const float* decay, int32_t* ids_out, uint32_t* flags_out, void* stream);
+
 /* Penalised temperature / top-k / top-p sampling over logits [B*V] (device
  * fp32, V <= 65536).  The Albatross article (RWKV-Runner backend) names the
  * adapter's sampling defaults (temperature 1.0, top_p 0.3, top_k 0) and the

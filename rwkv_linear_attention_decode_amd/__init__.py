@@ -139,6 +139,7 @@ def lib() -> ctypes.CDLL:
         "rwkv7_prefill_seq": [vp, vp, i64, i32, vp, i32, vp, u64, vp],
         "rwkv7_greedy_workspace_bytes": [i32, i32, P(u64)],
         "rwkv7_greedy": [i32, i32, vp, vp, i64, vp, vp, vp, vp, vp, vp, u64, vp],
+        "rwkv7_greedy_noalloc": [i32, i32, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp],
         "rwkv7_sample_workspace_bytes": [i32, i32, P(u64)],
         "rwkv7_sample": [i32, i32, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, u64, vp],
         "rwkv7_poll_error": [vp, vp, P(ctypes.c_uint32)],
@@ -301,6 +302,16 @@ def rwkv7_greedy(logits, occ_pool, n_slots: int, slot_idx, presence, frequency, 
     _check(lib().rwkv7_greedy(B, V, _ptr(logits), _ptr(occ_pool), n_slots, _ptr(slot_idx),
                               _ptr(presence), _ptr(frequency), _ptr(decay), _ptr(ids_out),
                               ws.data_ptr(), ws.numel(), _stream(stream)), "rwkv7_greedy")
+
+
+def rwkv7_greedy_noalloc(logits, occ_pool, n_slots: int, slot_idx, presence, frequency, decay, ids_out,
+                         flags_out, stream=None):
+    """rwkv7_greedy without a workspace (its partials in the library's static
+    device array); device error bits are ORed into flags_out (uint32/int32 [1])."""
+    B, V = logits.shape
+    _check(lib().rwkv7_greedy_noalloc(B, V, _ptr(logits), _ptr(occ_pool), n_slots, _ptr(slot_idx),
+                                      _ptr(presence), _ptr(frequency), _ptr(decay), _ptr(ids_out),
+                                      _ptr(flags_out), _stream(stream)), "rwkv7_greedy_noalloc")
 
 
 def rwkv7_sample_workspace_bytes(B: int, V: int) -> int:

@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <utility>
 #include <string>
 #include <tuple>
@@ -1111,6 +1112,71 @@ int rwkv7_greedy(int32_t B, int32_t V, const float* logits, float* occ_pool, int
   const uint64_t tail = (ws_bytes - 2 * part) / ALIGN * ALIGN;
   a.part_val = (float*)(base + tail);
   a.part_idx = (int*)(base + tail + part);
+  a.B = B; a.V = V;
+  HIP_TRY(launch_greedy(a, (hipStream_t)stream), "greedy");
+  return RWKV7_OK;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------ allocation-free greedy
+// The partial (max, index) results of rwkv7_greedy_noalloc live in this
+// file-scope device array, one copy per GPU, kept until the process ends:
+// value partials [B * nblk] fp32 at offset 0, index partials [B * nblk] int32
+// at offset GREEDY_NOALLOC_PART.  In host code `scratch` is only a stand-in
+// for the symbol; its device address comes from hipGetSymbolAddress.
+namespace {
+constexpr uint64_t GREEDY_NOALLOC_PART = 32768;   // bytes per partial array: 8192 (row, block) pairs
+static __device__ __align__(256) unsigned char scratch[2 * GREEDY_NOALLOC_PART];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up once per device).
+int scratch_address(void** out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(RWKV7_ENOTSUP, "device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(RWKV7_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return RWKV7_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int rwkv7_greedy_noalloc(int32_t B, int32_t V, const float* logits, float* occ_pool, int64_t n_slots,
+                         const int32_t* slot_idx, const float* presence, const float* frequency,
+                         const float* decay, int32_t* ids_out, uint32_t* flags_out, void* stream) {
+  if (B < 1 || V < 1) return fail(RWKV7_EINVAL, "B and V must be >= 1");
+  if (n_slots < 1) return fail(RWKV7_EINVAL, "n_slots must be >= 1");
+  if (!logits || !occ_pool || !slot_idx || !presence || !frequency || !decay || !ids_out || !flags_out)
+    return fail(RWKV7_EINVAL, "null pointer argument");
+  const int nblk = greedy_blocks(V);
+  if ((uint64_t)B * nblk * 4 > GREEDY_NOALLOC_PART)
+    return fail(RWKV7_ESHAPE, "B * ceil(V / 2048) = %lld exceeds the %llu row-blocks of the static scratch "
+                "(e.g. B <= 256 at V = 65536)", (long long)B * nblk,
+                (unsigned long long)(GREEDY_NOALLOC_PART / 4));
+  void* base = nullptr;
+  int rc = scratch_address(&base);
+  if (rc) return rc;
+  GreedyArgs a;
+  a.logits = logits; a.occ = occ_pool; a.n_slots = n_slots; a.slot_idx = slot_idx;
+  a.presence = presence; a.frequency = frequency; a.decay = decay; a.ids = ids_out;
+  a.nblk = nblk;
+  a.err = flags_out;
+  // every (row, block) partial is written by the first pass before the second reads it,
+  // so nothing in the array needs clearing between calls
+  a.part_val = (float*)base;
+  a.part_idx = (int*)((char*)base + GREEDY_NOALLOC_PART);
   a.B = B; a.V = V;
   HIP_TRY(launch_greedy(a, (hipStream_t)stream), "greedy");
   return RWKV7_OK;
