@@ -192,31 +192,22 @@ def time_repeats(run_step, steps: int, repeats: int):
     return out
 
 
-def hbm_attainable():
-    """Measured HBM bandwidth of plain streaming kernels on a 4 GiB buffer
-    (far beyond the 256 MB MALL): a full read (sum of fp32 elements) and a
-    device-to-device copy (read + write).  Reported beside the 8 TB/s peak
-    that the roofline fractions use."""
+def hbm_attainable(R):
+    """Measured streaming-read bandwidth (rwkv7_read_bandwidth: every 16-byte
+    chunk once, non-temporal and plain loads) of a 4 GiB buffer, far beyond
+    the 256 MB MALL: the attainable HBM read rate, reported beside the 8 TB/s
+    peak that the roofline fractions use.  Also the re-read rate of a 64 MB
+    buffer (plain loads), which the MALL can serve between kernels."""
     import torch
-    n = 1 << 30
-    x = torch.ones(n, dtype=torch.float32, device="cuda")
-    y = torch.empty_like(x)
-    res = {}
-    for name, fn, nbytes in (("read", lambda: x.sum(), 4 * n), ("copy", lambda: y.copy_(x), 8 * n)):
-        fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ts = []
-        for _ in range(5):
-            e0.record()
-            fn()
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e-3)
-        res[f"{name}_gbs"] = round(nbytes / float(np.median(ts)) / 1e9, 1)
-    del x, y
+    big = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    small = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    res = {"read_gbs": round(R.rwkv7_read_bandwidth(big, True, 5), 1),
+           "read_plain_gbs": round(R.rwkv7_read_bandwidth(big, False, 5), 1),
+           "reread_64mb_gbs": round(R.rwkv7_read_bandwidth(small, False, 20), 1),
+           "how": "rwkv7_read_bandwidth: 8 workgroups x 256 threads per CU, grid-stride 16-byte loads, "
+                  "4 GiB buffer (5 launches after one warm-up); re-read: a 64 MB buffer, 20 launches"}
+    del big, small
     torch.cuda.empty_cache()
-    res["how"] = "torch sum (read) and copy_ (read + write) of a 4 GiB fp32 buffer, median of 5, HIP events"
     return res
 
 
@@ -652,8 +643,9 @@ def main():
     m, weights = build_model(R, shape, n_slots=n_slots, max_B=max([1] + Bs + Ss),
                              max_T=max([512] + Ts))
 
-    hbm = hbm_attainable()
-    log(f"[bench] attainable HBM: read {hbm['read_gbs']} GB/s, copy {hbm['copy_gbs']} GB/s")
+    hbm = hbm_attainable(R)
+    log(f"[bench] streaming read: {hbm['read_gbs']} GB/s (4 GiB, non-temporal), {hbm['read_plain_gbs']} GB/s "
+        f"(plain); 64 MB re-read {hbm['reread_64mb_gbs']} GB/s")
     dt, reps, nnz, kb, run_step, slot, tok, logits = decode_b1(R, args, shape, m)
     ms = dt / args.steps * 1e3
     sb = step_bytes(shape, 1, nnz, True)

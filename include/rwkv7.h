@@ -296,7 +296,9 @@ const char* rwkv7_last_error(void);
    with loop 3, and T in {2, 4}, N = 8 with loop 4, both with 64-deep stages), the K stage depth
    KKK (32, 64 or 128), the K loop P (0 plain, 1 pipelined LDS reads, 2 two stages of global
    loads in flight, 3 stages loaded straight into a three-deep LDS ring, 4 the same with
-   eight waves (T, N in {2, 4}); 3 and 4 fall back to 2 (0 for 4 x 4 tiles) where K is not a
+   eight waves (T, N in {2, 4}), 5 a deeper LDS ring of as many stages as fit about 144 KB
+   (up to nine; one workgroup per CU), 6 the same in about 72 KB (two per CU), for KKK in
+   {64, 128}; 3 to 6 fall back to 2 (0 for 4 x 4 tiles) where K is not a
    multiple of KKK) and the K split S (0 automatic); e.g. 2206430 = 64 x 64
    tiles, 64-deep stages, loop 3, automatic split.  Unsupported combinations fail with
    EINVAL. */
@@ -344,6 +346,17 @@ int rwkv7_time_kernel(rwkv7_model* model, void* pool, int64_t n_slots, int32_t B
                       const int32_t* slot_idx, const int32_t* token_ids, float* logits_out,
                       int32_t kernel_class, int32_t layer, int32_t iters, void* ws,
                       uint64_t ws_bytes, void* stream, double* avg_ms);
+
+/* Measured streaming-read bandwidth: `iters` back-to-back launches of a
+ * plain kernel that reads every 16-byte chunk of `buf` (device memory,
+ * `bytes` long) once (8 workgroups of 256 threads per CU, grid-stride,
+ * non-temporal loads when `nontemporal` != 0), after one untimed launch;
+ * synchronises `stream` and returns GB/s (1e9 bytes) in *gbs.  The buffer is
+ * only read.  For reporting the attainable HBM rate next to the 8 TB/s peak
+ * (a buffer far beyond the 256 MB MALL), or the MALL's rate on a re-read of
+ * a small one. */
+int rwkv7_read_bandwidth(const void* buf, uint64_t bytes, int32_t nontemporal, int32_t iters, void* stream,
+                         double* gbs);
 
 /* Name of the kernel symbol a class launches on the decode path for batch B
  * (for matching rocprofv3 output), or "" for an unknown class. */

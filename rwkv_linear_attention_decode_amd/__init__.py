@@ -38,7 +38,8 @@ OPT_INT8 = 15
 def gemm_plan_code(tm, tn, ks, pipe=0, split=0):
     """Value of an OPT_GEMM_PLAN_* option: tile 32*tm x 32*tn, stage depth ks,
     K loop `pipe` (0 plain, 1 pipelined LDS reads, 2 two stages of global loads in
-    flight, 3 LDS-DMA ring, 4 the same with eight waves), K split (0 = automatic)."""
+    flight, 3 LDS-DMA ring, 4 the same with eight waves, 5 a deep LDS-DMA ring filling
+    about 144 KB of LDS, 6 the same in about 72 KB), K split (0 = automatic)."""
     return ((tm * 10 + tn) * 1000 + ks) * 100 + pipe * 10 + split
 K_LN_MIX, K_PROJ_IN, K_WKV, K_PROJ_OUT, K_CMIX_KEY, K_CMIX_VALUE, K_HEAD, K_OTHER = range(8)
 K_NAMES = ("ln_mix", "proj_in", "wkv", "proj_out", "cmix_key", "cmix_value", "head", "other")
@@ -148,6 +149,7 @@ def lib() -> ctypes.CDLL:
         "rwkv7_kernel_timing": [vp, i32, P(ctypes.c_double), P(i64), i32],
         "rwkv7_debug_cmix_buffers": [vp, vp, i32, P(vp), P(vp), P(vp), P(vp)],
         "rwkv7_debug_wkv_out": [vp, vp, i32, P(vp), P(i32)],
+        "rwkv7_read_bandwidth": [vp, u64, i32, i32, vp, P(ctypes.c_double)],
         "rwkv7_time_kernel": [vp, vp, i64, i32, vp, vp, vp, i32, i32, i32, vp, u64, vp,
                               P(ctypes.c_double)],
         "rwkv7_sched_create": [P(SchedConfig), P(SchedBackend), P(vp)],
@@ -381,6 +383,14 @@ def rwkv7_debug_cmix_buffers(model: int, ws, B: int) -> Tuple[int, int, int, int
     _check(lib().rwkv7_debug_cmix_buffers(model, ws.data_ptr(), B, *[ctypes.byref(o) for o in out]),
            "rwkv7_debug_cmix_buffers")
     return tuple(o.value for o in out)
+
+
+def rwkv7_read_bandwidth(buf, nontemporal: bool = True, iters: int = 5, stream=None) -> float:
+    """GB/s of a plain streaming read of the device tensor ``buf``."""
+    v = ctypes.c_double()
+    _check(lib().rwkv7_read_bandwidth(buf.data_ptr(), buf.numel() * buf.element_size(), int(nontemporal), iters,
+                                      _stream(stream), ctypes.byref(v)), "rwkv7_read_bandwidth")
+    return v.value
 
 
 def rwkv7_debug_wkv_out(model: int, ws, B: int) -> Tuple[int, bool]:

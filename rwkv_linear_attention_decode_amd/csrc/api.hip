@@ -88,6 +88,7 @@ int check_config(const rwkv7_config* c, Dims* d) {
 // ------------------------------------------------------------ packed layout
 struct LayerPtrs {
   half_t *w_in, *w2, *a2, *v2, *g2, *w_o, *w_key, *w_val_hm, *w_val_km;
+  half_t* wkv_ad;   // w2 | a2 | v2 | g2 per head in the order the WKV threads read them
   float *ln1_w, *ln1_b, *ln2_w, *ln2_b, *lnx_w, *lnx_b, *mu6, *w0, *a0, *v0, *k_k, *k_a, *r_k,
       *mu_k, *b_key;
 };
@@ -163,6 +164,7 @@ Packed pack_layout(const Dims& d, char* base) {
     q.a2 = (half_t*)take(C * d.Da * 2);
     q.v2 = (half_t*)take(C * d.Dv * 2);
     q.g2 = (half_t*)take(C * d.Dg * 2);
+    q.wkv_ad = (half_t*)take(C * (d.Dw + d.Da + d.Dv + d.Dg) * 2);
     q.w_o = (half_t*)take(C * C * 2);
     q.w_key = (half_t*)take(F * C * 2);
     q.w_val_hm = (half_t*)take(F * C * 2);
@@ -442,7 +444,7 @@ WkvArgs wkv_args(const rwkv7_model* m, int l, float* pool, int64_t n_slots, cons
   a.rkv = w.rkv; a.lin = w.lin; a.Lin = d.Lin;
   a.off_a = d.Dwp; a.off_v = d.Dwp + d.Dap; a.off_g = d.Dwp + d.Dap + d.Dvp;
   a.Dw = d.Dw; a.Da = d.Da; a.Dv = d.Dv; a.Dg = d.Dg;
-  a.w2 = q.w2; a.a2 = q.a2; a.v2 = q.v2; a.g2 = q.g2;
+  a.w2 = q.w2; a.a2 = q.a2; a.v2 = q.v2; a.g2 = q.g2; a.adp = q.wkv_ad;
   a.w0 = q.w0; a.a0 = q.a0; a.v0 = q.v0; a.k_k = q.k_k; a.k_a = q.k_a; a.r_k = q.r_k;
   a.lnx_w = q.lnx_w; a.lnx_b = q.lnx_b;
   a.vfirst = w.vfirst;
@@ -934,6 +936,7 @@ int rwkv7_load(const rwkv7_config* cfg, const rwkv7_tensor* tensors, int32_t n_t
     PK(mat(q.a2, d.Da, p + "att.a2"), "pack");
     PK(mat(q.v2, d.Dv, p + "att.v2"), "pack");
     PK(mat(q.g2, d.Dg, p + "att.g2"), "pack");
+    PK(launch_pack_wkv_adapters(q.wkv_ad, q.w2, q.a2, q.v2, q.g2, d.C, d.Dw, d.Da, d.Dv, d.Dg, st), "pack");
     PK(mat(q.w_o, C, p + "att.output.weight"), "pack");
     PK(mat(q.w_key, C, p + "ffn.key.weight"), "pack");
     PK(mat(q.w_val_km, d.F, p + "ffn.value.weight"), "pack");
@@ -1179,6 +1182,32 @@ int rwkv7_greedy_noalloc(int32_t B, int32_t V, const float* logits, float* occ_p
   a.part_idx = (int*)((char*)base + GREEDY_NOALLOC_PART);
   a.B = B; a.V = V;
   HIP_TRY(launch_greedy(a, (hipStream_t)stream), "greedy");
+  return RWKV7_OK;
+}
+
+int rwkv7_read_bandwidth(const void* buf, uint64_t bytes, int32_t nontemporal, int32_t iters, void* stream,
+                         double* gbs) {
+  if (!buf || !gbs || bytes < 16 || iters < 1) return fail(RWKV7_EINVAL, "buf, gbs, bytes >= 16, iters >= 1");
+  hipStream_t st = (hipStream_t)stream;
+  hipDeviceProp_t prop;
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+  HIP_TRY(hipGetDeviceProperties(&prop, dev), "hipGetDeviceProperties");
+  const int grid = prop.multiProcessorCount * 8;
+  HIP_TRY(launch_read_stream(buf, (int64_t)bytes, nontemporal != 0, grid, st), "read stream");   // warm-up
+  hipEvent_t a = nullptr, b = nullptr;
+  HIP_TRY(hipEventCreate(&a), "hipEventCreate");
+  HIP_TRY(hipEventCreate(&b), "hipEventCreate");
+  hipError_t e = hipEventRecord(a, st);
+  for (int i = 0; i < iters && e == hipSuccess; ++i) e = launch_read_stream(buf, (int64_t)bytes, nontemporal != 0, grid, st);
+  if (e == hipSuccess) e = hipEventRecord(b, st);
+  if (e == hipSuccess) e = hipEventSynchronize(b);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+  hipEventDestroy(a);
+  hipEventDestroy(b);
+  if (e != hipSuccess) return hip_fail(e, "read bandwidth");
+  *gbs = (double)bytes * iters / (ms * 1e-3) / 1e9;
   return RWKV7_OK;
 }
 

@@ -564,6 +564,160 @@ __global__ __launch_bounds__(64 * NW) void k_mm_dma(ProjArgs a) {
     mm_epilogue<TM, BN>(a, sg, acc, ks_id, n0, m0, wm0, wn0, lane);
 }
 
+// ------------------------------------------------------- LDS-DMA ring
+// k_mm_dma with a deeper ring: `nslot` stages (a launch argument; dynamic
+// LDS of nslot * (MT + NT) * KS * 2 bytes), nslot - 1 of them in flight
+// while one is multiplied.  A decode projection (M <= 256) streams each
+// weight once; what bounds it is how many bytes each CU keeps in flight
+// against the memory latency, not the MFMA rate, and a three-slot ring
+// keeps too few (about 20 GB/s per CU at M = 64).  At the top of stage r
+// the stages r .. r + nslot - 2 are in flight; once the last stage has been
+// issued, one full wait covers the rest, which are then multiplied out with
+// no further barrier.
+// vmcnt <= stages * NIW for a runtime stage count (the count is an
+// instruction immediate; the branch is on a workgroup-uniform value)
+template <int NIW, int K>
+__device__ inline void wait_k() {   // vmcnt <= K * NIW, or less where that exceeds the field
+  constexpr int k = K * NIW <= 63 ? K : 63 / NIW;
+  wait_vm<k * NIW>();
+}
+template <int NIW>
+__device__ inline void wait_stages(int stages) {
+  switch (stages) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_k<NIW, 1>(); break;
+    case 2: wait_k<NIW, 2>(); break;
+    case 3: wait_k<NIW, 3>(); break;
+    case 4: wait_k<NIW, 4>(); break;
+    case 5: wait_k<NIW, 5>(); break;
+    case 6: wait_k<NIW, 6>(); break;
+    default: wait_k<NIW, 7>(); break;
+  }
+}
+constexpr int RING_MAX_SLOTS = 9;   // stages - 2 <= 7 in flight behind the one waited for
+
+template <int TM, int TN, int KS>
+__global__ __launch_bounds__(256) void k_mm_ring(ProjArgs a, int nslot) {
+  constexpr int NW = 4;
+  constexpr int MT = 32 * TM, NT = 32 * TN, CPR = KS / 8, KH = KS / 32;
+  constexpr int SLOTS = (MT + NT) * CPR;
+  constexpr int NIW = SLOTS / (64 * NW);
+  constexpr int ASL = MT * CPR;
+  static_assert(SLOTS % (64 * NW) == 0, "whole DMA instructions per wave");
+  extern __shared__ __attribute__((aligned(1024))) half_t Ld[];
+
+  const int n_tiles = a.tile0[a.nseg];
+  const int total = n_tiles * a.m_tiles * a.split;
+  const int per_xcd = (total + 7) / 8;
+  const int lin = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (lin >= total) return;
+  const int ks_id = lin % a.split;
+  const int m_tile = (lin / a.split) % a.m_tiles;
+  const int n_tile = lin / (a.split * a.m_tiles);
+  Seg sg = a.seg[0];
+  int t0 = 0;
+#pragma unroll
+  for (int i = 1; i < MAX_SEGS; ++i)
+    if (i < a.nseg && n_tile >= a.tile0[i]) {
+      sg = a.seg[i];
+      t0 = a.tile0[i];
+    }
+  const int n0 = sg.row0 + (n_tile - t0) * NT;
+  const int m0 = m_tile * MT;
+  const bool own = sg.W != nullptr;
+  const int K = own ? sg.K : a.K;
+  const half_t* Wb = own ? sg.W - (long)sg.row0 * K : a.W;
+  const half_t* A = reinterpret_cast<const half_t*>(sg.act) + sg.act_off;
+  const int lda = sg.ld_act;
+  const int nst = K / KS;
+  const int st0 = (int)((long)nst * ks_id / a.split);
+  const int st1 = (int)((long)nst * (ks_id + 1) / a.split);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm0 = (wave >> 1) * 16 * TM, wn0 = (wave & 1) * 16 * TN;
+
+  const half_t* src[NIW];
+#pragma unroll
+  for (int q = 0; q < NIW; ++q) {
+    const int S = (q * NW + wave) * 64 + lane;
+    if (S < ASL) {
+      const int r = S / CPR, c = (S % CPR) ^ swz<CPR>(r);
+      src[q] = A + (long)min(m0 + r, a.M - 1) * lda + c * 8;
+    } else {
+      const int r = (S - ASL) / CPR, c = ((S - ASL) % CPR) ^ swz<CPR>(r);
+      src[q] = Wb + (long)min(n0 + r, sg.row1 - 1) * K + c * 8;
+    }
+  }
+  const unsigned lds0 = (unsigned)(uintptr_t)&Ld[0];
+  auto issue = [&](int stg, int slot) {
+#pragma unroll
+    for (int q = 0; q < NIW; ++q)
+      dma16(src[q] + (long)stg * KS,
+            __builtin_amdgcn_readfirstlane(lds0 + slot * SLOTS * 16 + (q * NW + wave) * 1024));
+  };
+  int aoff[KH][TM], boff[KH][TN];
+#pragma unroll
+  for (int h = 0; h < KH; ++h) {
+    const int c = 4 * h + (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = wm0 + 16 * i + (lane & 15);
+      aoff[h][i] = (r * CPR + (c ^ swz<CPR>(r))) * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int r = wn0 + 16 * j + (lane & 15);
+      boff[h][j] = (ASL + r * CPR + (c ^ swz<CPR>(r))) * 16;
+    }
+  }
+  floatx4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int slot) {
+    const char* Lb = reinterpret_cast<const char*>(Ld) + slot * SLOTS * 16;
+#pragma unroll
+    for (int h = 0; h < KH; ++h) {
+      half8 af[TM], bf[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const half8*>(Lb + aoff[h][i]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bf[j] = *reinterpret_cast<const half8*>(Lb + boff[h][j]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  const int nrel = st1 - st0;
+  const int pre = min(nrel, nslot - 1);
+  for (int r = 0; r < pre; ++r) issue(st0 + r, r);
+  // steady state: stage r + nslot - 1 is issued into the slot stage r - 1 used
+  int r = 0, slot = 0, fill = nslot - 1;
+  for (; r + nslot - 1 < nrel; ++r) {
+    wait_stages<NIW>(nslot - 2);   // stage r has landed (this wave's part)
+    __syncthreads();               // every wave's; every wave is done with stage r - 1's slot
+    issue(st0 + r + nslot - 1, fill);
+    compute(slot);
+    slot = slot + 1 == nslot ? 0 : slot + 1;
+    fill = fill + 1 == nslot ? 0 : fill + 1;
+  }
+  // tail: nothing more to issue
+  wait_vm<0>();
+  __syncthreads();
+  for (; r < nrel; ++r) {
+    compute(slot);
+    slot = slot + 1 == nslot ? 0 : slot + 1;
+  }
+  const bool lds_epi = (int)(nslot * SLOTS * 16) >= MT * (NT + 4) * 4;
+  if (lds_epi)
+    mm_epilogue_lds<TM, TN, MT, NT>(a, sg, acc, ks_id, n0, m0, wm0, wn0, lane, reinterpret_cast<float*>(Ld));
+  else
+    mm_epilogue<TM, TN>(a, sg, acc, ks_id, n0, m0, wm0, wn0, lane);
+}
+
 // Fixed-order sum of the split-K partials, then the segment's epilogue.
 __global__ __launch_bounds__(256) void k_mm_reduce(ProjArgs a) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
@@ -666,8 +820,32 @@ static void mm_launch_dma(int ks, dim3 grid, hipStream_t st, const ProjArgs& a) 
   hipLaunchKernelGGL((k_mm_dma<TM, TN, 64, NW>), grid, dim3(64 * NW), 0, st, a);
 }
 
+// Ring depth of K loops 5 (about 144 KB of LDS: one workgroup per CU) and
+// 6 (about 72 KB: two per CU); 0 when fewer than three stages fit.
+static constexpr int ring_stage_bytes(int tm, int tn, int ks) { return 32 * (tm + tn) * ks * 2; }
+static int ring_slots(int tm, int tn, int ks, int pipe) {
+  const int budget = pipe == 5 ? 147456 : 73728;
+  int n = budget / ring_stage_bytes(tm, tn, ks);
+  if (n > RING_MAX_SLOTS) n = RING_MAX_SLOTS;
+  return n >= 3 ? n : 0;
+}
+
+template <int TM, int TN>
+static void mm_launch_ring(int ks, int pipe, dim3 grid, hipStream_t st, const ProjArgs& a) {
+  const int n = ring_slots(TM, TN, ks, pipe);
+  const size_t lds = (size_t)n * ring_stage_bytes(TM, TN, ks);
+  if (ks == 128)
+    hipLaunchKernelGGL((k_mm_ring<TM, TN, 128>), grid, dim3(256), lds, st, a, n);
+  else
+    hipLaunchKernelGGL((k_mm_ring<TM, TN, 64>), grid, dim3(256), lds, st, a, n);
+}
+
 template <int TM, int TN>
 static void mm_launch(int ks, int pipe, dim3 grid, hipStream_t st, const ProjArgs& a) {
+  if (pipe == 5 || pipe == 6) {
+    mm_launch_ring<TM, TN>(ks, pipe, grid, st, a);
+    return;
+  }
   if (pipe == 3) {
     mm_launch_dma<TM, TN, 4>(ks, grid, st, a);
     return;
@@ -692,7 +870,11 @@ static void mm_launch(int ks, int pipe, dim3 grid, hipStream_t st, const ProjArg
 }
 
 static bool mm_cfg_ok(int tm, int tn, int ks, int pipe) {
-  if (pipe < 0 || pipe > 4) return false;
+  if (pipe < 0 || pipe > 6) return false;
+  if (pipe == 5 || pipe == 6) {   // LDS-DMA ring
+    if (!((tm == 1 || tm == 2 || tm == 4) && (tn == 2 || tn == 4))) return false;
+    return (ks == 64 || ks == 128) && ring_slots(tm, tn, ks, pipe) >= 3;
+  }
   if (pipe == 4) {   // eight waves: N blocks split over four wave columns
     if (tn == 8)      // 256-wide tiles, 64-deep stages (three of them fill up to 144 KB of LDS)
       return (tm == 2 || tm == 4) && ks == 64;

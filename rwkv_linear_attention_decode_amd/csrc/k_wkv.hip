@@ -51,17 +51,12 @@ RW_DEV void wkv_prologue(const WkvArgs& a, int b, int h, HeadVecs& hv, float* s_
   // every load unconditional and its address picked by selects, so the
   // NCHK loads issue back to back (layer 0 loads its unused value-gate rows
   // too: they are packed like every layer's, and its gate is not applied)
+  // the head's adapter block is packed so that load q of thread t is 16-byte
+  // chunk q * 256 + t: every wave instruction reads 1 KB contiguously
   u32x4 wch[NCHK];
+  const half_t* adp = a.adp + (long)h * NCHK * 2048 + t * 8;
 #pragma unroll
-  for (int q = 0; q < NCHK; ++q) {
-    const int e0 = (qd * NCHK + q) * 8;
-    const half_t* pw = a.w2 + (long)c * a.Dw + e0;
-    const half_t* pa = a.a2 + (long)c * a.Da + (e0 - e1);
-    const half_t* pv = a.v2 + (long)c * a.Dv + (e0 - e2);
-    const half_t* pg = a.g2 + (long)c * a.Dg + (e0 - e3);
-    const half_t* W = e0 < e1 ? pw : e0 < e2 ? pa : e0 < e3 ? pv : pg;
-    wch[q] = ld16(W);
-  }
+  for (int q = 0; q < NCHK; ++q) wch[q] = ld16(adp + q * 2048);
   // per-channel vectors for wave 0's key step
   float k_k = 0.f, k_a = 0.f, r_k = 0.f, vf = 0.f;
   if (wave == 0) {
@@ -378,6 +373,37 @@ __global__ __launch_bounds__(256) void k_wkv_decode_rows(WkvArgs a) {
 #define WKV_NCHK_CASES(X) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) \
   X(13) X(14) X(15) X(16) X(17) X(18) X(19) X(20) X(21) X(22) X(23) X(24) X(25) X(26)   \
   X(27) X(28) X(29) X(30) X(31) X(32)
+
+// The decode / prep prologue's adapter layout: per head h, 16-byte chunk
+// q * 256 + t holds chunk e = (t % 4) * NCHK + q (8 halves) of channel
+// h * 64 + t / 4's concatenated row w2 | a2 | v2 | g2 (NCHK = sum of ranks / 32).
+__global__ void k_pack_wkv_adapters(half_t* dst, const half_t* w2, const half_t* a2, const half_t* v2,
+                                    const half_t* g2, int C, int Dw, int Da, int Dv, int Dg) {
+  const int nchk = (Dw + Da + Dv + Dg) / 32;
+  const long chunk = (long)blockIdx.x * 256 + threadIdx.x;
+  if (chunk >= (long)C / 64 * nchk * 256) return;
+  const int h = (int)(chunk / (nchk * 256));
+  const int q = (int)(chunk / 256 % nchk);
+  const int t = (int)(chunk % 256);
+  const long c = (long)h * 64 + t / 4;
+  const int e0 = ((t % 4) * nchk + q) * 8;
+  const int e1 = Dw, e2 = Dw + Da, e3 = Dw + Da + Dv;
+  const half_t* src = e0 < e1 ? w2 + c * Dw + e0
+                    : e0 < e2 ? a2 + c * Da + (e0 - e1)
+                    : e0 < e3 ? v2 + c * Dv + (e0 - e2)
+                              : g2 + c * Dg + (e0 - e3);
+  *reinterpret_cast<u32x4*>(dst + chunk * 8) = *reinterpret_cast<const u32x4*>(src);
+}
+
+hipError_t launch_pack_wkv_adapters(half_t* dst, const half_t* w2, const half_t* a2, const half_t* v2,
+                                    const half_t* g2, int C, int Dw, int Da, int Dv, int Dg, hipStream_t st) {
+  const int dsum = Dw + Da + Dv + Dg;
+  if (dsum % 32 || C % 64 || Dw % 8 || Da % 8 || Dv % 8 || Dg % 8) return hipSuccess;   // layout unused then
+  const long chunks = (long)C / 64 * (dsum / 32) * 256;
+  hipLaunchKernelGGL(k_pack_wkv_adapters, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, dst, w2, a2, v2,
+                     g2, C, Dw, Da, Dv, Dg);
+  return hipGetLastError();
+}
 
 // 0 selects the variant that reads precomputed adapter outputs
 static int wkv_nchk(const WkvArgs& a) {

@@ -202,6 +202,7 @@ constexpr int SAMPLE_MAX_V = 65536;
 hipError_t launch_sample(const SampleArgs& a, hipStream_t st);
 
 // int8 weights: per-row symmetric codes (byte = code + 128) and fp32 scales of W [rows][K]
+hipError_t launch_read_stream(const void* buf, int64_t bytes, bool nt, int grid, hipStream_t st);
 hipError_t launch_quant_rows(const half_t* W, int64_t rows, int K, uint8_t* q, float* sc, hipStream_t st);
 
 // api.hip, for the scheduler: set the thread's last-error text and return
@@ -228,6 +229,7 @@ struct WkvArgs {
   const half_t* a2;        // [C][Da]
   const half_t* v2;        // [C][Dv]
   const half_t* g2;        // [C][Dg]
+  const half_t* adp;       // the four as read by the decode / prep prologue (rwkv7_load packs them)
   const float* w0;
   const float* a0;
   const float* v0;
@@ -253,6 +255,8 @@ struct WkvArgs {
   float* q_y;              // raw readout ([wkv_chunk_rows(T)][C] for the chunked scan)
   float* q_rec;            // chunked scan: per (16-token chunk, head) records (wkv_chunk_rec_floats)
 };
+hipError_t launch_pack_wkv_adapters(half_t* dst, const half_t* w2, const half_t* a2, const half_t* v2,
+                                    const half_t* g2, int C, int Dw, int Da, int Dv, int Dg, hipStream_t st);
 hipError_t launch_wkv_decode(const WkvArgs& a, hipStream_t st);
 hipError_t launch_wkv_prep(const WkvArgs& a, hipStream_t st);   // sequence: per (t, h)
 hipError_t launch_wkv_scan(const WkvArgs& a, hipStream_t st);   // sequence: serial in t

@@ -167,10 +167,12 @@ GEMM_PLAN_KEYS = (8, 9, 10, 11, 12, 13)   # OPT_GEMM_PLAN_PROJ_IN .. _HEAD
     (2, 2, 64, 3, 0), (4, 4, 64, 3, 0), (1, 2, 128, 3, 0), (2, 4, 32, 3, 2),
     (4, 2, 64, 3, 1), (1, 4, 64, 3, 3), (2, 2, 128, 3, 0), (2, 5, 64, 3, 0), (2, 5, 64, 3, 2),
     (2, 2, 64, 4, 0), (4, 4, 64, 4, 0), (2, 4, 64, 4, 2), (4, 2, 64, 4, 1), (2, 2, 32, 4, 0),
-    (4, 4, 32, 4, 3), (2, 2, 128, 4, 0), (4, 8, 64, 4, 0), (2, 8, 64, 4, 2)])
+    (4, 4, 32, 4, 3), (2, 2, 128, 4, 0), (4, 8, 64, 4, 0), (2, 8, 64, 4, 2),
+    (1, 2, 128, 5, 0), (2, 2, 64, 5, 0), (2, 2, 64, 5, 3), (2, 4, 64, 5, 0), (4, 4, 64, 5, 0),
+    (4, 2, 64, 5, 2), (1, 4, 64, 6, 2), (1, 2, 128, 6, 0), (4, 2, 64, 6, 1), (2, 2, 64, 6, 2)])
 def test_gemm_plans_match_oracle(model, W, R, tm, tn, ks, pipe, split):
     """Every MFMA projection (prefill and an 8-row step) forced onto one tile
-    plan: tile shapes, stage depths, the five K loops and K splits, with K
+    plan: tile shapes, stage depths, the seven K loops and K splits, with K
     from 32 (adapter ranks) to 1024 (channel-mix value) and ragged row
     counts, against the oracle and against the built-in plans."""
     code = R.gemm_plan_code(tm, tn, ks, pipe, split)
@@ -221,7 +223,9 @@ def test_gemm_plan_option_validation(model, R):
                 R.gemm_plan_code(4, 4, 128), R.gemm_plan_code(1, 4, 64, 4), R.gemm_plan_code(2, 4, 128, 3),
                 R.gemm_plan_code(1, 2, 32, 3), R.gemm_plan_code(2, 5, 32, 3), R.gemm_plan_code(2, 5, 64, 2),
                 R.gemm_plan_code(4, 5, 64, 3), R.gemm_plan_code(1, 2, 64, 4), R.gemm_plan_code(2, 4, 32, 4),
-                R.gemm_plan_code(2, 4, 128, 4), R.gemm_plan_code(2, 2, 64, 5), R.gemm_plan_code(4, 8, 64, 3),
+                R.gemm_plan_code(2, 4, 128, 4), R.gemm_plan_code(2, 2, 64, 7), R.gemm_plan_code(4, 8, 64, 3),
+                R.gemm_plan_code(4, 4, 128, 5), R.gemm_plan_code(2, 2, 32, 5), R.gemm_plan_code(2, 2, 128, 6),
+                R.gemm_plan_code(2, 5, 64, 5),
                 R.gemm_plan_code(4, 8, 128, 4), R.gemm_plan_code(1, 8, 64, 4), -5, 10 ** 8):
         with pytest.raises(R.RWKV7Error):
             model.set_option(8, bad)
