@@ -900,7 +900,9 @@ static bool mm_cfg_ok(int tm, int tn, int ks, int pipe) {
 // weights streamed from HBM (rotated over six copies), then the 2.9B model's
 // own projections chosen one at a time on whole graph-replayed decode steps
 // (B = 64, 256; the 7.2B model at B = 256) and 512- and 2048-token prefill
-// chunks.  A kernel timed alone can
+// chunks.  At M <= 64: 64 x 64 tiles with 128-deep stages on the DMA loop,
+// split 6 for the narrow outputs (W_o, value; their partials go to the next
+// LayerNorm) and no split for the key (3.63 -> 3.50 ms per 2.9B B = 64 step).  A kernel timed alone can
 // rank plans differently from the step it runs in (the 64 x 160 key tiles
 // are 12 % faster alone and only even in the step), so the step decides.  "Narrow" outputs are one model width (value,
 // output projection), "head" the vocabulary, "wide" the rest (key, input
@@ -918,11 +920,11 @@ static MmPlan mm_choose(const ProjArgs& a, int total_rows) {
   if (N <= 4096) {                                   // narrow
     if (K >= 8192) {                                 // channel-mix value
       if (K >= 16384) return M > 64 && M <= 256 ? MmPlan{4, 4, 64, 4, 3} : MmPlan{4, 4, 64, 0, 6};
-      if (M <= 64) return {2, 2, 64, 2, 0};
+      if (M <= 64) return {2, 2, 128, 3, 6};
       if (M <= 256) return {4, 4, 64, 4, 6};
       return M <= 1024 ? MmPlan{2, 4, 64, 3, 3} : MmPlan{4, 8, 64, 4, 0};
     }
-    if (M <= 64) return {1, 2, 128, 0, 0};
+    if (M <= 64) return {2, 2, 128, 3, 6};
     return M <= 256 ? MmPlan{2, 2, 64, 4, 0} : MmPlan{2, 4, 64, 4, 0};
   }
   if (N >= 32768)   // head
@@ -930,7 +932,8 @@ static MmPlan mm_choose(const ProjArgs& a, int total_rows) {
   const bool rank_k = K < 1024;                      // adapters' second stage
   if (M <= 64) {
     if (rank_k) return {1, 2, 128, 0, 0};
-    return N <= 8192 ? MmPlan{1, 2, 128, 3, 0} : MmPlan{2, 2, 64, 2, 0};
+    // the key: one K range (no split, so no reduction launch before its ReLU^2)
+    return N <= 8192 ? MmPlan{1, 2, 128, 3, 0} : MmPlan{2, 2, 128, 3, 1};
   }
   if (M <= 256) {
     if (rank_k) return {2, 2, 64, 2, 0};

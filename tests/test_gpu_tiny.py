@@ -249,7 +249,11 @@ def test_prefill_equals_steps_on_gpu(model, R):
         model.set_option(R.OPT_PREFILL_SCAN, 0)
     a, b, c = gstate(model, 2), gstate(model, 3), gstate(model, 4)
     assert rel(a, b) <= TOL
-    assert rel(c, a) <= 1e-5
+    # 37 rows and 16 rows take different GEMM tile plans (K split 6 against none),
+    # so the fp32 sums run in another order and the fp16 activations between the
+    # projections can round an ulp (2^-11) apart: ~3e-5, not the bitwise agreement
+    # of one plan
+    assert rel(c, a) <= 1e-4
     cnt = model.counters().cpu().numpy()
     assert cnt[2] == cnt[3] == cnt[4] == 37
 
