@@ -950,6 +950,9 @@ static MmPlan mm_choose(const ProjArgs& a, int total_rows) {
   }
   if (rank_k) return {2, 2, 32, 2, 0};
   if (K >= 4096) return N >= 10240 ? MmPlan{2, 4, 32, 1, 1} : MmPlan{4, 2, 64, 2, 0};
+  // the key (one segment): 128 x 256 tiles, one K range (whole 512- and 2048-token
+  // prefills 1.4 - 1.6 % faster than 64 x 64 / 128 x 128 tiles)
+  if (N >= 10240 && a.nseg == 1 && K % 64 == 0) return {4, 8, 64, 4, 1};
   if (N >= 10240) return M <= 1024 ? MmPlan{2, 2, 64, 4, 0} : MmPlan{4, 4, 64, 4, 0};
   return {4, 2, 64, 4, 0};
 }
