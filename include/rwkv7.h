@@ -311,6 +311,12 @@ const char* rwkv7_last_error(void);
 
 #define RWKV7_OPT_INT8 15  /* 1: decode steps of B <= 2 on the GEMV path stream the int8 copies made
                               by rwkv7_quantize_int8 (ENOTSUP before it); 0 (default): fp16 */
+#define RWKV7_OPT_LN_SPLIT 16  /* workgroups per row of the LayerNorm + token-shift kernel on the
+                                 MFMA decode path: 0 (default) automatic (256 / B, at least
+                                 2 for B <= 256, 1 above), n > 0 at most n (capped at C / 512,
+                                 or C / 256 for C / 256 odd).  Each workgroup reads the whole row for the
+                                 statistics and loads and writes its share of the columns;
+                                 results do not depend on it */
 int rwkv7_set_option(rwkv7_model* model, int32_t key, int64_t value);
 int rwkv7_get_option(const rwkv7_model* model, int32_t key, int64_t* value);
 

@@ -33,6 +33,8 @@ OPT_GEMM_PLAN_CMIX_VALUE = 12
 OPT_GEMM_PLAN_HEAD = 13
 OPT_PREFILL_SCAN = 14
 OPT_INT8 = 15
+# workgroups per row of the batched decode LayerNorm kernel (0 = automatic)
+OPT_LN_SPLIT = 16
 
 
 def gemm_plan_code(tm, tn, ks, pipe=0, split=0):

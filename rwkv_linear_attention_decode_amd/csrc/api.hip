@@ -277,7 +277,7 @@ struct rwkv7_model {
   Dims d;
   Packed pk;
   int64_t opt_graph = 1, opt_gemv_max = 2, opt_sparse_max = 4, opt_timing = 0, opt_chunk = 2048,
-          opt_fuse_ln = 1, opt_fuse_value = 1, opt_prefill_scan = 0, opt_int8 = 0;
+          opt_fuse_ln = 1, opt_fuse_value = 1, opt_prefill_scan = 0, opt_int8 = 0, opt_ln_split = 0;
   Q8 q8{};
   bool has_q8 = false;
   // tile plan per MFMA projection (RWKV7_OPT_GEMM_PLAN_* order), 0 = built-in
@@ -470,6 +470,19 @@ Path decode_path(const rwkv7_model* m, int B) {
   return p;
 }
 
+// Workgroups per row of the batched decode LayerNorm kernel: a few rows
+// leave most CUs idle and each workgroup's time goes into its loads, so the
+// row's per-column vectors are spread over several workgroups, about 256
+// in all and at least two per row up to B = 256 (whole-step timing at the
+// 2.9B and 7.2B shapes, B 8 to 256).
+int ln_blocks(const rwkv7_model* m, int B) {
+  const int ne = m->d.C / 256;
+  const int units = ne % 2 == 0 ? ne / 2 : ne;
+  int n = (int)m->opt_ln_split;
+  if (n <= 0) n = B > 256 ? 1 : std::max(2, 256 / std::max(B, 1));
+  return std::max(1, std::min(n, units));
+}
+
 // mixing vector (index into the six time-mix coefficient rows r,w,k,v,a,g)
 // read by each block of the fused input projection
 constexpr int kInMix[7] = {0, 2, 3, 1, 4, 3, 5};
@@ -501,17 +514,25 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
   // Otherwise a LayerNorm kernel writes the mixed rows and the shift.
   // MFMA path: a residual projection split over K leaves its partial sums
   // for the LayerNorm that follows it to add into x (no reduction launch)
+  // A LayerNorm that folds partials in writes the new residual to the other
+  // buffer (its column blocks all read the whole old row): xc is the current one.
   int pending = 0;
   int* const defer = path.fused ? nullptr : &pending;
+  const int ncb = ln_blocks(m, B);
+  float* xc = w.x;
+  float* xn = w.x2;
   for (int l = 0; l < d.L; ++l) {
     L.layer = l;
     const LayerPtrs& q = m->pk.layers[l];
     const int64_t lo = (int64_t)l * d.layer_floats;
     LnMixArgs la;
     memset(&la, 0, sizeof la);
-    la.x = w.x; la.C = C; la.R = B; la.mode = LNMIX_DECODE;
-    la.parts = pending ? w.part : nullptr; la.nparts = pending;
-    pending = 0;
+    la.x = xc; la.C = C; la.R = B; la.mode = LNMIX_DECODE; la.ncb = ncb;
+    if (pending) {
+      la.parts = w.part; la.nparts = pending; la.x_out = xn;
+      std::swap(xc, xn);
+      pending = 0;
+    }
     la.g = q.ln1_w; la.b = q.ln1_b;
     la.pool = pool; la.slot_stride = d.slot_floats; la.n_slots = n_slots; la.shift_off = lo;
     la.slots = w.slots; la.seq_slot = -1;
@@ -522,7 +543,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
     proj_in_args(d, q, w, B, f16, pa);
     if (q8) { pa.Wq = m->q8.layers[l].w_in; pa.Wsc = m->q8.layers[l].s_in; }
     if (path.fused) {
-      pa.ln = LnPro{w.x, q.ln1_w, q.ln1_b, pool, d.slot_floats, n_slots, lo, w.slots, w.u_att, LNP_MIX, 0};
+      pa.ln = LnPro{xc, q.ln1_w, q.ln1_b, pool, d.slot_floats, n_slots, lo, w.slots, w.u_att, LNP_MIX, 0};
       for (int s = 0; s < 7; ++s) pa.seg[s].mix = q.mu6 + (int64_t)kInMix[s] * C;
     } else {
       RUN(RWKV7_K_LN_MIX, "ln_mix(tmix)", launch_ln_mix(la, st));
@@ -543,7 +564,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
     ProjArgs po;
     memset(&po, 0, sizeof po);
     po.W = q.w_o; po.K = C; po.M = B; po.nseg = 1;
-    po.seg[0] = mkseg(0, C, EPI_RESID, w.yg, C, w.x, C);
+    po.seg[0] = mkseg(0, C, EPI_RESID, w.yg, C, xc, C);
     if (q8) { po.Wq = m->q8.layers[l].w_o; po.Wsc = m->q8.layers[l].s_o; }
     RUN(RWKV7_K_PROJ_OUT, "proj_out", proj(path.gemv, po, C, w, st, m->opt_plan[2], defer));
 
@@ -565,7 +586,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
       if (path.fuse_value) { pk.vWq = m->q8.layers[l].w_val; pk.vSc = m->q8.layers[l].s_val; }
     }
     if (path.fused) {
-      pk.ln = LnPro{w.x, q.ln2_w, q.ln2_b, pool, d.slot_floats, n_slots, lo + C, w.slots, w.u_ffn, LNP_MIX, 0};
+      pk.ln = LnPro{xc, q.ln2_w, q.ln2_b, pool, d.slot_floats, n_slots, lo + C, w.slots, w.u_ffn, LNP_MIX, 0};
       pk.seg[0].mix = q.mu_k;
     } else {
       LnMixArgs lc = la;
@@ -573,7 +594,11 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
       lc.shift_off = lo + C;
       lc.mu = q.mu_k; lc.nq = 1;
       lc.out = w.xk; lc.out_q_stride = 0;
-      lc.parts = pending ? w.part : nullptr; lc.nparts = pending;
+      lc.x = xc; lc.parts = nullptr; lc.nparts = 0; lc.x_out = nullptr;
+      if (pending) {
+        lc.parts = w.part; lc.nparts = pending; lc.x_out = xn;
+        std::swap(xc, xn);
+      }
       RUN(RWKV7_K_LN_MIX, "ln_mix(cmix)", launch_ln_mix(lc, st));
     }
     pending = 0;
@@ -583,7 +608,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
       CmixFoldArgs fa;
       memset(&fa, 0, sizeof fa);
       fa.part = w.vpart; fa.nwg = (d.F + gemv_launch_rows(B, C, d.F, 1, true) - 1) / gemv_launch_rows(B, C, d.F, 1, true);
-      fa.mask = w.mask; fa.x = w.x; fa.u_ffn = path.fused ? w.u_ffn : nullptr;
+      fa.mask = w.mask; fa.x = xc; fa.u_ffn = path.fused ? w.u_ffn : nullptr;
       fa.pool = pool; fa.slot_stride = d.slot_floats; fa.n_slots = n_slots; fa.shift_off = lo + C;
       fa.slots = w.slots; fa.B = B; fa.C = C; fa.F = d.F;
       if (l == d.L - 1) { fa.dbg_idx = w.dbg_idx; fa.dbg_cnt = w.dbg_cnt; }
@@ -592,7 +617,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
       CmixArgs ca;
       memset(&ca, 0, sizeof ca);
       ca.pre = w.pre; ca.mask = w.mask; ca.Wv = q.w_val_hm;
-      ca.x = w.x; ca.u_ffn = path.fused ? w.u_ffn : nullptr;
+      ca.x = xc; ca.u_ffn = path.fused ? w.u_ffn : nullptr;
       ca.pool = pool; ca.slot_stride = d.slot_floats; ca.n_slots = n_slots; ca.shift_off = lo + C;
       ca.slots = w.slots; ca.B = B; ca.C = C; ca.F = d.F;
       if (l == d.L - 1) { ca.dbg_idx = w.dbg_idx; ca.dbg_cnt = w.dbg_cnt; }
@@ -601,7 +626,7 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
       ProjArgs pv;
       memset(&pv, 0, sizeof pv);
       pv.W = q.w_val_km; pv.K = d.F; pv.M = B; pv.nseg = 1;
-      pv.seg[0] = mkseg(0, C, EPI_RESID, w.pre, d.F, w.x, C);
+      pv.seg[0] = mkseg(0, C, EPI_RESID, w.pre, d.F, xc, C);
       RUN(RWKV7_K_CMIX_VALUE, "cmix_value", proj(false, pv, C, w, st, m->opt_plan[4], defer));
       if (path.fused) {
         CommitArgs ca{w.u_ffn, pool, d.slot_floats, n_slots, lo + C, w.slots, B, C};
@@ -617,15 +642,15 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
   ph.seg[0] = mkseg(0, d.V, EPI_NONE, w.xo, C, logits, d.V);
   if (q8) { ph.Wq = m->q8.head; ph.Wsc = m->q8.s_head; }
   if (path.fused) {
-    ph.ln = LnPro{w.x, m->pk.lnout_w, m->pk.lnout_b, nullptr, 0, 0, 0, nullptr, nullptr, LNP_PLAIN, 0};
+    ph.ln = LnPro{xc, m->pk.lnout_w, m->pk.lnout_b, nullptr, 0, 0, 0, nullptr, nullptr, LNP_PLAIN, 0};
   } else {
     LnMixArgs lo;
     memset(&lo, 0, sizeof lo);
-    lo.x = w.x; lo.C = C; lo.R = B; lo.mode = LNMIX_PLAIN;
+    lo.x = xc; lo.C = C; lo.R = B; lo.mode = LNMIX_PLAIN; lo.ncb = ncb;
     lo.g = m->pk.lnout_w; lo.b = m->pk.lnout_b;
     lo.nq = 1; lo.mu = nullptr;
     lo.out = w.xo; lo.out_f16 = f16; lo.out_q_stride = 0;
-    lo.parts = pending ? w.part : nullptr; lo.nparts = pending;
+    if (pending) { lo.parts = w.part; lo.nparts = pending; lo.x_out = xn; }
     RUN(RWKV7_K_LN_MIX, "ln_out", launch_ln_mix(lo, st));
   }
   RUN(RWKV7_K_HEAD, "head", proj(path.gemv, ph, d.V, w, st, m->opt_plan[5]));
@@ -658,7 +683,7 @@ int enqueue_prefill_chunk(rwkv7_model* m, float* pool, int64_t n_slots, int slot
     const int64_t lo = (int64_t)l * d.layer_floats;
     LnMixArgs la;
     memset(&la, 0, sizeof la);
-    la.x = xc; la.C = C; la.R = T; la.mode = LNMIX_SEQ;
+    la.x = xc; la.C = C; la.R = T; la.mode = LNMIX_SEQ; la.ncb = 1;
     if (pending) {
       la.parts = w.part; la.nparts = pending; la.x_out = xn;
       std::swap(xc, xn);
@@ -1332,6 +1357,9 @@ int rwkv7_set_option(rwkv7_model* m, int32_t key, int64_t value) {
     case RWKV7_OPT_INT8:
       if (value && !m->has_q8) return fail(RWKV7_ENOTSUP, "INT8 needs rwkv7_quantize_int8 first");
       m->opt_int8 = value ? 1 : 0; break;
+    case RWKV7_OPT_LN_SPLIT:
+      if (value < 0 || value > 16) return fail(RWKV7_EINVAL, "LN_SPLIT must be in [0, 16]");
+      m->opt_ln_split = value; break;
     case RWKV7_OPT_GEMM_PLAN_PROJ_IN:
     case RWKV7_OPT_GEMM_PLAN_ADAPTERS:
     case RWKV7_OPT_GEMM_PLAN_PROJ_OUT:
@@ -1350,7 +1378,7 @@ int rwkv7_set_option(rwkv7_model* m, int32_t key, int64_t value) {
   }
   // cached graphs bake in the kernel path: drop them when it may change
   if (key == RWKV7_OPT_GEMV_MAX_B || key == RWKV7_OPT_SPARSE_MAX_B || key == RWKV7_OPT_FUSE_LN ||
-      key == RWKV7_OPT_FUSE_VALUE || key == RWKV7_OPT_INT8 || (key >= RWKV7_OPT_GEMM_PLAN_PROJ_IN && key <= RWKV7_OPT_GEMM_PLAN_HEAD))
+      key == RWKV7_OPT_FUSE_VALUE || key == RWKV7_OPT_INT8 || key == RWKV7_OPT_LN_SPLIT || (key >= RWKV7_OPT_GEMM_PLAN_PROJ_IN && key <= RWKV7_OPT_GEMM_PLAN_HEAD))
     drop_graphs(m);
   return RWKV7_OK;
 }
@@ -1367,6 +1395,7 @@ int rwkv7_get_option(const rwkv7_model* m, int32_t key, int64_t* value) {
     case RWKV7_OPT_FUSE_VALUE: *value = m->opt_fuse_value; break;
     case RWKV7_OPT_PREFILL_SCAN: *value = m->opt_prefill_scan; break;
     case RWKV7_OPT_INT8: *value = m->opt_int8; break;
+    case RWKV7_OPT_LN_SPLIT: *value = m->opt_ln_split; break;
     case RWKV7_OPT_GEMM_PLAN_PROJ_IN:
     case RWKV7_OPT_GEMM_PLAN_ADAPTERS:
     case RWKV7_OPT_GEMM_PLAN_PROJ_OUT:

@@ -165,11 +165,46 @@ RW_DEV void lnm_store(float* p, const float (&v)[NE], int t) {
     for (int i = 0; i < NE; ++i) p[t + 256 * i] = v[i];
   }
 }
+// Column blocks: a row's units (512-column pairs for NE even, 256-column
+// slices for NE odd) are dealt round robin to the workgroups of the row;
+// bit u of `own` is set for the units this workgroup loads and stores.
 template <int NE>
-RW_DEV void lnm_store_f16(half_t* p, const float (&v)[NE], int t) {
+RW_DEV constexpr int lnm_units() {
+  return NE % 2 == 0 ? NE / 2 : NE;
+}
+template <int NE>
+RW_DEV void lnm_load_own(const float* p, float (&d)[NE], int t, uint32_t own) {
   if constexpr (NE % 2 == 0) {
 #pragma unroll
     for (int k = 0; k < NE / 2; ++k) {
+      float2 x = make_float2(0.0f, 0.0f);
+      if ((own >> k) & 1u) x = *reinterpret_cast<const float2*>(p + 2 * t + 512 * k);
+      d[2 * k] = x.x;
+      d[2 * k + 1] = x.y;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NE; ++i) d[i] = ((own >> i) & 1u) ? p[t + 256 * i] : 0.0f;
+  }
+}
+template <int NE>
+RW_DEV void lnm_store_own(float* p, const float (&v)[NE], int t, uint32_t own) {
+  if constexpr (NE % 2 == 0) {
+#pragma unroll
+    for (int k = 0; k < NE / 2; ++k)
+      if ((own >> k) & 1u) *reinterpret_cast<float2*>(p + 2 * t + 512 * k) = make_float2(v[2 * k], v[2 * k + 1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NE; ++i)
+      if ((own >> i) & 1u) p[t + 256 * i] = v[i];
+  }
+}
+template <int NE>
+RW_DEV void lnm_store_f16_own(half_t* p, const float (&v)[NE], int t, uint32_t own) {
+  if constexpr (NE % 2 == 0) {
+#pragma unroll
+    for (int k = 0; k < NE / 2; ++k) {
+      if (!((own >> k) & 1u)) continue;
       half2v h;
       h[0] = (half_t)v[2 * k];
       h[1] = (half_t)v[2 * k + 1];
@@ -177,7 +212,8 @@ RW_DEV void lnm_store_f16(half_t* p, const float (&v)[NE], int t) {
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < NE; ++i) p[t + 256 * i] = (half_t)v[i];
+    for (int i = 0; i < NE; ++i)
+      if ((own >> i) & 1u) p[t + 256 * i] = (half_t)v[i];
   }
 }
 
@@ -187,11 +223,16 @@ __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
   const int r = blockIdx.x;
   const int C = a.C;
   const int t = threadIdx.x;
+  // column block blockIdx.y of gridDim.y: every block of a row reads the
+  // whole row (and its partials) for the statistics, and loads and writes
+  // only its own units of everything else
+  uint32_t own = 0;
+  for (int u = blockIdx.y; u < lnm_units<NE>(); u += gridDim.y) own |= 1u << u;
   float v[NE], gv[NE], bv[NE], pv[NE], mu[6][NE];
   float* xr = a.x + (long)r * C;
   lnm_load<NE>(xr, v, t);
-  lnm_load<NE>(a.g, gv, t);
-  lnm_load<NE>(a.b, bv, t);
+  lnm_load_own<NE>(a.g, gv, t, own);
+  lnm_load_own<NE>(a.b, bv, t, own);
   const float* sh_in = nullptr;      // stored shift to mix with (decode / first token)
   float* sh_out = nullptr;           // where the new shift goes (decode)
   if (a.mode == LNMIX_DECODE) {
@@ -206,7 +247,7 @@ __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
   const bool prev_row = a.mode == LNMIX_SEQ && r > 0;   // LayerNorm of the previous token
   const float* xp = a.x + (long)(r - 1) * C;
   if (sh_in) {
-    lnm_load<NE>(sh_in, pv, t);
+    lnm_load_own<NE>(sh_in, pv, t, own);
   } else if (prev_row) {
     lnm_load<NE>(xp, pv, t);
   } else {
@@ -233,7 +274,7 @@ __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
 #pragma unroll
   for (int q = 0; q < 6; ++q) {
     if (q < a.nq && a.mu) {
-      lnm_load<NE>(a.mu + (long)q * C, mu[q], t);
+      lnm_load_own<NE>(a.mu + (long)q * C, mu[q], t, own);
     } else {
 #pragma unroll
       for (int i = 0; i < NE; ++i) mu[q][i] = 0.0f;
@@ -266,7 +307,7 @@ __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < NE; ++i) v[i] += acc[i];
-    lnm_store<NE>(a.x_out ? a.x_out + (long)r * C : xr, v, t);
+    lnm_store_own<NE>(a.x_out ? a.x_out + (long)r * C : xr, v, t, own);
   }
 
   float mean, rstd;
@@ -283,7 +324,7 @@ __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
 #pragma unroll
     for (int i = 0; i < NE; ++i) pv[i] = u[i];
   }
-  if (sh_out) lnm_store<NE>(sh_out, u, t);
+  if (sh_out) lnm_store_own<NE>(sh_out, u, t, own);
   if (a.mode == LNMIX_SEQ && r == a.R - 1) lnm_store<NE>(a.shift_tmp, u, t);
 
 #pragma unroll
@@ -294,9 +335,9 @@ __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
     for (int i = 0; i < NE; ++i) o[i] = u[i] + (pv[i] - u[i]) * mu[q][i];
     const long off = q * a.out_q_stride + (long)r * C;
     if (a.out_f16)
-      lnm_store_f16<NE>((half_t*)a.out + off, o, t);
+      lnm_store_f16_own<NE>((half_t*)a.out + off, o, t, own);
     else
-      lnm_store<NE>((float*)a.out + off, o, t);
+      lnm_store_own<NE>((float*)a.out + off, o, t, own);
   }
 }
 
@@ -304,7 +345,14 @@ hipError_t launch_ln_mix(const LnMixArgs& a, hipStream_t st) {
   if (a.C % 256) return hipErrorInvalidValue;
   if (a.nq < 1 || a.nq > 6) return hipErrorInvalidValue;
   if (a.mode == LNMIX_SEQ && a.nparts && (!a.x_out || a.x_out == a.x)) return hipErrorInvalidValue;
-  NE_DISPATCH(a.C, k_ln_mix, dim3(a.R), dim3(256), 0, st, a);
+  // column blocks: not in sequence mode (a row also reads the previous row),
+  // and with partials only into another buffer (the blocks of a row read
+  // the whole residual row while its other blocks write theirs)
+  const int units = (a.C / 256) % 2 == 0 ? a.C / 512 : a.C / 256;
+  if (a.ncb < 1 || a.ncb > units) return hipErrorInvalidValue;
+  if (a.ncb > 1 && (a.mode == LNMIX_SEQ || (a.nparts && (!a.x_out || a.x_out == a.x))))
+    return hipErrorInvalidValue;
+  NE_DISPATCH(a.C, k_ln_mix, dim3(a.R, a.ncb), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

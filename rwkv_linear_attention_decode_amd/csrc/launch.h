@@ -95,6 +95,9 @@ struct LnMixArgs {
   void* out;                // [nq][R][C] (q stride out_q_stride elements)
   int out_f16;
   int64_t out_q_stride;
+  int ncb;                  // workgroups per row, each owning every ncb-th 512-column pair
+                            // (256-column slice for C / 256 odd); 1 = the whole row.  Above
+                            // 1: not in sequence mode, and partials need x_out != x
 };
 hipError_t launch_ln_mix(const LnMixArgs& a, hipStream_t st);
 

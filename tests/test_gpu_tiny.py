@@ -289,6 +289,48 @@ def test_prefill_scan_option_validation(model, R):
     assert R.rwkv7_get_option(model.handle, R.OPT_PREFILL_SCAN) == 0
 
 
+@pytest.mark.parametrize("C", [1024, 3072])
+def test_ln_split_bit_identical(R, C):
+    """The batched LayerNorm kernel's column blocks (OPT_LN_SPLIT) change who
+    computes which columns, never the arithmetic: logits and states are
+    bit-identical for every split, and match the oracle.  C 1024 has two
+    512-column pairs, C 3072 six (splits 4 and 5 deal them unevenly)."""
+    import dataclasses
+    sh = dataclasses.replace(S, name=f"tiny-c{C}", n_embd=C, n_head=C // 64, ffn=4 * C)
+    wts = synth.make_weights(sh, bkey=synth.bkey_table(S))   # the tiny shape's key bias
+    B, steps = 8, 3
+    m = R.Model.from_numpy(sh, wts, n_slots=B, max_B=B, max_T=16)
+    prompts = [np.random.default_rng(40 + b).integers(0, sh.vocab, 5).astype(np.int32) for b in range(B)]
+    feeds = np.random.default_rng(50).integers(0, sh.vocab, (steps, B)).astype(np.int32)
+    slots = dev(list(range(B)))
+    runs = {}
+    units = C // 512 if (C // 256) % 2 == 0 else C // 256
+    for split in [1] + list(range(2, units + 1)) + [0]:
+        m.set_option(R.OPT_LN_SPLIT, split)
+        m.reset(slots)
+        for b in range(B):
+            m.prefill(b, dev(prompts[b]))
+        out = torch.empty(steps, B, sh.vocab, device="cuda")
+        for t in range(steps):
+            m.decode_step(slots, dev(feeds[t]), out[t])
+        torch.cuda.synchronize()
+        runs[split] = (out.cpu().numpy(), np.stack([m.slot_state(b).cpu().numpy() for b in range(B)]))
+        assert m.poll_error() == 0
+    for split, (lg, stt) in runs.items():
+        assert np.array_equal(lg, runs[1][0]), split
+        assert np.array_equal(stt, runs[1][1]), split
+    with pytest.raises(R.RWKV7Error):
+        m.set_option(R.OPT_LN_SPLIT, 17)
+    Wo = O.Weights(sh, wts)
+    for b in (0, B - 1):
+        st = O.State(sh)
+        O.seq(Wo, st, prompts[b], want_logits=False)
+        ref = O.seq(Wo, st, feeds[:, b], want_logits=True)
+        assert rel(runs[1][0][:, b], ref) <= TOL
+        assert rel(runs[1][1][b], st.flat()) <= TOL
+    m.close()
+
+
 def test_prefill_matches_oracle(model, W):
     toks = prompt(8, 50)
     fresh(model, [5])
