@@ -81,6 +81,17 @@ def test_null_and_range_checks_without_device():
     assert L.rwkv7_greedy_workspace_bytes(0, 5, ctypes.byref(u)) == R.RWKV7_EINVAL
     assert L.rwkv7_poll_error(None, None, None) == R.RWKV7_EINVAL
     assert L.rwkv7_set_option(None, 1, 1) == R.RWKV7_EINVAL
+    assert L.rwkv7_set_option(None, R.OPT_LN_SPLIT, 2) == R.RWKV7_EINVAL
+    d = ctypes.c_double()
+    assert L.rwkv7_read_bandwidth(None, 1 << 20, 1, 1, None, ctypes.byref(d)) == R.RWKV7_EINVAL
+    buf = ctypes.create_string_buffer(64)
+    assert L.rwkv7_read_bandwidth(buf, 8, 1, 1, None, ctypes.byref(d)) == R.RWKV7_EINVAL   # under 16 bytes
+    assert L.rwkv7_read_bandwidth(buf, 64, 1, 0, None, ctypes.byref(d)) == R.RWKV7_EINVAL  # no iterations
+    assert L.rwkv7_greedy_noalloc(0, 10, None, None, 1, None, None, None, None, None, None, None) == R.RWKV7_EINVAL
+    # beyond the static scratch: rejected on the host, before any pointer is used
+    assert L.rwkv7_greedy_noalloc(257, 65536, buf, buf, 1, buf, buf, buf, buf, buf, buf, None) == R.RWKV7_ESHAPE
+    u2 = ctypes.c_uint64()
+    assert L.rwkv7_sched_gpu_backend_bytes(None, 4, 16, ctypes.byref(u), ctypes.byref(u2)) == R.RWKV7_EINVAL
     cfg = R.make_config(synth.TINY)
     assert L.rwkv7_workspace_bytes(ctypes.byref(cfg), 0, 1, ctypes.byref(u)) == R.RWKV7_EINVAL
     assert L.rwkv7_state_bytes(ctypes.byref(cfg), 0, ctypes.byref(u), None) == R.RWKV7_EINVAL
