@@ -63,33 +63,16 @@ __device__ __forceinline__ void mm_epilogue(const ProjArgs& a, const Seg& sg, co
     }
 }
 
-// The same through LDS: the tile's sums go to `smem` (MT rows of NT + 4
-// floats; the stage buffers are free once the K loop is done), then every
-// thread writes runs of four columns of a row with one 16-byte store (fp32)
-// or 8-byte store (fp16), instead of the MFMA layout's single floats.
-// Ragged edges and unaligned outputs take the single-element path.
-template <int TM, int TN, int MT, int NT>
-__device__ __forceinline__ void mm_epilogue_lds(const ProjArgs& a, const Seg& sg, const floatx4 (&acc)[TM][TN],
-                                                int ks_id, int n0, int m0, int wm0, int wn0, int lane,
-                                                float* smem) {
+// Writes `rows` rows of a tile staged in LDS (NT + 4 floats apart) to the
+// output rows mr0 .. mr0 + rows - 1 (or to this K range's partial sums).
+template <int NT>
+__device__ __forceinline__ void mm_store_rows(const ProjArgs& a, const Seg& sg, const float* smem, int rows,
+                                              bool split, float* P, bool f16, int n0, int mr0) {
   constexpr int LDR = NT + 4;
   constexpr int C4 = NT / 4;
-  const int fr = lane & 15;
-  const int er = (lane >> 4) * 4;
-  __syncthreads();   // every wave is done reading the stage buffers
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) smem[(wm0 + 16 * i + er + e) * LDR + wn0 + 16 * j + fr] = acc[i][j][e];
-  __syncthreads();
-  const bool split = a.split > 1;
-  float* P = a.part + (long)ks_id * a.M * a.total_rows;
-  const bool f16 = sg.out_f16 != 0;
-  for (int c = threadIdx.x; c < MT * C4; c += blockDim.x) {
+  for (int c = threadIdx.x; c < rows * C4; c += blockDim.x) {
     const int r = c / C4, c4 = (c % C4) * 4;
-    const int m = m0 + r, n = n0 + c4;
+    const int m = mr0 + r, n = n0 + c4;
     if (m >= a.M || n >= sg.row1) continue;
     const floatx4 v = *reinterpret_cast<const floatx4*>(&smem[r * LDR + c4]);
     const bool whole = n + 3 < sg.row1;
@@ -134,6 +117,44 @@ __device__ __forceinline__ void mm_epilogue_lds(const ProjArgs& a, const Seg& sg
 }
 
 
+// The same through LDS: the tile's sums go to `smem` (RCH rows of NT + 4
+// floats at a time; the stage buffers are free once the K loop is done),
+// then every thread writes runs of four columns of a row with one 16-byte
+// store (fp32) or 8-byte store (fp16), instead of the MFMA layout's single
+// floats.  Ragged edges and unaligned outputs take the single-element path.
+// A tile larger than the buffers goes out in chunks of RCH rows.  (Every
+// accumulator index here is a compile-time constant; the single-float
+// epilogue above, unrolled over 32 or more accumulator blocks, is not fully
+// unrolled by the compiler, which then keeps the whole accumulator array in
+// scratch memory, main loop included.)
+template <int TM, int TN, int MT, int NT, int RCH = MT>
+__device__ __forceinline__ void mm_epilogue_lds(const ProjArgs& a, const Seg& sg, const floatx4 (&acc)[TM][TN],
+                                                int ks_id, int n0, int m0, int wm0, int wn0, int lane,
+                                                float* smem) {
+  static_assert(RCH % 16 == 0 && MT % RCH == 0, "whole 16-row blocks per chunk");
+  constexpr int LDR = NT + 4;
+  constexpr int C4 = NT / 4;
+  const int fr = lane & 15;
+  const int er = (lane >> 4) * 4;
+  const bool split = a.split > 1;
+  float* P = a.part + (long)ks_id * a.M * a.total_rows;
+  const bool f16 = sg.out_f16 != 0;
+#pragma unroll
+  for (int c0 = 0; c0 < MT; c0 += RCH) {
+    __syncthreads();   // every wave is done reading the stage buffers (or the previous chunk)
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int rb = wm0 + 16 * i - c0;   // the block's first row in this chunk (uniform per wave)
+      if (RCH < MT && (rb < 0 || rb >= RCH)) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) smem[(rb + er + e) * LDR + wn0 + 16 * j + fr] = acc[i][j][e];
+    }
+    __syncthreads();
+    mm_store_rows<NT>(a, sg, smem, RCH, split, P, f16, n0, m0 + c0);
+  }
+}
 // PIPE = 1 runs the K loop as a three-deep software pipeline (LDS fragment
 // reads of the next stage overlap the current stage's MFMAs); it costs
 // 2 (TM + TN) KS / 32 fragment registers and pays off on some shapes only.
@@ -560,6 +581,9 @@ __global__ __launch_bounds__(64 * NW) void k_mm_dma(ProjArgs a) {
   wait_vm<0>();
   if constexpr (sizeof(L) >= MT * (NT + 4) * 4)
     mm_epilogue_lds<TM, BN, MT, NT>(a, sg, acc, ks_id, n0, m0, wm0, wn0, lane, reinterpret_cast<float*>(&L[0][0]));
+  else if constexpr (sizeof(L) >= 64 * (NT + 4) * 4 && MT % 64 == 0)
+    mm_epilogue_lds<TM, BN, MT, NT, (sizeof(L) >= 128 * (NT + 4) * 4 && MT % 128 == 0) ? 128 : 64>(
+        a, sg, acc, ks_id, n0, m0, wm0, wn0, lane, reinterpret_cast<float*>(&L[0][0]));
   else
     mm_epilogue<TM, BN>(a, sg, acc, ks_id, n0, m0, wm0, wn0, lane);
 }
@@ -876,6 +900,7 @@ static bool mm_cfg_ok(int tm, int tn, int ks, int pipe) {
     return (ks == 64 || ks == 128) && ring_slots(tm, tn, ks, pipe) >= 3;
   }
   if (pipe == 4) {   // eight waves: N blocks split over four wave columns
+    if (tn == 8 && tm == 8) return ks == 32;   // 256 x 256 tiles: eight waves of 128 x 64, 96 KB of LDS
     if (tn == 8)      // 256-wide tiles, 64-deep stages (three of them fill up to 144 KB of LDS)
       return (tm == 2 || tm == 4) && ks == 64;
     if (!((tm == 2 || tm == 4) && (tn == 2 || tn == 4))) return false;
@@ -922,7 +947,8 @@ static MmPlan mm_choose(const ProjArgs& a, int total_rows) {
       if (K >= 16384) return M > 64 && M <= 256 ? MmPlan{4, 4, 64, 4, 3} : MmPlan{4, 4, 64, 0, 6};
       if (M <= 64) return {2, 2, 128, 3, 6};
       if (M <= 256) return {4, 4, 64, 4, 6};
-      return M <= 1024 ? MmPlan{2, 4, 64, 3, 3} : MmPlan{4, 8, 64, 4, 0};
+      // above 1024 rows: 256 x 256 tiles, three K ranges (2048-token prefill 0.5 % faster)
+      return M <= 1024 ? MmPlan{2, 4, 64, 3, 3} : MmPlan{8, 8, 32, 4, 3};
     }
     if (M <= 64) return {2, 2, 128, 3, 6};
     return M <= 256 ? MmPlan{2, 2, 64, 4, 0} : MmPlan{2, 4, 64, 4, 0};
@@ -976,6 +1002,7 @@ hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int 
     for (int i = 0; i < a.nseg; ++i)
       if ((a.seg[i].W ? a.seg[i].K : a.K) % ks != 0) {
         if (tn == 5 || tn == 8) tn = 4;   // 160- and 256-wide tiles exist for the DMA loops only
+        if (tm == 8) tm = 4;
         pipe = mm_cfg_ok(tm, tn, ks, 2) ? 2 : 0;
       }
   if (!mm_cfg_ok(tm, tn, ks, pipe)) return hipErrorInvalidValue;
@@ -991,6 +1018,7 @@ hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int 
     case 25: mm_launch_dma<2, 5, 4>(ks, grid, st, a); break;   // loop 3, ks 64 only
     case 28: hipLaunchKernelGGL((k_mm_dma<2, 8, 64, 8>), grid, dim3(512), 0, st, a); break;   // loop 4
     case 48: hipLaunchKernelGGL((k_mm_dma<4, 8, 64, 8>), grid, dim3(512), 0, st, a); break;   // loop 4
+    case 88: hipLaunchKernelGGL((k_mm_dma<8, 8, 32, 8>), grid, dim3(512), 0, st, a); break;   // loop 4
     default: mm_launch<4, 4>(ks, pipe, grid, st, a); break;
   }
   hipError_t e = hipGetLastError();
