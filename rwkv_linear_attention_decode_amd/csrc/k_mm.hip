@@ -953,8 +953,9 @@ static MmPlan mm_choose(const ProjArgs& a, int total_rows) {
     if (M <= 64) return {2, 2, 128, 3, 6};
     return M <= 256 ? MmPlan{2, 2, 64, 4, 0} : MmPlan{2, 4, 64, 4, 0};
   }
-  if (N >= 32768)   // head
-    return M <= 64 ? MmPlan{2, 4, 64, 3, 0} : M <= 256 ? MmPlan{4, 8, 64, 4, 0} : MmPlan{4, 4, 64, 0, 0};
+  if (N >= 32768)   // head (193 - 256 rows: 256 x 256 tiles, one per CU for a 65536-token vocabulary)
+    return M <= 64 ? MmPlan{2, 4, 64, 3, 0} : M <= 192 ? MmPlan{4, 8, 64, 4, 0} : M <= 256 ? MmPlan{8, 8, 32, 4, 0}
+                                                                                 : MmPlan{4, 4, 64, 0, 0};
   const bool rank_k = K < 1024;                      // adapters' second stage
   if (M <= 64) {
     if (rank_k) return {1, 2, 128, 0, 0};
