@@ -1498,7 +1498,7 @@ const char* rwkv7_kernel_name(const rwkv7_model* m, int32_t cls, int32_t B) {
     case RWKV7_K_HEAD:
       return p.gemv ? gemv_kernel_name(B, m->d.C, EPI_NONE, m->d.V, 1, p.fused, q) : gemm_kernel_name(B, m->d.V, m->d.C);
     case RWKV7_K_WKV: {
-      if (!p.gemv) return "k_wkv_decode_rows";
+      if (!p.gemv) return wkv_rows_waves(B * m->d.H) == 5 ? "k_wkv_decode_rows<5>" : "k_wkv_decode_rows<4>";
       static char name[32];
       snprintf(name, sizeof name, "k_wkv_decode<%d>", (m->d.Dw + m->d.Da + m->d.Dv + m->d.Dg) / 32);
       return name;

@@ -278,11 +278,12 @@ struct WaveVecs {
   float a[64], bb[64], kt[64], d[64], r[64], v[64], y[64];
 };
 
-__global__ __launch_bounds__(256) void k_wkv_decode_rows(WkvArgs a) {
-  __shared__ __attribute__((aligned(16))) WaveVecs wv[4];
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void k_wkv_decode_rows(WkvArgs a) {
+  __shared__ __attribute__((aligned(16))) WaveVecs wv[NW];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int item = blockIdx.x * 4 + wave;        // (row, head) pair
+  const int item = blockIdx.x * NW + wave;       // (row, head) pair
   const bool live = item < a.B * a.H;
   const int b = live ? item / a.H : 0;
   const int h = live ? item % a.H : 0;
@@ -412,11 +413,23 @@ static int wkv_nchk(const WkvArgs& a) {
   return dsum % 32 ? -1 : dsum / 32;
 }
 
+// Waves per workgroup of the many-row kernel: four or five, whichever puts
+// fewer waves on the busiest CU when the workgroups are dealt evenly over
+// 256 CUs (2560 (row, head) pairs: 512 workgroups of five, two per CU,
+// instead of 640 of four, which leave half the CUs a third).
+int wkv_rows_waves(int items) {
+  const int w4 = (items + 3) / 4, w5 = (items + 4) / 5;
+  return (w5 + 255) / 256 * 5 < (w4 + 255) / 256 * 4 ? 5 : 4;
+}
+
 hipError_t launch_wkv_decode(const WkvArgs& a, hipStream_t st) {
   if (a.Lin > LIN_MAX) return hipErrorInvalidValue;
   if (a.lo && !a.u_att) {
     const int items = a.B * a.H;
-    hipLaunchKernelGGL(k_wkv_decode_rows, dim3((items + 3) / 4), dim3(256), 0, st, a);
+    if (wkv_rows_waves(items) == 5)
+      hipLaunchKernelGGL(k_wkv_decode_rows<5>, dim3((items + 4) / 5), dim3(320), 0, st, a);
+    else
+      hipLaunchKernelGGL(k_wkv_decode_rows<4>, dim3((items + 3) / 4), dim3(256), 0, st, a);
     return hipGetLastError();
   }
   switch (wkv_nchk(a)) {

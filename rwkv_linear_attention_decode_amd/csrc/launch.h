@@ -260,6 +260,7 @@ struct WkvArgs {
 };
 hipError_t launch_pack_wkv_adapters(half_t* dst, const half_t* w2, const half_t* a2, const half_t* v2,
                                     const half_t* g2, int C, int Dw, int Da, int Dv, int Dg, hipStream_t st);
+int wkv_rows_waves(int items);   // waves per workgroup of the many-row WKV decode kernel
 hipError_t launch_wkv_decode(const WkvArgs& a, hipStream_t st);
 hipError_t launch_wkv_prep(const WkvArgs& a, hipStream_t st);   // sequence: per (t, h)
 hipError_t launch_wkv_scan(const WkvArgs& a, hipStream_t st);   // sequence: serial in t
