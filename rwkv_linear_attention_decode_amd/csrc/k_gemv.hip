@@ -29,6 +29,21 @@ constexpr int kFusedMaxFloats = 80;
 // longer waits behind a separate compaction pass.
 enum : int { GV_MIXED = 0, GV_PRE = 1, GV_RESID = 2, GV_NONE = 3, GV_PREV = 4 };
 
+// Sum over each aligned group of LPR lanes (all lanes active): DPP moves for
+// 16 and 64 lanes (an xor shuffle is an LDS permute), shuffles otherwise.
+template <int LPR>
+RW_DEV float group_sum(float v) {
+  if constexpr (LPR == 64) {
+    return wave_sum(v);
+  } else if constexpr (LPR == 16) {
+    return sum16(v);
+  } else {
+#pragma unroll
+    for (int o = LPR / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+  }
+}
+
 // NWV waves per workgroup: 4, or 5 for launches with neither the fused
 // LayerNorm prologue nor the value epilogue (both written for four waves).
 // Q: the int8 route.  A weight byte u holds the code u - 128 of a symmetric
@@ -206,9 +221,7 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv(ProjArgs a) {
 #pragma unroll
   for (int i = 0; i < RPW; ++i)
 #pragma unroll
-    for (int b = 0; b < B; ++b)
-#pragma unroll
-      for (int o = LPR / 2; o >= 1; o >>= 1) acc[i][b] += __shfl_xor(acc[i][b], o);
+    for (int b = 0; b < B; ++b) acc[i][b] = group_sum<LPR>(acc[i][b]);
 
   if constexpr (Q) {
     // remove the byte bias with the group's activation sums, then scale the row
@@ -220,9 +233,7 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv(ProjArgs a) {
       for (int c = 0; c < NCH; ++c)
 #pragma unroll
         for (int e = 0; e < 8; ++e) t += xa[b][c][e];
-#pragma unroll
-      for (int o = LPR / 2; o >= 1; o >>= 1) t += __shfl_xor(t, o);
-      sx[b] = t;
+      sx[b] = group_sum<LPR>(t);
     }
 #pragma unroll
     for (int i = 0; i < RPW; ++i)
