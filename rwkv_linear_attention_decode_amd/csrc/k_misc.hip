@@ -530,15 +530,18 @@ __global__ __launch_bounds__(1024) void k_cmix_sparse(CmixArgs a) {
     if (t == 0) *a.dbg_cnt = total;
   }
 
-  // ---- gather: thread t -> row group rg = t/4 (256 of them), 8 columns.
+  // ---- gather: lane 16 c + g of wave w -> row group rg = 16 w + g (256 of
+  // them), columns 8 c .. 8 c + 7 of the slice (the row groups of a chunk
+  // are 16 consecutive lanes, summed by DPP).
   // Workgroups are dealt round-robin to the 8 XCDs; consecutive slices go to
   // the same XCD so the two 64-byte halves of a 128-byte line share an L2.
   const int nsl = a.C / CMIX_COLS;
   const int per_xcd = (nsl + 7) / 8;
   const int slice = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (slice >= nsl) return;
-  const int rg = t >> 2;
-  const int c8 = (t & 3) * 8;
+  static_assert(CMIX_COLS == 32, "four 8-column chunks per slice");
+  const int rg = wave * 16 + (lane & 15);
+  const int c8 = (lane >> 4) * 8;
   const int cb = slice * CMIX_COLS + c8;
   float acc[B][8];
 #pragma unroll
@@ -580,18 +583,14 @@ __global__ __launch_bounds__(1024) void k_cmix_sparse(CmixArgs a) {
     }
   }
 
-  // ---- fixed-order reduction: the 16 row groups of a wave by shuffles
-  // (lane = 4*group + column chunk), then the 16 waves through LDS
+  // ---- fixed-order reduction: the 16 row groups of a wave by DPP
+  // (lane = 16 * column chunk + group), then the 16 waves through LDS
 #pragma unroll
   for (int b = 0; b < B; ++b)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float v = acc[b][e];
-      v += __shfl_xor(v, 4);
-      v += __shfl_xor(v, 8);
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      if (lane < 4) s_red[wave][b][c8 + e] = v;
+      const float v = sum16(acc[b][e]);
+      if ((lane & 15) == 0) s_red[wave][b][c8 + e] = v;
     }
   __syncthreads();
   if (t < B * CMIX_COLS) {
@@ -610,10 +609,9 @@ __global__ __launch_bounds__(1024) void k_cmix_sparse(CmixArgs a) {
 }
 
 // x += the value partial sums of the fused key projection.  Each workgroup
-// owns FOLD_COLS columns: thread t sums 8 of them over partials rg, rg + R,
-// ... (R = 1024 / (FOLD_COLS / 8) row groups, rg = t / (FOLD_COLS / 8)),
-// then lanes and waves meet in a fixed order, so the result does not depend
-// on timing.  32-column slices read whole 128-byte lines of each partial row
+// owns FOLD_COLS columns: a thread sums 8 of them over partials rg, rg + R,
+// ... (R = 1024 / (FOLD_COLS / 8) row groups), then lanes and waves meet in a
+// fixed order, so the result does not depend on timing.  32-column slices read whole 128-byte lines of each partial row
 // (8-column slices, with four times the workgroups, measured slower).
 // Workgroup 0 also writes the debug active list when asked.
 constexpr int FOLD_COLS = 32;
@@ -635,8 +633,10 @@ __global__ __launch_bounds__(1024) void k_cmix_fold(CmixFoldArgs a) {
     if (t == 0) *a.dbg_cnt = total;
   }
   if (slice >= nsl) return;
-  const int rg = t / CPT;
-  const int c8 = (t % CPT) * 8;
+  // lane 16 c + g of wave w: row group 16 w + g, columns 8 c .. 8 c + 7
+  static_assert(CPT == 4, "four 8-column chunks per slice");
+  const int rg = wave * 16 + (lane & 15);
+  const int c8 = (lane >> 4) * 8;
   const int cb = slice * FOLD_COLS + c8;
   float acc[B][8];
 #pragma unroll
@@ -670,10 +670,8 @@ __global__ __launch_bounds__(1024) void k_cmix_fold(CmixFoldArgs a) {
   for (int b = 0; b < B; ++b)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float v = acc[b][e];
-#pragma unroll
-      for (int o = CPT; o < 64; o <<= 1) v += __shfl_xor(v, o);
-      if (lane < CPT) s_red[wave][b][c8 + e] = v;
+      const float v = sum16(acc[b][e]);
+      if ((lane & 15) == 0) s_red[wave][b][c8 + e] = v;
     }
   __syncthreads();
   if (t < B * FOLD_COLS) {
