@@ -303,28 +303,37 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv(ProjArgs a) {
     float corr[B];   // int8 route: sum of h * s over the rows taken, times the bias 128
 #pragma unroll
     for (int b = 0; b < B; ++b) corr[b] = 0.f;
-    // up to four active rows per pass: their loads are issued together
+    // up to VP active rows per pass, their loads issued together (only for
+    // the pass's rows: the condition is the same in every thread; columns
+    // past the row end re-read the last chunk and are not stored), so a
+    // workgroup with up to VP active rows of its 20 (about 3 on average at
+    // 85 % sparsity) makes one dependent round trip
+    constexpr int VP = 12;
+    const int c0l = c0 < nchunk ? c0 : nchunk - 1;
+    const int c1l = c1 < nchunk ? c1 : nchunk - 1;
     while (act) {
-      int rr[4];
+      int rr[VP];
       int nr = 0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < VP; ++u) {
         rr[u] = act ? __builtin_ctz(act) : 0;
         nr += act ? 1 : 0;
         act &= act - 1;
       }
-      if constexpr (Q) {
-        u32x2 q0[4], q1[4];
-        float vs[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+      for (int u = 1; u < VP; ++u) rr[u] = u < nr ? rr[u] : rr[0];
+      if constexpr (Q) {
+        u32x2 q0[VP], q1[VP];
+        float vs[VP];
+#pragma unroll
+        for (int u = 0; u < VP; ++u) {
           const uint8_t* wr = a.vWq + (long)(row_wg + rr[u]) * a.vC;
-          q0[u] = (u < nr && c0 < nchunk) ? ld8(wr + c0 * 8) : u32x2{0u, 0u};
-          q1[u] = (u < nr && c1 < nchunk) ? ld8(wr + c1 * 8) : u32x2{0u, 0u};
+          q0[u] = u < nr ? ld8(wr + c0l * 8) : u32x2{0u, 0u};
+          q1[u] = u < nr ? ld8(wr + c1l * 8) : u32x2{0u, 0u};
           vs[u] = u < nr ? a.vSc[row_wg + rr[u]] : 0.f;
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < VP; ++u) {
           if (u < nr) {
 #pragma unroll
             for (int b = 0; b < B; ++b) {
@@ -342,15 +351,15 @@ __global__ __launch_bounds__(64 * NWV) void k_gemv(ProjArgs a) {
         }
         continue;
       }
-      u32x4 w0[4], w1[4];
+      u32x4 w0[VP], w1[VP];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < VP; ++u) {
         const half_t* wr = a.vW + (long)(row_wg + rr[u]) * a.vC;
-        w0[u] = (u < nr && c0 < nchunk) ? ld16(wr + c0 * 8) : u32x4{0u, 0u, 0u, 0u};
-        w1[u] = (u < nr && c1 < nchunk) ? ld16(wr + c1 * 8) : u32x4{0u, 0u, 0u, 0u};
+        w0[u] = u < nr ? ld16(wr + c0l * 8) : u32x4{0u, 0u, 0u, 0u};
+        w1[u] = u < nr ? ld16(wr + c1l * 8) : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < VP; ++u) {
         if (u < nr) {
           const half8 h0 = __builtin_bit_cast(half8, w0[u]);
           const half8 h1 = __builtin_bit_cast(half8, w1[u]);
