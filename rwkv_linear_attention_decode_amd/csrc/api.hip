@@ -504,9 +504,8 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
 
   ValidateArgs va{slot_idx, tok, B, B, n_slots, d.V, -1, w.slots, w.tok, w.err, counters,
                   nullptr, 0};
-  RUN(RWKV7_K_OTHER, "validate", launch_validate(va, st));
   EmbedArgs ea{m->pk.emb, m->pk.ln0_w, m->pk.ln0_b, w.tok, w.x, B, C};
-  RUN(RWKV7_K_OTHER, "embed", launch_embed(ea, st));
+  RUN(RWKV7_K_OTHER, "validate + embed", launch_embed_rows(va, ea, st));
 
   // Fused path (small B): LayerNorm + token-shift mix run inside the GEMV
   // prologues; the new shifts are committed by the following kernel (WKV

@@ -129,6 +129,63 @@ hipError_t launch_embed(const EmbedArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Decode rows in one launch: workgroup r checks row r's slot (range; a slot
+// listed by an earlier row drops this row, so the first occurrence keeps it)
+// and token, writes their sanitized copies, bumps the slot's counter, and
+// embeds the token with LN0 -- what k_validate and k_embed do, with the
+// earlier-row comparisons spread over the workgroup's threads.
+template <int NE>
+__global__ __launch_bounds__(256) void k_embed_rows(ValidateArgs v, EmbedArgs a) {
+  __shared__ float red[8];
+  __shared__ int s_dup;
+  const int r = blockIdx.x;
+  const int t = threadIdx.x;
+  if (t == 0) s_dup = 0;
+  __syncthreads();
+  const int s = v.slot_idx[r];
+  const bool in_range = s >= 0 && (int64_t)s < v.n_slots;
+  if (in_range)
+    for (int j = t; j < r; j += 256)
+      if (v.slot_idx[j] == s) s_dup = 1;   // any writer: the value is the same
+  __syncthreads();
+  int tok = v.tokens[r];
+  const bool tok_ok = tok >= 0 && tok < v.vocab;
+  if (!tok_ok) tok = 0;
+  if (t == 0) {
+    uint32_t bits = 0;
+    int out = s;
+    if (!in_range) {
+      bits |= ERRB_SLOT_RANGE;
+      out = -1;
+    } else if (s_dup) {
+      bits |= ERRB_SLOT_DUP;
+      out = -1;
+    }
+    if (!tok_ok) bits |= ERRB_TOKEN_RANGE;
+    v.slots_out[r] = out;
+    v.tok_out[r] = tok;
+    if (out >= 0 && v.counters) v.counters[out] += 1;
+    if (bits) set_err(v.err, bits);
+  }
+  const half_t* e = a.emb + (long)tok * a.C;
+  float x[NE];
+#pragma unroll
+  for (int i = 0; i < NE; ++i) x[i] = (float)e[t + 256 * i];
+  float mean, rstd;
+  ln_rows<NE>(x, &mean, &rstd, red);
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    const int c = t + 256 * i;
+    a.x[(long)r * a.C + c] = (x[i] - mean) * rstd * a.g[c] + a.b[c];
+  }
+}
+
+hipError_t launch_embed_rows(const ValidateArgs& v, const EmbedArgs& a, hipStream_t st) {
+  if (a.C % 256 || v.n_rows != a.R || v.n_tok != a.R || v.n_zero) return hipErrorInvalidValue;
+  NE_DISPATCH(a.C, k_embed_rows, dim3(a.R), dim3(256), 0, st, v, a);
+  return hipGetLastError();
+}
+
 // ============================================================== LN + token-shift mix
 // One workgroup per row.  Every global load the row needs (x, partial sums,
 // LayerNorm weights, the stored shift or the previous token's row, and all

@@ -71,6 +71,8 @@ struct EmbedArgs {
   int R, C;
 };
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t st);
+// decode: k_validate's row checks and k_embed in one launch (n_rows == n_tok == R)
+hipError_t launch_embed_rows(const ValidateArgs& v, const EmbedArgs& a, hipStream_t st);
 
 enum { LNMIX_DECODE = 0, LNMIX_SEQ = 1, LNMIX_PLAIN = 2 };
 struct LnMixArgs {
