@@ -8,9 +8,11 @@
 #include <limits.h>
 
 // ============================================================== validation
-// One workgroup.  Decode: checks every row's slot (range, duplicates) and
-// token (range), writes sanitized copies, bumps each valid slot's counter.
-// Prefill: checks tokens and bumps the slot's counter by n_tok.
+// One workgroup.  Rows (n_rows > 0): checks every row's slot (range,
+// duplicates) and token (range), writes sanitized copies, bumps each valid
+// slot's counter (decode steps do this inside k_embed_rows instead, one
+// workgroup per row).  Prefill: checks tokens and bumps the slot's counter
+// by n_tok.
 // Rows whose slot repeats an earlier row's slot are dropped (the first
 // occurrence keeps it).  The slot list is scanned from LDS when it fits.
 constexpr int VALIDATE_LDS_ROWS = 4096;
