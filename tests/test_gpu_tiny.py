@@ -333,6 +333,20 @@ def test_ln_split_bit_identical(R, C):
     m.close()
 
 
+def test_read_bandwidth_reads_only(R):
+    """rwkv7_read_bandwidth streams a buffer and leaves it as it was; a size that
+    is not a multiple of 16 bytes reads the whole 16-byte chunks only."""
+    buf = torch.arange(1 << 20, dtype=torch.float32, device="cuda")
+    ref = buf.clone()
+    for nt in (True, False):
+        gbs = R.rwkv7_read_bandwidth(buf, nontemporal=nt, iters=3)
+        assert gbs > 0
+    tail = buf.view(torch.uint8)[: (1 << 22) - 8]
+    assert R.rwkv7_read_bandwidth(tail, iters=1) > 0
+    torch.cuda.synchronize()
+    assert torch.equal(buf, ref)
+
+
 def test_prefill_matches_oracle(model, W):
     toks = prompt(8, 50)
     fresh(model, [5])
