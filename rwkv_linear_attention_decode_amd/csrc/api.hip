@@ -187,7 +187,7 @@ Packed pack_layout(const Dims& d, char* base) {
 struct Ws {
   uint32_t* err;
   int *slots, *tok;
-  float *x, *x2, *xq, *rkv, *lin, *lo, *vfirst, *yg, *xk, *pre, *xo, *shift_tmp, *u_att, *u_ffn;
+  float *x, *x2, *xq, *rkv, *lin, *lo, *vfirst, *yg, *xk, *pre, *xo, *shift_tmp, *shift_tmp2, *u_att, *u_ffn;
   unsigned char* mask;
   int *dbg_idx, *dbg_cnt;
   float *q_d, *q_a, *q_b, *q_kt, *q_v, *q_g, *q_bonus, *q_brk, *q_y;
@@ -224,6 +224,7 @@ Ws ws_layout(const Dims& d, int R, char* base) {
   w.mask = (unsigned char*)take(F);
   w.xo = (float*)take(r * C * 4);
   w.shift_tmp = (float*)take(C * 4);
+  w.shift_tmp2 = (float*)take(C * 4);   // prefill: the channel-mix LayerNorm's last row
   w.dbg_idx = (int*)take(F * 4);
   w.dbg_cnt = (int*)take(4);
   w.u_att = (float*)take(r * C * 4);
@@ -677,12 +678,20 @@ int enqueue_prefill_chunk(rwkv7_model* m, float* pool, int64_t n_slots, int slot
   float* xc = w.x;
   float* xn = w.x2;
   int pending = 0;
+  // A LayerNorm's last-row output is the slot's new shift, but its own first
+  // row still reads the old one: it goes to a temporary, copied into the slot
+  // by the next LayerNorm launch (the channel-mix one for the time-mix shift,
+  // the next layer's time-mix one for the channel-mix shift).
+  const float* cp_ffn = nullptr;   // the previous layer's channel-mix shift, not yet in the slot
   for (int l = 0; l < d.L; ++l) {
     const LayerPtrs& q = m->pk.layers[l];
     const int64_t lo = (int64_t)l * d.layer_floats;
     LnMixArgs la;
     memset(&la, 0, sizeof la);
     la.x = xc; la.C = C; la.R = T; la.mode = LNMIX_SEQ; la.ncb = 1;
+    if (cp_ffn) {
+      la.cp_src = cp_ffn; la.cp_dst = slot_base + lo - d.layer_floats + C; la.cp_n = C;
+    }
     if (pending) {
       la.parts = w.part; la.nparts = pending; la.x_out = xn;
       std::swap(xc, xn);
@@ -694,7 +703,6 @@ int enqueue_prefill_chunk(rwkv7_model* m, float* pool, int64_t n_slots, int slot
     la.mu = q.mu6; la.nq = 6;
     la.out = w.xq; la.out_f16 = 1; la.out_q_stride = (int64_t)T * C;
     RUN(RWKV7_K_LN_MIX, "ln_mix(tmix)", launch_ln_mix(la, st));
-    RUN(RWKV7_K_OTHER, "shift copy", launch_copy_f32(slot_base + lo, w.shift_tmp, C, st));
 
     ProjArgs pa;
     proj_in_args(d, q, w, T, true, pa);
@@ -730,6 +738,8 @@ int enqueue_prefill_chunk(rwkv7_model* m, float* pool, int64_t n_slots, int slot
     LnMixArgs lc = la;
     lc.g = q.ln2_w; lc.b = q.ln2_b;
     lc.shift_off = lo + C;
+    lc.shift_tmp = w.shift_tmp2;
+    lc.cp_src = w.shift_tmp; lc.cp_dst = slot_base + lo; lc.cp_n = C;   // this layer's time-mix shift
     lc.mu = q.mu_k; lc.nq = 1;
     lc.out = w.xk; lc.out_q_stride = 0;
     lc.x = xc; lc.parts = nullptr; lc.nparts = 0; lc.x_out = nullptr;
@@ -739,7 +749,7 @@ int enqueue_prefill_chunk(rwkv7_model* m, float* pool, int64_t n_slots, int slot
       pending = 0;
     }
     RUN(RWKV7_K_LN_MIX, "ln_mix(cmix)", launch_ln_mix(lc, st));
-    RUN(RWKV7_K_OTHER, "shift copy", launch_copy_f32(slot_base + lo + C, w.shift_tmp, C, st));
+    cp_ffn = w.shift_tmp2;
 
     ProjArgs pk;
     memset(&pk, 0, sizeof pk);
@@ -754,7 +764,10 @@ int enqueue_prefill_chunk(rwkv7_model* m, float* pool, int64_t n_slots, int slot
     pv.seg[0] = mkseg(0, C, EPI_RESID, w.pre, d.F, xc, C);
     RUN(RWKV7_K_CMIX_VALUE, "cmix_value", proj(false, pv, C, w, st, m->opt_plan[4], &pending));
   }
-  // the last layer's value partials are not needed: prefill returns no logits
+  // the last layer's channel-mix shift; its value partials are not needed
+  // (prefill returns no logits)
+  RUN(RWKV7_K_OTHER, "shift copy",
+      launch_copy_f32(slot_base + (int64_t)(d.L - 1) * d.layer_floats + C, w.shift_tmp2, C, st));
   return RWKV7_OK;
 }
 

@@ -287,6 +287,8 @@ __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
   // only its own units of everything else
   uint32_t own = 0;
   for (int u = blockIdx.y; u < lnm_units<NE>(); u += gridDim.y) own |= 1u << u;
+  if (a.cp_n && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = t; i < a.cp_n; i += 256) a.cp_dst[i] = a.cp_src[i];
   float v[NE], gv[NE], bv[NE], pv[NE], mu[6][NE];
   float* xr = a.x + (long)r * C;
   lnm_load<NE>(xr, v, t);
@@ -404,6 +406,7 @@ hipError_t launch_ln_mix(const LnMixArgs& a, hipStream_t st) {
   if (a.C % 256) return hipErrorInvalidValue;
   if (a.nq < 1 || a.nq > 6) return hipErrorInvalidValue;
   if (a.mode == LNMIX_SEQ && a.nparts && (!a.x_out || a.x_out == a.x)) return hipErrorInvalidValue;
+  if (a.cp_n < 0 || (a.cp_n && (!a.cp_src || !a.cp_dst || a.cp_src == a.shift_tmp))) return hipErrorInvalidValue;
   // column blocks: not in sequence mode (a row also reads the previous row),
   // and with partials only into another buffer (the blocks of a row read
   // the whole residual row while its other blocks write theirs)

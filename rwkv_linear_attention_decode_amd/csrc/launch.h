@@ -100,6 +100,9 @@ struct LnMixArgs {
   int ncb;                  // workgroups per row, each owning every ncb-th 512-column pair
                             // (256-column slice for C / 256 odd); 1 = the whole row.  Above
                             // 1: not in sequence mode, and partials need x_out != x
+  const float* cp_src;      // side job of workgroup 0: cp_dst[0 .. cp_n) = cp_src[...]
+  float* cp_dst;            // (prefill: the previous LayerNorm's last-row output into
+  int cp_n;                 // its slot's shift, once nothing reads the old one)
 };
 hipError_t launch_ln_mix(const LnMixArgs& a, hipStream_t st);
 
