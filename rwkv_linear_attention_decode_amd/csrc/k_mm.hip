@@ -965,6 +965,13 @@ static MmPlan mm_choose(const ProjArgs& a, int total_rows) {
   if (M <= 256) {
     if (rank_k) return {2, 2, 64, 2, 0};
     if (K >= 4096) return N >= 16384 ? MmPlan{4, 4, 64, 4, 0} : MmPlan{4, 2, 64, 4, 0};
+    // the key on 64 x 128 tiles with one K range while they fit one round of
+    // 256 CUs (2.9B: up to 192 rows; 38 -> 29 us at 128 and 192 rows), and
+    // up to 128 rows the input projection on 64 x 64 tiles with 128-deep
+    // stages (40 -> 32 us): whole 128-token prefill 4.93 -> 4.37 ms, B = 128
+    // decode steps 5.40 -> 4.93 ms
+    if (a.nseg == 1 && (long)(M + 63) / 64 * ((N + 127) / 128) <= 256) return {2, 4, 64, 3, 1};
+    if (M <= 128 && a.nseg > 1) return {2, 2, 128, 3, 0};
     // one segment: 64 x 160 tiles when they fill the CUs in fewer column-widths
     // of rounds than 64 x 64 tiles (2.9B key at M = 256: 256 tiles, one per CU,
     // instead of 640, which leave half the CUs a third round)
