@@ -375,8 +375,9 @@ def sample_timing(R, m, logits, occ, slots, pres, freq, dec, reps=20):
     """rwkv7_sample on a step's logits with the adapter defaults the pages give
     (temperature 1.0, top_p 0.3, top_k 0) and the workload's penalties; seeded
     uniforms, a copy of the occurrence rows.  Algorithmic bytes: logits read
-    plus occurrence read and write (12 B per token); the workspace passes of
-    the radix selects stay in L2 and are not counted."""
+    plus occurrence read and write (12 B per token); the second read of the
+    logits and occurrences and the key workspace (written once, read again
+    by the selection's gather) are not counted."""
     import torch
     B, V = logits.shape
     ws = torch.zeros(R.rwkv7_sample_workspace_bytes(B, V), dtype=torch.uint8, device="cuda")

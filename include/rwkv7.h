@@ -210,7 +210,11 @@ int rwkv7_greedy_noalloc(int32_t B, int32_t V, const float* logits, float* occ_p
  *   candidates: tokens with forbidden[v] == 0 (forbidden may be NULL) and z
  *     finite;
  *   order: z descending (IEEE total order, -0 after +0), then index ascending;
- *   weight: floor(exp(z - max z) * 2^31), computed in fp64;
+ *   weight: floor(exp(z - max z) * 2^31), z - max z in fp64 and exp by a
+ *     fixed sequence of fp64 operations, each rounded to nearest even and none
+ *     fused (Cody-Waite reduction with ln2 split at 2^-40, the degree-13
+ *     Taylor polynomial by Horner's rule, scaling by 2^n; within 2 ulp of
+ *     exp), so every implementation of the definition gets the same weights;
  *   top-k (0 < top_k[b] < candidates): the first top_k[b] candidates;
  *   top-p (top_p[b] < 1): the shortest non-empty prefix of those whose weight
  *     sum reaches ceil(top_p[b] * their total) (fp64 product);
@@ -226,8 +230,9 @@ int rwkv7_greedy_noalloc(int32_t B, int32_t V, const float* logits, float* occ_p
  * top_k: device int32[B]; forbidden: device uint8[V] or NULL; ids_out:
  * device int32[B].  The caller draws the uniforms.  `ws`: a device buffer of
  * rwkv7_sample_workspace_bytes (its first word is the error word read by
- * rwkv7_poll_error).  EINVAL for null pointers or sizes, ENOTSUP for V >
- * 65536, ESHAPE for a short workspace; nothing is launched then. */
+ * rwkv7_poll_error; about 4 V + 49 KB per row).  EINVAL for null pointers
+ * or sizes, ENOTSUP for V > 65536, ESHAPE for a short workspace; nothing is
+ * launched then. */
 int rwkv7_sample_workspace_bytes(int32_t B, int32_t V, uint64_t* bytes);
 int rwkv7_sample(int32_t B, int32_t V, const float* logits, float* occ_pool, int64_t n_slots,
                  const int32_t* slot_idx, const float* presence, const float* frequency,

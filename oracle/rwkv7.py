@@ -37,11 +37,13 @@ the shifts and the head -- with planted slips in each that the fixture
 rejects; sparse = dense channel-mix; whole-model invariants (sequence =
 steps, batch = singles, prefix split, slot permutation, bounded state);
 greedy brute force and a hand-worked penalty example
-(tests/golden/greedy_penalty.json).  Parity against any third party is
+(tests/golden/greedy_penalty.json); the sampler against softmax frequencies
+and its exp_fixed against a correctly rounded exp.  Parity against any third party is
 unpinned: the pages print no logits, states or weights.
 """
 from __future__ import annotations
 
+import math
 from typing import Dict, List, Optional, Sequence
 
 import numpy as np
@@ -401,6 +403,41 @@ def _order_key(z: np.ndarray) -> np.ndarray:
     return np.where(bits >> 31, (~bits) & 0xFFFFFFFF, bits | 0x80000000)
 
 
+# exp for the sampling weights, evaluated by a fixed sequence of IEEE float64
+# operations (each rounded to nearest even, none fused), so that any
+# implementation that performs the same operations gets the same bits:
+# Cody and Waite's argument reduction t = n ln2 + r with ln2 split in two
+# (ln2_hi has 40 fractional bits, so n * ln2_hi is exact for |n| <= 32),
+# then the degree-13 Taylor polynomial of exp(r), |r| <= ln2 / 2, by Horner's
+# rule, scaled by 2**n.  Truncation error < 5e-18 relative; the rounding of
+# the 30 operations adds a few ulp.
+_EXP_INV_LN2 = float.fromhex("0x1.71547652b82fep+0")     # 1/ln2 rounded to float64
+_EXP_LN2_HI = float.fromhex("0x1.62e42fefa4000p-1")      # ln2 rounded to a multiple of 2**-40
+_EXP_LN2_LO = float.fromhex("-0x1.8432a1b0e2634p-43")    # ln2 - ln2_hi rounded to float64
+_EXP_TAYLOR = [1.0 / math.factorial(k) for k in range(14)]   # 1/k! rounded to float64
+
+
+def exp_fixed(t) -> np.ndarray:
+    """exp(t) for float64 t in [-22, 0] (see the comment above); 0 below -22."""
+    t = np.asarray(t, dtype=np.float64)
+    inside = t >= -22.0
+    ti = np.where(inside, t, 0.0)
+    n = np.rint(np.multiply(ti, _EXP_INV_LN2))
+    r = np.subtract(np.subtract(ti, np.multiply(n, _EXP_LN2_HI)), np.multiply(n, _EXP_LN2_LO))
+    p = np.full_like(ti, _EXP_TAYLOR[13])
+    for k in range(12, -1, -1):
+        p = np.add(_EXP_TAYLOR[k], np.multiply(r, p))
+    return np.where(inside, np.ldexp(p, n.astype(np.int32)), 0.0)
+
+
+def sample_weights(z: np.ndarray, m) -> np.ndarray:
+    """The sampler's fixed-point weights floor(exp(z - m) * 2**31) as int64
+    (z float32 candidates, m their maximum): z - m in float64 (exact operands,
+    one rounding), exp by exp_fixed, the scaling by 2**31 exact."""
+    t = np.subtract(np.asarray(z, dtype=np.float32).astype(np.float64), np.float64(m))
+    return np.floor(exp_fixed(t) * 2.0 ** 31).astype(np.int64)
+
+
 def sample_penalized(logits: np.ndarray, occ: np.ndarray, presence, frequency, decay_, temperature,
                      top_p, top_k, forbidden, uniform):
     """Penalised temperature / top-k / top-p sampling per row, with the occurrence update.
@@ -414,7 +451,8 @@ def sample_penalized(logits: np.ndarray, occ: np.ndarray, presence, frequency, d
       l' as in greedy_penalized (float32); z = l' / T (float32);
       candidates: tokens not forbidden with z finite;
       order: z descending (IEEE total order, -0 after +0), then index ascending;
-      weight: W = floor(exp(z - max z) * 2**31), computed in float64 (0 .. 2**31);
+      weight: W = floor(exp(z - max z) * 2**31) (0 .. 2**31), z - max z in
+        float64 and exp by exp_fixed (a fixed sequence of float64 operations);
       top-k (0 < k < candidates): the first k candidates in that order;
       top-p (p < 1): the shortest non-empty prefix of those whose weight sum
         reaches ceil(p * S_k) (float64 product, S_k = their weight sum);
@@ -458,7 +496,7 @@ def sample_penalized(logits: np.ndarray, occ: np.ndarray, presence, frequency, d
             comp = (_order_key(zc) << np.uint64(16)) | (np.uint64(0xFFFF) - idx[ci])
             order = ci[np.argsort(comp)[::-1]]                       # descending, unique keys
             m = np.float64(zc.max())
-            w = np.floor(np.exp(z[order].astype(np.float64) - m) * 2.0 ** 31).astype(np.int64)
+            w = sample_weights(z[order], m)
             n = len(order)
             k = 1 if greedy else int(top_k[b])
             kk = n if (k <= 0 or k >= n) else k

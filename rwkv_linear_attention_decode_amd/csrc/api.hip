@@ -1248,10 +1248,39 @@ int rwkv7_read_bandwidth(const void* buf, uint64_t bytes, int32_t nontemporal, i
   return RWKV7_OK;
 }
 
+// Sample workspace: error word | key [B][V] u32 | histogram
+// counts [B][4096] u32 | histogram weights [B][4096] u64 | per-workgroup max
+// [B][SAMPLE_MAX_G] f32 | candidates [B] u32 | weight sums [B] u64.  Fills `a`'s
+// pointers when it is not null; returns the size.
+static uint64_t sample_layout(int64_t B, int64_t V, SampleArgs* a, char* base = nullptr) {
+  uint64_t off = ALIGN;
+  auto take = [&](uint64_t bytes) {
+    const uint64_t o = off;
+    off += align_up(bytes);
+    return base + o;
+  };
+  char* key = take((uint64_t)B * V * 4);
+  char* hc = take((uint64_t)B * 4096 * 4);
+  char* hm = take((uint64_t)B * 4096 * 8);
+  char* pm = take((uint64_t)B * SAMPLE_MAX_G * 4);
+  char* rn = take((uint64_t)B * 4);
+  char* rt = take((uint64_t)B * 8);
+  if (a) {
+    a->err = (uint32_t*)base;
+    a->key = (uint32_t*)key;
+    a->hcnt = (uint32_t*)hc;
+    a->hmass = (unsigned long long*)hm;
+    a->pmax = (float*)pm;
+    a->rown = (uint32_t*)rn;
+    a->rowtot = (unsigned long long*)rt;
+  }
+  return off;
+}
+
 int rwkv7_sample_workspace_bytes(int32_t B, int32_t V, uint64_t* bytes) {
   if (!bytes) return fail(RWKV7_EINVAL, "bytes is NULL");
   if (B < 1 || V < 1) return fail(RWKV7_EINVAL, "B and V must be >= 1");
-  *bytes = ALIGN + align_up((uint64_t)B * V * 4) * 2;
+  *bytes = sample_layout(B, V, nullptr);
   return RWKV7_OK;
 }
 
@@ -1276,11 +1305,8 @@ int rwkv7_sample(int32_t B, int32_t V, const float* logits, float* occ_pool, int
   a.presence = presence; a.frequency = frequency; a.decay = decay;
   a.temperature = temperature; a.top_p = top_p; a.top_k = top_k; a.forbidden = forbidden;
   a.uniform = uniform; a.ids = ids_out;
-  char* base = (char*)ws;
-  a.err = (uint32_t*)base;
-  a.key = (uint32_t*)(base + ALIGN);
-  a.wt = (uint32_t*)(base + ALIGN + align_up((uint64_t)B * V * 4));
-  a.B = B; a.V = V;
+  sample_layout(B, V, &a, (char*)ws);
+  a.B = B; a.V = V; a.G = sample_groups(B, V);
   HIP_TRY(launch_sample(a, (hipStream_t)stream), "sample");
   return RWKV7_OK;
 }

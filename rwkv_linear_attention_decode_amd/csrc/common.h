@@ -157,6 +157,22 @@ RW_DEV float block_sum_256(float v, float* red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
+// Single fp32 operations rounded to nearest even.  HIP's __fmul_rn
+// family are plain operators, which the compiler may fuse into an FMA after
+// inlining; these may not be fused.
+RW_DEV float mul_rn(float x, float y) {
+#pragma clang fp contract(off)
+  return x * y;
+}
+RW_DEV float add_rn(float x, float y) {
+#pragma clang fp contract(off)
+  return x + y;
+}
+RW_DEV float sub_rn(float x, float y) {
+#pragma clang fp contract(off)
+  return x - y;
+}
+
 RW_DEV void set_err(uint32_t* err, uint32_t bits) {
   if (err) atomicOr(err, bits);
 }

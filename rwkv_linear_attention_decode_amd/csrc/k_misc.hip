@@ -797,12 +797,14 @@ constexpr int GREEDY_PER_BLOCK = 2048;
 // Error bits of row b's slot: outside the pool, or listed by an earlier row.
 // Such a row reads and updates no occurrence row (two rows naming one slot
 // would otherwise update it from two workgroups at once).
+// Every thread of the workgroup must call it (the earlier rows are split over
+// the threads; it holds a barrier) and gets the same bits.
 RW_DEV uint32_t row_slot_bits(const int* slot_idx, int b, int64_t n_slots) {
   const int slot = slot_idx[b];
-  if (slot < 0 || (int64_t)slot >= n_slots) return ERRB_SLOT_RANGE;
-  for (int j = 0; j < b; ++j)
-    if (slot_idx[j] == slot) return ERRB_SLOT_DUP;
-  return 0u;
+  if (slot < 0 || (int64_t)slot >= n_slots) return ERRB_SLOT_RANGE;   // the same in every thread
+  int dup = 0;
+  for (int j = threadIdx.x; j < b; j += blockDim.x) dup |= slot_idx[j] == slot;
+  return __syncthreads_or(dup) ? ERRB_SLOT_DUP : 0u;
 }
 
 __global__ __launch_bounds__(256) void k_greedy_part(GreedyArgs a) {
@@ -824,8 +826,8 @@ __global__ __launch_bounds__(256) void k_greedy_part(GreedyArgs a) {
     float l = lg[v];
     if (occ) {
       const float o = occ[v];
-      if (o > 0.f) l = __fsub_rn(l, __fadd_rn(__fmul_rn(freq, o), pres));
-      occ[v] = __fmul_rn(o, dec);
+      if (o > 0.f) l = sub_rn(l, add_rn(mul_rn(freq, o), pres));
+      occ[v] = mul_rn(o, dec);
     }
     if (better(l, v, bv, bi)) {
       bv = l;
@@ -854,6 +856,7 @@ __global__ __launch_bounds__(256) void k_greedy_part(GreedyArgs a) {
 
 __global__ __launch_bounds__(64) void k_greedy_final(GreedyArgs a) {
   const int b = blockIdx.x;
+  const uint32_t bad = row_slot_bits(a.slot_idx, b, a.n_slots);
   float bv = 0.f;
   int bi = INT_MAX;
   for (int k = threadIdx.x; k < a.nblk; k += 64) {
@@ -880,9 +883,9 @@ __global__ __launch_bounds__(64) void k_greedy_final(GreedyArgs a) {
     }
     a.ids[b] = id;
     const int slot = a.slot_idx[b];
-    if (!row_slot_bits(a.slot_idx, b, a.n_slots)) {
+    if (!bad) {
       float* o = a.occ + (int64_t)slot * a.V + id;
-      *o = __fadd_rn(*o, 1.0f);
+      *o = add_rn(*o, 1.0f);
     }
   }
 }
@@ -895,90 +898,477 @@ __global__ __launch_bounds__(64) void k_greedy_final(GreedyArgs a) {
 //   z = l' / T (fp32, l' as in greedy); candidates: not forbidden, z finite;
 //   order: the 48-bit key (ordered bits of z) << 16 | (0xFFFF - index), so
 //   z descending then index ascending, every key distinct;
-//   weight: floor(exp(z - max z) * 2^31) in fp64;
+//   weight: floor(smp_exp(z - max z) * 2^31), z - max z in fp64;
 //   top-k, top-p and the draw each take the shortest prefix of that order
 //   whose count or weight sum reaches a goal (k; ceil(p * S_k); floor(u * S)
-//   + 1), found by a radix select over the key, 12 bits per level, with
-//   count and weight histograms in LDS (integer atomics, so the sums do not
-//   depend on timing).
-// One 1024-thread workgroup per row; the keys and weights go through the
-// workspace between the passes.
-constexpr int SMP_THREADS = 1024;
+//   + 1).  The kept sets are prefixes of the whole order and every goal is at
+//   most its set's total, so each search runs over the whole order.
+// Three launches per call:
+//   k_smp_max, grid (G, B): each workgroup takes a chunk of the row and
+//     writes the chunk's largest z; it also clears its share of the row's
+//     histogram and totals;
+//   k_smp_weights, grid (G, B): the row's max from the G partials; key and
+//     weight of every token into the workspace; the chunk's histogram over
+//     the key's top 12 bits (count and weight sum, integer atomics in LDS)
+//     added into the row's histogram; the occurrence decay;
+//   k_smp_select, grid B: each search finds its top-level bin from the row's
+//     histogram, gathers that bin's tokens into LDS once (a later search in
+//     the same bin reuses them) and resolves the remaining 36 bits in three
+//     12-bit levels; then occ[id] += 1.
+// Integer sums do not depend on the order of the atomics, so neither does
+// the result.
+constexpr int SMP_THREADS = 1024;   // k_smp_select
+constexpr int SMP_PT = 256;         // k_smp_max, k_smp_weights
 constexpr int SMP_BINS = 4096;
+constexpr int SMP_LIST = 8192;      // tokens gathered into LDS for the finer levels
 
-constexpr int SMP_LIST = 4096;   // tokens of one top-level bin kept in LDS for the finer levels
+// exp(t) for t in [-22, 0] (0 below) by a fixed sequence of fp64 operations,
+// none fused: Cody and Waite's reduction t = n ln2 + r with ln2 split into
+// ln2_hi (40 fractional bits: n * ln2_hi is exact for |n| <= 32) and ln2_lo,
+// then the degree-13 Taylor polynomial of exp(r), |r| <= ln2 / 2, by Horner's
+// rule (truncation < 5e-18 relative), scaled by 2^n.  The constants are
+// 1/ln2, ln2_hi, ln2 - ln2_hi and 1/k!, each rounded to fp64.
+RW_DEV double smp_exp(double t) {
+#pragma clang fp contract(off)
+  if (!(t >= -22.0)) return 0.0;
+  constexpr double inv_ln2 = 0x1.71547652b82fep+0;
+  constexpr double ln2_hi = 0x1.62e42fefa4000p-1;
+  constexpr double ln2_lo = -0x1.8432a1b0e2634p-43;
+  constexpr double c[14] = {1.0, 1.0, 1.0 / 2, 1.0 / 6, 1.0 / 24, 1.0 / 120, 1.0 / 720, 1.0 / 5040,
+                            1.0 / 40320, 1.0 / 362880, 1.0 / 3628800, 1.0 / 39916800, 1.0 / 479001600,
+                            1.0 / 6227020800.0};
+  const double n = rint(t * inv_ln2);
+  const double r = (t - n * ln2_hi) - n * ln2_lo;
+  double p = c[13];
+#pragma unroll
+  for (int k = 12; k >= 0; --k) p = c[k] + r * p;
+  return ldexp(p, (int)n);
+}
+
+RW_DEV uint32_t smp_weight(float z, float mx) {
+  const double e = smp_exp((double)z - (double)mx);   // exact operands, one rounding
+  return (uint32_t)(e * 2147483648.0);                  // exact scaling; truncation = floor
+}
+
+RW_DEV uint32_t smp_order_key(float z) {
+  const uint32_t b = __float_as_uint(z);
+  return (b >> 31) ? ~b : (b | 0x80000000u);
+}
+
+// Penalised, tempered logit; NaN marks a token that is not a candidate.
+struct SmpRow {
+  float pres, freq, T;
+  bool greedy;
+  RW_DEV float z(float l, float o, bool forb) const {
+    const float lp = o > 0.f ? sub_rn(l, add_rn(mul_rn(freq, o), pres)) : l;
+    const float x = greedy ? lp : __fdiv_rn(lp, T);
+    return (!isfinite(x) || forb) ? NAN : x;
+  }
+};
+
+RW_DEV SmpRow smp_row(const SampleArgs& a, int b) {
+  SmpRow r;
+  r.T = a.temperature[b];
+  r.pres = a.presence[b];
+  r.freq = a.frequency[b];
+  r.greedy = !(r.T > 0.f);
+  return r;
+}
+
+// z from its order key (the inverse of smp_order_key).
+RW_DEV float smp_key_z(uint32_t k) { return __uint_as_float((k >> 31) ? (k & 0x7FFFFFFFu) : ~k); }
+
+// Chunk [v0, v1) of the row for workgroup g of G (starts are multiples of 256).
+RW_DEV void smp_chunk(int V, int G, int g, int& v0, int& v1) {
+  const int ch = ((V + G - 1) / G + SMP_PT - 1) / SMP_PT * SMP_PT;
+  v0 = min(V, g * ch);
+  v1 = min(V, v0 + ch);
+}
+
+// NV consecutive tokens from v (NV = 4: v and v1 multiples of 4, rows 16-byte
+// aligned); past v1 a token reads as NaN (not a candidate).
+template <int NV>
+RW_DEV void smp_load(const float* lg, const float* occ, const unsigned char* forb, int v, int v1, float (&l)[NV],
+                     float (&o)[NV], bool (&f)[NV]) {
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    l[e] = NAN;
+    o[e] = 0.f;
+    f[e] = false;
+  }
+  if (v >= v1) return;
+  if constexpr (NV == 4) {
+    const float4 x = *reinterpret_cast<const float4*>(lg + v);
+    l[0] = x.x; l[1] = x.y; l[2] = x.z; l[3] = x.w;
+    if (occ) {
+      const float4 y = *reinterpret_cast<const float4*>(occ + v);
+      o[0] = y.x; o[1] = y.y; o[2] = y.z; o[3] = y.w;
+    }
+    if (forb) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(forb + v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[e] = ((w >> (8 * e)) & 0xFFu) != 0u;
+    }
+  } else {
+    l[0] = lg[v];
+    if (occ) o[0] = occ[v];
+    if (forb) f[0] = forb[v] != 0;
+  }
+}
+
+template <int NV>
+__global__ __launch_bounds__(SMP_PT) void k_smp_max(SampleArgs a) {
+  constexpr int U = NV == 4 ? 4 : 8;
+  __shared__ float red[SMP_PT / 64];
+  const int g = blockIdx.x, b = blockIdx.y, t = threadIdx.x, G = gridDim.x;
+  const int nb = SMP_BINS / G;   // G is a power of two <= 64
+  for (int i = t; i < nb; i += SMP_PT) {
+    a.hcnt[(int64_t)b * SMP_BINS + g * nb + i] = 0u;
+    a.hmass[(int64_t)b * SMP_BINS + g * nb + i] = 0ull;
+  }
+  if (g == 0 && t == 0) {
+    a.rown[b] = 0u;
+    a.rowtot[b] = 0ull;
+  }
+  const bool bad = row_slot_bits(a.slot_idx, b, a.n_slots) != 0u;
+  const float* occ = bad ? nullptr : a.occ + (int64_t)a.slot_idx[b] * a.V;
+  const float* lg = a.logits + (int64_t)b * a.V;
+  const SmpRow row = smp_row(a, b);
+  int v0, v1;
+  smp_chunk(a.V, G, g, v0, v1);
+  float mx = -INFINITY;
+  for (int base = v0 + NV * t; base < v1; base += SMP_PT * NV * U) {
+    float l[U][NV], o[U][NV];
+    bool f[U][NV];
+#pragma unroll
+    for (int i = 0; i < U; ++i) smp_load<NV>(lg, occ, a.forbidden, base + SMP_PT * NV * i, v1, l[i], o[i], f[i]);
+#pragma unroll
+    for (int i = 0; i < U; ++i)
+#pragma unroll
+      for (int e = 0; e < NV; ++e) {
+        const float x = row.z(l[i][e], o[i][e], f[i][e]);
+        if (x == x) mx = fmaxf(mx, x);
+      }
+  }
+  mx = wave_max(mx);
+  if ((t & 63) == 0) red[t >> 6] = mx;
+  __syncthreads();
+  if (t == 0) a.pmax[(int64_t)b * SAMPLE_MAX_G + g] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+template <int NV>
+__global__ __launch_bounds__(SMP_PT) void k_smp_weights(SampleArgs a) {
+  constexpr int U = NV == 4 ? 4 : 8;
+  __shared__ uint32_t hc[SMP_BINS];
+  __shared__ unsigned long long hm[SMP_BINS];
+  __shared__ unsigned long long red[2][SMP_PT / 64];
+  const int g = blockIdx.x, b = blockIdx.y, t = threadIdx.x, G = gridDim.x;
+  for (int i = t; i < SMP_BINS; i += SMP_PT) {
+    hc[i] = 0u;
+    hm[i] = 0ull;
+  }
+  float mx = -INFINITY;
+  for (int j = 0; j < G; ++j) mx = fmaxf(mx, a.pmax[(int64_t)b * SAMPLE_MAX_G + j]);
+  const bool bad = row_slot_bits(a.slot_idx, b, a.n_slots) != 0u;
+  float* occ = bad ? nullptr : a.occ + (int64_t)a.slot_idx[b] * a.V;
+  const float* lg = a.logits + (int64_t)b * a.V;
+  uint32_t* key = a.key + (int64_t)b * a.V;
+  const SmpRow row = smp_row(a, b);
+  const float dec = a.decay[b];
+  int v0, v1;
+  smp_chunk(a.V, G, g, v0, v1);
+  __syncthreads();
+  unsigned long long n = 0, tot = 0;
+  for (int base = v0 + NV * t; base < v1; base += SMP_PT * NV * U) {
+    float l[U][NV], o[U][NV];
+    bool f[U][NV];
+#pragma unroll
+    for (int i = 0; i < U; ++i) smp_load<NV>(lg, occ, a.forbidden, base + SMP_PT * NV * i, v1, l[i], o[i], f[i]);
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int v = base + SMP_PT * NV * i;
+      if (v >= v1) continue;
+      uint32_t k[NV];
+      float od[NV];
+#pragma unroll
+      for (int e = 0; e < NV; ++e) {
+        const float x = row.z(l[i][e], o[i][e], f[i][e]);
+        const bool c = x == x;
+        const uint32_t w = c ? smp_weight(x, mx) : 0u;
+        k[e] = c ? smp_order_key(x) : 0u;
+        if (c) {
+          atomicAdd(&hc[k[e] >> 20], 1u);   // bits 47..36 of the 48-bit key
+          atomicAdd(&hm[k[e] >> 20], (unsigned long long)w);
+        }
+        n += c;
+        tot += w;
+        od[e] = mul_rn(o[i][e], dec);
+      }
+      if constexpr (NV == 4) {
+        *reinterpret_cast<u32x4*>(key + v) = u32x4{k[0], k[1], k[2], k[3]};
+        if (occ) *reinterpret_cast<float4*>(occ + v) = float4{od[0], od[1], od[2], od[3]};
+      } else {
+        key[v] = k[0];
+        if (occ) occ[v] = od[0];
+      }
+    }
+  }
+  // wave sums of the two totals, then one atomic each per workgroup
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    n += __shfl_xor(n, o);
+    tot += __shfl_xor(tot, o);
+  }
+  if ((t & 63) == 0) {
+    red[0][t >> 6] = n;
+    red[1][t >> 6] = tot;
+  }
+  __syncthreads();
+  for (int i = t; i < SMP_BINS; i += SMP_PT) {
+    if (hc[i]) {
+      atomicAdd(&a.hcnt[(int64_t)b * SMP_BINS + i], hc[i]);
+      atomicAdd(&a.hmass[(int64_t)b * SMP_BINS + i], hm[i]);
+    }
+  }
+  if (t == 0) {
+    const unsigned long long cn = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+    const unsigned long long ct = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+    if (cn) {
+      atomicAdd(&a.rown[b], (uint32_t)cn);
+      atomicAdd(&a.rowtot[b], ct);
+    }
+  }
+}
+
+constexpr int SMP_SMALL = 64;   // a bin this small is resolved by one wave
 
 struct SampleLds {
   uint32_t cnt[SMP_BINS];
   unsigned long long mass[SMP_BINS];
-  unsigned long long lkey[SMP_LIST];
+  unsigned long long lkey[SMP_LIST];   // gathered tokens: 48-bit key and weight
   uint32_t lwt[SMP_LIST];
-  int lcount;
-  unsigned long long wtot[16];
-  float fred[16];
+  unsigned long long skey[SMP_SMALL];
+  uint32_t swt[SMP_SMALL];
+  int lcount, lrange, lbin, scount;    // the list holds every token with digit >= lrange, or digit == lbin
+  unsigned long long wtot[2][SMP_THREADS / 64];
   int sel_digit;
-  unsigned long long sel_c, sel_m, sel_here;
+  uint32_t sel_cnt;
+  unsigned long long sel_c, sel_m;
+  unsigned long long res_key, res_m;
 };
 
-RW_DEV uint64_t smp_order_key(float z) {
-  const uint32_t b = __float_as_uint(z);
-  return (b >> 31) ? (uint64_t)(~b) : (uint64_t)(b | 0x80000000u);
-}
-
-// Exclusive prefix sum over the 1024 threads (in thread order).
-RW_DEV unsigned long long smp_exscan(unsigned long long v, SampleLds& L) {
+// Exclusive prefix sums of two values over the 1024 threads (in thread order).
+RW_DEV void smp_exscan2(unsigned long long& x, unsigned long long& y, SampleLds& L) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  unsigned long long incl = v;
+  unsigned long long ix = x, iy = y;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const unsigned long long n = __shfl_up(incl, o);
-    if (lane >= o) incl += n;
+    const unsigned long long nx = __shfl_up(ix, o), ny = __shfl_up(iy, o);
+    if (lane >= o) {
+      ix += nx;
+      iy += ny;
+    }
   }
-  if (lane == 63) L.wtot[wave] = incl;
+  if (lane == 63) {
+    L.wtot[0][wave] = ix;
+    L.wtot[1][wave] = iy;
+  }
   __syncthreads();
-  unsigned long long base = 0;
-  for (int w = 0; w < wave; ++w) base += L.wtot[w];
+  unsigned long long bx = 0, by = 0;
+  for (int w = 0; w < wave; ++w) {
+    bx += L.wtot[0][w];
+    by += L.wtot[1][w];
+  }
   __syncthreads();
-  return base + incl - v;
+  x = bx + ix - x;
+  y = by + iy - y;
 }
 
-RW_DEV unsigned long long smp_sum(unsigned long long v, SampleLds& L) {
-  const unsigned long long e = smp_exscan(v, L);
-  if (threadIdx.x == SMP_THREADS - 1) L.sel_here = e + v;
-  __syncthreads();
-  const unsigned long long r = L.sel_here;
-  __syncthreads();
-  return r;
-}
-
-// The shortest prefix, in descending key order, of the row's candidates with
-// key >= lo whose count (by_mass false) or weight sum reaches goal (1 <= goal
-// <= that set's total).  Returns the key of its last token; *pm: the prefix's
-// weight sum.  The first level reads the row from the workspace; when the
-// chosen top-level bin holds at most SMP_LIST tokens they are gathered into
-// LDS once and the three finer levels read that list instead.
-RW_DEV uint64_t smp_key(const uint32_t* key, int v) {   // 48-bit order key of token v (0: none)
-  const uint32_t k = key[v];
-  return k ? ((uint64_t)k << 16) | (uint64_t)(0xFFFF - v) : 0ull;
-}
-
-RW_DEV uint64_t smp_select(const uint32_t* key, const uint32_t* wt, int V, uint64_t lo, bool by_mass,
-                           unsigned long long goal, unsigned long long* pm, SampleLds& L,
-                           bool hist_ready = false) {
+// One level of a search: thread t owns bins 4095 - 4t down to 4092 - 4t (in
+// descending key order); the bin where the running count (or weight sum)
+// first reaches `goal` goes to L.sel_*.  above_c / above_m: count and weight
+// of the tokens before every bin of this level.
+RW_DEV void smp_pick(const unsigned long long (&bc)[4], const unsigned long long (&bm)[4], bool by_mass,
+                     unsigned long long goal, unsigned long long above_c, unsigned long long above_m, SampleLds& L) {
   const int t = threadIdx.x;
-  uint64_t prefix = 0;
-  unsigned long long above_c = 0, above_m = 0, here_m = 0;
-  bool listed = false;
-  for (int level = 0; level < 4; ++level) {
+  unsigned long long sc = bc[0] + bc[1] + bc[2] + bc[3], sm = bm[0] + bm[1] + bm[2] + bm[3];
+  smp_exscan2(sc, sm, L);
+  unsigned long long rc = above_c + sc, rm = above_m + sm;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const unsigned long long before = by_mass ? rm : rc, here = by_mass ? bm[q] : bc[q];
+    if (here && before < goal && before + here >= goal) {
+      L.sel_digit = SMP_BINS - 1 - 4 * t - q;
+      L.sel_cnt = (uint32_t)bc[q];
+      L.sel_c = rc;
+      L.sel_m = rm;
+    }
+    rc += bc[q];
+    rm += bm[q];
+  }
+  __syncthreads();
+}
+
+// This thread's four bins of a histogram (see smp_pick).
+template <typename C, typename M>
+RW_DEV void smp_bins(const C* cnt, const M* mass, unsigned long long (&bc)[4], unsigned long long (&bm)[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int d = SMP_BINS - 1 - 4 * threadIdx.x - q;
+    bc[q] = cnt[d];
+    bm[q] = mass[d];
+  }
+}
+
+// Append (key, weight) to an LDS array, one atomic per wave for the lanes
+// that hit; entries at or past `cap` are dropped (the counts bound them).
+RW_DEV void smp_append(bool hit, uint64_t c, uint32_t w, int* count, unsigned long long* keys, uint32_t* wts,
+                       int cap) {
+  const uint64_t m = __ballot(hit);
+  if (!m) return;
+  const int lane = threadIdx.x & 63, leader = __ffsll((unsigned long long)m) - 1;
+  int at = 0;
+  if (lane == leader) at = atomicAdd(count, __popcll(m));
+  at = __shfl(at, leader);
+  const int j = at + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+  if (hit && j < cap) {
+    keys[j] = c;
+    wts[j] = w;
+  }
+}
+
+RW_DEV uint64_t smp_key48(uint32_t k, int v) { return ((uint64_t)k << 16) | (uint64_t)(0xFFFF - v); }
+
+// Every candidate of the row whose top-level digit is >= d (range) or == d,
+// into the LDS list; then the weights of the listed tokens.
+template <int NV>
+RW_DEV void smp_gather(const uint32_t* key, int V, float mx, int d, bool range, SampleLds& L) {
+  constexpr int U = 8;
+  const int t = threadIdx.x;
+  for (int base = NV * t; base - NV * t < V; base += SMP_THREADS * NV * U) {
+    uint32_t k[U][NV];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int v = base + SMP_THREADS * NV * i;
+      if constexpr (NV == 4) {
+        const u32x4 x = v < V ? *reinterpret_cast<const u32x4*>(key + v) : u32x4{0u, 0u, 0u, 0u};
+        k[i][0] = x[0]; k[i][1] = x[1]; k[i][2] = x[2]; k[i][3] = x[3];
+      } else {
+        k[i][0] = v < V ? key[v] : 0u;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < U; ++i)
+#pragma unroll
+      for (int e = 0; e < NV; ++e) {
+        const int v = base + SMP_THREADS * NV * i + e;
+        const int dg = (int)(k[i][e] >> 20);
+        const bool hit = k[i][e] != 0u && (range ? dg >= d : dg == d);
+        smp_append(hit, smp_key48(k[i][e], v), 0u, &L.lcount, L.lkey, L.lwt, SMP_LIST);
+      }
+  }
+  __syncthreads();
+  const int nl = min(L.lcount, SMP_LIST);
+  for (int i = threadIdx.x; i < nl; i += SMP_THREADS) L.lwt[i] = smp_weight(smp_key_z((uint32_t)(L.lkey[i] >> 16)), mx);
+}
+
+// The few (<= SMP_SMALL) candidates whose keys share `prefix`'s top `bits`
+// bits: gathered, then wave 0 finds the first whose running count (weight
+// sum) reaches `goal`.  Returns its key; *pm: the weight sum through it.
+RW_DEV uint64_t smp_small(const uint32_t* key, int V, float mx, bool listed, uint64_t prefix, int bits,
+                          unsigned long long above_c, unsigned long long above_m, bool by_mass,
+                          unsigned long long goal, unsigned long long* pm, SampleLds& L) {
+  const int t = threadIdx.x, lane = t & 63;
+  const int sh = 48 - bits;
+  if (t == 0) L.scount = 0;
+  __syncthreads();
+  if (listed) {
+    const int nl = min(L.lcount, SMP_LIST);
+    for (int base = 0; base < nl; base += SMP_THREADS) {
+      const int i = base + t;
+      const uint64_t c = i < nl ? L.lkey[i] : 0ull;
+      const bool hit = i < nl && (c >> sh) == (prefix >> sh);
+      smp_append(hit, c, hit ? L.lwt[i] : 0u, &L.scount, L.skey, L.swt, SMP_SMALL);
+    }
+  } else {
+    for (int base = 0; base < V; base += SMP_THREADS) {
+      const int v = base + t;
+      const uint32_t k = v < V ? key[v] : 0u;
+      const uint64_t c = smp_key48(k, v);
+      const bool hit = k != 0u && (c >> sh) == (prefix >> sh);
+      smp_append(hit, c, hit ? smp_weight(smp_key_z(k), mx) : 0u, &L.scount, L.skey, L.swt, SMP_SMALL);
+    }
+  }
+  __syncthreads();
+  if (t < 64) {
+    const int n = min(L.scount, SMP_SMALL);
+    const uint64_t my = lane < n ? L.skey[lane] : 0ull;
+    unsigned long long cc = 0, cm = 0;
+    for (int j = 0; j < n; ++j) {
+      const uint64_t kj = L.skey[j];
+      if (kj >= my) {
+        cc += 1;
+        cm += L.swt[j];
+      }
+    }
+    const bool q = lane < n && (by_mass ? above_m + cm : above_c + cc) >= goal;
+    uint64_t best = q ? my : 0ull;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint64_t x = __shfl_xor(best, o);
+      best = x > best ? x : best;
+    }
+    if (q && my == best) {
+      L.res_key = best;
+      L.res_m = above_m + cm;
+    }
+  }
+  __syncthreads();
+  *pm = L.res_m;
+  return L.res_key;
+}
+
+// The shortest prefix of the row's order whose count (by_mass false) or
+// weight sum reaches goal (1 <= goal <= the row's total).  Returns the 48-bit
+// key of its last token; *pm: the prefix's weight sum.
+template <int NV>
+RW_DEV uint64_t smp_search(const SampleArgs& a, int b, float mx, const unsigned long long (&h0c)[4],
+                           const unsigned long long (&h0m)[4], bool by_mass, unsigned long long goal,
+                           unsigned long long* pm, SampleLds& L) {
+  const int t = threadIdx.x;
+  const int V = a.V;
+  const uint32_t* key = a.key + (int64_t)b * V;
+  smp_pick(h0c, h0m, by_mass, goal, 0, 0, L);
+  const int d0 = L.sel_digit;
+  uint32_t cnt = L.sel_cnt;
+  unsigned long long above_c = L.sel_c, above_m = L.sel_m;
+  bool listed = d0 >= L.lrange || d0 == L.lbin;   // the same in every thread
+  if (!listed && cnt <= SMP_LIST) {
+    const bool range = above_c + cnt <= SMP_LIST;
+    __syncthreads();
+    if (t == 0) {
+      L.lcount = 0;
+      L.lrange = range ? d0 : SMP_BINS;
+      L.lbin = range ? -1 : d0;
+    }
+    __syncthreads();
+    smp_gather<NV>(key, V, mx, d0, range, L);
+    __syncthreads();
+    listed = true;
+  }
+  uint64_t prefix = (uint64_t)d0 << 36;
+  for (int level = 1;; ++level) {
+    if (cnt <= SMP_SMALL || level == 4)   // all 48 bits fixed: one token
+      return smp_small(key, V, mx, listed, prefix, 12 * level, above_c, above_m, by_mass, goal, pm, L);
     const int shift = 36 - 12 * level;
-    if (level == 0 && hist_ready) goto scan;   // the top-level histogram of every candidate is in LDS
     for (int i = t; i < SMP_BINS; i += SMP_THREADS) {
       L.cnt[i] = 0;
       L.mass[i] = 0;
     }
     __syncthreads();
     if (listed) {
-      for (int i = t; i < L.lcount; i += SMP_THREADS) {
+      const int nl = min(L.lcount, SMP_LIST);
+      for (int i = t; i < nl; i += SMP_THREADS) {
         const uint64_t c = L.lkey[i];
         if ((c >> (shift + 12)) == (prefix >> (shift + 12))) {
           const int d = (int)((c >> shift) & (SMP_BINS - 1));
@@ -988,171 +1378,104 @@ RW_DEV uint64_t smp_select(const uint32_t* key, const uint32_t* wt, int V, uint6
       }
     } else {
       for (int v = t; v < V; v += SMP_THREADS) {
-        const uint64_t c = smp_key(key, v);
-        if (c >= lo && c != 0 && (level == 0 || (c >> (shift + 12)) == (prefix >> (shift + 12)))) {
+        const uint32_t k = key[v];
+        const uint64_t c = smp_key48(k, v);
+        if (k != 0u && (c >> (shift + 12)) == (prefix >> (shift + 12))) {
           const int d = (int)((c >> shift) & (SMP_BINS - 1));
           atomicAdd(&L.cnt[d], 1u);
-          atomicAdd(&L.mass[d], (unsigned long long)wt[v]);
+          atomicAdd(&L.mass[d], (unsigned long long)smp_weight(smp_key_z(k), mx));
         }
       }
     }
     __syncthreads();
-  scan:
-    // thread t owns bins 4095 - 4t down to 4092 - 4t
-    unsigned long long bc[4], bm[4], sc = 0, sm = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int d = SMP_BINS - 1 - 4 * t - q;
-      bc[q] = L.cnt[d];
-      bm[q] = L.mass[d];
-      sc += bc[q];
-      sm += bm[q];
-    }
-    unsigned long long rc = above_c + smp_exscan(sc, L), rm = above_m + smp_exscan(sm, L);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const unsigned long long before = by_mass ? rm : rc, here = by_mass ? bm[q] : bc[q];
-      if (here && before < goal && before + here >= goal) {
-        L.sel_digit = SMP_BINS - 1 - 4 * t - q;
-        L.sel_c = rc;
-        L.sel_m = rm;
-        L.sel_here = bm[q];
-      }
-      rc += bc[q];
-      rm += bm[q];
-    }
-    __syncthreads();
+    unsigned long long bc[4], bm[4];
+    smp_bins(L.cnt, L.mass, bc, bm);
+    smp_pick(bc, bm, by_mass, goal, above_c, above_m, L);
     prefix |= (uint64_t)L.sel_digit << shift;
+    cnt = L.sel_cnt;
     above_c = L.sel_c;
     above_m = L.sel_m;
-    here_m = L.sel_here;
-    const bool gather = level == 0 && L.cnt[L.sel_digit] <= SMP_LIST;   // the same in every thread
-    if (gather && t == 0) L.lcount = 0;
     __syncthreads();
-    if (gather) {
-      // the tokens of the chosen bin (all >= lo: the bin is at or above lo's)
-      for (int v = t; v < V; v += SMP_THREADS) {
-        const uint64_t c = smp_key(key, v);
-        if (c >= lo && c != 0 && (c >> 36) == (prefix >> 36)) {
-          const int i = atomicAdd(&L.lcount, 1);
-          L.lkey[i] = c;
-          L.lwt[i] = wt[v];
-        }
-      }
-      __syncthreads();
-      listed = true;
-    }
   }
-  *pm = above_m + here_m;   // the last level's bin holds the boundary token alone
-  return prefix;
 }
 
-__global__ __launch_bounds__(1024) void k_sample(SampleArgs a) {
+template <int NV>
+__global__ __launch_bounds__(SMP_THREADS) void k_smp_select(SampleArgs a) {
   __shared__ SampleLds L;
   const int b = blockIdx.x, t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
-  const int V = a.V;
-  const int slot = a.slot_idx[b];
   const uint32_t bad = row_slot_bits(a.slot_idx, b, a.n_slots);
   if (bad && t == 0) set_err(a.err, bad);
-  float* occ = bad ? nullptr : a.occ + (int64_t)slot * V;
-  const float* lg = a.logits + (int64_t)b * V;
-  uint32_t* key = a.key + (int64_t)b * V;
-  uint32_t* wt = a.wt + (int64_t)b * V;
-  const float T = a.temperature[b], pres = a.presence[b], freq = a.frequency[b];
-  const bool greedy = !(T > 0.f);
-
-  // penalised, tempered logit of token v; NaN marks a token that is not a
-  // candidate (the second pass recomputes it: the same fp32 ops)
-  auto zval = [&](int v) {
-    const float l = lg[v];
-    const float o = occ ? occ[v] : 0.f;
-    const float lp = o > 0.f ? __fsub_rn(l, __fadd_rn(__fmul_rn(freq, o), pres)) : l;
-    const float x = greedy ? lp : __fdiv_rn(lp, T);
-    return (!isfinite(x) || (a.forbidden && a.forbidden[v])) ? NAN : x;
-  };
-  float mx = -INFINITY;
-  for (int v = t; v < V; v += SMP_THREADS) {
-    const float x = zval(v);
-    if (x == x) mx = fmaxf(mx, x);
+  if (t == 0) {
+    L.lcount = 0;
+    L.lrange = SMP_BINS;
+    L.lbin = -1;
+    L.sel_digit = 0;
+    L.sel_cnt = 0;
+    L.sel_c = L.sel_m = 0;
+    L.res_key = L.res_m = 0;
   }
+  const unsigned long long n = a.rown[b], tot = a.rowtot[b];
+  // the row's max: the G partials, one per lane of every wave
+  float mx = (t & 63) < a.G ? a.pmax[(int64_t)b * SAMPLE_MAX_G + (t & 63)] : -INFINITY;
   mx = wave_max(mx);
-  if (lane == 0) L.fred[wave] = mx;
+  unsigned long long h0c[4], h0m[4];   // this thread's bins of the row's top-level histogram
+  smp_bins(a.hcnt + (int64_t)b * SMP_BINS, a.hmass + (int64_t)b * SMP_BINS, h0c, h0m);
+  const bool greedy = !(a.temperature[b] > 0.f);
   __syncthreads();
-  mx = L.fred[0];
-  for (int w = 1; w < SMP_THREADS / 64; ++w) mx = fmaxf(mx, L.fred[w]);
-
-  // keys and weights, and the top-level histogram of every candidate (the
-  // first selection starts from it)
-  for (int i = t; i < SMP_BINS; i += SMP_THREADS) {
-    L.cnt[i] = 0;
-    L.mass[i] = 0;
-  }
-  __syncthreads();
-  unsigned long long n = 0, tot = 0;
-#pragma unroll 1
-  for (int v = t; v < V; v += SMP_THREADS) {
-    const float x = zval(v);
-    const bool c = x == x;
-    const uint32_t w = c ? (uint32_t)floor(exp((double)x - (double)mx) * 2147483648.0) : 0u;
-    const uint32_t k = c ? (uint32_t)smp_order_key(x) : 0u;
-    key[v] = k;
-    wt[v] = w;
-    if (c) {
-      const int d = (int)(k >> 20);   // bits 47..36 of the 48-bit key
-      atomicAdd(&L.cnt[d], 1u);
-      atomicAdd(&L.mass[d], (unsigned long long)w);
-    }
-    n += c;
-    tot += w;
-  }
-  n = smp_sum(n, L);
-  tot = smp_sum(tot, L);   // the barriers inside also publish key / wt to the workgroup
-
   int id = 0;
   if (n == 0) {
     if (t == 0) set_err(a.err, ERRB_ALL_NAN);
   } else {
     const int k = greedy ? 1 : a.top_k[b];
-    uint64_t lo = 1;
     unsigned long long S = tot;
-    bool ready = true;   // the histogram in LDS covers every candidate (key >= 1)
-    if (k > 0 && (unsigned long long)k < n) {
-      lo = smp_select(key, wt, V, lo, false, (unsigned long long)k, &S, L, ready);
-      ready = false;
-    }
+    if (k > 0 && (unsigned long long)k < n) smp_search<NV>(a, b, mx, h0c, h0m, false, (unsigned long long)k, &S, L);
     const float p = a.top_p[b];
     if (p < 1.f) {
       const double g = ceil((double)p * (double)S);
-      lo = smp_select(key, wt, V, lo, true, g < 1.0 ? 1ull : (unsigned long long)g, &S, L, ready);
-      ready = false;
+      smp_search<NV>(a, b, mx, h0c, h0m, true, g < 1.0 ? 1ull : (unsigned long long)g, &S, L);
     }
     float u = a.uniform[b];
     if (!(u >= 0.f)) u = 0.f;
     if (u >= 1.f) u = 0x1.fffffep-1f;
     const unsigned long long target = (unsigned long long)floor((double)u * (double)S);
     unsigned long long m;
-    const uint64_t kb = smp_select(key, wt, V, lo, true, target + 1, &m, L, ready);
+    const uint64_t kb = smp_search<NV>(a, b, mx, h0c, h0m, true, target + 1, &m, L);
     id = 0xFFFF - (int)(kb & 0xFFFF);
-    if (id >= V) {   // not reachable when every goal is within its set's total
+    if (kb == 0 || id >= a.V) {   // not reachable when every goal is within its set's total
       id = 0;
       if (t == 0) set_err(a.err, ERRB_ALL_NAN);
     }
   }
-  if (occ) {
-    const float dec = a.decay[b];
-    for (int v = t; v < V; v += SMP_THREADS) {
-      float o = __fmul_rn(occ[v], dec);
-      if (v == id) o = __fadd_rn(o, 1.0f);
-      occ[v] = o;
+  if (t == 0) {
+    a.ids[b] = id;
+    if (!bad) {
+      float* o = a.occ + (int64_t)a.slot_idx[b] * a.V + id;
+      *o = add_rn(*o, 1.0f);
     }
   }
-  if (t == 0) a.ids[b] = id;
+}
+
+int sample_groups(int B, int V) {
+  int G = 1;
+  while (G < SAMPLE_MAX_G && (int64_t)B * G * 2 <= 512 && (int64_t)V >= (int64_t)G * 2 * 1024) G *= 2;
+  return G;
 }
 
 hipError_t launch_sample(const SampleArgs& a, hipStream_t st) {
-  if (a.B < 1 || a.V < 1 || a.V > SAMPLE_MAX_V) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_sample, dim3(a.B), dim3(SMP_THREADS), 0, st, a);
+  if (a.B < 1 || a.V < 1 || a.V > SAMPLE_MAX_V || a.G < 1 || a.G > SAMPLE_MAX_G || (a.G & (a.G - 1)))
+    return hipErrorInvalidValue;
+  // 16-byte loads and stores when every row starts 16-byte aligned
+  const bool vec = a.V % 4 == 0 && (uintptr_t)a.logits % 16 == 0 && (uintptr_t)a.occ % 16 == 0 &&
+                   (uintptr_t)a.key % 16 == 0 && (!a.forbidden || (uintptr_t)a.forbidden % 4 == 0);
+  if (vec) {
+    hipLaunchKernelGGL(k_smp_max<4>, dim3(a.G, a.B), dim3(SMP_PT), 0, st, a);
+    hipLaunchKernelGGL(k_smp_weights<4>, dim3(a.G, a.B), dim3(SMP_PT), 0, st, a);
+    hipLaunchKernelGGL(k_smp_select<4>, dim3(a.B), dim3(SMP_THREADS), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(k_smp_max<1>, dim3(a.G, a.B), dim3(SMP_PT), 0, st, a);
+    hipLaunchKernelGGL(k_smp_weights<1>, dim3(a.G, a.B), dim3(SMP_PT), 0, st, a);
+    hipLaunchKernelGGL(k_smp_select<1>, dim3(a.B), dim3(SMP_THREADS), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -186,7 +186,8 @@ struct GreedyArgs {
 int greedy_blocks(int V);
 hipError_t launch_greedy(const GreedyArgs& a, hipStream_t st);
 
-// penalised temperature / top-k / top-p sampling (one workgroup per row, V <= 65536)
+// penalised temperature / top-k / top-p sampling (V <= 65536): three launches,
+// the first two over G workgroups per row, the third one workgroup per row
 struct SampleArgs {
   const float* logits;
   float* occ;
@@ -203,10 +204,16 @@ struct SampleArgs {
   int* ids;
   uint32_t* err;
   uint32_t* key;                    // [B][V] workspace: ordered bits of z (0 = not a candidate)
-  uint32_t* wt;                     // [B][V] workspace: fixed-point weights
-  int B, V;
+  uint32_t* hcnt;                   // [B][4096] workspace: top-level histogram, token counts
+  unsigned long long* hmass;        // [B][4096] workspace: top-level histogram, weight sums
+  float* pmax;                      // [B][SAMPLE_MAX_G] workspace: per-workgroup max z
+  uint32_t* rown;                   // [B] workspace: candidates per row
+  unsigned long long* rowtot;       // [B] workspace: weight sum per row
+  int B, V, G;                      // G = sample_groups(B, V)
 };
 constexpr int SAMPLE_MAX_V = 65536;
+constexpr int SAMPLE_MAX_G = 64;
+int sample_groups(int B, int V);
 hipError_t launch_sample(const SampleArgs& a, hipStream_t st);
 
 // int8 weights: per-row symmetric codes (byte = code + 128) and fp32 scales of W [rows][K]

@@ -1,10 +1,12 @@
 """rwkv7_sample (penalised temperature / top-k / top-p sampling) through the
 C ABI against the oracle's sampler on the same logits and uniforms: ids and
 the updated occurrence rows bit for bit (every decision is integer
-arithmetic on fp64 fixed-point weights, the penalties separately rounded
-fp32 ops).  Peaky and nearly flat logits (tens of thousands of tokens inside
-the nucleus), penalties, a forbidden mask, the greedy special case against
-rwkv7_greedy, the all-forbidden error and the host-side checks."""
+arithmetic on fixed-point weights from a fixed sequence of fp64 operations,
+the penalties separately rounded fp32 ops).  Peaky and nearly flat logits
+(tens of thousands of tokens inside the nucleus), a whole row inside one
+top-level bin, every split of a row over workgroups, penalties (with ties
+that a fused multiply-add would break), a forbidden mask, the greedy special
+case against rwkv7_greedy, the all-forbidden error and the host-side checks."""
 import numpy as np
 import pytest
 import torch
@@ -75,6 +77,101 @@ def test_sample_many_uniforms_flat_row(R):
     assert err == 0
     assert ids.tolist() == o_ids.tolist()
     assert len(set(ids.tolist())) > 32
+
+
+@pytest.mark.parametrize("B,V", [(1, 1000), (1, 4097), (3, 65535), (37, 65536), (300, 4097)])
+def test_sample_chunking(R, B, V):
+    """Row counts and vocabulary sizes that give every split of a row over
+    workgroups (64 down to 1), ragged chunks, and rows whose maximum is the
+    last token."""
+    rng = np.random.default_rng(B * 100003 + V)
+    lg = (rng.normal(size=(B, V)) * 2.0).astype(np.float32)
+    lg[::3, V - 1] = 9.0
+    occ = np.zeros((B, V), np.float32)
+    m = rng.random((B, V)) < 0.05
+    occ[m] = rng.integers(1, 4, m.sum()).astype(np.float32)
+    T = rng.choice([0.0, 0.8, 1.0, 1.5], B)
+    p = rng.choice([0.1, 0.3, 0.95, 1.0], B)
+    k = rng.choice([0, 0, 1, 40], B)
+    args = (lg, occ, np.full(B, 0.3), np.full(B, 0.7), np.full(B, 0.99), T, p, k,
+            rng.random(V) < 0.02, rng.random(B).astype(np.float32))
+    ids, occ_g, err = run(R, *args)
+    o_ids, o_occ, o_err = O.sample_penalized(*args)
+    assert err == 0 and not o_err.any()
+    assert ids.tolist() == o_ids.tolist()
+    assert np.array_equal(occ_g, o_occ)
+
+
+@pytest.mark.parametrize("kind", ["one_bin", "all_equal"])
+def test_sample_crowded_top_bin(R, kind):
+    """Every token in one top-level bin (more than the 4096 the selection
+    gathers into LDS): z in [0.5, 0.5625), or all logits equal so that only
+    the index orders them."""
+    V, B = 65536, 8
+    rng = np.random.default_rng(21)
+    row = (0.5 + rng.uniform(0, 0.06, V)).astype(np.float32) if kind == "one_bin" else np.zeros(V, np.float32)
+    lg = np.tile(row, (B, 1))
+    u = ((np.arange(B) + rng.random(B)) / B).astype(np.float32)
+    args = (lg, np.zeros((B, V), np.float32), np.zeros(B), np.zeros(B), np.ones(B), np.ones(B),
+            np.array([0.3, 1.0, 0.05, 0.5, 0.9, 1.0, 0.3, 0.7]), np.array([0, 0, 0, 100, 0, 5000, 9000, 0]),
+            None, u)
+    ids, occ, err = run(R, *args)
+    o_ids, o_occ, _ = O.sample_penalized(*args)
+    assert err == 0
+    assert ids.tolist() == o_ids.tolist()
+    assert np.array_equal(occ, o_occ)
+
+
+def _penalty_cases(n, seed):
+    """float32 (frequency, occurrence, presence) with frequency * occurrence +
+    presence rounded once (an FMA) different from the product rounded and then
+    the sum rounded (more than 0.6 ulp between the exact value and the latter)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        f, o, p = rng.uniform(0.1, 2.0, 3).astype(np.float32)
+        two = np.float32(np.float32(f * o) + p)
+        exact = Fraction(float(f)) * Fraction(float(o)) + Fraction(float(p))
+        if abs(exact - Fraction(float(two))) > Fraction(float(np.spacing(two))) * Fraction(6, 10):
+            out.append((f, o, p, two))
+    return out
+
+
+def test_penalty_rounded_per_operation(R):
+    """The penalty l - (frequency * occ + presence) takes three separately
+    rounded fp32 operations in both selections.  Each case is a tie: row A
+    penalises token 0 (logit 0) against token 1 whose logit is the separately
+    rounded penalised value; row B swaps them.  The lower index wins a tie, so
+    the pick is 0 in both rows; a fused multiply-add moves token 0 (row A) or
+    token 1 (row B) by an ulp and picks 1 in one of them."""
+    cases = _penalty_cases(32, 3)
+    V, B = 256, 2 * len(cases)
+    lg = np.full((B, V), -50.0, np.float32)
+    occ = np.zeros((B, V), np.float32)
+    pres, freq = np.zeros(B, np.float32), np.zeros(B, np.float32)
+    for i, (f, o, p, two) in enumerate(cases):
+        a, b = 2 * i, 2 * i + 1
+        lg[a, 0], occ[a, 0], lg[a, 1] = 0.0, o, -two
+        lg[b, 0], lg[b, 1], occ[b, 1] = -two, 0.0, o
+        pres[a] = pres[b] = p
+        freq[a] = freq[b] = f
+    dec = np.full(B, 0.75, np.float32)
+    for T, k in ((0.0, 0), (1.0, 1)):
+        args = (lg, occ, pres, freq, dec, np.full(B, T), np.ones(B), np.full(B, k), None, np.full(B, 0.5))
+        o_ids, o_occ, _ = O.sample_penalized(*args)
+        assert (o_ids == 0).all()
+        ids, occ_g, err = run(R, *args)
+        assert err == 0 and ids.tolist() == o_ids.tolist(), T
+        assert np.array_equal(occ_g, o_occ)
+    dev = "cuda"
+    f = lambda x: torch.tensor(np.asarray(x, np.float32), device=dev)
+    g_occ, g_ids = f(occ), torch.zeros(B, dtype=torch.int32, device=dev)
+    ws = torch.zeros(R.rwkv7_greedy_workspace_bytes(B, V), dtype=torch.uint8, device=dev)
+    R.rwkv7_greedy(f(lg), g_occ, B, torch.arange(B, dtype=torch.int32, device=dev), f(pres), f(freq), f(dec),
+                   g_ids, ws)
+    assert g_ids.cpu().tolist() == [0] * B
+    assert np.array_equal(g_occ.cpu().numpy(), o_occ)
 
 
 def test_greedy_special_case_and_determinism(R):

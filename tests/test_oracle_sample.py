@@ -114,3 +114,74 @@ def test_uniform_is_clamped_and_occ_updated():
     ids, occ, _ = O.sample_penalized(lg[None], np.array([[2.0, 0.0, 1.0]], np.float32), [0.0], [0.0],
                                      [0.5], [1.0], [1.0], [0], None, [0.0])
     assert ids[0] == 2 and occ[0].tolist() == [1.0, 0.0, 1.5]
+
+
+def _exp_exact(t):
+    """exp(t) to 40 digits (decimal), rounded to float64 (a correctly rounded exp)."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 40
+    return float(Decimal(float(t)).exp())
+
+
+def _exp_points():
+    rng = np.random.default_rng(11)
+    ln2 = np.log(2.0)
+    special = [0.0, -0.0, -1e-300, -2.0 ** -60, -ln2 / 2, -ln2, -21.487, -21.5, -22.0]
+    special += [-k * ln2 for k in range(1, 32)] + [-(k + 0.5) * ln2 for k in range(31)]
+    return np.concatenate([special, -rng.uniform(0, 22, 3000), -rng.uniform(0, 1e-3, 200)])
+
+
+def test_exp_fixed_is_exp_to_2_ulp():
+    """The weights' exp (a fixed float64 operation sequence, so that any
+    implementation of the same sequence matches bit for bit) against a
+    correctly rounded exp: within 2 ulp over [-22, 0]; exactly 1 at 0 and 0
+    below -22."""
+    t = _exp_points()
+    e = O.exp_fixed(t)
+    ref = np.array([_exp_exact(x) for x in t])
+    ulp = np.abs(e - ref) / np.spacing(ref)
+    assert ulp.max() <= 2.0, (t[np.argmax(ulp)], ulp.max())
+    assert O.exp_fixed(np.array([0.0]))[0] == 1.0 and O.exp_fixed(np.array([-0.0]))[0] == 1.0
+    assert (O.exp_fixed(np.array([-22.000001, -50.0, -1e30, -np.inf])) == 0.0).all()
+
+
+def test_sample_weights_fixed_point():
+    """floor(exp(z - m) * 2^31): 2^31 at the maximum, 2^(31-k) at z = m - k ln2
+    within one unit, 0 once exp(z - m) < 2^-31 (z - m < -21.4875...), and equal
+    to the floor of the correctly rounded value except where that value is
+    within 1e-6 of an integer."""
+    z = np.float32([3.0, 2.5, -18.4, -19.0])
+    assert O.sample_weights(z, np.float32(3.0))[0] == 2 ** 31
+    ln2 = np.log(2.0)
+    for k in range(1, 31):
+        zk = np.float32(3.0 - k * ln2)
+        w = int(O.sample_weights(np.array([zk]), np.float32(3.0))[0])
+        exact = _exp_exact(float(np.float64(zk) - 3.0)) * 2.0 ** 31
+        assert w == int(np.floor(exact)) and abs(w - 2.0 ** (31 - k)) <= 2.0 ** (31 - k) * 1e-6 + 1
+    assert O.sample_weights(np.float32([-21.48]), np.float32(0.0))[0] == 1
+    assert O.sample_weights(np.float32([-21.49]), np.float32(0.0))[0] == 0
+    rng = np.random.default_rng(5)
+    zs = rng.normal(0, 4, 4000).astype(np.float32)
+    m = zs.max()
+    w = O.sample_weights(zs, m)
+    exact = np.array([_exp_exact(float(np.float64(x) - np.float64(m))) for x in zs]) * 2.0 ** 31
+    fl = np.floor(exact)
+    near = np.abs(exact - np.round(exact)) < 1e-6
+    assert np.array_equal(w[~near], fl[~near].astype(np.int64))
+    assert near.sum() <= 2
+
+
+@pytest.mark.parametrize("slip", ["lo", "degree", "hi"])
+def test_exp_fixed_pins_catch_slips(monkeypatch, slip):
+    """A dropped low part of ln2, a polynomial two degrees short or ln2_hi
+    rounded to fewer bits each break the 2-ulp bound."""
+    if slip == "lo":
+        monkeypatch.setattr(O, "_EXP_LN2_LO", 0.0)
+    elif slip == "degree":
+        monkeypatch.setattr(O, "_EXP_TAYLOR", O._EXP_TAYLOR[:12] + [0.0, 0.0])
+    else:
+        monkeypatch.setattr(O, "_EXP_LN2_HI", float(np.float32(O._EXP_LN2_HI)))
+    t = _exp_points()
+    e = O.exp_fixed(t)
+    ref = np.array([_exp_exact(x) for x in t])
+    assert (np.abs(e - ref) / np.spacing(ref)).max() > 2.0
