@@ -323,6 +323,16 @@ const char* rwkv7_last_error(void);
                                  or C / 256 for C / 256 odd).  Each workgroup reads the whole row for the
                                  statistics and loads and writes its share of the columns;
                                  results do not depend on it */
+#define RWKV7_OPT_WKV_ADAPTERS 17  /* the adapters' second stage (decay, alpha, value gate, gate) on
+                                      the MFMA decode path: 0 (default) inside the WKV kernel, one
+                                      workgroup per head and block of rows, with the rows per wave
+                                      chosen for B and the ranks (1 up to 128 rows, 2 above; 4 where
+                                      the ranks sum past 512); 1 a separate MFMA projection whose
+                                      outputs the WKV kernel reads; 2, 3, 4 inside the WKV kernel
+                                      with 1, 2, 4 rows per wave.  Shapes without an instantiated
+                                      adapter step
+                                      (ranks other than 32/32/32/64, 64/64/32/320, 128/128/64/480)
+                                      always take 1 */
 int rwkv7_set_option(rwkv7_model* model, int32_t key, int64_t value);
 int rwkv7_get_option(const rwkv7_model* model, int32_t key, int64_t* value);
 

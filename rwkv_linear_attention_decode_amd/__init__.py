@@ -35,6 +35,7 @@ OPT_PREFILL_SCAN = 14
 OPT_INT8 = 15
 # workgroups per row of the batched decode LayerNorm kernel (0 = automatic)
 OPT_LN_SPLIT = 16
+OPT_WKV_ADAPTERS = 17
 
 
 def gemm_plan_code(tm, tn, ks, pipe=0, split=0):

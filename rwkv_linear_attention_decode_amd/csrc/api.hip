@@ -278,7 +278,8 @@ struct rwkv7_model {
   Dims d;
   Packed pk;
   int64_t opt_graph = 1, opt_gemv_max = 2, opt_sparse_max = 4, opt_timing = 0, opt_chunk = 2048,
-          opt_fuse_ln = 1, opt_fuse_value = 1, opt_prefill_scan = 0, opt_int8 = 0, opt_ln_split = 0;
+          opt_fuse_ln = 1, opt_fuse_value = 1, opt_prefill_scan = 0, opt_int8 = 0, opt_ln_split = 0,
+          opt_wkv_ad = 0;
   Q8 q8{};
   bool has_q8 = false;
   // tile plan per MFMA projection (RWKV7_OPT_GEMM_PLAN_* order), 0 = built-in
@@ -484,6 +485,25 @@ int ln_blocks(const rwkv7_model* m, int B) {
   return std::max(1, std::min(n, units));
 }
 
+// Rows per wave of the many-row WKV kernel that computes the adapters' second
+// stage itself (0: a separate MFMA projection computes them).  Default, from
+// whole graph-replayed steps against the separate projection: where the
+// adapter operands leave registers for the first row's state (ranks summing
+// to <= 512, e.g. 2.9B), one row per wave up to 128 rows and two above
+// (B 8 to 256: 1.8-6.1 % faster); otherwise (7.2B) four, which spreads the
+// adapter step over more rows (B 64 and 256: 2.3 and 1.8 % faster).
+int wkv_ad_rows_per_wave(const rwkv7_model* m, int B) {
+  switch (m->opt_wkv_ad) {
+    case 1: return 0;
+    case 2: return 1;
+    case 3: return 2;
+    case 4: return 4;
+    default:
+      if (m->d.Dw + m->d.Da + m->d.Dv + m->d.Dg > 512) return 4;
+      return B <= 128 ? 1 : 2;
+  }
+}
+
 // mixing vector (index into the six time-mix coefficient rows r,w,k,v,a,g)
 // read by each block of the fused input projection
 constexpr int kInMix[7] = {0, 2, 3, 1, 4, 3, 5};
@@ -553,11 +573,17 @@ int enqueue_decode(rwkv7_model* m, float* pool, int64_t n_slots, int B, const in
     WkvArgs wa = wkv_args(m, l, pool, n_slots, w, B, f16);
     wa.u_att = path.fused ? w.u_att : nullptr;
     if (!path.gemv) {
-      // many rows: the adapter outputs as one MFMA projection, WKV reads them
-      ProjArgs pl;
-      lora_args(d, q, w, B, pl);
-      RUN(RWKV7_K_PROJ_IN, "adapters", proj(false, pl, 4 * C, w, st, m->opt_plan[1]));
-      wa.lo = w.lo;
+      const int rpw = wkv_ad_rows_per_wave(m, B);
+      if (rpw && wkv_chunk_adapters_ok(wa)) {
+        // many rows, the adapters' second stage inside the WKV kernel
+        wa.ad_rpw = rpw;
+      } else {
+        // many rows: the adapter outputs as one MFMA projection, WKV reads them
+        ProjArgs pl;
+        lora_args(d, q, w, B, pl);
+        RUN(RWKV7_K_PROJ_IN, "adapters", proj(false, pl, 4 * C, w, st, m->opt_plan[1]));
+        wa.lo = w.lo;
+      }
     }
     RUN(RWKV7_K_WKV, "wkv", launch_wkv_decode(wa, st));
 
@@ -1398,6 +1424,9 @@ int rwkv7_set_option(rwkv7_model* m, int32_t key, int64_t value) {
     case RWKV7_OPT_LN_SPLIT:
       if (value < 0 || value > 16) return fail(RWKV7_EINVAL, "LN_SPLIT must be in [0, 16]");
       m->opt_ln_split = value; break;
+    case RWKV7_OPT_WKV_ADAPTERS:
+      if (value < 0 || value > 4) return fail(RWKV7_EINVAL, "WKV_ADAPTERS must be in [0, 4]");
+      m->opt_wkv_ad = value; break;
     case RWKV7_OPT_GEMM_PLAN_PROJ_IN:
     case RWKV7_OPT_GEMM_PLAN_ADAPTERS:
     case RWKV7_OPT_GEMM_PLAN_PROJ_OUT:
@@ -1416,7 +1445,7 @@ int rwkv7_set_option(rwkv7_model* m, int32_t key, int64_t value) {
   }
   // cached graphs bake in the kernel path: drop them when it may change
   if (key == RWKV7_OPT_GEMV_MAX_B || key == RWKV7_OPT_SPARSE_MAX_B || key == RWKV7_OPT_FUSE_LN ||
-      key == RWKV7_OPT_FUSE_VALUE || key == RWKV7_OPT_INT8 || key == RWKV7_OPT_LN_SPLIT || (key >= RWKV7_OPT_GEMM_PLAN_PROJ_IN && key <= RWKV7_OPT_GEMM_PLAN_HEAD))
+      key == RWKV7_OPT_FUSE_VALUE || key == RWKV7_OPT_INT8 || key == RWKV7_OPT_LN_SPLIT || key == RWKV7_OPT_WKV_ADAPTERS || (key >= RWKV7_OPT_GEMM_PLAN_PROJ_IN && key <= RWKV7_OPT_GEMM_PLAN_HEAD))
     drop_graphs(m);
   return RWKV7_OK;
 }
@@ -1434,6 +1463,7 @@ int rwkv7_get_option(const rwkv7_model* m, int32_t key, int64_t* value) {
     case RWKV7_OPT_PREFILL_SCAN: *value = m->opt_prefill_scan; break;
     case RWKV7_OPT_INT8: *value = m->opt_int8; break;
     case RWKV7_OPT_LN_SPLIT: *value = m->opt_ln_split; break;
+    case RWKV7_OPT_WKV_ADAPTERS: *value = m->opt_wkv_ad; break;
     case RWKV7_OPT_GEMM_PLAN_PROJ_IN:
     case RWKV7_OPT_GEMM_PLAN_ADAPTERS:
     case RWKV7_OPT_GEMM_PLAN_PROJ_OUT:

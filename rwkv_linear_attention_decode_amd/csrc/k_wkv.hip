@@ -268,6 +268,22 @@ __global__ __launch_bounds__(256) void k_wkv_decode(WkvArgs a) {
   if (commit) base[h * 64 + (t - 64)] = u_new;
 }
 
+// Adapter outputs of 16 tokens (or batch rows) x 16 channels on the fp16
+// matrix cores: D = lin_seg (16 x D) W_seg^T (D x 16), 32 ranks per step;
+// lane l supplies lin row l % 16 and weight row l % 16, ranks 8 (l / 16) ..
+// +7 of the step, and holds D[4 (l / 16) + i][l % 16] in component i.
+template <int D>
+RW_DEV floatx4 chunk_adapter(const half_t* lin_row, const half_t* w_row) {
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k0 = 0; k0 < D; k0 += 32) {
+    const half8 x = __builtin_bit_cast(half8, ld16(lin_row + k0));
+    const half8 y = __builtin_bit_cast(half8, ld16(w_row + k0));
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(x, y, acc, 0, 0, 0);
+  }
+  return acc;
+}
+
 // Many rows with precomputed adapter outputs: one wave per (row, head), four
 // per workgroup.  Lane l owns channel l of the head for the per-channel
 // vectors and float4 number 64 q + l (q = 0..15) of the state: value rows
@@ -370,6 +386,184 @@ __global__ __launch_bounds__(64 * NW) void k_wkv_decode_rows(WkvArgs a) {
   }
 }
 
+// Many rows with the adapters' second stage computed here instead of by a
+// separate MFMA projection: one workgroup per (head, block of 4 RPW rows).
+// Wave w first takes channels 16 w .. 16 w + 15 of all four adapters for the
+// block's rows on the fp16 matrix cores (as the chunked prefill does for 16
+// tokens; the 16-row tile's rows past the block are padding), through LDS to
+// every wave; then rows w RPW .. w RPW + RPW - 1 one after another, each as
+// k_wkv_decode_rows does for one (row, head).  The ranks are template
+// arguments so every load of the adapter step issues at once.
+// sum over N 32-rank steps of operands already in registers
+template <int N>
+RW_DEV floatx4 ad_prod(const u32x4 (&x)[N], const u32x4 (&y)[N]) {
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < N; ++k)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, x[k]), __builtin_bit_cast(half8, y[k]), acc,
+                                                0, 0, 0);
+  return acc;
+}
+
+template <int DW, int DA, int DV, int DG, int RPW>
+__global__ __launch_bounds__(256) void k_wkv_decode_ad(WkvArgs a) {
+  constexpr int RB = 4 * RPW;
+  __shared__ __attribute__((aligned(16))) float ad[4][16][64];   // decay | alpha | value gate | gate
+  __shared__ __attribute__((aligned(16))) WaveVecs wv[4];
+  const int H = a.H, C = a.C;
+  const int h = blockIdx.x % H, b0 = (blockIdx.x / H) * RB;
+  // wave-uniform as far as the compiler knows too: slot lookups go to scalar loads
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  auto state_ptr = [&](int rl) -> float* {
+    const int b = b0 + rl;
+    const int slot = b < a.B ? a.slots[b] : -1;
+    return slot >= 0 && slot < a.n_slots
+               ? a.pool + (long)slot * a.slot_stride + a.layer_off + 2L * C + (long)h * 4096 + 4 * lane
+               : nullptr;
+  };
+  // Every adapter operand of the wave is loaded at once; then, when the
+  // registers allow, the state of the wave's first row, which does not
+  // depend on the adapters and so flies during them.  Loads complete in
+  // order, so the adapter products wait for their own operands only.
+  constexpr int NW_ = DW / 32, NA = DA / 32, NV = DV / 32, NG = DG / 32;
+  constexpr bool EARLY = NW_ + NA + NV + NG <= 16;
+  const int r16 = lane & 15, k8 = 8 * (lane >> 4);
+  const int ch = h * 64 + 16 * wave + r16;   // weight row of this lane
+  float* S = EARLY ? state_ptr(wave * RPW) : nullptr;
+  const int cc = h * 64 + lane;
+  // per-row vectors r, k, v and the value residual's v_first (row clamped)
+  auto load_row = [&](int rl, float& r, float& k, float& v, float& vf) {
+    const int bc = min(b0 + rl, a.B - 1);
+    const long rb = (long)bc * 3 * C + cc;
+    r = a.rkv[rb];
+    k = a.rkv[rb + C];
+    v = a.rkv[rb + 2 * C];
+    vf = a.layer > 0 ? a.vfirst[(long)bc * C + cc] : 0.f;
+  };
+  float r0, k0, v0r, vf0;
+  load_row(wave * RPW, r0, k0, v0r, vf0);
+  const float k_k = a.k_k[cc], k_a = a.k_a[cc], r_k = a.r_k[cc];
+  const float gw = a.lnx_w[cc], gb = a.lnx_b[cc];
+  u32x4 xw[NW_], yw[NW_], xa[NA], ya[NA], xv[NV], yv[NV], xg[NG], yg[NG];
+  {
+    const half_t* lin = reinterpret_cast<const half_t*>(a.lin) + (long)min(b0 + r16, a.B - 1) * a.Lin + k8;
+#pragma unroll
+    for (int k = 0; k < NW_; ++k) { xw[k] = ld16(lin + 32 * k); yw[k] = ld16(a.w2 + (long)ch * DW + k8 + 32 * k); }
+#pragma unroll
+    for (int k = 0; k < NA; ++k) { xa[k] = ld16(lin + a.off_a + 32 * k); ya[k] = ld16(a.a2 + (long)ch * DA + k8 + 32 * k); }
+#pragma unroll
+    for (int k = 0; k < NV; ++k) { xv[k] = ld16(lin + a.off_v + 32 * k); yv[k] = ld16(a.v2 + (long)ch * DV + k8 + 32 * k); }
+#pragma unroll
+    for (int k = 0; k < NG; ++k) { xg[k] = ld16(lin + a.off_g + 32 * k); yg[k] = ld16(a.g2 + (long)ch * DG + k8 + 32 * k); }
+  }
+  const float w0 = a.w0[ch], a0 = a.a0[ch], v0 = a.v0[ch];
+  __builtin_amdgcn_sched_barrier(0);
+  // a row without a state (no slot, or past B) reads the pool's first floats
+  // and zeroes them: unconditional loads keep the waits exact
+  auto load_state = [&](floatx4 (&st)[16], const float* p) {
+    const float* src = p ? p : a.pool + 4 * lane;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) st[q] = ldf4_nt(src + 256 * q);
+  };
+  floatx4 s[16];
+  if constexpr (EARLY) load_state(s, S);
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    const floatx4 zw = ad_prod<NW_>(xw, yw), za = ad_prod<NA>(xa, ya), zv = ad_prod<NV>(xv, yv),
+                  zg = ad_prod<NG>(xg, yg);
+    // lane holds channel 16 w + r16 of rows 4 (lane / 16) + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = 4 * (lane >> 4) + i, col = 16 * wave + r16;
+      const float sw = 1.0f / (1.0f + expf(-(zw[i] + w0)));
+      ad[0][rr][col] = expf(-0.60653065971263342f * sw);     // decay
+      ad[1][rr][col] = 1.0f / (1.0f + expf(-(za[i] + a0)));  // alpha
+      ad[2][rr][col] = 1.0f / (1.0f + expf(-(zv[i] + v0)));  // value gate
+      ad[3][rr][col] = zg[i];                                // gate
+    }
+  }
+  __syncthreads();
+  WaveVecs& w = wv[wave];
+  for (int j = 0; j < RPW; ++j) {
+    const int rl = wave * RPW + j;
+    const int b = b0 + rl;
+    const bool live = b < a.B;
+    float r = r0, k = k0, v = v0r, vf = vf0;
+    if (j > 0) load_row(rl, r, k, v, vf);
+    if (j > 0 || !EARLY) {
+      S = state_ptr(rl);
+      load_state(s, S);
+    }
+    const float dk = ad[0][rl][lane], al = ad[1][rl][lane], vg = ad[2][rl][lane], g = ad[3][rl][lane];
+
+    const float kap = k * k_k;
+    const float nrm = sqrtf(wave_sum(kap * kap));
+    const float kh = kap / fmaxf(nrm, 1e-12f);
+    const float kt = k * (1.0f + (al - 1.0f) * k_a);
+    if (a.layer == 0) {
+      if (live) a.vfirst[(long)b * C + cc] = v;
+    } else {
+      v = v + (vf - v) * vg;
+    }
+    const float bonus = wave_sum(r * kt * r_k);
+    w.a[lane] = -kh;
+    w.bb[lane] = kh * al;
+    w.kt[lane] = kt;
+    w.d[lane] = dk;
+    w.r[lane] = r;
+    w.v[lane] = v;
+    __syncthreads();
+
+    const int j0 = 4 * (lane & 15);
+    const floatx4 av = *reinterpret_cast<const floatx4*>(&w.a[j0]);
+    const floatx4 bv = *reinterpret_cast<const floatx4*>(&w.bb[j0]);
+    const floatx4 kv = *reinterpret_cast<const floatx4*>(&w.kt[j0]);
+    const floatx4 dv = *reinterpret_cast<const floatx4*>(&w.d[j0]);
+    const floatx4 rv = *reinterpret_cast<const floatx4*>(&w.r[j0]);
+    if (!S) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) s[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    float y[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const float sa = sum16(s[q][0] * av[0] + s[q][1] * av[1] + s[q][2] * av[2] + s[q][3] * av[3]);
+      const float vi = w.v[4 * q + (lane >> 4)];
+      float yy = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float sn = s[q][c] * dv[c] + sa * bv[c] + vi * kv[c];
+        s[q][c] = sn;
+        yy = fmaf(sn, rv[c], yy);
+      }
+      y[q] = yy;
+    }
+    if (S) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) stf4_nt(S + 256 * q, s[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const float yy = sum16(y[q]);
+      if ((lane & 15) == 0) w.y[4 * q + (lane >> 4)] = yy;
+    }
+    __syncthreads();
+    // GroupNorm over the head's readouts, bonus, gate
+    const float yl = w.y[lane];
+    const float mean = wave_sum(yl) * (1.0f / 64.0f);
+    const float dlt = yl - mean;
+    const float var = wave_sum(dlt * dlt) * (1.0f / 64.0f);
+    const float o = (dlt / sqrtf(var + 64e-5f) * gw + gb + bonus * v) * g;
+    if (live) {
+      const long off = (long)b * C + cc;
+      if (a.yout_f16)
+        ((half_t*)a.yout)[off] = (half_t)o;
+      else
+        ((float*)a.yout)[off] = o;
+    }
+  }
+}
+
 // chunks of 8 per thread: (Dw + Da + Dv + Dg) / 32
 #define WKV_NCHK_CASES(X) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) \
   X(13) X(14) X(15) X(16) X(17) X(18) X(19) X(20) X(21) X(22) X(23) X(24) X(25) X(26)   \
@@ -422,8 +616,37 @@ int wkv_rows_waves(int items) {
   return (w5 + 255) / 256 * 5 < (w4 + 255) / 256 * 4 ? 5 : 4;
 }
 
+// Adapter ranks (Dw, Da, Dv, Dg) with instantiated matrix-core adapter
+// steps (the tiny, 2.9B and 7.2B shapes), and whether a launch can use them:
+// fp16 first-stage activations at offsets that keep 16-byte loads aligned.
+#define CHUNK_AD_CASES(X) X(32, 32, 32, 64) X(64, 64, 32, 320) X(128, 128, 64, 480)
+bool wkv_chunk_adapters_ok(const WkvArgs& a) {
+  if (a.off_a % 8 || a.off_v % 8 || a.off_g % 8 || a.Lin % 8) return false;
+#define X(w, al, v, g) if (a.Dw == w && a.Da == al && a.Dv == v && a.Dg == g) return true;
+  CHUNK_AD_CASES(X)
+#undef X
+  return false;
+}
+
 hipError_t launch_wkv_decode(const WkvArgs& a, hipStream_t st) {
   if (a.Lin > LIN_MAX) return hipErrorInvalidValue;
+  if (a.ad_rpw && !a.lo && !a.u_att) {
+    // many rows, adapters in the kernel: ad_rpw rows per wave
+    if (!wkv_chunk_adapters_ok(a) || (a.ad_rpw != 1 && a.ad_rpw != 2 && a.ad_rpw != 4))
+      return hipErrorInvalidValue;
+    const int rb = 4 * a.ad_rpw;
+    const dim3 grid((unsigned)(((a.B + rb - 1) / rb) * a.H));
+#define X(w, al, v, g)                                                                              \
+  if (a.Dw == w && a.Da == al && a.Dv == v && a.Dg == g) {                                          \
+    if (a.ad_rpw == 1) hipLaunchKernelGGL((k_wkv_decode_ad<w, al, v, g, 1>), grid, dim3(256), 0, st, a); \
+    else if (a.ad_rpw == 2) hipLaunchKernelGGL((k_wkv_decode_ad<w, al, v, g, 2>), grid, dim3(256), 0, st, a); \
+    else hipLaunchKernelGGL((k_wkv_decode_ad<w, al, v, g, 4>), grid, dim3(256), 0, st, a);         \
+    return hipGetLastError();                                                                       \
+  }
+    CHUNK_AD_CASES(X)
+#undef X
+    return hipErrorInvalidValue;
+  }
   if (a.lo && !a.u_att) {
     const int items = a.B * a.H;
     if (wkv_rows_waves(items) == 5)
@@ -641,22 +864,6 @@ struct ChunkPrepLds {
   float m[4][CH][CH + 1];   // C, E, F, H
   float g[CH][CH + 1];
 };
-
-// Adapter outputs of 16 tokens x 16 channels on the fp16 matrix cores: D =
-// lin_seg (16 x D) W_seg^T (D x 16), 32 ranks per step; lane l supplies lin
-// row l % 16 and weight row l % 16, ranks 8 (l / 16) .. +7 of the step, and
-// holds D[4 (l / 16) + i][l % 16] in component i.
-template <int D>
-RW_DEV floatx4 chunk_adapter(const half_t* lin_row, const half_t* w_row) {
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int k0 = 0; k0 < D; k0 += 32) {
-    const half8 x = __builtin_bit_cast(half8, ld16(lin_row + k0));
-    const half8 y = __builtin_bit_cast(half8, ld16(w_row + k0));
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(x, y, acc, 0, 0, 0);
-  }
-  return acc;
-}
 
 // Grid: n_chunks * H workgroups of 256 threads; thread (t, j4) = (tid / 16,
 // 4 (tid % 16)) owns token t of the chunk and key columns j4..j4+3.  The
@@ -1022,14 +1229,6 @@ hipError_t launch_wkv_scan(const WkvArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 // adapter ranks (w, a, v, g) with an in-kernel second stage: the tiny, 2.9B and 7.2B shapes
-#define CHUNK_AD_CASES(X) X(32, 32, 32, 64) X(64, 64, 32, 320) X(128, 128, 64, 480)
-bool wkv_chunk_adapters_ok(const WkvArgs& a) {
-  if (a.off_a % 8 || a.off_v % 8 || a.off_g % 8 || a.Lin % 8) return false;
-#define X(w, al, v, g) if (a.Dw == w && a.Da == al && a.Dv == v && a.Dg == g) return true;
-  CHUNK_AD_CASES(X)
-#undef X
-  return false;
-}
 hipError_t launch_wkv_chunk_prep(const WkvArgs& a, hipStream_t st) {
   if (!a.q_rec || a.B < 1) return hipErrorInvalidValue;
   const dim3 grid(chunk_count(a.B) * a.H);

@@ -255,6 +255,8 @@ struct WkvArgs {
   const float* lnx_b;
   float* vfirst;           // [B][C]
   const float* lo;         // [B][4C] precomputed decay | alpha | value gate | gate, or nullptr
+  int ad_rpw;              // many-row decode with lo null: the WKV kernel computes the adapters'
+                           // second stage from fp16 lin, this many rows per wave (1, 2, 4); 0 = not
   const float* u_att;      // decode: [B][C] new time-mix shift to commit, or nullptr
   void* yout;              // [B][C] gated, normalised readout (fp32 or fp16)
   int yout_f16;

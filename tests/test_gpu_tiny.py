@@ -157,6 +157,53 @@ def test_batched_step_paths(model, W, R, B, gemv, sparse, fuse, fval):
         model.set_option(R.OPT_FUSE_VALUE, 1)
 
 
+def test_wkv_adapter_paths(weights, W, R):
+    """The adapters' second stage on the MFMA decode path, computed by the WKV
+    kernel (1, 2 or 4 rows per wave: blocks of 4, 8 or 16 rows of a head, the
+    16-row matrix-core tile padded) or by a separate MFMA projection: every
+    variant against the oracle, and the in-kernel ones against the separate
+    projection (the same fp16 products, summed in another order).  Row
+    counts 3, 8 and 21 give partial, whole and ragged blocks; the slots are
+    a permutation so rows and slots differ."""
+    n = 24
+    m = R.Model.from_numpy(S, weights, n_slots=n, max_B=n, max_T=16)
+    try:
+        for B in (3, 8, 21):
+            slots = [(7 * i + 5) % n for i in range(B)]
+            prompts = [prompt(300 + i, 2 + i % 5) for i in range(B)]
+            feeds = [[int(t) for t in prompt(400 + st, B)] for st in range(3)]
+            refs = []
+            states = [O.State(S) for _ in range(B)]
+            for st_, pr in zip(states, prompts):
+                O.seq(W, st_, pr, want_logits=False)
+            for toks in feeds:
+                refs.append(O.step(W, states, toks))
+            runs = {}
+            for opt in (1, 2, 3, 4, 0):
+                m.set_option(R.OPT_WKV_ADAPTERS, opt)
+                m.reset(dev(slots))
+                for s_, pr in zip(slots, prompts):
+                    m.prefill(s_, dev(pr))
+                out = torch.empty(3, B, S.vocab, device="cuda")
+                for t, toks in enumerate(feeds):
+                    m.decode_step(dev(slots), dev(toks), out[t])
+                got = out.cpu().numpy()
+                runs[opt] = (got, np.stack([gstate(m, s_) for s_ in slots]))
+                assert m.poll_error() == 0
+                for t in range(3):
+                    for b in range(B):
+                        assert rel(got[t, b], refs[t][b]) <= TOL, (B, opt, t, b)
+                for b in range(B):
+                    assert rel(runs[opt][1][b], states[b].flat()) <= TOL, (B, opt, b)
+            for opt in (2, 3, 4, 0):
+                assert rel(runs[opt][0], runs[1][0]) <= 1e-4, (B, opt)
+                assert rel(runs[opt][1], runs[1][1]) <= 1e-4, (B, opt)
+        with pytest.raises(R.RWKV7Error):
+            m.set_option(R.OPT_WKV_ADAPTERS, 5)
+    finally:
+        m.close()
+
+
 GEMM_PLAN_KEYS = (8, 9, 10, 11, 12, 13)   # OPT_GEMM_PLAN_PROJ_IN .. _HEAD
 
 
