@@ -299,7 +299,8 @@ const char* rwkv7_last_error(void);
    plan for the shape.  Otherwise the decimal digits "T N KKK P S" of the value give the
    workgroup tile (32 T rows x 32 N columns, T in {1, 2, 4}, N in {2, 4}; also T = 2, N = 5
    with loop 3, and T in {2, 4}, N = 8 with loop 4, both with 64-deep stages, and T = N = 8
-   with loop 4 and 32-deep stages), the K stage depth
+   or T = 8, N = 10 (written as the digits 9 0: 256 x 320 tiles) with loop 4 and 32-deep
+   stages), the K stage depth
    KKK (32, 64 or 128), the K loop P (0 plain, 1 pipelined LDS reads, 2 two stages of global
    loads in flight, 3 stages loaded straight into a three-deep LDS ring, 4 the same with
    eight waves (T, N in {2, 4}), 5 a deeper LDS ring of as many stages as fit about 144 KB

@@ -42,7 +42,8 @@ def gemm_plan_code(tm, tn, ks, pipe=0, split=0):
     """Value of an OPT_GEMM_PLAN_* option: tile 32*tm x 32*tn, stage depth ks,
     K loop `pipe` (0 plain, 1 pipelined LDS reads, 2 two stages of global loads in
     flight, 3 LDS-DMA ring, 4 the same with eight waves, 5 a deep LDS-DMA ring filling
-    about 144 KB of LDS, 6 the same in about 72 KB), K split (0 = automatic)."""
+    about 144 KB of LDS, 6 the same in about 72 KB), K split (0 = automatic).
+    tm = 8, tn = 10 (256 x 320 tiles) gives the digits 9 0, which the library reads so."""
     return ((tm * 10 + tn) * 1000 + ks) * 100 + pipe * 10 + split
 K_LN_MIX, K_PROJ_IN, K_WKV, K_PROJ_OUT, K_CMIX_KEY, K_CMIX_VALUE, K_HEAD, K_OTHER = range(8)
 K_NAMES = ("ln_mix", "proj_in", "wkv", "proj_out", "cmix_key", "cmix_value", "head", "other")

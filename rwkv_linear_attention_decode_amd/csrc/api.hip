@@ -364,8 +364,10 @@ Seg mkseg(int row0, int row1, int epi, const void* act, int ld_act, void* out, i
 struct PlanCode {
   int tm, tn, ks, pipe, split;
 };
+// "T N KKK P S"; the pair "9 0" (= 8 * 10 + 10) stands for T = 8, N = 10
 static PlanCode decode_plan(int64_t v) {
-  return {(int)(v / 1000000 % 10), (int)(v / 100000 % 10), (int)(v / 100 % 1000), (int)(v / 10 % 10),
+  const int tt = (int)(v / 100000 % 100);
+  return {tt == 90 ? 8 : tt / 10, tt == 90 ? 10 : tt % 10, (int)(v / 100 % 1000), (int)(v / 10 % 10),
           (int)(v % 10)};
 }
 

@@ -458,10 +458,13 @@ __global__ __launch_bounds__(64 * NW) void k_mm_dma(ProjArgs a) {
   constexpr int WC = NW / 2;               // wave columns
   constexpr int BN = 2 * TN / WC;          // 16 x 16 blocks per wave along N
   constexpr int SLOTS = (MT + NT) * CPR;   // 16-byte slots per stage
-  constexpr int NIW = SLOTS / (64 * NW);   // DMA instructions per wave and stage
+  // every wave issues the same whole number of DMA instructions per stage (so
+  // the wait counts are exact); lanes past the stage's slots fill padding
+  constexpr int NIW = (SLOTS + 64 * NW - 1) / (64 * NW);   // DMA instructions per wave and stage
+  constexpr int SLOTS_PAD = NIW * 64 * NW;
   constexpr int ASL = MT * CPR;            // slots of the A rows
-  static_assert(SLOTS % (64 * NW) == 0 && (2 * TN) % WC == 0, "whole DMA instructions and blocks per wave");
-  __shared__ __attribute__((aligned(1024))) half_t L[3][SLOTS * 8];
+  static_assert((2 * TN) % WC == 0, "whole blocks per wave");
+  __shared__ __attribute__((aligned(1024))) half_t L[3][SLOTS_PAD * 8];
 
   const int n_tiles = a.tile0[a.nseg];
   const int total = n_tiles * a.m_tiles * a.split;
@@ -502,9 +505,11 @@ __global__ __launch_bounds__(64 * NW) void k_mm_dma(ProjArgs a) {
     if (S < ASL) {
       const int r = S / CPR, c = (S % CPR) ^ swz<CPR>(r);
       src[q] = A + (long)min(m0 + r, a.M - 1) * lda + c * 8;
-    } else {
+    } else if (S < SLOTS) {
       const int r = (S - ASL) / CPR, c = ((S - ASL) % CPR) ^ swz<CPR>(r);
       src[q] = Wb + (long)min(n0 + r, sg.row1 - 1) * K + c * 8;
+    } else {   // padding slot: any valid row chunk of A
+      src[q] = A + (long)min(m0, a.M - 1) * lda;
     }
   }
   const unsigned lds0 = (unsigned)(uintptr_t)&L[0][0];
@@ -512,7 +517,7 @@ __global__ __launch_bounds__(64 * NW) void k_mm_dma(ProjArgs a) {
 #pragma unroll
     for (int q = 0; q < NIW; ++q)
       dma16(src[q] + (long)stg * KS,
-            __builtin_amdgcn_readfirstlane(lds0 + slot * SLOTS * 16 + (q * NW + wave) * 1024));
+            __builtin_amdgcn_readfirstlane(lds0 + slot * SLOTS_PAD * 16 + (q * NW + wave) * 1024));
   };
   int aoff[KH][TM], boff[KH][BN];   // byte offsets of this lane's fragments in a stage
 #pragma unroll
@@ -901,6 +906,7 @@ static bool mm_cfg_ok(int tm, int tn, int ks, int pipe) {
   }
   if (pipe == 4) {   // eight waves: N blocks split over four wave columns
     if (tn == 8 && tm == 8) return ks == 32;   // 256 x 256 tiles: eight waves of 128 x 64, 96 KB of LDS
+    if (tn == 10) return tm == 8 && ks == 32;   // 256 x 320 tiles: eight waves of 128 x 80, 120 KB of LDS
     if (tn == 8)      // 256-wide tiles, 64-deep stages (three of them fill up to 144 KB of LDS)
       return (tm == 2 || tm == 4) && ks == 64;
     if (!((tm == 2 || tm == 4) && (tn == 2 || tn == 4))) return false;
@@ -992,6 +998,16 @@ static MmPlan mm_choose(const ProjArgs& a, int total_rows) {
     return N <= 8192 ? MmPlan{4, 2, 64, 4, 0} : MmPlan{2, 2, 64, 1, 0};
   }
   if (rank_k) return {2, 2, 32, 2, 0};
+  // above 1024 rows: 256 x 320 tiles where they make one round of 192 - 256
+  // workgroups (2.9B at 2048 rows: the key 256 tiles, the input projection
+  // 224; whole 2048-token prefills 24.09 -> 21.95 ms; at 1024 rows half the
+  // CUs would idle)
+  if (M > 1024 && K % 32 == 0) {
+    long t = 0;
+    for (int i = 0; i < a.nseg; ++i) t += (a.seg[i].row1 - a.seg[i].row0 + 319) / 320;
+    t *= (M + 255) / 256;
+    if (t >= 192 && t <= 256) return {8, 10, 32, 4, 1};
+  }
   if (K >= 4096) return N >= 10240 ? MmPlan{2, 4, 32, 1, 1} : MmPlan{4, 2, 64, 2, 0};
   // the key (one segment): 128 x 256 tiles, one K range (whole 512- and 2048-token
   // prefills 1.4 - 1.6 % faster than 64 x 64 / 128 x 128 tiles)
@@ -1018,7 +1034,7 @@ hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int 
   if (pipe >= 3)   // the DMA loops need whole stages: otherwise a register-staged loop
     for (int i = 0; i < a.nseg; ++i)
       if ((a.seg[i].W ? a.seg[i].K : a.K) % ks != 0) {
-        if (tn == 5 || tn == 8) tn = 4;   // 160- and 256-wide tiles exist for the DMA loops only
+        if (tn == 5 || tn == 8 || tn == 10) tn = 4;   // 160-, 256- and 320-wide tiles: DMA loops only
         if (tm == 8) tm = 4;
         pipe = mm_cfg_ok(tm, tn, ks, 2) ? 2 : 0;
       }
@@ -1036,6 +1052,7 @@ hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int 
     case 28: hipLaunchKernelGGL((k_mm_dma<2, 8, 64, 8>), grid, dim3(512), 0, st, a); break;   // loop 4
     case 48: hipLaunchKernelGGL((k_mm_dma<4, 8, 64, 8>), grid, dim3(512), 0, st, a); break;   // loop 4
     case 88: hipLaunchKernelGGL((k_mm_dma<8, 8, 32, 8>), grid, dim3(512), 0, st, a); break;   // loop 4
+    case 90: hipLaunchKernelGGL((k_mm_dma<8, 10, 32, 8>), grid, dim3(512), 0, st, a); break;  // 256 x 320
     default: mm_launch<4, 4>(ks, pipe, grid, st, a); break;
   }
   hipError_t e = hipGetLastError();
