@@ -915,6 +915,7 @@ static bool mm_cfg_ok(int tm, int tn, int ks, int pipe) {
   }
   if (pipe == 3) {
     if (tm == 2 && tn == 5) return ks == 64;   // 64 x 160 tiles (see mm_choose)
+    if (tm == 4 && tn == 1) return ks == 64 || ks == 128;   // 128 x 32 tiles (see mm_choose)
     if (!((tm == 1 || tm == 2 || tm == 4) && (tn == 2 || tn == 4))) return false;
     if (ks == 32) return tm >= 2;
     return (ks == 64 || ks == 128) && mm_dma_lds_bytes(tm, tn, ks) <= 98304;
@@ -961,6 +962,10 @@ static MmPlan mm_choose(const ProjArgs& a, int total_rows) {
     if (K >= 8192) {                                 // channel-mix value
       if (K >= 16384) return M > 64 && M <= 256 ? MmPlan{4, 4, 64, 4, 3} : MmPlan{4, 4, 64, 0, 6};
       if (M <= 64) return {2, 2, 128, 3, 6};
+      // 65 - 128 rows: 128 x 32 tiles in three K ranges, 240 workgroups each
+      // reading its weight columns once (2.9B: 128-token prefill 4.50 -> 4.40
+      // ms, B = 128 steps 4.80 -> 4.74 ms; slower at 256 rows)
+      if (M <= 128) return {4, 1, 128, 3, 3};
       if (M <= 256) return {4, 4, 64, 4, 6};
       // above 1024 rows: 256 x 256 tiles, three K ranges (2048-token prefill 0.5 % faster)
       return M <= 1024 ? MmPlan{2, 4, 64, 3, 3} : MmPlan{8, 8, 32, 4, 3};
@@ -1034,8 +1039,9 @@ hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int 
   if (pipe >= 3)   // the DMA loops need whole stages: otherwise a register-staged loop
     for (int i = 0; i < a.nseg; ++i)
       if ((a.seg[i].W ? a.seg[i].K : a.K) % ks != 0) {
-        if (tn == 5 || tn == 8 || tn == 10) tn = 4;   // 160-, 256- and 320-wide tiles: DMA loops only
+        if (tn == 1 || tn == 5 || tn == 8 || tn == 10) tn = tn == 1 ? 2 : 4;   // 32-, 160-, 256-, 320-wide: DMA only
         if (tm == 8) tm = 4;
+        if (!mm_cfg_ok(tm, tn, ks, 2) && !mm_cfg_ok(tm, tn, ks, 0)) ks = 64;   // register loops' LDS limits
         pipe = mm_cfg_ok(tm, tn, ks, 2) ? 2 : 0;
       }
   if (!mm_cfg_ok(tm, tn, ks, pipe)) return hipErrorInvalidValue;
@@ -1049,6 +1055,12 @@ hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int 
     case 24: mm_launch<2, 4>(ks, pipe, grid, st, a); break;
     case 42: mm_launch<4, 2>(ks, pipe, grid, st, a); break;
     case 25: mm_launch_dma<2, 5, 4>(ks, grid, st, a); break;   // loop 3, ks 64 only
+    case 41:   // loop 3: 128 x 32 tiles, four waves of 64 x 16
+      if (ks == 64)
+        hipLaunchKernelGGL((k_mm_dma<4, 1, 64, 4>), grid, dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((k_mm_dma<4, 1, 128, 4>), grid, dim3(256), 0, st, a);
+      break;
     case 28: hipLaunchKernelGGL((k_mm_dma<2, 8, 64, 8>), grid, dim3(512), 0, st, a); break;   // loop 4
     case 48: hipLaunchKernelGGL((k_mm_dma<4, 8, 64, 8>), grid, dim3(512), 0, st, a); break;   // loop 4
     case 88: hipLaunchKernelGGL((k_mm_dma<8, 8, 32, 8>), grid, dim3(512), 0, st, a); break;   // loop 4

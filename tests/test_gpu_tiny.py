@@ -215,7 +215,7 @@ GEMM_PLAN_KEYS = (8, 9, 10, 11, 12, 13)   # OPT_GEMM_PLAN_PROJ_IN .. _HEAD
     (4, 2, 64, 3, 1), (1, 4, 64, 3, 3), (2, 2, 128, 3, 0), (2, 5, 64, 3, 0), (2, 5, 64, 3, 2),
     (2, 2, 64, 4, 0), (4, 4, 64, 4, 0), (2, 4, 64, 4, 2), (4, 2, 64, 4, 1), (2, 2, 32, 4, 0),
     (4, 4, 32, 4, 3), (2, 2, 128, 4, 0), (4, 8, 64, 4, 0), (2, 8, 64, 4, 2), (8, 8, 32, 4, 3), (8, 8, 32, 4, 0),
-    (8, 10, 32, 4, 0), (8, 10, 32, 4, 2),
+    (8, 10, 32, 4, 0), (8, 10, 32, 4, 2), (4, 1, 64, 3, 0), (4, 1, 128, 3, 3),
     (4, 4, 32, 3, 2),
     (1, 2, 128, 5, 0), (2, 2, 64, 5, 0), (2, 2, 64, 5, 3), (2, 4, 64, 5, 0), (4, 4, 64, 5, 0),
     (4, 2, 64, 5, 2), (1, 4, 64, 6, 2), (1, 2, 128, 6, 0), (4, 2, 64, 6, 1), (2, 2, 64, 6, 2)])
@@ -277,7 +277,8 @@ def test_gemm_plan_option_validation(model, R):
                 R.gemm_plan_code(2, 5, 64, 5),
                 R.gemm_plan_code(4, 8, 128, 4), R.gemm_plan_code(1, 8, 64, 4), R.gemm_plan_code(8, 8, 64, 4),
                 R.gemm_plan_code(8, 8, 32, 3), R.gemm_plan_code(8, 4, 32, 4), R.gemm_plan_code(8, 10, 64, 4),
-                R.gemm_plan_code(8, 10, 32, 3), R.gemm_plan_code(9, 0, 64, 4), -5, 10 ** 8):
+                R.gemm_plan_code(8, 10, 32, 3), R.gemm_plan_code(9, 0, 64, 4), R.gemm_plan_code(4, 1, 32, 3),
+                R.gemm_plan_code(2, 1, 64, 3), R.gemm_plan_code(4, 1, 64, 4), -5, 10 ** 8):
         with pytest.raises(R.RWKV7Error):
             model.set_option(8, bad)
     model.set_option(8, 0)
