@@ -298,7 +298,7 @@ const char* rwkv7_last_error(void);
 /* Tile plan of one MFMA projection (B > GEMV_MAX_B and prefill); 0 (default) = the built-in
    plan for the shape.  Otherwise the decimal digits "T N KKK P S" of the value give the
    workgroup tile (32 T rows x 32 N columns, T in {1, 2, 4}, N in {2, 4}; also T = 4, N = 1
-   with loop 3 and 64- or 128-deep stages, T = 2, N = 5
+   with loop 3 and 64- or 128-deep stages, T in {2, 4}, N = 5
    with loop 3, and T in {2, 4}, N = 8 with loop 4, both with 64-deep stages, and T = N = 8
    or T = 8, N = 10 (written as the digits 9 0: 256 x 320 tiles) with loop 4 and 32-deep
    stages), the K stage depth

@@ -916,6 +916,7 @@ static bool mm_cfg_ok(int tm, int tn, int ks, int pipe) {
   if (pipe == 3) {
     if (tm == 2 && tn == 5) return ks == 64;   // 64 x 160 tiles (see mm_choose)
     if (tm == 4 && tn == 1) return ks == 64 || ks == 128;   // 128 x 32 tiles (see mm_choose)
+    if (tm == 4 && tn == 5) return ks == 64;   // 128 x 160 tiles, 108 KB of LDS (see mm_choose)
     if (!((tm == 1 || tm == 2 || tm == 4) && (tn == 2 || tn == 4))) return false;
     if (ks == 32) return tm >= 2;
     return (ks == 64 || ks == 128) && mm_dma_lds_bytes(tm, tn, ks) <= 98304;
@@ -968,7 +969,9 @@ static MmPlan mm_choose(const ProjArgs& a, int total_rows) {
       if (M <= 128) return {4, 1, 128, 3, 3};
       if (M <= 256) return {4, 4, 64, 4, 6};
       // above 1024 rows: 256 x 256 tiles, three K ranges (2048-token prefill 0.5 % faster)
-      return M <= 1024 ? MmPlan{2, 4, 64, 3, 3} : MmPlan{8, 8, 32, 4, 3};
+      // 257 - 1024 rows: 128 x 160 tiles in four K ranges (one round of 256
+      // workgroups at 512 rows; 512-token prefill 8.14 -> 7.84 ms)
+      return M <= 1024 ? MmPlan{4, 5, 64, 3, 4} : MmPlan{8, 8, 32, 4, 3};
     }
     if (M <= 64) return {2, 2, 128, 3, 6};
     return M <= 256 ? MmPlan{2, 2, 64, 4, 0} : MmPlan{2, 4, 64, 4, 0};
@@ -1014,9 +1017,11 @@ static MmPlan mm_choose(const ProjArgs& a, int total_rows) {
     if (t >= 192 && t <= 256) return {8, 10, 32, 4, 1};
   }
   if (K >= 4096) return N >= 10240 ? MmPlan{2, 4, 32, 1, 1} : MmPlan{4, 2, 64, 2, 0};
-  // the key (one segment): 128 x 256 tiles, one K range (whole 512- and 2048-token
-  // prefills 1.4 - 1.6 % faster than 64 x 64 / 128 x 128 tiles)
-  if (N >= 10240 && a.nseg == 1 && K % 64 == 0) return {4, 8, 64, 4, 1};
+  // the key (one segment), one K range: up to 1024 rows 128 x 160 tiles (2.9B at
+  // 512 rows: 256 of them; 512- and 1024-token prefills 2.2 and 1.7 % faster
+  // than 128 x 256 tiles), above that 128 x 256 tiles where 256 x 320 ones do
+  // not make one round
+  if (N >= 10240 && a.nseg == 1 && K % 64 == 0) return M <= 1024 ? MmPlan{4, 5, 64, 3, 1} : MmPlan{4, 8, 64, 4, 1};
   if (N >= 10240) return M <= 1024 ? MmPlan{2, 2, 64, 4, 0} : MmPlan{4, 4, 64, 4, 0};
   return {4, 2, 64, 4, 0};
 }
@@ -1055,6 +1060,7 @@ hipError_t launch_gemm_cfg(ProjArgs a, int total_rows, int64_t part_floats, int 
     case 24: mm_launch<2, 4>(ks, pipe, grid, st, a); break;
     case 42: mm_launch<4, 2>(ks, pipe, grid, st, a); break;
     case 25: mm_launch_dma<2, 5, 4>(ks, grid, st, a); break;   // loop 3, ks 64 only
+    case 45: hipLaunchKernelGGL((k_mm_dma<4, 5, 64, 4>), grid, dim3(256), 0, st, a); break;   // loop 3
     case 41:   // loop 3: 128 x 32 tiles, four waves of 64 x 16
       if (ks == 64)
         hipLaunchKernelGGL((k_mm_dma<4, 1, 64, 4>), grid, dim3(256), 0, st, a);

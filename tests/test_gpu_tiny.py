@@ -215,7 +215,7 @@ GEMM_PLAN_KEYS = (8, 9, 10, 11, 12, 13)   # OPT_GEMM_PLAN_PROJ_IN .. _HEAD
     (4, 2, 64, 3, 1), (1, 4, 64, 3, 3), (2, 2, 128, 3, 0), (2, 5, 64, 3, 0), (2, 5, 64, 3, 2),
     (2, 2, 64, 4, 0), (4, 4, 64, 4, 0), (2, 4, 64, 4, 2), (4, 2, 64, 4, 1), (2, 2, 32, 4, 0),
     (4, 4, 32, 4, 3), (2, 2, 128, 4, 0), (4, 8, 64, 4, 0), (2, 8, 64, 4, 2), (8, 8, 32, 4, 3), (8, 8, 32, 4, 0),
-    (8, 10, 32, 4, 0), (8, 10, 32, 4, 2), (4, 1, 64, 3, 0), (4, 1, 128, 3, 3),
+    (8, 10, 32, 4, 0), (8, 10, 32, 4, 2), (4, 1, 64, 3, 0), (4, 1, 128, 3, 3), (4, 5, 64, 3, 0), (4, 5, 64, 3, 4),
     (4, 4, 32, 3, 2),
     (1, 2, 128, 5, 0), (2, 2, 64, 5, 0), (2, 2, 64, 5, 3), (2, 4, 64, 5, 0), (4, 4, 64, 5, 0),
     (4, 2, 64, 5, 2), (1, 4, 64, 6, 2), (1, 2, 128, 6, 0), (4, 2, 64, 6, 1), (2, 2, 64, 6, 2)])
@@ -271,7 +271,7 @@ def test_gemm_plan_option_validation(model, R):
     for bad in (R.gemm_plan_code(3, 2, 64), R.gemm_plan_code(2, 2, 48), R.gemm_plan_code(4, 4, 64, 2),
                 R.gemm_plan_code(4, 4, 128), R.gemm_plan_code(1, 4, 64, 4), R.gemm_plan_code(2, 4, 128, 3),
                 R.gemm_plan_code(1, 2, 32, 3), R.gemm_plan_code(2, 5, 32, 3), R.gemm_plan_code(2, 5, 64, 2),
-                R.gemm_plan_code(4, 5, 64, 3), R.gemm_plan_code(1, 2, 64, 4), R.gemm_plan_code(2, 4, 32, 4),
+                R.gemm_plan_code(4, 5, 128, 3), R.gemm_plan_code(4, 5, 32, 3), R.gemm_plan_code(1, 2, 64, 4), R.gemm_plan_code(2, 4, 32, 4),
                 R.gemm_plan_code(2, 4, 128, 4), R.gemm_plan_code(2, 2, 64, 7), R.gemm_plan_code(4, 8, 64, 3),
                 R.gemm_plan_code(4, 4, 128, 5), R.gemm_plan_code(2, 2, 32, 5), R.gemm_plan_code(2, 2, 128, 6),
                 R.gemm_plan_code(2, 5, 64, 5),
