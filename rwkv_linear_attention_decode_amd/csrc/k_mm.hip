@@ -1002,6 +1002,11 @@ static MmPlan mm_choose(const ProjArgs& a, int total_rows) {
     // up to 128 rows the input projection on 64 x 64 tiles with 128-deep
     // stages (40 -> 32 us): whole 128-token prefill 4.93 -> 4.37 ms, B = 128
     // decode steps 5.40 -> 4.93 ms
+    // 65 - 128 rows: the key on 128 x 128 tiles in three K ranges (240
+    // workgroups, each operand read once per tile pair) plus the reduction
+    // launch beats one K range (2.9B: 128-token prefill 4.41 -> 4.31 ms, B = 128
+    // steps 4.73 -> 4.66 ms)
+    if (a.nseg == 1 && M > 64 && M <= 128 && N >= 8192) return {4, 4, 64, 4, 3};
     if (a.nseg == 1 && (long)(M + 63) / 64 * ((N + 127) / 128) <= 256) return {2, 4, 64, 3, 1};
     if (M <= 128 && a.nseg > 1) return {2, 2, 128, 3, 0};
     // one segment: 64 x 160 tiles when they fill the CUs in fewer column-widths
