@@ -843,6 +843,8 @@ __global__ __launch_bounds__(256) void k_wkv_scan(WkvArgs a) {
 // only is the identity (e^{l_L} = 1, every other entry 0).  The chunk count
 // is padded to a multiple of 3 (the scan's unroll) with such chunks.
 constexpr int CH = 16;
+// a compile-time integer as a value (ring slots, unrolled trip counts)
+template <int U> struct RingSlot { static constexpr int value = U; };
 __host__ __device__ inline int chunk_count(int T) { return ((T + CH - 1) / CH + 2) / 3 * 3; }
 // per (chunk, head) record, floats:
 //   A2 [16][64] | Q [16][64] | btil^T [64][16] | K2^T [64][16] | Z [16][16] | e^{l_L} [64]
@@ -898,15 +900,62 @@ __global__ __launch_bounds__(256, 3) void k_wkv_chunk_prep(WkvArgs a) {
   if constexpr (AD) {
     const int lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, k8 = 8 * (lane >> 4);
-    const int tr = c * CH + r16;
-    const half_t* lin = reinterpret_cast<const half_t*>(a.lin) + (long)(tr < T ? tr : T - 1) * a.Lin + k8;
     const int ch = h * 64 + 16 * w + r16;   // weight row of this lane
-    const floatx4 zw = chunk_adapter<DW>(lin, a.w2 + (long)ch * DW + k8);
-    const floatx4 za = chunk_adapter<DA>(lin + a.off_a, a.a2 + (long)ch * DA + k8);
-    const floatx4 zv = chunk_adapter<DV>(lin + a.off_v, a.v2 + (long)ch * DV + k8);
-    const floatx4 zg = chunk_adapter<DG>(lin + a.off_g, a.g2 + (long)ch * DG + k8);
-    // lane holds channel 16 w + r16 of tokens 4 (lane / 16) + i
+    // this wave's second-stage weights, all loaded at once
+    constexpr int NW_ = DW / 32, NA = DA / 32, NV = DV / 32, NG = DG / 32;
+    u32x4 yw[NW_], ya[NA], yv[NV], yg[NG];
+#pragma unroll
+    for (int k = 0; k < NW_; ++k) yw[k] = ld16(a.w2 + (long)ch * DW + k8 + 32 * k);
+#pragma unroll
+    for (int k = 0; k < NA; ++k) ya[k] = ld16(a.a2 + (long)ch * DA + k8 + 32 * k);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) yv[k] = ld16(a.v2 + (long)ch * DV + k8 + 32 * k);
+#pragma unroll
+    for (int k = 0; k < NG; ++k) yg[k] = ld16(a.g2 + (long)ch * DG + k8 + 32 * k);
     const float w0 = a.w0[ch], a0 = a.a0[ch], v0 = a.v0[ch];
+    // The chunk's 16 rows of first-stage activations, which all four waves
+    // multiply, go through LDS once instead of being loaded by every wave:
+    // row r holds the ranks w | a | v | g at stride XR halves (the 8-half pad
+    // puts the 16 rows' fragment reads on distinct banks).  The tile aliases
+    // the front of L, which is first written after the products.
+    constexpr int XN = DW + DA + DV + DG, XC = XN / 8, XR = XN + 8;
+    constexpr int XIT = (CH * XC + 255) / 256;
+    static_assert(CH * XR * 2 <= sizeof(ChunkPrepLds), "activation tile fits the LDS block");
+    half_t* xs = reinterpret_cast<half_t*>(&L);
+    {
+      const half_t* lin = reinterpret_cast<const half_t*>(a.lin);
+      u32x4 xv[XIT];
+#pragma unroll
+      for (int i = 0; i < XIT; ++i) {
+        const int e0 = i * 256 + tid, e = e0 < CH * XC ? e0 : CH * XC - 1;   // loads unconditional
+        const int r = e / XC, k = 8 * (e % XC);
+        const int src = k < DW ? k : k < DW + DA ? a.off_a + k - DW : k < DW + DA + DV ? a.off_v + k - DW - DA
+                                                                                     : a.off_g + k - DW - DA - DV;
+        const int tr = c * CH + r;
+        xv[i] = ld16(lin + (long)(tr < T ? tr : T - 1) * a.Lin + src);
+      }
+#pragma unroll
+      for (int i = 0; i < XIT; ++i) {
+        const int e = i * 256 + tid;
+        if (e < CH * XC) *reinterpret_cast<u32x4*>(xs + (e / XC) * XR + 8 * (e % XC)) = xv[i];
+      }
+    }
+    __syncthreads();
+    const half_t* xr = xs + r16 * XR + k8;
+    auto prod = [&](const half_t* x, const u32x4* y, auto n) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < decltype(n)::value; ++k)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const half8*>(x + 32 * k),
+                                                    __builtin_bit_cast(half8, y[k]), acc, 0, 0, 0);
+      return acc;
+    };
+    const floatx4 zw = prod(xr, yw, RingSlot<NW_>{});
+    const floatx4 za = prod(xr + DW, ya, RingSlot<NA>{});
+    const floatx4 zv = prod(xr + DW + DA, yv, RingSlot<NV>{});
+    const floatx4 zg = prod(xr + DW + DA + DV, yg, RingSlot<NG>{});
+    __syncthreads();   // every wave's fragment reads precede the writes below
+    // lane holds channel 16 w + r16 of tokens 4 (lane / 16) + i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tt = 4 * (lane >> 4) + i, col = 16 * w + r16;
@@ -1092,7 +1141,6 @@ struct ChunkRegs {
   floatx4 r[5];
   float v;
 };
-template <int U> struct RingSlot { static constexpr int value = U; };
 
 __global__ __launch_bounds__(256) void k_wkv_chunk_scan(WkvArgs a) {
   __shared__ __attribute__((aligned(16))) ChunkBuf cb[3];
