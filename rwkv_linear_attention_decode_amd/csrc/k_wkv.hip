@@ -182,14 +182,18 @@ RW_DEV void wkv_prologue_lean(const WkvArgs& a, int b, int h, HeadVecs& hv) {
 
 // GroupNorm over the head's 64 readouts + bonus * v, times the gate (wave 0);
 // gw, gb: this lane's GroupNorm weight and bias (loaded early by the caller).
-RW_DEV float wkv_epilogue(const HeadVecs& hv, float y, float gw, float gb) {
-  const int lane = threadIdx.x & 63;
+// The same for a lane that holds its channel's v and gate itself.
+RW_DEV float gn_bonus_gate(float y, float v, float g, float bonus, float gw, float gb) {
   const float mean = wave_sum(y) * (1.0f / 64.0f);
   const float dlt = y - mean;
   const float var = wave_sum(dlt * dlt) * (1.0f / 64.0f);
   float o = dlt / sqrtf(var + 64e-5f) * gw + gb;
-  o += hv.bonus * hv.v[lane];
-  return o * hv.g[lane];
+  o += bonus * v;
+  return o * g;
+}
+RW_DEV float wkv_epilogue(const HeadVecs& hv, float y, float gw, float gb) {
+  const int lane = threadIdx.x & 63;
+  return gn_bonus_gate(y, hv.v[lane], hv.g[lane], hv.bonus, gw, gb);
 }
 
 // State layout in the workgroup: the head's 64 x 64 state is 1024 float4;
@@ -1241,19 +1245,17 @@ __global__ __launch_bounds__(256) void k_wkv_chunk_scan(WkvArgs a) {
   stf4(S, st);
 }
 
-__global__ __launch_bounds__(64) void k_wkv_post(WkvArgs a) {
-  __shared__ HeadVecs hv;
-  const int tk = blockIdx.x / a.H;
-  const int h = blockIdx.x % a.H;
-  const int t = threadIdx.x;
+// One wave per (token, head), four per workgroup: lane t owns channel t and
+// holds its own readout, v and gate, so no LDS and no barrier are needed.
+__global__ __launch_bounds__(256) void k_wkv_post(WkvArgs a) {
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= a.B * a.H) return;   // whole waves
+  const int tk = item / a.H;
+  const int h = item % a.H;
+  const int t = threadIdx.x & 63;
   const long off = (long)tk * a.C + h * 64 + t;
   const float gw = a.lnx_w[h * 64 + t], gb = a.lnx_b[h * 64 + t];
-  const float yv = a.q_y[off];
-  hv.v[t] = a.q_v[off];
-  hv.g[t] = a.q_g[off];
-  if (t == 0) hv.bonus = a.q_bonus[(long)tk * a.H + h];
-  __syncthreads();
-  const float o = wkv_epilogue(hv, yv, gw, gb);
+  const float o = gn_bonus_gate(a.q_y[off], a.q_v[off], a.q_g[off], a.q_bonus[(long)tk * a.H + h], gw, gb);
   if (a.yout_f16)
     ((half_t*)a.yout)[off] = (half_t)o;
   else
@@ -1301,6 +1303,6 @@ hipError_t launch_wkv_chunk_scan(const WkvArgs& a, hipStream_t st) {
 int64_t wkv_chunk_rec_floats(int T, int H) { return (int64_t)chunk_count(T) * H * REC; }
 int wkv_chunk_rows(int T) { return chunk_count(T) * CH; }
 hipError_t launch_wkv_post(const WkvArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_wkv_post, dim3(a.B * a.H), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(k_wkv_post, dim3((a.B * a.H + 3) / 4), dim3(256), 0, st, a);
   return hipGetLastError();
 }
