@@ -394,20 +394,14 @@ __global__ __launch_bounds__(64 * NW) void k_wkv_decode_rows(WkvArgs a) {
 // separate MFMA projection: one workgroup per (head, block of 4 RPW rows).
 // Wave w first takes channels 16 w .. 16 w + 15 of all four adapters for the
 // block's rows on the fp16 matrix cores (as the chunked prefill does for 16
-// tokens; the 16-row tile's rows past the block are padding), through LDS to
-// every wave; then rows w RPW .. w RPW + RPW - 1 one after another, each as
-// k_wkv_decode_rows does for one (row, head).  The ranks are template
-// arguments so every load of the adapter step issues at once.
-// sum over N 32-rank steps of operands already in registers
-template <int N>
-RW_DEV floatx4 ad_prod(const u32x4 (&x)[N], const u32x4 (&y)[N]) {
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int k = 0; k < N; ++k)
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, x[k]), __builtin_bit_cast(half8, y[k]), acc,
-                                                0, 0, 0);
-  return acc;
-}
+// tokens; the 16-row tile's rows past the block are padding), from the
+// block's activation rows that the workgroup stages in LDS once, and passes
+// the outputs through LDS to every wave; then rows w RPW .. w RPW + RPW - 1
+// one after another, each as k_wkv_decode_rows does for one (row, head).  The
+// ranks are template arguments so every load of the adapter step issues at
+// once.
+// a compile-time integer as a value (ring slots, unrolled trip counts)
+template <int U> struct RingSlot { static constexpr int value = U; };
 
 template <int DW, int DA, int DV, int DG, int RPW>
 __global__ __launch_bounds__(256) void k_wkv_decode_ad(WkvArgs a) {
@@ -448,18 +442,33 @@ __global__ __launch_bounds__(256) void k_wkv_decode_ad(WkvArgs a) {
   load_row(wave * RPW, r0, k0, v0r, vf0);
   const float k_k = a.k_k[cc], k_a = a.k_a[cc], r_k = a.r_k[cc];
   const float gw = a.lnx_w[cc], gb = a.lnx_b[cc];
-  u32x4 xw[NW_], yw[NW_], xa[NA], ya[NA], xv[NV], yv[NV], xg[NG], yg[NG];
+  // The block's RB rows of first-stage activations, which all four waves
+  // multiply, are loaded once by the workgroup (first, so the LDS stores wait
+  // for them only) and shared through LDS in rows padded by 8 halves; tile
+  // rows past the block repeat its rows (their products are never read).
+  constexpr int XN = DW + DA + DV + DG, XC = XN / 8, XR = XN + 8, XIT = (RB * XC + 255) / 256;
+  __shared__ __attribute__((aligned(16))) half_t xs[RB * XR];
+  u32x4 xl[XIT];
   {
-    const half_t* lin = reinterpret_cast<const half_t*>(a.lin) + (long)min(b0 + r16, a.B - 1) * a.Lin + k8;
+    const half_t* lin = reinterpret_cast<const half_t*>(a.lin);
 #pragma unroll
-    for (int k = 0; k < NW_; ++k) { xw[k] = ld16(lin + 32 * k); yw[k] = ld16(a.w2 + (long)ch * DW + k8 + 32 * k); }
-#pragma unroll
-    for (int k = 0; k < NA; ++k) { xa[k] = ld16(lin + a.off_a + 32 * k); ya[k] = ld16(a.a2 + (long)ch * DA + k8 + 32 * k); }
-#pragma unroll
-    for (int k = 0; k < NV; ++k) { xv[k] = ld16(lin + a.off_v + 32 * k); yv[k] = ld16(a.v2 + (long)ch * DV + k8 + 32 * k); }
-#pragma unroll
-    for (int k = 0; k < NG; ++k) { xg[k] = ld16(lin + a.off_g + 32 * k); yg[k] = ld16(a.g2 + (long)ch * DG + k8 + 32 * k); }
+    for (int i = 0; i < XIT; ++i) {
+      const int e0 = i * 256 + (int)threadIdx.x, e = e0 < RB * XC ? e0 : RB * XC - 1;   // loads unconditional
+      const int r = e / XC, k = 8 * (e % XC);
+      const int src = k < DW ? k : k < DW + DA ? a.off_a + k - DW : k < DW + DA + DV ? a.off_v + k - DW - DA
+                                                                                   : a.off_g + k - DW - DA - DV;
+      xl[i] = ld16(lin + (long)min(b0 + r, a.B - 1) * a.Lin + src);
+    }
   }
+  u32x4 yw[NW_], ya[NA], yv[NV], yg[NG];
+#pragma unroll
+  for (int k = 0; k < NW_; ++k) yw[k] = ld16(a.w2 + (long)ch * DW + k8 + 32 * k);
+#pragma unroll
+  for (int k = 0; k < NA; ++k) ya[k] = ld16(a.a2 + (long)ch * DA + k8 + 32 * k);
+#pragma unroll
+  for (int k = 0; k < NV; ++k) yv[k] = ld16(a.v2 + (long)ch * DV + k8 + 32 * k);
+#pragma unroll
+  for (int k = 0; k < NG; ++k) yg[k] = ld16(a.g2 + (long)ch * DG + k8 + 32 * k);
   const float w0 = a.w0[ch], a0 = a.a0[ch], v0 = a.v0[ch];
   __builtin_amdgcn_sched_barrier(0);
   // a row without a state (no slot, or past B) reads the pool's first floats
@@ -472,9 +481,24 @@ __global__ __launch_bounds__(256) void k_wkv_decode_ad(WkvArgs a) {
   floatx4 s[16];
   if constexpr (EARLY) load_state(s, S);
   __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < XIT; ++i) {
+    const int e = i * 256 + (int)threadIdx.x;
+    if (e < RB * XC) *reinterpret_cast<u32x4*>(xs + (e / XC) * XR + 8 * (e % XC)) = xl[i];
+  }
+  __syncthreads();
   {
-    const floatx4 zw = ad_prod<NW_>(xw, yw), za = ad_prod<NA>(xa, ya), zv = ad_prod<NV>(xv, yv),
-                  zg = ad_prod<NG>(xg, yg);
+    const half_t* xr = xs + (r16 % RB) * XR + k8;
+    auto prod = [&](const half_t* x, const u32x4* y, auto n) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < decltype(n)::value; ++k)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const half8*>(x + 32 * k),
+                                                    __builtin_bit_cast(half8, y[k]), acc, 0, 0, 0);
+      return acc;
+    };
+    const floatx4 zw = prod(xr, yw, RingSlot<NW_>{}), za = prod(xr + DW, ya, RingSlot<NA>{}),
+                  zv = prod(xr + DW + DA, yv, RingSlot<NV>{}), zg = prod(xr + DW + DA + DV, yg, RingSlot<NG>{});
     // lane holds channel 16 w + r16 of rows 4 (lane / 16) + i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -848,7 +872,6 @@ __global__ __launch_bounds__(256) void k_wkv_scan(WkvArgs a) {
 // is padded to a multiple of 3 (the scan's unroll) with such chunks.
 constexpr int CH = 16;
 // a compile-time integer as a value (ring slots, unrolled trip counts)
-template <int U> struct RingSlot { static constexpr int value = U; };
 __host__ __device__ inline int chunk_count(int T) { return ((T + CH - 1) / CH + 2) / 3 * 3; }
 // per (chunk, head) record, floats:
 //   A2 [16][64] | Q [16][64] | btil^T [64][16] | K2^T [64][16] | Z [16][16] | e^{l_L} [64]
