@@ -328,8 +328,8 @@ const char* rwkv7_last_error(void);
 #define RWKV7_OPT_WKV_ADAPTERS 17  /* the adapters' second stage (decay, alpha, value gate, gate) on
                                       the MFMA decode path: 0 (default) inside the WKV kernel, one
                                       workgroup per head and block of rows, with the rows per wave
-                                      chosen for B and the ranks (1 up to 128 rows, 2 above; 4 where
-                                      the ranks sum past 512); 1 a separate MFMA projection whose
+                                      chosen for B and the ranks (1; 2 up to 128 rows where the
+                                      ranks sum past 512); 1 a separate MFMA projection whose
                                       outputs the WKV kernel reads; 2, 3, 4 inside the WKV kernel
                                       with 1, 2, 4 rows per wave.  Shapes without an instantiated
                                       adapter step

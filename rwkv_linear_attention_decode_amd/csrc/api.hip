@@ -501,8 +501,10 @@ int wkv_ad_rows_per_wave(const rwkv7_model* m, int B) {
     case 3: return 2;
     case 4: return 4;
     default:
-      if (m->d.Dw + m->d.Da + m->d.Dv + m->d.Dg > 512) return 4;
-      return B <= 128 ? 1 : 2;
+      // whole-step sweeps: one row per wave, except two up to 128 rows when
+      // the ranks sum past 512 (7.2B)
+      if (m->d.Dw + m->d.Da + m->d.Dv + m->d.Dg > 512) return B <= 128 ? 2 : 1;
+      return 1;
   }
 }
 
@@ -1568,8 +1570,20 @@ const char* rwkv7_kernel_name(const rwkv7_model* m, int32_t cls, int32_t B) {
     case RWKV7_K_HEAD:
       return p.gemv ? gemv_kernel_name(B, m->d.C, EPI_NONE, m->d.V, 1, p.fused, q) : gemm_kernel_name(B, m->d.V, m->d.C);
     case RWKV7_K_WKV: {
-      if (!p.gemv) return wkv_rows_waves(B * m->d.H) == 5 ? "k_wkv_decode_rows<5>" : "k_wkv_decode_rows<4>";
-      static char name[32];
+      static char name[48];
+      if (!p.gemv) {
+        const Dims& d = m->d;
+        WkvArgs t;
+        memset(&t, 0, sizeof t);
+        t.Lin = d.Lin; t.off_a = d.Dwp; t.off_v = d.Dwp + d.Dap; t.off_g = d.Dwp + d.Dap + d.Dvp;
+        t.Dw = d.Dw; t.Da = d.Da; t.Dv = d.Dv; t.Dg = d.Dg;
+        const int rpw = wkv_ad_rows_per_wave(m, B);
+        if (rpw && wkv_chunk_adapters_ok(t)) {
+          snprintf(name, sizeof name, "k_wkv_decode_ad<%d, %d, %d, %d, %d>", d.Dw, d.Da, d.Dv, d.Dg, rpw);
+          return name;
+        }
+        return wkv_rows_waves(B * d.H) == 5 ? "k_wkv_decode_rows<5>" : "k_wkv_decode_rows<4>";
+      }
       snprintf(name, sizeof name, "k_wkv_decode<%d>", (m->d.Dw + m->d.Da + m->d.Dv + m->d.Dg) / 32);
       return name;
     }
