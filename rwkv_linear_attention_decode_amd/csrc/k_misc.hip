@@ -276,7 +276,10 @@ RW_DEV void lnm_store_f16_own(half_t* p, const float (&v)[NE], int t, uint32_t o
   }
 }
 
-template <int NE>
+// LATE: the mixing vectors are loaded after the statistics, so they are not
+// live across the reductions (fewer registers, more workgroups per CU; the
+// sequence path, where rows fill the CUs several times over)
+template <int NE, bool LATE = false>
 __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
   __shared__ float red[16];
   const int r = blockIdx.x;
@@ -332,15 +335,18 @@ __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
 #pragma unroll
     for (int i = 0; i < NE; ++i) pv[i] += acc[i];
   }
+  auto load_mu = [&]() {
 #pragma unroll
-  for (int q = 0; q < 6; ++q) {
-    if (q < a.nq && a.mu) {
-      lnm_load_own<NE>(a.mu + (long)q * C, mu[q], t, own);
-    } else {
+    for (int q = 0; q < 6; ++q) {
+      if (q < a.nq && a.mu) {
+        lnm_load_own<NE>(a.mu + (long)q * C, mu[q], t, own);
+      } else {
 #pragma unroll
-      for (int i = 0; i < NE; ++i) mu[q][i] = 0.0f;
+        for (int i = 0; i < NE; ++i) mu[q][i] = 0.0f;
+      }
     }
-  }
+  };
+  if constexpr (!LATE) load_mu();
   if (a.nparts > 0) {
     // x += (sum of the split-K partials of the residual projection, in range
     // order): the same arithmetic as the GEMM's own reduction pass
@@ -373,6 +379,7 @@ __global__ __launch_bounds__(256) void k_ln_mix(LnMixArgs a) {
 
   float mean, rstd;
   ln_rows<NE>(v, &mean, &rstd, red);
+  if constexpr (LATE) load_mu();
   float u[NE];
 #pragma unroll
   for (int i = 0; i < NE; ++i) u[i] = (v[i] - mean) * rstd * gv[i] + bv[i];
@@ -414,6 +421,15 @@ hipError_t launch_ln_mix(const LnMixArgs& a, hipStream_t st) {
   if (a.ncb < 1 || a.ncb > units) return hipErrorInvalidValue;
   if (a.ncb > 1 && (a.mode == LNMIX_SEQ || (a.nparts && (!a.x_out || a.x_out == a.x))))
     return hipErrorInvalidValue;
+  if (a.mode == LNMIX_SEQ) {
+    switch (a.C / 256) {
+#define X(n) case n: hipLaunchKernelGGL((k_ln_mix<n, true>), dim3(a.R, a.ncb), dim3(256), 0, st, a); break;
+      X(1) X(2) X(4) X(8) X(10) X(12) X(16)
+#undef X
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   NE_DISPATCH(a.C, k_ln_mix, dim3(a.R, a.ncb), dim3(256), 0, st, a);
   return hipGetLastError();
 }
