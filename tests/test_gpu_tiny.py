@@ -198,6 +198,13 @@ def test_wkv_adapter_paths(weights, W, R):
             for opt in (2, 3, 4, 0):
                 assert rel(runs[opt][0], runs[1][0]) <= 1e-4, (B, opt)
                 assert rel(runs[opt][1], runs[1][1]) <= 1e-4, (B, opt)
+        # the kernel-name query follows the option (rows per wave as the last argument)
+        for opt, name in ((0, "k_wkv_decode_ad<32, 32, 32, 64, 1>"), (2, "k_wkv_decode_ad<32, 32, 32, 64, 1>"),
+                          (3, "k_wkv_decode_ad<32, 32, 32, 64, 2>"), (4, "k_wkv_decode_ad<32, 32, 32, 64, 4>"),
+                          (1, "k_wkv_decode_rows<")):
+            m.set_option(R.OPT_WKV_ADAPTERS, opt)
+            assert R.rwkv7_kernel_name(m.handle, R.K_WKV, 8).startswith(name), (opt, name)
+        assert R.rwkv7_kernel_name(m.handle, R.K_WKV, 1).startswith("k_wkv_decode<")
         with pytest.raises(R.RWKV7Error):
             m.set_option(R.OPT_WKV_ADAPTERS, 5)
     finally:
